@@ -1,0 +1,317 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle.
+
+Each test checks the oracle against brute force written differently (integer
+matmul, lexsort, a library attention routine), closed forms, invariants or the
+hand-worked example in tests/golden, so that a dropped term, a wrong sign or
+index, or a transposed operand in the oracle fails at least one of them.
+"""
+import json
+import math
+import os
+from decimal import Decimal, getcontext
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from dsa_top_token_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def f32_bits(x):
+    return np.asarray(x, np.float32).view(np.uint32)
+
+
+def correctly_rounded_f32(x: Decimal) -> np.float32:
+    """Round a Decimal to the nearest float32 (ties to even), exactly."""
+    c = np.float32(float(x))
+    best = c
+    for cand in (np.nextafter(c, np.float32(-np.inf)), c,
+                 np.nextafter(c, np.float32(np.inf))):
+        e_c, e_b = abs(Decimal(float(cand)) - x), abs(Decimal(float(best)) - x)
+        if e_c < e_b or (e_c == e_b and (int(f32_bits(cand)) & 1) == 0):
+            best = cand
+    return np.float32(best)
+
+
+@pytest.mark.parametrize("d", [4, 32, 64, 96, 128, 160, 256])
+def test_index_scale_is_correctly_rounded(d):
+    getcontext().prec = 60
+    exact = Decimal(1) / Decimal(d).sqrt()
+    assert f32_bits(oracle.index_scale(d)) == f32_bits(correctly_rounded_f32(exact))
+
+
+KNOWN_SCALE_BITS = {96: 0x3DD105EC, 128: 0x3DB504F3, 160: 0x3DA1E89B, 4: 0x3F000000}
+
+
+@pytest.mark.parametrize("d", sorted(KNOWN_SCALE_BITS))
+def test_index_scale_known_bits(d):
+    assert int(f32_bits(oracle.index_scale(d))) == KNOWN_SCALE_BITS[d]
+
+
+def test_fp8_decoding_matches_torch_for_every_code():
+    # d = 1, key = +1 (or -1): the score is relu(value) (or relu(-value)), so
+    # every non-NaN e4m3fn code is decoded through the indexer itself.
+    codes = torch.arange(256, dtype=torch.int16).to(torch.uint8)
+    fp = codes.view(torch.float8_e4m3fn)
+    ref = fp.to(torch.float32).numpy()
+    ok = ~np.isnan(ref)
+    q = fp.reshape(1, 256, 1)
+    for sign in (1.0, -1.0):
+        k = torch.tensor([[[sign]]], dtype=torch.float32).to(torch.float8_e4m3fn)
+        s = oracle.index_scores(q, k, q_pos0=0, dtype="fp8")[0, :, 0]
+        exp = np.maximum(ref * sign, 0).astype(np.float32)
+        assert np.array_equal(f32_bits(s[ok]), f32_bits(exp[ok]))
+
+
+def test_bf16_decoding_matches_torch():
+    g = torch.Generator().manual_seed(7)
+    bits = torch.randint(0, 1 << 16, (4096,), generator=g, dtype=torch.int32)
+    bits = bits.to(torch.int16)
+    vals = bits.view(torch.bfloat16)
+    ref = vals.to(torch.float32).numpy()
+    ok = np.isfinite(ref) & (np.abs(ref) < 1e30) & (np.abs(ref) > 1e-30)
+    q = vals.reshape(1, -1, 1)
+    k = torch.ones((1, 1, 1), dtype=torch.bfloat16)
+    s = oracle.index_scores(q, k, q_pos0=10 ** 6, dtype="bf16")[0, :, 0]
+    exp = np.maximum(ref, 0).astype(np.float32)
+    assert np.array_equal(f32_bits(s[ok]), f32_bits(exp[ok]))
+
+
+def brute_scores(q_int, k_int, q_pos0, d):
+    """Integer matmul, one float32 multiply by the exact-rounded scale, ReLU,
+    -inf past each query's position."""
+    getcontext().prec = 60
+    scale = correctly_rounded_f32(Decimal(1) / Decimal(d).sqrt())
+    n = np.einsum("bic,bjc->bij", q_int.astype(np.int64), k_int.astype(np.int64))
+    s = (n.astype(np.float32) * scale).astype(np.float32)
+    s = np.where(s > 0, s, np.float32(0)).astype(np.float32)
+    n_q, n_k = q_int.shape[1], k_int.shape[1]
+    pos = q_pos0 + np.arange(n_q)[:, None]
+    s[:, np.arange(n_k)[None, :] > pos] = -np.inf
+    return s
+
+
+@pytest.mark.parametrize("dtype", ["fp8", "bf16"])
+@pytest.mark.parametrize("d,n_q,n_k,q_pos0", [
+    (32, 37, 37, 0), (96, 19, 53, 34), (160, 8, 40, 5), (128, 1, 300, 299)])
+def test_index_scores_vs_integer_matmul(dtype, d, n_q, n_k, q_pos0):
+    g = torch.Generator().manual_seed(d * 1000 + n_q)
+    qi = torch.randint(-4, 5, (2, n_q, d), generator=g)
+    ki = torch.randint(-5, 6, (2, n_k, d), generator=g)
+    tdt = torch.float8_e4m3fn if dtype == "fp8" else torch.bfloat16
+    s = oracle.index_scores(qi.to(tdt), ki.to(tdt), q_pos0=q_pos0)
+    exp = brute_scores(qi.numpy(), ki.numpy(), q_pos0, d)
+    assert np.array_equal(f32_bits(s), f32_bits(exp))
+    # invariants: never -0.0, -inf exactly past pos
+    fin = np.isfinite(s)
+    assert not np.any(f32_bits(s[fin]) == 0x80000000)
+    assert np.all(s[fin] >= 0)
+    pos = q_pos0 + np.arange(n_q)[:, None]
+    assert np.array_equal(~fin[0], np.arange(n_k)[None, :] > pos)
+
+
+def test_index_scores_row_slab_matches_full():
+    w = synth.WORKLOADS["prefill_1k"].replace(n_q=96, n_k=96)
+    x = synth.make_inputs(w, parts=("q_idx", "k_idx"))
+    full = oracle.index_scores(x["q_idx"], x["k_idx"], 0)
+    slab = oracle.index_scores(x["q_idx"], x["k_idx"], 0, q_begin=40, q_end=71)
+    assert np.array_equal(f32_bits(full[:, 40:71]), f32_bits(slab))
+
+
+def test_index_scores_bf16_nonintegers_exact_dot():
+    # bf16 N(0,1) products are exact in double and their sums of 160 terms
+    # stay exact, so the score is fl32(exact dot) * scale, like the matmul in
+    # float64 below (also exact).
+    g = torch.Generator().manual_seed(3)
+    q = torch.randn((1, 9, 160), generator=g).to(torch.bfloat16)
+    k = torch.randn((1, 9, 160), generator=g).to(torch.bfloat16)
+    s = oracle.index_scores(q, k, 0)
+    getcontext().prec = 60
+    scale = correctly_rounded_f32(Decimal(1) / Decimal(160).sqrt())
+    dot = q.double().numpy()[0] @ k.double().numpy()[0].T
+    exp = np.maximum((dot.astype(np.float32) * scale).astype(np.float32), 0)
+    mask = np.arange(9)[None, :] > np.arange(9)[:, None]
+    exp[mask] = -np.inf
+    assert np.array_equal(f32_bits(s[0]), f32_bits(exp))
+
+
+def brute_topk(scores, pos_begin, k):
+    B, rows, n_k = scores.shape
+    out = np.full((B, rows, k), -1, np.int32)
+    for b in range(B):
+        for r in range(rows):
+            n = min(pos_begin + r + 1, n_k)
+            s = scores[b, r, :n]
+            order = np.lexsort((np.arange(n), -s.astype(np.float64)))
+            sel = np.sort(order[:min(k, n)])
+            out[b, r, :len(sel)] = sel
+    return out
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 7, 40, 64, 100])
+@pytest.mark.parametrize("levels", [3, 50, 0])
+def test_topk_vs_lexsort(k, levels):
+    g = np.random.default_rng(k * 100 + levels)
+    B, rows, n_k, pos_begin = 2, 23, 64, 41
+    if levels:
+        s = (g.integers(0, levels, (B, rows, n_k)) * 0.25).astype(np.float32)
+    else:
+        s = np.maximum(g.standard_normal((B, rows, n_k)), 0).astype(np.float32)
+    for r in range(rows):
+        s[:, r, pos_begin + r + 1:] = -np.inf
+    got = oracle.topk(s, pos_begin, k)
+    assert np.array_equal(got, brute_topk(s, pos_begin, k))
+
+
+def check_topk_invariants(scores, idx, pos_begin, k):
+    B, rows, n_k = scores.shape
+    for b in range(B):
+        for r in range(rows):
+            n = min(pos_begin + r + 1, n_k)
+            row = idx[b, r]
+            m = min(k, n)
+            sel = row[:m]
+            assert np.all(row[m:] == -1)
+            assert np.all((sel >= 0) & (sel < n))
+            assert np.all(np.diff(sel) > 0)
+            mask = np.zeros(n, bool)
+            mask[sel] = True
+            s = scores[b, r, :n]
+            if m < n:
+                # every selected key precedes every unselected one
+                worst_sel = min(zip(-s[mask], np.nonzero(mask)[0]), key=lambda t: (-t[0], -t[1]))
+                best_un = min(zip(-s[~mask], np.nonzero(~mask)[0]))
+                assert (worst_sel[0], worst_sel[1]) < best_un
+
+
+def test_topk_invariants_on_synthetic_rows():
+    w = synth.WORKLOADS["prefill_1k"].replace(n_q=300, n_k=300, top_k=64)
+    x = synth.make_inputs(w, parts=("q_idx", "k_idx"))
+    s = oracle.index_scores(x["q_idx"], x["k_idx"], 0)
+    idx = oracle.topk(s, 0, 64)
+    check_topk_invariants(s, idx, 0, 64)
+    assert np.array_equal(idx, brute_topk(s, 0, 64))
+
+
+def test_topk_all_zero_query_picks_first_keys():
+    # every score is 0, so the k lowest indices win
+    n = 50
+    s = np.zeros((1, n, n), np.float32)
+    for r in range(n):
+        s[0, r, r + 1:] = -np.inf
+    idx = oracle.topk(s, 0, 8)
+    for r in range(n):
+        m = min(8, r + 1)
+        assert list(idx[0, r, :m]) == list(range(m))
+
+
+def test_worked_example():
+    ex = json.load(open(os.path.join(GOLDEN, "worked_example_d4.json")))
+    q = torch.tensor([ex["q_idx"]], dtype=torch.float32).to(torch.float8_e4m3fn)
+    k = torch.tensor([ex["k_idx"]], dtype=torch.float32).to(torch.float8_e4m3fn)
+    s = oracle.index_scores(q, k, ex["q_pos0"])[0]
+    exp = np.array([[float(v) for v in row] for row in ex["scores"]], np.float32)
+    assert np.array_equal(f32_bits(s), f32_bits(exp))
+    for kk, rows in ex["topk"].items():
+        got = oracle.topk(s[None], 0, int(kk))[0]
+        assert got.tolist() == rows, kk
+    att = ex["attention"]
+    idx = oracle.topk(s[None], 0, att["top_k"])
+    V = torch.tensor([att["V"]], dtype=torch.bfloat16)
+    Q = torch.zeros((1, 4, att["Q_zero_heads"], 2), dtype=torch.bfloat16)
+    O, lse = oracle.sparse_attn(Q, V, V, idx)
+    assert np.allclose(O[0, :, 0], np.array(att["O"]), atol=0, rtol=0)
+    lse_exp = [0.0 if v == "0" else math.log(2) for v in att["lse"]]
+    assert np.allclose(lse[0, :, 0], lse_exp, atol=1e-7)
+
+
+def dense_attn_torch(Q, K, V, q_pos0):
+    """Dense MQA attention with the causal mask, through torch's
+    scaled_dot_product_attention in float64 (K/V expanded to every head)."""
+    B, n_q, H, D = Q.shape
+    n_k = K.shape[1]
+    q = Q.double().permute(0, 2, 1, 3)
+    k = K.double()[:, None].expand(B, H, n_k, D)
+    v = V.double()[:, None].expand(B, H, n_k, D)
+    pos = q_pos0 + torch.arange(n_q)[:, None]
+    mask = torch.arange(n_k)[None, :] <= pos
+    o = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=mask)
+    return o.permute(0, 2, 1, 3).numpy()
+
+
+@pytest.mark.parametrize("n_q,n_k,q_pos0,H", [(33, 33, 0, 4), (5, 70, 65, 3)])
+def test_attention_full_selection_equals_dense(n_q, n_k, q_pos0, H):
+    g = torch.Generator().manual_seed(n_k)
+    Q = torch.randn((2, n_q, H, 128), generator=g).to(torch.bfloat16)
+    K = torch.randn((2, n_k, 128), generator=g).to(torch.bfloat16)
+    V = torch.randn((2, n_k, 128), generator=g).to(torch.bfloat16)
+    k = n_k + 3
+    idx = np.full((2, n_q, k), -1, np.int32)
+    for i in range(n_q):
+        idx[:, i, :q_pos0 + i + 1] = np.arange(q_pos0 + i + 1)
+    O, lse = oracle.sparse_attn(Q, K, V, idx)
+    ref = dense_attn_torch(Q, K, V, q_pos0)
+    assert np.max(np.abs(O - ref)) < 1e-6
+    # lse against a direct log-sum-exp over the causal keys (torch logsumexp)
+    s = torch.einsum("bihd,bjd->bihj", Q.double(), K.double()) / math.sqrt(128)
+    pos = q_pos0 + torch.arange(n_q)
+    s = s.masked_fill(torch.arange(n_k)[None, None, None, :] > pos[None, :, None, None], -math.inf)
+    assert np.max(np.abs(lse - torch.logsumexp(s, -1).numpy())) < 1e-5
+
+
+def test_attention_closed_forms():
+    g = torch.Generator().manual_seed(11)
+    n_k, H = 40, 2
+    V = torch.randn((1, n_k, 128), generator=g).to(torch.bfloat16)
+    K = torch.randn((1, n_k, 128), generator=g).to(torch.bfloat16)
+    sel = np.array([[[3, 9, 17, 30, -1, -1]]], np.int32)
+    # Q = 0: uniform weights, O = mean of the selected V rows, lse = ln 4
+    O, lse = oracle.sparse_attn(torch.zeros((1, 1, H, 128), dtype=torch.bfloat16), K, V, sel)
+    mean = V.double().numpy()[0, [3, 9, 17, 30]].mean(0)
+    assert np.max(np.abs(O[0, 0] - mean[None])) < 1e-6
+    assert np.allclose(lse, math.log(4), atol=1e-6)
+    # a single selected key: O is that V row exactly
+    Q = torch.randn((1, 1, H, 128), generator=g).to(torch.bfloat16)
+    one = np.array([[[21, -1, -1]]], np.int32)
+    O1, _ = oracle.sparse_attn(Q, K, V, one)
+    assert np.array_equal(O1[0, 0], np.repeat(V.float().numpy()[0, 21][None], H, 0))
+    # permuting the selection changes nothing; O stays inside the V hull
+    O2, _ = oracle.sparse_attn(Q, K, V, sel)
+    O3, _ = oracle.sparse_attn(Q, K, V, sel[:, :, [5, 2, 0, 4, 3, 1]])
+    assert np.max(np.abs(O2 - O3)) < 1e-6
+    rows = V.float().numpy()[0, [3, 9, 17, 30]]
+    assert np.all(O2[0, 0] <= rows.max(0) + 1e-6) and np.all(O2[0, 0] >= rows.min(0) - 1e-6)
+
+
+@pytest.mark.parametrize("name", ["prefill_1k", "decode_32k"])
+def test_forward_is_the_three_stages(name):
+    w = synth.WORKLOADS[name]
+    if w.mode == "prefill":
+        w = w.replace(n_q=200, n_k=200, top_k=32, n_heads=2)
+        qb, qe = 150, 200
+    else:
+        w = w.replace(batch=2, n_k=700, q_pos0=699, top_k=64, n_heads=2)
+        qb, qe = 0, 1
+    x = synth.make_inputs(w)
+    idx, O, lse = oracle.forward(x["q_idx"], x["k_idx"], x["Q"], x["K"], x["V"],
+                                 w.q_pos0, w.top_k, qb, qe)
+    s = oracle.index_scores(x["q_idx"], x["k_idx"], w.q_pos0, qb, qe)
+    idx2 = oracle.topk(s, w.q_pos0 + qb, w.top_k)
+    O2, lse2 = oracle.sparse_attn(x["Q"][:, qb:qe], x["K"], x["V"], idx2)
+    assert np.array_equal(idx, idx2)
+    assert np.array_equal(O, O2) and np.array_equal(lse, lse2)
+    check_topk_invariants(s, idx, w.q_pos0 + qb, w.top_k)
+
+
+def test_clustered_generator_range_and_ties():
+    w = synth.WORKLOADS["decode_128k_clustered"].replace(batch=2, n_k=4096)
+    x = synth.make_inputs(w, parts=("q_idx", "k_idx"))
+    kv = x["k_idx"].float()
+    assert kv.min() >= -5 and kv.max() <= 5
+    assert torch.equal(kv, kv.round())
+    s = oracle.index_scores(x["q_idx"], x["k_idx"], w.q_pos0)
+    # heavy ties: far fewer distinct scores than keys
+    assert len(np.unique(s[0, 0])) < 400
