@@ -1,0 +1,205 @@
+"""MI355X (gfx950) DSA path: lightning indexer -> top-k -> sparse MQA attention.
+
+A thin ctypes binding over libdsa.so (include/dsa.h). Every step of the path
+runs in the library's HIP kernels; this module only checks tensors, builds
+the dsa_problem description, allocates outputs and workspace through torch
+and passes raw device pointers plus torch's current stream. There is no CPU
+fallback: if libdsa.so is missing, every call raises.
+
+Method: the DeepSeek-V3.2 DSA page (kwkr.cn/news/60693), sections 3.2
+(indexer score), 3.3 (top-k then attention over the kept keys), 4.1-4.3
+(precisions, shared K/V across heads, one fused chain).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdsa.so")
+
+DSA_OK = 0
+STATUS = {0: "DSA_OK", -1: "DSA_E_NULL", -2: "DSA_E_SHAPE", -3: "DSA_E_UNSUPPORTED",
+          -4: "DSA_E_ALIGN", -5: "DSA_E_WORKSPACE", -6: "DSA_E_HIP"}
+IDX_FP8, IDX_BF16 = 0, 1
+OP_TOPK, OP_ATTN, OP_FORWARD = 1, 2, 3
+HEAD_DIM = 128
+
+EXPORTS = ("dsa_workspace_size", "dsa_index_scores", "dsa_topk", "dsa_sparse_attn",
+           "dsa_forward", "dsa_status_str", "dsa_last_error")
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("batch", "n_q", "n_k", "q_pos0", "d_idx", "idx_dtype", "top_k",
+                 "n_heads", "head_dim")]
+
+
+class DSAError(RuntimeError):
+    def __init__(self, status, detail):
+        super().__init__("%s: %s" % (STATUS.get(status, status), detail))
+        self.status = status
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def load():
+    """Load libdsa.so (built in-tree by build.py); raise if it is absent."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(
+                    "libdsa.so is not built (%s); run __graft_entry__.build() or "
+                    "python dsa_top_token_amd/build.py" % LIB_PATH)
+            lib = ctypes.CDLL(LIB_PATH)
+            P, I, S = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+            PP = ctypes.POINTER(Problem)
+            lib.dsa_workspace_size.argtypes = [PP, I, ctypes.POINTER(S)]
+            lib.dsa_index_scores.argtypes = [PP, P, P, I, I, P, P]
+            lib.dsa_topk.argtypes = [PP, P, I, I, P, P, S, P]
+            lib.dsa_sparse_attn.argtypes = [PP, P, P, P, P, P, P, P, S, P]
+            lib.dsa_forward.argtypes = [PP, P, P, P, P, P, P, P, P, P, S, P]
+            for f in (lib.dsa_workspace_size, lib.dsa_index_scores, lib.dsa_topk,
+                      lib.dsa_sparse_attn, lib.dsa_forward):
+                f.restype = I
+            lib.dsa_status_str.argtypes = [I]
+            lib.dsa_status_str.restype = ctypes.c_char_p
+            lib.dsa_last_error.argtypes = []
+            lib.dsa_last_error.restype = ctypes.c_char_p
+            _lib = lib
+    return _lib
+
+
+def _check(rc):
+    if rc != DSA_OK:
+        raise DSAError(rc, load().dsa_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def make_problem(batch, n_q, n_k, q_pos0, d_idx, idx_dtype, top_k, n_heads,
+                 head_dim=HEAD_DIM) -> Problem:
+    if isinstance(idx_dtype, torch.dtype):
+        idx_dtype = IDX_FP8 if idx_dtype == torch.float8_e4m3fn else IDX_BF16
+    elif isinstance(idx_dtype, str):
+        idx_dtype = {"fp8": IDX_FP8, "bf16": IDX_BF16}[idx_dtype]
+    return Problem(batch, n_q, n_k, q_pos0, d_idx, idx_dtype, top_k, n_heads, head_dim)
+
+
+def workspace_size(p: Problem, op: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().dsa_workspace_size(ctypes.byref(p), op, ctypes.byref(n)))
+    return n.value
+
+
+def _dev_tensor(t, name, dtypes, ndim):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError("%s must be a CUDA (HIP) tensor" % name)
+    if t.dtype not in dtypes:
+        raise TypeError("%s has dtype %s, expected one of %s" % (name, t.dtype, dtypes))
+    if t.dim() != ndim or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous %d-d tensor" % (name, ndim))
+    return t
+
+
+_IDX_DTYPES = (torch.float8_e4m3fn, torch.bfloat16)
+
+
+def _workspace(p, op, dev):
+    n = workspace_size(p, op)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=dev), n
+
+
+def index_scores(q_idx, k_idx, q_pos0, q_begin=0, q_end=None, top_k=1, n_heads=1):
+    """Indexer scores [B, q_end-q_begin, n_k] float32 (-inf past each query)."""
+    _dev_tensor(q_idx, "q_idx", _IDX_DTYPES, 3)
+    _dev_tensor(k_idx, "k_idx", (q_idx.dtype,), 3)
+    B, n_q, d = q_idx.shape
+    n_k = k_idx.shape[1]
+    q_end = n_q if q_end is None else q_end
+    p = make_problem(B, n_q, n_k, q_pos0, d, q_idx.dtype, top_k, n_heads)
+    out = torch.empty((B, max(q_end - q_begin, 0), n_k), dtype=torch.float32,
+                      device=q_idx.device)
+    _check(load().dsa_index_scores(ctypes.byref(p), _ptr(q_idx), _ptr(k_idx), q_begin,
+                                   q_end, _ptr(out), _stream(q_idx.device)))
+    return out
+
+
+def topk(scores, q_pos0, top_k, n_q=None, q_begin=0, d_idx=32):
+    """Top-k indices [B, rows, top_k] int32 (ascending, -1 padded) of score rows
+    belonging to queries q_begin.. of sequences with n_q queries at q_pos0."""
+    _dev_tensor(scores, "scores", (torch.float32,), 3)
+    B, rows, n_k = scores.shape
+    n_q = q_begin + rows if n_q is None else n_q
+    p = make_problem(B, n_q, n_k, q_pos0, d_idx, IDX_FP8, top_k, 1)
+    idx = torch.empty((B, rows, top_k), dtype=torch.int32, device=scores.device)
+    ws, n = _workspace(p, OP_TOPK, scores.device)
+    _check(load().dsa_topk(ctypes.byref(p), _ptr(scores), q_begin, q_begin + rows,
+                           _ptr(idx), _ptr(ws), n, _stream(scores.device)))
+    return idx
+
+
+def sparse_attn(Q, K, V, idx, want_lse=True, q_pos0=None):
+    """O [B, n_q, H, 128] bf16 and lse [B, n_q, H] float32 (or None)."""
+    _dev_tensor(Q, "Q", (torch.bfloat16,), 4)
+    _dev_tensor(K, "K", (torch.bfloat16,), 3)
+    _dev_tensor(V, "V", (torch.bfloat16,), 3)
+    _dev_tensor(idx, "idx", (torch.int32,), 3)
+    B, n_q, H, D = Q.shape
+    n_k = K.shape[1]
+    top_k = idx.shape[2]
+    if q_pos0 is None:
+        q_pos0 = n_k - n_q
+    p = make_problem(B, n_q, n_k, q_pos0, 32, IDX_FP8, top_k, H, D)
+    O = torch.empty_like(Q)
+    lse = torch.empty((B, n_q, H), dtype=torch.float32, device=Q.device) if want_lse else None
+    ws, n = _workspace(p, OP_ATTN, Q.device)
+    _check(load().dsa_sparse_attn(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(idx),
+                                  _ptr(O), _ptr(lse), _ptr(ws), n, _stream(Q.device)))
+    return O, lse
+
+
+class Forward:
+    """dsa_forward with its workspace allocated once for a fixed problem."""
+
+    def __init__(self, problem: Problem, device):
+        self.p = problem
+        self.device = torch.device(device)
+        self.ws, self.ws_bytes = _workspace(problem, OP_FORWARD, self.device)
+
+    def __call__(self, q_idx, k_idx, Q, K, V, O, idx_out=None, lse=None):
+        _check(load().dsa_forward(ctypes.byref(self.p), _ptr(q_idx), _ptr(k_idx), _ptr(Q),
+                                  _ptr(K), _ptr(V), _ptr(idx_out), _ptr(O), _ptr(lse),
+                                  _ptr(self.ws), self.ws_bytes, _stream(self.device)))
+
+
+def forward(q_idx, k_idx, Q, K, V, q_pos0, top_k, want_idx=True, want_lse=True):
+    """The fused chain. Returns (idx [B,n_q,top_k] int32 or None,
+    O [B,n_q,H,128] bf16, lse [B,n_q,H] float32 or None)."""
+    _dev_tensor(q_idx, "q_idx", _IDX_DTYPES, 3)
+    _dev_tensor(k_idx, "k_idx", (q_idx.dtype,), 3)
+    _dev_tensor(Q, "Q", (torch.bfloat16,), 4)
+    _dev_tensor(K, "K", (torch.bfloat16,), 3)
+    _dev_tensor(V, "V", (torch.bfloat16,), 3)
+    B, n_q, d = q_idx.shape
+    n_k = k_idx.shape[1]
+    H = Q.shape[2]
+    p = make_problem(B, n_q, n_k, q_pos0, d, q_idx.dtype, top_k, H, Q.shape[3])
+    dev = Q.device
+    idx = torch.empty((B, n_q, top_k), dtype=torch.int32, device=dev) if want_idx else None
+    O = torch.empty_like(Q)
+    lse = torch.empty((B, n_q, H), dtype=torch.float32, device=dev) if want_lse else None
+    Forward(p, dev)(q_idx, k_idx, Q, K, V, O, idx, lse)
+    return idx, O, lse

@@ -1,0 +1,299 @@
+// C ABI of the DSA library: argument validation, workspace layout and the
+// launch sequence of each call. Every check runs on the host before anything
+// is enqueued; the library allocates no device memory.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/dsa.h"
+#include "dsa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+dsa_status fail(dsa_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+dsa_status ok() {
+    g_last_error.clear();
+    return DSA_OK;
+}
+
+constexpr long long kMaxKeys = 4194304;
+constexpr int kMaxTopK = 4096;
+constexpr int kMaxHeads = 16;
+constexpr int kHeadDim = 128;
+constexpr size_t kAlign = 256;
+constexpr size_t kScoreSlabBytes = size_t(2) << 30;  // score rows staged per forward pass
+constexpr size_t kPartFloats = 16 * (kHeadDim + 4);   // attention partial per (task)
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+dsa_status check_problem(const dsa_problem* p) {
+    if (!p) return fail(DSA_E_NULL, "problem is NULL");
+    if (p->batch < 1 || p->n_q < 1 || p->n_k < 1 || p->q_pos0 < 0)
+        return fail(DSA_E_SHAPE, "batch, n_q, n_k must be >= 1 and q_pos0 >= 0 "
+                    "(got batch=%d n_q=%d n_k=%d q_pos0=%d)", p->batch, p->n_q, p->n_k, p->q_pos0);
+    if (p->n_k > kMaxKeys)
+        return fail(DSA_E_SHAPE, "n_k=%d exceeds %lld", p->n_k, kMaxKeys);
+    if ((long long)p->q_pos0 + p->n_q > p->n_k)
+        return fail(DSA_E_SHAPE, "q_pos0 + n_q = %lld exceeds n_k = %d",
+                    (long long)p->q_pos0 + p->n_q, p->n_k);
+    if (p->d_idx < 1) return fail(DSA_E_SHAPE, "d_idx=%d must be positive", p->d_idx);
+    if (p->d_idx % 32 != 0 || p->d_idx > 256)
+        return fail(DSA_E_UNSUPPORTED, "d_idx=%d must be a multiple of 32 in [32, 256]", p->d_idx);
+    if (p->idx_dtype != DSA_IDX_FP8_E4M3FN && p->idx_dtype != DSA_IDX_BF16)
+        return fail(DSA_E_UNSUPPORTED, "idx_dtype=%d is neither fp8 e4m3fn (0) nor bf16 (1)",
+                    p->idx_dtype);
+    if (p->top_k < 1) return fail(DSA_E_SHAPE, "top_k=%d must be >= 1", p->top_k);
+    if (p->top_k > kMaxTopK)
+        return fail(DSA_E_UNSUPPORTED, "top_k=%d exceeds %d", p->top_k, kMaxTopK);
+    if (p->n_heads < 1) return fail(DSA_E_SHAPE, "n_heads=%d must be >= 1", p->n_heads);
+    if (p->n_heads > kMaxHeads)
+        return fail(DSA_E_UNSUPPORTED, "n_heads=%d exceeds %d", p->n_heads, kMaxHeads);
+    if (p->head_dim != kHeadDim)
+        return fail(DSA_E_UNSUPPORTED, "head_dim=%d must be %d", p->head_dim, kHeadDim);
+    const long long rows = (long long)p->batch * p->n_q;
+    if (rows * p->top_k > (1LL << 40) || rows > (1LL << 31))
+        return fail(DSA_E_SHAPE, "batch * n_q = %lld is too large", rows);
+    return DSA_OK;
+}
+
+dsa_status check_ptrs(std::initializer_list<const void*> ptrs, const char* names) {
+    int i = 0;
+    for (const void* q : ptrs) {
+        if (!q) return fail(DSA_E_NULL, "required pointer #%d of (%s) is NULL", i, names);
+        if (misaligned(q))
+            return fail(DSA_E_ALIGN, "pointer #%d of (%s) is not 16-byte aligned", i, names);
+        ++i;
+    }
+    return DSA_OK;
+}
+
+float index_scale(int d) { return (float)std::pow((double)d, -0.5); }
+
+// Rows of each sequence whose scores one forward pass stages at a time.
+int slab_rows(const dsa_problem* p) {
+    const size_t row_bytes = (size_t)p->batch * p->n_k * sizeof(float);
+    size_t r = kScoreSlabBytes / row_bytes;
+    if (r < 1) r = 1;
+    if (r > (size_t)p->n_q) r = (size_t)p->n_q;
+    return (int)r;
+}
+
+size_t attn_ws_bytes(const dsa_problem* p) {
+    int ns, len;
+    dsa::attn_split_plan(p->batch, p->n_q, p->top_k, &ns, &len);
+    if (ns <= 1) return 0;
+    return align_up((size_t)p->batch * p->n_q * ns * kPartFloats * sizeof(float));
+}
+
+struct ForwardLayout {
+    size_t scores, idx, part, total;
+};
+
+ForwardLayout forward_layout(const dsa_problem* p) {
+    ForwardLayout L;
+    L.scores = 0;
+    const size_t sb = align_up((size_t)p->batch * slab_rows(p) * p->n_k * sizeof(float));
+    L.idx = sb;
+    const size_t ib = align_up((size_t)p->batch * p->n_q * p->top_k * sizeof(int32_t));
+    L.part = L.idx + ib;
+    L.total = L.part + attn_ws_bytes(p);
+    return L;
+}
+
+dsa_status hip_fail(hipError_t e, const char* what) {
+    return fail(DSA_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+dsa::AttnArgs attn_args(const dsa_problem* p, const void* Q, const void* K, const void* V,
+                        const int32_t* idx, void* O, float* lse, void* part) {
+    dsa::AttnArgs a{};
+    a.Q = static_cast<const uint16_t*>(Q);
+    a.K = static_cast<const uint16_t*>(K);
+    a.V = static_cast<const uint16_t*>(V);
+    a.idx = idx;
+    a.O = static_cast<uint16_t*>(O);
+    a.lse = lse;
+    a.part = static_cast<float*>(part);
+    a.B = p->batch;
+    a.n_q = p->n_q;
+    a.n_k = p->n_k;
+    a.H = p->n_heads;
+    a.k = p->top_k;
+    dsa::attn_split_plan(p->batch, p->n_q, p->top_k, &a.n_split, &a.split_len);
+    return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+dsa_status dsa_workspace_size(const dsa_problem* p, int32_t op, size_t* bytes) {
+    if (!bytes) return fail(DSA_E_NULL, "bytes is NULL");
+    dsa_status s = check_problem(p);
+    if (s != DSA_OK) return s;
+    switch (op) {
+        case DSA_OP_TOPK: *bytes = 0; break;
+        case DSA_OP_ATTN: *bytes = attn_ws_bytes(p); break;
+        case DSA_OP_FORWARD: *bytes = forward_layout(p).total; break;
+        default: return fail(DSA_E_UNSUPPORTED, "unknown op %d", op);
+    }
+    return ok();
+}
+
+dsa_status dsa_index_scores(const dsa_problem* p, const void* q_idx, const void* k_idx,
+                            int32_t q_begin, int32_t q_end, float* scores, void* stream) {
+    dsa_status s = check_problem(p);
+    if (s != DSA_OK) return s;
+    if ((s = check_ptrs({q_idx, k_idx, scores}, "q_idx, k_idx, scores")) != DSA_OK) return s;
+    if (q_begin < 0 || q_end > p->n_q || q_begin >= q_end)
+        return fail(DSA_E_SHAPE, "need 0 <= q_begin < q_end <= n_q (got %d, %d, n_q=%d)",
+                    q_begin, q_end, p->n_q);
+    dsa::IndexArgs a{};
+    a.q = q_idx;
+    a.k = k_idx;
+    a.scores = scores;
+    a.B = p->batch;
+    a.n_q = p->n_q;
+    a.n_k = p->n_k;
+    a.q_pos0 = p->q_pos0;
+    a.d = p->d_idx;
+    a.dtype = p->idx_dtype;
+    a.q_begin = q_begin;
+    a.q_end = q_end;
+    a.scale = index_scale(p->d_idx);
+    a.write_masked = 1;
+    hipError_t e = dsa::launch_index_scores(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "index_scores launch");
+    return ok();
+}
+
+dsa_status dsa_topk(const dsa_problem* p, const float* scores, int32_t q_begin, int32_t q_end,
+                    int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+    (void)ws;
+    (void)ws_bytes;
+    dsa_status s = check_problem(p);
+    if (s != DSA_OK) return s;
+    if ((s = check_ptrs({scores, idx}, "scores, idx")) != DSA_OK) return s;
+    if (q_begin < 0 || q_end > p->n_q || q_begin >= q_end)
+        return fail(DSA_E_SHAPE, "need 0 <= q_begin < q_end <= n_q (got %d, %d, n_q=%d)",
+                    q_begin, q_end, p->n_q);
+    dsa::TopkArgs a{};
+    a.scores = scores;
+    a.idx = idx;
+    a.B = p->batch;
+    a.rows = q_end - q_begin;
+    a.n_k = p->n_k;
+    a.k = p->top_k;
+    a.pos_begin = (long long)p->q_pos0 + q_begin;
+    a.idx_rows = a.rows;
+    a.idx_row0 = 0;
+    hipError_t e = dsa::launch_topk(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "topk launch");
+    return ok();
+}
+
+dsa_status dsa_sparse_attn(const dsa_problem* p, const void* Q, const void* K, const void* V,
+                           const int32_t* idx, void* O, float* lse, void* ws, size_t ws_bytes,
+                           void* stream) {
+    dsa_status s = check_problem(p);
+    if (s != DSA_OK) return s;
+    if ((s = check_ptrs({Q, K, V, idx, O}, "Q, K, V, idx, O")) != DSA_OK) return s;
+    if (lse && misaligned(lse)) return fail(DSA_E_ALIGN, "lse is not 16-byte aligned");
+    const size_t need = attn_ws_bytes(p);
+    if (need > 0 && (!ws || ws_bytes < need))
+        return fail(DSA_E_WORKSPACE, "attention needs %zu workspace bytes (got %zu)", need,
+                    ws ? ws_bytes : (size_t)0);
+    if (need > 0 && misaligned(ws)) return fail(DSA_E_ALIGN, "workspace is not 16-byte aligned");
+    dsa::AttnArgs a = attn_args(p, Q, K, V, idx, O, lse, ws);
+    hipError_t e = dsa::launch_sparse_attn(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "sparse_attn launch");
+    return ok();
+}
+
+dsa_status dsa_forward(const dsa_problem* p, const void* q_idx, const void* k_idx, const void* Q,
+                       const void* K, const void* V, int32_t* idx_out, void* O, float* lse,
+                       void* ws, size_t ws_bytes, void* stream) {
+    dsa_status s = check_problem(p);
+    if (s != DSA_OK) return s;
+    if ((s = check_ptrs({q_idx, k_idx, Q, K, V, O}, "q_idx, k_idx, Q, K, V, O")) != DSA_OK)
+        return s;
+    if (idx_out && misaligned(idx_out)) return fail(DSA_E_ALIGN, "idx_out is not 16-byte aligned");
+    if (lse && misaligned(lse)) return fail(DSA_E_ALIGN, "lse is not 16-byte aligned");
+    const ForwardLayout L = forward_layout(p);
+    if (!ws || ws_bytes < L.total)
+        return fail(DSA_E_WORKSPACE, "forward needs %zu workspace bytes (got %zu)", L.total,
+                    ws ? ws_bytes : (size_t)0);
+    if (misaligned(ws)) return fail(DSA_E_ALIGN, "workspace is not 16-byte aligned");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    char* w = static_cast<char*>(ws);
+    float* scores = reinterpret_cast<float*>(w + L.scores);
+    int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(w + L.idx);
+    const int R = slab_rows(p);
+
+    dsa::IndexArgs ia{};
+    ia.q = q_idx;
+    ia.k = k_idx;
+    ia.scores = scores;
+    ia.B = p->batch;
+    ia.n_q = p->n_q;
+    ia.n_k = p->n_k;
+    ia.q_pos0 = p->q_pos0;
+    ia.d = p->d_idx;
+    ia.dtype = p->idx_dtype;
+    ia.scale = index_scale(p->d_idx);
+    ia.write_masked = 0;  // the selection never reads past a query's position
+    dsa::TopkArgs ta{};
+    ta.scores = scores;
+    ta.idx = idx;
+    ta.B = p->batch;
+    ta.n_k = p->n_k;
+    ta.k = p->top_k;
+    ta.idx_rows = p->n_q;
+    for (int r0 = 0; r0 < p->n_q; r0 += R) {
+        const int r1 = r0 + R < p->n_q ? r0 + R : p->n_q;
+        ia.q_begin = r0;
+        ia.q_end = r1;
+        hipError_t e = dsa::launch_index_scores(ia, st);
+        if (e != hipSuccess) return hip_fail(e, "index_scores launch");
+        ta.rows = r1 - r0;
+        ta.pos_begin = (long long)p->q_pos0 + r0;
+        ta.idx_row0 = r0;
+        e = dsa::launch_topk(ta, st);
+        if (e != hipSuccess) return hip_fail(e, "topk launch");
+    }
+    dsa::AttnArgs aa = attn_args(p, Q, K, V, idx, O, lse, w + L.part);
+    hipError_t e = dsa::launch_sparse_attn(aa, st);
+    if (e != hipSuccess) return hip_fail(e, "sparse_attn launch");
+    return ok();
+}
+
+const char* dsa_status_str(int32_t status) {
+    switch (status) {
+        case DSA_OK: return "DSA_OK";
+        case DSA_E_NULL: return "DSA_E_NULL";
+        case DSA_E_SHAPE: return "DSA_E_SHAPE";
+        case DSA_E_UNSUPPORTED: return "DSA_E_UNSUPPORTED";
+        case DSA_E_ALIGN: return "DSA_E_ALIGN";
+        case DSA_E_WORKSPACE: return "DSA_E_WORKSPACE";
+        case DSA_E_HIP: return "DSA_E_HIP";
+        default: return "DSA_E_UNKNOWN";
+    }
+}
+
+const char* dsa_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

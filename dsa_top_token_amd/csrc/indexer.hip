@@ -1,0 +1,209 @@
+// Lightning-indexer scores on gfx950 matrix cores.
+//
+// DeepSeek-V3.2 DSA page (kwkr.cn/news/60693), section 3.2: the score of a
+// query/key pair is relu(q_idx . k_idx * dim^-0.5) over a small indexer
+// dimension, computed as an FP8 matrix product (section 4.1); bf16 inputs are
+// the page's fallback precision (section 7.3).
+//
+// Each wave owns a 16-query x 64-key block: four 16x16 output tiles, each the
+// sum of d/128 v_mfma_scale_f32_16x16x128_f8f6f4 (+ (d%128)/32
+// v_mfma_f32_16x16x32_fp8) or d/32 v_mfma_f32_16x16x32_bf16 products. The
+// fp32 accumulator is scaled by fl32(d^-0.5) once, passed through ReLU and
+// masked past the query's position in the epilogue.
+//
+// Contraction order: both operands of an MFMA place the same contraction
+// index k in the same (lane group, register) slot, so any fixed assignment of
+// row bytes to slots yields the full dot product. Each lane therefore loads
+// contiguous bytes of its row: [128c + 32g, +32) for fp8 chunk c, lane group
+// g = lane / 16. For the integer-valued inputs the sum is exact in fp32, so
+// the result does not depend on the order.
+#include "dsa_internal.h"
+
+namespace dsa {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kE8M0One = 127;  // E8M0 block scale encoding 2^0
+
+template <int DT, int D> struct Frag;
+
+// fp8 e4m3fn row fragment: NB chunks of 128 bytes (32 per lane) and NS
+// chunks of 32 bytes (8 per lane).
+template <int D> struct Frag<0, D> {
+    static constexpr int NB = D / 128, NS = (D % 128) / 32;
+    i32x8 big[NB > 0 ? NB : 1];
+    long small[NS > 0 ? NS : 1];
+    __device__ __forceinline__ void load(const uint8_t* row, int g) {
+#pragma unroll
+        for (int c = 0; c < NB; ++c) {
+            const i32x4* p = reinterpret_cast<const i32x4*>(row + 128 * c + 32 * g);
+            i32x4 lo = p[0], hi = p[1];
+            big[c] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
+#pragma unroll
+        for (int c = 0; c < NS; ++c)
+            small[c] = *reinterpret_cast<const long*>(row + 128 * NB + 32 * c + 8 * g);
+    }
+};
+
+// bf16 row fragment: D/32 chunks of 32 elements (8 per lane).
+template <int D> struct Frag<1, D> {
+    static constexpr int NC = D / 32;
+    bf16x8 v[NC];
+    __device__ __forceinline__ void load(const uint8_t* row, int g) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+            v[c] = *reinterpret_cast<const bf16x8*>(row + 64 * c + 16 * g);
+    }
+};
+
+template <int D>
+__device__ __forceinline__ f32x4 tile_dot(const Frag<0, D>& a, const Frag<0, D>& b) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < Frag<0, D>::NB; ++c)
+        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            a.big[c], b.big[c], acc, 0, 0, 0, kE8M0One, 0, kE8M0One);
+#pragma unroll
+    for (int c = 0; c < Frag<0, D>::NS; ++c)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a.small[c], b.small[c], acc, 0, 0, 0);
+    return acc;
+}
+
+template <int D>
+__device__ __forceinline__ f32x4 tile_dot(const Frag<1, D>& a, const Frag<1, D>& b) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < Frag<1, D>::NC; ++c)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v[c], b.v[c], acc, 0, 0, 0);
+    return acc;
+}
+
+// relu(x * scale) with +0.0 for every non-positive (or NaN) product.
+__device__ __forceinline__ float relu_scaled(float x, float scale) {
+    const float s = x * scale;
+    return s > 0.0f ? s : 0.0f;
+}
+
+// Workgroup = 4 waves arranged WM (queries) x WN (keys); each wave computes
+// 16 queries x 64 keys per iteration and ITER iterations.
+template <int DT, int D, int WM, int WN, int ITER>
+__global__ __launch_bounds__(256) void index_scores_kernel(IndexArgs a) {
+    constexpr int ES = DT == 0 ? 1 : 2;
+    constexpr int RB = D * ES;  // bytes per indexer row
+    constexpr int QB = 16 * WM;
+    constexpr int KB = 64 * WN * ITER;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave % WM, wn = wave / WM;
+    const int m = lane & 15, g = lane >> 4;
+    const int rows = a.q_end - a.q_begin;
+    const int n_kb = (a.n_k + KB - 1) / KB;
+    const int n_qb = (rows + QB - 1) / QB;
+    unsigned bid = blockIdx.x;
+    const int kb = bid % n_kb;
+    bid /= n_kb;
+    const int qb = bid % n_qb;
+    const int b = bid / n_qb;
+    const int wrow0 = qb * QB + wm * 16;
+    if (wrow0 >= rows) return;
+    const long long pos0 = (long long)a.q_pos0 + a.q_begin;
+    const long long wmaxpos = pos0 + min(wrow0 + 16, rows) - 1;
+    const float ninf = -__builtin_inff();
+    float* const out = a.scores + (size_t)b * rows * (size_t)a.n_k;
+
+    Frag<DT, D> fa;
+    {
+        const int ra = min(wrow0 + m, rows - 1);
+        fa.load(static_cast<const uint8_t*>(a.q) +
+                    ((size_t)b * a.n_q + a.q_begin + ra) * RB, g);
+    }
+    const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + (size_t)b * a.n_k * RB;
+
+    for (int it = 0; it < ITER; ++it) {
+        const int k0 = kb * KB + (it * WN + wn) * 64;
+        if (k0 >= a.n_k) break;
+        if (k0 > wmaxpos) {  // every key of the block lies past every query
+            if (a.write_masked) {
+                for (int e = lane; e < 16 * 64; e += 64) {
+                    const int row = wrow0 + (e >> 6), key = k0 + (e & 63);
+                    if (row < rows && key < a.n_k) out[(size_t)row * a.n_k + key] = ninf;
+                }
+            }
+            continue;
+        }
+        f32x4 acc[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int kr = min(k0 + 16 * t + m, a.n_k - 1);
+            Frag<DT, D> fb;
+            fb.load(kbase + (size_t)kr * RB, g);
+            acc[t] = tile_dot<D>(fa, fb);
+        }
+        // Output tile layout: lane holds rows 4g + r, key column m.
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = wrow0 + 4 * g + r;
+            if (row >= rows) continue;
+            const long long pos = pos0 + row;
+            float* orow = out + (size_t)row * a.n_k;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int key = k0 + 16 * t + m;
+                if (key >= a.n_k) continue;
+                if (key > pos) {
+                    if (a.write_masked) orow[key] = ninf;
+                } else {
+                    orow[key] = relu_scaled(acc[t][r], a.scale);
+                }
+            }
+        }
+    }
+}
+
+template <int DT, int D>
+hipError_t launch_dt_d(const IndexArgs& a, hipStream_t s) {
+    const int rows = a.q_end - a.q_begin;
+    if (rows <= 16) {
+        // Few queries per sequence (decode): the 4 waves split the keys.
+        constexpr int QB = 16, KB = 256;
+        const long long nb = (long long)a.B * ((rows + QB - 1) / QB) * ((a.n_k + KB - 1) / KB);
+        if (nb > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL((index_scores_kernel<DT, D, 1, 4, 1>), dim3((unsigned)nb), dim3(256),
+                           0, s, a);
+    } else {
+        constexpr int QB = 64, KB = 256;
+        const long long nb = (long long)a.B * ((rows + QB - 1) / QB) * ((a.n_k + KB - 1) / KB);
+        if (nb > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL((index_scores_kernel<DT, D, 4, 1, 4>), dim3((unsigned)nb), dim3(256),
+                           0, s, a);
+    }
+    return hipGetLastError();
+}
+
+template <int DT>
+hipError_t launch_dt(const IndexArgs& a, hipStream_t s) {
+    switch (a.d) {
+        case 32: return launch_dt_d<DT, 32>(a, s);
+        case 64: return launch_dt_d<DT, 64>(a, s);
+        case 96: return launch_dt_d<DT, 96>(a, s);
+        case 128: return launch_dt_d<DT, 128>(a, s);
+        case 160: return launch_dt_d<DT, 160>(a, s);
+        case 192: return launch_dt_d<DT, 192>(a, s);
+        case 224: return launch_dt_d<DT, 224>(a, s);
+        case 256: return launch_dt_d<DT, 256>(a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_index_scores(const IndexArgs& a, hipStream_t s) {
+    if (a.q_end <= a.q_begin || a.B <= 0) return hipSuccess;
+    return a.dtype == 0 ? launch_dt<0>(a, s) : launch_dt<1>(a, s);
+}
+
+}  // namespace dsa

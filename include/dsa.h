@@ -1,0 +1,137 @@
+/*
+ * dsa.h - C ABI of the MI355X (gfx950) DSA library: lightning indexer ->
+ * top-k selection -> sparse MQA attention.
+ *
+ * The method is the one on the DeepSeek-V3.2 DSA page (kwkr.cn/news/60693):
+ *   section 3.2  indexer score relu(q_idx . k_idx * d_idx^-0.5) per query/key
+ *   section 3.3  each query keeps its top_k highest-scoring keys; ordinary
+ *                softmax attention then runs over those keys only
+ *   section 4.1  FP8 indexer inputs (BF16 also accepted, section 7.3), a
+ *                comparison-based selection, BF16 attention
+ *   section 4.2  every query head shares one K/V set (MQA)
+ *   section 4.3  the whole chain as one call (dsa_forward)
+ *   section 7.2  top_k / index_dim / precision are per-workload parameters
+ *
+ * Conventions for every call:
+ *   - Tensors are caller-owned DEVICE memory, row-major and contiguous, each
+ *     pointer 16-byte aligned. The library never allocates, frees or keeps a
+ *     pointer after the call returns; all work is enqueued on `stream` (a
+ *     hipStream_t; NULL is the default stream) and is complete when that
+ *     stream is synchronised.
+ *   - Query i (0-based) of a sequence sits at position pos(i) = q_pos0 + i and
+ *     sees keys 0..pos(i) (itself included). Prefill is q_pos0 = 0 with
+ *     n_q = n_k; one decode token is n_q = 1, q_pos0 = n_k - 1.
+ *   - All arguments are validated on the host before anything is enqueued; on
+ *     any error nothing is enqueued and a negative dsa_status is returned,
+ *     with a sentence in dsa_last_error(). A failed HIP launch returns
+ *     DSA_E_HIP. Device faults surface at the caller's synchronisation.
+ *   - No call blocks the host or synchronises the stream.
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DSA_OK = 0,
+    DSA_E_NULL = -1,        /* a required pointer is NULL */
+    DSA_E_SHAPE = -2,       /* sizes out of range or inconsistent */
+    DSA_E_UNSUPPORTED = -3, /* a valid problem this library does not handle */
+    DSA_E_ALIGN = -4,       /* a pointer is not 16-byte aligned */
+    DSA_E_WORKSPACE = -5,   /* workspace missing or smaller than required */
+    DSA_E_HIP = -6          /* the HIP runtime reported an error */
+} dsa_status;
+
+/* Element type of q_idx / k_idx (the "precision" parameter). */
+typedef enum {
+    DSA_IDX_FP8_E4M3FN = 0, /* OCP float8 e4m3fn, 1 byte */
+    DSA_IDX_BF16 = 1        /* bfloat16, 2 bytes */
+} dsa_idx_dtype;
+
+/* Which call a workspace size is asked for. */
+typedef enum { DSA_OP_TOPK = 1, DSA_OP_ATTN = 2, DSA_OP_FORWARD = 3 } dsa_op;
+
+/* Problem description shared by every call.
+ *   batch     B >= 1 independent sequences
+ *   n_q       queries per sequence, 1 <= n_q, q_pos0 + n_q <= n_k
+ *   n_k       keys per sequence, 1 <= n_k <= 4194304
+ *   q_pos0    position of query 0 (>= 0)
+ *   d_idx     indexer dimension ("index_dim"): a multiple of 32, 32..256
+ *   idx_dtype a dsa_idx_dtype
+ *   top_k     keys kept per query, 1..4096
+ *   n_heads   H query heads sharing one K/V row set, 1..16
+ *   head_dim  must be 128 */
+typedef struct {
+    int32_t batch, n_q, n_k, q_pos0;
+    int32_t d_idx, idx_dtype;
+    int32_t top_k;
+    int32_t n_heads, head_dim;
+} dsa_problem;
+
+/* Bytes of device workspace `op` needs for problem `p` (written to *bytes;
+ * 0 means no workspace). Pure host function. */
+dsa_status dsa_workspace_size(const dsa_problem* p, int32_t op, size_t* bytes);
+
+/* Indexer scores (DSA page, section 3.2) for query rows [q_begin, q_end) of
+ * every sequence:
+ *   scores[b][r][j] = relu(fl32(q_idx[b][q_begin+r] . k_idx[b][j]) * s),
+ *   s = dim^-0.5 rounded to float32, for j <= pos(q_begin+r);
+ *   scores[b][r][j] = -inf for j > pos(q_begin+r).
+ * q_idx [B][n_q][d_idx], k_idx [B][n_k][d_idx] in idx_dtype;
+ * scores float32 [B][q_end-q_begin][n_k]. The dot product is accumulated in
+ * float32 on matrix cores, exact whenever every partial sum is (for example
+ * for the small-integer inputs of the benchmarks). Needs 0 <= q_begin < q_end
+ * <= n_q. */
+dsa_status dsa_index_scores(const dsa_problem* p, const void* q_idx,
+                            const void* k_idx, int32_t q_begin, int32_t q_end,
+                            float* scores, void* stream);
+
+/* Top-k selection (DSA page, section 3.3) over score rows produced as above:
+ * row r of sequence b belongs to query q_begin + r and its candidates are keys
+ * 0..pos(q_begin+r). Keeps the min(top_k, pos+1) candidates ranked first by
+ * (score descending, key index ascending) - ties go to the lower index - and
+ * writes them in ascending key order, padding the row with -1:
+ * idx int32 [B][q_end-q_begin][top_k]. Scores must be >= +0.0 or -inf (as the
+ * indexer writes them); ranking compares float32 bit patterns. */
+dsa_status dsa_topk(const dsa_problem* p, const float* scores, int32_t q_begin,
+                    int32_t q_end, int32_t* idx, void* ws, size_t ws_bytes,
+                    void* stream);
+
+/* Sparse MQA attention (DSA page, sections 3.3 and 4.2) for all n_q queries:
+ *   O[b][i][h] = sum_{j in sel} softmax_j(Q[b][i][h] . K[b][j] / sqrt(128)) V[b][j]
+ * where sel is the set of entries of idx[b][i][0..top_k) inside [0, n_k)
+ * (entries outside, such as the -1 padding, are ignored; an empty set gives
+ * O = 0 and lse = -inf). Q [B][n_q][H][128], K, V [B][n_k][128] bfloat16;
+ * idx int32 [B][n_q][top_k]; O bfloat16 [B][n_q][H][128]; lse (optional,
+ * NULL to skip) float32 [B][n_q][H], natural-log sum of exp of the scaled
+ * scores. Accumulation is float32; probabilities enter the PV product as
+ * bfloat16. */
+dsa_status dsa_sparse_attn(const dsa_problem* p, const void* Q, const void* K,
+                           const void* V, const int32_t* idx, void* O,
+                           float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* The whole chain (DSA page, section 4.3): indexer scores, top-k, sparse
+ * attention, with the same definitions and layouts as the three calls above.
+ * idx_out (optional) receives the selection [B][n_q][top_k]; lse optional.
+ * Intermediate scores live in the workspace. */
+dsa_status dsa_forward(const dsa_problem* p, const void* q_idx,
+                       const void* k_idx, const void* Q, const void* K,
+                       const void* V, int32_t* idx_out, void* O, float* lse,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* Static name of a status code. */
+const char* dsa_status_str(int32_t status);
+
+/* Detail of the last error reported on the calling thread ("" if none). */
+const char* dsa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H */

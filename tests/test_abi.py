@@ -1,0 +1,124 @@
+"""Host-side checks of the C ABI: the library loads on a machine without a
+GPU, exports every function include/dsa.h declares, sizes workspaces, and
+rejects bad arguments before it touches the HIP runtime."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dsa_top_token_amd as dsa
+from dsa_top_token_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("dsa_index_scores", "dsa_topk", "dsa_sparse_attn", "dsa_forward",
+              "dsa_workspace_size", "dsa_status_str", "dsa_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = dsa.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(declared_functions()) <= set(dsa.EXPORTS)
+
+
+def test_status_strings():
+    lib = dsa.load()
+    for code, name in dsa.STATUS.items():
+        assert lib.dsa_status_str(code).decode() == name
+
+
+def prob(**kw):
+    base = dict(batch=1, n_q=64, n_k=64, q_pos0=0, d_idx=128, idx_dtype=0, top_k=8,
+                n_heads=8, head_dim=128)
+    base.update(kw)
+    return dsa.Problem(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=0), -2), (dict(n_q=0), -2), (dict(n_k=0), -2), (dict(q_pos0=-1), -2),
+    (dict(q_pos0=1), -2), (dict(n_q=65), -2), (dict(n_k=1 << 23, n_q=1, q_pos0=0), -2),
+    (dict(d_idx=0), -2), (dict(d_idx=100), -3), (dict(d_idx=288), -3),
+    (dict(idx_dtype=2), -3), (dict(top_k=0), -2), (dict(top_k=4097), -3),
+    (dict(n_heads=0), -2), (dict(n_heads=17), -3), (dict(head_dim=64), -3),
+])
+def test_bad_problems_are_rejected(kw, status):
+    n = ctypes.c_size_t(0)
+    p = prob(**kw)
+    rc = dsa.load().dsa_workspace_size(ctypes.byref(p), dsa.OP_FORWARD, ctypes.byref(n))
+    assert rc == status, dsa.load().dsa_last_error()
+    assert dsa.load().dsa_last_error().decode() != ""
+
+
+FAKE = ctypes.c_void_p(0x100000)       # never dereferenced: validation fails first
+ODD = ctypes.c_void_p(0x100008)        # 8-byte aligned only
+
+
+def test_null_and_misaligned_pointers():
+    lib = dsa.load()
+    p = prob()
+    P = ctypes.byref(p)
+    assert lib.dsa_index_scores(None, FAKE, FAKE, 0, 1, FAKE, None) == -1
+    assert lib.dsa_index_scores(P, None, FAKE, 0, 1, FAKE, None) == -1
+    assert lib.dsa_index_scores(P, FAKE, FAKE, 0, 1, None, None) == -1
+    assert lib.dsa_index_scores(P, ODD, FAKE, 0, 1, FAKE, None) == -4
+    assert lib.dsa_index_scores(P, FAKE, FAKE, 1, 1, FAKE, None) == -2
+    assert lib.dsa_index_scores(P, FAKE, FAKE, 0, 65, FAKE, None) == -2
+    assert lib.dsa_topk(P, None, 0, 1, FAKE, None, 0, None) == -1
+    assert lib.dsa_topk(P, FAKE, 0, 1, ODD, None, 0, None) == -4
+    assert lib.dsa_topk(P, FAKE, -1, 1, FAKE, None, 0, None) == -2
+    assert lib.dsa_sparse_attn(P, FAKE, FAKE, None, FAKE, FAKE, None, None, 0, None) == -1
+    assert lib.dsa_sparse_attn(P, FAKE, FAKE, FAKE, FAKE, FAKE, ODD, None, 0, None) == -4
+    # forward needs its workspace
+    assert lib.dsa_forward(P, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, None, 0,
+                           None) == -5
+    need = dsa.workspace_size(p, dsa.OP_FORWARD)
+    assert lib.dsa_forward(P, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, FAKE,
+                           need - 1, None) == -5
+    assert lib.dsa_forward(P, FAKE, FAKE, FAKE, FAKE, FAKE, ODD, FAKE, None, FAKE,
+                           need, None) == -4
+
+
+def test_attention_workspace_only_when_split():
+    # decode-sized batches split each query's keys; prefill does not
+    dec = synth.WORKLOADS["decode_128k_clustered"]
+    p = dsa.make_problem(dec.batch, dec.n_q, dec.n_k, dec.q_pos0, dec.d_idx, dec.idx_dtype,
+                         dec.top_k, dec.n_heads)
+    assert dsa.workspace_size(p, dsa.OP_ATTN) > 0
+    pre = synth.WORKLOADS["prefill_64k"]
+    p = dsa.make_problem(pre.batch, pre.n_q, pre.n_k, pre.q_pos0, pre.d_idx, pre.idx_dtype,
+                         pre.top_k, pre.n_heads)
+    assert dsa.workspace_size(p, dsa.OP_ATTN) == 0
+    assert dsa.workspace_size(p, dsa.OP_TOPK) == 0
+
+
+@pytest.mark.parametrize("name", sorted(synth.WORKLOADS))
+def test_forward_workspace_fits(name):
+    w = synth.WORKLOADS[name]
+    p = dsa.make_problem(w.batch, w.n_q, w.n_k, w.q_pos0, w.d_idx, w.idx_dtype, w.top_k,
+                         w.n_heads)
+    n = dsa.workspace_size(p, dsa.OP_FORWARD)
+    # scores slab (<= 2 GiB) + index lists + attention partials
+    idx_bytes = w.batch * w.n_q * w.top_k * 4
+    assert idx_bytes <= n <= (2 << 30) + idx_bytes + (64 << 20)
+
+
+def test_product_path_has_no_oracle_or_cpu_fallback():
+    # the package never imports the oracle and has no CPU compute path
+    pkg = os.path.join(ROOT, "dsa_top_token_amd")
+    for f in os.listdir(pkg):
+        if f.endswith(".py"):
+            src = open(os.path.join(pkg, f)).read()
+            assert "import oracle" not in src and "from oracle" not in src, f

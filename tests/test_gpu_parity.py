@@ -1,0 +1,254 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Indexer scores and top-k index lists must match bit for bit; attention
+outputs must stay within max-abs 2e-2 and relative-L2 1e-2 of the oracle's
+fp32 result (lse within 1e-3). Small cases are compared element by element;
+full-size workloads in the benchmark's launch configuration are compared on
+every query the oracle can afford (all decode queries, sampled prefill rows)
+plus properties checked on every row.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import dsa_top_token_amd as dsa
+from dsa_top_token_amd import synth
+from dsa_top_token_amd.synth import Workload
+
+pytestmark = pytest.mark.gpu
+
+ATOL, RTOL_L2, LSE_TOL = 2e-2, 1e-2, 1e-3
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def bits(x):
+    return np.asarray(x, np.float32).view(np.uint32)
+
+
+def assert_attn_close(O_gpu, O_ref, lse_gpu=None, lse_ref=None, what=""):
+    o = O_gpu.float().cpu().numpy()
+    d = o - O_ref
+    max_abs = float(np.max(np.abs(d))) if d.size else 0.0
+    rel = float(np.linalg.norm(d) / max(np.linalg.norm(O_ref), 1e-30))
+    assert max_abs <= ATOL and rel <= RTOL_L2, "%s max_abs=%.3g rel_l2=%.3g" % (what, max_abs, rel)
+    if lse_gpu is not None:
+        l = lse_gpu.cpu().numpy()
+        fin = np.isfinite(lse_ref)
+        assert np.array_equal(fin, np.isfinite(l)), what
+        if fin.any():
+            err = float(np.max(np.abs(l[fin] - lse_ref[fin])))
+            assert err <= LSE_TOL, "%s lse err %.3g" % (what, err)
+
+
+def to_dev(x):
+    return {k: v.to("cuda") for k, v in x.items()}
+
+
+SMALL = [
+    synth.WORKLOADS["prefill_1k"],
+    Workload("prefill_bf16_d160_ragged", "prefill", 1, 777, 777, 0, 160, "bf16", 100, 16),
+    Workload("decode_fp8_d96_ragged", "decode", 5, 1, 3001, 3000, 96, "fp8", 1024, 16),
+    Workload("decode_clustered_small", "decode", 4, 1, 5000, 4999, 128, "fp8", 2048, 16,
+             clustered=True),
+    Workload("chunked_prefill", "prefill", 2, 50, 300, 250, 64, "fp8", 37, 3),
+    Workload("single_key", "decode", 1, 1, 1, 0, 32, "fp8", 1, 1),
+    Workload("topk_above_len_bf16_d256", "prefill", 2, 70, 70, 0, 256, "bf16", 4096, 4),
+    Workload("prefill_d192_k1", "prefill", 1, 130, 130, 0, 192, "fp8", 1, 5),
+]
+
+
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
+def test_index_scores_bit_exact(gpu_lib, w):
+    say("index_scores %s" % w.name)
+    x = synth.make_inputs(w, seed=1, parts=("q_idx", "k_idx"))
+    ref = oracle.index_scores(x["q_idx"], x["k_idx"], w.q_pos0)
+    got = dsa.index_scores(x["q_idx"].cuda(), x["k_idx"].cuda(), w.q_pos0).cpu().numpy()
+    assert np.array_equal(bits(got), bits(ref))
+    if w.n_q > 3:  # a row slab in the middle
+        a, b = w.n_q // 3, w.n_q // 3 + max(1, w.n_q // 4)
+        got = dsa.index_scores(x["q_idx"].cuda(), x["k_idx"].cuda(), w.q_pos0, a, b)
+        assert np.array_equal(bits(got.cpu().numpy()), bits(ref[:, a:b]))
+
+
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
+def test_topk_bit_exact_on_oracle_scores(gpu_lib, w):
+    say("topk %s" % w.name)
+    x = synth.make_inputs(w, seed=2, parts=("q_idx", "k_idx"))
+    s = oracle.index_scores(x["q_idx"], x["k_idx"], w.q_pos0)
+    ref = oracle.topk(s, w.q_pos0, w.top_k)
+    got = dsa.topk(torch.from_numpy(s).cuda(), w.q_pos0, w.top_k).cpu().numpy()
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("n_k", [1000, 4097, 9999])
+@pytest.mark.parametrize("levels", [1, 3, 40, 0])
+@pytest.mark.parametrize("k", [1, 7, 600])
+def test_topk_ties_and_ragged_rows(gpu_lib, n_k, levels, k):
+    say("topk ties n_k=%d levels=%d k=%d" % (n_k, levels, k))
+    g = np.random.default_rng(n_k * 7 + levels * 3 + k)
+    rows = 6
+    if levels:
+        s = (g.integers(0, levels, (2, rows, n_k)) * 0.375).astype(np.float32)
+    else:
+        s = np.maximum(g.standard_normal((2, rows, n_k)), 0).astype(np.float32)
+    pos_begin = n_k - rows - 3 if n_k > rows + 3 else 0
+    for r in range(rows):
+        s[:, r, pos_begin + r + 1:] = -np.inf
+    ref = oracle.topk(s, pos_begin, k)
+    got = dsa.topk(torch.from_numpy(s).cuda(), pos_begin, k, n_q=rows, q_begin=0)
+    # dsa.topk takes q_pos0 of query 0; rows are queries 0..rows-1
+    assert np.array_equal(got.cpu().numpy(), ref)
+
+
+def random_selection(g, B, n_q, n_k, k, q_pos0, holes=True):
+    idx = np.full((B, n_q, k), -1, np.int32)
+    for b in range(B):
+        for i in range(n_q):
+            n = min(k, q_pos0 + i + 1)
+            sel = np.sort(g.choice(q_pos0 + i + 1, n, replace=False))
+            idx[b, i, :n] = sel
+            if holes and n > 2:
+                idx[b, i, g.integers(0, n)] = -1
+                idx[b, i, g.integers(0, n)] = n_k + 5  # out of range: ignored
+    return idx
+
+
+@pytest.mark.parametrize("B,n_q,n_k,H,k,q_pos0", [
+    (1, 300, 300, 8, 64, 0),       # one wave per query
+    (2, 40, 2000, 16, 512, 1960),  # few queries: split keys + combine
+    (3, 1, 6000, 16, 2048, 5999),  # decode-like
+    (1, 17, 17, 1, 4096, 0),       # k far above the row length
+    (2, 5, 900, 13, 96, 895),
+])
+def test_sparse_attn_vs_oracle(gpu_lib, B, n_q, n_k, H, k, q_pos0):
+    say("sparse_attn B=%d n_q=%d n_k=%d H=%d k=%d" % (B, n_q, n_k, H, k))
+    w = Workload("attn", "prefill", B, n_q, n_k, q_pos0, 32, "fp8", k, H)
+    x = synth.make_inputs(w, seed=3, parts=("Q", "K", "V"))
+    idx = random_selection(np.random.default_rng(B * n_k + k), B, n_q, n_k, k, q_pos0)
+    O_ref, lse_ref = oracle.sparse_attn(x["Q"], x["K"], x["V"], idx)
+    O, lse = dsa.sparse_attn(x["Q"].cuda(), x["K"].cuda(), x["V"].cuda(),
+                             torch.from_numpy(idx).cuda(), q_pos0=q_pos0)
+    assert_attn_close(O, O_ref, lse, lse_ref, "attn")
+
+
+def test_sparse_attn_empty_selection(gpu_lib):
+    w = Workload("attn", "decode", 2, 1, 64, 63, 32, "fp8", 32, 4)
+    x = synth.make_inputs(w, seed=4, parts=("Q", "K", "V"))
+    idx = np.full((2, 1, 32), -1, np.int32)
+    idx[1, 0, :3] = [5, 9, 60]
+    O_ref, lse_ref = oracle.sparse_attn(x["Q"], x["K"], x["V"], idx)
+    O, lse = dsa.sparse_attn(x["Q"].cuda(), x["K"].cuda(), x["V"].cuda(),
+                             torch.from_numpy(idx).cuda())
+    assert torch.all(O[0].float() == 0)
+    assert torch.all(torch.isneginf(lse[0]))
+    assert_attn_close(O, O_ref, lse, lse_ref, "empty")
+
+
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
+def test_forward_small_vs_oracle(gpu_lib, w):
+    say("forward %s" % w.name)
+    x = synth.make_inputs(w, seed=5)
+    idx_ref, O_ref, lse_ref = oracle.forward(x["q_idx"], x["k_idx"], x["Q"], x["K"], x["V"],
+                                             w.q_pos0, w.top_k)
+    d = to_dev(x)
+    idx, O, lse = dsa.forward(d["q_idx"], d["k_idx"], d["Q"], d["K"], d["V"], w.q_pos0,
+                              w.top_k)
+    assert np.array_equal(idx.cpu().numpy(), idx_ref)
+    assert_attn_close(O, O_ref, lse, lse_ref, w.name)
+    # deterministic: a second call gives identical bits
+    idx2, O2, lse2 = dsa.forward(d["q_idx"], d["k_idx"], d["Q"], d["K"], d["V"], w.q_pos0,
+                                 w.top_k)
+    assert torch.equal(idx, idx2) and torch.equal(O.view(torch.int16), O2.view(torch.int16))
+    assert torch.equal(lse, lse2)
+
+
+def test_all_zero_query_selects_first_keys(gpu_lib):
+    w = Workload("zeros", "prefill", 1, 600, 600, 0, 128, "fp8", 64, 2)
+    x = synth.make_inputs(w, seed=6)
+    x["q_idx"] = torch.zeros_like(x["q_idx"])
+    d = to_dev(x)
+    idx, _, _ = dsa.forward(d["q_idx"], d["k_idx"], d["Q"], d["K"], d["V"], 0, 64)
+    idx = idx.cpu().numpy()[0]
+    for i in range(600):
+        m = min(64, i + 1)
+        assert list(idx[i, :m]) == list(range(m)) and np.all(idx[i, m:] == -1)
+
+
+def check_selection_properties(idx, q_pos0, k):
+    """On the GPU, for every row: ascending, inside [0, pos], min(k, pos+1)
+    entries, -1 padding."""
+    B, n_q, _ = idx.shape
+    pos = q_pos0 + torch.arange(n_q, device=idx.device)[None, :, None]
+    n_sel = torch.clamp(pos + 1, max=k)
+    slot = torch.arange(k, device=idx.device)[None, None, :]
+    valid = slot < n_sel
+    assert torch.all(torch.where(valid, idx >= 0, idx == -1))
+    assert torch.all(torch.where(valid, idx <= pos, True))
+    inc = idx[:, :, 1:] > idx[:, :, :-1]
+    assert torch.all(torch.where(valid[:, :, 1:], inc, True))
+
+
+def run_full(w, sample_rows, gen_device="cpu"):
+    say("full-size %s: generating inputs" % w.name)
+    x = synth.make_inputs(w, seed=0, device=gen_device)
+    d = to_dev(x) if gen_device == "cpu" else x
+    say("full-size %s: GPU forward" % w.name)
+    idx, O, lse = dsa.forward(d["q_idx"], d["k_idx"], d["Q"], d["K"], d["V"], w.q_pos0,
+                              w.top_k)
+    torch.cuda.synchronize()
+    check_selection_properties(idx, w.q_pos0, w.top_k)
+    xc = x if gen_device == "cpu" else {k: v.cpu() for k, v in x.items()}
+    for (a, b) in sample_rows:
+        say("full-size %s: oracle rows [%d, %d)" % (w.name, a, b))
+        idx_ref, O_ref, lse_ref = oracle.forward(xc["q_idx"], xc["k_idx"], xc["Q"], xc["K"],
+                                                 xc["V"], w.q_pos0, w.top_k, a, b)
+        assert np.array_equal(idx[:, a:b].cpu().numpy(), idx_ref), (a, b)
+        assert_attn_close(O[:, a:b], O_ref, lse[:, a:b], lse_ref, "%s rows %d-%d" % (w.name, a, b))
+    return x, d
+
+
+def test_full_decode_32k(gpu_lib):
+    w = synth.WORKLOADS["decode_32k"]
+    run_full(w, [(0, 1)])
+
+
+def test_full_decode_128k_clustered(gpu_lib):
+    w = synth.WORKLOADS["decode_128k_clustered"]
+    run_full(w, [(0, 1)])
+
+
+def prefill_samples(L, k):
+    g = np.random.default_rng(L)
+    rows = [(0, 3), (k - 3, k + 3), (2 * k - 1, 2 * k + 1), (L - 4, L)]
+    for r in sorted(g.integers(2 * k + 1, L - 4, 6)):
+        rows.append((int(r), int(r) + 2))
+    return rows
+
+
+def test_full_prefill_64k(gpu_lib):
+    w = synth.WORKLOADS["prefill_64k"]
+    x, d = run_full(w, prefill_samples(w.n_q, w.top_k))
+    # indexer scores of sampled row slabs at full width, bit for bit
+    for (a, b) in [(5, 9), (40000, 40006), (w.n_q - 3, w.n_q)]:
+        got = dsa.index_scores(d["q_idx"], d["k_idx"], 0, a, b).cpu().numpy()
+        ref = oracle.index_scores(x["q_idx"], x["k_idx"], 0, a, b)
+        assert np.array_equal(bits(got), bits(ref)), (a, b)
+
+
+def test_full_prefill_128k_bf16(gpu_lib):
+    w = synth.WORKLOADS["prefill_128k"]
+    x, d = run_full(w, prefill_samples(w.n_q, w.top_k))
+    for (a, b) in [(0, 4), (99999, 100003), (w.n_q - 2, w.n_q)]:
+        got = dsa.index_scores(d["q_idx"], d["k_idx"], 0, a, b).cpu().numpy()
+        ref = oracle.index_scores(x["q_idx"], x["k_idx"], 0, a, b)
+        assert np.array_equal(bits(got), bits(ref)), (a, b)
+
+
+def test_full_prefill_batch2_many_slabs(gpu_lib):
+    # two sequences, several score slabs per forward call
+    w = Workload("prefill_b2_40k", "prefill", 2, 40000, 40000, 0, 128, "fp8", 1024, 16)
+    run_full(w, [(0, 2), (1022, 1026), (6550, 6560), (13107, 13110), (39998, 40000)])
