@@ -1,0 +1,251 @@
+#!/usr/bin/env python3
+"""Throughput of the DSA path (indexer -> top-k -> sparse MQA attention) on one
+MI355X, printed as one JSON line.
+
+A step is one dsa_forward call over one batch of synthetic inputs already
+resident in HBM. The default workload is the 128K-context decode batch:
+64 sequences x 131072 keys, indexer dim 128 in fp8 e4m3fn with clustered
+keys, top_k 2048, 16 query heads on one shared K/V set. value = queries/s.
+
+The roofline object covers the slowest of the three stages, timed alone with
+HIP events on the stream it runs on; cpu_baseline times the CPU oracle on a
+bounded sample of the same inputs (rank 0, one GPU only).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK = {"hbm": 8000.0, "fp8": 5000.0, "bf16": 2500.0}  # GB/s, TFLOP/s (dense)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = {
+    "indexer": "dsa_top_token_amd/csrc/indexer.hip",
+    "topk": "dsa_top_token_amd/csrc/topk.hip",
+    "attn": "dsa_top_token_amd/csrc/attn.hip",
+}
+
+
+def source_hash(stage):
+    with open(os.path.join(ROOT, KERNEL_SOURCES[stage]), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def stage_work(w, stage):
+    """Algorithmic work of one launch of `stage` on workload w:
+    (bound, amount, unit, peak)."""
+    es = 1 if w.idx_dtype == "fp8" else 2
+    if stage == "indexer":
+        if w.mode == "decode":
+            # stream every key's indexer row once (+ the query rows)
+            b = w.batch * w.n_k * w.d_idx * es + w.batch * w.n_q * w.d_idx * es
+            return "hbm", b / 1e9, "GB/s", PEAK["hbm"]
+        f = 2.0 * w.d_idx * w.n_causal_pairs()
+        return "mfma", f / 1e12, "TFLOP/s", PEAK[w.idx_dtype]
+    if stage == "topk":
+        # read each candidate score once, write the index lists
+        b = 4 * w.n_causal_pairs() + 4 * w.batch * w.n_q * w.top_k
+        return "hbm", b / 1e9, "GB/s", PEAK["hbm"]
+    # attention: gather each selected K and V row once, read Q, write O
+    b = w.n_selected() * 2 * 128 * 2 + 2 * w.batch * w.n_q * w.n_heads * 128 * 2
+    return "hbm", b / 1e9, "GB/s", PEAK["hbm"]
+
+
+def calib_copy(nbytes=1 << 30, reps=5):
+    """A plain device copy of known size (for scaling PMC byte counters)."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calib_copy_bytes": nbytes, "reps": reps}))
+
+
+def cpu_baseline(w, x, target_s=12.0):
+    """Time the oracle on a bounded sample of the workload's queries."""
+    import oracle
+    t_probe0 = time.perf_counter()
+    if w.mode == "decode":
+        # one decode row per sequence: sample sequences
+        def run(nseq):
+            xs = {k: v[:nseq] for k, v in x.items()}
+            oracle.forward(xs["q_idx"], xs["k_idx"], xs["Q"], xs["K"], xs["V"], w.q_pos0,
+                           w.top_k)
+            return nseq
+        nthreads = oracle.num_threads()
+        probe = min(w.batch, nthreads)
+        t0 = time.perf_counter()
+        run(probe)
+        tp = time.perf_counter() - t0
+        n = probe
+        if tp < target_s:
+            n = int(min(w.batch, max(probe, probe * target_s / max(tp, 1e-3))))
+            n = max(probe, n // probe * probe)
+        t0 = time.perf_counter()
+        q = run(n)
+        dt = time.perf_counter() - t0
+        sample = "%d of %d sequences (one decode query each), all stages" % (n, w.batch)
+    else:
+        # prefill: a stratified set of query rows
+        nthreads = oracle.num_threads()
+        rows = []
+        step = max(1, w.n_q // 64)
+        for r in range(0, w.n_q, step):
+            rows.append(r)
+        t0 = time.perf_counter()
+        q = 0
+        for r in rows:
+            oracle.forward(x["q_idx"], x["k_idx"], x["Q"], x["K"], x["V"], w.q_pos0, w.top_k,
+                           r, min(r + nthreads, w.n_q))
+            q += min(r + nthreads, w.n_q) - r
+            if time.perf_counter() - t0 > target_s:
+                break
+        dt = time.perf_counter() - t0
+        sample = "%d query rows of %d, strided through the prefill, all stages" % (q, w.n_q)
+    del t_probe0
+    return {"value": q / dt, "unit": "queries/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "sample": sample, "seconds": round(dt, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode_128k_clustered")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-stages", action="store_true",
+                    help="skip the per-stage timing loops")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (PMC byte scaling)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        sys.stderr.write("bench.py measures one GPU only: this path runs on a single "
+                         "MI355X with no sharding or collectives (asked for %d GPUs)\n"
+                         % max(args.gpus, world))
+        sys.exit(2)
+
+    import torch
+    if args.calib_copy:
+        calib_copy()
+        return
+
+    import dsa_top_token_amd as dsa
+    from dsa_top_token_amd import synth
+
+    w = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    x = synth.make_inputs(w, seed=args.seed)  # canonical CPU draw
+    d = {k: v.to(dev) for k, v in x.items()}
+    p = dsa.make_problem(w.batch, w.n_q, w.n_k, w.q_pos0, w.d_idx, w.idx_dtype, w.top_k,
+                         w.n_heads)
+    fwd = dsa.Forward(p, dev)
+    O = torch.empty_like(d["Q"])
+    idx = torch.empty((w.batch, w.n_q, w.top_k), dtype=torch.int32, device=dev)
+    lse = torch.empty((w.batch, w.n_q, w.n_heads), dtype=torch.float32, device=dev)
+
+    def step():
+        fwd(d["q_idx"], d["k_idx"], d["Q"], d["K"], d["V"], O, idx, lse)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = wall * 1e3 / args.steps
+    queries = w.batch * w.n_q
+    value = queries / (ms / 1e3)
+
+    # Per-stage timing: each stage alone, K launches between HIP events
+    # recorded on the stream the library launches on (torch's current stream).
+    stages = {}
+    roof = None
+    if not args.no_stages:
+        lib = dsa.load()
+        stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        P = ctypes.byref(p)
+        rows_slab = w.n_q
+        scores = torch.empty((w.batch, rows_slab, w.n_k), dtype=torch.float32, device=dev) \
+            if w.batch * rows_slab * w.n_k <= (1 << 31) else None
+        attn_ws = torch.empty(max(dsa.workspace_size(p, dsa.OP_ATTN), 1), dtype=torch.uint8,
+                              device=dev)
+        calls = {}
+        if scores is not None:
+            calls["indexer"] = lambda: lib.dsa_index_scores(
+                P, d["q_idx"].data_ptr(), d["k_idx"].data_ptr(), 0, w.n_q,
+                scores.data_ptr(), stream)
+            calls["topk"] = lambda: lib.dsa_topk(P, scores.data_ptr(), 0, w.n_q,
+                                                 idx.data_ptr(), None, 0, stream)
+        calls["attn"] = lambda: lib.dsa_sparse_attn(
+            P, d["Q"].data_ptr(), d["K"].data_ptr(), d["V"].data_ptr(), idx.data_ptr(),
+            O.data_ptr(), lse.data_ptr(), attn_ws.data_ptr(), attn_ws.numel(), stream)
+        n_rep = max(3, args.steps)
+        for name, fn in calls.items():
+            for _ in range(2):
+                assert fn() == 0, lib.dsa_last_error()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(n_rep):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            stages[name] = e0.elapsed_time(e1) / n_rep
+        step()  # leave idx/O from a full forward
+        torch.cuda.synchronize()
+        dom = max(stages, key=stages.get)
+        bound, amount, unit, peak = stage_work(w, dom)
+        achieved = amount / (stages[dom] / 1e3)
+        traffic = None
+        if os.path.exists(TRAFFIC_FILE):
+            rec = json.load(open(TRAFFIC_FILE)).get("%s/%s" % (w.name, dom))
+            if rec and rec.get("source_sha256_16") == source_hash(dom):
+                traffic = rec.get("bytes_per_launch")
+        roof = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+                "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": dom,
+                "launch_ms": round(stages[dom], 4)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, x)
+
+    out = {
+        "metric": "queries/sec (indexer+top-k+sparse attn) at 128K ctx; % of fp8 MFMA / HBM peak",
+        "value": round(value, 2),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": ("fp8" if w.idx_dtype == "fp8" else "bf16") + "+bf16",
+        "data": "synthetic (seeded integer indexer inputs, N(0,1) bf16 Q/K/V)",
+        "config": {"workload": w.name, "mode": w.mode, "batch": w.batch, "n_q": w.n_q,
+                   "n_k": w.n_k, "d_idx": w.d_idx, "idx_dtype": w.idx_dtype,
+                   "top_k": w.top_k, "n_heads": w.n_heads, "clustered_keys": w.clustered,
+                   "parallelism": "single GPU"},
+        "stages_ms": {k: round(v, 4) for k, v in stages.items()},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()
