@@ -14,7 +14,6 @@ bounded sample of the same inputs (rank 0, one GPU only).
 from __future__ import annotations
 
 import argparse
-import ctypes
 import hashlib
 import json
 import os
@@ -171,42 +170,19 @@ def main():
     queries = w.batch * w.n_q
     value = queries / (ms / 1e3)
 
-    # Per-stage timing: each stage alone, K launches between HIP events
-    # recorded on the stream the library launches on (torch's current stream).
+    # Per-stage device time of the same forward call, from HIP events that
+    # dsa_forward_timed records on this stream between the stage kernels.
     stages = {}
     roof = None
     if not args.no_stages:
-        lib = dsa.load()
-        stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
-        P = ctypes.byref(p)
-        rows_slab = w.n_q
-        scores = torch.empty((w.batch, rows_slab, w.n_k), dtype=torch.float32, device=dev) \
-            if w.batch * rows_slab * w.n_k <= (1 << 31) else None
-        attn_ws = torch.empty(max(dsa.workspace_size(p, dsa.OP_ATTN), 1), dtype=torch.uint8,
-                              device=dev)
-        calls = {}
-        if scores is not None:
-            calls["indexer"] = lambda: lib.dsa_index_scores(
-                P, d["q_idx"].data_ptr(), d["k_idx"].data_ptr(), 0, w.n_q,
-                scores.data_ptr(), stream)
-            calls["topk"] = lambda: lib.dsa_topk(P, scores.data_ptr(), 0, w.n_q,
-                                                 idx.data_ptr(), None, 0, stream)
-        calls["attn"] = lambda: lib.dsa_sparse_attn(
-            P, d["Q"].data_ptr(), d["K"].data_ptr(), d["V"].data_ptr(), idx.data_ptr(),
-            O.data_ptr(), lse.data_ptr(), attn_ws.data_ptr(), attn_ws.numel(), stream)
+        names = ("indexer", "topk", "attn")
+        tot = [0.0, 0.0, 0.0]
         n_rep = max(3, args.steps)
-        for name, fn in calls.items():
-            for _ in range(2):
-                assert fn() == 0, lib.dsa_last_error()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(n_rep):
-                fn()
-            e1.record()
-            torch.cuda.synchronize()
-            stages[name] = e0.elapsed_time(e1) / n_rep
-        step()  # leave idx/O from a full forward
-        torch.cuda.synchronize()
+        slabs = 1
+        for _ in range(n_rep):
+            ms3, slabs = fwd.timed(d["q_idx"], d["k_idx"], d["Q"], d["K"], d["V"], O, idx, lse)
+            tot = [a + b for a, b in zip(tot, ms3)]
+        stages = {n: t / n_rep for n, t in zip(names, tot)}
         dom = max(stages, key=stages.get)
         bound, amount, unit, peak = stage_work(w, dom)
         achieved = amount / (stages[dom] / 1e3)
@@ -214,10 +190,10 @@ def main():
         if os.path.exists(TRAFFIC_FILE):
             rec = json.load(open(TRAFFIC_FILE)).get("%s/%s" % (w.name, dom))
             if rec and rec.get("source_sha256_16") == source_hash(dom):
-                traffic = rec.get("bytes_per_launch")
+                traffic = rec.get("bytes_per_step")
         roof = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                 "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": dom,
-                "launch_ms": round(stages[dom], 4)}
+                "stage_ms": round(stages[dom], 4), "launches_per_step": slabs}
 
     cpu = None
     if not args.no_cpu_baseline:

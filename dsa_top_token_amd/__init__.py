@@ -29,7 +29,7 @@ OP_TOPK, OP_ATTN, OP_FORWARD = 1, 2, 3
 HEAD_DIM = 128
 
 EXPORTS = ("dsa_workspace_size", "dsa_index_scores", "dsa_topk", "dsa_sparse_attn",
-           "dsa_forward", "dsa_status_str", "dsa_last_error")
+           "dsa_forward", "dsa_forward_timed", "dsa_status_str", "dsa_last_error")
 
 
 class Problem(ctypes.Structure):
@@ -65,8 +65,9 @@ def load():
             lib.dsa_topk.argtypes = [PP, P, I, I, P, P, S, P]
             lib.dsa_sparse_attn.argtypes = [PP, P, P, P, P, P, P, P, S, P]
             lib.dsa_forward.argtypes = [PP, P, P, P, P, P, P, P, P, P, S, P]
+            lib.dsa_forward_timed.argtypes = [PP, P, P, P, P, P, P, P, P, P, S, P, P, P]
             for f in (lib.dsa_workspace_size, lib.dsa_index_scores, lib.dsa_topk,
-                      lib.dsa_sparse_attn, lib.dsa_forward):
+                      lib.dsa_sparse_attn, lib.dsa_forward, lib.dsa_forward_timed):
                 f.restype = I
             lib.dsa_status_str.argtypes = [I]
             lib.dsa_status_str.restype = ctypes.c_char_p
@@ -183,6 +184,17 @@ class Forward:
         _check(load().dsa_forward(ctypes.byref(self.p), _ptr(q_idx), _ptr(k_idx), _ptr(Q),
                                   _ptr(K), _ptr(V), _ptr(idx_out), _ptr(O), _ptr(lse),
                                   _ptr(self.ws), self.ws_bytes, _stream(self.device)))
+
+    def timed(self, q_idx, k_idx, Q, K, V, O, idx_out=None, lse=None):
+        """Run once through dsa_forward_timed; returns ([indexer, top-k,
+        attention] milliseconds, number of row slabs). Blocks until done."""
+        ms = (ctypes.c_float * 3)()
+        slabs = ctypes.c_int32(0)
+        _check(load().dsa_forward_timed(ctypes.byref(self.p), _ptr(q_idx), _ptr(k_idx),
+                                        _ptr(Q), _ptr(K), _ptr(V), _ptr(idx_out), _ptr(O),
+                                        _ptr(lse), _ptr(self.ws), self.ws_bytes,
+                                        _stream(self.device), ms, ctypes.byref(slabs)))
+        return list(ms), slabs.value
 
 
 def forward(q_idx, k_idx, Q, K, V, q_pos0, top_k, want_idx=True, want_lse=True):

@@ -5,6 +5,8 @@
 #include <cstdarg>
 #include <cstdio>
 #include <string>
+#include <utility>
+#include <vector>
 
 #include "../../include/dsa.h"
 #include "dsa_internal.h"
@@ -99,17 +101,30 @@ size_t attn_ws_bytes(const dsa_problem* p) {
     return align_up((size_t)p->batch * p->n_q * ns * kPartFloats * sizeof(float));
 }
 
+// Workspace of dsa_topk: the chunked schedule's buffers for the largest row
+// slab that uses it (the schedule is chosen by batch * rows, so smaller slabs
+// need less).
+size_t topk_ws_bytes_max(const dsa_problem* p) {
+    for (int rows = p->n_q < 256 ? p->n_q : 256; rows >= 1; --rows)
+        if (dsa::topk_use_chunked(p->batch, rows, p->n_k))
+            return align_up(dsa::topk_ws_bytes(p->batch, rows, p->n_k));
+    return 0;
+}
+
 struct ForwardLayout {
-    size_t scores, idx, part, total;
+    size_t scores, idx, topk, part, total;
 };
 
 ForwardLayout forward_layout(const dsa_problem* p) {
     ForwardLayout L;
     L.scores = 0;
-    const size_t sb = align_up((size_t)p->batch * slab_rows(p) * p->n_k * sizeof(float));
+    const int R = slab_rows(p);
+    const size_t sb = align_up((size_t)p->batch * R * p->n_k * sizeof(float));
     L.idx = sb;
     const size_t ib = align_up((size_t)p->batch * p->n_q * p->top_k * sizeof(int32_t));
-    L.part = L.idx + ib;
+    L.topk = L.idx + ib;
+    const size_t tb = align_up(dsa::topk_ws_bytes(p->batch, R, p->n_k));
+    L.part = L.topk + tb;
     L.total = L.part + attn_ws_bytes(p);
     return L;
 }
@@ -137,96 +152,36 @@ dsa::AttnArgs attn_args(const dsa_problem* p, const void* Q, const void* K, cons
     return a;
 }
 
-}  // namespace
-
-extern "C" {
-
-dsa_status dsa_workspace_size(const dsa_problem* p, int32_t op, size_t* bytes) {
-    if (!bytes) return fail(DSA_E_NULL, "bytes is NULL");
-    dsa_status s = check_problem(p);
-    if (s != DSA_OK) return s;
-    switch (op) {
-        case DSA_OP_TOPK: *bytes = 0; break;
-        case DSA_OP_ATTN: *bytes = attn_ws_bytes(p); break;
-        case DSA_OP_FORWARD: *bytes = forward_layout(p).total; break;
-        default: return fail(DSA_E_UNSUPPORTED, "unknown op %d", op);
+// HIP events recorded between the stages of a forward call (profiling).
+// mark(s) starts a segment charged to stage s (0 indexer, 1 top-k,
+// 2 attention; -1 ends the last segment).
+struct StageTimer {
+    hipStream_t st;
+    std::vector<std::pair<int, hipEvent_t>> marks;
+    hipError_t err = hipSuccess;
+    void mark(int stage) {
+        hipEvent_t e = nullptr;
+        if (err == hipSuccess) err = hipEventCreate(&e);
+        if (err == hipSuccess) err = hipEventRecord(e, st);
+        if (err == hipSuccess) marks.push_back({stage, e});
     }
-    return ok();
-}
+    hipError_t finish(float* ms) {
+        if (err == hipSuccess && !marks.empty()) err = hipEventSynchronize(marks.back().second);
+        for (size_t i = 0; err == hipSuccess && i + 1 < marks.size(); ++i) {
+            float t = 0.f;
+            err = hipEventElapsedTime(&t, marks[i].second, marks[i + 1].second);
+            if (marks[i].first >= 0) ms[marks[i].first] += t;
+        }
+        for (auto& m : marks) hipEventDestroy(m.second);
+        marks.clear();
+        return err;
+    }
+};
 
-dsa_status dsa_index_scores(const dsa_problem* p, const void* q_idx, const void* k_idx,
-                            int32_t q_begin, int32_t q_end, float* scores, void* stream) {
-    dsa_status s = check_problem(p);
-    if (s != DSA_OK) return s;
-    if ((s = check_ptrs({q_idx, k_idx, scores}, "q_idx, k_idx, scores")) != DSA_OK) return s;
-    if (q_begin < 0 || q_end > p->n_q || q_begin >= q_end)
-        return fail(DSA_E_SHAPE, "need 0 <= q_begin < q_end <= n_q (got %d, %d, n_q=%d)",
-                    q_begin, q_end, p->n_q);
-    dsa::IndexArgs a{};
-    a.q = q_idx;
-    a.k = k_idx;
-    a.scores = scores;
-    a.B = p->batch;
-    a.n_q = p->n_q;
-    a.n_k = p->n_k;
-    a.q_pos0 = p->q_pos0;
-    a.d = p->d_idx;
-    a.dtype = p->idx_dtype;
-    a.q_begin = q_begin;
-    a.q_end = q_end;
-    a.scale = index_scale(p->d_idx);
-    a.write_masked = 1;
-    hipError_t e = dsa::launch_index_scores(a, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return hip_fail(e, "index_scores launch");
-    return ok();
-}
-
-dsa_status dsa_topk(const dsa_problem* p, const float* scores, int32_t q_begin, int32_t q_end,
-                    int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
-    (void)ws;
-    (void)ws_bytes;
-    dsa_status s = check_problem(p);
-    if (s != DSA_OK) return s;
-    if ((s = check_ptrs({scores, idx}, "scores, idx")) != DSA_OK) return s;
-    if (q_begin < 0 || q_end > p->n_q || q_begin >= q_end)
-        return fail(DSA_E_SHAPE, "need 0 <= q_begin < q_end <= n_q (got %d, %d, n_q=%d)",
-                    q_begin, q_end, p->n_q);
-    dsa::TopkArgs a{};
-    a.scores = scores;
-    a.idx = idx;
-    a.B = p->batch;
-    a.rows = q_end - q_begin;
-    a.n_k = p->n_k;
-    a.k = p->top_k;
-    a.pos_begin = (long long)p->q_pos0 + q_begin;
-    a.idx_rows = a.rows;
-    a.idx_row0 = 0;
-    hipError_t e = dsa::launch_topk(a, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return hip_fail(e, "topk launch");
-    return ok();
-}
-
-dsa_status dsa_sparse_attn(const dsa_problem* p, const void* Q, const void* K, const void* V,
-                           const int32_t* idx, void* O, float* lse, void* ws, size_t ws_bytes,
-                           void* stream) {
-    dsa_status s = check_problem(p);
-    if (s != DSA_OK) return s;
-    if ((s = check_ptrs({Q, K, V, idx, O}, "Q, K, V, idx, O")) != DSA_OK) return s;
-    if (lse && misaligned(lse)) return fail(DSA_E_ALIGN, "lse is not 16-byte aligned");
-    const size_t need = attn_ws_bytes(p);
-    if (need > 0 && (!ws || ws_bytes < need))
-        return fail(DSA_E_WORKSPACE, "attention needs %zu workspace bytes (got %zu)", need,
-                    ws ? ws_bytes : (size_t)0);
-    if (need > 0 && misaligned(ws)) return fail(DSA_E_ALIGN, "workspace is not 16-byte aligned");
-    dsa::AttnArgs a = attn_args(p, Q, K, V, idx, O, lse, ws);
-    hipError_t e = dsa::launch_sparse_attn(a, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return hip_fail(e, "sparse_attn launch");
-    return ok();
-}
-
-dsa_status dsa_forward(const dsa_problem* p, const void* q_idx, const void* k_idx, const void* Q,
-                       const void* K, const void* V, int32_t* idx_out, void* O, float* lse,
-                       void* ws, size_t ws_bytes, void* stream) {
+dsa_status forward_impl(const dsa_problem* p, const void* q_idx, const void* k_idx,
+                        const void* Q, const void* K, const void* V, int32_t* idx_out, void* O,
+                        float* lse, void* ws, size_t ws_bytes, void* stream, StageTimer* tm,
+                        int32_t* n_slabs) {
     dsa_status s = check_problem(p);
     if (s != DSA_OK) return s;
     if ((s = check_ptrs({q_idx, k_idx, Q, K, V, O}, "q_idx, k_idx, Q, K, V, O")) != DSA_OK)
@@ -263,21 +218,153 @@ dsa_status dsa_forward(const dsa_problem* p, const void* q_idx, const void* k_id
     ta.n_k = p->n_k;
     ta.k = p->top_k;
     ta.idx_rows = p->n_q;
-    for (int r0 = 0; r0 < p->n_q; r0 += R) {
+    ta.ws = w + L.topk;
+    int slabs = 0;
+    for (int r0 = 0; r0 < p->n_q; r0 += R, ++slabs) {
         const int r1 = r0 + R < p->n_q ? r0 + R : p->n_q;
         ia.q_begin = r0;
         ia.q_end = r1;
-        hipError_t e = dsa::launch_index_scores(ia, st);
-        if (e != hipSuccess) return hip_fail(e, "index_scores launch");
         ta.rows = r1 - r0;
         ta.pos_begin = (long long)p->q_pos0 + r0;
         ta.idx_row0 = r0;
+        // One query per sequence on the chunked top-k schedule: the indexer
+        // kernel builds the row histograms the selection starts from.
+        const bool fuse = ta.rows == 1 && dsa::topk_use_chunked(p->batch, 1, p->n_k);
+        ia.hist = fuse ? dsa::topk_hist_ptr(ta.ws) : nullptr;
+        ta.hist_ready = fuse ? 1 : 0;
+        hipError_t e = hipSuccess;
+        if (tm) tm->mark(1);
+        if (fuse && (e = dsa::launch_topk_prepare(ta, ta.ws, st)) != hipSuccess)
+            return hip_fail(e, "topk prepare launch");
+        if (tm) tm->mark(0);
+        e = dsa::launch_index_scores(ia, st);
+        if (e != hipSuccess) return hip_fail(e, "index_scores launch");
+        if (tm) tm->mark(1);
         e = dsa::launch_topk(ta, st);
         if (e != hipSuccess) return hip_fail(e, "topk launch");
     }
+    if (tm) tm->mark(2);
     dsa::AttnArgs aa = attn_args(p, Q, K, V, idx, O, lse, w + L.part);
     hipError_t e = dsa::launch_sparse_attn(aa, st);
     if (e != hipSuccess) return hip_fail(e, "sparse_attn launch");
+    if (tm) tm->mark(-1);
+    if (n_slabs) *n_slabs = slabs;
+    return DSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+dsa_status dsa_workspace_size(const dsa_problem* p, int32_t op, size_t* bytes) {
+    if (!bytes) return fail(DSA_E_NULL, "bytes is NULL");
+    dsa_status s = check_problem(p);
+    if (s != DSA_OK) return s;
+    switch (op) {
+        case DSA_OP_TOPK: *bytes = topk_ws_bytes_max(p); break;
+        case DSA_OP_ATTN: *bytes = attn_ws_bytes(p); break;
+        case DSA_OP_FORWARD: *bytes = forward_layout(p).total; break;
+        default: return fail(DSA_E_UNSUPPORTED, "unknown op %d", op);
+    }
+    return ok();
+}
+
+dsa_status dsa_index_scores(const dsa_problem* p, const void* q_idx, const void* k_idx,
+                            int32_t q_begin, int32_t q_end, float* scores, void* stream) {
+    dsa_status s = check_problem(p);
+    if (s != DSA_OK) return s;
+    if ((s = check_ptrs({q_idx, k_idx, scores}, "q_idx, k_idx, scores")) != DSA_OK) return s;
+    if (q_begin < 0 || q_end > p->n_q || q_begin >= q_end)
+        return fail(DSA_E_SHAPE, "need 0 <= q_begin < q_end <= n_q (got %d, %d, n_q=%d)",
+                    q_begin, q_end, p->n_q);
+    dsa::IndexArgs a{};
+    a.q = q_idx;
+    a.k = k_idx;
+    a.scores = scores;
+    a.B = p->batch;
+    a.n_q = p->n_q;
+    a.n_k = p->n_k;
+    a.q_pos0 = p->q_pos0;
+    a.d = p->d_idx;
+    a.dtype = p->idx_dtype;
+    a.q_begin = q_begin;
+    a.q_end = q_end;
+    a.scale = index_scale(p->d_idx);
+    a.write_masked = 1;
+    hipError_t e = dsa::launch_index_scores(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "index_scores launch");
+    return ok();
+}
+
+dsa_status dsa_topk(const dsa_problem* p, const float* scores, int32_t q_begin, int32_t q_end,
+                    int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+    dsa_status s = check_problem(p);
+    if (s != DSA_OK) return s;
+    if ((s = check_ptrs({scores, idx}, "scores, idx")) != DSA_OK) return s;
+    if (q_begin < 0 || q_end > p->n_q || q_begin >= q_end)
+        return fail(DSA_E_SHAPE, "need 0 <= q_begin < q_end <= n_q (got %d, %d, n_q=%d)",
+                    q_begin, q_end, p->n_q);
+    const size_t need = dsa::topk_ws_bytes(p->batch, q_end - q_begin, p->n_k);
+    if (need > 0 && (!ws || ws_bytes < need))
+        return fail(DSA_E_WORKSPACE, "top-k needs %zu workspace bytes (got %zu)", need,
+                    ws ? ws_bytes : (size_t)0);
+    if (need > 0 && misaligned(ws)) return fail(DSA_E_ALIGN, "workspace is not 16-byte aligned");
+    dsa::TopkArgs a{};
+    a.scores = scores;
+    a.idx = idx;
+    a.B = p->batch;
+    a.rows = q_end - q_begin;
+    a.n_k = p->n_k;
+    a.k = p->top_k;
+    a.pos_begin = (long long)p->q_pos0 + q_begin;
+    a.idx_rows = a.rows;
+    a.idx_row0 = 0;
+    a.ws = ws;
+    a.hist_ready = 0;
+    hipError_t e = dsa::launch_topk(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "topk launch");
+    return ok();
+}
+
+dsa_status dsa_sparse_attn(const dsa_problem* p, const void* Q, const void* K, const void* V,
+                           const int32_t* idx, void* O, float* lse, void* ws, size_t ws_bytes,
+                           void* stream) {
+    dsa_status s = check_problem(p);
+    if (s != DSA_OK) return s;
+    if ((s = check_ptrs({Q, K, V, idx, O}, "Q, K, V, idx, O")) != DSA_OK) return s;
+    if (lse && misaligned(lse)) return fail(DSA_E_ALIGN, "lse is not 16-byte aligned");
+    const size_t need = attn_ws_bytes(p);
+    if (need > 0 && (!ws || ws_bytes < need))
+        return fail(DSA_E_WORKSPACE, "attention needs %zu workspace bytes (got %zu)", need,
+                    ws ? ws_bytes : (size_t)0);
+    if (need > 0 && misaligned(ws)) return fail(DSA_E_ALIGN, "workspace is not 16-byte aligned");
+    dsa::AttnArgs a = attn_args(p, Q, K, V, idx, O, lse, ws);
+    hipError_t e = dsa::launch_sparse_attn(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "sparse_attn launch");
+    return ok();
+}
+
+dsa_status dsa_forward(const dsa_problem* p, const void* q_idx, const void* k_idx, const void* Q,
+                       const void* K, const void* V, int32_t* idx_out, void* O, float* lse,
+                       void* ws, size_t ws_bytes, void* stream) {
+    dsa_status s = forward_impl(p, q_idx, k_idx, Q, K, V, idx_out, O, lse, ws, ws_bytes, stream,
+                                nullptr, nullptr);
+    return s == DSA_OK ? ok() : s;
+}
+
+dsa_status dsa_forward_timed(const dsa_problem* p, const void* q_idx, const void* k_idx,
+                             const void* Q, const void* K, const void* V, int32_t* idx_out,
+                             void* O, float* lse, void* ws, size_t ws_bytes, void* stream,
+                             float* stage_ms, int32_t* n_slabs) {
+    if (!stage_ms) return fail(DSA_E_NULL, "stage_ms is NULL");
+    StageTimer tm;
+    tm.st = static_cast<hipStream_t>(stream);
+    for (int i = 0; i < 3; ++i) stage_ms[i] = 0.f;
+    dsa_status s = forward_impl(p, q_idx, k_idx, Q, K, V, idx_out, O, lse, ws, ws_bytes, stream,
+                                &tm, n_slabs);
+    hipError_t e = tm.finish(stage_ms);
+    if (s != DSA_OK) return s;
+    if (e != hipSuccess) return hip_fail(e, "stage timing events");
     return ok();
 }
 

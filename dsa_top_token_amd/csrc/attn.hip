@@ -206,38 +206,44 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(AttnArgs a) {
     }
 }
 
-// Merge of split partials: one thread per (query, head, 4 dims).
+// Merge of split partials: one wave per (query, head); lane l owns dims
+// 2l, 2l+1. Every split's (max, sum) pair is read first, then the rescaled
+// partial outputs are summed.
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
-    const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
-    const long long total = (long long)a.B * a.n_q * a.H * (HD / 4);
-    if (t >= total) return;
-    const int c4 = (int)(t % (HD / 4));
-    const long long qh = t / (HD / 4);
+    const int lane = threadIdx.x & 63;
+    const long long qh = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (qh >= (long long)a.B * a.n_q * a.H) return;
     const int h = (int)(qh % a.H);
     const long long qrow = qh / a.H;
     const float ninf = -__builtin_inff();
     const float* base = a.part + (size_t)qrow * a.n_split * 16 * PART + (size_t)h * PART;
+    const size_t stride = (size_t)16 * PART;
+    // lanes read the split statistics in parallel (n_split <= 64 per pass)
     float M = ninf;
-    for (int s = 0; s < a.n_split; ++s) M = fmaxf(M, base[(size_t)s * 16 * PART + HD]);
-    float L = 0.f;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s0 = 0; s0 < a.n_split; s0 += 64) {
+        const int s = s0 + lane;
+        const float ms = s < a.n_split ? base[(size_t)s * stride + HD] : ninf;
+        M = fmaxf(M, ms);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+    float L = 0.f, o0 = 0.f, o1 = 0.f;
     if (M != ninf) {
         for (int s = 0; s < a.n_split; ++s) {
-            const float* ps = base + (size_t)s * 16 * PART;
+            const float* ps = base + (size_t)s * stride;
             const float w = exp2f(ps[HD] - M);
             L += w * ps[HD + 1];
-            const float4 v = *reinterpret_cast<const float4*>(ps + 4 * c4);
-            acc.x += w * v.x;
-            acc.y += w * v.y;
-            acc.z += w * v.z;
-            acc.w += w * v.w;
+            const float2 v = *reinterpret_cast<const float2*>(ps + 2 * lane);
+            o0 += w * v.x;
+            o1 += w * v.y;
         }
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
-    const bf16x4 h4 = {(__bf16)(acc.x * inv), (__bf16)(acc.y * inv), (__bf16)(acc.z * inv),
-                       (__bf16)(acc.w * inv)};
-    *reinterpret_cast<uint2*>(a.O + (qrow * a.H + h) * HD + 4 * c4) = __builtin_bit_cast(uint2, h4);
-    if (a.lse && c4 == 0) a.lse[qrow * a.H + h] = L > 0.f ? (M + log2f(L)) * kLn2 : ninf;
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 h2 = {(__bf16)(o0 * inv), (__bf16)(o1 * inv)};
+    *reinterpret_cast<uint32_t*>(a.O + (qrow * a.H + h) * HD + 2 * lane) =
+        __builtin_bit_cast(uint32_t, h2);
+    if (a.lse && lane == 0) a.lse[qrow * a.H + h] = L > 0.f ? (M + log2f(L)) * kLn2 : ninf;
 }
 
 }  // namespace
@@ -267,8 +273,7 @@ hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(sparse_attn_kernel<true>, dim3((unsigned)nb), dim3(256), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const long long total = (long long)a.B * a.n_q * a.H * (HD / 4);
-    const long long nc = (total + 255) / 256;
+    const long long nc = ((long long)a.B * a.n_q * a.H + 3) / 4;
     if (nc > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)nc), dim3(256), 0, s, a);
     return hipGetLastError();

@@ -15,6 +15,8 @@ struct IndexArgs {
     int q_begin, q_end;
     float scale;            // fl32(d^-0.5)
     int write_masked;       // 1: write -inf past each query's position
+    uint32_t* hist;         // optional (one query row per sequence only):
+                            // per-row digit-1 histograms of the top-k schedule
 };
 
 // Top-k over score rows; row r of sequence b belongs to position pos_begin + r
@@ -25,6 +27,8 @@ struct TopkArgs {
     int B, rows, n_k, k;
     long long pos_begin;
     int idx_rows, idx_row0;
+    void* ws;               // chunked schedule workspace (topk_ws_bytes)
+    int hist_ready;         // 1: the indexer already built the row histograms
 };
 
 // Sparse MQA attention. When n_split > 1 the kernel writes unnormalised
@@ -43,6 +47,14 @@ struct AttnArgs {
 
 hipError_t launch_index_scores(const IndexArgs& a, hipStream_t s);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
+
+// Chunked top-k schedule (few long rows): whether it is used, its workspace,
+// where its row histograms live inside that workspace, and the kernel that
+// clears them before an indexer call that builds them.
+bool topk_use_chunked(int B, int rows, int n_k);
+size_t topk_ws_bytes(int B, int rows, int n_k);
+uint32_t* topk_hist_ptr(void* ws);
+hipError_t launch_topk_prepare(const TopkArgs& a, void* ws, hipStream_t s);
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t s);
 
 // Split plan of the attention: splits per query and entries per split.

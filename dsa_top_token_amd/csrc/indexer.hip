@@ -17,7 +17,7 @@
 // contiguous bytes of its row: [128c + 32g, +32) for fp8 chunk c, lane group
 // g = lane / 16. For the integer-valued inputs the sum is exact in fp32, so
 // the result does not depend on the order.
-#include "dsa_internal.h"
+#include "topk_common.h"
 
 namespace dsa {
 namespace {
@@ -91,8 +91,16 @@ __device__ __forceinline__ float relu_scaled(float x, float scale) {
 
 // Workgroup = 4 waves arranged WM (queries) x WN (keys); each wave computes
 // 16 queries x 64 keys per iteration and ITER iterations.
-template <int DT, int D, int WM, int WN, int ITER>
+// With HIST (one query row per sequence), the workgroup also histograms the
+// digit-1 radix of its scores' order keys in LDS and adds the counts to the
+// sequence's row histogram, which the top-k selection starts from.
+template <int DT, int D, int WM, int WN, int ITER, bool HIST>
 __global__ __launch_bounds__(256) void index_scores_kernel(IndexArgs a) {
+    __shared__ uint32_t lhist[HIST ? topk::BINS : 1];
+    if (HIST) {
+        for (int i = threadIdx.x; i < topk::BINS; i += 256) lhist[i] = 0u;
+        __syncthreads();
+    }
     constexpr int ES = DT == 0 ? 1 : 2;
     constexpr int RB = D * ES;  // bytes per indexer row
     constexpr int QB = 16 * WM;
@@ -109,7 +117,7 @@ __global__ __launch_bounds__(256) void index_scores_kernel(IndexArgs a) {
     const int qb = bid % n_qb;
     const int b = bid / n_qb;
     const int wrow0 = qb * QB + wm * 16;
-    if (wrow0 >= rows) return;
+    if (wrow0 >= rows) return;  // never taken when HIST (WM == 1)
     const long long pos0 = (long long)a.q_pos0 + a.q_begin;
     const long long wmaxpos = pos0 + min(wrow0 + 16, rows) - 1;
     const float ninf = -__builtin_inff();
@@ -161,25 +169,47 @@ __global__ __launch_bounds__(256) void index_scores_kernel(IndexArgs a) {
                 }
             }
         }
+        if (HIST) {
+            // Row 0 sits in register 0 of lanes 0..15.
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int key = k0 + 16 * t + m;
+                const bool act = g == 0 && key < a.n_k && key <= pos0;
+                const float s = relu_scaled(acc[t][0], a.scale);
+                topk::hist_add(lhist, topk::rank_key(s) >> topk::SHIFT1, act);
+            }
+        }
+    }
+    if (HIST) {
+        __syncthreads();
+        uint32_t* gh = a.hist + (size_t)b * topk::BINS;
+        for (int i = threadIdx.x; i < topk::BINS; i += 256)
+            if (lhist[i]) atomicAdd(&gh[i], lhist[i]);
     }
 }
 
 template <int DT, int D>
 hipError_t launch_dt_d(const IndexArgs& a, hipStream_t s) {
     const int rows = a.q_end - a.q_begin;
+    if (a.hist && rows != 1) return hipErrorInvalidValue;
     if (rows <= 16) {
         // Few queries per sequence (decode): the 4 waves split the keys.
-        constexpr int QB = 16, KB = 256;
+        constexpr int QB = 16, KB = 1024;
         const long long nb = (long long)a.B * ((rows + QB - 1) / QB) * ((a.n_k + KB - 1) / KB);
         if (nb > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL((index_scores_kernel<DT, D, 1, 4, 1>), dim3((unsigned)nb), dim3(256),
-                           0, s, a);
+        if (a.hist)
+            hipLaunchKernelGGL((index_scores_kernel<DT, D, 1, 4, 4, true>), dim3((unsigned)nb),
+                               dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL((index_scores_kernel<DT, D, 1, 4, 4, false>), dim3((unsigned)nb),
+                               dim3(256), 0, s, a);
     } else {
+        if (a.hist) return hipErrorInvalidValue;
         constexpr int QB = 64, KB = 256;
         const long long nb = (long long)a.B * ((rows + QB - 1) / QB) * ((a.n_k + KB - 1) / KB);
         if (nb > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL((index_scores_kernel<DT, D, 4, 1, 4>), dim3((unsigned)nb), dim3(256),
-                           0, s, a);
+        hipLaunchKernelGGL((index_scores_kernel<DT, D, 4, 1, 4, false>), dim3((unsigned)nb),
+                           dim3(256), 0, s, a);
     }
     return hipGetLastError();
 }

@@ -2,104 +2,56 @@
 //
 // DeepSeek-V3.2 DSA page (kwkr.cn/news/60693), section 3.3: each query keeps
 // the top_k keys by indexer score; section 4.1 describes the selection stage
-// as plain comparisons. Here the comparisons are on 32-bit order keys (the
-// float32 bit pattern made monotone), resolved by a three-round radix select
-// (11 + 11 + 10 bits) and an ordered compaction:
-//   round 1  histogram of key bits 31..21 over the row -> threshold bin b1
-//   round 2  histogram of bits 20..10 among keys in b1 -> bin b2; the keys
-//            of b1 are also gathered into LDS when they fit
-//   round 3  histogram of bits 9..0 among keys in (b1, b2) -> exact value T
-//   output   every key above T, plus the `rem` lowest-index keys equal to T,
-//            written in ascending key order via a block-wide prefix scan.
-// Ties at T therefore go to the lower key index. One 512-thread workgroup
-// owns one score row; histograms live in LDS, and lanes of a wave that fall
-// in the same bin add to it once (ReLU zeros are one large tie class).
-#include "dsa_internal.h"
+// as plain comparisons. Comparisons here are on 32-bit order keys (the
+// float32 bit pattern made monotone) and ties go to the lower key index.
+//
+// Two schedules share the same radix digits (key bits 31..21, 20..10, 9..0):
+//
+// Per-row (many rows, as in prefill): one 512-thread workgroup per row runs
+//   three histogram rounds to find the exact k-th key T and the number `rem`
+//   of T-ties to keep, then an ordered compaction writes every key above T
+//   plus the first `rem` keys equal to T, in ascending index order.
+//
+// Chunked (few long rows, as in decode): a row is split into 2048-key chunks
+//   so the whole chip works on it.
+//     hist     per-row histogram of digit 1 (or built by the indexer kernel)
+//     select_a per chunk: count keys above the threshold bin b1 and write
+//              the keys inside b1 to the chunk's own candidate slot (an LDS
+//              counter, no device-wide atomics)
+//     select_b per row: finish digits 2 and 3 on the candidates (-> T), pick
+//              the tie cut-off index j_T by a radix select on indices, and
+//              turn per-chunk counts into output offsets
+//     out      per chunk: ordered compaction of keys > T or (= T and j <= j_T)
+//   A row whose candidates overflow (a chunk slot, or the LDS list of
+//   select_b) falls back to the per-row schedule inside select_b.
+#include "topk_common.h"
 
 namespace dsa {
 namespace {
 
-constexpr int NT = 512;
-constexpr int NW = NT / 64;
-constexpr int BINS = 2048;
-constexpr int CAP = 8192;
+using namespace topk;
 
-// Order key: float order mapped to unsigned order (-0.0 ranks with +0.0).
-__device__ __forceinline__ uint32_t rank_key(float f) {
-    uint32_t u = __float_as_uint(f);
-    if (u == 0x80000000u) u = 0u;
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
+constexpr int ROW_NT = 512;       // per-row schedule threads
+constexpr int ROW_CAP = 8192;     // per-row LDS candidate capacity (digit-2 keys)
+constexpr int CHUNK = 2048;       // chunked schedule: keys per chunk
+constexpr int CH_NT = 256;        // chunked schedule: threads of hist/select_a/out
+constexpr int SB_NT = 512;        // select_b threads
+constexpr int CAND_CAP = 12288;   // chunked schedule: candidates per row
+constexpr int CH_CAP = 512;       // chunked schedule: candidates kept per chunk
+constexpr int MAX_CHUNKS = 2048;  // 4M keys / CHUNK
+constexpr int MULTI_MAX_ROWS = 256;
+constexpr int MULTI_MIN_KEYS = 4 * CHUNK;
 
-// Histogram increment for the whole wave (call with every lane present).
-// Lanes that share the first active lane's bin add with one atomic.
-__device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t bin, bool active) {
-    const unsigned long long act = __ballot(active);
-    if (act == 0ull) return;
-    const int leader = __ffsll((long long)act) - 1;
-    const uint32_t lead_bin = __shfl(bin, leader);
-    const bool same = active && bin == lead_bin;
-    const unsigned long long same_mask = __ballot(same);
-    if ((int)__lane_id() == leader) atomicAdd(&hist[lead_bin], (uint32_t)__popcll(same_mask));
-    if (active && !same) atomicAdd(&hist[bin], 1u);
-}
-
-// Exclusive prefix sum over the workgroup; *total receives the sum.
-__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    uint32_t x = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = __shfl_up(x, o);
-        if (lane >= o) x += y;
-    }
-    if (lane == 63) wsum[w] = x;
-    __syncthreads();
-    uint32_t pre = 0, tot = 0;
-#pragma unroll
-    for (int i = 0; i < NW; ++i) {
-        const uint32_t s = wsum[i];
-        pre += i < w ? s : 0u;
-        tot += s;
-    }
-    __syncthreads();
-    *total = tot;
-    return pre + x - v;
-}
-
-// The bin holding the rem-th largest counted key: res[0] = bin, res[1] = keys
-// in higher bins (so res[1] < rem <= res[1] + hist[bin]).
-__device__ __forceinline__ void find_bin(const uint32_t* hist, uint32_t rem, uint32_t* wsum,
-                                         uint32_t* res) {
-    constexpr int PER = BINS / NT;
-    const int hi = BINS - 1 - (int)threadIdx.x * PER;
-    uint32_t c[PER], loc = 0;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        c[i] = hist[hi - i];
-        loc += c[i];
-    }
-    uint32_t tot;
-    uint32_t above = block_excl_scan(loc, wsum, &tot);
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        if (above < rem && above + c[i] >= rem) {
-            res[0] = (uint32_t)(hi - i);
-            res[1] = above;
-        }
-        above += c[i];
-    }
-    __syncthreads();
-}
-
-// Four consecutive order keys starting at element j (j % 4 == 0); lanes past
-// n get valid = false.
+// Four consecutive order keys starting at element j (j % 4 == 0), valid
+// below n.
 template <bool VEC>
 __device__ __forceinline__ void load4(const float* row, int j, int n, uint32_t key[4], bool ok[4]) {
     if (VEC && j + 3 < n) {
         const float4 v = *reinterpret_cast<const float4*>(row + j);
-        key[0] = rank_key(v.x); key[1] = rank_key(v.y);
-        key[2] = rank_key(v.z); key[3] = rank_key(v.w);
+        key[0] = rank_key(v.x);
+        key[1] = rank_key(v.y);
+        key[2] = rank_key(v.z);
+        key[3] = rank_key(v.w);
         ok[0] = ok[1] = ok[2] = ok[3] = true;
     } else {
 #pragma unroll
@@ -110,26 +62,14 @@ __device__ __forceinline__ void load4(const float* row, int j, int n, uint32_t k
     }
 }
 
+// The per-row schedule for one row of n > k candidates, run by a ROW_NT-thread
+// workgroup. LDS: hist[BINS], cand[ROW_CAP], wsum[ROW_NT/64], res[4].
 template <bool VEC>
-__global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
-    __shared__ uint32_t hist[BINS];
-    __shared__ uint32_t cand[CAP];
-    __shared__ uint32_t wsum[NW];
-    __shared__ uint32_t res[4];
+__device__ void row_topk(const float* row, int n, int k, int32_t* out, uint32_t* hist,
+                         uint32_t* cand, uint32_t* wsum, uint32_t* res) {
+    constexpr int NT = ROW_NT;
     const int tid = threadIdx.x;
-    const unsigned rid = blockIdx.x;
-    const int b = (int)(rid / (unsigned)a.rows), r = (int)(rid % (unsigned)a.rows);
-    const long long pos = a.pos_begin + r;
-    const int n = (int)min((long long)a.n_k, pos + 1);
-    const float* row = a.scores + (size_t)rid * a.n_k;
-    int32_t* out = a.idx + ((size_t)b * a.idx_rows + a.idx_row0 + r) * a.k;
-    const int k = a.k;
-    if (n <= k) {
-        for (int j = tid; j < k; j += NT) out[j] = j < n ? j : -1;
-        return;
-    }
-
-    // Round 1: bits 31..21.
+    // Digit 1.
     for (int i = tid; i < BINS; i += NT) hist[i] = 0u;
     if (tid == 0) res[2] = 0u;
     __syncthreads();
@@ -138,17 +78,16 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
         bool ok[4];
         load4<VEC>(row, base + 4 * tid, n, key, ok);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) hist_add(hist, key[e] >> 21, ok[e]);
+        for (int e = 0; e < 4; ++e) hist_add(hist, key[e] >> SHIFT1, ok[e]);
     }
     __syncthreads();
-    find_bin(hist, (uint32_t)k, wsum, res);
+    find_bin<NT>(hist, (uint32_t)k, wsum, res);
     const uint32_t b1 = res[0];
     uint32_t rem = (uint32_t)k - res[1];
     const uint32_t cnt1 = hist[b1];
-    const bool gather = cnt1 <= (uint32_t)CAP;
+    const bool gather = cnt1 <= (uint32_t)ROW_CAP;
     __syncthreads();
-
-    // Round 2: bits 20..10 of the keys in bin b1.
+    // Digit 2 among keys in b1 (gathered into LDS when they fit).
     for (int i = tid; i < BINS; i += NT) hist[i] = 0u;
     __syncthreads();
     for (int base = 0; base < n; base += 4 * NT) {
@@ -157,18 +96,17 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
         load4<VEC>(row, base + 4 * tid, n, key, ok);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const bool in = ok[e] && (key[e] >> 21) == b1;
-            hist_add(hist, (key[e] >> 10) & 2047u, in);
+            const bool in = ok[e] && (key[e] >> SHIFT1) == b1;
+            hist_add(hist, (key[e] >> SHIFT2) & (BINS - 1), in);
             if (gather && in) cand[atomicAdd(&res[2], 1u)] = key[e];
         }
     }
     __syncthreads();
-    find_bin(hist, rem, wsum, res);
+    find_bin<NT>(hist, rem, wsum, res);
     const uint32_t pre22 = (b1 << 11) | res[0];
     rem -= res[1];
     __syncthreads();
-
-    // Round 3: bits 9..0 of the keys in (b1, b2).
+    // Digit 3 among keys in (b1, b2).
     for (int i = tid; i < BINS; i += NT) hist[i] = 0u;
     __syncthreads();
     if (gather) {
@@ -176,7 +114,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
             const int c = base + tid;
             const bool ok = c < (int)cnt1;
             const uint32_t key = ok ? cand[c] : 0u;
-            hist_add(hist, key & 1023u, ok && (key >> 10) == pre22);
+            hist_add(hist, key & 1023u, ok && (key >> SHIFT2) == pre22);
         }
     } else {
         for (int base = 0; base < n; base += 4 * NT) {
@@ -185,16 +123,16 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
             load4<VEC>(row, base + 4 * tid, n, key, ok);
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                hist_add(hist, key[e] & 1023u, ok[e] && (key[e] >> 10) == pre22);
+                hist_add(hist, key[e] & 1023u, ok[e] && (key[e] >> SHIFT2) == pre22);
         }
     }
     __syncthreads();
-    find_bin(hist, rem, wsum, res);
+    find_bin<NT>(hist, rem, wsum, res);
     const uint32_t T = (pre22 << 10) | res[0];
     rem -= res[1];
     const uint32_t n_gt = (uint32_t)k - rem;
 
-    // Ordered compaction: 8 consecutive keys per thread per chunk.
+    // Ordered compaction: 8 consecutive keys per thread per pass.
     uint32_t gt_run = 0, eq_run = 0;
     for (int base = 0; base < n; base += 8 * NT) {
         const int j0 = base + 8 * tid;
@@ -209,7 +147,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
             eq += (ok[e] && key[e] == T) ? 1u : 0u;
         }
         uint32_t tot;
-        const uint32_t pk = block_excl_scan((gt << 16) | eq, wsum, &tot);
+        const uint32_t pk = block_excl_scan<NT>((gt << 16) | eq, wsum, &tot);
         uint32_t gb = gt_run + (pk >> 16), eb = eq_run + (pk & 0xffffu);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -229,17 +167,435 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
     }
 }
 
+__device__ __forceinline__ void fill_prefix(int32_t* out, int n, int k, int tid, int nt) {
+    for (int j = tid; j < k; j += nt) out[j] = j < n ? j : -1;
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(ROW_NT) void topk_row_kernel(TopkArgs a) {
+    __shared__ uint32_t hist[BINS];
+    __shared__ uint32_t cand[ROW_CAP];
+    __shared__ uint32_t wsum[ROW_NT / 64];
+    __shared__ uint32_t res[4];
+    const unsigned rid = blockIdx.x;
+    const int b = (int)(rid / (unsigned)a.rows), r = (int)(rid % (unsigned)a.rows);
+    const long long pos = a.pos_begin + r;
+    const int n = (int)min((long long)a.n_k, pos + 1);
+    const float* row = a.scores + (size_t)rid * a.n_k;
+    int32_t* out = a.idx + ((size_t)b * a.idx_rows + a.idx_row0 + r) * a.k;
+    if (n <= a.k) {
+        fill_prefix(out, n, a.k, threadIdx.x, ROW_NT);
+        return;
+    }
+    row_topk<VEC>(row, n, a.k, out, hist, cand, wsum, res);
+}
+
+// ---------------------------------------------------------------------------
+// Chunked schedule.
+
+struct MultiWs {
+    uint32_t* hist;      // [slots][BINS]
+    uint32_t* cnt;       // [slots][n_chunks] candidates found per chunk
+    uint2* cand;         // [slots][n_chunks][CH_CAP] (key, index)
+    uint32_t* chunk_gt;  // [slots][n_chunks] keys above bin b1 per chunk
+    uint32_t* chunk_off; // [slots][n_chunks] output offset per chunk
+    uint32_t* state;     // [slots][4]: T, j_T, fallback-done flag
+};
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+MultiWs carve(void* ws, int slots, int n_chunks, size_t* total) {
+    char* p = static_cast<char*>(ws);
+    size_t off = 0;
+    MultiWs w;
+    w.hist = reinterpret_cast<uint32_t*>(p + off);
+    off += align256((size_t)slots * BINS * 4);
+    w.cnt = reinterpret_cast<uint32_t*>(p + off);
+    off += align256((size_t)slots * n_chunks * 4);
+    w.cand = reinterpret_cast<uint2*>(p + off);
+    off += align256((size_t)slots * n_chunks * CH_CAP * 8);
+    w.chunk_gt = reinterpret_cast<uint32_t*>(p + off);
+    off += align256((size_t)slots * n_chunks * 4);
+    w.chunk_off = reinterpret_cast<uint32_t*>(p + off);
+    off += align256((size_t)slots * n_chunks * 4);
+    w.state = reinterpret_cast<uint32_t*>(p + off);
+    off += align256((size_t)slots * 16);
+    if (total) *total = off;
+    return w;
+}
+
+struct MultiArgs {
+    TopkArgs t;
+    MultiWs w;
+    int n_chunks;
+};
+
+__device__ __forceinline__ void slot_info(const MultiArgs& a, int slot, int* b, int* r, int* n) {
+    *b = slot / a.t.rows;
+    *r = slot % a.t.rows;
+    *n = (int)min((long long)a.t.n_k, a.t.pos_begin + *r + 1);
+}
+
+// Zero the per-row histograms (a kernel rather than a memset so the sequence
+// can be captured in a graph).
+__global__ __launch_bounds__(256) void topk_prepare_kernel(MultiArgs a) {
+    const long long total = (long long)a.t.B * a.t.rows * BINS;
+    for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < total;
+         i += (long long)gridDim.x * 256)
+        a.w.hist[i] = 0u;
+}
+
+// Digit-1 histogram of every chunk, flushed into the row's histogram.
+template <bool VEC>
+__global__ __launch_bounds__(CH_NT) void topk_hist_kernel(MultiArgs a) {
+    __shared__ uint32_t hist[BINS];
+    const int slot = blockIdx.x / a.n_chunks, c = blockIdx.x % a.n_chunks;
+    int b, r, n;
+    slot_info(a, slot, &b, &r, &n);
+    const int j0 = c * CHUNK;
+    if (n <= a.t.k || j0 >= n) return;
+    const int j1 = min(n, j0 + CHUNK);
+    for (int i = threadIdx.x; i < BINS; i += CH_NT) hist[i] = 0u;
+    __syncthreads();
+    const float* row = a.t.scores + (size_t)slot * a.t.n_k;
+    for (int base = j0; base < j1; base += 4 * CH_NT) {
+        uint32_t key[4];
+        bool ok[4];
+        load4<VEC>(row, base + 4 * threadIdx.x, j1, key, ok);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) hist_add(hist, key[e] >> SHIFT1, ok[e]);
+    }
+    __syncthreads();
+    uint32_t* g = a.w.hist + (size_t)slot * BINS;
+    for (int i = threadIdx.x; i < BINS; i += CH_NT)
+        if (hist[i]) atomicAdd(&g[i], hist[i]);
+}
+
+// Per chunk: count keys above bin b1; store the keys inside b1 (with their
+// indices) in the chunk's candidate slot, in any order.
+template <bool VEC>
+__global__ __launch_bounds__(CH_NT) void topk_select_a_kernel(MultiArgs a) {
+    __shared__ uint32_t hist[BINS];
+    __shared__ uint32_t wsum[CH_NT / 64];
+    __shared__ uint32_t res[4];
+    const int slot = blockIdx.x / a.n_chunks, c = blockIdx.x % a.n_chunks;
+    int b, r, n;
+    slot_info(a, slot, &b, &r, &n);
+    if (n <= a.t.k) return;
+    const size_t sc = (size_t)slot * a.n_chunks + c;
+    const int j0 = c * CHUNK;
+    if (j0 >= n) {
+        if (threadIdx.x == 0) {
+            a.w.chunk_gt[sc] = 0u;
+            a.w.cnt[sc] = 0u;
+        }
+        return;
+    }
+    const int j1 = min(n, j0 + CHUNK);
+    const uint32_t* g = a.w.hist + (size_t)slot * BINS;
+    for (int i = threadIdx.x; i < BINS; i += CH_NT) hist[i] = g[i];
+    if (threadIdx.x == 0) res[2] = 0u;
+    __syncthreads();
+    find_bin<CH_NT>(hist, (uint32_t)a.t.k, wsum, res);
+    const uint32_t b1 = res[0];
+    const float* row = a.t.scores + (size_t)slot * a.t.n_k;
+    uint2* cand = a.w.cand + sc * CH_CAP;
+    const int lane = threadIdx.x & 63;
+    uint32_t gt = 0;
+    for (int base = j0; base < j1; base += 4 * CH_NT) {
+        const int j = base + 4 * threadIdx.x;
+        uint32_t key[4];
+        bool ok[4];
+        load4<VEC>(row, j, j1, key, ok);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t bin = key[e] >> SHIFT1;
+            gt += (ok[e] && bin > b1) ? 1u : 0u;
+            const bool in = ok[e] && bin == b1;
+            const unsigned long long m = __ballot(in);
+            if (m) {
+                const int leader = __ffsll((long long)m) - 1;
+                uint32_t p0 = 0;
+                if (lane == leader) p0 = atomicAdd(&res[2], (uint32_t)__popcll(m));
+                p0 = __shfl(p0, leader);
+                if (in) {
+                    const uint32_t p = p0 + (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
+                    if (p < (uint32_t)CH_CAP) cand[p] = make_uint2(key[e], (uint32_t)(j + e));
+                }
+            }
+        }
+    }
+    uint32_t tot;
+    block_excl_scan<CH_NT>(gt, wsum, &tot);
+    if (threadIdx.x == 0) {
+        a.w.chunk_gt[sc] = tot;
+        a.w.cnt[sc] = res[2];
+    }
+}
+
+// Per row: exact threshold T and tie cut-off j_T from the candidates, and the
+// output offset of every chunk.
+template <bool VEC>
+__global__ __launch_bounds__(SB_NT) void topk_select_b_kernel(MultiArgs a) {
+    // LDS: hist[BINS] | keys[CAND_CAP] | idx[CAND_CAP] | cs[MAX_CHUNKS] | wsum | res
+    __shared__ uint32_t smem[BINS + 2 * CAND_CAP + MAX_CHUNKS + SB_NT / 64 + 4];
+    uint32_t* hist = smem;
+    uint32_t* keys = smem + BINS;
+    uint32_t* jj = keys + CAND_CAP;
+    uint32_t* cs = jj + CAND_CAP;
+    uint32_t* wsum = cs + MAX_CHUNKS;
+    uint32_t* res = wsum + SB_NT / 64;
+    const int tid = threadIdx.x;
+    const int slot = blockIdx.x;
+    int b, r, n;
+    slot_info(a, slot, &b, &r, &n);
+    const int k = a.t.k;
+    int32_t* out = a.t.idx + ((size_t)b * a.t.idx_rows + a.t.idx_row0 + r) * k;
+    uint32_t* st = a.w.state + (size_t)slot * 4;
+    if (n <= k) {
+        fill_prefix(out, n, k, tid, SB_NT);
+        return;
+    }
+    // Candidate counts per chunk -> offsets in the LDS list (cs holds them).
+    const int nch = a.n_chunks;
+    constexpr int PER = MAX_CHUNKS / SB_NT;
+    const uint32_t* ccnt = a.w.cnt + (size_t)slot * nch;
+    uint32_t cv[PER], cloc = 0, cmax = 0;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+        const int c = tid * PER + e;
+        cv[e] = c < nch ? ccnt[c] : 0u;
+        cloc += cv[e];
+        cmax = max(cmax, cv[e]);
+    }
+    if (tid == 0) res[3] = 0u;
+    uint32_t cnt;
+    uint32_t coff = block_excl_scan<SB_NT>(cloc, wsum, &cnt);  // has barriers
+    if (cmax > (uint32_t)CH_CAP || cnt > (uint32_t)CAND_CAP) res[3] = 1u;
+    __syncthreads();
+    const bool overflow = res[3] != 0u;
+    __syncthreads();
+    if (overflow) {
+        // A candidate slot overflowed: resolve the row on its own.
+        row_topk<VEC>(a.t.scores + (size_t)slot * a.t.n_k, n, k, out, hist, keys, wsum, res);
+        if (tid == 0) st[2] = 1u;
+        return;
+    }
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+        const int c = tid * PER + e;
+        if (c < nch) cs[c] = coff;
+        coff += cv[e];
+    }
+    const uint32_t* g = a.w.hist + (size_t)slot * BINS;
+    for (int i = tid; i < BINS; i += SB_NT) hist[i] = g[i];
+    __syncthreads();
+    // Copy every chunk's candidates: one wave per chunk at a time.
+    {
+        const int wv = tid >> 6, ln = tid & 63;
+        for (int c = wv; c < nch; c += SB_NT / 64) {
+            const uint32_t nc = ccnt[c], o = cs[c];
+            const uint2* src = a.w.cand + ((size_t)slot * nch + c) * CH_CAP;
+            for (uint32_t i = ln; i < nc; i += 64) {
+                const uint2 v = src[i];
+                keys[o + i] = v.x;
+                jj[o + i] = v.y;
+            }
+        }
+    }
+    __syncthreads();
+    find_bin<SB_NT>(hist, (uint32_t)k, wsum, res);
+    const uint32_t b1 = res[0];
+    uint32_t rem = (uint32_t)k - res[1];
+    __syncthreads();
+    // Digit 2.
+    for (int i = tid; i < BINS; i += SB_NT) hist[i] = 0u;
+    __syncthreads();
+    for (int base = 0; base < (int)cnt; base += SB_NT) {
+        const int i = base + tid;
+        const bool ok = i < (int)cnt;
+        hist_add(hist, ok ? (keys[i] >> SHIFT2) & (BINS - 1) : 0u, ok);
+    }
+    __syncthreads();
+    find_bin<SB_NT>(hist, rem, wsum, res);
+    const uint32_t pre22 = (b1 << 11) | res[0];
+    rem -= res[1];
+    __syncthreads();
+    // Digit 3.
+    for (int i = tid; i < BINS; i += SB_NT) hist[i] = 0u;
+    __syncthreads();
+    for (int base = 0; base < (int)cnt; base += SB_NT) {
+        const int i = base + tid;
+        const bool ok = i < (int)cnt && (keys[i] >> SHIFT2) == pre22;
+        hist_add(hist, ok ? keys[i] & 1023u : 0u, ok);
+    }
+    __syncthreads();
+    find_bin<SB_NT>(hist, rem, wsum, res);
+    const uint32_t T = (pre22 << 10) | res[0];
+    rem -= res[1];
+    __syncthreads();
+    // Tie cut-off: the rem-th smallest index among keys equal to T, found as
+    // the rem-th largest of (2^22 - 1 - j) in two 11-bit digits.
+    constexpr uint32_t JMAX = (1u << 22) - 1u;
+    for (int i = tid; i < BINS; i += SB_NT) hist[i] = 0u;
+    __syncthreads();
+    for (int base = 0; base < (int)cnt; base += SB_NT) {
+        const int i = base + tid;
+        const bool ok = i < (int)cnt && keys[i] == T;
+        hist_add(hist, ok ? (JMAX - jj[i]) >> 11 : 0u, ok);
+    }
+    __syncthreads();
+    find_bin<SB_NT>(hist, rem, wsum, res);
+    const uint32_t a1 = res[0];
+    const uint32_t remj = rem - res[1];
+    __syncthreads();
+    for (int i = tid; i < BINS; i += SB_NT) hist[i] = 0u;
+    __syncthreads();
+    for (int base = 0; base < (int)cnt; base += SB_NT) {
+        const int i = base + tid;
+        const bool ok = i < (int)cnt && keys[i] == T && ((JMAX - jj[i]) >> 11) == a1;
+        hist_add(hist, ok ? (JMAX - jj[i]) & 2047u : 0u, ok);
+    }
+    __syncthreads();
+    find_bin<SB_NT>(hist, remj, wsum, res);
+    const uint32_t jT = JMAX - ((a1 << 11) | res[0]);
+    __syncthreads();
+    // Selected candidates per chunk, then chunk offsets.
+    for (int i = tid; i < nch; i += SB_NT) cs[i] = 0u;
+    __syncthreads();
+    for (int i = tid; i < (int)cnt; i += SB_NT) {
+        const uint32_t key = keys[i], j = jj[i];
+        if (key > T || (key == T && j <= jT)) atomicAdd(&cs[j / CHUNK], 1u);
+    }
+    __syncthreads();
+    uint32_t v[PER], loc = 0;
+    const uint32_t* cg = a.w.chunk_gt + (size_t)slot * nch;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+        const int c = tid * PER + e;
+        v[e] = c < nch ? cg[c] + cs[c] : 0u;
+        loc += v[e];
+    }
+    uint32_t tot;
+    uint32_t off = block_excl_scan<SB_NT>(loc, wsum, &tot);
+    uint32_t* co = a.w.chunk_off + (size_t)slot * nch;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+        const int c = tid * PER + e;
+        if (c < nch) co[c] = off;
+        off += v[e];
+    }
+    if (tid == 0) {
+        st[0] = T;
+        st[1] = jT;
+        st[2] = 0u;
+    }
+}
+
+// Per chunk: ordered compaction of the selected keys into the output row.
+template <bool VEC>
+__global__ __launch_bounds__(CH_NT) void topk_out_kernel(MultiArgs a) {
+    __shared__ uint32_t wsum[CH_NT / 64];
+    constexpr int E = CHUNK / CH_NT;  // 8 consecutive keys per thread
+    const int slot = blockIdx.x / a.n_chunks, c = blockIdx.x % a.n_chunks;
+    int b, r, n;
+    slot_info(a, slot, &b, &r, &n);
+    const int k = a.t.k;
+    const int j0 = c * CHUNK;
+    if (n <= k || j0 >= n) return;
+    const uint32_t* st = a.w.state + (size_t)slot * 4;
+    if (st[2]) return;
+    const uint32_t T = st[0], jT = st[1];
+    const uint32_t off = a.w.chunk_off[(size_t)slot * a.n_chunks + c];
+    const int j1 = min(n, j0 + CHUNK);
+    const float* row = a.t.scores + (size_t)slot * a.t.n_k;
+    int32_t* out = a.t.idx + ((size_t)b * a.t.idx_rows + a.t.idx_row0 + r) * k;
+    const int jt = j0 + E * threadIdx.x;
+    uint32_t key[E];
+    bool ok[E];
+#pragma unroll
+    for (int e = 0; e < E; e += 4) load4<VEC>(row, jt + e, j1, key + e, ok + e);
+    uint32_t cntl = 0;
+    bool sel[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        sel[e] = ok[e] && (key[e] > T || (key[e] == T && (uint32_t)(jt + e) <= jT));
+        cntl += sel[e] ? 1u : 0u;
+    }
+    uint32_t tot;
+    uint32_t o = off + block_excl_scan<CH_NT>(cntl, wsum, &tot);
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        if (sel[e]) {
+            if (o < (uint32_t)k) out[o] = jt + e;
+            ++o;
+        }
+}
+
 }  // namespace
 
-hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
-    const long long nb = (long long)a.B * a.rows;
-    if (nb <= 0) return hipSuccess;
-    if (nb > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    const bool vec = (a.n_k % 4 == 0) && ((reinterpret_cast<uintptr_t>(a.scores) & 15) == 0);
-    if (vec)
-        hipLaunchKernelGGL(topk_kernel<true>, dim3((unsigned)nb), dim3(NT), 0, s, a);
-    else
-        hipLaunchKernelGGL(topk_kernel<false>, dim3((unsigned)nb), dim3(NT), 0, s, a);
+bool topk_use_chunked(int B, int rows, int n_k) {
+    return (long long)B * rows <= MULTI_MAX_ROWS && n_k >= MULTI_MIN_KEYS;
+}
+
+size_t topk_ws_bytes(int B, int rows, int n_k) {
+    if (!topk_use_chunked(B, rows, n_k)) return 0;
+    size_t total = 0;
+    carve(nullptr, B * rows, (n_k + CHUNK - 1) / CHUNK, &total);
+    return total;
+}
+
+uint32_t* topk_hist_ptr(void* ws) { return static_cast<uint32_t*>(ws); }
+
+hipError_t launch_topk_prepare(const TopkArgs& t, void* ws, hipStream_t s) {
+    MultiArgs a{t, carve(ws, t.B * t.rows, (t.n_k + CHUNK - 1) / CHUNK, nullptr),
+                (t.n_k + CHUNK - 1) / CHUNK};
+    const long long total = (long long)t.B * t.rows * BINS;
+    const unsigned nb = (unsigned)min(1024LL, (total + 255) / 256);
+    hipLaunchKernelGGL(topk_prepare_kernel, dim3(nb), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_topk(const TopkArgs& t, hipStream_t s) {
+    const long long rows = (long long)t.B * t.rows;
+    if (rows <= 0) return hipSuccess;
+    if (rows > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    const bool vec = (t.n_k % 4 == 0) && ((reinterpret_cast<uintptr_t>(t.scores) & 15) == 0);
+    if (!topk_use_chunked(t.B, t.rows, t.n_k)) {
+        if (vec)
+            hipLaunchKernelGGL(topk_row_kernel<true>, dim3((unsigned)rows), dim3(ROW_NT), 0, s, t);
+        else
+            hipLaunchKernelGGL(topk_row_kernel<false>, dim3((unsigned)rows), dim3(ROW_NT), 0, s, t);
+        return hipGetLastError();
+    }
+    if (!t.ws) return hipErrorInvalidValue;
+    const int nch = (t.n_k + CHUNK - 1) / CHUNK;
+    MultiArgs a{t, carve(t.ws, t.B * t.rows, nch, nullptr), nch};
+    hipError_t e;
+    if (!t.hist_ready) {
+        if ((e = launch_topk_prepare(t, t.ws, s)) != hipSuccess) return e;
+        if (vec)
+            hipLaunchKernelGGL(topk_hist_kernel<true>, dim3((unsigned)(rows * nch)), dim3(CH_NT),
+                               0, s, a);
+        else
+            hipLaunchKernelGGL(topk_hist_kernel<false>, dim3((unsigned)(rows * nch)), dim3(CH_NT),
+                               0, s, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if (vec) {
+        hipLaunchKernelGGL(topk_select_a_kernel<true>, dim3((unsigned)(rows * nch)), dim3(CH_NT),
+                           0, s, a);
+        hipLaunchKernelGGL(topk_select_b_kernel<true>, dim3((unsigned)rows), dim3(SB_NT), 0, s, a);
+        hipLaunchKernelGGL(topk_out_kernel<true>, dim3((unsigned)(rows * nch)), dim3(CH_NT), 0, s,
+                           a);
+    } else {
+        hipLaunchKernelGGL(topk_select_a_kernel<false>, dim3((unsigned)(rows * nch)), dim3(CH_NT),
+                           0, s, a);
+        hipLaunchKernelGGL(topk_select_b_kernel<false>, dim3((unsigned)rows), dim3(SB_NT), 0, s,
+                           a);
+        hipLaunchKernelGGL(topk_out_kernel<false>, dim3((unsigned)(rows * nch)), dim3(CH_NT), 0,
+                           s, a);
+    }
     return hipGetLastError();
 }
 

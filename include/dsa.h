@@ -25,7 +25,8 @@
  *     any error nothing is enqueued and a negative dsa_status is returned,
  *     with a sentence in dsa_last_error(). A failed HIP launch returns
  *     DSA_E_HIP. Device faults surface at the caller's synchronisation.
- *   - No call blocks the host or synchronises the stream.
+ *   - No call blocks the host or synchronises the stream, except the
+ *     profiling variant dsa_forward_timed.
  */
 #ifndef DSA_H
 #define DSA_H
@@ -123,6 +124,20 @@ dsa_status dsa_forward(const dsa_problem* p, const void* q_idx,
                        const void* k_idx, const void* Q, const void* K,
                        const void* V, int32_t* idx_out, void* O, float* lse,
                        void* ws, size_t ws_bytes, void* stream);
+
+/* dsa_forward for profiling: the same work and results, plus the device time
+ * of each stage. HIP events are recorded on `stream` around the indexer
+ * kernel, the top-k kernels and the attention kernels of every row slab; the
+ * call then waits for the stream (it blocks the calling thread, unlike
+ * dsa_forward) and writes the milliseconds spent in each stage, summed over
+ * slabs, to stage_ms[0] (indexer), stage_ms[1] (top-k) and stage_ms[2]
+ * (attention), and the number of row slabs (indexer launches) to *n_slabs
+ * (optional). stage_ms must not be NULL. */
+dsa_status dsa_forward_timed(const dsa_problem* p, const void* q_idx,
+                             const void* k_idx, const void* Q, const void* K,
+                             const void* V, int32_t* idx_out, void* O,
+                             float* lse, void* ws, size_t ws_bytes,
+                             void* stream, float* stage_ms, int32_t* n_slabs);
 
 /* Static name of a status code. */
 const char* dsa_status_str(int32_t status);

@@ -101,6 +101,15 @@ def test_attention_workspace_only_when_split():
     p = dsa.make_problem(pre.batch, pre.n_q, pre.n_k, pre.q_pos0, pre.d_idx, pre.idx_dtype,
                          pre.top_k, pre.n_heads)
     assert dsa.workspace_size(p, dsa.OP_ATTN) == 0
+
+
+def test_topk_workspace_only_for_long_rows():
+    # few long rows use the chunked schedule, which needs a workspace
+    dec = synth.WORKLOADS["decode_128k_clustered"]
+    p = dsa.make_problem(dec.batch, dec.n_q, dec.n_k, dec.q_pos0, dec.d_idx, dec.idx_dtype,
+                         dec.top_k, dec.n_heads)
+    assert dsa.workspace_size(p, dsa.OP_TOPK) > 0
+    p = dsa.make_problem(4, 1, 4000, 3999, 128, "fp8", 64, 1)
     assert dsa.workspace_size(p, dsa.OP_TOPK) == 0
 
 

@@ -58,6 +58,14 @@ SMALL = [
     Workload("single_key", "decode", 1, 1, 1, 0, 32, "fp8", 1, 1),
     Workload("topk_above_len_bf16_d256", "prefill", 2, 70, 70, 0, 256, "bf16", 4096, 4),
     Workload("prefill_d192_k1", "prefill", 1, 130, 130, 0, 192, "fp8", 1, 5),
+    # long decode rows: chunked top-k with the histogram built by the indexer
+    Workload("decode_chunked_20k", "decode", 3, 1, 20000, 19999, 128, "fp8", 2048, 16),
+    Workload("decode_chunked_odd_len", "decode", 2, 1, 16390, 16389, 96, "fp8", 700, 8),
+    Workload("decode_chunked_clustered", "decode", 2, 1, 40000, 39999, 128, "fp8", 1500, 16,
+             clustered=True),
+    Workload("decode_chunked_bf16", "decode", 2, 1, 9000, 8999, 160, "bf16", 4096, 4),
+    # a few long query rows (chunked top-k with its own histogram pass)
+    Workload("chunked_prefill_long", "prefill", 2, 9, 12000, 11991, 64, "fp8", 333, 2),
 ]
 
 
@@ -84,7 +92,7 @@ def test_topk_bit_exact_on_oracle_scores(gpu_lib, w):
     assert np.array_equal(got, ref)
 
 
-@pytest.mark.parametrize("n_k", [1000, 4097, 9999])
+@pytest.mark.parametrize("n_k", [1000, 4097, 9999, 20000])
 @pytest.mark.parametrize("levels", [1, 3, 40, 0])
 @pytest.mark.parametrize("k", [1, 7, 600])
 def test_topk_ties_and_ragged_rows(gpu_lib, n_k, levels, k):
@@ -164,6 +172,23 @@ def test_forward_small_vs_oracle(gpu_lib, w):
                                  w.top_k)
     assert torch.equal(idx, idx2) and torch.equal(O.view(torch.int16), O2.view(torch.int16))
     assert torch.equal(lse, lse2)
+
+
+@pytest.mark.parametrize("n_k", [20000, 20001])
+def test_decode_all_zero_query_overflows_candidates(gpu_lib, n_k):
+    # every score is 0: the threshold bin holds the whole row, more than the
+    # chunked schedule's candidate list, so the row falls back to the
+    # per-row schedule; the k lowest indices win
+    w = Workload("zeros_decode", "decode", 3, 1, n_k, n_k - 1, 128, "fp8", 300, 2)
+    x = synth.make_inputs(w, seed=7)
+    x["q_idx"][1] = 0
+    d = to_dev(x)
+    idx, O, lse = dsa.forward(d["q_idx"], d["k_idx"], d["Q"], d["K"], d["V"], w.q_pos0, 300)
+    idx_ref, O_ref, lse_ref = oracle.forward(x["q_idx"], x["k_idx"], x["Q"], x["K"], x["V"],
+                                             w.q_pos0, 300)
+    assert np.array_equal(idx.cpu().numpy(), idx_ref)
+    assert list(idx_ref[1, 0]) == list(range(300))
+    assert_attn_close(O, O_ref, lse, lse_ref, "zeros decode")
 
 
 def test_all_zero_query_selects_first_keys(gpu_lib):
@@ -252,3 +277,26 @@ def test_full_prefill_batch2_many_slabs(gpu_lib):
     # two sequences, several score slabs per forward call
     w = Workload("prefill_b2_40k", "prefill", 2, 40000, 40000, 0, 128, "fp8", 1024, 16)
     run_full(w, [(0, 2), (1022, 1026), (6550, 6560), (13107, 13110), (39998, 40000)])
+
+
+@pytest.mark.parametrize("name", ["decode_chunked_20k", "prefill_1k"])
+def test_forward_timed_matches_forward(gpu_lib, name):
+    w = [s for s in SMALL if s.name == name][0]
+    x = to_dev(synth.make_inputs(w, seed=8))
+    p = dsa.make_problem(w.batch, w.n_q, w.n_k, w.q_pos0, w.d_idx, w.idx_dtype, w.top_k,
+                         w.n_heads)
+    fwd = dsa.Forward(p, "cuda")
+    outs = []
+    for timed in (False, True):
+        O = torch.empty_like(x["Q"])
+        idx = torch.empty((w.batch, w.n_q, w.top_k), dtype=torch.int32, device="cuda")
+        lse = torch.empty((w.batch, w.n_q, w.n_heads), dtype=torch.float32, device="cuda")
+        if timed:
+            ms, slabs = fwd.timed(x["q_idx"], x["k_idx"], x["Q"], x["K"], x["V"], O, idx, lse)
+            assert slabs == 1 and all(t > 0 for t in ms), ms
+        else:
+            fwd(x["q_idx"], x["k_idx"], x["Q"], x["K"], x["V"], O, idx, lse)
+        torch.cuda.synchronize()
+        outs.append((idx, O, lse))
+    assert torch.equal(outs[0][0], outs[1][0])
+    assert torch.equal(outs[0][1].view(torch.int16), outs[1][1].view(torch.int16))
