@@ -33,20 +33,28 @@ template <int DT, int D> struct Frag;
 
 // fp8 e4m3fn row fragment: NB chunks of 128 bytes (32 per lane) and NS
 // chunks of 32 bytes (8 per lane).
+// NT selects nontemporal loads (rows streamed once from HBM).
+template <bool NT, typename T>
+__device__ __forceinline__ T ld(const T* p) {
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+
 template <int D> struct Frag<0, D> {
     static constexpr int NB = D / 128, NS = (D % 128) / 32;
     i32x8 big[NB > 0 ? NB : 1];
     long small[NS > 0 ? NS : 1];
+    template <bool NT = false>
     __device__ __forceinline__ void load(const uint8_t* row, int g) {
 #pragma unroll
         for (int c = 0; c < NB; ++c) {
             const i32x4* p = reinterpret_cast<const i32x4*>(row + 128 * c + 32 * g);
-            i32x4 lo = p[0], hi = p[1];
+            i32x4 lo = ld<NT>(p), hi = ld<NT>(p + 1);
             big[c] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         }
 #pragma unroll
         for (int c = 0; c < NS; ++c)
-            small[c] = *reinterpret_cast<const long*>(row + 128 * NB + 32 * c + 8 * g);
+            small[c] = ld<NT>(reinterpret_cast<const long*>(row + 128 * NB + 32 * c + 8 * g));
     }
 };
 
@@ -54,10 +62,13 @@ template <int D> struct Frag<0, D> {
 template <int D> struct Frag<1, D> {
     static constexpr int NC = D / 32;
     bf16x8 v[NC];
+    template <bool NT = false>
     __device__ __forceinline__ void load(const uint8_t* row, int g) {
 #pragma unroll
-        for (int c = 0; c < NC; ++c)
-            v[c] = *reinterpret_cast<const bf16x8*>(row + 64 * c + 16 * g);
+        for (int c = 0; c < NC; ++c) {
+            const i32x4 w = ld<NT>(reinterpret_cast<const i32x4*>(row + 64 * c + 16 * g));
+            v[c] = __builtin_bit_cast(bf16x8, w);
+        }
     }
 };
 
@@ -72,6 +83,44 @@ __device__ __forceinline__ f32x4 tile_dot(const Frag<0, D>& a, const Frag<0, D>&
     for (int c = 0; c < Frag<0, D>::NS; ++c)
         acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a.small[c], b.small[c], acc, 0, 0, 0);
     return acc;
+}
+
+// The same fp8 product through v_mfma_f32_16x16x32_fp8_fp8 only (the 32-byte
+// chunks split into four 8-byte steps, the pairing of bytes unchanged).
+template <int D>
+__device__ __forceinline__ f32x4 tile_dot_k32(const Frag<0, D>& a, const Frag<0, D>& b) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < Frag<0, D>::NB; ++c) {
+        const long* pa = reinterpret_cast<const long*>(&a.big[c]);
+        const long* pb = reinterpret_cast<const long*>(&b.big[c]);
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(pa[s], pb[s], acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int c = 0; c < Frag<0, D>::NS; ++c)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a.small[c], b.small[c], acc, 0, 0, 0);
+    return acc;
+}
+
+template <int D>
+__device__ __forceinline__ f32x4 tile_dot_k32(const Frag<1, D>& a, const Frag<1, D>& b) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < Frag<1, D>::NC; ++c)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v[c], b.v[c], acc, 0, 0, 0);
+    return acc;
+}
+
+// Wait states before reading the accumulators of the scaled 16x16x128 fp8
+// MFMA: reads the scheduler places a few cycles after the instruction have
+// returned incomplete rows 8..15, so the results are read only after this
+// padding, with no instruction allowed to move across it.
+__device__ __forceinline__ void mfma_drain() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 template <int D>
@@ -151,6 +200,9 @@ __global__ __launch_bounds__(256) void index_scores_kernel(IndexArgs a) {
             fb.load(kbase + (size_t)kr * RB, g);
             acc[t] = tile_dot<D>(fa, fb);
         }
+        if constexpr (DT == 0) {
+            if constexpr (Frag<0, D>::NB > 0) mfma_drain();
+        }
         // Output tile layout: lane holds rows 4g + r, key column m.
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -188,11 +240,122 @@ __global__ __launch_bounds__(256) void index_scores_kernel(IndexArgs a) {
     }
 }
 
+// One query row per sequence (decode). The 16 keys of a tile are the MFMA's
+// row operand and the query is broadcast to all 16 columns, so every lane
+// (column n, lane group g) ends up with the scores of keys 4g..4g+3 of the
+// tile. A wave loads all TILES key tiles of a step before its first MFMA
+// (TILES x 2 KiB in flight for d = 128 fp8), then lanes n < TILES pick tile
+// n's four scores and store them as one float4: the step's 16*TILES scores
+// leave as one contiguous store. With HIST the same lanes add the scores'
+// digit-1 radix to an LDS histogram that is flushed into the sequence's row
+// histogram at the end.
+template <int DT, int D, int TILES, int STEPS, bool HIST>
+__global__ __launch_bounds__(256) void index_decode_kernel(IndexArgs a) {
+    static_assert(TILES == 8, "the tile pick below assumes 8 tiles per step");
+    __shared__ uint32_t lhist[HIST ? topk::BINS : 1];
+    if (HIST) {
+        for (int i = threadIdx.x; i < topk::BINS; i += 256) lhist[i] = 0u;
+        __syncthreads();
+    }
+    constexpr int ES = DT == 0 ? 1 : 2;
+    constexpr int RB = D * ES;
+    constexpr int KW = 16 * TILES * STEPS;  // keys per wave
+    constexpr int KB = 4 * KW;              // keys per workgroup
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n = lane & 15, g = lane >> 4;
+    const int n_kb = (a.n_k + KB - 1) / KB;
+    const int kb = blockIdx.x % n_kb, b = blockIdx.x / n_kb;
+    // The one row of this sequence: query q_begin at position pos.
+    const long long pos = (long long)a.q_pos0 + a.q_begin;
+    const int lim = (int)min((long long)a.n_k, pos + 1);  // keys < lim are scored
+    const float ninf = -__builtin_inff();
+    float* const out = a.scores + (size_t)b * a.n_k;
+
+    Frag<DT, D> fq;
+    fq.load(static_cast<const uint8_t*>(a.q) + ((size_t)b * a.n_q + a.q_begin) * RB, g);
+    const uint8_t* __restrict__ kbase =
+        static_cast<const uint8_t*>(a.k) + (size_t)b * a.n_k * RB;
+    const int sel = n & (TILES - 1);
+    const bool writer = n < TILES;
+
+    // Scores of every step stay in registers until the wave has issued its
+    // last load: on this hardware stores share the load counter, so a store
+    // issued between steps would make the next step's load waits also wait
+    // for the store to complete.
+    float sc[STEPS][4];
+    int key0s[STEPS];
+#pragma unroll
+    for (int st = 0; st < STEPS; ++st) {
+        const int k0 = kb * KB + wave * KW + st * 16 * TILES;
+        key0s[st] = k0 + 16 * sel + 4 * g;
+        if (k0 >= a.n_k) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sc[st][r] = ninf;
+            continue;
+        }
+        Frag<DT, D> fk[TILES];
+#pragma unroll
+        for (int t = 0; t < TILES; ++t)
+            fk[t].template load<true>(kbase + (size_t)min(k0 + 16 * t + n, a.n_k - 1) * RB, g);
+        // Keep every load of the step ahead of the first MFMA (the scheduler
+        // would otherwise recycle two fragments and expose the latency).
+        __builtin_amdgcn_sched_barrier(0);
+        f32x4 acc[TILES];
+#pragma unroll
+        for (int t = 0; t < TILES; ++t) acc[t] = tile_dot_k32<D>(fk[t], fq);
+        // Lane picks tile `sel` (three levels of selects on n's bits).
+        f32x4 v01 = (sel & 1) ? acc[1] : acc[0];
+        f32x4 v23 = (sel & 1) ? acc[3] : acc[2];
+        f32x4 v45 = (sel & 1) ? acc[5] : acc[4];
+        f32x4 v67 = (sel & 1) ? acc[7] : acc[6];
+        f32x4 v03 = (sel & 2) ? v23 : v01;
+        f32x4 v47 = (sel & 2) ? v67 : v45;
+        f32x4 v = (sel & 4) ? v47 : v03;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            sc[st][r] = key0s[st] + r < lim ? relu_scaled(v[r], a.scale) : ninf;
+    }
+#pragma unroll
+    for (int st = 0; st < STEPS; ++st) {
+        const int key0 = key0s[st];
+        if (writer && key0 + 3 < a.n_k && (a.write_masked || key0 + 3 < lim)) {
+            *reinterpret_cast<float4*>(out + key0) =
+                make_float4(sc[st][0], sc[st][1], sc[st][2], sc[st][3]);
+        } else if (writer) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (key0 + r < a.n_k && (a.write_masked || key0 + r < lim)) out[key0 + r] = sc[st][r];
+        }
+        if (HIST) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                topk::hist_add(lhist, topk::rank_key(sc[st][r]) >> topk::SHIFT1,
+                               writer && key0 + r < lim);
+        }
+    }
+    if (HIST) {
+        __syncthreads();
+        uint32_t* gh = a.hist + (size_t)b * topk::BINS;
+        for (int i = threadIdx.x; i < topk::BINS; i += 256)
+            if (lhist[i]) atomicAdd(&gh[i], lhist[i]);
+    }
+}
+
 template <int DT, int D>
 hipError_t launch_dt_d(const IndexArgs& a, hipStream_t s) {
     const int rows = a.q_end - a.q_begin;
     if (a.hist && rows != 1) return hipErrorInvalidValue;
-    if (rows <= 16) {
+    if (rows == 1) {
+        constexpr int TILES = 8, STEPS = 2, KB = 4 * 16 * TILES * STEPS;
+        const long long nb = (long long)a.B * ((a.n_k + KB - 1) / KB);
+        if (nb > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+        if (a.hist)
+            hipLaunchKernelGGL((index_decode_kernel<DT, D, TILES, STEPS, true>),
+                               dim3((unsigned)nb), dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL((index_decode_kernel<DT, D, TILES, STEPS, false>),
+                               dim3((unsigned)nb), dim3(256), 0, s, a);
+    } else if (rows <= 16) {
         // Few queries per sequence (decode): the 4 waves split the keys.
         constexpr int QB = 16, KB = 1024;
         const long long nb = (long long)a.B * ((rows + QB - 1) / QB) * ((a.n_k + KB - 1) / KB);
