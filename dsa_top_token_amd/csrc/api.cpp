@@ -94,12 +94,15 @@ int slab_rows(const dsa_problem* p) {
     return (int)r;
 }
 
+// Attention workspace: per-(row, split) partials (none when every row is
+// handled by one wave).
 size_t attn_ws_bytes(const dsa_problem* p) {
     int ns, len;
     dsa::attn_split_plan(p->batch, p->n_q, p->top_k, &ns, &len);
-    if (ns <= 1) return 0;
+    if ((long long)p->batch * p->n_q >= 2048) return 0;
     return align_up((size_t)p->batch * p->n_q * ns * kPartFloats * sizeof(float));
 }
+
 
 // Workspace of dsa_topk: the chunked schedule's buffers for the largest row
 // slab that uses it (the schedule is chosen by batch * rows, so smaller slabs
@@ -123,7 +126,11 @@ ForwardLayout forward_layout(const dsa_problem* p) {
     L.idx = sb;
     const size_t ib = align_up((size_t)p->batch * p->n_q * p->top_k * sizeof(int32_t));
     L.topk = L.idx + ib;
-    const size_t tb = align_up(dsa::topk_ws_bytes(p->batch, R, p->n_k));
+    size_t tb = align_up(dsa::topk_ws_bytes(p->batch, R, p->n_k));
+    if (dsa::decode_select_applies(R, p->n_k, p->top_k)) {
+        const size_t db = align_up(dsa::decode_select_ws_bytes(p->batch, p->n_k));
+        tb = db > tb ? db : tb;
+    }
     L.part = L.topk + tb;
     L.total = L.part + attn_ws_bytes(p);
     return L;
@@ -227,6 +234,37 @@ dsa_status forward_impl(const dsa_problem* p, const void* q_idx, const void* k_i
         ta.rows = r1 - r0;
         ta.pos_begin = (long long)p->q_pos0 + r0;
         ta.idx_row0 = r0;
+        if (dsa::decode_select_applies(ta.rows, p->n_k, p->top_k)) {
+            // One query row per sequence: sampled threshold, indexer that
+            // keeps only candidates, exact select; no score row is written.
+            dsa::DecodeArgs da{};
+            da.q = q_idx;
+            da.k = k_idx;
+            da.idx = idx;
+            da.B = p->batch;
+            da.n_q = p->n_q;
+            da.n_k = p->n_k;
+            da.q_pos0 = p->q_pos0;
+            da.d = p->d_idx;
+            da.dtype = p->idx_dtype;
+            da.top_k = p->top_k;
+            da.q_row = r0;
+            da.idx_rows = p->n_q;
+            da.idx_row0 = r0;
+            da.scale = index_scale(p->d_idx);
+            da.fallback = scores;
+            hipError_t e = hipSuccess;
+            if (tm) tm->mark(1);
+            if ((e = dsa::launch_decode_select(da, ta.ws, 0, st)) != hipSuccess)
+                return hip_fail(e, "decode threshold launch");
+            if (tm) tm->mark(0);
+            if ((e = dsa::launch_decode_select(da, ta.ws, 1, st)) != hipSuccess)
+                return hip_fail(e, "decode indexer launch");
+            if (tm) tm->mark(1);
+            if ((e = dsa::launch_decode_select(da, ta.ws, 2, st)) != hipSuccess)
+                return hip_fail(e, "decode select launch");
+            continue;
+        }
         // One query per sequence on the chunked top-k schedule: the indexer
         // kernel builds the row histograms the selection starts from.
         const bool fuse = ta.rows == 1 && dsa::topk_use_chunked(p->batch, 1, p->n_k);

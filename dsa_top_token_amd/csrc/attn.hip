@@ -47,23 +47,24 @@ __device__ __forceinline__ float wave_xor_sum(float v) {
     return v;
 }
 
-template <bool SPLIT>
-__global__ __launch_bounds__(256) void sparse_attn_kernel(AttnArgs a) {
-    __shared__ unsigned short vs[4][32][LROW];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// One wave's pass over selected-key slots e = e_first, e_first + e_step, ...
+// (32 slots each, all below e_end) of query row qrow: online softmax state
+// (running max in the log2 domain, this lane's partial sum) and the
+// unnormalised O^T tiles: lane (head m, group g) holds dims 16d + 4g + r.
+struct WaveState {
+    f32x4 o[8];
+    float mrun, lpart;
+};
+
+__device__ __forceinline__ void wave_attend(const AttnArgs& a, long long qrow, int e_first,
+                                            int e_end, int e_step,
+                                            unsigned short (*lv)[LROW], WaveState& ws) {
+    const int lane = threadIdx.x & 63;
     const int m = lane & 15, g = lane >> 4;
-    const long long task = (long long)blockIdx.x * 4 + wave;
-    const long long n_tasks = (long long)a.B * a.n_q * a.n_split;
-    if (task >= n_tasks) return;  // no workgroup barrier below
-    const int split = (int)(task % a.n_split);
-    const long long qrow = task / a.n_split;  // b * n_q + i
     const int b = (int)(qrow / a.n_q);
-    const int e0 = split * a.split_len;
-    const int e1 = min(a.k, e0 + a.split_len);
     const int32_t* sel = a.idx + qrow * (long long)a.k;
     const uint16_t* Kb = a.K + (size_t)b * a.n_k * HD;
     const uint16_t* Vb = a.V + (size_t)b * a.n_k * HD;
-    unsigned short(*lv)[LROW] = vs[wave];
 
     // Q^T fragment: lane (head m, group g) holds Q[m][32g + 8s .. +8] for s = 0..3,
     // matching the K fragment's dims below.
@@ -77,14 +78,15 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(AttnArgs a) {
         for (int s = 0; s < 4; ++s) qf[s] = as_bf16x8(u16x8{0, 0, 0, 0, 0, 0, 0, 0});
     }
 
-    f32x4 o[8];
 #pragma unroll
-    for (int d = 0; d < 8; ++d) o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int d = 0; d < 8; ++d) ws.o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
     const float ninf = -__builtin_inff();
-    float mrun = ninf, lpart = 0.f;
+    ws.mrun = ninf;
+    ws.lpart = 0.f;
     const float sl2 = 0.08838834764831845f * kLog2e;  // 128^-0.5 * log2(e)
+    const int e1 = e_end;
 
-    for (int e = e0; e < e1; e += 32) {
+    for (int e = e_first; e < e1; e += e_step) {
         // Key rows gathered by this lane: slot 16t + m, dims [32g, 32g + 32).
         int jr[2];
         bool vr[2];
@@ -143,19 +145,19 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int i = 1; i < 8; ++i) mx = fmaxf(mx, z[i]);
         mx = wave_xor_max(mx);
-        const float mnew = fmaxf(mrun, mx);
+        const float mnew = fmaxf(ws.mrun, mx);
         const bool live = mnew != ninf;
-        const float alpha = live ? exp2f(mrun - mnew) : 1.f;
+        const float alpha = live ? exp2f(ws.mrun - mnew) : 1.f;
         float p[8], psum = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             p[i] = live ? exp2f(z[i] - mnew) : 0.f;
             psum += p[i];
         }
-        lpart = lpart * alpha + psum;
-        mrun = mnew;
+        ws.lpart = ws.lpart * alpha + psum;
+        ws.mrun = mnew;
 #pragma unroll
-        for (int d = 0; d < 8; ++d) o[d] *= alpha;
+        for (int d = 0; d < 8; ++d) ws.o[d] *= alpha;
         bf16x8 pb;
 #pragma unroll
         for (int i = 0; i < 8; ++i) pb[i] = (__bf16)p[i];
@@ -173,109 +175,163 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(AttnArgs a) {
                 const int key = i < 4 ? 4 * g + i : 12 + 4 * g + i;
                 va[i] = lv[key][16 * d + m];
             }
-            o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va), pb, o[d], 0, 0, 0);
+            ws.o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va), pb, ws.o[d], 0, 0, 0);
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 
-    const float l = wave_xor_sum(lpart);
+}
+
+// One wave per query row (many queries): normalised O and lse directly.
+__global__ __launch_bounds__(256) void sparse_attn_kernel(AttnArgs a) {
+    __shared__ unsigned short vs[4][32][LROW];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int m = lane & 15, g = lane >> 4;
+    const long long qrow = (long long)blockIdx.x * 4 + wave;
+    if (qrow >= (long long)a.B * a.n_q) return;  // no workgroup barrier below
+    WaveState ws;
+    wave_attend(a, qrow, 0, a.k, 32, vs[wave], ws);
+    const float l = wave_xor_sum(ws.lpart);
     if (m >= a.H) return;
-    if (!SPLIT) {
-        const float inv = l > 0.f ? 1.f / l : 0.f;
-        uint16_t* op = a.O + (qrow * a.H + m) * HD;
+    const float ninf = -__builtin_inff();
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    uint16_t* op = a.O + (qrow * a.H + m) * HD;
 #pragma unroll
-        for (int d = 0; d < 8; ++d) {
-            bf16x4 h4;
+    for (int d = 0; d < 8; ++d) {
+        bf16x4 h4;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) h4[r] = (__bf16)(o[d][r] * inv);
-            *reinterpret_cast<uint2*>(op + 16 * d + 4 * g) = __builtin_bit_cast(uint2, h4);
+        for (int r = 0; r < 4; ++r) h4[r] = (__bf16)(ws.o[d][r] * inv);
+        *reinterpret_cast<uint2*>(op + 16 * d + 4 * g) = __builtin_bit_cast(uint2, h4);
+    }
+    if (a.lse && g == 0) a.lse[qrow * a.H + m] = l > 0.f ? (ws.mrun + log2f(l)) * kLn2 : ninf;
+}
+
+// Few query rows: a 4-wave workgroup per (query, split). Waves take every
+// fourth 32-slot step of the split and merge in LDS; each workgroup writes its
+// split's partial (max, sum, unnormalised O per head) for the combine kernel.
+__global__ __launch_bounds__(256) void sparse_attn_split_kernel(AttnArgs a) {
+    __shared__ float lds[4 * 32 * LROW / 2];  // V staging, then the merge buffer
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int m = lane & 15, g = lane >> 4;
+    const int split = (int)(blockIdx.x % (unsigned)a.n_split);
+    const long long qrow = blockIdx.x / (unsigned)a.n_split;
+    const int e0 = split * a.split_len;
+    const int e1 = min(a.k, e0 + a.split_len);
+    const float ninf = -__builtin_inff();
+    unsigned short(*vstage)[32][LROW] = reinterpret_cast<unsigned short(*)[32][LROW]>(lds);
+    WaveState ws;
+    wave_attend(a, qrow, e0 + 32 * wave, e1, 128, vstage[wave], ws);
+    const float lw = wave_xor_sum(ws.lpart);
+    __syncthreads();  // V staging no longer needed
+    // merge buffer: [wave][head][PART] with O[128], max, sum
+    float* mb = lds;
+    float* mine = mb + ((size_t)wave * 16 + m) * PART;
+#pragma unroll
+    for (int d = 0; d < 8; ++d)
+        *reinterpret_cast<float4*>(mine + 16 * d + 4 * g) =
+            make_float4(ws.o[d][0], ws.o[d][1], ws.o[d][2], ws.o[d][3]);
+    if (g == 0) {
+        mine[HD] = ws.mrun;
+        mine[HD + 1] = lw;
+    }
+    __syncthreads();
+    // thread t: head h = t / 16, dims 8c .. 8c + 7 with c = t % 16
+    const int h = threadIdx.x >> 4, c = threadIdx.x & 15;
+    float M = ninf;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, mb[((size_t)w * 16 + h) * PART + HD]);
+    float L = 0.f, acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+    if (M != ninf) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const float* src = mb + ((size_t)w * 16 + h) * PART;
+            const float sc = exp2f(src[HD] - M);
+            L += sc * src[HD + 1];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] += sc * src[8 * c + i];
         }
-        if (a.lse && g == 0) a.lse[qrow * a.H + m] = l > 0.f ? (mrun + log2f(l)) * kLn2 : ninf;
-    } else {
-        float* pp = a.part + ((size_t)task * 16 + m) * PART;
+    }
+    float* pp = a.part + ((size_t)blockIdx.x * 16 + h) * PART;
 #pragma unroll
-        for (int d = 0; d < 8; ++d)
-            *reinterpret_cast<float4*>(pp + 16 * d + 4 * g) =
-                make_float4(o[d][0], o[d][1], o[d][2], o[d][3]);
-        if (g == 0) {
-            pp[HD] = mrun;
-            pp[HD + 1] = l;
-        }
+    for (int i = 0; i < 8; i += 4)
+        *reinterpret_cast<float4*>(pp + 8 * c + i) =
+            make_float4(acc[i], acc[i + 1], acc[i + 2], acc[i + 3]);
+    if (c == 0) {
+        pp[HD] = M;
+        pp[HD + 1] = L;
     }
 }
 
-// Merge of split partials: one wave per (query, head); lane l owns dims
-// 2l, 2l+1. Every split's (max, sum) pair is read first, then the rescaled
-// partial outputs are summed.
+// Merge of the split partials of one query row per workgroup: thread t takes
+// head t / 16 and dims 8 * (t % 16) .. +8.
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
-    const int lane = threadIdx.x & 63;
-    const long long qh = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (qh >= (long long)a.B * a.n_q * a.H) return;
-    const int h = (int)(qh % a.H);
-    const long long qrow = qh / a.H;
+    const long long qrow = blockIdx.x;
+    const int h = threadIdx.x >> 4, c = threadIdx.x & 15;
+    if (h >= a.H) return;
     const float ninf = -__builtin_inff();
-    const float* base = a.part + (size_t)qrow * a.n_split * 16 * PART + (size_t)h * PART;
+    const float* base = a.part + ((size_t)qrow * a.n_split * 16 + h) * PART;
     const size_t stride = (size_t)16 * PART;
-    // lanes read the split statistics in parallel (n_split <= 64 per pass)
-    float M = ninf;
-    for (int s0 = 0; s0 < a.n_split; s0 += 64) {
-        const int s = s0 + lane;
-        const float ms = s < a.n_split ? base[(size_t)s * stride + HD] : ninf;
-        M = fmaxf(M, ms);
-    }
+    float MM = ninf;
+    for (int s = 0; s < a.n_split; ++s) MM = fmaxf(MM, base[(size_t)s * stride + HD]);
+    float LL = 0.f, o8[8];
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-    float L = 0.f, o0 = 0.f, o1 = 0.f;
-    if (M != ninf) {
+    for (int i = 0; i < 8; ++i) o8[i] = 0.f;
+    if (MM != ninf) {
         for (int s = 0; s < a.n_split; ++s) {
             const float* ps = base + (size_t)s * stride;
-            const float w = exp2f(ps[HD] - M);
-            L += w * ps[HD + 1];
-            const float2 v = *reinterpret_cast<const float2*>(ps + 2 * lane);
-            o0 += w * v.x;
-            o1 += w * v.y;
+            const float sc = exp2f(ps[HD] - MM);
+            LL += sc * ps[HD + 1];
+            const float4 v0 = *reinterpret_cast<const float4*>(ps + 8 * c);
+            const float4 v1 = *reinterpret_cast<const float4*>(ps + 8 * c + 4);
+            o8[0] += sc * v0.x; o8[1] += sc * v0.y; o8[2] += sc * v0.z; o8[3] += sc * v0.w;
+            o8[4] += sc * v1.x; o8[5] += sc * v1.y; o8[6] += sc * v1.z; o8[7] += sc * v1.w;
         }
     }
-    const float inv = L > 0.f ? 1.f / L : 0.f;
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    const bf16x2 h2 = {(__bf16)(o0 * inv), (__bf16)(o1 * inv)};
-    *reinterpret_cast<uint32_t*>(a.O + (qrow * a.H + h) * HD + 2 * lane) =
-        __builtin_bit_cast(uint32_t, h2);
-    if (a.lse && lane == 0) a.lse[qrow * a.H + h] = L > 0.f ? (M + log2f(L)) * kLn2 : ninf;
+    const float inv = LL > 0.f ? 1.f / LL : 0.f;
+    bf16x8 h8;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) h8[i] = (__bf16)(o8[i] * inv);
+    *reinterpret_cast<uint4*>(a.O + (qrow * a.H + h) * HD + 8 * c) = __builtin_bit_cast(uint4, h8);
+    if (a.lse && c == 0) a.lse[qrow * a.H + h] = LL > 0.f ? (MM + log2f(LL)) * kLn2 : ninf;
 }
 
 }  // namespace
 
 void attn_split_plan(int B, int n_q, int k, int* n_split, int* split_len) {
+    // Many rows: one wave per row. Few rows: 4-wave workgroups per (row,
+    // split), splits of a multiple of 128 slots, about 4096 waves in all.
     const long long rows = (long long)B * n_q;
-    const int max_split = (k + 63) / 64;  // at least 64 entries per split
-    long long want = (2048 + rows - 1) / rows;
+    if (rows >= 2048) {
+        *n_split = 1;
+        *split_len = k;
+        return;
+    }
+    const int max_split = (k + 127) / 128;
+    long long want = (1024 + rows - 1) / rows;
     int ns = (int)(want < 1 ? 1 : (want > max_split ? max_split : want));
-    if (ns < 1) ns = 1;
     int len = (k + ns - 1) / ns;
-    len = (len + 31) / 32 * 32;
+    len = (len + 127) / 128 * 128;
     ns = (k + len - 1) / len;
     *n_split = ns;
     *split_len = len;
 }
 
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t s) {
-    const long long tasks = (long long)a.B * a.n_q * a.n_split;
-    if (tasks <= 0) return hipSuccess;
-    const long long nb = (tasks + 3) / 4;
-    if (nb > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    if (a.n_split == 1) {
-        hipLaunchKernelGGL(sparse_attn_kernel<false>, dim3((unsigned)nb), dim3(256), 0, s, a);
+    const long long rows = (long long)a.B * a.n_q;
+    if (rows <= 0) return hipSuccess;
+    if (rows >= 2048) {
+        const long long nb = (rows + 3) / 4;
+        if (nb > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL(sparse_attn_kernel, dim3((unsigned)nb), dim3(256), 0, s, a);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL(sparse_attn_kernel<true>, dim3((unsigned)nb), dim3(256), 0, s, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const long long nc = ((long long)a.B * a.n_q * a.H + 3) / 4;
-    if (nc > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)nc), dim3(256), 0, s, a);
+    const long long nb = rows * a.n_split;
+    hipLaunchKernelGGL(sparse_attn_split_kernel, dim3((unsigned)nb), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)rows), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

@@ -1,0 +1,440 @@
+// Decode-shaped selection (one query row per sequence, long key rows) with a
+// sampled threshold, on gfx950.
+//
+// DeepSeek-V3.2 DSA page (kwkr.cn/news/60693), sections 3.2-3.3: the indexer
+// scores every key of the query's prefix and the query keeps its top_k keys.
+// Here the full score row never reaches memory:
+//   threshold  one workgroup per sequence scores every S-th key
+//              (S = max(32, ceil(n/8192))) and takes as tau the lower edge
+//              of the 22-bit radix bin holding the m-th largest order key of
+//              that sample, m = ceil(1.5 * top_k / S). About 1.5 * top_k keys
+//              of the row are expected to reach tau.
+//   filter     the streaming indexer kernel scores every key and keeps only
+//              those whose order key is >= tau, each wave writing its own
+//              (order key, index) list for its 256 keys in ascending index
+//              order (no device atomics).
+//   select     one workgroup per sequence loads the candidates into LDS,
+//              finds the exact k-th key T by radix rounds, cuts the T-ties at
+//              the index j_T that keeps the lowest indices, and writes the
+//              selection in ascending index order.
+// The result is exact whenever at least top_k keys reach tau, which select
+// checks; otherwise (or when the candidates exceed its LDS list) select
+// recomputes the row's scores into the workspace and runs the per-row radix
+// selection on them.
+#include "frag.h"
+#include "topk_common.h"
+
+namespace dsa {
+namespace {
+
+using namespace frag;
+using namespace topk;
+
+constexpr int TH_NT = 1024;
+constexpr int TH_TILES = 8;       // sample tiles a threshold wave loads at once
+constexpr int TH_MAX_SAMPLES = 8192;
+constexpr int SLOT = 256;          // keys per filter wave = one candidate list
+constexpr int SEL_NT = 512;
+constexpr int SEL_CAP = 12288;     // candidates select can hold in LDS
+constexpr int SEL_MAX_SLOTS = 4096;
+
+struct Plan {
+    int n, S, ns, m;
+};
+
+__device__ __forceinline__ Plan plan_row(const DecodeArgs& a) {
+    Plan p;
+    const long long pos = (long long)a.q_pos0 + a.q_row;
+    p.n = (int)min((long long)a.n_k, pos + 1);
+    p.S = max(32, (p.n + TH_MAX_SAMPLES - 1) / TH_MAX_SAMPLES);
+    p.ns = (p.n + p.S - 1) / p.S;
+    p.m = (3 * a.top_k + 2 * p.S - 1) / (2 * p.S);  // ceil(1.5 k / S)
+    return p;
+}
+
+// m-th largest (m >= 1) of cnt order keys held in LDS, by radix rounds on
+// 11 + 11 + 10 bits. With ROUNDS = 2 the result is the lower edge of the
+// 22-bit bin holding the m-th largest key (at least m keys are >= it).
+template <int NT, int ROUNDS = 3>
+__device__ uint32_t kth_largest(const uint32_t* keys, int cnt, uint32_t m, uint32_t* hist,
+                                uint32_t* wsum, uint32_t* res) {
+    const int tid = threadIdx.x;
+    uint32_t prefix = 0;
+    int shift_done = 32;
+    const int shifts[3] = {SHIFT1, SHIFT2, 0};
+    const uint32_t masks[3] = {2047u, 2047u, 1023u};
+#pragma unroll
+    for (int round = 0; round < ROUNDS; ++round) {
+        const int sh = shifts[round];
+        for (int i = tid; i < BINS; i += NT) hist[i] = 0u;
+        __syncthreads();
+        for (int base = 0; base < cnt; base += NT) {
+            const int i = base + tid;
+            const uint32_t key = i < cnt ? keys[i] : 0u;
+            const bool in = i < cnt && (shift_done >= 32 || (key >> shift_done) == prefix);
+            hist_add(hist, (key >> sh) & masks[round], in);
+        }
+        __syncthreads();
+        find_bin<NT>(hist, m, wsum, res);
+        prefix = (shift_done >= 32 ? 0u : prefix << (shift_done - sh)) | res[0];
+        m -= res[1];
+        shift_done = sh;
+        __syncthreads();
+    }
+    return prefix << shift_done;
+}
+
+// Scores of keys t0 + 16*0.., as order keys, for the 16 keys of one tile whose
+// row index is key(i) for tile row i; lanes with column 0 hold rows 4g..4g+3.
+template <int DT, int D>
+__device__ __forceinline__ f32x4 key_tile(const uint8_t* kbase, int key_row, const Frag<DT, D>& fq,
+                                          int g) {
+    constexpr int RB = D * (DT == 0 ? 1 : 2);
+    Frag<DT, D> fk;
+    fk.load(kbase + (size_t)key_row * RB, g);
+    return tile_dot_k32<D>(fk, fq);
+}
+
+template <int DT, int D>
+__global__ __launch_bounds__(TH_NT) void decode_threshold_kernel(DecodeArgs a) {
+    __shared__ uint32_t samp[TH_MAX_SAMPLES];
+    __shared__ uint32_t hist[BINS];
+    __shared__ uint32_t wsum[TH_NT / 64];
+    __shared__ uint32_t res[4];
+    constexpr int RB = D * (DT == 0 ? 1 : 2);
+    const int b = blockIdx.x;
+    const Plan p = plan_row(a);
+    if (p.n <= a.top_k || p.ns <= p.m) {
+        if (threadIdx.x == 0) a.tau[b] = 0u;  // every key is a candidate
+        return;
+    }
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n = lane & 15, g = lane >> 4;
+    Frag<DT, D> fq;
+    fq.load(static_cast<const uint8_t*>(a.q) + ((size_t)b * a.n_q + a.q_row) * RB, g);
+    const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + (size_t)b * a.n_k * RB;
+    // Waves take TH_TILES tiles of 16 samples at a time, all loads first.
+    for (int t0 = wave * 16 * TH_TILES; t0 < p.ns; t0 += (TH_NT / 64) * 16 * TH_TILES) {
+        Frag<DT, D> fk[TH_TILES];
+#pragma unroll
+        for (int t = 0; t < TH_TILES; ++t)
+            fk[t].load(kbase + (size_t)(min(t0 + 16 * t + n, p.ns - 1) * p.S) * RB, g);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < TH_TILES; ++t) {
+            const f32x4 acc = tile_dot_k32<D>(fk[t], fq);
+            if (n == 0) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = t0 + 16 * t + 4 * g + r;
+                    if (i < p.ns) samp[i] = rank_key(relu_scaled(acc[r], a.scale));
+                }
+            }
+        }
+    }
+    __syncthreads();
+    const uint32_t tau = kth_largest<TH_NT, 2>(samp, p.ns, (uint32_t)p.m, hist, wsum, res);
+    if (threadIdx.x == 0) a.tau[b] = tau;
+}
+
+// The streaming indexer of one query row per sequence (see index_decode_kernel
+// in indexer.hip for the tile layout), keeping only keys at or above tau.
+template <int DT, int D>
+__global__ __launch_bounds__(256) void decode_filter_kernel(DecodeArgs a) {
+    constexpr int TILES = 8, STEPS = 2;
+    constexpr int RB = D * (DT == 0 ? 1 : 2);
+    constexpr int KW = 16 * TILES * STEPS;  // = SLOT
+    constexpr int KB = 4 * KW;
+    static_assert(KW == SLOT, "one candidate list per wave");
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n = lane & 15, g = lane >> 4;
+    const int n_kb = (a.n_k + KB - 1) / KB;
+    const int kb = blockIdx.x % n_kb, b = blockIdx.x / n_kb;
+    const Plan p = plan_row(a);
+    const int lim = p.n;
+    const uint32_t tau = a.tau[b];
+    const int slot = kb * 4 + wave;
+    const int n_slots = (a.n_k + SLOT - 1) / SLOT;
+
+    Frag<DT, D> fq;
+    fq.load(static_cast<const uint8_t*>(a.q) + ((size_t)b * a.n_q + a.q_row) * RB, g);
+    const uint8_t* __restrict__ kbase =
+        static_cast<const uint8_t*>(a.k) + (size_t)b * a.n_k * RB;
+    const int sel = n & (TILES - 1);
+    const bool writer = n < TILES;
+    uint32_t sk[STEPS][4];
+    int key0s[STEPS];
+#pragma unroll
+    for (int st = 0; st < STEPS; ++st) {
+        const int k0 = kb * KB + wave * KW + st * 16 * TILES;
+        key0s[st] = k0 + 16 * sel + 4 * g;
+        if (k0 >= lim) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sk[st][r] = 0u;
+            continue;
+        }
+        Frag<DT, D> fk[TILES];
+#pragma unroll
+        for (int t = 0; t < TILES; ++t)
+            fk[t].template load<true>(kbase + (size_t)min(k0 + 16 * t + n, a.n_k - 1) * RB, g);
+        __builtin_amdgcn_sched_barrier(0);
+        f32x4 acc[TILES];
+#pragma unroll
+        for (int t = 0; t < TILES; ++t) acc[t] = tile_dot_k32<D>(fk[t], fq);
+        f32x4 v01 = (sel & 1) ? acc[1] : acc[0];
+        f32x4 v23 = (sel & 1) ? acc[3] : acc[2];
+        f32x4 v45 = (sel & 1) ? acc[5] : acc[4];
+        f32x4 v67 = (sel & 1) ? acc[7] : acc[6];
+        f32x4 v03 = (sel & 2) ? v23 : v01;
+        f32x4 v47 = (sel & 2) ? v67 : v45;
+        f32x4 v = (sel & 4) ? v47 : v03;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sk[st][r] = rank_key(relu_scaled(v[r], a.scale));
+    }
+    // Candidates of this wave into its list in ascending index order. In a
+    // step, writer lane (sel, g) holds keys k0 + 16*sel + 4*g + r, so its place
+    // in index order is p = 4*sel + g: counts are gathered into position order
+    // (lane p takes lane 16*(p%4) + p/4), scanned, and scattered back.
+    uint2* list = a.cand + ((size_t)b * n_slots + slot) * SLOT;
+    uint32_t count = 0;
+    const int src = 16 * (lane & 3) + ((lane >> 2) & 7);
+    const int myp = 4 * sel + g;
+#pragma unroll
+    for (int st = 0; st < STEPS; ++st) {
+        bool c[4];
+        uint32_t cl = 0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int j = key0s[st] + r;
+            c[r] = writer && j < lim && sk[st][r] >= tau;
+            cl += c[r] ? 1u : 0u;
+        }
+        uint32_t cp = (uint32_t)__shfl((int)cl, src);
+        if (lane >= 32) cp = 0u;
+        const uint32_t incl = wave_incl_scan(cp);
+        const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)incl, 31);
+        uint32_t o = count + (uint32_t)__shfl((int)(incl - cp), myp);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            if (c[r]) list[o++] = make_uint2(sk[st][r], (uint32_t)(key0s[st] + r));
+        count += tot;
+    }
+    if (lane == 0 && slot < n_slots) a.cnt[(size_t)b * n_slots + slot] = count;
+}
+
+// Every score of the row (order keys) into `row` (fallback path of select).
+template <int DT, int D>
+__device__ void row_scores(const DecodeArgs& a, int b, int nkeys, float* row) {
+    constexpr int RB = D * (DT == 0 ? 1 : 2);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n = lane & 15, g = lane >> 4;
+    Frag<DT, D> fq;
+    fq.load(static_cast<const uint8_t*>(a.q) + ((size_t)b * a.n_q + a.q_row) * RB, g);
+    const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + (size_t)b * a.n_k * RB;
+    for (int t0 = wave * 16; t0 < nkeys; t0 += (SEL_NT / 64) * 16) {
+        const f32x4 acc = key_tile<DT, D>(kbase, min(t0 + n, nkeys - 1), fq, g);
+        if (n == 0) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (t0 + 4 * g + r < nkeys) row[t0 + 4 * g + r] = relu_scaled(acc[r], a.scale);
+        }
+    }
+}
+
+template <int DT, int D>
+__global__ __launch_bounds__(SEL_NT) void decode_select_kernel(DecodeArgs a) {
+    // LDS: keys | idx (candidates), hist, per-slot candidate offsets, scan
+    // scratch.
+    __shared__ uint32_t keys[SEL_CAP];
+    __shared__ uint32_t jj[SEL_CAP];
+    __shared__ uint32_t hist[BINS];
+    __shared__ uint32_t soff[SEL_MAX_SLOTS + 1];
+    __shared__ uint32_t wsum[SEL_NT / 64];
+    __shared__ uint32_t res[4];
+    const int tid = threadIdx.x;
+    const int b = blockIdx.x;
+    const Plan p = plan_row(a);
+    const int k = a.top_k;
+    int32_t* out = a.idx + ((size_t)b * a.idx_rows + a.idx_row0) * k;
+    if (p.n <= k) {
+        fill_prefix(out, p.n, k, tid, SEL_NT);
+        return;
+    }
+    const int n_slots = (a.n_k + SLOT - 1) / SLOT;
+    const int used = (p.n + SLOT - 1) / SLOT;  // slots holding keys < n
+    // Candidate offsets per slot.
+    constexpr int PER = SEL_MAX_SLOTS / SEL_NT;
+    const uint32_t* gcnt = a.cnt + (size_t)b * n_slots;
+    uint32_t cv[PER], loc = 0;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+        const int s = tid * PER + e;
+        cv[e] = s < used ? gcnt[s] : 0u;
+        loc += cv[e];
+    }
+    uint32_t total;
+    uint32_t off = block_excl_scan<SEL_NT>(loc, wsum, &total);
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+        const int s = tid * PER + e;
+        if (s <= SEL_MAX_SLOTS - 1) soff[s] = off;
+        off += cv[e];
+    }
+    if (tid == 0) soff[SEL_MAX_SLOTS] = total;
+    __syncthreads();
+    if (total < (uint32_t)k || total > (uint32_t)SEL_CAP) {
+        // tau kept fewer than k keys, or more than the LDS list holds:
+        // recompute the whole row and select on it directly.
+        float* row = a.fallback + (size_t)b * a.n_k;
+        row_scores<DT, D>(a, b, p.n, row);
+        __threadfence();
+        __syncthreads();
+        row_topk<SEL_NT, SEL_CAP, false>(row, p.n, k, out, hist, keys, wsum, res);
+        return;
+    }
+    // Load every candidate (lists are in index order, slots in key order, so
+    // the LDS list is sorted by index). Thread t copies a contiguous block,
+    // eight loads in flight at a time.
+    {
+        const int E = ((int)total + SEL_NT - 1) / SEL_NT;
+        const int c0 = tid * E, c1 = min((int)total, c0 + E);
+        if (c0 < c1) {
+            int s = 0, hi = used - 1;  // last slot with soff[s] <= c0
+            while (s < hi) {
+                const int mid = (s + hi + 1) >> 1;
+                if (soff[mid] <= (uint32_t)c0) s = mid;
+                else hi = mid - 1;
+            }
+            for (int c = c0; c < c1; c += 8) {
+                uint2 v[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int cc = c + u;
+                    if (cc < c1) {
+                        while (soff[s + 1] <= (uint32_t)cc) ++s;
+                        v[u] = a.cand[((size_t)b * n_slots + s) * SLOT + (cc - soff[s])];
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    if (c + u < c1) {
+                        keys[c + u] = v[u].x;
+                        jj[c + u] = v[u].y;
+                    }
+            }
+        }
+    }
+    __syncthreads();
+    const int cnt = (int)total;
+    // Exact k-th key T and how many of its ties to keep.
+    const uint32_t T = kth_largest<SEL_NT>(keys, cnt, (uint32_t)k, hist, wsum, res);
+    uint32_t gt = 0, eq = 0;
+    for (int i = tid; i < cnt; i += SEL_NT) {
+        gt += keys[i] > T ? 1u : 0u;
+        eq += keys[i] == T ? 1u : 0u;
+    }
+    uint32_t ge;
+    block_excl_scan<SEL_NT>((gt << 16) | eq, wsum, &ge);
+    const uint32_t n_gt = ge >> 16, n_eq = ge & 0xffffu;
+    const uint32_t rem = (uint32_t)k - n_gt;  // ties to keep, >= 1
+    // Tie cut-off j_T: the rem-th smallest index among keys equal to T, found
+    // as the rem-th largest of (2^22 - 1 - j); all ties are kept if they fit.
+    constexpr uint32_t JMAX = (1u << 22) - 1u;
+    uint32_t jT = JMAX;
+    if (n_eq > rem) {
+        for (int i = tid; i < BINS; i += SEL_NT) hist[i] = 0u;
+        __syncthreads();
+        for (int base = 0; base < cnt; base += SEL_NT) {
+            const int i = base + tid;
+            const bool ok = i < cnt && keys[i] == T;
+            hist_add(hist, ok ? (JMAX - jj[i]) >> 11 : 0u, ok);
+        }
+        __syncthreads();
+        find_bin<SEL_NT>(hist, rem, wsum, res);
+        const uint32_t a1 = res[0];
+        const uint32_t remj = rem - res[1];
+        __syncthreads();
+        for (int i = tid; i < BINS; i += SEL_NT) hist[i] = 0u;
+        __syncthreads();
+        for (int base = 0; base < cnt; base += SEL_NT) {
+            const int i = base + tid;
+            const bool ok = i < cnt && keys[i] == T && ((JMAX - jj[i]) >> 11) == a1;
+            hist_add(hist, ok ? (JMAX - jj[i]) & 2047u : 0u, ok);
+        }
+        __syncthreads();
+        find_bin<SEL_NT>(hist, remj, wsum, res);
+        jT = JMAX - ((a1 << 11) | res[0]);
+        __syncthreads();
+    }
+    // Ordered compaction of the selected candidates (the list is sorted by
+    // index): thread t takes a contiguous block.
+    const int E = (cnt + SEL_NT - 1) / SEL_NT;
+    const int c0 = tid * E, c1 = min(cnt, c0 + E);
+    uint32_t mine = 0;
+    for (int i = c0; i < c1; ++i)
+        mine += (keys[i] > T || (keys[i] == T && jj[i] <= jT)) ? 1u : 0u;
+    uint32_t stot;
+    uint32_t o = block_excl_scan<SEL_NT>(mine, wsum, &stot);
+    for (int i = c0; i < c1; ++i)
+        if (keys[i] > T || (keys[i] == T && jj[i] <= jT)) {
+            if (o < (uint32_t)k) out[o] = (int32_t)jj[i];
+            ++o;
+        }
+}
+
+template <int DT, int D>
+hipError_t launch_d(const DecodeArgs& a, int part, hipStream_t s) {
+    if (part == 0) {
+        hipLaunchKernelGGL((decode_threshold_kernel<DT, D>), dim3(a.B), dim3(TH_NT), 0, s, a);
+    } else if (part == 1) {
+        const int KB = 4 * SLOT;
+        const long long nb = (long long)a.B * ((a.n_k + KB - 1) / KB);
+        if (nb > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL((decode_filter_kernel<DT, D>), dim3((unsigned)nb), dim3(256), 0, s, a);
+    } else {
+        hipLaunchKernelGGL((decode_select_kernel<DT, D>), dim3(a.B), dim3(SEL_NT), 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+template <int DT>
+hipError_t launch_dt(const DecodeArgs& a, int part, hipStream_t s) {
+    switch (a.d) {
+        case 32: return launch_d<DT, 32>(a, part, s);
+        case 64: return launch_d<DT, 64>(a, part, s);
+        case 96: return launch_d<DT, 96>(a, part, s);
+        case 128: return launch_d<DT, 128>(a, part, s);
+        case 160: return launch_d<DT, 160>(a, part, s);
+        case 192: return launch_d<DT, 192>(a, part, s);
+        case 224: return launch_d<DT, 224>(a, part, s);
+        case 256: return launch_d<DT, 256>(a, part, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+bool decode_select_applies(int rows, int n_k, int top_k) {
+    return rows == 1 && n_k >= 8192 && (long long)n_k <= (long long)SEL_MAX_SLOTS * SLOT &&
+           top_k <= SEL_CAP;
+}
+
+size_t decode_select_ws_bytes(int B, int n_k) {
+    const size_t n_slots = (n_k + SLOT - 1) / SLOT;
+    auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+    return al((size_t)B * 4) + al((size_t)B * n_slots * 4) + al((size_t)B * n_slots * SLOT * 8);
+}
+
+hipError_t launch_decode_select(DecodeArgs a, void* ws, int part, hipStream_t s) {
+    const size_t n_slots = (a.n_k + SLOT - 1) / SLOT;
+    auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+    char* p = static_cast<char*>(ws);
+    a.tau = reinterpret_cast<uint32_t*>(p);
+    p += al((size_t)a.B * 4);
+    a.cnt = reinterpret_cast<uint32_t*>(p);
+    p += al((size_t)a.B * n_slots * 4);
+    a.cand = reinterpret_cast<uint2*>(p);
+    return a.dtype == 0 ? launch_dt<0>(a, part, s) : launch_dt<1>(a, part, s);
+}
+
+}  // namespace dsa

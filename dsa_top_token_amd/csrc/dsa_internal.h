@@ -31,8 +31,8 @@ struct TopkArgs {
     int hist_ready;         // 1: the indexer already built the row histograms
 };
 
-// Sparse MQA attention. When n_split > 1 the kernel writes unnormalised
-// partials to `part` and a combine kernel finishes O / lse.
+// Sparse MQA attention. With few query rows each (row, split) workgroup
+// writes an unnormalised partial to `part` and a combine kernel merges them.
 struct AttnArgs {
     const uint16_t* Q;      // [B][n_q][H][128] bf16
     const uint16_t* K;      // [B][n_k][128] bf16
@@ -40,9 +40,25 @@ struct AttnArgs {
     const int32_t* idx;     // [B][n_q][k]
     uint16_t* O;            // [B][n_q][H][128] bf16
     float* lse;             // [B][n_q][H] or nullptr
-    float* part;            // [B*n_q][n_split][16][128 + 2] fp32 partials
+    float* part;            // [B*n_q][n_split][16][128 + 4] fp32 partials
     int B, n_q, n_k, H, k;
-    int n_split, split_len; // entries of idx handled per split (multiple of 32)
+    int n_split, split_len; // entries of idx handled per split (multiple of 128)
+};
+
+// One query row per sequence, selection without a materialised score row
+// (sampled threshold, filtered candidates, exact select).
+struct DecodeArgs {
+    const void* q;          // [B][n_q][d]
+    const void* k;          // [B][n_k][d]
+    int32_t* idx;           // [B][idx_rows][top_k]; row idx_row0 is written
+    int B, n_q, n_k, q_pos0, d, dtype, top_k;
+    int q_row;              // the query row of every sequence (0 <= q_row < n_q)
+    int idx_rows, idx_row0;
+    float scale;            // fl32(d^-0.5)
+    float* fallback;        // [B][n_k] score rows for rows the threshold misses
+    uint32_t* tau;          // set by launch_decode_select from its workspace
+    uint32_t* cnt;
+    uint2* cand;
 };
 
 hipError_t launch_index_scores(const IndexArgs& a, hipStream_t s);
@@ -56,6 +72,11 @@ size_t topk_ws_bytes(int B, int rows, int n_k);
 uint32_t* topk_hist_ptr(void* ws);
 hipError_t launch_topk_prepare(const TopkArgs& a, void* ws, hipStream_t s);
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t s);
+
+bool decode_select_applies(int rows, int n_k, int top_k);
+size_t decode_select_ws_bytes(int B, int n_k);
+// part 0: sampled threshold, 1: indexer + filter, 2: exact select.
+hipError_t launch_decode_select(DecodeArgs a, void* ws, int part, hipStream_t s);
 
 // Split plan of the attention: splits per query and entries per split.
 void attn_split_plan(int B, int n_q, int k, int* n_split, int* split_len);

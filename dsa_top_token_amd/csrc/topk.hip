@@ -42,134 +42,6 @@ constexpr int MAX_CHUNKS = 2048;  // 4M keys / CHUNK
 constexpr int MULTI_MAX_ROWS = 256;
 constexpr int MULTI_MIN_KEYS = 4 * CHUNK;
 
-// Four consecutive order keys starting at element j (j % 4 == 0), valid
-// below n.
-template <bool VEC>
-__device__ __forceinline__ void load4(const float* row, int j, int n, uint32_t key[4], bool ok[4]) {
-    if (VEC && j + 3 < n) {
-        const float4 v = *reinterpret_cast<const float4*>(row + j);
-        key[0] = rank_key(v.x);
-        key[1] = rank_key(v.y);
-        key[2] = rank_key(v.z);
-        key[3] = rank_key(v.w);
-        ok[0] = ok[1] = ok[2] = ok[3] = true;
-    } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            ok[e] = j + e < n;
-            key[e] = ok[e] ? rank_key(row[j + e]) : 0u;
-        }
-    }
-}
-
-// The per-row schedule for one row of n > k candidates, run by a ROW_NT-thread
-// workgroup. LDS: hist[BINS], cand[ROW_CAP], wsum[ROW_NT/64], res[4].
-template <bool VEC>
-__device__ void row_topk(const float* row, int n, int k, int32_t* out, uint32_t* hist,
-                         uint32_t* cand, uint32_t* wsum, uint32_t* res) {
-    constexpr int NT = ROW_NT;
-    const int tid = threadIdx.x;
-    // Digit 1.
-    for (int i = tid; i < BINS; i += NT) hist[i] = 0u;
-    if (tid == 0) res[2] = 0u;
-    __syncthreads();
-    for (int base = 0; base < n; base += 4 * NT) {
-        uint32_t key[4];
-        bool ok[4];
-        load4<VEC>(row, base + 4 * tid, n, key, ok);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) hist_add(hist, key[e] >> SHIFT1, ok[e]);
-    }
-    __syncthreads();
-    find_bin<NT>(hist, (uint32_t)k, wsum, res);
-    const uint32_t b1 = res[0];
-    uint32_t rem = (uint32_t)k - res[1];
-    const uint32_t cnt1 = hist[b1];
-    const bool gather = cnt1 <= (uint32_t)ROW_CAP;
-    __syncthreads();
-    // Digit 2 among keys in b1 (gathered into LDS when they fit).
-    for (int i = tid; i < BINS; i += NT) hist[i] = 0u;
-    __syncthreads();
-    for (int base = 0; base < n; base += 4 * NT) {
-        uint32_t key[4];
-        bool ok[4];
-        load4<VEC>(row, base + 4 * tid, n, key, ok);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const bool in = ok[e] && (key[e] >> SHIFT1) == b1;
-            hist_add(hist, (key[e] >> SHIFT2) & (BINS - 1), in);
-            if (gather && in) cand[atomicAdd(&res[2], 1u)] = key[e];
-        }
-    }
-    __syncthreads();
-    find_bin<NT>(hist, rem, wsum, res);
-    const uint32_t pre22 = (b1 << 11) | res[0];
-    rem -= res[1];
-    __syncthreads();
-    // Digit 3 among keys in (b1, b2).
-    for (int i = tid; i < BINS; i += NT) hist[i] = 0u;
-    __syncthreads();
-    if (gather) {
-        for (int base = 0; base < (int)cnt1; base += NT) {
-            const int c = base + tid;
-            const bool ok = c < (int)cnt1;
-            const uint32_t key = ok ? cand[c] : 0u;
-            hist_add(hist, key & 1023u, ok && (key >> SHIFT2) == pre22);
-        }
-    } else {
-        for (int base = 0; base < n; base += 4 * NT) {
-            uint32_t key[4];
-            bool ok[4];
-            load4<VEC>(row, base + 4 * tid, n, key, ok);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                hist_add(hist, key[e] & 1023u, ok[e] && (key[e] >> SHIFT2) == pre22);
-        }
-    }
-    __syncthreads();
-    find_bin<NT>(hist, rem, wsum, res);
-    const uint32_t T = (pre22 << 10) | res[0];
-    rem -= res[1];
-    const uint32_t n_gt = (uint32_t)k - rem;
-
-    // Ordered compaction: 8 consecutive keys per thread per pass.
-    uint32_t gt_run = 0, eq_run = 0;
-    for (int base = 0; base < n; base += 8 * NT) {
-        const int j0 = base + 8 * tid;
-        uint32_t key[8];
-        bool ok[8];
-        load4<VEC>(row, j0, n, key, ok);
-        load4<VEC>(row, j0 + 4, n, key + 4, ok + 4);
-        uint32_t gt = 0, eq = 0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            gt += (ok[e] && key[e] > T) ? 1u : 0u;
-            eq += (ok[e] && key[e] == T) ? 1u : 0u;
-        }
-        uint32_t tot;
-        const uint32_t pk = block_excl_scan<NT>((gt << 16) | eq, wsum, &tot);
-        uint32_t gb = gt_run + (pk >> 16), eb = eq_run + (pk & 0xffffu);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            if (!ok[e]) continue;
-            if (key[e] > T) {
-                const uint32_t o = gb + min(eb, rem);
-                if (o < (uint32_t)k) out[o] = j0 + e;
-                ++gb;
-            } else if (key[e] == T) {
-                if (eb < rem && gb + eb < (uint32_t)k) out[gb + eb] = j0 + e;
-                ++eb;
-            }
-        }
-        gt_run += tot >> 16;
-        eq_run += tot & 0xffffu;
-        if (gt_run >= n_gt && eq_run >= rem) break;
-    }
-}
-
-__device__ __forceinline__ void fill_prefix(int32_t* out, int n, int k, int tid, int nt) {
-    for (int j = tid; j < k; j += nt) out[j] = j < n ? j : -1;
-}
 
 template <bool VEC>
 __global__ __launch_bounds__(ROW_NT) void topk_row_kernel(TopkArgs a) {
@@ -187,7 +59,7 @@ __global__ __launch_bounds__(ROW_NT) void topk_row_kernel(TopkArgs a) {
         fill_prefix(out, n, a.k, threadIdx.x, ROW_NT);
         return;
     }
-    row_topk<VEC>(row, n, a.k, out, hist, cand, wsum, res);
+    row_topk<ROW_NT, ROW_CAP, VEC>(row, n, a.k, out, hist, cand, wsum, res);
 }
 
 // ---------------------------------------------------------------------------
@@ -377,7 +249,8 @@ __global__ __launch_bounds__(SB_NT) void topk_select_b_kernel(MultiArgs a) {
     __syncthreads();
     if (overflow) {
         // A candidate slot overflowed: resolve the row on its own.
-        row_topk<VEC>(a.t.scores + (size_t)slot * a.t.n_k, n, k, out, hist, keys, wsum, res);
+        row_topk<SB_NT, ROW_CAP, VEC>(a.t.scores + (size_t)slot * a.t.n_k, n, k, out, hist, keys, wsum,
+                                      res);
         if (tid == 0) st[2] = 1u;
         return;
     }

@@ -25,11 +25,27 @@ __device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t bin, bool acti
     const unsigned long long act = __ballot(active);
     if (act == 0ull) return;
     const int leader = __ffsll((long long)act) - 1;
-    const uint32_t lead_bin = __shfl(bin, leader);
+    const uint32_t lead_bin = __builtin_amdgcn_readlane(bin, leader);
     const bool same = active && bin == lead_bin;
     const unsigned long long same_mask = __ballot(same);
     if ((int)__lane_id() == leader) atomicAdd(&hist[lead_bin], (uint32_t)__popcll(same_mask));
     if (active && !same) atomicAdd(&hist[bin], 1u);
+}
+
+// Inclusive prefix sum across the 64 lanes of a wave: DPP row shifts within
+// each 16-lane row, then the row totals (read from lanes 15, 31, 47).
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+    // row_shr:n = 0x110 + n; lanes shifted in from outside the row read 0
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, true);
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, true);
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, true);
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, true);
+    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)x, 15);
+    const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)x, 31);
+    const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)x, 47);
+    const int row = (int)(threadIdx.x & 63) >> 4;
+    x += (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
+    return x;
 }
 
 // Exclusive prefix sum over an NT-thread workgroup; *total gets the sum.
@@ -38,12 +54,7 @@ template <int NT>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
     constexpr int NW = NT / 64;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    uint32_t x = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = __shfl_up(x, o);
-        if (lane >= o) x += y;
-    }
+    const uint32_t x = wave_incl_scan(v);
     if (lane == 63) wsum[w] = x;
     __syncthreads();
     uint32_t pre = 0, tot = 0;
@@ -82,6 +93,138 @@ __device__ __forceinline__ void find_bin(const uint32_t* hist, uint32_t rem, uin
         above += c[i];
     }
     __syncthreads();
+}
+
+// Four consecutive order keys starting at element j (j % 4 == 0), valid
+// below n.
+template <bool VEC>
+__device__ __forceinline__ void load4(const float* row, int j, int n, uint32_t key[4], bool ok[4]) {
+    if (VEC && j + 3 < n) {
+        const float4 v = *reinterpret_cast<const float4*>(row + j);
+        key[0] = rank_key(v.x);
+        key[1] = rank_key(v.y);
+        key[2] = rank_key(v.z);
+        key[3] = rank_key(v.w);
+        ok[0] = ok[1] = ok[2] = ok[3] = true;
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            ok[e] = j + e < n;
+            key[e] = ok[e] ? rank_key(row[j + e]) : 0u;
+        }
+    }
+}
+
+// Exact top-k of one score row of n > k candidates, run by an NT-thread
+// workgroup: three histogram rounds find the k-th order key T and the number
+// `rem` of T-ties to keep, then an ordered compaction writes every key above
+// T plus the first `rem` keys equal to T, in ascending index order.
+// LDS: hist[BINS], cand[CAP] (keys of the digit-1 threshold bin, when they
+// fit), wsum[NT/64], res[4].
+template <int NT, int CAP, bool VEC>
+__device__ void row_topk(const float* row, int n, int k, int32_t* out, uint32_t* hist,
+                         uint32_t* cand, uint32_t* wsum, uint32_t* res) {
+    const int tid = threadIdx.x;
+    // Digit 1.
+    for (int i = tid; i < BINS; i += NT) hist[i] = 0u;
+    if (tid == 0) res[2] = 0u;
+    __syncthreads();
+    for (int base = 0; base < n; base += 4 * NT) {
+        uint32_t key[4];
+        bool ok[4];
+        load4<VEC>(row, base + 4 * tid, n, key, ok);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) hist_add(hist, key[e] >> SHIFT1, ok[e]);
+    }
+    __syncthreads();
+    find_bin<NT>(hist, (uint32_t)k, wsum, res);
+    const uint32_t b1 = res[0];
+    uint32_t rem = (uint32_t)k - res[1];
+    const uint32_t cnt1 = hist[b1];
+    const bool gather = cnt1 <= (uint32_t)CAP;
+    __syncthreads();
+    // Digit 2 among keys in b1 (gathered into LDS when they fit).
+    for (int i = tid; i < BINS; i += NT) hist[i] = 0u;
+    __syncthreads();
+    for (int base = 0; base < n; base += 4 * NT) {
+        uint32_t key[4];
+        bool ok[4];
+        load4<VEC>(row, base + 4 * tid, n, key, ok);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const bool in = ok[e] && (key[e] >> SHIFT1) == b1;
+            hist_add(hist, (key[e] >> SHIFT2) & (BINS - 1), in);
+            if (gather && in) cand[atomicAdd(&res[2], 1u)] = key[e];
+        }
+    }
+    __syncthreads();
+    find_bin<NT>(hist, rem, wsum, res);
+    const uint32_t pre22 = (b1 << 11) | res[0];
+    rem -= res[1];
+    __syncthreads();
+    // Digit 3 among keys in (b1, b2).
+    for (int i = tid; i < BINS; i += NT) hist[i] = 0u;
+    __syncthreads();
+    if (gather) {
+        for (int base = 0; base < (int)cnt1; base += NT) {
+            const int c = base + tid;
+            const bool ok = c < (int)cnt1;
+            const uint32_t key = ok ? cand[c] : 0u;
+            hist_add(hist, key & 1023u, ok && (key >> SHIFT2) == pre22);
+        }
+    } else {
+        for (int base = 0; base < n; base += 4 * NT) {
+            uint32_t key[4];
+            bool ok[4];
+            load4<VEC>(row, base + 4 * tid, n, key, ok);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                hist_add(hist, key[e] & 1023u, ok[e] && (key[e] >> SHIFT2) == pre22);
+        }
+    }
+    __syncthreads();
+    find_bin<NT>(hist, rem, wsum, res);
+    const uint32_t T = (pre22 << 10) | res[0];
+    rem -= res[1];
+    const uint32_t n_gt = (uint32_t)k - rem;
+
+    // Ordered compaction: 8 consecutive keys per thread per pass.
+    uint32_t gt_run = 0, eq_run = 0;
+    for (int base = 0; base < n; base += 8 * NT) {
+        const int j0 = base + 8 * tid;
+        uint32_t key[8];
+        bool ok[8];
+        load4<VEC>(row, j0, n, key, ok);
+        load4<VEC>(row, j0 + 4, n, key + 4, ok + 4);
+        uint32_t gt = 0, eq = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            gt += (ok[e] && key[e] > T) ? 1u : 0u;
+            eq += (ok[e] && key[e] == T) ? 1u : 0u;
+        }
+        uint32_t tot;
+        const uint32_t pk = block_excl_scan<NT>((gt << 16) | eq, wsum, &tot);
+        uint32_t gb = gt_run + (pk >> 16), eb = eq_run + (pk & 0xffffu);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            if (!ok[e]) continue;
+            if (key[e] > T) {
+                const uint32_t o = gb + min(eb, rem);
+                if (o < (uint32_t)k) out[o] = j0 + e;
+                ++gb;
+            } else if (key[e] == T) {
+                if (eb < rem && gb + eb < (uint32_t)k) out[gb + eb] = j0 + e;
+                ++eb;
+            }
+        }
+        gt_run += tot >> 16;
+        eq_run += tot & 0xffffu;
+        if (gt_run >= n_gt && eq_run >= rem) break;
+    }
+}
+
+__device__ __forceinline__ void fill_prefix(int32_t* out, int n, int k, int tid, int nt) {
+    for (int j = tid; j < k; j += nt) out[j] = j < n ? j : -1;
 }
 
 }  // namespace topk

@@ -64,6 +64,7 @@ SMALL = [
     Workload("decode_chunked_clustered", "decode", 2, 1, 40000, 39999, 128, "fp8", 1500, 16,
              clustered=True),
     Workload("decode_chunked_bf16", "decode", 2, 1, 9000, 8999, 160, "bf16", 4096, 4),
+    Workload("decode_pos_inside_row", "decode", 2, 1, 30000, 25000, 128, "fp8", 900, 16),
     # a few long query rows (chunked top-k with its own histogram pass)
     Workload("chunked_prefill_long", "prefill", 2, 9, 12000, 11991, 64, "fp8", 333, 2),
 ]
@@ -189,6 +190,28 @@ def test_decode_all_zero_query_overflows_candidates(gpu_lib, n_k):
     assert np.array_equal(idx.cpu().numpy(), idx_ref)
     assert list(idx_ref[1, 0]) == list(range(300))
     assert_attn_close(O, O_ref, lse, lse_ref, "zeros decode")
+
+
+def test_decode_threshold_misses_falls_back(gpu_lib):
+    # Only every 32nd key (the ones the threshold pass samples) scores above
+    # zero, so the sampled threshold keeps far fewer than k keys and the
+    # select kernel must recompute the row.
+    n_k, k = 20000, 300
+    w = Workload("sampled_only", "decode", 2, 1, n_k, n_k - 1, 128, "fp8", k, 4)
+    x = synth.make_inputs(w, seed=9)
+    q = x["q_idx"].float()
+    g = torch.Generator().manual_seed(9)
+    noise = torch.randint(-1, 2, (2, n_k, 128), generator=g).float()
+    kk = (-q).expand(2, n_k, 128).clone()
+    kk[:, ::32] = (q + noise[:, ::32]).clamp(-5, 5)
+    x["k_idx"] = kk.to(torch.float8_e4m3fn)
+    d = to_dev(x)
+    idx, O, lse = dsa.forward(d["q_idx"], d["k_idx"], d["Q"], d["K"], d["V"], w.q_pos0, k)
+    idx_ref, O_ref, lse_ref = oracle.forward(x["q_idx"], x["k_idx"], x["Q"], x["K"], x["V"],
+                                             w.q_pos0, k)
+    assert np.array_equal(idx.cpu().numpy(), idx_ref)
+    assert np.all(idx_ref % 32 == 0)
+    assert_attn_close(O, O_ref, lse, lse_ref, "sampled only")
 
 
 def test_all_zero_query_selects_first_keys(gpu_lib):
