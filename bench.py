@@ -25,16 +25,24 @@ sys.path.insert(0, ROOT)
 
 PEAK = {"hbm": 8000.0, "fp8": 5000.0, "bf16": 2500.0}  # GB/s, TFLOP/s (dense)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+# Sources of the kernels behind each stage (decode rows use decode.hip's
+# threshold / filter / select kernels).
 KERNEL_SOURCES = {
-    "indexer": "dsa_top_token_amd/csrc/indexer.hip",
-    "topk": "dsa_top_token_amd/csrc/topk.hip",
-    "attn": "dsa_top_token_amd/csrc/attn.hip",
+    ("prefill", "indexer"): ["indexer.hip", "frag.h"],
+    ("prefill", "topk"): ["topk.hip", "topk_common.h"],
+    ("prefill", "attn"): ["attn.hip"],
+    ("decode", "indexer"): ["decode.hip", "frag.h"],
+    ("decode", "topk"): ["decode.hip", "topk_common.h"],
+    ("decode", "attn"): ["attn.hip"],
 }
 
 
-def source_hash(stage):
-    with open(os.path.join(ROOT, KERNEL_SOURCES[stage]), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_hash(mode, stage):
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[(mode, stage)]:
+        with open(os.path.join(ROOT, "dsa_top_token_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def stage_work(w, stage):
@@ -189,7 +197,7 @@ def main():
         traffic = None
         if os.path.exists(TRAFFIC_FILE):
             rec = json.load(open(TRAFFIC_FILE)).get("%s/%s" % (w.name, dom))
-            if rec and rec.get("source_sha256_16") == source_hash(dom):
+            if rec and rec.get("source_sha256_16") == source_hash(w.mode, dom):
                 traffic = rec.get("bytes_per_step")
         roof = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                 "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": dom,
