@@ -114,6 +114,16 @@ size_t topk_ws_bytes_max(const dsa_problem* p) {
     return 0;
 }
 
+// Query rows per slab of the many-row path: the candidate lists of one slab
+// stay within kScoreSlabBytes.
+int prefill_slab_rows(const dsa_problem* p) {
+    const size_t row_bytes = (size_t)p->batch * dsa::prefill_cap(p->top_k) * 8;
+    size_t r = kScoreSlabBytes / row_bytes;
+    if (r < 1) r = 1;
+    if (r > (size_t)p->n_q) r = (size_t)p->n_q;
+    return (int)r;
+}
+
 struct ForwardLayout {
     size_t scores, idx, topk, part, total;
 };
@@ -121,6 +131,16 @@ struct ForwardLayout {
 ForwardLayout forward_layout(const dsa_problem* p) {
     ForwardLayout L;
     L.scores = 0;
+    if (p->n_q > 1) {
+        // many rows: candidate lists and thresholds, no score rows
+        const size_t ib = align_up((size_t)p->batch * p->n_q * p->top_k * sizeof(int32_t));
+        L.idx = 0;
+        L.topk = ib;
+        L.part = L.topk + align_up(dsa::prefill_ws_bytes(p->batch, prefill_slab_rows(p), p->n_k,
+                                                         p->top_k));
+        L.total = L.part + attn_ws_bytes(p);
+        return L;
+    }
     const int R = slab_rows(p);
     const size_t sb = align_up((size_t)p->batch * R * p->n_k * sizeof(float));
     L.idx = sb;
@@ -227,7 +247,39 @@ dsa_status forward_impl(const dsa_problem* p, const void* q_idx, const void* k_i
     ta.idx_rows = p->n_q;
     ta.ws = w + L.topk;
     int slabs = 0;
-    for (int r0 = 0; r0 < p->n_q; r0 += R, ++slabs) {
+    if (p->n_q > 1) {
+        // Many query rows: threshold, indexer sweep keeping candidates,
+        // per-row select and fallback, slab by slab.
+        const int RP = prefill_slab_rows(p);
+        for (int r0 = 0; r0 < p->n_q; r0 += RP, ++slabs) {
+            const int r1 = r0 + RP < p->n_q ? r0 + RP : p->n_q;
+            dsa::PrefillArgs pa{};
+            pa.q = q_idx;
+            pa.k = k_idx;
+            pa.idx = idx;
+            pa.B = p->batch;
+            pa.n_q = p->n_q;
+            pa.n_k = p->n_k;
+            pa.q_pos0 = p->q_pos0;
+            pa.d = p->d_idx;
+            pa.dtype = p->idx_dtype;
+            pa.top_k = p->top_k;
+            pa.row0 = r0;
+            pa.rows = r1 - r0;
+            pa.idx_rows = p->n_q;
+            pa.idx_row0 = r0;
+            pa.scale = index_scale(p->d_idx);
+            static const char* what[4] = {"prefill threshold launch", "prefill indexer launch",
+                                          "prefill select launch", "prefill fallback launch"};
+            static const int stage[4] = {1, 0, 1, 1};
+            for (int part = 0; part < 4; ++part) {
+                if (tm) tm->mark(stage[part]);
+                hipError_t e = dsa::launch_prefill_select(pa, ta.ws, part, st);
+                if (e != hipSuccess) return hip_fail(e, what[part]);
+            }
+        }
+    }
+    for (int r0 = 0; p->n_q == 1 && r0 < p->n_q; r0 += R, ++slabs) {
         const int r1 = r0 + R < p->n_q ? r0 + R : p->n_q;
         ia.q_begin = r0;
         ia.q_end = r1;

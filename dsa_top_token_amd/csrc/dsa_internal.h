@@ -73,6 +73,30 @@ uint32_t* topk_hist_ptr(void* ws);
 hipError_t launch_topk_prepare(const TopkArgs& a, void* ws, hipStream_t s);
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t s);
 
+// Many query rows per sequence: sampled threshold, indexer sweep that keeps
+// only candidates, one-wave-per-row exact select, fallback for missed rows.
+struct PrefillArgs {
+    const void* q;          // [B][n_q][d]
+    const void* k;          // [B][n_k][d]
+    int32_t* idx;           // [B][idx_rows][top_k]; slab row r -> idx row idx_row0 + r
+    int B, n_q, n_k, q_pos0, d, dtype, top_k;
+    int row0, rows;         // the slab: query rows [row0, row0 + rows) of every sequence
+    int idx_rows, idx_row0;
+    float scale;
+    int cap;                // candidates kept per row (set by launch_prefill_select)
+    float* tau_acc;         // workspace pointers (set by launch_prefill_select)
+    uint32_t* cnt;
+    uint2* cand;
+    uint32_t* fb_list;
+    uint32_t* fb_count;
+    float* fb_scores;
+};
+
+int prefill_cap(int top_k);
+size_t prefill_ws_bytes(int B, int rows, int n_k, int top_k);
+// part 0: threshold, 1: indexer sweep, 2: select, 3: fallback.
+hipError_t launch_prefill_select(PrefillArgs a, void* ws, int part, hipStream_t s);
+
 bool decode_select_applies(int rows, int n_k, int top_k);
 size_t decode_select_ws_bytes(int B, int n_k);
 // part 0: sampled threshold, 1: indexer + filter, 2: exact select.
