@@ -36,6 +36,7 @@ constexpr int kMaxHeads = 16;
 constexpr int kHeadDim = 128;
 constexpr size_t kAlign = 256;
 constexpr size_t kScoreSlabBytes = size_t(2) << 30;  // score rows staged per forward pass
+constexpr size_t kPrefillSlabBytes = size_t(4) << 30;  // candidate lists per forward pass
 constexpr size_t kPartFloats = 16 * (kHeadDim + 4);   // attention partial per (task)
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -114,14 +115,18 @@ size_t topk_ws_bytes_max(const dsa_problem* p) {
     return 0;
 }
 
-// Query rows per slab of the many-row path: the candidate lists of one slab
-// stay within kScoreSlabBytes.
-int prefill_slab_rows(const dsa_problem* p) {
+// Slabs of the many-row path: slab s holds query rows s, s + n, s + 2n, ...
+// (n slabs), so every slab mixes short and long rows; the candidate lists of
+// one slab stay within kPrefillSlabBytes.
+int prefill_slabs(const dsa_problem* p) {
     const size_t row_bytes = (size_t)p->batch * dsa::prefill_cap(p->top_k) * 8;
-    size_t r = kScoreSlabBytes / row_bytes;
-    if (r < 1) r = 1;
-    if (r > (size_t)p->n_q) r = (size_t)p->n_q;
-    return (int)r;
+    const size_t per = kPrefillSlabBytes / row_bytes > 0 ? kPrefillSlabBytes / row_bytes : 1;
+    return (int)(((size_t)p->n_q + per - 1) / per);
+}
+
+int prefill_slab_rows(const dsa_problem* p) {
+    const int n = prefill_slabs(p);
+    return (p->n_q + n - 1) / n;
 }
 
 struct ForwardLayout {
@@ -250,9 +255,8 @@ dsa_status forward_impl(const dsa_problem* p, const void* q_idx, const void* k_i
     if (p->n_q > 1) {
         // Many query rows: threshold, indexer sweep keeping candidates,
         // per-row select and fallback, slab by slab.
-        const int RP = prefill_slab_rows(p);
-        for (int r0 = 0; r0 < p->n_q; r0 += RP, ++slabs) {
-            const int r1 = r0 + RP < p->n_q ? r0 + RP : p->n_q;
+        const int NS = prefill_slabs(p);
+        for (int s0 = 0; s0 < NS; ++s0, ++slabs) {
             dsa::PrefillArgs pa{};
             pa.q = q_idx;
             pa.k = k_idx;
@@ -264,10 +268,9 @@ dsa_status forward_impl(const dsa_problem* p, const void* q_idx, const void* k_i
             pa.d = p->d_idx;
             pa.dtype = p->idx_dtype;
             pa.top_k = p->top_k;
-            pa.row0 = r0;
-            pa.rows = r1 - r0;
-            pa.idx_rows = p->n_q;
-            pa.idx_row0 = r0;
+            pa.row0 = s0;
+            pa.rstride = NS;
+            pa.rows = (p->n_q - s0 + NS - 1) / NS;
             pa.scale = index_scale(p->d_idx);
             static const char* what[4] = {"prefill threshold launch", "prefill indexer launch",
                                           "prefill select launch", "prefill fallback launch"};

@@ -75,13 +75,13 @@ hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t s);
 
 // Many query rows per sequence: sampled threshold, indexer sweep that keeps
 // only candidates, one-wave-per-row exact select, fallback for missed rows.
+// A slab holds the query rows row0 + i * rstride, i in [0, rows).
 struct PrefillArgs {
     const void* q;          // [B][n_q][d]
     const void* k;          // [B][n_k][d]
-    int32_t* idx;           // [B][idx_rows][top_k]; slab row r -> idx row idx_row0 + r
+    int32_t* idx;           // [B][n_q][top_k]; slab row i -> query row row0 + i * rstride
     int B, n_q, n_k, q_pos0, d, dtype, top_k;
-    int row0, rows;         // the slab: query rows [row0, row0 + rows) of every sequence
-    int idx_rows, idx_row0;
+    int row0, rstride, rows;
     float scale;
     int cap;                // candidates kept per row (set by launch_prefill_select)
     float* tau_acc;         // workspace pointers (set by launch_prefill_select)

@@ -8,20 +8,22 @@
 //   threshold  per 16-row block: scores every S-th key of each row's prefix
 //              (MFMA), two 10-bit radix rounds over those samples give tau,
 //              the lower edge of the 20-bit bin holding the m-th largest
-//              sample (m = ceil(1.5 k / S)); tau is turned into the smallest
-//              fp32 accumulator value whose scaled score reaches it.
-//   filter     per 256-row block (4 waves x 64 rows): sweeps the block's
-//              causal keys in 64-key chunks staged in LDS, computes the
-//              scores on MFMA and keeps every (order key, index) whose
-//              accumulator reaches the row's threshold, appended to the row's
-//              list in ascending index order (per-row counts live in the
-//              registers of the row's lane group; no atomics).
-//   select     one wave per row: the candidates' order keys sit in registers,
-//              three radix rounds find the exact k-th key T, a radix select
-//              on indices cuts the T-ties at the lowest indices, and an
-//              ordered compaction writes the row. Rows with k or fewer keys
-//              are filled directly. A row whose threshold kept fewer than k
-//              keys, or more than its list holds, is queued.
+//              sample (m S ~ 2 top_k); tau becomes the smallest fp32
+//              accumulator whose scaled score reaches it. A row whose sample
+//              threshold is not positive keeps every non-negative
+//              accumulator instead ("zero mode").
+//   filter     per 64-row block (4 waves x 16 rows): sweeps the block's
+//              causal keys in 64-key chunks staged in LDS. Keys are the MFMA
+//              row operand, so each lane holds 16 consecutive keys of one
+//              query; a subtract and a funnel shift per score build the
+//              lane's accept mask, and the accepted (accumulator, index)
+//              pairs go to the row's list in ascending index order.
+//   select     one wave per row over its list: three radix rounds give the
+//              exact k-th key T, the T-ties are cut in list (= index) order.
+//              A zero-mode row with fewer than top_k positive scores takes
+//              its positives plus the lowest-index zero scores. A row whose
+//              threshold kept fewer than top_k keys, or more than its list
+//              holds, is queued.
 //   fallback   a persistent kernel recomputes each queued row's scores into
 //              the workspace and selects on them with the per-row radix
 //              schedule.
@@ -37,13 +39,15 @@ using namespace topk;
 constexpr int TH_ROWS = 16;       // rows per threshold workgroup
 constexpr int TH_BINS = 1024;     // 10-bit digits of the threshold rounds
 constexpr int TH_MAX_SAMPLES = 4096;
+constexpr int TH_TARGET = 64;     // samples expected above tau
 constexpr int FL_CHUNK = 64;      // keys per staged chunk of the filter
-constexpr int FL_ROWS_W = 64;     // rows per filter wave
-constexpr int FL_ROWS = 4 * FL_ROWS_W;
+constexpr int FL_ROWS = 64;       // rows per filter workgroup (16 per wave)
 constexpr int FB_WGS = 256;       // fallback workgroups
 
-__device__ __forceinline__ int row_len(const PrefillArgs& a, int r) {
-    const long long pos = (long long)a.q_pos0 + a.row0 + r;
+__device__ __forceinline__ int qrow(const PrefillArgs& a, int i) { return a.row0 + i * a.rstride; }
+
+__device__ __forceinline__ int row_len(const PrefillArgs& a, int i) {
+    const long long pos = (long long)a.q_pos0 + qrow(a, i);
     return (int)min((long long)a.n_k, pos + 1);
 }
 
@@ -56,6 +60,14 @@ __device__ float raw_threshold(float tau, float scale) {
     for (int it = 0; it < 64 && x * scale < tau; ++it)
         x = __uint_as_float(__float_as_uint(x) + 1u);
     return x;
+}
+
+__device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(x), 63);
+}
+
+__device__ __forceinline__ unsigned long long lanes_below() {
+    return (1ull << (threadIdx.x & 63)) - 1ull;
 }
 
 // The bin of a wave-private histogram (nbins, bins owned top-down by lanes)
@@ -105,13 +117,13 @@ __global__ __launch_bounds__(256) void prefill_threshold_kernel(PrefillArgs a) {
     if (blockIdx.x == 0 && threadIdx.x == 0) *a.fb_count = 0u;
     // Sampling plan of the block (shared stride, per-row sample counts).
     const int nmax = row_len(a, min(r0 + TH_ROWS, a.rows) - 1);
-    const int S = max(32, (nmax + TH_MAX_SAMPLES - 1) / TH_MAX_SAMPLES);
-    const uint32_t m = (uint32_t)((3 * a.top_k + 2 * S - 1) / (2 * S));
+    const int S = max(max(1, 2 * a.top_k / TH_TARGET), (nmax + TH_MAX_SAMPLES - 1) / TH_MAX_SAMPLES);
+    const uint32_t m = (uint32_t)((2 * a.top_k + S - 1) / S);
     const int ns_max = (nmax + S - 1) / S;
 
     Frag<DT, D> fq;  // A operand: the block's 16 query rows
     fq.load(static_cast<const uint8_t*>(a.q) +
-                ((size_t)b * a.n_q + a.row0 + min(r0 + n, a.rows - 1)) * RB, g);
+                ((size_t)b * a.n_q + qrow(a, min(r0 + n, a.rows - 1))) * RB, g);
     const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + (size_t)b * a.n_k * RB;
     // Sample count of the rows this lane's scores belong to (rows 4g + r).
     int ns_r[4];
@@ -159,11 +171,11 @@ __global__ __launch_bounds__(256) void prefill_threshold_kernel(PrefillArgs a) {
                         if (len <= a.top_k) {
                             tacc = __builtin_inff();  // trivial row: no candidates
                         } else if ((uint32_t)ns <= m) {
-                            tacc = -__builtin_inff();  // every key is a candidate
+                            tacc = 0.0f;  // zero mode
                         } else {
                             const uint32_t tkey = (digit1[row] << 22) | (bin << 12);
                             if (tkey <= 0x80000000u) {
-                                tacc = -__builtin_inff();
+                                tacc = 0.0f;  // zero mode
                             } else {
                                 const float tau = __uint_as_float(tkey & 0x7fffffffu);
                                 tacc = raw_threshold(tau, a.scale);
@@ -187,41 +199,33 @@ __global__ __launch_bounds__(256) void prefill_filter_kernel(PrefillArgs a) {
     constexpr int CHUNK_BYTES = FL_CHUNK * RB;
     constexpr int LD_PER_THREAD = (CHUNK_BYTES + 256 * 16 - 1) / (256 * 16);
     __shared__ __attribute__((aligned(16))) uint8_t kt[2][FL_CHUNK * PITCH];
+    // per-wave copy of each lane's 16 accumulators: [wave][u][lane] x 4
+    __shared__ f32x4 stage[4][4][64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n = lane & 15, g = lane >> 4;
     const int n_blk = (a.rows + FL_ROWS - 1) / FL_ROWS;
     // largest blocks (latest rows) first
     const int blk = n_blk - 1 - (int)(blockIdx.x / (unsigned)a.B);
     const int b = blockIdx.x % a.B;
-    const int r0 = blk * FL_ROWS;
-    const int wr0 = r0 + wave * FL_ROWS_W;
-    const long long pos_base = (long long)a.q_pos0 + a.row0;
-    const int blk_last = min(r0 + FL_ROWS, a.rows) - 1;
-    const int kend = (int)min((long long)a.n_k, pos_base + blk_last + 1);
+    const int i0 = blk * FL_ROWS;
+    const int wi0 = i0 + wave * 16;
+    const int kend = row_len(a, min(i0 + FL_ROWS, a.rows) - 1);
     const int n_chunks = (kend + FL_CHUNK - 1) / FL_CHUNK;
     const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + (size_t)b * a.n_k * RB;
 
-    // A fragments (4 row tiles) and per-row thresholds of this lane's rows.
-    Frag<DT, D> fa[4];
-    float tacc[4][4];
-    int pos_r[4][4];
-    uint32_t cnt[4][4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        const int qr = min(wr0 + 16 * t + n, a.rows - 1);
-        fa[t].load(static_cast<const uint8_t*>(a.q) + ((size_t)b * a.n_q + a.row0 + qr) * RB, g);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = wr0 + 16 * t + 4 * g + r;
-            tacc[t][r] = row < a.rows ? a.tau_acc[(size_t)b * a.rows + row] : __builtin_inff();
-            pos_r[t][r] = (int)(pos_base + row);
-            cnt[t][r] = 0u;
-        }
-    }
-    const int wave_last = min(wr0 + FL_ROWS_W, a.rows) - 1;
-    const long long wave_maxpos = pos_base + wave_last;
-    const long long wave_minpos = pos_base + wr0;
-    const bool wave_live = wr0 < a.rows;
+    // This lane's query (column n of the B operand) and its row state.
+    const int my_i = min(wi0 + n, a.rows - 1);
+    const bool live = wi0 + n < a.rows;
+    const int my_len = live ? row_len(a, my_i) : 0;
+    const float tau = live ? a.tau_acc[(size_t)b * a.rows + my_i] : __builtin_inff();
+    const bool wave_live = wi0 < a.rows;
+    const int w_kend = wave_live ? row_len(a, min(wi0 + 15, a.rows - 1)) : 0;
+    const int w_kmin = wave_live ? row_len(a, wi0) : 0;
+    Frag<DT, D> fq;
+    fq.load(static_cast<const uint8_t*>(a.q) + ((size_t)b * a.n_q + qrow(a, my_i)) * RB, g);
+    uint2* list = a.cand + ((size_t)b * a.rows + my_i) * a.cap;
+    const uint32_t cap = (uint32_t)a.cap;
+    uint32_t cnt = 0;  // the row's list length (same in the row's 4 lanes)
 
     auto load_chunk = [&](int c, i32x4* stg) {
         const uint8_t* src = kbase + (size_t)c * CHUNK_BYTES;
@@ -245,109 +249,154 @@ __global__ __launch_bounds__(256) void prefill_filter_kernel(PrefillArgs a) {
         }
     };
 
+    // A operand row n of key tile u is key 16 (n / 4) + 4 u + n % 4 of the
+    // chunk, so output row 4 g + r of tile u is key 16 g + 4 u + r: lane
+    // (n, g) holds keys [16 g, 16 g + 16) of the chunk for query n.
+    const int krow = 16 * (n >> 2) + (n & 3);
+
     i32x4 stg[LD_PER_THREAD];
     if (n_chunks > 0) {
         load_chunk(0, stg);
         store_chunk(0, stg);
     }
     __syncthreads();
-    uint2* cand_rows = a.cand + ((size_t)b * a.rows) * a.cap;
     for (int c = 0; c < n_chunks; ++c) {
         const int buf = c & 1;
         if (c + 1 < n_chunks) load_chunk(c + 1, stg);
         const int k0 = c * FL_CHUNK;
-        if (wave_live && k0 <= wave_maxpos) {
-            f32x4 acc[4][4];
+        if (k0 < w_kend) {
+            f32x4 acc[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                Frag<DT, D> fb;
-                fb.load(&kt[buf][(16 * u + n) * PITCH], g);
-#pragma unroll
-                for (int t = 0; t < 4; ++t) acc[t][u] = tile_dot<D>(fa[t], fb);
+                Frag<DT, D> fk;
+                fk.load(&kt[buf][(krow + 4 * u) * PITCH], g);
+                acc[u] = tile_dot<D>(fk, fq);
             }
             if constexpr (DT == 0) {
                 if constexpr (Frag<0, D>::NB > 0) mfma_drain();
             }
-            const bool diag = k0 + FL_CHUNK - 1 > wave_minpos || k0 + FL_CHUNK > a.n_k;
+            // bit i of rej: sign of (accumulator of key 16 g + i) - tau
+            uint32_t rej = 0;
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
+            for (int i = 15; i >= 0; --i)
+                rej = __builtin_amdgcn_alignbit(rej, __float_as_uint(acc[i >> 2][i & 3] - tau), 31);
+            uint32_t bits = ~rej & 0xffffu;
+            if (k0 + FL_CHUNK > w_kmin) {
+                const int v = my_len - (k0 + 16 * g);
+                bits &= v >= 16 ? 0xffffu : (v <= 0 ? 0u : (1u << v) - 1u);
+            }
+            // The row's lanes g = 0..3 hold consecutive key ranges: exclusive
+            // prefix of their counts.
+            const uint32_t lc = (uint32_t)__popc(bits);
+            const uint32_t x1 = (uint32_t)__shfl_xor((int)lc, 16);
+            const uint32_t s01 = lc + x1;
+            const uint32_t x2 = (uint32_t)__shfl_xor((int)s01, 32);
+            const uint32_t tot = s01 + x2;
+            uint32_t o = cnt + ((g & 1) ? x1 : 0u) + ((g & 2) ? x2 : 0u);
+            if (cnt + tot > cap) bits = 0u;  // overflowing row: its list is abandoned
+            cnt += tot;
+            if (__ballot(bits != 0u) != 0ull) {
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int key = k0 + 16 * u + n;
-                    bool cr[4];
-                    bool any = false;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        cr[r] = acc[t][u][r] >= tacc[t][r];
-                        if (diag) cr[r] = cr[r] && key <= pos_r[t][r] && key < a.n_k;
-                        any = any || cr[r];
-                    }
-                    if (__ballot(any) == 0ull) continue;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const unsigned long long msk = __ballot(cr[r]);
-                        if (msk == 0ull) continue;
-                        const uint32_t seg = (uint32_t)(msk >> (16 * g)) & 0xffffu;
-                        if (cr[r]) {
-                            const uint32_t o = cnt[t][r] + (uint32_t)__popc(seg & ((1u << n) - 1u));
-                            if (o < (uint32_t)a.cap) {
-                                const int row = wr0 + 16 * t + 4 * g + r;
-                                cand_rows[(size_t)row * a.cap + o] =
-                                    make_uint2(rank_key(relu_scaled(acc[t][u][r], a.scale)),
-                                               (uint32_t)key);
-                            }
-                        }
-                        cnt[t][r] += (uint32_t)__popc(seg);
-                    }
+                for (int u = 0; u < 4; ++u) stage[wave][u][lane] = acc[u];
+                const uint32_t kb = (uint32_t)(k0 + 16 * g);
+                while (bits != 0u) {
+                    const int i = __builtin_ctz(bits);
+                    bits &= bits - 1u;
+                    const float v = reinterpret_cast<const float*>(&stage[wave][i >> 2][lane])[i & 3];
+                    list[o] = make_uint2(__float_as_uint(v), kb + (uint32_t)i);
+                    ++o;
                 }
             }
         }
         if (c + 1 < n_chunks) store_chunk(buf ^ 1, stg);
         __syncthreads();
     }
-    if (n == 0) {
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = wr0 + 16 * t + 4 * g + r;
-                if (row < a.rows) a.cnt[(size_t)b * a.rows + row] = cnt[t][r];
-            }
-    }
+    if (g == 0 && live) a.cnt[(size_t)b * a.rows + my_i] = cnt;
 }
 
 // ------------------------------------------------------------------- select
 
-// One 64-thread workgroup (one wave) per row. Dynamic LDS: the row's order
-// keys (cap words) then a 2048-bin histogram.
+__device__ __forceinline__ uint32_t cand_key(uint32_t acc_bits, float scale) {
+    return rank_key(relu_scaled(__uint_as_float(acc_bits), scale));
+}
+
+// One 64-thread workgroup (one wave) per row; the list is read from global
+// memory on every pass.
 __global__ __launch_bounds__(64) void prefill_select_kernel(PrefillArgs a) {
-    extern __shared__ uint32_t smem[];
-    uint32_t* keys = smem;
-    uint32_t* hist = smem + a.cap;
+    __shared__ uint32_t hist[BINS];
     const int lane = threadIdx.x;
     const long long task = blockIdx.x;
-    const int b = (int)(task / a.rows), row = (int)(task % a.rows);
-    const int n = row_len(a, row);
+    const int b = (int)(task / a.rows), i = (int)(task % a.rows);
+    const int n = row_len(a, i);
     const int k = a.top_k;
-    int32_t* out = a.idx + ((size_t)b * a.idx_rows + a.idx_row0 + row) * k;
+    int32_t* out = a.idx + ((size_t)b * a.n_q + qrow(a, i)) * k;
     if (n <= k) {
         fill_prefix(out, n, k, lane, 64);
         return;
     }
     const uint32_t cnt = a.cnt[task];
-    if (cnt < (uint32_t)k || cnt > (uint32_t)a.cap) {
+    const bool zero_mode = __float_as_uint(a.tau_acc[task]) == 0u;
+    if (cnt > (uint32_t)a.cap || (!zero_mode && cnt < (uint32_t)k)) {
         if (lane == 0) a.fb_list[atomicAdd(a.fb_count, 1u)] = (uint32_t)task;
         return;
     }
     const uint2* cl = a.cand + (size_t)task * a.cap;
     const int cn = (int)cnt;
-    for (int c = lane; c < cn; c += 64) keys[c] = cl[c].x;
+    const float scale = a.scale;
+    constexpr uint32_t ZERO_KEY = 0x80000000u;  // order key of a zero score
+
+    if (zero_mode) {
+        // The list holds every key with a positive score (plus some zeros);
+        // every key off the list scores zero.
+        uint32_t np = 0;
+        for (int c = lane; c < cn; c += 64) np += cand_key(cl[c].x, scale) > ZERO_KEY ? 1u : 0u;
+        np = wave_sum(np);
+        if (np < (uint32_t)k) {
+            // Positives plus the lowest-index zeros. With P the positives in
+            // index order, P[r] - r zeros precede P[r]; the first cs
+            // positives (P[r] - r < Z) come before the Z-th zero.
+            const uint32_t Z = (uint32_t)k - np;
+            uint32_t run = 0, cs = 0;
+            for (int c0 = 0; c0 < cn; c0 += 64) {
+                const int c = c0 + lane;
+                bool pos = false;
+                uint32_t j = 0;
+                if (c < cn) {
+                    const uint2 e = cl[c];
+                    pos = cand_key(e.x, scale) > ZERO_KEY;
+                    j = e.y;
+                }
+                const unsigned long long pm = __ballot(pos);
+                const uint32_t r = run + (uint32_t)__popcll(pm & lanes_below());
+                cs += (uint32_t)__popcll(__ballot(pos && j - r < Z));
+                run += (uint32_t)__popcll(pm);
+            }
+            const uint32_t head = Z + cs;  // out[0, head) = 0 .. head - 1
+            for (uint32_t o = lane; o < head; o += 64) out[o] = (int32_t)o;
+            run = 0;
+            for (int c0 = 0; c0 < cn; c0 += 64) {
+                const int c = c0 + lane;
+                bool pos = false;
+                uint32_t j = 0;
+                if (c < cn) {
+                    const uint2 e = cl[c];
+                    pos = cand_key(e.x, scale) > ZERO_KEY;
+                    j = e.y;
+                }
+                const unsigned long long pm = __ballot(pos);
+                const uint32_t r = run + (uint32_t)__popcll(pm & lanes_below());
+                if (pos && r >= cs) out[Z + r] = (int32_t)j;
+                run += (uint32_t)__popcll(pm);
+            }
+            return;
+        }
+    }
+
     auto wave_sync = [] {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     };
-    wave_sync();
     // Exact k-th key: digits 31..21, 20..10, 9..0.
     uint32_t rem = (uint32_t)k, prefix = 0;
 #pragma unroll 1
@@ -355,13 +404,22 @@ __global__ __launch_bounds__(64) void prefill_select_kernel(PrefillArgs a) {
         const int sh = round == 0 ? 21 : (round == 1 ? 10 : 0);
         const int psh = round == 1 ? 21 : 10;  // prefix bits of the earlier rounds
         const uint32_t msk = round == 2 ? 1023u : 2047u;
-        for (int i = lane; i < BINS; i += 64) hist[i] = 0u;
+        for (int t = lane; t < BINS; t += 64) hist[t] = 0u;
         wave_sync();
-        for (int c0 = 0; c0 < cn; c0 += 64) {
-            const int c = c0 + lane;
-            const uint32_t key = c < cn ? keys[c] : 0u;
-            const bool in = c < cn && (round == 0 || (key >> psh) == prefix);
-            hist_add(hist, (key >> sh) & msk, in);
+        for (int c0 = 0; c0 < cn; c0 += 256) {
+            uint32_t key[4];
+            bool ok[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int c = c0 + 64 * u + lane;
+                ok[u] = c < cn;
+                key[u] = ok[u] ? cand_key(cl[c].x, scale) : 0u;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const bool in = ok[u] && (round == 0 || (key[u] >> psh) == prefix);
+                hist_add(hist, (key[u] >> sh) & msk, in);
+            }
         }
         wave_sync();
         uint32_t above;
@@ -370,55 +428,25 @@ __global__ __launch_bounds__(64) void prefill_select_kernel(PrefillArgs a) {
         rem -= above;
         wave_sync();
     }
-    const uint32_t T = prefix;
-    uint32_t gt = 0, eq = 0;
-    for (int c = lane; c < cn; c += 64) {
-        gt += keys[c] > T ? 1u : 0u;
-        eq += keys[c] == T ? 1u : 0u;
-    }
-    const uint32_t pk = wave_incl_scan((gt << 16) | eq);
-    const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)pk, 63);
-    const uint32_t n_gt = tot >> 16, n_eq = tot & 0xffffu;
-    const uint32_t keep = (uint32_t)k - n_gt;  // ties to keep (>= 1)
-    // Tie cut-off: keep the `keep` lowest indices among keys equal to T.
-    constexpr uint32_t JMAX = (1u << 22) - 1u;
-    uint32_t jT = JMAX;
-    if (n_eq > keep) {
-        uint32_t r2 = keep, pre = 0;
-#pragma unroll 1
-        for (int round = 0; round < 2; ++round) {
-            for (int i = lane; i < BINS; i += 64) hist[i] = 0u;
-            wave_sync();
-            for (int c0 = 0; c0 < cn; c0 += 64) {
-                const int c = c0 + lane;
-                const bool tie = c < cn && keys[c] == T;
-                const uint32_t kj = tie ? JMAX - cl[c].y : 0u;
-                const bool in = tie && (round == 0 || (kj >> 11) == pre);
-                hist_add(hist, round == 0 ? (kj >> 11) : (kj & 2047u), in);
-            }
-            wave_sync();
-            uint32_t above;
-            const uint32_t bin = wave_find_bin<BINS>(hist, r2, &above);
-            pre = round == 0 ? bin : ((pre << 11) | bin);
-            r2 -= above;
-            wave_sync();
-        }
-        jT = JMAX - pre;
-    }
-    // Ordered compaction over the index-sorted list, 64 candidates at a time.
-    uint32_t base = 0;
-    for (int c0 = 0; c0 < cn; c0 += 64) {
+    const uint32_t T = prefix;  // keep every key above T and the first rem keys equal to T
+    // Ordered compaction over the index-ordered list.
+    uint32_t base = 0, eq_run = 0;
+    for (int c0 = 0; c0 < cn && base < (uint32_t)k; c0 += 64) {
         const int c = c0 + lane;
-        bool s = false;
-        uint32_t j = 0;
-        if (c < cn && keys[c] >= T) {
-            j = cl[c].y;
-            s = keys[c] > T || j <= jT;
+        uint32_t key = 0, j = 0;
+        if (c < cn) {
+            const uint2 e = cl[c];
+            key = cand_key(e.x, scale);
+            j = e.y;
         }
-        const unsigned long long msk = __ballot(s);
-        const uint32_t o = base + (uint32_t)__popcll(msk & ((1ull << lane) - 1ull));
-        if (s && o < (uint32_t)k) out[o] = (int32_t)j;
-        base += (uint32_t)__popcll(msk);
+        const bool gt = c < cn && key > T;
+        const bool eq = c < cn && key == T;
+        const unsigned long long me = __ballot(eq);
+        const bool keep = gt || (eq && eq_run + (uint32_t)__popcll(me & lanes_below()) < rem);
+        const unsigned long long mk = __ballot(keep);
+        if (keep) out[base + (uint32_t)__popcll(mk & lanes_below())] = (int32_t)j;
+        base += (uint32_t)__popcll(mk);
+        eq_run += (uint32_t)__popcll(me);
     }
 }
 
@@ -437,10 +465,10 @@ __global__ __launch_bounds__(512) void prefill_fallback_kernel(PrefillArgs a) {
     float* srow = a.fb_scores + (size_t)blockIdx.x * a.n_k;
     for (uint32_t f = blockIdx.x; f < total; f += gridDim.x) {
         const uint32_t task = a.fb_list[f];
-        const int b = (int)(task / a.rows), row = (int)(task % a.rows);
-        const int len = row_len(a, row);
+        const int b = (int)(task / a.rows), i = (int)(task % a.rows);
+        const int len = row_len(a, i);
         Frag<DT, D> fq;  // the query row, broadcast to all 16 B columns
-        fq.load(static_cast<const uint8_t*>(a.q) + ((size_t)b * a.n_q + a.row0 + row) * RB, g);
+        fq.load(static_cast<const uint8_t*>(a.q) + ((size_t)b * a.n_q + qrow(a, i)) * RB, g);
         const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + (size_t)b * a.n_k * RB;
         for (int t0 = wave * 16; t0 < len; t0 += 8 * 16) {
             Frag<DT, D> fk;
@@ -454,7 +482,7 @@ __global__ __launch_bounds__(512) void prefill_fallback_kernel(PrefillArgs a) {
         }
         __threadfence();
         __syncthreads();
-        int32_t* out = a.idx + ((size_t)b * a.idx_rows + a.idx_row0 + row) * a.top_k;
+        int32_t* out = a.idx + ((size_t)b * a.n_q + qrow(a, i)) * a.top_k;
         row_topk<512, 8192, false>(srow, len, a.top_k, out, hist, cand, wsum, res);
         __syncthreads();
     }
@@ -474,8 +502,7 @@ hipError_t launch_d(const PrefillArgs& a, int part, hipStream_t s) {
         hipLaunchKernelGGL((prefill_filter_kernel<DT, D>), dim3((unsigned)nb), dim3(256), 0, s, a);
     } else if (part == 2) {
         if (rows > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-        const size_t lds = ((size_t)a.cap + BINS) * 4;
-        hipLaunchKernelGGL(prefill_select_kernel, dim3((unsigned)rows), dim3(64), lds, s, a);
+        hipLaunchKernelGGL(prefill_select_kernel, dim3((unsigned)rows), dim3(64), 0, s, a);
     } else {
         hipLaunchKernelGGL((prefill_fallback_kernel<DT, D>), dim3(FB_WGS), dim3(512), 0, s, a);
     }
@@ -500,9 +527,8 @@ hipError_t launch_dt(const PrefillArgs& a, int part, hipStream_t s) {
 }  // namespace
 
 int prefill_cap(int top_k) {
-    // candidate list per row: about 2.5 k plus room for ties, whole waves
-    const int c = (5 * top_k / 2 + 512 + 63) / 64 * 64;
-    return c;
+    // expected list length is about 2 top_k; room for sampling spread and ties
+    return (3 * top_k + 768 + 63) / 64 * 64;
 }
 
 size_t prefill_ws_bytes(int B, int rows, int n_k, int top_k) {
