@@ -12,18 +12,23 @@
 //              accumulator whose scaled score reaches it. A row whose sample
 //              threshold is not positive keeps every non-negative
 //              accumulator instead ("zero mode").
-//   filter     per 64-row block (4 waves x 16 rows): sweeps the block's
-//              causal keys in 64-key chunks staged in LDS. Keys are the MFMA
-//              row operand, so each lane holds 16 consecutive keys of one
-//              query; a subtract and a funnel shift per score build the
-//              lane's accept mask, and the accepted (accumulator, index)
-//              pairs go to the row's list in ascending index order.
-//   select     one wave per row over its list: three radix rounds give the
-//              exact k-th key T, the T-ties are cut in list (= index) order.
-//              A zero-mode row with fewer than top_k positive scores takes
-//              its positives plus the lowest-index zero scores. A row whose
-//              threshold kept fewer than top_k keys, or more than its list
-//              holds, is queued.
+//   filter     per 64-row block: a producer wave streams the block's causal
+//              keys into an LDS ring of 64-key chunks with global->LDS copies
+//              (granule-major layout, several chunks in flight); four
+//              consumer waves of 16 rows each score every chunk on MFMA.
+//              Keys are the MFMA row operand, so each lane holds 16
+//              consecutive keys of one query; a subtract and a funnel shift
+//              per score build the lane's accept mask, and the accepted
+//              (accumulator, index) pairs go to the row's list in ascending
+//              index order.
+//   select     one 256-thread workgroup per row with its list in registers:
+//              radix rounds of 12-bit digits over the order keys relative to
+//              the row's smallest (as many rounds as the key range needs)
+//              give the exact k-th key T; the T-ties are cut in list (=
+//              index) order. A zero-mode row with fewer than top_k positive
+//              scores takes its positives plus the lowest-index zero scores.
+//              A row whose threshold kept fewer than top_k keys, or more than
+//              its list holds, is queued.
 //   fallback   a persistent kernel recomputes each queued row's scores into
 //              the workspace and selects on them with the per-row radix
 //              schedule.
@@ -62,14 +67,6 @@ __device__ float raw_threshold(float tau, float scale) {
     return x;
 }
 
-__device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
-    return (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(x), 63);
-}
-
-__device__ __forceinline__ unsigned long long lanes_below() {
-    return (1ull << (threadIdx.x & 63)) - 1ull;
-}
-
 // The bin of a wave-private histogram (nbins, bins owned top-down by lanes)
 // holding the rem-th largest counted key: returns bin, *above = count of
 // keys in higher bins. Every lane of the wave calls it.
@@ -99,6 +96,39 @@ __device__ __forceinline__ uint32_t wave_find_bin(const uint32_t* hist, uint32_t
     const int src = f ? __ffsll((long long)f) - 1 : 0;
     *above_out = (uint32_t)__builtin_amdgcn_readlane((int)ab, src);
     return (uint32_t)__builtin_amdgcn_readlane((int)bin, src);
+}
+
+// Fragment of row position rp from a granule-major LDS tile: byte b of row
+// rp sits at tile + (b / 16) * COLB + 16 rp + b % 16 (the same bytes, in the
+// same register slots, as Frag::load takes from a contiguous row).
+template <int COLB, int D>
+__device__ __forceinline__ void load_cm(Frag<0, D>& f, const uint8_t* tile, int rp, int g) {
+    const uint8_t* t = tile + 16 * rp;
+#pragma unroll
+    for (int c = 0; c < Frag<0, D>::NB; ++c) {
+        const i32x4 lo = *reinterpret_cast<const i32x4*>(t + (8 * c + g) * COLB);
+        const i32x4 hi = *reinterpret_cast<const i32x4*>(t + (8 * c + 4 + g) * COLB);
+        f.big[c] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+#pragma unroll
+    for (int c = 0; c < Frag<0, D>::NS; ++c)
+        f.small[c] = *reinterpret_cast<const long*>(
+            t + (8 * Frag<0, D>::NB + 2 * c + (g >> 1)) * COLB + 8 * (g & 1));
+}
+
+template <int COLB, int D>
+__device__ __forceinline__ void load_cm(Frag<1, D>& f, const uint8_t* tile, int rp, int g) {
+    const uint8_t* t = tile + 16 * rp;
+#pragma unroll
+    for (int c = 0; c < Frag<1, D>::NC; ++c)
+        f.v[c] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const i32x4*>(t + (4 * c + g) * COLB));
+}
+
+// s_waitcnt with vmcnt = N (expcnt and lgkmcnt left open).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
 }
 
 // ---------------------------------------------------------------- threshold
@@ -192,13 +222,22 @@ __global__ __launch_bounds__(256) void prefill_threshold_kernel(PrefillArgs a) {
 
 // ------------------------------------------------------------------- filter
 
+// Ring depth of the key-chunk pipeline (chunks in flight ahead of the one
+// being consumed is FL_NBUF - 1).
+template <int RB>
+constexpr int fl_nbuf() { return FL_CHUNK * RB <= 8192 ? 3 : 2; }
+static_assert(FL_CHUNK == 64, "the producer's lane -> key map covers 64 keys");
+
 template <int DT, int D>
-__global__ __launch_bounds__(256) void prefill_filter_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(320) void prefill_filter_kernel(PrefillArgs a) {
     constexpr int RB = D * (DT == 0 ? 1 : 2);
-    constexpr int PITCH = RB + 16;
-    constexpr int CHUNK_BYTES = FL_CHUNK * RB;
-    constexpr int LD_PER_THREAD = (CHUNK_BYTES + 256 * 16 - 1) / (256 * 16);
-    __shared__ __attribute__((aligned(16))) uint8_t kt[2][FL_CHUNK * PITCH];
+    constexpr int GPR = RB / 16;            // 16-byte granules per key row
+    constexpr int COLB = FL_CHUNK * 16;     // bytes of one granule column
+    constexpr int NBUF = fl_nbuf<RB>();
+    static_assert(RB % 16 == 0 && (NBUF - 1) * GPR < 64, "chunk pipeline");
+    // Key chunks, granule-major: granule j of the key at row position rp
+    // (see krow below) is at ring[slot] + j * COLB + 16 rp.
+    __shared__ __attribute__((aligned(16))) uint8_t ring[NBUF][FL_CHUNK * RB];
     // per-wave copy of each lane's 16 accumulators: [wave][u][lane] x 4
     __shared__ f32x4 stage[4][4][64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -208,12 +247,49 @@ __global__ __launch_bounds__(256) void prefill_filter_kernel(PrefillArgs a) {
     const int blk = n_blk - 1 - (int)(blockIdx.x / (unsigned)a.B);
     const int b = blockIdx.x % a.B;
     const int i0 = blk * FL_ROWS;
-    const int wi0 = i0 + wave * 16;
     const int kend = row_len(a, min(i0 + FL_ROWS, a.rows) - 1);
     const int n_chunks = (kend + FL_CHUNK - 1) / FL_CHUNK;
     const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + (size_t)b * a.n_k * RB;
 
-    // This lane's query (column n of the B operand) and its row state.
+    if (wave == 4) {
+        // Producer: global -> LDS copies, NBUF - 1 chunks ahead. Lane l moves
+        // the key at row position l: chunk row 16 ((l / 4) % 4) + 4 (l / 16) + l % 4.
+        const int kr = 16 * ((lane >> 2) & 3) + 4 * (lane >> 4) + (lane & 3);
+        auto issue = [&](int c) {
+            const int key = min(c * FL_CHUNK + kr, a.n_k - 1);
+            const uint8_t* src = kbase + (size_t)key * RB;
+            uint8_t* dst = ring[c % NBUF];
+#pragma unroll
+            for (int j = 0; j < GPR; ++j)
+                __builtin_amdgcn_global_load_lds(src + 16 * j, dst + j * COLB, 16, 0, 0);
+        };
+        const int pre = min(NBUF - 1, n_chunks);
+        for (int c = 0; c < pre; ++c) issue(c);
+        for (int c = 0; c < n_chunks; ++c) {
+            // chunk c has landed once at most `ahead` later chunks are in flight
+            const int ahead = min(c + NBUF - 1, n_chunks) - c - 1;
+            if constexpr (NBUF > 2) {
+                if (ahead >= 2) wait_vmcnt<2 * GPR>();
+                else if (ahead == 1) wait_vmcnt<GPR>();
+                else wait_vmcnt<0>();
+            } else {
+                if (ahead >= 1) wait_vmcnt<GPR>();
+                else wait_vmcnt<0>();
+            }
+            // A workgroup barrier without the release fence of __syncthreads
+            // (that fence would wait for every copy in flight); the wait
+            // above has already made chunk c visible in LDS.
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            if (c + NBUF - 1 < n_chunks) issue(c + NBUF - 1);
+        }
+        wait_vmcnt<0>();
+        return;
+    }
+
+    // Consumers: wave w scores rows [i0 + 16 w, +16) against each chunk.
+    const int wi0 = i0 + wave * 16;
     const int my_i = min(wi0 + n, a.rows - 1);
     const bool live = wi0 + n < a.rows;
     const int my_len = live ? row_len(a, my_i) : 0;
@@ -223,58 +299,31 @@ __global__ __launch_bounds__(256) void prefill_filter_kernel(PrefillArgs a) {
     const int w_kmin = wave_live ? row_len(a, wi0) : 0;
     Frag<DT, D> fq;
     fq.load(static_cast<const uint8_t*>(a.q) + ((size_t)b * a.n_q + qrow(a, my_i)) * RB, g);
+    wait_vmcnt<0>();  // the query fragment is in registers before the chunk loop
     uint2* list = a.cand + ((size_t)b * a.rows + my_i) * a.cap;
     const uint32_t cap = (uint32_t)a.cap;
     uint32_t cnt = 0;  // the row's list length (same in the row's 4 lanes)
 
-    auto load_chunk = [&](int c, i32x4* stg) {
-        const uint8_t* src = kbase + (size_t)c * CHUNK_BYTES;
-        const size_t lim = (size_t)(a.n_k - c * FL_CHUNK) * RB;  // bytes of valid keys
-#pragma unroll
-        for (int i = 0; i < LD_PER_THREAD; ++i) {
-            const size_t off = (size_t)(threadIdx.x + 256 * i) * 16;
-            stg[i] = off < (size_t)CHUNK_BYTES && off < lim
-                         ? *reinterpret_cast<const i32x4*>(src + off)
-                         : i32x4{0, 0, 0, 0};
-        }
-    };
-    auto store_chunk = [&](int buf, const i32x4* stg) {
-#pragma unroll
-        for (int i = 0; i < LD_PER_THREAD; ++i) {
-            const int off = (threadIdx.x + 256 * i) * 16;
-            if (off < CHUNK_BYTES) {
-                const int row = off / RB, col = off % RB;
-                *reinterpret_cast<i32x4*>(&kt[buf][row * PITCH + col]) = stg[i];
-            }
-        }
-    };
-
-    // A operand row n of key tile u is key 16 (n / 4) + 4 u + n % 4 of the
-    // chunk, so output row 4 g + r of tile u is key 16 g + 4 u + r: lane
-    // (n, g) holds keys [16 g, 16 g + 16) of the chunk for query n.
-    const int krow = 16 * (n >> 2) + (n & 3);
-
-    i32x4 stg[LD_PER_THREAD];
-    if (n_chunks > 0) {
-        load_chunk(0, stg);
-        store_chunk(0, stg);
-    }
-    __syncthreads();
+    // A operand row n of key tile u is chunk key 16 (n / 4) + 4 u + n % 4
+    // (row position 16 u + n), so output row 4 g + r of tile u is key
+    // 16 g + 4 u + r: lane (n, g) holds keys [16 g, 16 g + 16) of the chunk.
     for (int c = 0; c < n_chunks; ++c) {
-        const int buf = c & 1;
-        if (c + 1 < n_chunks) load_chunk(c + 1, stg);
+        __syncthreads();
         const int k0 = c * FL_CHUNK;
         if (k0 < w_kend) {
+            const uint8_t* tile = ring[c % NBUF];
+            // Every fragment load of the chunk completes before the first
+            // MFMA, so no load can overwrite an operand register of an MFMA
+            // still queued behind a dependent accumulate chain.
+            Frag<DT, D> fk[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) load_cm<COLB>(fk[u], tile, 16 * u + n, g);
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+            __builtin_amdgcn_sched_barrier(0);
             f32x4 acc[4];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                Frag<DT, D> fk;
-                fk.load(&kt[buf][(krow + 4 * u) * PITCH], g);
-                acc[u] = tile_dot<D>(fk, fq);
-            }
-            if constexpr (DT == 0) {
-                if constexpr (Frag<0, D>::NB > 0) mfma_drain();
-            }
+            for (int u = 0; u < 4; ++u) acc[u] = tile_dot<D>(fk[u], fq);
+            __builtin_amdgcn_sched_barrier(0);
             // bit i of rej: sign of (accumulator of key 16 g + i) - tau
             uint32_t rej = 0;
 #pragma unroll
@@ -292,24 +341,26 @@ __global__ __launch_bounds__(256) void prefill_filter_kernel(PrefillArgs a) {
             const uint32_t s01 = lc + x1;
             const uint32_t x2 = (uint32_t)__shfl_xor((int)s01, 32);
             const uint32_t tot = s01 + x2;
-            uint32_t o = cnt + ((g & 1) ? x1 : 0u) + ((g & 2) ? x2 : 0u);
-            if (cnt + tot > cap) bits = 0u;  // overflowing row: its list is abandoned
+            const uint32_t o = cnt + ((g & 1) ? x1 : 0u) + ((g & 2) ? x2 : 0u);
+            // An overflowing row's list is abandoned (the row is recomputed
+            // by the fallback); nothing is stored at or past cap.
+            const uint32_t ne = cnt + tot > cap ? 0u : lc;
+            if (ne == 0u) bits = 0u;
             cnt += tot;
             if (__ballot(bits != 0u) != 0ull) {
 #pragma unroll
                 for (int u = 0; u < 4; ++u) stage[wave][u][lane] = acc[u];
+                const float* st = reinterpret_cast<const float*>(&stage[wave][0][lane]);
                 const uint32_t kb = (uint32_t)(k0 + 16 * g);
+                uint32_t oo = o;
                 while (bits != 0u) {
                     const int i = __builtin_ctz(bits);
                     bits &= bits - 1u;
-                    const float v = reinterpret_cast<const float*>(&stage[wave][i >> 2][lane])[i & 3];
-                    list[o] = make_uint2(__float_as_uint(v), kb + (uint32_t)i);
-                    ++o;
+                    list[oo++] = make_uint2(__float_as_uint(st[(i >> 2) * 256 + (i & 3)]),
+                                            kb + (uint32_t)i);
                 }
             }
         }
-        if (c + 1 < n_chunks) store_chunk(buf ^ 1, stg);
-        __syncthreads();
     }
     if (g == 0 && live) a.cnt[(size_t)b * a.rows + my_i] = cnt;
 }
@@ -320,133 +371,195 @@ __device__ __forceinline__ uint32_t cand_key(uint32_t acc_bits, float scale) {
     return rank_key(relu_scaled(__uint_as_float(acc_bits), scale));
 }
 
-// One 64-thread workgroup (one wave) per row; the list is read from global
-// memory on every pass.
-__global__ __launch_bounds__(64) void prefill_select_kernel(PrefillArgs a) {
-    __shared__ uint32_t hist[BINS];
-    const int lane = threadIdx.x;
+constexpr int SL_NT = 256;      // threads per select workgroup (one row each)
+constexpr int SL_BINS = 4096;   // 12-bit digits of the relative order keys
+
+// Sum over the SL_NT-thread workgroup (contains barriers).
+__device__ __forceinline__ uint32_t block_total(uint32_t v, uint32_t* wsum) {
+    uint32_t tot;
+    block_excl_scan<SL_NT>(v, wsum, &tot);
+    return tot;
+}
+
+// Bin of an SL_BINS histogram holding the rem-th largest counted key:
+// res[0] = bin, res[1] = keys in higher bins. Contains barriers.
+__device__ __forceinline__ void block_find_bin(const uint32_t* hist, uint32_t rem,
+                                               uint32_t* wsum, uint32_t* res) {
+    constexpr int PER = SL_BINS / SL_NT;
+    const int hi = SL_BINS - 1 - (int)threadIdx.x * PER;
+    uint32_t c[PER], loc = 0;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+        c[q] = hist[hi - q];
+        loc += c[q];
+    }
+    uint32_t tot;
+    uint32_t above = block_excl_scan<SL_NT>(loc, wsum, &tot);
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+        if (above < rem && above + c[q] >= rem) {
+            res[0] = (uint32_t)(hi - q);
+            res[1] = above;
+        }
+        above += c[q];
+    }
+    __syncthreads();
+}
+
+// One SL_NT-thread workgroup per row. Thread t holds list entries
+// [t P, t P + P) in registers (P even, P <= PER), so the workgroup's
+// registers hold the list in index order.
+template <int PER>
+__global__ __launch_bounds__(SL_NT) void prefill_select_kernel(PrefillArgs a) {
+    __shared__ uint32_t hist[SL_BINS];
+    __shared__ uint32_t wsum[SL_NT / 64];
+    __shared__ uint32_t res[4];
+    const int tid = threadIdx.x;
     const long long task = blockIdx.x;
     const int b = (int)(task / a.rows), i = (int)(task % a.rows);
     const int n = row_len(a, i);
     const int k = a.top_k;
     int32_t* out = a.idx + ((size_t)b * a.n_q + qrow(a, i)) * k;
     if (n <= k) {
-        fill_prefix(out, n, k, lane, 64);
+        fill_prefix(out, n, k, tid, SL_NT);
         return;
     }
     const uint32_t cnt = a.cnt[task];
     const bool zero_mode = __float_as_uint(a.tau_acc[task]) == 0u;
     if (cnt > (uint32_t)a.cap || (!zero_mode && cnt < (uint32_t)k)) {
-        if (lane == 0) a.fb_list[atomicAdd(a.fb_count, 1u)] = (uint32_t)task;
+        if (tid == 0) a.fb_list[atomicAdd(a.fb_count, 1u)] = (uint32_t)task;
         return;
     }
     const uint2* cl = a.cand + (size_t)task * a.cap;
     const int cn = (int)cnt;
     const float scale = a.scale;
     constexpr uint32_t ZERO_KEY = 0x80000000u;  // order key of a zero score
+    const int P = (cn + 2 * SL_NT - 1) / (2 * SL_NT) * 2;
+    const int c0 = tid * P;
+    uint32_t key[PER], idx[PER];
+#pragma unroll
+    for (int e = 0; e < PER; e += 2) {
+        key[e] = key[e + 1] = 0u;
+        idx[e] = idx[e + 1] = 0u;
+        const int c = c0 + e;
+        if (e < P && c < cn) {
+            uint4 v;
+            if (c + 1 < cn) {
+                v = *reinterpret_cast<const uint4*>(cl + c);
+            } else {
+                const uint2 w = cl[c];
+                v = make_uint4(w.x, w.y, 0u, 0u);
+            }
+            key[e] = cand_key(v.x, scale);
+            idx[e] = v.y;
+            if (c + 1 < cn) {
+                key[e + 1] = cand_key(v.z, scale);
+                idx[e + 1] = v.w;
+            }
+        }
+    }
+    auto valid = [&](int e) { return e < P && c0 + e < cn; };
 
     if (zero_mode) {
         // The list holds every key with a positive score (plus some zeros);
         // every key off the list scores zero.
-        uint32_t np = 0;
-        for (int c = lane; c < cn; c += 64) np += cand_key(cl[c].x, scale) > ZERO_KEY ? 1u : 0u;
-        np = wave_sum(np);
+        uint32_t npl = 0;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) npl += valid(e) && key[e] > ZERO_KEY ? 1u : 0u;
+        uint32_t np;
+        const uint32_t pbase = block_excl_scan<SL_NT>(npl, wsum, &np);
         if (np < (uint32_t)k) {
             // Positives plus the lowest-index zeros. With P the positives in
             // index order, P[r] - r zeros precede P[r]; the first cs
             // positives (P[r] - r < Z) come before the Z-th zero.
             const uint32_t Z = (uint32_t)k - np;
-            uint32_t run = 0, cs = 0;
-            for (int c0 = 0; c0 < cn; c0 += 64) {
-                const int c = c0 + lane;
-                bool pos = false;
-                uint32_t j = 0;
-                if (c < cn) {
-                    const uint2 e = cl[c];
-                    pos = cand_key(e.x, scale) > ZERO_KEY;
-                    j = e.y;
+            uint32_t r = pbase, csl = 0;
+#pragma unroll
+            for (int e = 0; e < PER; ++e) {
+                if (valid(e) && key[e] > ZERO_KEY) {
+                    csl += idx[e] - r < Z ? 1u : 0u;
+                    ++r;
                 }
-                const unsigned long long pm = __ballot(pos);
-                const uint32_t r = run + (uint32_t)__popcll(pm & lanes_below());
-                cs += (uint32_t)__popcll(__ballot(pos && j - r < Z));
-                run += (uint32_t)__popcll(pm);
             }
+            const uint32_t cs = block_total(csl, wsum);
             const uint32_t head = Z + cs;  // out[0, head) = 0 .. head - 1
-            for (uint32_t o = lane; o < head; o += 64) out[o] = (int32_t)o;
-            run = 0;
-            for (int c0 = 0; c0 < cn; c0 += 64) {
-                const int c = c0 + lane;
-                bool pos = false;
-                uint32_t j = 0;
-                if (c < cn) {
-                    const uint2 e = cl[c];
-                    pos = cand_key(e.x, scale) > ZERO_KEY;
-                    j = e.y;
+            for (uint32_t o = tid; o < head; o += SL_NT) out[o] = (int32_t)o;
+            r = pbase;
+#pragma unroll
+            for (int e = 0; e < PER; ++e) {
+                if (valid(e) && key[e] > ZERO_KEY) {
+                    if (r >= cs) out[Z + r] = (int32_t)idx[e];
+                    ++r;
                 }
-                const unsigned long long pm = __ballot(pos);
-                const uint32_t r = run + (uint32_t)__popcll(pm & lanes_below());
-                if (pos && r >= cs) out[Z + r] = (int32_t)j;
-                run += (uint32_t)__popcll(pm);
             }
             return;
         }
     }
 
-    auto wave_sync = [] {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-        __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    };
-    // Exact k-th key: digits 31..21, 20..10, 9..0.
-    uint32_t rem = (uint32_t)k, prefix = 0;
-#pragma unroll 1
-    for (int round = 0; round < 3; ++round) {
-        const int sh = round == 0 ? 21 : (round == 1 ? 10 : 0);
-        const int psh = round == 1 ? 21 : 10;  // prefix bits of the earlier rounds
-        const uint32_t msk = round == 2 ? 1023u : 2047u;
-        for (int t = lane; t < BINS; t += 64) hist[t] = 0u;
-        wave_sync();
-        for (int c0 = 0; c0 < cn; c0 += 256) {
-            uint32_t key[4];
-            bool ok[4];
+    // Range of the row's order keys: digits are taken relative to the
+    // smallest, over only as many 12-bit rounds as the range needs.
+    uint32_t lo = 0xffffffffu, hi = 0u;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int c = c0 + 64 * u + lane;
-                ok[u] = c < cn;
-                key[u] = ok[u] ? cand_key(cl[c].x, scale) : 0u;
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const bool in = ok[u] && (round == 0 || (key[u] >> psh) == prefix);
-                hist_add(hist, (key[u] >> sh) & msk, in);
-            }
+    for (int e = 0; e < PER; ++e) {
+        if (valid(e)) {
+            lo = min(lo, key[e]);
+            hi = max(hi, key[e]);
         }
-        wave_sync();
-        uint32_t above;
-        const uint32_t bin = wave_find_bin<BINS>(hist, rem, &above);
-        prefix = round == 0 ? bin : ((prefix << (round == 1 ? 11 : 10)) | bin);
-        rem -= above;
-        wave_sync();
     }
-    const uint32_t T = prefix;  // keep every key above T and the first rem keys equal to T
-    // Ordered compaction over the index-ordered list.
-    uint32_t base = 0, eq_run = 0;
-    for (int c0 = 0; c0 < cn && base < (uint32_t)k; c0 += 64) {
-        const int c = c0 + lane;
-        uint32_t key = 0, j = 0;
-        if (c < cn) {
-            const uint2 e = cl[c];
-            key = cand_key(e.x, scale);
-            j = e.y;
+    if (tid == 0) {
+        res[2] = 0xffffffffu;
+        res[3] = 0u;
+    }
+    __syncthreads();
+    if (lo <= hi) {
+        atomicMin(&res[2], lo);
+        atomicMax(&res[3], hi);
+    }
+    __syncthreads();
+    const uint32_t kmin = res[2];
+    const uint32_t range = res[3] - kmin;
+    __syncthreads();
+    const int R = (32 - __clz((int)range) + 11) / 12;  // 0..3 rounds
+    uint32_t rem = (uint32_t)k, prefix = 0;
+    for (int r = 0; r < R; ++r) {
+        const int sh = 12 * (R - 1 - r);
+        const int hsh = r == 0 ? 0 : sh + 12;
+        for (int q = tid; q < SL_BINS; q += SL_NT) hist[q] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            const uint32_t d = key[e] - kmin;
+            if (valid(e) && (r == 0 || (d >> hsh) == prefix)) atomicAdd(&hist[(d >> sh) & 4095u], 1u);
         }
-        const bool gt = c < cn && key > T;
-        const bool eq = c < cn && key == T;
-        const unsigned long long me = __ballot(eq);
-        const bool keep = gt || (eq && eq_run + (uint32_t)__popcll(me & lanes_below()) < rem);
-        const unsigned long long mk = __ballot(keep);
-        if (keep) out[base + (uint32_t)__popcll(mk & lanes_below())] = (int32_t)j;
-        base += (uint32_t)__popcll(mk);
-        eq_run += (uint32_t)__popcll(me);
+        __syncthreads();
+        block_find_bin(hist, rem, wsum, res);
+        prefix = (prefix << 12) | res[0];
+        rem -= res[1];
+        __syncthreads();
+    }
+    const uint32_t T = kmin + prefix;  // keep every key above T and the first rem keys equal to T
+    // Ordered compaction over the index-ordered list.
+    uint32_t gtl = 0, eql = 0;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+        if (valid(e)) {
+            gtl += key[e] > T ? 1u : 0u;
+            eql += key[e] == T ? 1u : 0u;
+        }
+    }
+    uint32_t tot;
+    const uint32_t pk = block_excl_scan<SL_NT>((gtl << 16) | eql, wsum, &tot);
+    uint32_t gb = pk >> 16, eb = pk & 0xffffu;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+        if (!valid(e)) continue;
+        if (key[e] > T) {
+            out[gb + min(eb, rem)] = (int32_t)idx[e];
+            ++gb;
+        } else if (key[e] == T) {
+            if (eb < rem) out[gb + eb] = (int32_t)idx[e];
+            ++eb;
+        }
     }
 }
 
@@ -499,10 +612,16 @@ hipError_t launch_d(const PrefillArgs& a, int part, hipStream_t s) {
     } else if (part == 1) {
         const long long nb = (long long)a.B * ((a.rows + FL_ROWS - 1) / FL_ROWS);
         if (nb > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL((prefill_filter_kernel<DT, D>), dim3((unsigned)nb), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((prefill_filter_kernel<DT, D>), dim3((unsigned)nb), dim3(320), 0, s, a);
     } else if (part == 2) {
         if (rows > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL(prefill_select_kernel, dim3((unsigned)rows), dim3(64), 0, s, a);
+        const dim3 grid((unsigned)rows), blk(SL_NT);
+        if (a.cap <= 4 * SL_NT) hipLaunchKernelGGL(prefill_select_kernel<4>, grid, blk, 0, s, a);
+        else if (a.cap <= 8 * SL_NT) hipLaunchKernelGGL(prefill_select_kernel<8>, grid, blk, 0, s, a);
+        else if (a.cap <= 16 * SL_NT) hipLaunchKernelGGL(prefill_select_kernel<16>, grid, blk, 0, s, a);
+        else if (a.cap <= 28 * SL_NT) hipLaunchKernelGGL(prefill_select_kernel<28>, grid, blk, 0, s, a);
+        else if (a.cap <= 52 * SL_NT) hipLaunchKernelGGL(prefill_select_kernel<52>, grid, blk, 0, s, a);
+        else return hipErrorInvalidValue;
     } else {
         hipLaunchKernelGGL((prefill_fallback_kernel<DT, D>), dim3(FB_WGS), dim3(512), 0, s, a);
     }
