@@ -28,8 +28,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # Sources of the kernels behind each stage (decode rows use decode.hip's
 # threshold / filter / select kernels).
 KERNEL_SOURCES = {
-    ("prefill", "indexer"): ["indexer.hip", "frag.h"],
-    ("prefill", "topk"): ["topk.hip", "topk_common.h"],
+    ("prefill", "indexer"): ["prefill.hip", "frag.h"],
+    ("prefill", "topk"): ["prefill.hip", "topk_common.h"],
     ("prefill", "attn"): ["attn.hip"],
     ("decode", "indexer"): ["decode.hip", "frag.h"],
     ("decode", "topk"): ["decode.hip", "topk_common.h"],

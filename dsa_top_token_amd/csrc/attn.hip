@@ -266,30 +266,55 @@ __global__ __launch_bounds__(256) void sparse_attn_split_kernel(AttnArgs a) {
     }
 }
 
-// Merge of the split partials of one query row per workgroup: thread t takes
-// head t / 16 and dims 8 * (t % 16) .. +8.
-__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
+// Merge of the split partials: a 64-thread workgroup per (query row, group of
+// four heads); thread t takes head 4 * blockIdx.y + t / 16 and dims
+// 8 * (t % 16) .. +8. One online pass (running maximum, earlier sums rescaled
+// when it grows) with sixteen splits' partials in flight at a time.
+__global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a) {
+    constexpr int G = 16;
     const long long qrow = blockIdx.x;
-    const int h = threadIdx.x >> 4, c = threadIdx.x & 15;
+    const int h = 4 * (int)blockIdx.y + (threadIdx.x >> 4), c = threadIdx.x & 15;
     if (h >= a.H) return;
     const float ninf = -__builtin_inff();
     const float* base = a.part + ((size_t)qrow * a.n_split * 16 + h) * PART;
     const size_t stride = (size_t)16 * PART;
-    float MM = ninf;
-    for (int s = 0; s < a.n_split; ++s) MM = fmaxf(MM, base[(size_t)s * stride + HD]);
-    float LL = 0.f, o8[8];
+    float MM = ninf, LL = 0.f, o8[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) o8[i] = 0.f;
-    if (MM != ninf) {
-        for (int s = 0; s < a.n_split; ++s) {
-            const float* ps = base + (size_t)s * stride;
-            const float sc = exp2f(ps[HD] - MM);
-            LL += sc * ps[HD + 1];
-            const float4 v0 = *reinterpret_cast<const float4*>(ps + 8 * c);
-            const float4 v1 = *reinterpret_cast<const float4*>(ps + 8 * c + 4);
-            o8[0] += sc * v0.x; o8[1] += sc * v0.y; o8[2] += sc * v0.z; o8[3] += sc * v0.w;
-            o8[4] += sc * v1.x; o8[5] += sc * v1.y; o8[6] += sc * v1.z; o8[7] += sc * v1.w;
+    for (int s0 = 0; s0 < a.n_split; s0 += G) {
+        float mg[G], lg[G];
+        float4 v0[G], v1[G];
+#pragma unroll
+        for (int q = 0; q < G; ++q) {
+            mg[q] = ninf;
+            lg[q] = 0.f;
+            v0[q] = v1[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (s0 + q < a.n_split) {
+                const float* ps = base + (size_t)(s0 + q) * stride;
+                mg[q] = ps[HD];
+                lg[q] = ps[HD + 1];
+                v0[q] = *reinterpret_cast<const float4*>(ps + 8 * c);
+                v1[q] = *reinterpret_cast<const float4*>(ps + 8 * c + 4);
+            }
         }
+        float cm = ninf;
+#pragma unroll
+        for (int q = 0; q < G; ++q) cm = fmaxf(cm, mg[q]);
+        const float nm = fmaxf(MM, cm);
+        if (nm == ninf) continue;
+        const float so = MM == ninf ? 0.f : exp2f(MM - nm);
+        LL *= so;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o8[i] *= so;
+#pragma unroll
+        for (int q = 0; q < G; ++q) {
+            if (mg[q] == ninf) continue;
+            const float sc = exp2f(mg[q] - nm);
+            LL += sc * lg[q];
+            o8[0] += sc * v0[q].x; o8[1] += sc * v0[q].y; o8[2] += sc * v0[q].z; o8[3] += sc * v0[q].w;
+            o8[4] += sc * v1[q].x; o8[5] += sc * v1[q].y; o8[6] += sc * v1[q].z; o8[7] += sc * v1[q].w;
+        }
+        MM = nm;
     }
     const float inv = LL > 0.f ? 1.f / LL : 0.f;
     bf16x8 h8;
@@ -303,7 +328,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
 
 void attn_split_plan(int B, int n_q, int k, int* n_split, int* split_len) {
     // Many rows: one wave per row. Few rows: 4-wave workgroups per (row,
-    // split), splits of a multiple of 128 slots, about 4096 waves in all.
+    // split), splits of a multiple of 128 slots, about 2048 waves in all.
     const long long rows = (long long)B * n_q;
     if (rows >= 2048) {
         *n_split = 1;
@@ -311,7 +336,7 @@ void attn_split_plan(int B, int n_q, int k, int* n_split, int* split_len) {
         return;
     }
     const int max_split = (k + 127) / 128;
-    long long want = (1024 + rows - 1) / rows;
+    long long want = (512 + rows - 1) / rows;
     int ns = (int)(want < 1 ? 1 : (want > max_split ? max_split : want));
     int len = (k + ns - 1) / ns;
     len = (len + 127) / 128 * 128;
@@ -331,7 +356,8 @@ hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t s) {
     }
     const long long nb = rows * a.n_split;
     hipLaunchKernelGGL(sparse_attn_split_kernel, dim3((unsigned)nb), dim3(256), 0, s, a);
-    hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)rows), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)rows, (unsigned)((a.H + 3) / 4)), dim3(64), 0,
+                       s, a);
     return hipGetLastError();
 }
 

@@ -12,7 +12,9 @@
 //   filter     the streaming indexer kernel scores every key and keeps only
 //              those whose order key is >= tau, each wave writing its own
 //              (order key, index) list for its 256 keys in ascending index
-//              order (no device atomics).
+//              order (no device atomics). 128-byte key rows are streamed by
+//              contiguous nontemporal global->LDS copies into a two-buffer
+//              ring per wave; other widths load MFMA fragments directly.
 //   select     one workgroup per sequence loads the candidates into LDS,
 //              finds the exact k-th key T by radix rounds, cuts the T-ties at
 //              the index j_T that keeps the lowest indices, and writes the
@@ -222,6 +224,144 @@ __global__ __launch_bounds__(256) void decode_filter_kernel(DecodeArgs a) {
     if (lane == 0 && slot < n_slots) a.cnt[(size_t)b * n_slots + slot] = count;
 }
 
+// Cache-policy operand of a global->LDS copy: nontemporal (keys are streamed
+// once).
+constexpr int kNontemporal = 2;
+
+// s_waitcnt with vmcnt = N (expcnt and lgkmcnt left open).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
+}
+
+// 128-byte key rows staged in LDS by contiguous 1 KB global->LDS copies.
+// Granule j (16 bytes) of row r of a 64-row buffer sits at 16-byte slot
+// 8 r + (j ^ f(r)), f(r) = (r mod 8) ^ ((r / 8) mod 2): each copy
+// instruction still covers 8 whole rows of global memory, and the 16 rows a
+// fragment read touches (fixed j) land in 16 distinct bank groups.
+__device__ __forceinline__ int sw_slot(int r, int j) { return 8 * r + (j ^ ((r & 7) ^ ((r >> 3) & 1))); }
+
+template <int DT, int D>
+__device__ __forceinline__ void load_sw(Frag<DT, D>& f, const uint8_t* buf, int r, int g) {
+    static_assert(D * (DT == 0 ? 1 : 2) == 128, "128-byte rows");
+    const i32x4 lo = *reinterpret_cast<const i32x4*>(buf + 16 * sw_slot(r, g));
+    const i32x4 hi = *reinterpret_cast<const i32x4*>(buf + 16 * sw_slot(r, g + 4));
+    if constexpr (DT == 0) {
+        f.big[0] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    } else {
+        f.v[0] = __builtin_bit_cast(bf16x8, lo);
+        f.v[1] = __builtin_bit_cast(bf16x8, hi);
+    }
+}
+
+// The filter for 128-byte key rows: each wave streams its 256 keys in four
+// 64-key steps through a two-buffer LDS ring (contiguous 1 KB copies), the
+// same scores and candidate lists as decode_filter_kernel.
+template <int DT, int D>
+__global__ __launch_bounds__(256) void decode_filter_lds_kernel(DecodeArgs a) {
+    constexpr int TILES = 4, STEPS = 4;
+    constexpr int RB = 128;
+    constexpr int KW = 16 * TILES * STEPS;  // = SLOT
+    constexpr int KB = 4 * KW;
+    constexpr int STEP_BYTES = 16 * TILES * RB;  // 8 KB = 8 copies of 1 KB
+    static_assert(KW == SLOT && D * (DT == 0 ? 1 : 2) == RB, "one candidate list per wave");
+    __shared__ __attribute__((aligned(16))) uint8_t ring[4][2][STEP_BYTES];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n = lane & 15, g = lane >> 4;
+    const int n_kb = (a.n_k + KB - 1) / KB;
+    const int kb = blockIdx.x % n_kb, b = blockIdx.x / n_kb;
+    const Plan p = plan_row(a);
+    const int lim = p.n;
+    const int slot = kb * 4 + wave;
+    const int n_slots = (a.n_k + SLOT - 1) / SLOT;
+    const int kw0 = kb * KB + wave * KW;
+    if (kw0 >= lim) {  // no key of this wave is in the row (wave-uniform)
+        if (lane == 0 && slot < n_slots) a.cnt[(size_t)b * n_slots + slot] = 0u;
+        return;
+    }
+    const uint32_t tau = a.tau[b];
+    const uint8_t* __restrict__ kbase = static_cast<const uint8_t*>(a.k) + (size_t)b * a.n_k * RB;
+    // Copy lane l of instruction i moves granule ((l % 8) ^ f(r)) of row
+    // r = 8 i + l / 8 into slot 64 i + l.
+    auto issue = [&](int st) {
+        const int k0 = kw0 + st * 16 * TILES;
+        uint8_t* dst = ring[wave][st & 1];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = 8 * i + (lane >> 3);
+            const int j = (lane & 7) ^ ((r & 7) ^ ((r >> 3) & 1));
+            const uint8_t* src = kbase + (size_t)min(k0 + r, a.n_k - 1) * RB + 16 * j;
+            __builtin_amdgcn_global_load_lds(src, dst + 1024 * i, 16, 0, kNontemporal);
+        }
+    };
+    Frag<DT, D> fq;
+    fq.load(static_cast<const uint8_t*>(a.q) + ((size_t)b * a.n_q + a.q_row) * RB, g);
+    issue(0);
+    issue(1);
+    const int sel = n & (TILES - 1);
+    const bool writer = n < TILES;
+    uint32_t sk[STEPS][4];
+    int key0s[STEPS];
+#pragma unroll
+    for (int st = 0; st < STEPS; ++st) {
+        const int k0 = kw0 + st * 16 * TILES;
+        key0s[st] = k0 + 16 * sel + 4 * g;
+        // step st has landed once only the copies issued after it remain
+        __builtin_amdgcn_sched_barrier(0);
+        if (st + 1 < STEPS) wait_vmcnt<8>();
+        else wait_vmcnt<0>();
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        const uint8_t* buf = ring[wave][st & 1];
+        Frag<DT, D> fk[TILES];
+#pragma unroll
+        for (int t = 0; t < TILES; ++t) load_sw(fk[t], buf, 16 * t + n, g);
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the buffer may be refilled
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("" ::: "memory");
+        if (st + 2 < STEPS) issue(st + 2);
+        f32x4 acc[TILES];
+#pragma unroll
+        for (int t = 0; t < TILES; ++t) acc[t] = tile_dot_k32<D>(fk[t], fq);
+        const f32x4 v01 = (sel & 1) ? acc[1] : acc[0];
+        const f32x4 v23 = (sel & 1) ? acc[3] : acc[2];
+        const f32x4 v = (sel & 2) ? v23 : v01;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            sk[st][r] = k0 < lim ? rank_key(relu_scaled(v[r], a.scale)) : 0u;
+    }
+    // Candidates of this wave into its list in ascending index order. In a
+    // step, writer lane (sel, g) holds keys k0 + 16*sel + 4*g + r, so its place
+    // in index order is p = 4*sel + g: counts are gathered into position order
+    // (lane p takes lane 16*(p%4) + p/4), scanned, and scattered back.
+    uint2* list = a.cand + ((size_t)b * n_slots + slot) * SLOT;
+    uint32_t count = 0;
+    const int src = 16 * (lane & 3) + ((lane >> 2) & 3);
+    const int myp = 4 * sel + g;
+#pragma unroll
+    for (int st = 0; st < STEPS; ++st) {
+        bool c[4];
+        uint32_t cl = 0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int j = key0s[st] + r;
+            c[r] = writer && j < lim && sk[st][r] >= tau;
+            cl += c[r] ? 1u : 0u;
+        }
+        uint32_t cp = (uint32_t)__shfl((int)cl, src);
+        if (lane >= 16) cp = 0u;
+        const uint32_t incl = wave_incl_scan(cp);
+        const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)incl, 15);
+        uint32_t o = count + (uint32_t)__shfl((int)(incl - cp), myp);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            if (c[r]) list[o++] = make_uint2(sk[st][r], (uint32_t)(key0s[st] + r));
+        count += tot;
+    }
+    if (lane == 0 && slot < n_slots) a.cnt[(size_t)b * n_slots + slot] = count;
+}
+
 // Every score of the row (order keys) into `row` (fallback path of select).
 template <int DT, int D>
 __device__ void row_scores(const DecodeArgs& a, int b, int nkeys, float* row) {
@@ -390,7 +530,10 @@ hipError_t launch_d(const DecodeArgs& a, int part, hipStream_t s) {
         const int KB = 4 * SLOT;
         const long long nb = (long long)a.B * ((a.n_k + KB - 1) / KB);
         if (nb > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL((decode_filter_kernel<DT, D>), dim3((unsigned)nb), dim3(256), 0, s, a);
+        if constexpr (D * (DT == 0 ? 1 : 2) == 128)
+            hipLaunchKernelGGL((decode_filter_lds_kernel<DT, D>), dim3((unsigned)nb), dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL((decode_filter_kernel<DT, D>), dim3((unsigned)nb), dim3(256), 0, s, a);
     } else {
         hipLaunchKernelGGL((decode_select_kernel<DT, D>), dim3(a.B), dim3(SEL_NT), 0, s, a);
     }
