@@ -5,10 +5,11 @@
 // scores every key of the query's prefix and the query keeps its top_k keys.
 // Here the full score row never reaches memory:
 //   threshold  one workgroup per sequence scores every S-th key
-//              (S = max(32, ceil(n/8192))) and takes as tau the lower edge
-//              of the 22-bit radix bin holding the m-th largest order key of
-//              that sample, m = ceil(1.5 * top_k / S). About 1.5 * top_k keys
-//              of the row are expected to reach tau.
+//              (S = max(top_k / 32, ceil(n/8192))) and takes as tau the lower edge
+//              of the bin (two 8-bit radix rounds over the sample keys
+//              relative to the smallest) holding the m-th largest sample,
+//              m = ceil(2 * top_k / S). About 2 * top_k keys of the row are
+//              expected to reach tau.
 //   filter     the streaming indexer kernel scores every key and keeps only
 //              those whose order key is >= tau, each wave writing its own
 //              (order key, index) list for its 256 keys in ascending index
@@ -16,9 +17,10 @@
 //              contiguous nontemporal global->LDS copies into a two-buffer
 //              ring per wave; other widths load MFMA fragments directly.
 //   select     one workgroup per sequence loads the candidates into LDS,
-//              finds the exact k-th key T by radix rounds, cuts the T-ties at
-//              the index j_T that keeps the lowest indices, and writes the
-//              selection in ascending index order.
+//              finds the exact k-th key T by 12-bit radix rounds over the
+//              keys relative to the smallest candidate, and writes the
+//              selection in ascending index order, cutting the T-ties in
+//              list (= index) order.
 // The result is exact whenever at least top_k keys reach tau, which select
 // checks; otherwise (or when the candidates exceed its LDS list) select
 // recomputes the row's scores into the workspace and runs the per-row radix
@@ -32,7 +34,6 @@ namespace {
 using namespace frag;
 using namespace topk;
 
-constexpr int TH_NT = 1024;
 constexpr int TH_TILES = 8;       // sample tiles a threshold wave loads at once
 constexpr int TH_MAX_SAMPLES = 8192;
 constexpr int SLOT = 256;          // keys per filter wave = one candidate list
@@ -48,42 +49,12 @@ __device__ __forceinline__ Plan plan_row(const DecodeArgs& a) {
     Plan p;
     const long long pos = (long long)a.q_pos0 + a.q_row;
     p.n = (int)min((long long)a.n_k, pos + 1);
-    p.S = max(32, (p.n + TH_MAX_SAMPLES - 1) / TH_MAX_SAMPLES);
+    // about 64 samples are expected above tau (sd ~ S sqrt(m)): the miss
+    // margin (k of the expected 2k candidates) is sqrt(k / (2 S)) = 4 sd
+    p.S = max(max(1, a.top_k / 32), (p.n + TH_MAX_SAMPLES - 1) / TH_MAX_SAMPLES);
     p.ns = (p.n + p.S - 1) / p.S;
-    p.m = (3 * a.top_k + 2 * p.S - 1) / (2 * p.S);  // ceil(1.5 k / S)
+    p.m = (2 * a.top_k + p.S - 1) / p.S;  // ceil(2 k / S)
     return p;
-}
-
-// m-th largest (m >= 1) of cnt order keys held in LDS, by radix rounds on
-// 11 + 11 + 10 bits. With ROUNDS = 2 the result is the lower edge of the
-// 22-bit bin holding the m-th largest key (at least m keys are >= it).
-template <int NT, int ROUNDS = 3>
-__device__ uint32_t kth_largest(const uint32_t* keys, int cnt, uint32_t m, uint32_t* hist,
-                                uint32_t* wsum, uint32_t* res) {
-    const int tid = threadIdx.x;
-    uint32_t prefix = 0;
-    int shift_done = 32;
-    const int shifts[3] = {SHIFT1, SHIFT2, 0};
-    const uint32_t masks[3] = {2047u, 2047u, 1023u};
-#pragma unroll
-    for (int round = 0; round < ROUNDS; ++round) {
-        const int sh = shifts[round];
-        for (int i = tid; i < BINS; i += NT) hist[i] = 0u;
-        __syncthreads();
-        for (int base = 0; base < cnt; base += NT) {
-            const int i = base + tid;
-            const uint32_t key = i < cnt ? keys[i] : 0u;
-            const bool in = i < cnt && (shift_done >= 32 || (key >> shift_done) == prefix);
-            hist_add(hist, (key >> sh) & masks[round], in);
-        }
-        __syncthreads();
-        find_bin<NT>(hist, m, wsum, res);
-        prefix = (shift_done >= 32 ? 0u : prefix << (shift_done - sh)) | res[0];
-        m -= res[1];
-        shift_done = sh;
-        __syncthreads();
-    }
-    return prefix << shift_done;
 }
 
 // Scores of keys t0 + 16*0.., as order keys, for the 16 keys of one tile whose
@@ -97,25 +68,57 @@ __device__ __forceinline__ f32x4 key_tile(const uint8_t* kbase, int key_row, con
     return tile_dot_k32<D>(fk, fq);
 }
 
+constexpr int TH_NT = 1024;   // threads of the threshold workgroup (one per row)
+constexpr int RB12 = 4096;    // 12-bit digits of the select rounds
+
+// Bin of a 256-bin histogram holding the rem-th largest counted key, found
+// by wave 0 alone: res[0] = bin, res[1] = keys in higher bins.
+__device__ __forceinline__ void find_bin8(const uint32_t* hist, uint32_t rem, uint32_t* res) {
+    if (threadIdx.x >= 64) return;
+    const int lane = threadIdx.x;
+    const int hi = 255 - 4 * lane;
+    uint32_t c[4], loc = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        c[q] = hist[hi - q];
+        loc += c[q];
+    }
+    uint32_t above = wave_incl_scan(loc) - loc;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        if (above < rem && above + c[q] >= rem) {
+            res[0] = (uint32_t)(hi - q);
+            res[1] = above;
+        }
+        above += c[q];
+    }
+}
+
+// Sampled threshold of each row: every S-th key's order key into LDS, then
+// two 8-bit radix rounds over the keys relative to the smallest sample give
+// the lower edge of the bin holding the m-th largest sample (at least m
+// samples reach it). tau only steers how many candidates the filter keeps;
+// the selection is exact for any tau.
 template <int DT, int D>
 __global__ __launch_bounds__(TH_NT) void decode_threshold_kernel(DecodeArgs a) {
     __shared__ uint32_t samp[TH_MAX_SAMPLES];
-    __shared__ uint32_t hist[BINS];
-    __shared__ uint32_t wsum[TH_NT / 64];
+    __shared__ uint32_t hist[256];
     __shared__ uint32_t res[4];
     constexpr int RB = D * (DT == 0 ? 1 : 2);
+    const int tid = threadIdx.x;
     const int b = blockIdx.x;
     const Plan p = plan_row(a);
     if (p.n <= a.top_k || p.ns <= p.m) {
-        if (threadIdx.x == 0) a.tau[b] = 0u;  // every key is a candidate
+        if (tid == 0) a.tau[b] = 0u;  // every key is a candidate
         return;
     }
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = tid & 63, wave = tid >> 6;
     const int n = lane & 15, g = lane >> 4;
     Frag<DT, D> fq;
     fq.load(static_cast<const uint8_t*>(a.q) + ((size_t)b * a.n_q + a.q_row) * RB, g);
     const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + (size_t)b * a.n_k * RB;
     // Waves take TH_TILES tiles of 16 samples at a time, all loads first.
+    uint32_t lo = 0xffffffffu, hi = 0u;
     for (int t0 = wave * 16 * TH_TILES; t0 < p.ns; t0 += (TH_NT / 64) * 16 * TH_TILES) {
         Frag<DT, D> fk[TH_TILES];
 #pragma unroll
@@ -129,14 +132,78 @@ __global__ __launch_bounds__(TH_NT) void decode_threshold_kernel(DecodeArgs a) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int i = t0 + 16 * t + 4 * g + r;
-                    if (i < p.ns) samp[i] = rank_key(relu_scaled(acc[r], a.scale));
+                    if (i < p.ns) {
+                        const uint32_t key = rank_key(relu_scaled(acc[r], a.scale));
+                        samp[i] = key;
+                        lo = min(lo, key);
+                        hi = max(hi, key);
+                    }
                 }
             }
         }
     }
+    if (tid == 0) {
+        res[2] = 0xffffffffu;
+        res[3] = 0u;
+    }
     __syncthreads();
-    const uint32_t tau = kth_largest<TH_NT, 2>(samp, p.ns, (uint32_t)p.m, hist, wsum, res);
-    if (threadIdx.x == 0) a.tau[b] = tau;
+    lo = wave_min(lo);
+    hi = wave_max(hi);
+    if (lane == 0) {
+        atomicMin(&res[2], lo);
+        atomicMax(&res[3], hi);
+    }
+    __syncthreads();
+    const uint32_t kmin = res[2];
+    const uint32_t range = res[3] - kmin;
+    const int bits = 32 - __clz((int)range);
+    uint32_t rem = (uint32_t)p.m, prefix = 0;
+    int sh = bits;
+    for (int r = 0; r < 2 && sh > 0; ++r) {
+        const int hsh = sh;
+        sh = sh > 8 ? sh - 8 : 0;
+        if (tid < 256) hist[tid] = 0u;
+        __syncthreads();
+        for (int i0 = 0; i0 < p.ns; i0 += TH_NT) {
+            const int i = i0 + tid;
+            const uint32_t d = i < p.ns ? samp[i] - kmin : 0u;
+            const uint32_t dmask = (1u << (hsh - sh)) - 1u;  // this round's bits [sh, hsh)
+            hist_add(hist, (d >> sh) & dmask, i < p.ns && (r == 0 || (d >> hsh) == prefix));
+        }
+        __syncthreads();
+        find_bin8(hist, rem, res);
+        __syncthreads();
+        prefix = (prefix << (hsh - sh)) | res[0];
+        rem -= res[1];
+        __syncthreads();
+    }
+    if (tid == 0) a.tau[b] = kmin + (prefix << sh);
+}
+
+// Bin of an RB12-bin histogram holding the rem-th largest counted key over
+// an NT-thread workgroup: res[0] = bin, res[1] = keys in higher bins.
+template <int NT>
+__device__ __forceinline__ void find_bin12(const uint32_t* hist, uint32_t rem, uint32_t* wsum,
+                                           uint32_t* res) {
+    constexpr int PER = RB12 / NT;
+    const int hi = RB12 - 1 - (int)threadIdx.x * PER;
+    uint32_t c[PER], loc = 0;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+        c[q] = hist[hi - q];
+        loc += c[q];
+    }
+    uint32_t tot;
+    uint32_t above = block_excl_scan<NT>(loc, wsum, &tot);
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+        if (above < rem && above + c[q] >= rem) {
+            res[0] = (uint32_t)(hi - q);
+            res[1] = above;
+        }
+        above += c[q];
+    }
+    __syncthreads();
 }
 
 // The streaming indexer of one query row per sequence (see index_decode_kernel
@@ -387,7 +454,7 @@ __global__ __launch_bounds__(SEL_NT) void decode_select_kernel(DecodeArgs a) {
     // scratch.
     __shared__ uint32_t keys[SEL_CAP];
     __shared__ uint32_t jj[SEL_CAP];
-    __shared__ uint32_t hist[BINS];
+    __shared__ uint32_t hist[RB12];
     __shared__ uint32_t soff[SEL_MAX_SLOTS + 1];
     __shared__ uint32_t wsum[SEL_NT / 64];
     __shared__ uint32_t res[4];
@@ -466,60 +533,68 @@ __global__ __launch_bounds__(SEL_NT) void decode_select_kernel(DecodeArgs a) {
     }
     __syncthreads();
     const int cnt = (int)total;
-    // Exact k-th key T and how many of its ties to keep.
-    const uint32_t T = kth_largest<SEL_NT>(keys, cnt, (uint32_t)k, hist, wsum, res);
-    uint32_t gt = 0, eq = 0;
+    // Exact k-th key T: 12-bit radix rounds over the order keys relative to
+    // the smallest candidate, as many as the key range needs.
+    uint32_t lo = 0xffffffffu, hi = 0u;
     for (int i = tid; i < cnt; i += SEL_NT) {
-        gt += keys[i] > T ? 1u : 0u;
-        eq += keys[i] == T ? 1u : 0u;
+        lo = min(lo, keys[i]);
+        hi = max(hi, keys[i]);
     }
-    uint32_t ge;
-    block_excl_scan<SEL_NT>((gt << 16) | eq, wsum, &ge);
-    const uint32_t n_gt = ge >> 16, n_eq = ge & 0xffffu;
-    const uint32_t rem = (uint32_t)k - n_gt;  // ties to keep, >= 1
-    // Tie cut-off j_T: the rem-th smallest index among keys equal to T, found
-    // as the rem-th largest of (2^22 - 1 - j); all ties are kept if they fit.
-    constexpr uint32_t JMAX = (1u << 22) - 1u;
-    uint32_t jT = JMAX;
-    if (n_eq > rem) {
-        for (int i = tid; i < BINS; i += SEL_NT) hist[i] = 0u;
+    if (tid == 0) {
+        res[2] = 0xffffffffu;
+        res[3] = 0u;
+    }
+    __syncthreads();
+    lo = wave_min(lo);
+    hi = wave_max(hi);
+    if ((tid & 63) == 0) {
+        atomicMin(&res[2], lo);
+        atomicMax(&res[3], hi);
+    }
+    __syncthreads();
+    const uint32_t kmin = res[2];
+    const uint32_t range = res[3] - kmin;
+    __syncthreads();
+    const int R = (32 - __clz((int)range) + 11) / 12;
+    uint32_t rem = (uint32_t)k, prefix = 0;
+    for (int r = 0; r < R; ++r) {
+        const int sh = 12 * (R - 1 - r);
+        const int hsh = r == 0 ? 0 : sh + 12;
+        for (int q = tid; q < RB12; q += SEL_NT) hist[q] = 0u;
         __syncthreads();
-        for (int base = 0; base < cnt; base += SEL_NT) {
-            const int i = base + tid;
-            const bool ok = i < cnt && keys[i] == T;
-            hist_add(hist, ok ? (JMAX - jj[i]) >> 11 : 0u, ok);
+        for (int i0 = 0; i0 < cnt; i0 += SEL_NT) {
+            const int i = i0 + tid;
+            const uint32_t d = i < cnt ? keys[i] - kmin : 0u;
+            hist_add(hist, (d >> sh) & (RB12 - 1), i < cnt && (r == 0 || (d >> hsh) == prefix));
         }
         __syncthreads();
-        find_bin<SEL_NT>(hist, rem, wsum, res);
-        const uint32_t a1 = res[0];
-        const uint32_t remj = rem - res[1];
-        __syncthreads();
-        for (int i = tid; i < BINS; i += SEL_NT) hist[i] = 0u;
-        __syncthreads();
-        for (int base = 0; base < cnt; base += SEL_NT) {
-            const int i = base + tid;
-            const bool ok = i < cnt && keys[i] == T && ((JMAX - jj[i]) >> 11) == a1;
-            hist_add(hist, ok ? (JMAX - jj[i]) & 2047u : 0u, ok);
-        }
-        __syncthreads();
-        find_bin<SEL_NT>(hist, remj, wsum, res);
-        jT = JMAX - ((a1 << 11) | res[0]);
+        find_bin12<SEL_NT>(hist, rem, wsum, res);
+        prefix = (prefix << 12) | res[0];
+        rem -= res[1];
         __syncthreads();
     }
-    // Ordered compaction of the selected candidates (the list is sorted by
-    // index): thread t takes a contiguous block.
+    const uint32_t T = kmin + prefix;  // keep every key above T and the first rem keys equal to T
+    // Ordered compaction (the list is sorted by index): thread t takes a
+    // contiguous block; the T-ties are cut in list order.
     const int E = (cnt + SEL_NT - 1) / SEL_NT;
     const int c0 = tid * E, c1 = min(cnt, c0 + E);
-    uint32_t mine = 0;
-    for (int i = c0; i < c1; ++i)
-        mine += (keys[i] > T || (keys[i] == T && jj[i] <= jT)) ? 1u : 0u;
-    uint32_t stot;
-    uint32_t o = block_excl_scan<SEL_NT>(mine, wsum, &stot);
-    for (int i = c0; i < c1; ++i)
-        if (keys[i] > T || (keys[i] == T && jj[i] <= jT)) {
-            if (o < (uint32_t)k) out[o] = (int32_t)jj[i];
-            ++o;
+    uint32_t gtl = 0, eql = 0;
+    for (int i = c0; i < c1; ++i) {
+        gtl += keys[i] > T ? 1u : 0u;
+        eql += keys[i] == T ? 1u : 0u;
+    }
+    uint32_t tot;
+    const uint32_t pk = block_excl_scan<SEL_NT>((gtl << 16) | eql, wsum, &tot);
+    uint32_t gb = pk >> 16, eb = pk & 0xffffu;
+    for (int i = c0; i < c1; ++i) {
+        if (keys[i] > T) {
+            out[gb + min(eb, rem)] = (int32_t)jj[i];
+            ++gb;
+        } else if (keys[i] == T) {
+            if (eb < rem) out[gb + eb] = (int32_t)jj[i];
+            ++eb;
         }
+    }
 }
 
 template <int DT, int D>

@@ -511,7 +511,9 @@ __global__ __launch_bounds__(SL_NT) void prefill_select_kernel(PrefillArgs a) {
         res[3] = 0u;
     }
     __syncthreads();
-    if (lo <= hi) {
+    lo = wave_min(lo);
+    hi = wave_max(hi);
+    if ((tid & 63) == 0 && lo <= hi) {
         atomicMin(&res[2], lo);
         atomicMax(&res[3], hi);
     }

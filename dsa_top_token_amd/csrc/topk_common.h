@@ -48,6 +48,19 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
     return x;
 }
 
+// Minimum / maximum across the 64 lanes of a wave.
+__device__ __forceinline__ uint32_t wave_min(uint32_t x) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) x = min(x, (uint32_t)__shfl_xor((int)x, m));
+    return x;
+}
+
+__device__ __forceinline__ uint32_t wave_max(uint32_t x) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) x = max(x, (uint32_t)__shfl_xor((int)x, m));
+    return x;
+}
+
 // Exclusive prefix sum over an NT-thread workgroup; *total gets the sum.
 // wsum needs NT/64 words of LDS. Contains barriers: call from every thread.
 template <int NT>
