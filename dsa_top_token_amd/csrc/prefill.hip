@@ -371,8 +371,8 @@ __device__ __forceinline__ uint32_t cand_key(uint32_t acc_bits, float scale) {
     return rank_key(relu_scaled(__uint_as_float(acc_bits), scale));
 }
 
-constexpr int SL_NT = 256;      // threads per select workgroup (one row each)
-constexpr int SL_BINS = 4096;   // 12-bit digits of the relative order keys
+constexpr int SL_NT = 512;      // threads per select workgroup (one row each)
+constexpr int SL_GMAX = 1024;   // keys of a radix bin gathered for the refinement rounds
 
 // Sum over the SL_NT-thread workgroup (contains barriers).
 __device__ __forceinline__ uint32_t block_total(uint32_t v, uint32_t* wsum) {
@@ -381,41 +381,70 @@ __device__ __forceinline__ uint32_t block_total(uint32_t v, uint32_t* wsum) {
     return tot;
 }
 
-// Bin of an SL_BINS histogram holding the rem-th largest counted key:
-// res[0] = bin, res[1] = keys in higher bins. Contains barriers.
-__device__ __forceinline__ void block_find_bin(const uint32_t* hist, uint32_t rem,
-                                               uint32_t* wsum, uint32_t* res) {
-    constexpr int PER = SL_BINS / SL_NT;
-    const int hi = SL_BINS - 1 - (int)threadIdx.x * PER;
-    uint32_t c[PER], loc = 0;
+// Bin of a 256-bin histogram holding the rem-th largest counted key, found
+// by wave 0: res[0] = bin, res[1] = keys in higher bins. Called by wave 0.
+__device__ __forceinline__ void wave_find_bin8(const uint32_t* hist, uint32_t rem, uint32_t* res) {
+    const int lane = threadIdx.x & 63;
+    const int hi = 255 - 4 * lane;
+    uint32_t c[4], loc = 0;
 #pragma unroll
-    for (int q = 0; q < PER; ++q) {
+    for (int q = 0; q < 4; ++q) {
         c[q] = hist[hi - q];
         loc += c[q];
     }
-    uint32_t tot;
-    uint32_t above = block_excl_scan<SL_NT>(loc, wsum, &tot);
+    uint32_t above = wave_incl_scan(loc) - loc;
 #pragma unroll
-    for (int q = 0; q < PER; ++q) {
+    for (int q = 0; q < 4; ++q) {
         if (above < rem && above + c[q] >= rem) {
             res[0] = (uint32_t)(hi - q);
             res[1] = above;
         }
         above += c[q];
     }
-    __syncthreads();
+}
+
+// Orders one wave's LDS accesses across lanes (its histogram updates before
+// the reads that follow them).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 // One SL_NT-thread workgroup per row. Thread t holds list entries
-// [t P, t P + P) in registers (P even, P <= PER), so the workgroup's
-// registers hold the list in index order.
+// [t PER, t PER + PER) in registers, so the workgroup's registers hold the
+// list in index order. The k-th key T is found by 8-bit
+// radix rounds over the keys relative to the row's smallest: block-wide
+// while the current bin holds many keys, then by wave 0 alone over the keys
+// of that bin gathered into LDS.
+// Row state fetched ahead of its turn: count, threshold and the thread's
+// slice of the list (every slice lies inside the row's cap entries, so it is
+// loaded before the count is known).
 template <int PER>
-__global__ __launch_bounds__(SL_NT) void prefill_select_kernel(PrefillArgs a) {
-    __shared__ uint32_t hist[SL_BINS];
-    __shared__ uint32_t wsum[SL_NT / 64];
-    __shared__ uint32_t res[4];
+struct SelRow {
+    uint32_t cnt;
+    float tau;
+    uint4 raw[PER / 2];
+};
+
+template <int PER>
+__device__ __forceinline__ void sel_fetch(const PrefillArgs& a, long long task, SelRow<PER>& r) {
+    if (task >= (long long)a.B * a.rows) return;
+    r.cnt = a.cnt[task];
+    r.tau = a.tau_acc[task];
+    const uint2* cl = a.cand + (size_t)task * a.cap;
+    const int c0 = (int)threadIdx.x * PER;
+#pragma unroll
+    for (int e = 0; e < PER; e += 2)
+        r.raw[e / 2] = c0 + e + 1 < a.cap ? *reinterpret_cast<const uint4*>(cl + c0 + e)
+                                          : make_uint4(0u, 0u, 0u, 0u);
+}
+
+template <int PER>
+__device__ __forceinline__ void select_row(const PrefillArgs& a, long long task, const SelRow<PER>& rw,
+                                           uint32_t* hist, uint32_t* gk, uint32_t* wsum,
+                                           uint32_t* res) {
     const int tid = threadIdx.x;
-    const long long task = blockIdx.x;
     const int b = (int)(task / a.rows), i = (int)(task % a.rows);
     const int n = row_len(a, i);
     const int k = a.top_k;
@@ -424,41 +453,26 @@ __global__ __launch_bounds__(SL_NT) void prefill_select_kernel(PrefillArgs a) {
         fill_prefix(out, n, k, tid, SL_NT);
         return;
     }
-    const uint32_t cnt = a.cnt[task];
-    const bool zero_mode = __float_as_uint(a.tau_acc[task]) == 0u;
+    const uint32_t cnt = rw.cnt;
+    const bool zero_mode = __float_as_uint(rw.tau) == 0u;
     if (cnt > (uint32_t)a.cap || (!zero_mode && cnt < (uint32_t)k)) {
         if (tid == 0) a.fb_list[atomicAdd(a.fb_count, 1u)] = (uint32_t)task;
         return;
     }
-    const uint2* cl = a.cand + (size_t)task * a.cap;
+    const int c0 = tid * PER;
     const int cn = (int)cnt;
     const float scale = a.scale;
     constexpr uint32_t ZERO_KEY = 0x80000000u;  // order key of a zero score
-    const int P = (cn + 2 * SL_NT - 1) / (2 * SL_NT) * 2;
-    const int c0 = tid * P;
-    uint32_t key[PER], idx[PER];
+    auto valid = [&](int e) { return c0 + e < cn; };
+    uint32_t key[PER], ix[PER];
 #pragma unroll
     for (int e = 0; e < PER; e += 2) {
-        key[e] = key[e + 1] = 0u;
-        idx[e] = idx[e + 1] = 0u;
-        const int c = c0 + e;
-        if (e < P && c < cn) {
-            uint4 v;
-            if (c + 1 < cn) {
-                v = *reinterpret_cast<const uint4*>(cl + c);
-            } else {
-                const uint2 w = cl[c];
-                v = make_uint4(w.x, w.y, 0u, 0u);
-            }
-            key[e] = cand_key(v.x, scale);
-            idx[e] = v.y;
-            if (c + 1 < cn) {
-                key[e + 1] = cand_key(v.z, scale);
-                idx[e + 1] = v.w;
-            }
-        }
+        key[e] = valid(e) ? cand_key(rw.raw[e / 2].x, scale) : 0u;
+        key[e + 1] = valid(e + 1) ? cand_key(rw.raw[e / 2].z, scale) : 0u;
+        ix[e] = rw.raw[e / 2].y;
+        ix[e + 1] = rw.raw[e / 2].w;
     }
-    auto valid = [&](int e) { return e < P && c0 + e < cn; };
+    auto idx_of = [&](int e) { return ix[e]; };
 
     if (zero_mode) {
         // The list holds every key with a positive score (plus some zeros);
@@ -477,7 +491,7 @@ __global__ __launch_bounds__(SL_NT) void prefill_select_kernel(PrefillArgs a) {
 #pragma unroll
             for (int e = 0; e < PER; ++e) {
                 if (valid(e) && key[e] > ZERO_KEY) {
-                    csl += idx[e] - r < Z ? 1u : 0u;
+                    csl += idx_of(e) - r < Z ? 1u : 0u;
                     ++r;
                 }
             }
@@ -488,7 +502,7 @@ __global__ __launch_bounds__(SL_NT) void prefill_select_kernel(PrefillArgs a) {
 #pragma unroll
             for (int e = 0; e < PER; ++e) {
                 if (valid(e) && key[e] > ZERO_KEY) {
-                    if (r >= cs) out[Z + r] = (int32_t)idx[e];
+                    if (r >= cs) out[Z + r] = (int32_t)idx_of(e);
                     ++r;
                 }
             }
@@ -496,8 +510,7 @@ __global__ __launch_bounds__(SL_NT) void prefill_select_kernel(PrefillArgs a) {
         }
     }
 
-    // Range of the row's order keys: digits are taken relative to the
-    // smallest, over only as many 12-bit rounds as the range needs.
+    // Range of the row's order keys; digits are taken relative to the smallest.
     uint32_t lo = 0xffffffffu, hi = 0u;
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
@@ -509,6 +522,7 @@ __global__ __launch_bounds__(SL_NT) void prefill_select_kernel(PrefillArgs a) {
     if (tid == 0) {
         res[2] = 0xffffffffu;
         res[3] = 0u;
+        res[4] = 0u;
     }
     __syncthreads();
     lo = wave_min(lo);
@@ -520,24 +534,73 @@ __global__ __launch_bounds__(SL_NT) void prefill_select_kernel(PrefillArgs a) {
     __syncthreads();
     const uint32_t kmin = res[2];
     const uint32_t range = res[3] - kmin;
-    __syncthreads();
-    const int R = (32 - __clz((int)range) + 11) / 12;  // 0..3 rounds
+    // Radix rounds over bits [sh, hsh) of d = key - kmin, from the top.
     uint32_t rem = (uint32_t)k, prefix = 0;
-    for (int r = 0; r < R; ++r) {
-        const int sh = 12 * (R - 1 - r);
-        const int hsh = r == 0 ? 0 : sh + 12;
-        for (int q = tid; q < SL_BINS; q += SL_NT) hist[q] = 0u;
+    int sh = 32 - __clz((int)range);
+    bool first = true, gathered = false;
+    uint32_t G = 0;
+    while (sh > 0 && !gathered) {
+        const int hsh = sh;
+        sh = sh > 8 ? sh - 8 : 0;
+        const uint32_t mask = (1u << (hsh - sh)) - 1u;
+        if (tid < 256) hist[tid] = 0u;
         __syncthreads();
 #pragma unroll
         for (int e = 0; e < PER; ++e) {
             const uint32_t d = key[e] - kmin;
-            if (valid(e) && (r == 0 || (d >> hsh) == prefix)) atomicAdd(&hist[(d >> sh) & 4095u], 1u);
+            hist_add(hist, (d >> sh) & mask, valid(e) && (first || (d >> hsh) == prefix));
         }
         __syncthreads();
-        block_find_bin(hist, rem, wsum, res);
-        prefix = (prefix << 12) | res[0];
-        rem -= res[1];
+        if (tid < 64) wave_find_bin8(hist, rem, res);
         __syncthreads();
+        const uint32_t bin = res[0];
+        prefix = (prefix << (hsh - sh)) | bin;
+        rem -= res[1];
+        first = false;
+        // Few keys left in the bin: gather them for wave 0.
+        if (sh > 0 && hist[bin] <= (uint32_t)SL_GMAX) {
+#pragma unroll
+            for (int e = 0; e < PER; ++e) {
+                const uint32_t d = key[e] - kmin;
+                if (valid(e) && (d >> sh) == prefix) gk[atomicAdd(&res[4], 1u)] = d;
+            }
+            gathered = true;
+        }
+        __syncthreads();
+    }
+    if (gathered) {
+        G = res[4];
+        if (tid < 64) {
+            // wave 0 alone: the remaining rounds over the gathered keys
+            while (sh > 0) {
+                const int hsh = sh;
+                sh = sh > 8 ? sh - 8 : 0;
+                const uint32_t mask = (1u << (hsh - sh)) - 1u;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) hist[tid + 64 * q] = 0u;
+                wave_lds_sync();
+                for (uint32_t g0 = 0; g0 < G; g0 += 64) {
+                    const uint32_t gi = g0 + tid;
+                    const uint32_t d = gi < G ? gk[gi] : 0u;
+                    hist_add(hist, (d >> sh) & mask, gi < G && (d >> hsh) == prefix);
+                }
+                wave_lds_sync();
+                wave_find_bin8(hist, rem, res);
+                wave_lds_sync();
+                const uint32_t bin = (uint32_t)__builtin_amdgcn_readfirstlane((int)res[0]);
+                const uint32_t above = (uint32_t)__builtin_amdgcn_readfirstlane((int)res[1]);
+                prefix = (prefix << (hsh - sh)) | bin;
+                rem -= above;
+                wave_lds_sync();  // res and hist are rewritten by the next round
+            }
+            if (tid == 0) {
+                res[5] = prefix;
+                res[6] = rem;
+            }
+        }
+        __syncthreads();
+        prefix = res[5];
+        rem = res[6];
     }
     const uint32_t T = kmin + prefix;  // keep every key above T and the first rem keys equal to T
     // Ordered compaction over the index-ordered list.
@@ -556,13 +619,25 @@ __global__ __launch_bounds__(SL_NT) void prefill_select_kernel(PrefillArgs a) {
     for (int e = 0; e < PER; ++e) {
         if (!valid(e)) continue;
         if (key[e] > T) {
-            out[gb + min(eb, rem)] = (int32_t)idx[e];
+            out[gb + min(eb, rem)] = (int32_t)ix[e];
             ++gb;
         } else if (key[e] == T) {
-            if (eb < rem) out[gb + eb] = (int32_t)idx[e];
+            if (eb < rem) out[gb + eb] = (int32_t)ix[e];
             ++eb;
         }
     }
+}
+
+// One row per workgroup.
+template <int PER>
+__global__ __launch_bounds__(SL_NT) void prefill_select_kernel(PrefillArgs a) {
+    __shared__ uint32_t hist[256];
+    __shared__ uint32_t gk[SL_GMAX];
+    __shared__ uint32_t wsum[SL_NT / 64];
+    __shared__ uint32_t res[8];
+    SelRow<PER> rw;
+    sel_fetch<PER>(a, blockIdx.x, rw);
+    select_row<PER>(a, blockIdx.x, rw, hist, gk, wsum, res);
 }
 
 // ----------------------------------------------------------------- fallback
@@ -618,11 +693,14 @@ hipError_t launch_d(const PrefillArgs& a, int part, hipStream_t s) {
     } else if (part == 2) {
         if (rows > 0x7fffffffLL) return hipErrorInvalidConfiguration;
         const dim3 grid((unsigned)rows), blk(SL_NT);
-        if (a.cap <= 4 * SL_NT) hipLaunchKernelGGL(prefill_select_kernel<4>, grid, blk, 0, s, a);
-        else if (a.cap <= 8 * SL_NT) hipLaunchKernelGGL(prefill_select_kernel<8>, grid, blk, 0, s, a);
-        else if (a.cap <= 16 * SL_NT) hipLaunchKernelGGL(prefill_select_kernel<16>, grid, blk, 0, s, a);
-        else if (a.cap <= 28 * SL_NT) hipLaunchKernelGGL(prefill_select_kernel<28>, grid, blk, 0, s, a);
-        else if (a.cap <= 52 * SL_NT) hipLaunchKernelGGL(prefill_select_kernel<52>, grid, blk, 0, s, a);
+        // PER = 2 ceil(cap / (2 SL_NT)) entries per thread at most
+        const int per = (a.cap + 2 * SL_NT - 1) / (2 * SL_NT) * 2;
+        if (per <= 2) hipLaunchKernelGGL(prefill_select_kernel<2>, grid, blk, 0, s, a);
+        else if (per <= 4) hipLaunchKernelGGL(prefill_select_kernel<4>, grid, blk, 0, s, a);
+        else if (per <= 8) hipLaunchKernelGGL(prefill_select_kernel<8>, grid, blk, 0, s, a);
+        else if (per <= 12) hipLaunchKernelGGL(prefill_select_kernel<12>, grid, blk, 0, s, a);
+        else if (per <= 16) hipLaunchKernelGGL(prefill_select_kernel<16>, grid, blk, 0, s, a);
+        else if (per <= 26) hipLaunchKernelGGL(prefill_select_kernel<26>, grid, blk, 0, s, a);
         else return hipErrorInvalidValue;
     } else {
         hipLaunchKernelGGL((prefill_fallback_kernel<DT, D>), dim3(FB_WGS), dim3(512), 0, s, a);
