@@ -141,8 +141,18 @@ ForwardLayout forward_layout(const dsa_problem* p) {
         const size_t ib = align_up((size_t)p->batch * p->n_q * p->top_k * sizeof(int32_t));
         L.idx = 0;
         L.topk = ib;
-        L.part = L.topk + align_up(dsa::prefill_ws_bytes(p->batch, prefill_slab_rows(p), p->n_k,
+        const size_t pw = align_up(dsa::prefill_ws_bytes(p->batch, prefill_slab_rows(p), p->n_k,
                                                          p->top_k));
+        if (dsa::attn_ranged_applies(p->batch, p->n_q, p->n_k)) {
+            // the key-range attention's partials reuse the select's buffers,
+            // which are dead once the last slab's select has run
+            const size_t rw =
+                align_up(dsa::attn_ranged_ws_bytes(p->batch, p->n_q, p->n_k, p->q_pos0));
+            L.part = L.topk;
+            L.total = L.topk + (pw > rw ? pw : rw);
+            return L;
+        }
+        L.part = L.topk + pw;
         L.total = L.part + attn_ws_bytes(p);
         return L;
     }
@@ -338,6 +348,8 @@ dsa_status forward_impl(const dsa_problem* p, const void* q_idx, const void* k_i
     }
     if (tm) tm->mark(2);
     dsa::AttnArgs aa = attn_args(p, Q, K, V, idx, O, lse, w + L.part);
+    if (p->n_q > 1 && dsa::attn_ranged_applies(p->batch, p->n_q, p->n_k))
+        dsa::attn_set_ranged(aa, p->q_pos0, w + L.part);  // idx rows are sorted and causal
     hipError_t e = dsa::launch_sparse_attn(aa, st);
     if (e != hipSuccess) return hip_fail(e, "sparse_attn launch");
     if (tm) tm->mark(-1);

@@ -43,6 +43,12 @@ struct AttnArgs {
     float* part;            // [B*n_q][n_split][16][128 + 4] fp32 partials
     int B, n_q, n_k, H, k;
     int n_split, split_len; // entries of idx handled per split (multiple of 128)
+    // Key-range schedule (idx rows sorted ascending, causal, -1 padded at the
+    // end): set by attn_set_ranged.
+    int ranged, q_pos0, n_range;
+    long long parts_per_seq;
+    float* part_lse;        // [parts][16][2] log2-domain lse and scale 2^e of each partial
+    uint16_t* part_o;       // [parts][16][128] fp16 (O / l) * 2^-e of each partial
 };
 
 // One query row per sequence, selection without a materialised score row
@@ -104,5 +110,12 @@ hipError_t launch_decode_select(DecodeArgs a, void* ws, int part, hipStream_t s)
 
 // Split plan of the attention: splits per query and entries per split.
 void attn_split_plan(int B, int n_q, int k, int* n_split, int* split_len);
+
+// Key-range schedule of the many-row attention (sorted causal idx rows):
+// whether it applies, the workspace its partials need, and setting it up
+// on AttnArgs from a workspace pointer.
+bool attn_ranged_applies(int B, int n_q, int n_k);
+size_t attn_ranged_ws_bytes(int B, int n_q, int n_k, int q_pos0);
+void attn_set_ranged(AttnArgs& a, int q_pos0, void* ws);
 
 }  // namespace dsa

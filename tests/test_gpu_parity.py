@@ -226,6 +226,35 @@ def test_all_zero_query_selects_first_keys(gpu_lib):
         assert list(idx[i, :m]) == list(range(m)) and np.all(idx[i, m:] == -1)
 
 
+@pytest.mark.parametrize("w,rows", [
+    # every row reaches all three 8192-key ranges; two sequences
+    (Workload("ranged_chunked", "prefill", 2, 1100, 20000, 18900, 64, "fp8", 300, 16),
+     [(0, 3), (517, 520), (1097, 1100)]),
+    # rows below key 8192 finish in one range, the rest merge two partials;
+    # 5 heads, and rows just past 8192 often select no key of range 1
+    (Workload("ranged_prefill", "prefill", 1, 9000, 9000, 0, 32, "bf16", 200, 5),
+     [(0, 9000)]),
+], ids=lambda v: v.name if isinstance(v, Workload) else "")
+def test_forward_key_range_attention(gpu_lib, w, rows):
+    # Many sorted, causal rows over more than 8192 keys: the forward's
+    # attention runs range by range and merges per-range partials. Every row
+    # must agree with the one-pass attention call on the same selection, and
+    # the sampled rows with the oracle.
+    say("key-range attention %s" % w.name)
+    x = synth.make_inputs(w, seed=11)
+    d = to_dev(x)
+    idx, O, lse = dsa.forward(d["q_idx"], d["k_idx"], d["Q"], d["K"], d["V"], w.q_pos0,
+                              w.top_k)
+    check_selection_properties(idx, w.q_pos0, w.top_k)
+    O1, lse1 = dsa.sparse_attn(d["Q"], d["K"], d["V"], idx, q_pos0=w.q_pos0)
+    assert_attn_close(O, O1.float().cpu().numpy(), lse, lse1.cpu().numpy(), "vs one pass")
+    for (a, b) in rows:
+        idx_ref, O_ref, lse_ref = oracle.forward(x["q_idx"], x["k_idx"], x["Q"], x["K"],
+                                                 x["V"], w.q_pos0, w.top_k, a, b)
+        assert np.array_equal(idx[:, a:b].cpu().numpy(), idx_ref), (a, b)
+        assert_attn_close(O[:, a:b], O_ref, lse[:, a:b], lse_ref, "%s %d-%d" % (w.name, a, b))
+
+
 def check_selection_properties(idx, q_pos0, k):
     """On the GPU, for every row: ascending, inside [0, pos], min(k, pos+1)
     entries, -1 padding."""
