@@ -71,6 +71,7 @@ constexpr int QOFF = 2 * KVB;            // Q rows: 4 KB
 constexpr int WAVE_LDS = QOFF + 16 * ROWB;  // 20 KB
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+constexpr int kBufWord3 = 0x00020000;  // buffer descriptor word 3: 32-bit data format
 
 // idx entry of slot e + lane % 32, clamped into the row so every load is in
 // bounds (slots at or past e_end are masked out by slot_mask).
@@ -90,15 +91,17 @@ struct StepRows {
     u16x8 k[8], v[8];
 };
 
-__device__ __forceinline__ void load_rows(const uint16_t* Kb, const uint16_t* Vb, int n_k, int j,
-                                          int lane, StepRows& R) {
+// Buffer loads through descriptors that cover the sequence's n_k rows: an
+// entry outside [0, n_k) (the -1 padding, for one) lands past the end and
+// reads zeros, and slot_mask keeps it out of the softmax.
+__device__ __forceinline__ void load_rows(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
+                                          int j, int lane, StepRows& R) {
     const int q = lane >> 4, p = lane & 15;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-        const int jr = __shfl(j, 8 * q + c);
-        const size_t row = (jr >= 0 && jr < n_k) ? (size_t)jr : 0;
-        R.k[c] = *reinterpret_cast<const u16x8*>(Kb + row * HD + 8 * p);
-        R.v[c] = *reinterpret_cast<const u16x8*>(Vb + row * HD + 8 * p);
+        const uint32_t off = ((uint32_t)__shfl(j, 8 * q + c) << 8) + 16 * p;
+        R.k[c] = __builtin_bit_cast(u16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
+        R.v[c] = __builtin_bit_cast(u16x8, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
     }
 }
 
@@ -174,19 +177,24 @@ __device__ __forceinline__ void attend_step(const uint8_t* buf, uint32_t vm, con
 #pragma unroll
     for (int i = 1; i < 8; ++i) mx = fmaxf(mx, z[i]);
     mx = wave_xor_max(mx);
-    const float mnew = fmaxf(ws.mrun, mx);
-    const bool live = mnew != ninf;
-    const float alpha = live ? exp2f(ws.mrun - mnew) : 1.f;
+    // The reference maximum moves only when a head's maximum exceeds it by
+    // more than 8 (so p <= 2^8 in between); O and l are rescaled only then.
+    const bool grow = mx > ws.mrun + 8.f;
+    if (__ballot(grow) != 0ull) {
+        const float alpha = grow ? __builtin_amdgcn_exp2f(ws.mrun - mx) : 1.f;
+        ws.lpart *= alpha;
+#pragma unroll
+        for (int d = 0; d < 8; ++d) ws.o[d] *= alpha;
+        ws.mrun = grow ? mx : ws.mrun;
+    }
+    const float base = ws.mrun == ninf ? 0.f : ws.mrun;  // every z is -inf while mrun is
     float p[8], psum = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        p[i] = live ? exp2f(z[i] - mnew) : 0.f;
+        p[i] = __builtin_amdgcn_exp2f(z[i] - base);
         psum += p[i];
     }
-    ws.lpart = ws.lpart * alpha + psum;
-    ws.mrun = mnew;
-#pragma unroll
-    for (int d = 0; d < 8; ++d) ws.o[d] *= alpha;
+    ws.lpart += psum;
     bf16x8 pb;
 #pragma unroll
     for (int i = 0; i < 8; ++i) pb[i] = (__bf16)p[i];
@@ -228,9 +236,11 @@ __device__ __forceinline__ void wave_attend(const AttnArgs& a, long long qrow, i
     const int m = lane & 15, g = lane >> 4;
     const int b = (int)(qrow / a.n_q);
     const int32_t* sel = a.idx + qrow * (long long)a.k;
-    const uint16_t* Kb = a.K + (size_t)b * a.n_k * HD;
-    const uint16_t* Vb = a.V + (size_t)b * a.n_k * HD;
     const int n_k = a.n_k;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.K + (size_t)b * n_k * HD), (short)0, n_k * ROWB, kBufWord3);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.V + (size_t)b * n_k * HD), (short)0, n_k * ROWB, kBufWord3);
 #pragma unroll
     for (int d = 0; d < 8; ++d) ws.o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
     ws.mrun = -__builtin_inff();
@@ -249,7 +259,7 @@ __device__ __forceinline__ void wave_attend(const AttnArgs& a, long long qrow, i
     }
     StepRows R;
     uint32_t vc = slot_mask(jA, e_first, e_end, n_k, lane);
-    load_rows(Kb, Vb, n_k, jA, lane, R);
+    load_rows(rk, rv, jA, lane, R);
     uint8_t* qs = lds + QOFF;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -258,7 +268,7 @@ __device__ __forceinline__ void wave_attend(const AttnArgs& a, long long qrow, i
     }
     store_rows(lds, R, lane);
     uint32_t vn = slot_mask(jB, e_first + e_step, e_end, n_k, lane);
-    if (e_first + e_step < e_end) load_rows(Kb, Vb, n_k, jB, lane, R);
+    if (e_first + e_step < e_end) load_rows(rk, rv, jB, lane, R);
     jA = load_slot(sel, e_first + 2 * e_step, e_end, lane);
     wave_lds_fence();
     // Q^T fragment: lane (head m, group g) holds Q[m][32s + 8g .. +8] for s = 0..3.
@@ -277,7 +287,7 @@ __device__ __forceinline__ void wave_attend(const AttnArgs& a, long long qrow, i
         store_rows(lds, R, lane);
         vc = vn;
         vn = slot_mask(jA, e + 2 * e_step, e_end, n_k, lane);
-        if (e + 2 * e_step < e_end) load_rows(Kb, Vb, n_k, jA, lane, R);
+        if (e + 2 * e_step < e_end) load_rows(rk, rv, jA, lane, R);
         jB = load_slot(sel, e + 3 * e_step, e_end, lane);
         e += e_step;
         wave_lds_fence();
@@ -288,7 +298,7 @@ __device__ __forceinline__ void wave_attend(const AttnArgs& a, long long qrow, i
         store_rows(lds, R, lane);
         vc = vn;
         vn = slot_mask(jB, e + 2 * e_step, e_end, n_k, lane);
-        if (e + 2 * e_step < e_end) load_rows(Kb, Vb, n_k, jB, lane, R);
+        if (e + 2 * e_step < e_end) load_rows(rk, rv, jB, lane, R);
         jA = load_slot(sel, e + 3 * e_step, e_end, lane);
         e += e_step;
         wave_lds_fence();
