@@ -18,6 +18,7 @@
 // With n_split > 1 each task writes unnormalised partials (O, running max,
 // running sum) and a second kernel merges them by log-sum-exp rescaling.
 #include "dsa_internal.h"
+#include "lanes.h"
 
 namespace dsa {
 namespace {
@@ -36,17 +37,9 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u16x8 v) { return __builtin_bit_cast(bf16x8, v); }
 
-__device__ __forceinline__ float wave_xor_max(float v) {
-    v = fmaxf(v, __shfl_xor(v, 16));
-    v = fmaxf(v, __shfl_xor(v, 32));
-    return v;
-}
+__device__ __forceinline__ float wave_xor_max(float v) { return lanes4_max(v); }
 
-__device__ __forceinline__ float wave_xor_sum(float v) {
-    v += __shfl_xor(v, 16);
-    v += __shfl_xor(v, 32);
-    return v;
-}
+__device__ __forceinline__ float wave_xor_sum(float v) { return lanes4_sum(v); }
 
 // One wave's pass over selected-key slots e = e_first, e_first + e_step, ...
 // (32 slots each, all below e_end) of query row qrow: online softmax state

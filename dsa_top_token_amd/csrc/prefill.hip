@@ -34,6 +34,7 @@
 //              schedule.
 #include "frag.h"
 #include "topk_common.h"
+#include "lanes.h"
 
 namespace dsa {
 namespace {
@@ -225,7 +226,22 @@ __global__ __launch_bounds__(256) void prefill_threshold_kernel(PrefillArgs a) {
 // Ring depth of the key-chunk pipeline (chunks in flight ahead of the one
 // being consumed is FL_NBUF - 1).
 template <int RB>
-constexpr int fl_nbuf() { return FL_CHUNK * RB <= 8192 ? 3 : 2; }
+constexpr int fl_nbuf() { return FL_CHUNK * RB <= 8192 || RB <= 320 ? 3 : 2; }
+
+// Waits until at most `ahead` chunks of GPR copies each are in flight
+// (0 <= ahead <= A).
+template <int A, int GPR>
+__device__ __forceinline__ void wait_chunks(int ahead) {
+    if constexpr (A > 0) {
+        if (ahead >= A) {
+            wait_vmcnt<A * GPR>();
+            return;
+        }
+        wait_chunks<A - 1, GPR>(ahead);
+    } else {
+        wait_vmcnt<0>();
+    }
+}
 static_assert(FL_CHUNK == 64, "the producer's lane -> key map covers 64 keys");
 
 template <int DT, int D>
@@ -268,14 +284,7 @@ __global__ __launch_bounds__(320) void prefill_filter_kernel(PrefillArgs a) {
         for (int c = 0; c < n_chunks; ++c) {
             // chunk c has landed once at most `ahead` later chunks are in flight
             const int ahead = min(c + NBUF - 1, n_chunks) - c - 1;
-            if constexpr (NBUF > 2) {
-                if (ahead >= 2) wait_vmcnt<2 * GPR>();
-                else if (ahead == 1) wait_vmcnt<GPR>();
-                else wait_vmcnt<0>();
-            } else {
-                if (ahead >= 1) wait_vmcnt<GPR>();
-                else wait_vmcnt<0>();
-            }
+            wait_chunks<NBUF - 2, GPR>(ahead);
             // A workgroup barrier without the release fence of __syncthreads
             // (that fence would wait for every copy in flight); the wait
             // above has already made chunk c visible in LDS.
@@ -337,9 +346,9 @@ __global__ __launch_bounds__(320) void prefill_filter_kernel(PrefillArgs a) {
             // The row's lanes g = 0..3 hold consecutive key ranges: exclusive
             // prefix of their counts.
             const uint32_t lc = (uint32_t)__popc(bits);
-            const uint32_t x1 = (uint32_t)__shfl_xor((int)lc, 16);
+            const uint32_t x1 = lane_partner16(lc);
             const uint32_t s01 = lc + x1;
-            const uint32_t x2 = (uint32_t)__shfl_xor((int)s01, 32);
+            const uint32_t x2 = lane_partner32(s01);
             const uint32_t tot = s01 + x2;
             const uint32_t o = cnt + ((g & 1) ? x1 : 0u) + ((g & 2) ? x2 : 0u);
             // An overflowing row's list is abandoned (the row is recomputed

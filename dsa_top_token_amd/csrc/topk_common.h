@@ -3,6 +3,7 @@
 #pragma once
 
 #include "dsa_internal.h"
+#include "lanes.h"
 
 namespace dsa {
 namespace topk {
@@ -48,16 +49,21 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
     return x;
 }
 
-// Minimum / maximum across the 64 lanes of a wave.
+// Minimum / maximum across the 64 lanes of a wave (bits 5 and 4 of the lane
+// index on VALU permutes, the rest on swizzles).
 __device__ __forceinline__ uint32_t wave_min(uint32_t x) {
+    x = min(x, lane_partner32(x));
+    x = min(x, lane_partner16(x));
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) x = min(x, (uint32_t)__shfl_xor((int)x, m));
+    for (int m = 8; m >= 1; m >>= 1) x = min(x, (uint32_t)__shfl_xor((int)x, m));
     return x;
 }
 
 __device__ __forceinline__ uint32_t wave_max(uint32_t x) {
+    x = max(x, lane_partner32(x));
+    x = max(x, lane_partner16(x));
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) x = max(x, (uint32_t)__shfl_xor((int)x, m));
+    for (int m = 8; m >= 1; m >>= 1) x = max(x, (uint32_t)__shfl_xor((int)x, m));
     return x;
 }
 
