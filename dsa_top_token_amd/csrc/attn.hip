@@ -5,18 +5,18 @@
 // query heads share one K/V set (MQA), so one gathered K/V row serves every
 // head; section 4.1 runs this stage in BF16.
 //
-// One wave owns one (query, split) task: up to 16 heads against the split's
-// selected keys, 32 keys per step.
+// One wave owns one (query, split) or (query, key range) task: up to 16
+// heads against the task's selected keys, 32 keys per step.
 //   S^T (keys x heads) = K_sel (keys x 128) . Q^T    4+4 bf16 16x16x32 MFMAs
 //   online softmax per head (log2 domain, fp32)
 //   O^T (dims x heads) += V_sel^T . P^T              8 bf16 16x16x32 MFMAs
 // With S^T as the MFMA output, lane (head h = lane%16, group g = lane/16)
 // holds scores of keys 4g..4g+3 and 16+4g..16+4g+3, which is exactly the
 // 8-key slice of P^T the PV product wants from that lane (the contraction
-// order over keys is free). V rows are gathered with coalesced 64-byte
-// loads, staged in the wave's LDS slice and read back transposed.
-// With n_split > 1 each task writes unnormalised partials (O, running max,
-// running sum) and a second kernel merges them by log-sum-exp rescaling.
+// order over keys is free). Selected K and V rows are gathered with 16 lanes
+// per row, written to the wave's LDS slice and read back as fragments (K) and
+// with transposed reads (V^T).
+// Partials of split or key-range tasks are merged by log-sum-exp rescaling.
 #include "dsa_internal.h"
 #include "lanes.h"
 
