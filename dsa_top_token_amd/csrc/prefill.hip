@@ -436,6 +436,10 @@ struct SelRow {
     uint4 raw[PER / 2];
 };
 
+// Entries below this bound are fetched before the count is known; a row's
+// list almost always holds about 2 top_k entries or more.
+__device__ __forceinline__ int sel_spec(const PrefillArgs& a) { return min(a.cap, 2 * a.top_k); }
+
 template <int PER>
 __device__ __forceinline__ void sel_fetch(const PrefillArgs& a, long long task, SelRow<PER>& r) {
     if (task >= (long long)a.B * a.rows) return;
@@ -443,14 +447,29 @@ __device__ __forceinline__ void sel_fetch(const PrefillArgs& a, long long task, 
     r.tau = a.tau_acc[task];
     const uint2* cl = a.cand + (size_t)task * a.cap;
     const int c0 = (int)threadIdx.x * PER;
+    const int spec = sel_spec(a);
 #pragma unroll
     for (int e = 0; e < PER; e += 2)
-        r.raw[e / 2] = c0 + e + 1 < a.cap ? *reinterpret_cast<const uint4*>(cl + c0 + e)
-                                          : make_uint4(0u, 0u, 0u, 0u);
+        r.raw[e / 2] = c0 + e + 1 < spec ? *reinterpret_cast<const uint4*>(cl + c0 + e)
+                                         : make_uint4(0u, 0u, 0u, 0u);
+}
+
+// The rest of the thread's slice, once the count is known (entries past the
+// count are not read).
+template <int PER>
+__device__ __forceinline__ void sel_fetch_rest(const PrefillArgs& a, long long task, int cn,
+                                               SelRow<PER>& r) {
+    const uint2* cl = a.cand + (size_t)task * a.cap;
+    const int c0 = (int)threadIdx.x * PER;
+    const int spec = sel_spec(a);
+#pragma unroll
+    for (int e = 0; e < PER; e += 2)
+        if (c0 + e + 1 >= spec && c0 + e < cn && c0 + e + 1 < a.cap)
+            r.raw[e / 2] = *reinterpret_cast<const uint4*>(cl + c0 + e);
 }
 
 template <int PER>
-__device__ __forceinline__ void select_row(const PrefillArgs& a, long long task, const SelRow<PER>& rw,
+__device__ __forceinline__ void select_row(const PrefillArgs& a, long long task, SelRow<PER> rw,
                                            uint32_t* hist, uint32_t* gk, uint32_t* wsum,
                                            uint32_t* res) {
     const int tid = threadIdx.x;
@@ -470,6 +489,9 @@ __device__ __forceinline__ void select_row(const PrefillArgs& a, long long task,
     }
     const int c0 = tid * PER;
     const int cn = (int)cnt;
+    // Waves whose slices lie past the count skip every per-entry loop.
+    const bool wl = (tid & ~63) * PER < cn;
+    if (wl) sel_fetch_rest<PER>(a, task, cn, rw);
     const float scale = a.scale;
     constexpr uint32_t ZERO_KEY = 0x80000000u;  // order key of a zero score
     auto valid = [&](int e) { return c0 + e < cn; };
@@ -487,8 +509,10 @@ __device__ __forceinline__ void select_row(const PrefillArgs& a, long long task,
         // The list holds every key with a positive score (plus some zeros);
         // every key off the list scores zero.
         uint32_t npl = 0;
+        if (wl) {
 #pragma unroll
-        for (int e = 0; e < PER; ++e) npl += valid(e) && key[e] > ZERO_KEY ? 1u : 0u;
+            for (int e = 0; e < PER; ++e) npl += valid(e) && key[e] > ZERO_KEY ? 1u : 0u;
+        }
         uint32_t np;
         const uint32_t pbase = block_excl_scan<SL_NT>(npl, wsum, &np);
         if (np < (uint32_t)k) {
@@ -521,11 +545,13 @@ __device__ __forceinline__ void select_row(const PrefillArgs& a, long long task,
 
     // Range of the row's order keys; digits are taken relative to the smallest.
     uint32_t lo = 0xffffffffu, hi = 0u;
+    if (wl) {
 #pragma unroll
-    for (int e = 0; e < PER; ++e) {
-        if (valid(e)) {
-            lo = min(lo, key[e]);
-            hi = max(hi, key[e]);
+        for (int e = 0; e < PER; ++e) {
+            if (valid(e)) {
+                lo = min(lo, key[e]);
+                hi = max(hi, key[e]);
+            }
         }
     }
     if (tid == 0) {
@@ -554,10 +580,12 @@ __device__ __forceinline__ void select_row(const PrefillArgs& a, long long task,
         const uint32_t mask = (1u << (hsh - sh)) - 1u;
         if (tid < 256) hist[tid] = 0u;
         __syncthreads();
+        if (wl) {
 #pragma unroll
-        for (int e = 0; e < PER; ++e) {
-            const uint32_t d = key[e] - kmin;
-            hist_add(hist, (d >> sh) & mask, valid(e) && (first || (d >> hsh) == prefix));
+            for (int e = 0; e < PER; ++e) {
+                const uint32_t d = key[e] - kmin;
+                hist_add(hist, (d >> sh) & mask, valid(e) && (first || (d >> hsh) == prefix));
+            }
         }
         __syncthreads();
         if (tid < 64) wave_find_bin8(hist, rem, res);
@@ -568,10 +596,12 @@ __device__ __forceinline__ void select_row(const PrefillArgs& a, long long task,
         first = false;
         // Few keys left in the bin: gather them for wave 0.
         if (sh > 0 && hist[bin] <= (uint32_t)SL_GMAX) {
+            if (wl) {
 #pragma unroll
-            for (int e = 0; e < PER; ++e) {
-                const uint32_t d = key[e] - kmin;
-                if (valid(e) && (d >> sh) == prefix) gk[atomicAdd(&res[4], 1u)] = d;
+                for (int e = 0; e < PER; ++e) {
+                    const uint32_t d = key[e] - kmin;
+                    if (valid(e) && (d >> sh) == prefix) gk[atomicAdd(&res[4], 1u)] = d;
+                }
             }
             gathered = true;
         }
@@ -614,16 +644,19 @@ __device__ __forceinline__ void select_row(const PrefillArgs& a, long long task,
     const uint32_t T = kmin + prefix;  // keep every key above T and the first rem keys equal to T
     // Ordered compaction over the index-ordered list.
     uint32_t gtl = 0, eql = 0;
+    if (wl) {
 #pragma unroll
-    for (int e = 0; e < PER; ++e) {
-        if (valid(e)) {
-            gtl += key[e] > T ? 1u : 0u;
-            eql += key[e] == T ? 1u : 0u;
+        for (int e = 0; e < PER; ++e) {
+            if (valid(e)) {
+                gtl += key[e] > T ? 1u : 0u;
+                eql += key[e] == T ? 1u : 0u;
+            }
         }
     }
     uint32_t tot;
     const uint32_t pk = block_excl_scan<SL_NT>((gtl << 16) | eql, wsum, &tot);
     uint32_t gb = pk >> 16, eb = pk & 0xffffu;
+    if (!wl) return;
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
         if (!valid(e)) continue;
