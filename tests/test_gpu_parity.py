@@ -227,16 +227,16 @@ def test_all_zero_query_selects_first_keys(gpu_lib):
 
 
 @pytest.mark.parametrize("w,rows", [
-    # every row reaches all three 8192-key ranges; two sequences
+    # every row reaches both 12288-key ranges; two sequences
     (Workload("ranged_chunked", "prefill", 2, 1100, 20000, 18900, 64, "fp8", 300, 16),
      [(0, 3), (517, 520), (1097, 1100)]),
-    # rows below key 8192 finish in one range, the rest merge two partials;
-    # 5 heads, and rows just past 8192 often select no key of range 1
-    (Workload("ranged_prefill", "prefill", 1, 9000, 9000, 0, 32, "bf16", 200, 5),
-     [(0, 9000)]),
+    # rows below key 12288 finish in one range, the rest merge two partials;
+    # 5 heads, and rows just past 12288 often select no key of range 1
+    (Workload("ranged_prefill", "prefill", 1, 13000, 13000, 0, 32, "bf16", 200, 5),
+     [(0, 13000)]),
 ], ids=lambda v: v.name if isinstance(v, Workload) else "")
 def test_forward_key_range_attention(gpu_lib, w, rows):
-    # Many sorted, causal rows over more than 8192 keys: the forward's
+    # Many sorted, causal rows over more than 12288 keys: the forward's
     # attention runs range by range and merges per-range partials. Every row
     # must agree with the one-pass attention call on the same selection, and
     # the sampled rows with the oracle.
