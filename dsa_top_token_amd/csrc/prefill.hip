@@ -12,10 +12,10 @@
 //              accumulator whose scaled score reaches it. A row whose sample
 //              threshold is not positive keeps every non-negative
 //              accumulator instead ("zero mode").
-//   filter     per 64-row block: a producer wave streams the block's causal
+//   filter     per 64- or 128-row block: a producer wave streams the block's causal
 //              keys into an LDS ring of 64-key chunks with global->LDS copies
 //              (granule-major layout, several chunks in flight); four
-//              consumer waves of 16 rows each score every chunk on MFMA.
+//              consumer waves of 16 or 32 rows each score every chunk on MFMA.
 //              Keys are the MFMA row operand, so each lane holds 16
 //              consecutive keys of one query; a subtract and a funnel shift
 //              per score build the lane's accept mask, and the accepted
@@ -47,7 +47,6 @@ constexpr int TH_BINS = 1024;     // 10-bit digits of the threshold rounds
 constexpr int TH_MAX_SAMPLES = 4096;
 constexpr int TH_TARGET = 64;     // samples expected above tau
 constexpr int FL_CHUNK = 64;      // keys per staged chunk of the filter
-constexpr int FL_ROWS = 64;       // rows per filter workgroup (16 per wave)
 constexpr int FB_WGS = 256;       // fallback workgroups
 
 __device__ __forceinline__ int qrow(const PrefillArgs& a, int i) { return a.row0 + i * a.rstride; }
@@ -228,6 +227,13 @@ __global__ __launch_bounds__(256) void prefill_threshold_kernel(PrefillArgs a) {
 template <int RB>
 constexpr int fl_nbuf() { return FL_CHUNK * RB <= 8192 || RB <= 320 ? 3 : 2; }
 
+// Query tiles per consumer wave of the filter. Two tiles halve the ring
+// traffic and fragment reads per row (bf16 128K: 7.7 -> 6.4 ms); fp8 keys
+// are cheap to stream and there one tile keeps the longest workgroup's
+// chunk chain (which sets the kernel time at 64K) short.
+template <int DT, int D>
+constexpr int filter_qt() { return DT == 1 ? 2 : 1; }
+
 // Waits until at most `ahead` chunks of GPR copies each are in flight
 // (0 <= ahead <= A).
 template <int A, int GPR>
@@ -244,9 +250,13 @@ __device__ __forceinline__ void wait_chunks(int ahead) {
 }
 static_assert(FL_CHUNK == 64, "the producer's lane -> key map covers 64 keys");
 
-template <int DT, int D>
+// QT query tiles of 16 rows per consumer wave share every key fragment read
+// from the ring (the workgroup covers 64 QT rows).
+template <int DT, int D, int QT>
 __global__ __launch_bounds__(320) void prefill_filter_kernel(PrefillArgs a) {
     constexpr int RB = D * (DT == 0 ? 1 : 2);
+    constexpr int WROWS = 16 * QT;   // rows per consumer wave
+    constexpr int ROWS = 4 * WROWS;  // rows per workgroup
     constexpr int GPR = RB / 16;            // 16-byte granules per key row
     constexpr int COLB = FL_CHUNK * 16;     // bytes of one granule column
     constexpr int NBUF = fl_nbuf<RB>();
@@ -258,12 +268,12 @@ __global__ __launch_bounds__(320) void prefill_filter_kernel(PrefillArgs a) {
     __shared__ f32x4 stage[4][4][64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n = lane & 15, g = lane >> 4;
-    const int n_blk = (a.rows + FL_ROWS - 1) / FL_ROWS;
+    const int n_blk = (a.rows + ROWS - 1) / ROWS;
     // largest blocks (latest rows) first
     const int blk = n_blk - 1 - (int)(blockIdx.x / (unsigned)a.B);
     const int b = blockIdx.x % a.B;
-    const int i0 = blk * FL_ROWS;
-    const int kend = row_len(a, min(i0 + FL_ROWS, a.rows) - 1);
+    const int i0 = blk * ROWS;
+    const int kend = row_len(a, min(i0 + ROWS, a.rows) - 1);
     const int n_chunks = (kend + FL_CHUNK - 1) / FL_CHUNK;
     const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + (size_t)b * a.n_k * RB;
 
@@ -297,21 +307,31 @@ __global__ __launch_bounds__(320) void prefill_filter_kernel(PrefillArgs a) {
         return;
     }
 
-    // Consumers: wave w scores rows [i0 + 16 w, +16) against each chunk.
-    const int wi0 = i0 + wave * 16;
-    const int my_i = min(wi0 + n, a.rows - 1);
-    const bool live = wi0 + n < a.rows;
-    const int my_len = live ? row_len(a, my_i) : 0;
-    const float tau = live ? a.tau_acc[(size_t)b * a.rows + my_i] : __builtin_inff();
+    // Consumers: wave w scores rows [i0 + WROWS w, +WROWS) against each chunk,
+    // query tile t holding rows i0 + WROWS w + 16 t + n.
+    const int wi0 = i0 + wave * WROWS;
+    int my_i[QT], my_len[QT];
+    bool live[QT];
+    float tau[QT];
+    Frag<DT, D> fq[QT];
+    uint2* list[QT];
+    uint32_t cnt[QT];  // each row's list length (same in the row's 4 lanes)
+#pragma unroll
+    for (int t = 0; t < QT; ++t) {
+        const int r = wi0 + 16 * t + n;
+        live[t] = r < a.rows;
+        my_i[t] = min(r, a.rows - 1);
+        my_len[t] = live[t] ? row_len(a, my_i[t]) : 0;
+        tau[t] = live[t] ? a.tau_acc[(size_t)b * a.rows + my_i[t]] : __builtin_inff();
+        fq[t].load(static_cast<const uint8_t*>(a.q) + ((size_t)b * a.n_q + qrow(a, my_i[t])) * RB, g);
+        list[t] = a.cand + ((size_t)b * a.rows + my_i[t]) * a.cap;
+        cnt[t] = 0;
+    }
     const bool wave_live = wi0 < a.rows;
-    const int w_kend = wave_live ? row_len(a, min(wi0 + 15, a.rows - 1)) : 0;
+    const int w_kend = wave_live ? row_len(a, min(wi0 + WROWS - 1, a.rows - 1)) : 0;
     const int w_kmin = wave_live ? row_len(a, wi0) : 0;
-    Frag<DT, D> fq;
-    fq.load(static_cast<const uint8_t*>(a.q) + ((size_t)b * a.n_q + qrow(a, my_i)) * RB, g);
-    wait_vmcnt<0>();  // the query fragment is in registers before the chunk loop
-    uint2* list = a.cand + ((size_t)b * a.rows + my_i) * a.cap;
+    wait_vmcnt<0>();  // the query fragments are in registers before the chunk loop
     const uint32_t cap = (uint32_t)a.cap;
-    uint32_t cnt = 0;  // the row's list length (same in the row's 4 lanes)
 
     // A operand row n of key tile u is chunk key 16 (n / 4) + 4 u + n % 4
     // (row position 16 u + n), so output row 4 g + r of tile u is key
@@ -329,49 +349,57 @@ __global__ __launch_bounds__(320) void prefill_filter_kernel(PrefillArgs a) {
             for (int u = 0; u < 4; ++u) load_cm<COLB>(fk[u], tile, 16 * u + n, g);
             __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
             __builtin_amdgcn_sched_barrier(0);
-            f32x4 acc[4];
+            f32x4 acc[QT][4];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) acc[u] = tile_dot<D>(fk[u], fq);
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int t = 0; t < QT; ++t) acc[t][u] = tile_dot<D>(fk[u], fq[t]);
             __builtin_amdgcn_sched_barrier(0);
-            // bit i of rej: sign of (accumulator of key 16 g + i) - tau
-            uint32_t rej = 0;
 #pragma unroll
-            for (int i = 15; i >= 0; --i)
-                rej = __builtin_amdgcn_alignbit(rej, __float_as_uint(acc[i >> 2][i & 3] - tau), 31);
-            uint32_t bits = ~rej & 0xffffu;
-            if (k0 + FL_CHUNK > w_kmin) {
-                const int v = my_len - (k0 + 16 * g);
-                bits &= v >= 16 ? 0xffffu : (v <= 0 ? 0u : (1u << v) - 1u);
-            }
-            // The row's lanes g = 0..3 hold consecutive key ranges: exclusive
-            // prefix of their counts.
-            const uint32_t lc = (uint32_t)__popc(bits);
-            const uint32_t x1 = lane_partner16(lc);
-            const uint32_t s01 = lc + x1;
-            const uint32_t x2 = lane_partner32(s01);
-            const uint32_t tot = s01 + x2;
-            const uint32_t o = cnt + ((g & 1) ? x1 : 0u) + ((g & 2) ? x2 : 0u);
-            // An overflowing row's list is abandoned (the row is recomputed
-            // by the fallback); nothing is stored at or past cap.
-            const uint32_t ne = cnt + tot > cap ? 0u : lc;
-            if (ne == 0u) bits = 0u;
-            cnt += tot;
-            if (__ballot(bits != 0u) != 0ull) {
+            for (int t = 0; t < QT; ++t) {
+                // bit i of rej: sign of (accumulator of key 16 g + i) - tau
+                uint32_t rej = 0;
 #pragma unroll
-                for (int u = 0; u < 4; ++u) stage[wave][u][lane] = acc[u];
-                const float* st = reinterpret_cast<const float*>(&stage[wave][0][lane]);
-                const uint32_t kb = (uint32_t)(k0 + 16 * g);
-                uint32_t oo = o;
-                while (bits != 0u) {
-                    const int i = __builtin_ctz(bits);
-                    bits &= bits - 1u;
-                    list[oo++] = make_uint2(__float_as_uint(st[(i >> 2) * 256 + (i & 3)]),
-                                            kb + (uint32_t)i);
+                for (int i = 15; i >= 0; --i)
+                    rej = __builtin_amdgcn_alignbit(
+                        rej, __float_as_uint(acc[t][i >> 2][i & 3] - tau[t]), 31);
+                uint32_t bits = ~rej & 0xffffu;
+                if (k0 + FL_CHUNK > w_kmin) {
+                    const int v = my_len[t] - (k0 + 16 * g);
+                    bits &= v >= 16 ? 0xffffu : (v <= 0 ? 0u : (1u << v) - 1u);
+                }
+                // The row's lanes g = 0..3 hold consecutive key ranges:
+                // exclusive prefix of their counts.
+                const uint32_t lc = (uint32_t)__popc(bits);
+                const uint32_t x1 = lane_partner16(lc);
+                const uint32_t s01 = lc + x1;
+                const uint32_t x2 = lane_partner32(s01);
+                const uint32_t tot = s01 + x2;
+                const uint32_t o = cnt[t] + ((g & 1) ? x1 : 0u) + ((g & 2) ? x2 : 0u);
+                // An overflowing row's list is abandoned (the row is
+                // recomputed by the fallback); nothing is stored at or past cap.
+                const uint32_t ne = cnt[t] + tot > cap ? 0u : lc;
+                if (ne == 0u) bits = 0u;
+                cnt[t] += tot;
+                if (__ballot(bits != 0u) != 0ull) {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) stage[wave][u][lane] = acc[t][u];
+                    const float* st = reinterpret_cast<const float*>(&stage[wave][0][lane]);
+                    const uint32_t kb = (uint32_t)(k0 + 16 * g);
+                    uint32_t oo = o;
+                    while (bits != 0u) {
+                        const int i = __builtin_ctz(bits);
+                        bits &= bits - 1u;
+                        list[t][oo++] = make_uint2(__float_as_uint(st[(i >> 2) * 256 + (i & 3)]),
+                                                   kb + (uint32_t)i);
+                    }
                 }
             }
         }
     }
-    if (g == 0 && live) a.cnt[(size_t)b * a.rows + my_i] = cnt;
+#pragma unroll
+    for (int t = 0; t < QT; ++t)
+        if (g == 0 && live[t]) a.cnt[(size_t)b * a.rows + my_i[t]] = cnt[t];
 }
 
 // ------------------------------------------------------------------- select
@@ -729,9 +757,11 @@ hipError_t launch_d(const PrefillArgs& a, int part, hipStream_t s) {
         hipLaunchKernelGGL((prefill_threshold_kernel<DT, D>), dim3((unsigned)nb), dim3(256), 0, s,
                            a);
     } else if (part == 1) {
-        const long long nb = (long long)a.B * ((a.rows + FL_ROWS - 1) / FL_ROWS);
+        constexpr int QT = filter_qt<DT, D>();
+        const long long nb = (long long)a.B * ((a.rows + 64 * QT - 1) / (64 * QT));
         if (nb > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL((prefill_filter_kernel<DT, D>), dim3((unsigned)nb), dim3(320), 0, s, a);
+        hipLaunchKernelGGL((prefill_filter_kernel<DT, D, QT>), dim3((unsigned)nb), dim3(320), 0, s,
+                           a);
     } else if (part == 2) {
         if (rows > 0x7fffffffLL) return hipErrorInvalidConfiguration;
         const dim3 grid((unsigned)rows), blk(SL_NT);
