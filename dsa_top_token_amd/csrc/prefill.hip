@@ -411,12 +411,6 @@ __device__ __forceinline__ uint32_t cand_key(uint32_t acc_bits, float scale) {
 constexpr int SL_NT = 512;      // threads per select workgroup (one row each)
 constexpr int SL_GMAX = 1024;   // keys of a radix bin gathered for the refinement rounds
 
-// Sum over the SL_NT-thread workgroup (contains barriers).
-__device__ __forceinline__ uint32_t block_total(uint32_t v, uint32_t* wsum) {
-    uint32_t tot;
-    block_excl_scan<SL_NT>(v, wsum, &tot);
-    return tot;
-}
 
 // Bin of a 256-bin histogram holding the rem-th largest counted key, found
 // by wave 0: res[0] = bin, res[1] = keys in higher bins. Called by wave 0.
@@ -449,19 +443,18 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 // One SL_NT-thread workgroup per row. Thread t holds list entries
-// [t PER, t PER + PER) in registers, so the workgroup's registers hold the
-// list in index order. The k-th key T is found by 8-bit
-// radix rounds over the keys relative to the row's smallest: block-wide
-// while the current bin holds many keys, then by wave 0 alone over the keys
-// of that bin gathered into LDS.
-// Row state fetched ahead of its turn: count, threshold and the thread's
-// slice of the list (every slice lies inside the row's cap entries, so it is
-// loaded before the count is known).
+// t, t + SL_NT, t + 2 SL_NT, ... in registers, so every load instruction of a
+// wave reads 64 consecutive entries (a lane-per-slice layout made the address
+// unit the bottleneck). The k-th key T is found by 8-bit radix rounds over
+// the keys relative to the row's smallest: block-wide while the current bin
+// holds many keys, then by wave 0 alone over the keys of that bin gathered
+// into LDS. Positions in list (= index) order come from ballots within a
+// wave and one table of per-(slot, wave) counts scanned by wave 0.
 template <int PER>
 struct SelRow {
     uint32_t cnt;
     float tau;
-    uint4 raw[PER / 2];
+    uint2 raw[PER];
 };
 
 // Entries below this bound are fetched before the count is known; a row's
@@ -474,31 +467,66 @@ __device__ __forceinline__ void sel_fetch(const PrefillArgs& a, long long task, 
     r.cnt = a.cnt[task];
     r.tau = a.tau_acc[task];
     const uint2* cl = a.cand + (size_t)task * a.cap;
-    const int c0 = (int)threadIdx.x * PER;
     const int spec = sel_spec(a);
 #pragma unroll
-    for (int e = 0; e < PER; e += 2)
-        r.raw[e / 2] = c0 + e + 1 < spec ? *reinterpret_cast<const uint4*>(cl + c0 + e)
-                                         : make_uint4(0u, 0u, 0u, 0u);
+    for (int e = 0; e < PER; ++e) {
+        const int j = e * SL_NT + (int)threadIdx.x;
+        r.raw[e] = j < spec ? cl[j] : make_uint2(0u, 0u);
+    }
 }
 
-// The rest of the thread's slice, once the count is known (entries past the
-// count are not read).
+// The rest of the thread's entries, once the count is known (entries past
+// the count are not read).
 template <int PER>
 __device__ __forceinline__ void sel_fetch_rest(const PrefillArgs& a, long long task, int cn,
                                                SelRow<PER>& r) {
     const uint2* cl = a.cand + (size_t)task * a.cap;
-    const int c0 = (int)threadIdx.x * PER;
     const int spec = sel_spec(a);
 #pragma unroll
-    for (int e = 0; e < PER; e += 2)
-        if (c0 + e + 1 >= spec && c0 + e < cn && c0 + e + 1 < a.cap)
-            r.raw[e / 2] = *reinterpret_cast<const uint4*>(cl + c0 + e);
+    for (int e = 0; e < PER; ++e) {
+        const int j = e * SL_NT + (int)threadIdx.x;
+        if (j >= spec && j < cn) r.raw[e] = cl[j];
+    }
+}
+
+// Exclusive prefix, in list order, of two flags per entry packed as
+// (count of fa) << 16 | (count of fb): pre[e] for this thread's entry e
+// (list index e SL_NT + tid), *total for the row. tbl needs
+// PER * SL_NT / 64 + 1 words. Two workgroup barriers; call from every thread.
+template <int PER>
+__device__ __forceinline__ void list_prefix2(const bool fa[PER], const bool fb[PER], uint32_t* tbl,
+                                             uint32_t pre[PER], uint32_t* total) {
+    constexpr int NW = SL_NT / 64, NE = PER * NW;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+        const unsigned long long ma = __ballot(fa[e]), mb = __ballot(fb[e]);
+        pre[e] = (__builtin_amdgcn_mbcnt_hi((uint32_t)(ma >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)ma, 0u)) << 16) |
+                 __builtin_amdgcn_mbcnt_hi((uint32_t)(mb >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mb, 0u));
+        if (lane == 0) tbl[e * NW + w] = ((uint32_t)__popcll(ma) << 16) | (uint32_t)__popcll(mb);
+    }
+    __syncthreads();
+    if (w == 0) {
+        // (slot, wave) order is list order: slot e's 512 entries precede slot e + 1's
+        uint32_t carry = 0;
+#pragma unroll
+        for (int b0 = 0; b0 < NE; b0 += 64) {
+            const uint32_t v = b0 + lane < NE ? tbl[b0 + lane] : 0u;
+            const uint32_t inc = wave_incl_scan(v) + carry;
+            if (b0 + lane < NE) tbl[b0 + lane] = inc - v;
+            carry = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
+        }
+        if (lane == 0) tbl[NE] = carry;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < PER; ++e) pre[e] += tbl[e * NW + w];
+    *total = tbl[NE];
 }
 
 template <int PER>
 __device__ __forceinline__ void select_row(const PrefillArgs& a, long long task, SelRow<PER> rw,
-                                           uint32_t* hist, uint32_t* gk, uint32_t* wsum,
+                                           uint32_t* hist, uint32_t* gk, uint32_t* tbl,
                                            uint32_t* res) {
     const int tid = threadIdx.x;
     const int b = (int)(task / a.rows), i = (int)(task % a.rows);
@@ -515,57 +543,50 @@ __device__ __forceinline__ void select_row(const PrefillArgs& a, long long task,
         if (tid == 0) a.fb_list[atomicAdd(a.fb_count, 1u)] = (uint32_t)task;
         return;
     }
-    const int c0 = tid * PER;
     const int cn = (int)cnt;
-    // Waves whose slices lie past the count skip every per-entry loop.
-    const bool wl = (tid & ~63) * PER < cn;
-    if (wl) sel_fetch_rest<PER>(a, task, cn, rw);
+    sel_fetch_rest<PER>(a, task, cn, rw);
     const float scale = a.scale;
     constexpr uint32_t ZERO_KEY = 0x80000000u;  // order key of a zero score
-    auto valid = [&](int e) { return c0 + e < cn; };
+    // An entry past the count holds key 0, below every candidate's order key
+    // (scores are >= +0.0, so keys are >= ZERO_KEY): such entries never pass a
+    // comparison against ZERO_KEY or T, and the radix rounds place them in
+    // digit 0 (d = max(key, kmin) - kmin = 0), below the k-th key.
     uint32_t key[PER], ix[PER];
 #pragma unroll
-    for (int e = 0; e < PER; e += 2) {
-        key[e] = valid(e) ? cand_key(rw.raw[e / 2].x, scale) : 0u;
-        key[e + 1] = valid(e + 1) ? cand_key(rw.raw[e / 2].z, scale) : 0u;
-        ix[e] = rw.raw[e / 2].y;
-        ix[e + 1] = rw.raw[e / 2].w;
+    for (int e = 0; e < PER; ++e) {
+        key[e] = e * SL_NT + tid < cn ? cand_key(rw.raw[e].x, scale) : 0u;
+        ix[e] = rw.raw[e].y;
     }
-    auto idx_of = [&](int e) { return ix[e]; };
 
     if (zero_mode) {
         // The list holds every key with a positive score (plus some zeros);
         // every key off the list scores zero.
-        uint32_t npl = 0;
-        if (wl) {
+        bool pos[PER], none[PER];
 #pragma unroll
-            for (int e = 0; e < PER; ++e) npl += valid(e) && key[e] > ZERO_KEY ? 1u : 0u;
+        for (int e = 0; e < PER; ++e) {
+            pos[e] = key[e] > ZERO_KEY;
+            none[e] = false;
         }
-        uint32_t np;
-        const uint32_t pbase = block_excl_scan<SL_NT>(npl, wsum, &np);
+        uint32_t rk[PER], np;
+        list_prefix2<PER>(pos, none, tbl, rk, &np);
+        np >>= 16;
         if (np < (uint32_t)k) {
             // Positives plus the lowest-index zeros. With P the positives in
             // index order, P[r] - r zeros precede P[r]; the first cs
             // positives (P[r] - r < Z) come before the Z-th zero.
             const uint32_t Z = (uint32_t)k - np;
-            uint32_t r = pbase, csl = 0;
+            bool early[PER];
 #pragma unroll
-            for (int e = 0; e < PER; ++e) {
-                if (valid(e) && key[e] > ZERO_KEY) {
-                    csl += idx_of(e) - r < Z ? 1u : 0u;
-                    ++r;
-                }
-            }
-            const uint32_t cs = block_total(csl, wsum);
+            for (int e = 0; e < PER; ++e) early[e] = pos[e] && ix[e] - (rk[e] >> 16) < Z;
+            uint32_t dummy[PER], cs;
+            list_prefix2<PER>(early, none, tbl, dummy, &cs);
+            cs >>= 16;
             const uint32_t head = Z + cs;  // out[0, head) = 0 .. head - 1
             for (uint32_t o = tid; o < head; o += SL_NT) out[o] = (int32_t)o;
-            r = pbase;
 #pragma unroll
             for (int e = 0; e < PER; ++e) {
-                if (valid(e) && key[e] > ZERO_KEY) {
-                    if (r >= cs) out[Z + r] = (int32_t)idx_of(e);
-                    ++r;
-                }
+                const uint32_t r = rk[e] >> 16;
+                if (pos[e] && r >= cs) out[Z + r] = (int32_t)ix[e];
             }
             return;
         }
@@ -573,15 +594,12 @@ __device__ __forceinline__ void select_row(const PrefillArgs& a, long long task,
 
     // Range of the row's order keys; digits are taken relative to the smallest.
     uint32_t lo = 0xffffffffu, hi = 0u;
-    if (wl) {
 #pragma unroll
-        for (int e = 0; e < PER; ++e) {
-            if (valid(e)) {
-                lo = min(lo, key[e]);
-                hi = max(hi, key[e]);
-            }
-        }
+    for (int e = 0; e < PER; ++e) {
+        lo = min(lo, key[e] - 1u);  // an entry past the count wraps to the top
+        hi = max(hi, key[e]);
     }
+    lo += 1u;
     if (tid == 0) {
         res[2] = 0xffffffffu;
         res[3] = 0u;
@@ -608,12 +626,11 @@ __device__ __forceinline__ void select_row(const PrefillArgs& a, long long task,
         const uint32_t mask = (1u << (hsh - sh)) - 1u;
         if (tid < 256) hist[tid] = 0u;
         __syncthreads();
-        if (wl) {
 #pragma unroll
-            for (int e = 0; e < PER; ++e) {
-                const uint32_t d = key[e] - kmin;
-                hist_add(hist, (d >> sh) & mask, valid(e) && (first || (d >> hsh) == prefix));
-            }
+        for (int e = 0; e < PER; ++e) {
+            if (e * SL_NT >= cn) continue;  // workgroup-uniform
+            const uint32_t d = max(key[e], kmin) - kmin;
+            hist_add(hist, (d >> sh) & mask, first || (d >> hsh) == prefix);
         }
         __syncthreads();
         if (tid < 64) wave_find_bin8(hist, rem, res);
@@ -624,12 +641,11 @@ __device__ __forceinline__ void select_row(const PrefillArgs& a, long long task,
         first = false;
         // Few keys left in the bin: gather them for wave 0.
         if (sh > 0 && hist[bin] <= (uint32_t)SL_GMAX) {
-            if (wl) {
 #pragma unroll
-                for (int e = 0; e < PER; ++e) {
-                    const uint32_t d = key[e] - kmin;
-                    if (valid(e) && (d >> sh) == prefix) gk[atomicAdd(&res[4], 1u)] = d;
-                }
+            for (int e = 0; e < PER; ++e) {
+                if (e * SL_NT >= cn) continue;
+                const uint32_t d = max(key[e], kmin) - kmin;
+                if ((d >> sh) == prefix) gk[atomicAdd(&res[4], 1u)] = d;
             }
             gathered = true;
         }
@@ -670,44 +686,31 @@ __device__ __forceinline__ void select_row(const PrefillArgs& a, long long task,
         rem = res[6];
     }
     const uint32_t T = kmin + prefix;  // keep every key above T and the first rem keys equal to T
-    // Ordered compaction over the index-ordered list.
-    uint32_t gtl = 0, eql = 0;
-    if (wl) {
-#pragma unroll
-        for (int e = 0; e < PER; ++e) {
-            if (valid(e)) {
-                gtl += key[e] > T ? 1u : 0u;
-                eql += key[e] == T ? 1u : 0u;
-            }
-        }
-    }
-    uint32_t tot;
-    const uint32_t pk = block_excl_scan<SL_NT>((gtl << 16) | eql, wsum, &tot);
-    uint32_t gb = pk >> 16, eb = pk & 0xffffu;
-    if (!wl) return;
+    // Ordered compaction: every key above T, and the T-ties in list order.
+    bool gt[PER], eq[PER];
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
-        if (!valid(e)) continue;
-        if (key[e] > T) {
-            out[gb + min(eb, rem)] = (int32_t)ix[e];
-            ++gb;
-        } else if (key[e] == T) {
-            if (eb < rem) out[gb + eb] = (int32_t)ix[e];
-            ++eb;
-        }
+        gt[e] = key[e] > T;
+        eq[e] = key[e] == T;
+    }
+    uint32_t pk[PER], tot;
+    list_prefix2<PER>(gt, eq, tbl, pk, &tot);
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+        const uint32_t gb = pk[e] >> 16, eb = pk[e] & 0xffffu;
+        if (gt[e]) out[gb + min(eb, rem)] = (int32_t)ix[e];
+        else if (eq[e] && eb < rem) out[gb + eb] = (int32_t)ix[e];
     }
 }
-
-// One row per workgroup.
 template <int PER>
 __global__ __launch_bounds__(SL_NT) void prefill_select_kernel(PrefillArgs a) {
     __shared__ uint32_t hist[256];
     __shared__ uint32_t gk[SL_GMAX];
-    __shared__ uint32_t wsum[SL_NT / 64];
+    __shared__ uint32_t tbl[PER * SL_NT / 64 + 1];
     __shared__ uint32_t res[8];
     SelRow<PER> rw;
     sel_fetch<PER>(a, blockIdx.x, rw);
-    select_row<PER>(a, blockIdx.x, rw, hist, gk, wsum, res);
+    select_row<PER>(a, blockIdx.x, rw, hist, gk, tbl, res);
 }
 
 // ----------------------------------------------------------------- fallback
@@ -765,13 +768,14 @@ hipError_t launch_d(const PrefillArgs& a, int part, hipStream_t s) {
     } else if (part == 2) {
         if (rows > 0x7fffffffLL) return hipErrorInvalidConfiguration;
         const dim3 grid((unsigned)rows), blk(SL_NT);
-        // PER = 2 ceil(cap / (2 SL_NT)) entries per thread at most
-        const int per = (a.cap + 2 * SL_NT - 1) / (2 * SL_NT) * 2;
+        // PER = ceil(cap / SL_NT) entries per thread at most
+        const int per = (a.cap + SL_NT - 1) / SL_NT;
         if (per <= 2) hipLaunchKernelGGL(prefill_select_kernel<2>, grid, blk, 0, s, a);
         else if (per <= 4) hipLaunchKernelGGL(prefill_select_kernel<4>, grid, blk, 0, s, a);
         else if (per <= 8) hipLaunchKernelGGL(prefill_select_kernel<8>, grid, blk, 0, s, a);
-        else if (per <= 12) hipLaunchKernelGGL(prefill_select_kernel<12>, grid, blk, 0, s, a);
-        else if (per <= 16) hipLaunchKernelGGL(prefill_select_kernel<16>, grid, blk, 0, s, a);
+        else if (per <= 11) hipLaunchKernelGGL(prefill_select_kernel<11>, grid, blk, 0, s, a);
+        else if (per <= 14) hipLaunchKernelGGL(prefill_select_kernel<14>, grid, blk, 0, s, a);
+        else if (per <= 18) hipLaunchKernelGGL(prefill_select_kernel<18>, grid, blk, 0, s, a);
         else if (per <= 26) hipLaunchKernelGGL(prefill_select_kernel<26>, grid, blk, 0, s, a);
         else return hipErrorInvalidValue;
     } else {
