@@ -46,6 +46,7 @@ constexpr int TH_ROWS = 16;       // rows per threshold workgroup
 constexpr int TH_BINS = 1024;     // 10-bit digits of the threshold rounds
 constexpr int TH_MAX_SAMPLES = 4096;
 constexpr int TH_TARGET = 64;     // samples expected above tau
+constexpr int TH_UN = 4;          // sampled-key tiles loaded together per pass
 constexpr int FL_CHUNK = 64;      // keys per staged chunk of the filter
 constexpr int FB_WGS = 256;       // fallback workgroups
 
@@ -167,18 +168,26 @@ __global__ __launch_bounds__(256) void prefill_threshold_kernel(PrefillArgs a) {
     for (int round = 0; round < 2; ++round) {
         for (int i = threadIdx.x; i < TH_ROWS * TH_BINS; i += 256) (&hist[0][0])[i] = 0u;
         __syncthreads();
-        for (int t0 = wave * 16; t0 < ns_max; t0 += 4 * 16) {
-            Frag<DT, D> fk;
-            fk.load(kbase + (size_t)(min(t0 + n, ns_max - 1) * S) * RB, g);
-            const f32x4 acc = tile_dot_k32<D>(fq, fk);
+        // TH_UN tiles per pass: their sampled key rows are loaded together
+        // (one memory latency per pass, not per tile).
+        for (int t00 = wave * 16; t00 < ns_max; t00 += TH_UN * 4 * 16) {
+            Frag<DT, D> fk[TH_UN];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = 4 * g + r;
-                const uint32_t key = rank_key(relu_scaled(acc[r], a.scale));
-                const bool ok = t0 + n < ns_r[r];
-                const bool in = round == 0 ? ok : ok && (key >> 22) == digit1[row];
-                const uint32_t bin = round == 0 ? (key >> 22) : ((key >> 12) & 1023u);
-                hist_add(&hist[0][0], (uint32_t)row * TH_BINS + bin, in);
+            for (int u = 0; u < TH_UN; ++u)
+                fk[u].load(kbase + (size_t)(min(t00 + 64 * u + n, ns_max - 1) * S) * RB, g);
+#pragma unroll
+            for (int u = 0; u < TH_UN; ++u) {
+                const int t0 = t00 + 64 * u;
+                const f32x4 acc = tile_dot_k32<D>(fq, fk[u]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 4 * g + r;
+                    const uint32_t key = rank_key(relu_scaled(acc[r], a.scale));
+                    const bool ok = t0 + n < ns_r[r];
+                    const bool in = round == 0 ? ok : ok && (key >> 22) == digit1[row];
+                    const uint32_t bin = round == 0 ? (key >> 22) : ((key >> 12) & 1023u);
+                    hist_add(&hist[0][0], (uint32_t)row * TH_BINS + bin, in);
+                }
             }
         }
         __syncthreads();
