@@ -14,7 +14,7 @@
 //              accumulator instead ("zero mode").
 //   filter     per 64- or 128-row block: a producer wave streams the block's causal
 //              keys into an LDS ring of 64-key chunks with global->LDS copies
-//              (granule-major layout, several chunks in flight); four
+//              (several chunks in flight); four
 //              consumer waves of 16 or 32 rows each score every chunk on MFMA.
 //              Keys are the MFMA row operand, so each lane holds 16
 //              consecutive keys of one query; a subtract and a funnel shift
@@ -123,6 +123,71 @@ __device__ __forceinline__ void load_cm(Frag<1, D>& f, const uint8_t* tile, int 
 #pragma unroll
     for (int c = 0; c < Frag<1, D>::NC; ++c)
         f.v[c] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const i32x4*>(t + (4 * c + g) * COLB));
+}
+
+// Row-major key chunks in LDS: chunk key r occupies RB contiguous bytes at
+// tile + r RB, its 16-byte granule q at granule slot q ^ sw(r). The chunk is
+// contiguous in global memory too, so each 1 KB global->LDS copy reads 1 KB
+// of consecutive bytes (every 4 lanes one 64-byte segment: XOR keeps aligned
+// groups of four granules together). A fragment read touches chunk keys
+// r = 16 a + 4 u + b (a, b = 0..3) for one tile u; the row pitch already
+// separates some values of b in the LDS banks, so sw takes a and the bits of
+// b that the pitch leaves together, as far as q ^ sw stays below GPR.
+constexpr int gcd_c(int x, int y) { return y == 0 ? x : gcd_c(y, x % y); }
+
+template <int RB>
+struct RingSw {
+    static constexpr int GPR = RB / 16;             // granules per key row
+    static constexpr int P2 = GPR & -GPR;           // largest power of two dividing GPR
+    static constexpr int SWM = (P2 < 16 ? P2 : 16) - 1;
+    static constexpr int SB = (RB / 4) % 64 == 32 ? 1 : 0;  // pitch separates b & 1 only
+    __device__ static __forceinline__ int sw(int r) {
+        return (((r >> 4) & 3) | (((r & 3) >> SB) << 2)) & SWM;
+    }
+    // byte b of chunk key r
+    __device__ static __forceinline__ const uint8_t* at(const uint8_t* tile, int r, int b) {
+        return tile + r * RB + 16 * ((b >> 4) ^ sw(r)) + (b & 15);
+    }
+};
+
+// Fragment of chunk key r from a row-major ring slot (the same bytes, in the
+// same register slots, as Frag::load takes from a contiguous row). The XOR
+// only touches the low bits of the granule index, so each read is a
+// per-lane base plus a constant offset.
+template <int RB, int D>
+__device__ __forceinline__ void load_rm(Frag<0, D>& f, const uint8_t* tile, int r, int g) {
+    using W = RingSw<RB>;
+    const int sw = W::sw(r);
+    const uint8_t* row = tile + r * RB;
+    // granule 8c + h ^ sw = 8 (c ^ (sw >> 3)) + (h ^ (sw & 7))
+    const uint8_t* lo = row + 16 * (g ^ (sw & 7));
+    const uint8_t* hi = row + 16 * ((4 + g) ^ (sw & 7));
+    const int sc = sw >> 3;
+#pragma unroll
+    for (int c = 0; c < Frag<0, D>::NB; ++c) {
+        const int cc = W::SWM <= 7 ? c : (c ^ sc);
+        const i32x4 l = *reinterpret_cast<const i32x4*>(lo + 128 * cc);
+        const i32x4 h = *reinterpret_cast<const i32x4*>(hi + 128 * cc);
+        f.big[c] = i32x8{l[0], l[1], l[2], l[3], h[0], h[1], h[2], h[3]};
+    }
+#pragma unroll
+    for (int c = 0; c < Frag<0, D>::NS; ++c)
+        f.small[c] = *reinterpret_cast<const long*>(
+            W::at(tile, r, 128 * Frag<0, D>::NB + 32 * c + 8 * g));
+}
+
+template <int RB, int D>
+__device__ __forceinline__ void load_rm(Frag<1, D>& f, const uint8_t* tile, int r, int g) {
+    using W = RingSw<RB>;
+    const int sw = W::sw(r);
+    // granule 4c + g ^ sw = 4 (c ^ (sw >> 2)) + (g ^ (sw & 3))
+    const uint8_t* base = tile + r * RB + 16 * (g ^ (sw & 3));
+    const int sc = sw >> 2;
+#pragma unroll
+    for (int c = 0; c < Frag<1, D>::NC; ++c) {
+        const int cc = W::SWM <= 3 ? c : (c ^ sc);
+        f.v[c] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const i32x4*>(base + 64 * cc));
+    }
 }
 
 // s_waitcnt with vmcnt = N (expcnt and lgkmcnt left open).
@@ -264,14 +329,16 @@ static_assert(FL_CHUNK == 64, "the producer's lane -> key map covers 64 keys");
 template <int DT, int D, int QT>
 __global__ __launch_bounds__(320) void prefill_filter_kernel(PrefillArgs a) {
     constexpr int RB = D * (DT == 0 ? 1 : 2);
+    // Ring layout: row-major for fp8 keys (timed 1.31 -> 1.20 ms at 64K),
+    // granule-major for bf16 (row-major timed 6.4 -> 6.9 ms at 128K).
+    constexpr bool RM = DT == 0;
     constexpr int WROWS = 16 * QT;   // rows per consumer wave
     constexpr int ROWS = 4 * WROWS;  // rows per workgroup
     constexpr int GPR = RB / 16;            // 16-byte granules per key row
-    constexpr int COLB = FL_CHUNK * 16;     // bytes of one granule column
     constexpr int NBUF = fl_nbuf<RB>();
     static_assert(RB % 16 == 0 && (NBUF - 1) * GPR < 64, "chunk pipeline");
-    // Key chunks, granule-major: granule j of the key at row position rp
-    // (see krow below) is at ring[slot] + j * COLB + 16 rp.
+    // Key chunks: row-major with swizzled granules (RingSw), or granule-major
+    // (granule j of the key at row position rp at slot + j * 1024 + 16 rp).
     __shared__ __attribute__((aligned(16))) uint8_t ring[NBUF][FL_CHUNK * RB];
     // per-wave copy of each lane's 16 accumulators: [wave][u][lane] x 4
     __shared__ f32x4 stage[4][4][64];
@@ -287,16 +354,29 @@ __global__ __launch_bounds__(320) void prefill_filter_kernel(PrefillArgs a) {
     const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + (size_t)b * a.n_k * RB;
 
     if (wave == 4) {
-        // Producer: global -> LDS copies, NBUF - 1 chunks ahead. Lane l moves
-        // the key at row position l: chunk row 16 ((l / 4) % 4) + 4 (l / 16) + l % 4.
+        // Producer: global -> LDS copies, NBUF - 1 chunks ahead.
+        //   row-major (RM): copy i moves granules 64 i .. 64 i + 63 of the
+        //     chunk: lane l fills granule slot s = P % GPR of chunk key
+        //     r = P / GPR (P = 64 i + l) with the key's granule s ^ sw(r);
+        //   granule-major: copy j moves granule j of every key, lane l taking
+        //     the key at row position l (chunk key 16 ((l / 4) % 4) + 4 (l / 16)
+        //     + l % 4).
         const int kr = 16 * ((lane >> 2) & 3) + 4 * (lane >> 4) + (lane & 3);
         auto issue = [&](int c) {
-            const int key = min(c * FL_CHUNK + kr, a.n_k - 1);
-            const uint8_t* src = kbase + (size_t)key * RB;
             uint8_t* dst = ring[c % NBUF];
 #pragma unroll
-            for (int j = 0; j < GPR; ++j)
-                __builtin_amdgcn_global_load_lds(src + 16 * j, dst + j * COLB, 16, 0, 0);
+            for (int i = 0; i < GPR; ++i) {
+                if constexpr (RM) {
+                    const int P = 64 * i + lane, r = P / GPR, q = (P % GPR) ^ RingSw<RB>::sw(r);
+                    const int key = min(c * FL_CHUNK + r, a.n_k - 1);
+                    __builtin_amdgcn_global_load_lds(kbase + (size_t)key * RB + 16 * q,
+                                                     dst + 1024 * i, 16, 0, 0);
+                } else {
+                    const int key = min(c * FL_CHUNK + kr, a.n_k - 1);
+                    __builtin_amdgcn_global_load_lds(kbase + (size_t)key * RB + 16 * i,
+                                                     dst + i * (FL_CHUNK * 16), 16, 0, 0);
+                }
+            }
         };
         const int pre = min(NBUF - 1, n_chunks);
         for (int c = 0; c < pre; ++c) issue(c);
@@ -353,9 +433,14 @@ __global__ __launch_bounds__(320) void prefill_filter_kernel(PrefillArgs a) {
             // Every fragment load of the chunk completes before the first
             // MFMA, so no load can overwrite an operand register of an MFMA
             // still queued behind a dependent accumulate chain.
+            // A operand row n of key tile u: chunk key 16 (n / 4) + 4 u + n % 4
+            // (row position 16 u + n in the granule-major layout)
             Frag<DT, D> fk[4];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) load_cm<COLB>(fk[u], tile, 16 * u + n, g);
+            for (int u = 0; u < 4; ++u) {
+                if constexpr (RM) load_rm<RB>(fk[u], tile, 16 * (n >> 2) + 4 * u + (n & 3), g);
+                else load_cm<FL_CHUNK * 16>(fk[u], tile, 16 * u + n, g);
+            }
             __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
             __builtin_amdgcn_sched_barrier(0);
             f32x4 acc[QT][4];
