@@ -36,6 +36,8 @@
 #include "topk_common.h"
 #include "lanes.h"
 
+#include <type_traits>
+
 namespace dsa {
 namespace {
 
@@ -49,6 +51,8 @@ constexpr int TH_TARGET = 64;     // samples expected above tau
 constexpr int TH_UN = 4;          // sampled-key tiles loaded together per pass
 constexpr int FL_CHUNK = 64;      // keys per staged chunk of the filter
 constexpr int FB_WGS = 256;       // fallback workgroups
+constexpr int kBufWord3 = 0x00020000;  // buffer descriptor word 3: 32-bit data format
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ int qrow(const PrefillArgs& a, int i) { return a.row0 + i * a.rstride; }
 
@@ -403,7 +407,7 @@ __global__ __launch_bounds__(320) void prefill_filter_kernel(PrefillArgs a) {
     bool live[QT];
     float tau[QT];
     Frag<DT, D> fq[QT];
-    uint2* list[QT];
+    int row_vo[QT];    // byte offset of the row's list in the wave's list block
     uint32_t cnt[QT];  // each row's list length (same in the row's 4 lanes)
 #pragma unroll
     for (int t = 0; t < QT; ++t) {
@@ -413,19 +417,29 @@ __global__ __launch_bounds__(320) void prefill_filter_kernel(PrefillArgs a) {
         my_len[t] = live[t] ? row_len(a, my_i[t]) : 0;
         tau[t] = live[t] ? a.tau_acc[(size_t)b * a.rows + my_i[t]] : __builtin_inff();
         fq[t].load(static_cast<const uint8_t*>(a.q) + ((size_t)b * a.n_q + qrow(a, my_i[t])) * RB, g);
-        list[t] = a.cand + ((size_t)b * a.rows + my_i[t]) * a.cap;
+        row_vo[t] = (16 * t + n) * a.cap * 8;
         cnt[t] = 0;
     }
-    const bool wave_live = wi0 < a.rows;
-    const int w_kend = wave_live ? row_len(a, min(wi0 + WROWS - 1, a.rows - 1)) : 0;
-    const int w_kmin = wave_live ? row_len(a, wi0) : 0;
+    // Wave-uniform bounds (scalar registers, so the tail test is a branch).
+    const int wi0s = __builtin_amdgcn_readfirstlane(wi0);
+    const bool wave_live = wi0s < a.rows;
+    const int w_kend = wave_live ? row_len(a, min(wi0s + WROWS - 1, a.rows - 1)) : 0;
+    const int w_kmin = wave_live ? row_len(a, wi0s) : 0;
+    // The wave's WROWS lists are consecutive: one buffer descriptor covers
+    // them, and a store takes a 32-bit byte offset.
+    const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.cand + ((size_t)b * a.rows + (wave_live ? wi0s : 0)) * a.cap), (short)0,
+        WROWS * a.cap * 8, kBufWord3);
     wait_vmcnt<0>();  // the query fragments are in registers before the chunk loop
     const uint32_t cap = (uint32_t)a.cap;
 
     // A operand row n of key tile u is chunk key 16 (n / 4) + 4 u + n % 4
     // (row position 16 u + n), so output row 4 g + r of tile u is key
     // 16 g + 4 u + r: lane (n, g) holds keys [16 g, 16 g + 16) of the chunk.
-    for (int c = 0; c < n_chunks; ++c) {
+    // Chunks below w_kmin lie inside every row's causal range; only the
+    // later ones (TAIL) mask keys past a row's end.
+    auto chunk = [&](const int c, auto tail_tag) {
+        constexpr bool TAIL = decltype(tail_tag)::value;
         __syncthreads();
         const int k0 = c * FL_CHUNK;
         if (k0 < w_kend) {
@@ -458,7 +472,7 @@ __global__ __launch_bounds__(320) void prefill_filter_kernel(PrefillArgs a) {
                     rej = __builtin_amdgcn_alignbit(
                         rej, __float_as_uint(acc[t][i >> 2][i & 3] - tau[t]), 31);
                 uint32_t bits = ~rej & 0xffffu;
-                if (k0 + FL_CHUNK > w_kmin) {
+                if constexpr (TAIL) {
                     const int v = my_len[t] - (k0 + 16 * g);
                     bits &= v >= 16 ? 0xffffu : (v <= 0 ? 0u : (1u << v) - 1u);
                 }
@@ -478,19 +492,27 @@ __global__ __launch_bounds__(320) void prefill_filter_kernel(PrefillArgs a) {
                 if (__ballot(bits != 0u) != 0ull) {
 #pragma unroll
                     for (int u = 0; u < 4; ++u) stage[wave][u][lane] = acc[t][u];
-                    const float* st = reinterpret_cast<const float*>(&stage[wave][0][lane]);
+                    // accumulator i of this lane: byte (i / 4) * 1024 + (i % 4) * 4
+                    // of its stage column, = (260 i) & 0xC0C
+                    const uint8_t* sb = reinterpret_cast<const uint8_t*>(&stage[wave][0][lane]);
                     const uint32_t kb = (uint32_t)(k0 + 16 * g);
-                    uint32_t oo = o;
+                    int vo = row_vo[t] + (int)o * 8;
                     while (bits != 0u) {
                         const int i = __builtin_ctz(bits);
                         bits &= bits - 1u;
-                        list[t][oo++] = make_uint2(__float_as_uint(st[(i >> 2) * 256 + (i & 3)]),
-                                                   kb + (uint32_t)i);
+                        const uint32_t v = *reinterpret_cast<const uint32_t*>(sb + ((i * 260) & 0xC0C));
+                        const u32x2 e = {v, kb + (uint32_t)i};
+                        __builtin_amdgcn_raw_buffer_store_b64(e, lrs, vo, 0, 0);
+                        vo += 8;
                     }
                 }
             }
         }
-    }
+    };
+    const int c_full = min(n_chunks, w_kmin / FL_CHUNK);
+    int c = 0;
+    for (; c < c_full; ++c) chunk(c, std::false_type{});
+    for (; c < n_chunks; ++c) chunk(c, std::true_type{});
 #pragma unroll
     for (int t = 0; t < QT; ++t)
         if (g == 0 && live[t]) a.cnt[(size_t)b * a.rows + my_i[t]] = cnt[t];
