@@ -60,8 +60,9 @@ struct WaveState {
 // every bank once per 16 lanes.
 constexpr int ROWB = HD * 2;             // bytes of one K, V or Q row
 constexpr int KVB = 32 * ROWB;           // the K (or V) rows of one step: 8 KB
-constexpr int QOFF = 2 * KVB;            // Q rows: 4 KB
-constexpr int WAVE_LDS = QOFF + 16 * ROWB;  // 20 KB
+// 16 KB per wave (the prologue stages Q through the K rows' space): eight
+// waves per CU fit in 128 KB of LDS.
+constexpr int WAVE_LDS = 2 * KVB;
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 constexpr int kBufWord3 = 0x00020000;  // buffer descriptor word 3: 32-bit data format
@@ -253,16 +254,14 @@ __device__ __forceinline__ void wave_attend(const AttnArgs& a, long long qrow, i
     StepRows R;
     uint32_t vc = slot_mask(jA, e_first, e_end, n_k, lane);
     load_rows(rk, rv, jA, lane, R);
-    uint8_t* qs = lds + QOFF;
+    // Q goes through the K rows' space first (its fragments are read back
+    // before the first step's rows are stored there).
+    uint8_t* qs = lds;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
         const int rho = 4 * c + (lane >> 4);
         *reinterpret_cast<u16x8*>(qs + rho * ROWB + 16 * ((lane & 15) ^ rho)) = qv[c];
     }
-    store_rows(lds, R, lane);
-    uint32_t vn = slot_mask(jB, e_first + e_step, e_end, n_k, lane);
-    if (e_first + e_step < e_end) load_rows(rk, rv, jB, lane, R);
-    jA = load_slot(sel, e_first + 2 * e_step, e_end, lane);
     wave_lds_fence();
     // Q^T fragment: lane (head m, group g) holds Q[m][32s + 8g .. +8] for s = 0..3.
     bf16x8 qf[4];
@@ -271,6 +270,12 @@ __device__ __forceinline__ void wave_attend(const AttnArgs& a, long long qrow, i
         const u16x8 v = *reinterpret_cast<const u16x8*>(qs + m * ROWB + 16 * ((4 * s + g) ^ m));
         qf[s] = as_bf16x8(m < a.H ? v : u16x8{0, 0, 0, 0, 0, 0, 0, 0});
     }
+    wave_lds_fence();
+    store_rows(lds, R, lane);
+    uint32_t vn = slot_mask(jB, e_first + e_step, e_end, n_k, lane);
+    if (e_first + e_step < e_end) load_rows(rk, rv, jB, lane, R);
+    jA = load_slot(sel, e_first + 2 * e_step, e_end, lane);
+    wave_lds_fence();
     int e = e_first;
     for (;;) {
         // LDS: step e; R: step e + 1 (in flight); jA: idx of step e + 2.
