@@ -6,8 +6,8 @@
 // keys; the page fuses indexing, selection and masking to avoid writing the
 // intermediates. Kernels, per slab of query rows:
 //   threshold  per 16-row block: scores every S-th key of each row's prefix
-//              (MFMA), two 10-bit radix rounds over those samples give tau,
-//              the lower edge of the 20-bit bin holding the m-th largest
+//              (MFMA), two 9-bit radix rounds over those samples give tau,
+//              the lower edge of the 18-bit bin holding the m-th largest
 //              sample (m S ~ 2 top_k); tau becomes the smallest fp32
 //              accumulator whose scaled score reaches it. A row whose sample
 //              threshold is not positive keeps every non-negative
@@ -45,7 +45,9 @@ using namespace frag;
 using namespace topk;
 
 constexpr int TH_ROWS = 16;       // rows per threshold workgroup
-constexpr int TH_BINS = 1024;     // 10-bit digits of the threshold rounds
+constexpr int TH_DIG = 9;         // bits per digit of the two threshold rounds (the
+                                  // 16 x 512-bin histogram fits four workgroups per CU)
+constexpr int TH_BINS = 1 << TH_DIG;
 constexpr int TH_MAX_SAMPLES = 4096;
 constexpr int TH_TARGET = 64;     // samples expected above tau
 constexpr int TH_UN = 4;          // sampled-key tiles loaded together per pass
@@ -253,8 +255,9 @@ __global__ __launch_bounds__(256) void prefill_threshold_kernel(PrefillArgs a) {
                     const int row = 4 * g + r;
                     const uint32_t key = rank_key(relu_scaled(acc[r], a.scale));
                     const bool ok = t0 + n < ns_r[r];
-                    const bool in = round == 0 ? ok : ok && (key >> 22) == digit1[row];
-                    const uint32_t bin = round == 0 ? (key >> 22) : ((key >> 12) & 1023u);
+                    const bool in = round == 0 ? ok : ok && (key >> (32 - TH_DIG)) == digit1[row];
+                    const uint32_t bin = round == 0 ? (key >> (32 - TH_DIG))
+                                                    : ((key >> (32 - 2 * TH_DIG)) & (TH_BINS - 1u));
                     hist_add(&hist[0][0], (uint32_t)row * TH_BINS + bin, in);
                 }
             }
@@ -281,7 +284,7 @@ __global__ __launch_bounds__(256) void prefill_threshold_kernel(PrefillArgs a) {
                         } else if ((uint32_t)ns <= m) {
                             tacc = 0.0f;  // zero mode
                         } else {
-                            const uint32_t tkey = (digit1[row] << 22) | (bin << 12);
+                            const uint32_t tkey = (digit1[row] << (32 - TH_DIG)) | (bin << (32 - 2 * TH_DIG));
                             if (tkey <= 0x80000000u) {
                                 tacc = 0.0f;  // zero mode
                             } else {
