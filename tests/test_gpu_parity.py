@@ -214,6 +214,54 @@ def test_decode_threshold_misses_falls_back(gpu_lib):
     assert_attn_close(O, O_ref, lse, lse_ref, "sampled only")
 
 
+def test_prefill_threshold_misses_fall_back(gpu_lib):
+    # Only the keys the prefill threshold pass samples (every S-th key,
+    # S = 2 top_k / 64 = 20) score above zero. Rows longer than 1280 keys have
+    # more than m = 64 samples, so their threshold is positive and keeps only
+    # the sampled keys, fewer than top_k: the fallback kernel recomputes them.
+    n, k, S = 3000, 640, 20
+    w = Workload("prefill_sampled_only", "prefill", 1, n, n, 0, 128, "fp8", k, 2)
+    x = synth.make_inputs(w, seed=11)
+    g = torch.Generator().manual_seed(11)
+    x["q_idx"] = torch.ones(1, n, 128).to(torch.float8_e4m3fn)
+    kk = -torch.ones(1, n, 128)
+    kk[:, ::S] = torch.randint(1, 3, (1, (n + S - 1) // S, 128), generator=g).float()
+    x["k_idx"] = kk.to(torch.float8_e4m3fn)
+    d = to_dev(x)
+    say("prefill threshold miss: n=%d k=%d" % (n, k))
+    idx, O, lse = dsa.forward(d["q_idx"], d["k_idx"], d["Q"], d["K"], d["V"], 0, k)
+    idx_ref, O_ref, lse_ref = oracle.forward(x["q_idx"], x["k_idx"], x["Q"], x["K"], x["V"], 0, k)
+    assert np.array_equal(idx.cpu().numpy(), idx_ref)
+    # a long row (ascending indices): every sampled key plus the
+    # lowest-index zero scores
+    row = idx_ref[0, n - 1]
+    zeros = [j for j in range(n) if j % S][: k - n // S]
+    assert sorted(row.tolist()) == sorted(list(range(0, n, S)) + zeros)
+    assert_attn_close(O, O_ref, lse, lse_ref, "prefill sampled only")
+
+
+def test_prefill_equal_scores_overflow_falls_back(gpu_lib):
+    # Every score is equal and positive: the threshold admits whole rows, more
+    # than the candidate list holds (3 top_k + 768 = 960 entries) once a row
+    # is longer than that, so those rows are recomputed by the fallback; the
+    # k lowest indices win every row.
+    n, k = 2500, 64
+    w = Workload("prefill_equal", "prefill", 2, n, n, 0, 128, "fp8", k, 2)
+    x = synth.make_inputs(w, seed=12)
+    x["q_idx"] = torch.ones(2, n, 128).to(torch.float8_e4m3fn)
+    x["k_idx"] = torch.ones(2, n, 128).to(torch.float8_e4m3fn)
+    d = to_dev(x)
+    say("prefill equal scores: n=%d k=%d" % (n, k))
+    idx, O, lse = dsa.forward(d["q_idx"], d["k_idx"], d["Q"], d["K"], d["V"], 0, k)
+    idx_ref, O_ref, lse_ref = oracle.forward(x["q_idx"], x["k_idx"], x["Q"], x["K"], x["V"], 0, k)
+    got = idx.cpu().numpy()
+    assert np.array_equal(got, idx_ref)
+    for i in (0, 63, 64, 959, 960, 2499):
+        m = min(k, i + 1)
+        assert list(got[1, i, :m]) == list(range(m)) and np.all(got[1, i, m:] == -1)
+    assert_attn_close(O, O_ref, lse, lse_ref, "prefill equal scores")
+
+
 def test_all_zero_query_selects_first_keys(gpu_lib):
     w = Workload("zeros", "prefill", 1, 600, 600, 0, 128, "fp8", 64, 2)
     x = synth.make_inputs(w, seed=6)
