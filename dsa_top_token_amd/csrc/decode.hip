@@ -322,17 +322,24 @@ __device__ __forceinline__ void load_sw(Frag<DT, D>& f, const uint8_t* buf, int 
     }
 }
 
-// The filter for 128-byte key rows: each wave streams its 256 keys in four
-// 64-key steps through a two-buffer LDS ring (contiguous 1 KB copies), the
-// same scores and candidate lists as decode_filter_kernel.
+// Key rows of at most LDS_RB_MAX bytes take the LDS-staged filter.
+constexpr int LDS_RB_MAX = 160;
+
+// The filter for key rows of up to LDS_RB_MAX bytes: each wave streams its
+// 256 keys in four 64-key steps through a two-buffer LDS ring of contiguous
+// 1 KB copies (128-byte rows: swizzled per row as sw_slot gives; other
+// widths: the step's bytes in order), the same scores and candidate lists as
+// decode_filter_kernel.
 template <int DT, int D>
 __global__ __launch_bounds__(256) void decode_filter_lds_kernel(DecodeArgs a) {
     constexpr int TILES = 4, STEPS = 4;
-    constexpr int RB = 128;
+    constexpr int RB = D * (DT == 0 ? 1 : 2);
+    constexpr bool SW = RB == 128;
     constexpr int KW = 16 * TILES * STEPS;  // = SLOT
     constexpr int KB = 4 * KW;
-    constexpr int STEP_BYTES = 16 * TILES * RB;  // 8 KB = 8 copies of 1 KB
-    static_assert(KW == SLOT && D * (DT == 0 ? 1 : 2) == RB, "one candidate list per wave");
+    constexpr int STEP_BYTES = 16 * TILES * RB;  // RB / 16 copies of 1 KB
+    constexpr int CPS = STEP_BYTES / 1024;       // copies per step
+    static_assert(KW == SLOT && RB % 16 == 0 && RB <= LDS_RB_MAX, "one candidate list per wave");
     __shared__ __attribute__((aligned(16))) uint8_t ring[4][2][STEP_BYTES];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n = lane & 15, g = lane >> 4;
@@ -349,16 +356,24 @@ __global__ __launch_bounds__(256) void decode_filter_lds_kernel(DecodeArgs a) {
     }
     const uint32_t tau = a.tau[b];
     const uint8_t* __restrict__ kbase = static_cast<const uint8_t*>(a.k) + (size_t)b * a.n_k * RB;
-    // Copy lane l of instruction i moves granule ((l % 8) ^ f(r)) of row
-    // r = 8 i + l / 8 into slot 64 i + l.
+    // 128-byte rows: copy lane l of instruction i moves granule
+    // ((l % 8) ^ f(r)) of row r = 8 i + l / 8 into slot 64 i + l. Other
+    // widths: copy i moves bytes [1024 i, 1024 i + 1024) of the step (rows
+    // past the sequence read its last 16 bytes; they are masked later).
+    const size_t seq_bytes = (size_t)a.n_k * RB;
     auto issue = [&](int st) {
         const int k0 = kw0 + st * 16 * TILES;
         uint8_t* dst = ring[wave][st & 1];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int r = 8 * i + (lane >> 3);
-            const int j = (lane & 7) ^ ((r & 7) ^ ((r >> 3) & 1));
-            const uint8_t* src = kbase + (size_t)min(k0 + r, a.n_k - 1) * RB + 16 * j;
+        for (int i = 0; i < CPS; ++i) {
+            const uint8_t* src;
+            if constexpr (SW) {
+                const int r = 8 * i + (lane >> 3);
+                const int j = (lane & 7) ^ ((r & 7) ^ ((r >> 3) & 1));
+                src = kbase + (size_t)min(k0 + r, a.n_k - 1) * RB + 16 * j;
+            } else {
+                src = kbase + min((size_t)k0 * RB + 1024 * i + 16 * lane, seq_bytes - 16);
+            }
             __builtin_amdgcn_global_load_lds(src, dst + 1024 * i, 16, 0, kNontemporal);
         }
     };
@@ -376,14 +391,17 @@ __global__ __launch_bounds__(256) void decode_filter_lds_kernel(DecodeArgs a) {
         key0s[st] = k0 + 16 * sel + 4 * g;
         // step st has landed once only the copies issued after it remain
         __builtin_amdgcn_sched_barrier(0);
-        if (st + 1 < STEPS) wait_vmcnt<8>();
+        if (st + 1 < STEPS) wait_vmcnt<CPS>();
         else wait_vmcnt<0>();
         asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
         const uint8_t* buf = ring[wave][st & 1];
         Frag<DT, D> fk[TILES];
 #pragma unroll
-        for (int t = 0; t < TILES; ++t) load_sw(fk[t], buf, 16 * t + n, g);
+        for (int t = 0; t < TILES; ++t) {
+            if constexpr (SW) load_sw(fk[t], buf, 16 * t + n, g);
+            else fk[t].load(buf + (16 * t + n) * RB, g);
+        }
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the buffer may be refilled
         __builtin_amdgcn_sched_barrier(0);
         asm volatile("" ::: "memory");
@@ -605,7 +623,7 @@ hipError_t launch_d(const DecodeArgs& a, int part, hipStream_t s) {
         const int KB = 4 * SLOT;
         const long long nb = (long long)a.B * ((a.n_k + KB - 1) / KB);
         if (nb > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-        if constexpr (D * (DT == 0 ? 1 : 2) == 128)
+        if constexpr (D * (DT == 0 ? 1 : 2) <= LDS_RB_MAX)
             hipLaunchKernelGGL((decode_filter_lds_kernel<DT, D>), dim3((unsigned)nb), dim3(256), 0, s, a);
         else
             hipLaunchKernelGGL((decode_filter_kernel<DT, D>), dim3((unsigned)nb), dim3(256), 0, s, a);

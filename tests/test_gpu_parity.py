@@ -65,6 +65,11 @@ SMALL = [
              clustered=True),
     Workload("decode_chunked_bf16", "decode", 2, 1, 9000, 8999, 160, "bf16", 4096, 4),
     Workload("decode_pos_inside_row", "decode", 2, 1, 30000, 25000, 128, "fp8", 900, 16),
+    # LDS-staged decode filter at every row width it takes (16..160 bytes)
+    Workload("decode_fp8_d32_8k", "decode", 2, 1, 8192, 8191, 32, "fp8", 256, 2),
+    Workload("decode_fp8_d64_9k", "decode", 3, 1, 9000, 8999, 64, "fp8", 500, 4),
+    Workload("decode_fp8_d160_10k", "decode", 2, 1, 10001, 10000, 160, "fp8", 1000, 8),
+    Workload("decode_bf16_d32_12k", "decode", 2, 1, 12000, 11999, 32, "bf16", 600, 2),
     # a few long query rows (chunked top-k with its own histogram pass)
     Workload("chunked_prefill_long", "prefill", 2, 9, 12000, 11991, 64, "fp8", 333, 2),
 ]
