@@ -29,7 +29,8 @@ OP_TOPK, OP_ATTN, OP_FORWARD = 1, 2, 3
 HEAD_DIM = 128
 
 EXPORTS = ("dsa_workspace_size", "dsa_index_scores", "dsa_topk", "dsa_sparse_attn",
-           "dsa_forward", "dsa_forward_timed", "dsa_status_str", "dsa_last_error")
+           "dsa_forward", "dsa_forward_ragged", "dsa_forward_timed", "dsa_status_str",
+           "dsa_last_error")
 
 
 class Problem(ctypes.Structure):
@@ -65,9 +66,11 @@ def load():
             lib.dsa_topk.argtypes = [PP, P, I, I, P, P, S, P]
             lib.dsa_sparse_attn.argtypes = [PP, P, P, P, P, P, P, P, S, P]
             lib.dsa_forward.argtypes = [PP, P, P, P, P, P, P, P, P, P, S, P]
+            lib.dsa_forward_ragged.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, S, P]
             lib.dsa_forward_timed.argtypes = [PP, P, P, P, P, P, P, P, P, P, S, P, P, P]
             for f in (lib.dsa_workspace_size, lib.dsa_index_scores, lib.dsa_topk,
-                      lib.dsa_sparse_attn, lib.dsa_forward, lib.dsa_forward_timed):
+                      lib.dsa_sparse_attn, lib.dsa_forward, lib.dsa_forward_ragged,
+                      lib.dsa_forward_timed):
                 f.restype = I
             lib.dsa_status_str.argtypes = [I]
             lib.dsa_status_str.restype = ctypes.c_char_p
@@ -180,7 +183,15 @@ class Forward:
         self.device = torch.device(device)
         self.ws, self.ws_bytes = _workspace(problem, OP_FORWARD, self.device)
 
-    def __call__(self, q_idx, k_idx, Q, K, V, O, idx_out=None, lse=None):
+    def __call__(self, q_idx, k_idx, Q, K, V, O, idx_out=None, lse=None, seq_pos=None):
+        """seq_pos (int32 [B] on the device): a ragged decode batch through
+        dsa_forward_ragged (the problem has n_q = 1 and q_pos0 = 0)."""
+        if seq_pos is not None:
+            _check(load().dsa_forward_ragged(
+                ctypes.byref(self.p), _ptr(seq_pos), _ptr(q_idx), _ptr(k_idx), _ptr(Q), _ptr(K),
+                _ptr(V), _ptr(idx_out), _ptr(O), _ptr(lse), _ptr(self.ws), self.ws_bytes,
+                _stream(self.device)))
+            return
         _check(load().dsa_forward(ctypes.byref(self.p), _ptr(q_idx), _ptr(k_idx), _ptr(Q),
                                   _ptr(K), _ptr(V), _ptr(idx_out), _ptr(O), _ptr(lse),
                                   _ptr(self.ws), self.ws_bytes, _stream(self.device)))
@@ -197,9 +208,11 @@ class Forward:
         return list(ms), slabs.value
 
 
-def forward(q_idx, k_idx, Q, K, V, q_pos0, top_k, want_idx=True, want_lse=True):
+def forward(q_idx, k_idx, Q, K, V, q_pos0, top_k, want_idx=True, want_lse=True, seq_pos=None):
     """The fused chain. Returns (idx [B,n_q,top_k] int32 or None,
-    O [B,n_q,H,128] bf16, lse [B,n_q,H] float32 or None)."""
+    O [B,n_q,H,128] bf16, lse [B,n_q,H] float32 or None). With seq_pos (int32
+    [B] on the device; n_q = 1, q_pos0 = 0) the batch is ragged: the query of
+    sequence b sits at position seq_pos[b]."""
     _dev_tensor(q_idx, "q_idx", _IDX_DTYPES, 3)
     _dev_tensor(k_idx, "k_idx", (q_idx.dtype,), 3)
     _dev_tensor(Q, "Q", (torch.bfloat16,), 4)
@@ -213,5 +226,9 @@ def forward(q_idx, k_idx, Q, K, V, q_pos0, top_k, want_idx=True, want_lse=True):
     idx = torch.empty((B, n_q, top_k), dtype=torch.int32, device=dev) if want_idx else None
     O = torch.empty_like(Q)
     lse = torch.empty((B, n_q, H), dtype=torch.float32, device=dev) if want_lse else None
-    Forward(p, dev)(q_idx, k_idx, Q, K, V, O, idx, lse)
+    if seq_pos is not None:
+        _dev_tensor(seq_pos, "seq_pos", (torch.int32,), 1)
+        if seq_pos.shape[0] != B:
+            raise ValueError("seq_pos must have one entry per sequence")
+    Forward(p, dev)(q_idx, k_idx, Q, K, V, O, idx, lse, seq_pos=seq_pos)
     return idx, O, lse

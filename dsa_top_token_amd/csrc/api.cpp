@@ -223,7 +223,7 @@ struct StageTimer {
 dsa_status forward_impl(const dsa_problem* p, const void* q_idx, const void* k_idx,
                         const void* Q, const void* K, const void* V, int32_t* idx_out, void* O,
                         float* lse, void* ws, size_t ws_bytes, void* stream, StageTimer* tm,
-                        int32_t* n_slabs) {
+                        int32_t* n_slabs, const int32_t* seq_pos = nullptr) {
     dsa_status s = check_problem(p);
     if (s != DSA_OK) return s;
     if ((s = check_ptrs({q_idx, k_idx, Q, K, V, O}, "q_idx, k_idx, Q, K, V, O")) != DSA_OK)
@@ -253,6 +253,7 @@ dsa_status forward_impl(const dsa_problem* p, const void* q_idx, const void* k_i
     ia.dtype = p->idx_dtype;
     ia.scale = index_scale(p->d_idx);
     ia.write_masked = 0;  // the selection never reads past a query's position
+    ia.seq_pos = seq_pos;
     dsa::TopkArgs ta{};
     ta.scores = scores;
     ta.idx = idx;
@@ -260,6 +261,7 @@ dsa_status forward_impl(const dsa_problem* p, const void* q_idx, const void* k_i
     ta.n_k = p->n_k;
     ta.k = p->top_k;
     ta.idx_rows = p->n_q;
+    ta.seq_pos = seq_pos;
     ta.ws = w + L.topk;
     int slabs = 0;
     if (p->n_q > 1) {
@@ -318,6 +320,7 @@ dsa_status forward_impl(const dsa_problem* p, const void* q_idx, const void* k_i
             da.idx_row0 = r0;
             da.scale = index_scale(p->d_idx);
             da.fallback = scores;
+            da.seq_pos = seq_pos;
             hipError_t e = hipSuccess;
             if (tm) tm->mark(1);
             if ((e = dsa::launch_decode_select(da, ta.ws, 0, st)) != hipSuccess)
@@ -454,6 +457,25 @@ dsa_status dsa_forward(const dsa_problem* p, const void* q_idx, const void* k_id
                        void* ws, size_t ws_bytes, void* stream) {
     dsa_status s = forward_impl(p, q_idx, k_idx, Q, K, V, idx_out, O, lse, ws, ws_bytes, stream,
                                 nullptr, nullptr);
+    return s == DSA_OK ? ok() : s;
+}
+
+dsa_status dsa_forward_ragged(const dsa_problem* p, const int32_t* seq_pos, const void* q_idx,
+                              const void* k_idx, const void* Q, const void* K, const void* V,
+                              int32_t* idx_out, void* O, float* lse, void* ws, size_t ws_bytes,
+                              void* stream) {
+    dsa_status s = check_problem(p);
+    if (s != DSA_OK) return s;
+    if (!seq_pos) return fail(DSA_E_NULL, "seq_pos is NULL");
+    if (misaligned(seq_pos)) return fail(DSA_E_ALIGN, "seq_pos is not 16-byte aligned");
+    if (p->q_pos0 != 0)
+        return fail(DSA_E_SHAPE, "a ragged batch takes its positions from seq_pos (q_pos0 = %d, need 0)",
+                    p->q_pos0);
+    if (p->n_q != 1)
+        return fail(DSA_E_UNSUPPORTED, "ragged batches take one query per sequence (n_q = %d)",
+                    p->n_q);
+    s = forward_impl(p, q_idx, k_idx, Q, K, V, idx_out, O, lse, ws, ws_bytes, stream, nullptr,
+                     nullptr, seq_pos);
     return s == DSA_OK ? ok() : s;
 }
 

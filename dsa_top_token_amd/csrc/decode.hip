@@ -45,10 +45,10 @@ struct Plan {
     int n, S, ns, m;
 };
 
-__device__ __forceinline__ Plan plan_row(const DecodeArgs& a) {
+__device__ __forceinline__ Plan plan_row(const DecodeArgs& a, int b) {
     Plan p;
-    const long long pos = (long long)a.q_pos0 + a.q_row;
-    p.n = (int)min((long long)a.n_k, pos + 1);
+    const long long pos = (long long)a.q_pos0 + a.q_row + (a.seq_pos ? a.seq_pos[b] : 0);
+    p.n = (int)max(0LL, min((long long)a.n_k, pos + 1));
     // about 64 samples are expected above tau (sd ~ S sqrt(m)): the miss
     // margin (k of the expected 2k candidates) is sqrt(k / (2 S)) = 4 sd
     p.S = max(max(1, a.top_k / 32), (p.n + TH_MAX_SAMPLES - 1) / TH_MAX_SAMPLES);
@@ -107,7 +107,7 @@ __global__ __launch_bounds__(TH_NT) void decode_threshold_kernel(DecodeArgs a) {
     constexpr int RB = D * (DT == 0 ? 1 : 2);
     const int tid = threadIdx.x;
     const int b = blockIdx.x;
-    const Plan p = plan_row(a);
+    const Plan p = plan_row(a, b);
     if (p.n <= a.top_k || p.ns <= p.m) {
         if (tid == 0) a.tau[b] = 0u;  // every key is a candidate
         return;
@@ -219,7 +219,7 @@ __global__ __launch_bounds__(256) void decode_filter_kernel(DecodeArgs a) {
     const int n = lane & 15, g = lane >> 4;
     const int n_kb = (a.n_k + KB - 1) / KB;
     const int kb = blockIdx.x % n_kb, b = blockIdx.x / n_kb;
-    const Plan p = plan_row(a);
+    const Plan p = plan_row(a, b);
     const int lim = p.n;
     const uint32_t tau = a.tau[b];
     const int slot = kb * 4 + wave;
@@ -345,7 +345,7 @@ __global__ __launch_bounds__(256) void decode_filter_lds_kernel(DecodeArgs a) {
     const int n = lane & 15, g = lane >> 4;
     const int n_kb = (a.n_k + KB - 1) / KB;
     const int kb = blockIdx.x % n_kb, b = blockIdx.x / n_kb;
-    const Plan p = plan_row(a);
+    const Plan p = plan_row(a, b);
     const int lim = p.n;
     const int slot = kb * 4 + wave;
     const int n_slots = (a.n_k + SLOT - 1) / SLOT;
@@ -478,7 +478,7 @@ __global__ __launch_bounds__(SEL_NT) void decode_select_kernel(DecodeArgs a) {
     __shared__ uint32_t res[4];
     const int tid = threadIdx.x;
     const int b = blockIdx.x;
-    const Plan p = plan_row(a);
+    const Plan p = plan_row(a, b);
     const int k = a.top_k;
     int32_t* out = a.idx + ((size_t)b * a.idx_rows + a.idx_row0) * k;
     if (p.n <= k) {

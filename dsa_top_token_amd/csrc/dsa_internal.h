@@ -15,6 +15,8 @@ struct IndexArgs {
     int q_begin, q_end;
     float scale;            // fl32(d^-0.5)
     int write_masked;       // 1: write -inf past each query's position
+    const int32_t* seq_pos; // optional [B] (one query row per sequence only): each
+                            // sequence's positions are offset by seq_pos[b]
     uint32_t* hist;         // optional (one query row per sequence only):
                             // per-row digit-1 histograms of the top-k schedule
 };
@@ -26,6 +28,8 @@ struct TopkArgs {
     int32_t* idx;           // [B][idx_rows][k]
     int B, rows, n_k, k;
     long long pos_begin;
+    const int32_t* seq_pos; // optional [B]: row r of sequence b sits at
+                            // pos_begin + seq_pos[b] + r
     int idx_rows, idx_row0;
     void* ws;               // chunked schedule workspace (topk_ws_bytes)
     int hist_ready;         // 1: the indexer already built the row histograms
@@ -62,6 +66,8 @@ struct DecodeArgs {
     int idx_rows, idx_row0;
     float scale;            // fl32(d^-0.5)
     float* fallback;        // [B][n_k] score rows for rows the threshold misses
+    const int32_t* seq_pos; // optional [B]: the query of sequence b sits at
+                            // q_pos0 + seq_pos[b] + q_row
     uint32_t* tau;          // set by launch_decode_select from its workspace
     uint32_t* cnt;
     uint2* cand;

@@ -153,8 +153,8 @@ __global__ __launch_bounds__(256) void index_decode_kernel(IndexArgs a) {
     const int n_kb = (a.n_k + KB - 1) / KB;
     const int kb = blockIdx.x % n_kb, b = blockIdx.x / n_kb;
     // The one row of this sequence: query q_begin at position pos.
-    const long long pos = (long long)a.q_pos0 + a.q_begin;
-    const int lim = (int)min((long long)a.n_k, pos + 1);  // keys < lim are scored
+    const long long pos = (long long)a.q_pos0 + a.q_begin + (a.seq_pos ? a.seq_pos[b] : 0);
+    const int lim = (int)max(0LL, min((long long)a.n_k, pos + 1));  // keys < lim are scored
     const float ninf = -__builtin_inff();
     float* const out = a.scores + (size_t)b * a.n_k;
 
@@ -231,7 +231,7 @@ __global__ __launch_bounds__(256) void index_decode_kernel(IndexArgs a) {
 template <int DT, int D>
 hipError_t launch_dt_d(const IndexArgs& a, hipStream_t s) {
     const int rows = a.q_end - a.q_begin;
-    if (a.hist && rows != 1) return hipErrorInvalidValue;
+    if ((a.hist || a.seq_pos) && rows != 1) return hipErrorInvalidValue;
     if (rows == 1) {
         constexpr int TILES = 8, STEPS = 2, KB = 4 * 16 * TILES * STEPS;
         const long long nb = (long long)a.B * ((a.n_k + KB - 1) / KB);

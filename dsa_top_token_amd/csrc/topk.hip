@@ -51,8 +51,8 @@ __global__ __launch_bounds__(ROW_NT) void topk_row_kernel(TopkArgs a) {
     __shared__ uint32_t res[4];
     const unsigned rid = blockIdx.x;
     const int b = (int)(rid / (unsigned)a.rows), r = (int)(rid % (unsigned)a.rows);
-    const long long pos = a.pos_begin + r;
-    const int n = (int)min((long long)a.n_k, pos + 1);
+    const long long pos = a.pos_begin + r + (a.seq_pos ? a.seq_pos[b] : 0);
+    const int n = (int)max(0LL, min((long long)a.n_k, pos + 1));
     const float* row = a.scores + (size_t)rid * a.n_k;
     int32_t* out = a.idx + ((size_t)b * a.idx_rows + a.idx_row0 + r) * a.k;
     if (n <= a.k) {
@@ -105,7 +105,8 @@ struct MultiArgs {
 __device__ __forceinline__ void slot_info(const MultiArgs& a, int slot, int* b, int* r, int* n) {
     *b = slot / a.t.rows;
     *r = slot % a.t.rows;
-    *n = (int)min((long long)a.t.n_k, a.t.pos_begin + *r + 1);
+    const long long pos = a.t.pos_begin + *r + (a.t.seq_pos ? a.t.seq_pos[*b] : 0);
+    *n = (int)max(0LL, min((long long)a.t.n_k, pos + 1));
 }
 
 // Zero the per-row histograms (a kernel rather than a memset so the sequence

@@ -125,6 +125,24 @@ dsa_status dsa_forward(const dsa_problem* p, const void* q_idx,
                        const void* V, int32_t* idx_out, void* O, float* lse,
                        void* ws, size_t ws_bytes, void* stream);
 
+/* dsa_forward for a ragged decode batch (DSA page, sections 3.3 and 4.3, per
+ * sequence): one query per sequence (n_q = 1, and q_pos0 = 0 in *p), the
+ * query of sequence b at position seq_pos[b], seeing keys 0..seq_pos[b] of its
+ * row of n_k keys. Sequences of different lengths share the padded
+ * [B][n_k] layouts of dsa_forward; keys past a sequence's position are never
+ * read for it. seq_pos: int32 [B], device memory, 16-byte aligned; a value
+ * >= n_k acts as n_k - 1, and a value < 0 leaves the sequence's row empty
+ * (idx all -1, O = 0, lse = -inf). Results per sequence equal dsa_forward on
+ * that sequence alone with q_pos0 = seq_pos[b]. Same workspace as
+ * dsa_forward (dsa_workspace_size with DSA_OP_FORWARD). Errors: DSA_E_NULL
+ * (seq_pos NULL), DSA_E_SHAPE (q_pos0 != 0), DSA_E_UNSUPPORTED (n_q != 1),
+ * and those of dsa_forward. */
+dsa_status dsa_forward_ragged(const dsa_problem* p, const int32_t* seq_pos,
+                              const void* q_idx, const void* k_idx,
+                              const void* Q, const void* K, const void* V,
+                              int32_t* idx_out, void* O, float* lse, void* ws,
+                              size_t ws_bytes, void* stream);
+
 /* dsa_forward for profiling: the same work and results, plus the device time
  * of each stage. HIP events are recorded on `stream` around the indexer
  * kernel, the top-k kernels and the attention kernels of every row slab; the

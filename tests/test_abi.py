@@ -91,6 +91,21 @@ def test_null_and_misaligned_pointers():
                            need, None) == -4
 
 
+def test_ragged_forward_arguments():
+    lib = dsa.load()
+    dec = prob(n_q=1, n_k=64, q_pos0=0)
+    need = dsa.workspace_size(dec, dsa.OP_FORWARD)
+    args = (FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, need, None)
+    assert lib.dsa_forward_ragged(ctypes.byref(dec), None, *args) == -1
+    assert lib.dsa_forward_ragged(ctypes.byref(dec), ODD, *args) == -4
+    # positions come from seq_pos only, one query per sequence
+    assert lib.dsa_forward_ragged(ctypes.byref(prob(n_q=1, n_k=64, q_pos0=5)), FAKE, *args) == -2
+    assert lib.dsa_forward_ragged(ctypes.byref(prob(n_q=2, n_k=64)), FAKE, *args) == -3
+    # and the workspace of dsa_forward
+    assert lib.dsa_forward_ragged(ctypes.byref(dec), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                  FAKE, None, FAKE, need - 1, None) == -5
+
+
 def test_attention_workspace_only_when_split():
     # decode-sized batches split each query's keys; prefill does not
     dec = synth.WORKLOADS["decode_128k_clustered"]

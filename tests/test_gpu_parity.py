@@ -267,6 +267,46 @@ def test_prefill_equal_scores_overflow_falls_back(gpu_lib):
     assert_attn_close(O, O_ref, lse, lse_ref, "prefill equal scores")
 
 
+RAGGED = [
+    # decode select path (n_k >= 8192), positions short, at top_k, long,
+    # empty (-1) and past the row (clamped to n_k - 1)
+    (Workload("ragged_select", "decode", 7, 1, 20000, 0, 128, "fp8", 500, 4),
+     [19999, 0, 499, 500, 7000, -1, 25000]),
+    (Workload("ragged_select_clustered", "decode", 4, 1, 40000, 0, 128, "fp8", 1500, 16,
+              clustered=True), [39999, 1499, 20000, 9001]),
+    # wide bf16 rows (fragments straight from HBM)
+    (Workload("ragged_select_bf16", "decode", 3, 1, 9000, 0, 160, "bf16", 1000, 4),
+     [8999, 4000, 1200]),
+    # short rows: score row + top-k schedule
+    (Workload("ragged_topk", "decode", 4, 1, 3000, 0, 96, "fp8", 300, 8),
+     [2999, 100, 1500, 299]),
+]
+
+
+@pytest.mark.parametrize("w,pos", RAGGED, ids=lambda v: v.name if hasattr(v, "name") else "")
+def test_forward_ragged_decode(gpu_lib, w, pos):
+    # Each sequence of a ragged batch equals the oracle's forward on that
+    # sequence alone with its own query position.
+    say("ragged %s %s" % (w.name, pos))
+    x = synth.make_inputs(w, seed=13)
+    d = to_dev(x)
+    sp = torch.tensor(pos, dtype=torch.int32, device="cuda")
+    idx, O, lse = dsa.forward(d["q_idx"], d["k_idx"], d["Q"], d["K"], d["V"], 0, w.top_k,
+                              seq_pos=sp)
+    idx = idx.cpu().numpy()
+    for b, p in enumerate(pos):
+        if p < 0:
+            assert np.all(idx[b] == -1)
+            assert torch.all(O[b].float() == 0) and torch.all(torch.isneginf(lse[b]))
+            continue
+        p = min(p, w.n_k - 1)
+        sl = {k: v[b:b + 1] for k, v in x.items()}
+        i_ref, O_ref, l_ref = oracle.forward(sl["q_idx"], sl["k_idx"], sl["Q"], sl["K"],
+                                             sl["V"], p, w.top_k)
+        assert np.array_equal(idx[b:b + 1], i_ref), (w.name, b, p)
+        assert_attn_close(O[b:b + 1], O_ref, lse[b:b + 1], l_ref, "%s seq %d" % (w.name, b))
+
+
 def test_all_zero_query_selects_first_keys(gpu_lib):
     w = Workload("zeros", "prefill", 1, 600, 600, 0, 128, "fp8", 64, 2)
     x = synth.make_inputs(w, seed=6)
