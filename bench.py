@@ -45,23 +45,25 @@ def source_hash(mode, stage):
     return h.hexdigest()[:16]
 
 
-def stage_work(w, stage):
+def stage_work(w, stage, seed=0):
     """Algorithmic work of one launch of `stage` on workload w:
     (bound, amount, unit, peak)."""
     es = 1 if w.idx_dtype == "fp8" else 2
+    pairs = w.n_causal_pairs(seed)
     if stage == "indexer":
         if w.mode == "decode":
-            # stream every key's indexer row once (+ the query rows)
-            b = w.batch * w.n_k * w.d_idx * es + w.batch * w.n_q * w.d_idx * es
+            # stream the indexer row of every key in a query's range once
+            # (+ the query rows)
+            b = pairs * w.d_idx * es + w.batch * w.n_q * w.d_idx * es
             return "hbm", b / 1e9, "GB/s", PEAK["hbm"]
-        f = 2.0 * w.d_idx * w.n_causal_pairs()
+        f = 2.0 * w.d_idx * pairs
         return "mfma", f / 1e12, "TFLOP/s", PEAK[w.idx_dtype]
     if stage == "topk":
         # read each candidate score once, write the index lists
-        b = 4 * w.n_causal_pairs() + 4 * w.batch * w.n_q * w.top_k
+        b = 4 * pairs + 4 * w.batch * w.n_q * w.top_k
         return "hbm", b / 1e9, "GB/s", PEAK["hbm"]
     # attention: gather each selected K and V row once, read Q, write O
-    b = w.n_selected() * 2 * 128 * 2 + 2 * w.batch * w.n_q * w.n_heads * 128 * 2
+    b = w.n_selected(seed) * 2 * 128 * 2 + 2 * w.batch * w.n_q * w.n_heads * 128 * 2
     return "hbm", b / 1e9, "GB/s", PEAK["hbm"]
 
 
@@ -76,16 +78,23 @@ def calib_copy(nbytes=1 << 30, reps=5):
     print(json.dumps({"calib_copy_bytes": nbytes, "reps": reps}))
 
 
-def cpu_baseline(w, x, target_s=12.0):
+def cpu_baseline(w, x, target_s=12.0, seed=0):
     """Time the oracle on a bounded sample of the workload's queries."""
     import oracle
     t_probe0 = time.perf_counter()
     if w.mode == "decode":
         # one decode row per sequence: sample sequences
+        pos = w.positions(seed)
+
         def run(nseq):
-            xs = {k: v[:nseq] for k, v in x.items()}
-            oracle.forward(xs["q_idx"], xs["k_idx"], xs["Q"], xs["K"], xs["V"], w.q_pos0,
-                           w.top_k)
+            if not w.ragged:
+                xs = {k: v[:nseq] for k, v in x.items()}
+                oracle.forward(xs["q_idx"], xs["k_idx"], xs["Q"], xs["K"], xs["V"], w.q_pos0,
+                               w.top_k)
+                return nseq
+            xs = {k: v[:nseq] for k, v in x.items()}  # each sequence at its own position
+            oracle.forward(xs["q_idx"], xs["k_idx"], xs["Q"], xs["K"], xs["V"], 0, w.top_k,
+                           seq_pos=pos[:nseq])
             return nseq
         nthreads = oracle.num_threads()
         probe = min(w.batch, nthreads)
@@ -159,12 +168,15 @@ def main():
     p = dsa.make_problem(w.batch, w.n_q, w.n_k, w.q_pos0, w.d_idx, w.idx_dtype, w.top_k,
                          w.n_heads)
     fwd = dsa.Forward(p, dev)
+    # a ragged batch: each sequence's query position (device int32 [B])
+    sp = (torch.tensor(w.positions(args.seed), dtype=torch.int32, device=dev)
+          if w.ragged else None)
     O = torch.empty_like(d["Q"])
     idx = torch.empty((w.batch, w.n_q, w.top_k), dtype=torch.int32, device=dev)
     lse = torch.empty((w.batch, w.n_q, w.n_heads), dtype=torch.float32, device=dev)
 
     def step():
-        fwd(d["q_idx"], d["k_idx"], d["Q"], d["K"], d["V"], O, idx, lse)
+        fwd(d["q_idx"], d["k_idx"], d["Q"], d["K"], d["V"], O, idx, lse, seq_pos=sp)
 
     for _ in range(args.warmup):
         step()
@@ -188,11 +200,12 @@ def main():
         n_rep = max(3, args.steps)
         slabs = 1
         for _ in range(n_rep):
-            ms3, slabs = fwd.timed(d["q_idx"], d["k_idx"], d["Q"], d["K"], d["V"], O, idx, lse)
+            ms3, slabs = fwd.timed(d["q_idx"], d["k_idx"], d["Q"], d["K"], d["V"], O, idx, lse,
+                                   seq_pos=sp)
             tot = [a + b for a, b in zip(tot, ms3)]
         stages = {n: t / n_rep for n, t in zip(names, tot)}
         dom = max(stages, key=stages.get)
-        bound, amount, unit, peak = stage_work(w, dom)
+        bound, amount, unit, peak = stage_work(w, dom, args.seed)
         achieved = amount / (stages[dom] / 1e3)
         traffic = None
         if os.path.exists(TRAFFIC_FILE):
@@ -205,7 +218,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, x)
+        cpu = cpu_baseline(w, x, seed=args.seed)
 
     out = {
         "metric": "queries/sec (indexer+top-k+sparse attn) at 128K ctx; % of fp8 MFMA / HBM peak",
@@ -228,6 +241,10 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
     }
+    if w.ragged:
+        pos = w.positions(args.seed)
+        out["config"]["ragged"] = {"positions": "seeded, uniform in [n_k/8, n_k-1]",
+                                   "mean_len": round(sum(p + 1 for p in pos) / len(pos), 1)}
     print(json.dumps(out))
 
 

@@ -29,8 +29,8 @@ OP_TOPK, OP_ATTN, OP_FORWARD = 1, 2, 3
 HEAD_DIM = 128
 
 EXPORTS = ("dsa_workspace_size", "dsa_index_scores", "dsa_topk", "dsa_sparse_attn",
-           "dsa_forward", "dsa_forward_ragged", "dsa_forward_timed", "dsa_status_str",
-           "dsa_last_error")
+           "dsa_forward", "dsa_forward_ragged", "dsa_forward_timed",
+           "dsa_forward_ragged_timed", "dsa_status_str", "dsa_last_error")
 
 
 class Problem(ctypes.Structure):
@@ -68,9 +68,11 @@ def load():
             lib.dsa_forward.argtypes = [PP, P, P, P, P, P, P, P, P, P, S, P]
             lib.dsa_forward_ragged.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, S, P]
             lib.dsa_forward_timed.argtypes = [PP, P, P, P, P, P, P, P, P, P, S, P, P, P]
+            lib.dsa_forward_ragged_timed.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, S, P, P,
+                                                     P]
             for f in (lib.dsa_workspace_size, lib.dsa_index_scores, lib.dsa_topk,
                       lib.dsa_sparse_attn, lib.dsa_forward, lib.dsa_forward_ragged,
-                      lib.dsa_forward_timed):
+                      lib.dsa_forward_timed, lib.dsa_forward_ragged_timed):
                 f.restype = I
             lib.dsa_status_str.argtypes = [I]
             lib.dsa_status_str.restype = ctypes.c_char_p
@@ -196,11 +198,18 @@ class Forward:
                                   _ptr(K), _ptr(V), _ptr(idx_out), _ptr(O), _ptr(lse),
                                   _ptr(self.ws), self.ws_bytes, _stream(self.device)))
 
-    def timed(self, q_idx, k_idx, Q, K, V, O, idx_out=None, lse=None):
-        """Run once through dsa_forward_timed; returns ([indexer, top-k,
-        attention] milliseconds, number of row slabs). Blocks until done."""
+    def timed(self, q_idx, k_idx, Q, K, V, O, idx_out=None, lse=None, seq_pos=None):
+        """Run once through dsa_forward_timed (dsa_forward_ragged_timed with
+        seq_pos); returns ([indexer, top-k, attention] milliseconds, number of
+        row slabs). Blocks until done."""
         ms = (ctypes.c_float * 3)()
         slabs = ctypes.c_int32(0)
+        if seq_pos is not None:
+            _check(load().dsa_forward_ragged_timed(
+                ctypes.byref(self.p), _ptr(seq_pos), _ptr(q_idx), _ptr(k_idx), _ptr(Q), _ptr(K),
+                _ptr(V), _ptr(idx_out), _ptr(O), _ptr(lse), _ptr(self.ws), self.ws_bytes,
+                _stream(self.device), ms, ctypes.byref(slabs)))
+            return list(ms), slabs.value
         _check(load().dsa_forward_timed(ctypes.byref(self.p), _ptr(q_idx), _ptr(k_idx),
                                         _ptr(Q), _ptr(K), _ptr(V), _ptr(idx_out), _ptr(O),
                                         _ptr(lse), _ptr(self.ws), self.ws_bytes,

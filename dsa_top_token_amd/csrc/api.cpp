@@ -360,6 +360,22 @@ dsa_status forward_impl(const dsa_problem* p, const void* q_idx, const void* k_i
     return DSA_OK;
 }
 
+// Arguments a ragged batch adds to those of dsa_forward.
+dsa_status check_ragged(const dsa_problem* p, const int32_t* seq_pos) {
+    dsa_status s = check_problem(p);
+    if (s != DSA_OK) return s;
+    if (!seq_pos) return fail(DSA_E_NULL, "seq_pos is NULL");
+    if (misaligned(seq_pos)) return fail(DSA_E_ALIGN, "seq_pos is not 16-byte aligned");
+    if (p->q_pos0 != 0)
+        return fail(DSA_E_SHAPE,
+                    "a ragged batch takes its positions from seq_pos (q_pos0 = %d, need 0)",
+                    p->q_pos0);
+    if (p->n_q != 1)
+        return fail(DSA_E_UNSUPPORTED, "ragged batches take one query per sequence (n_q = %d)",
+                    p->n_q);
+    return DSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -464,19 +480,30 @@ dsa_status dsa_forward_ragged(const dsa_problem* p, const int32_t* seq_pos, cons
                               const void* k_idx, const void* Q, const void* K, const void* V,
                               int32_t* idx_out, void* O, float* lse, void* ws, size_t ws_bytes,
                               void* stream) {
-    dsa_status s = check_problem(p);
+    dsa_status s = check_ragged(p, seq_pos);
     if (s != DSA_OK) return s;
-    if (!seq_pos) return fail(DSA_E_NULL, "seq_pos is NULL");
-    if (misaligned(seq_pos)) return fail(DSA_E_ALIGN, "seq_pos is not 16-byte aligned");
-    if (p->q_pos0 != 0)
-        return fail(DSA_E_SHAPE, "a ragged batch takes its positions from seq_pos (q_pos0 = %d, need 0)",
-                    p->q_pos0);
-    if (p->n_q != 1)
-        return fail(DSA_E_UNSUPPORTED, "ragged batches take one query per sequence (n_q = %d)",
-                    p->n_q);
     s = forward_impl(p, q_idx, k_idx, Q, K, V, idx_out, O, lse, ws, ws_bytes, stream, nullptr,
                      nullptr, seq_pos);
     return s == DSA_OK ? ok() : s;
+}
+
+dsa_status dsa_forward_ragged_timed(const dsa_problem* p, const int32_t* seq_pos,
+                                    const void* q_idx, const void* k_idx, const void* Q,
+                                    const void* K, const void* V, int32_t* idx_out, void* O,
+                                    float* lse, void* ws, size_t ws_bytes, void* stream,
+                                    float* stage_ms, int32_t* n_slabs) {
+    if (!stage_ms) return fail(DSA_E_NULL, "stage_ms is NULL");
+    dsa_status s = check_ragged(p, seq_pos);
+    if (s != DSA_OK) return s;
+    StageTimer tm;
+    tm.st = static_cast<hipStream_t>(stream);
+    for (int i = 0; i < 3; ++i) stage_ms[i] = 0.f;
+    s = forward_impl(p, q_idx, k_idx, Q, K, V, idx_out, O, lse, ws, ws_bytes, stream, &tm,
+                     n_slabs, seq_pos);
+    hipError_t e = tm.finish(stage_ms);
+    if (s != DSA_OK) return s;
+    if (e != hipSuccess) return hip_fail(e, "stage timing events");
+    return ok();
 }
 
 dsa_status dsa_forward_timed(const dsa_problem* p, const void* q_idx, const void* k_idx,

@@ -16,7 +16,9 @@ Recipe (every tensor has its own CPU generator seeded with seed*1000 + tid):
     64 integer centroids per sequence in [-4, 4], integer noise in {-1, 0, 1},
     so values lie in [-5, 5] (still exact in e4m3fn);
   * Q [B, n_q, H, 128], K and V [B, n_k, 128]: N(0, 1) drawn in float32 and
-    rounded to bfloat16.
+    rounded to bfloat16;
+  * ragged decode batches: each sequence's query position uniform in
+    [n_k / 8, n_k - 1] (rows share the padded [B, n_k] layout).
 """
 from __future__ import annotations
 
@@ -26,7 +28,7 @@ from typing import Dict, Optional
 import torch
 
 TID = {"q_idx": 1, "k_idx": 2, "Q": 3, "K": 4, "V": 5,
-       "centroids": 6, "assign": 7, "noise": 8}
+       "centroids": 6, "assign": 7, "noise": 8, "positions": 9}
 
 HEAD_DIM = 128
 N_CENTROIDS = 64
@@ -45,6 +47,7 @@ class Workload:
     top_k: int
     n_heads: int
     clustered: bool = False
+    ragged: bool = False  # decode only: per-sequence query positions (positions())
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -53,17 +56,26 @@ class Workload:
     def torch_idx_dtype(self):
         return torch.float8_e4m3fn if self.idx_dtype == "fp8" else torch.bfloat16
 
-    def n_selected(self) -> int:
+    def positions(self, seed: int = 0):
+        """Position of query 0 of every sequence: q_pos0, or for a ragged
+        batch one seeded draw per sequence, uniform in [n_k / 8, n_k - 1]."""
+        if not self.ragged:
+            return [self.q_pos0] * self.batch
+        g = _gen(seed, "positions", "cpu")
+        return torch.randint(self.n_k // 8, self.n_k, (self.batch,), generator=g).tolist()
+
+    def n_selected(self, seed: int = 0) -> int:
         """Sum over queries of min(top_k, pos + 1): rows attended in total."""
         tot = 0
-        for i in range(self.n_q):
-            tot += min(self.top_k, self.q_pos0 + i + 1)
-        return tot * self.batch
+        for p0 in self.positions(seed):
+            for i in range(self.n_q):
+                tot += min(self.top_k, p0 + i + 1)
+        return tot
 
-    def n_causal_pairs(self) -> int:
+    def n_causal_pairs(self, seed: int = 0) -> int:
         """Sum over queries of pos + 1: indexer scores computed in total."""
-        a, n = self.q_pos0 + 1, self.n_q
-        return self.batch * (n * a + n * (n - 1) // 2)
+        n = self.n_q
+        return sum(n * (p0 + 1) + n * (n - 1) // 2 for p0 in self.positions(seed))
 
 
 def _prefill(name, L, d, dt, k, H, **kw):
@@ -86,6 +98,9 @@ WORKLOADS: Dict[str, Workload] = {
                 clustered=True),
     ]
 }
+# A ragged 128K decode batch (sequence lengths spread over the context).
+WORKLOADS["decode_128k_ragged"] = Workload("decode_128k_ragged", "decode", 64, 1, 131072, 0,
+                                           128, "fp8", 2048, 16, ragged=True)
 
 
 def _gen(seed: int, tid: str, device) -> torch.Generator:

@@ -143,6 +143,16 @@ dsa_status dsa_forward_ragged(const dsa_problem* p, const int32_t* seq_pos,
                               int32_t* idx_out, void* O, float* lse, void* ws,
                               size_t ws_bytes, void* stream);
 
+/* dsa_forward_ragged for profiling: the same work and results, plus the
+ * device time of each stage, as dsa_forward_timed reports it (blocks until
+ * the stream has finished; stage_ms must not be NULL). */
+dsa_status dsa_forward_ragged_timed(const dsa_problem* p, const int32_t* seq_pos,
+                                    const void* q_idx, const void* k_idx,
+                                    const void* Q, const void* K, const void* V,
+                                    int32_t* idx_out, void* O, float* lse,
+                                    void* ws, size_t ws_bytes, void* stream,
+                                    float* stage_ms, int32_t* n_slabs);
+
 /* dsa_forward for profiling: the same work and results, plus the device time
  * of each stage. HIP events are recorded on `stream` around the indexer
  * kernel, the top-k kernels and the attention kernels of every row slab; the

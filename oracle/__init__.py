@@ -50,10 +50,12 @@ def _load():
             lib.oracle_topk.argtypes = [I, I, I, I, I, P, P]
             lib.oracle_sparse_attn.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P]
             lib.oracle_forward.argtypes = [I] * 9 + [P] * 5 + [I, I, P, P, P]
+            lib.oracle_forward_seqpos.argtypes = [I, I, I, P] + [I] * 5 + [P] * 5 + [I, I, P,
+                                                                                  P, P]
             lib.oracle_num_threads.argtypes = []
             for f in (lib.oracle_index_scores, lib.oracle_topk,
                       lib.oracle_sparse_attn, lib.oracle_forward,
-                      lib.oracle_num_threads):
+                      lib.oracle_forward_seqpos, lib.oracle_num_threads):
                 f.restype = I
             _lib = lib
     return _lib
@@ -139,8 +141,10 @@ def sparse_attn(Q, K, V, idx, want_lse: bool = True):
 
 
 def forward(q_idx, k_idx, Q, K, V, q_pos0: int, k: int, q_begin: int = 0,
-            q_end=None, dtype=None):
+            q_end=None, dtype=None, seq_pos=None):
     """All three stages for query rows [q_begin, q_end) of every sequence.
+    With seq_pos (one int per sequence) query i of sequence b sits at
+    seq_pos[b] + i instead of q_pos0 + i.
 
     Returns (idx [B, rows, k] int32, O [B, rows, H, D] float32,
     lse [B, rows, H] float32)."""
@@ -154,6 +158,14 @@ def forward(q_idx, k_idx, Q, K, V, q_pos0: int, k: int, q_begin: int = 0,
     idx = np.empty((B, rows, k), np.int32)
     O = np.empty((B, rows, H, D), np.float32)
     lse = np.empty((B, rows, H), np.float32)
+    if seq_pos is not None:
+        sp = np.ascontiguousarray(np.asarray(seq_pos, np.int32).reshape(B))
+        rc = _load().oracle_forward_seqpos(B, n_q, n_k, _ptr(sp), d,
+                                           _dtype_code(q_idx, dtype), k, H, D, _ptr(qi),
+                                           _ptr(ki), _ptr(q), _ptr(kk), _ptr(vv), q_begin,
+                                           q_end, _ptr(idx), _ptr(O), _ptr(lse))
+        assert rc == 0, rc
+        return idx, O, lse
     rc = _load().oracle_forward(B, n_q, n_k, q_pos0, d, _dtype_code(q_idx, dtype),
                                 k, H, D, _ptr(qi), _ptr(ki), _ptr(q), _ptr(kk),
                                 _ptr(vv), q_begin, q_end, _ptr(idx), _ptr(O),

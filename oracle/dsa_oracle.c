@@ -235,10 +235,10 @@ int oracle_sparse_attn(int B, int n_q, int n_k, int H, int D, int k,
  * the full score matrix. Only query rows [q_begin, q_end) of each sequence are
  * computed; idx/O/lse are laid out [B][q_end-q_begin][...]. idx and lse may be
  * NULL. */
-int oracle_forward(int B, int n_q, int n_k, int q_pos0, int d, int dtype, int k,
-                   int H, int D, const void* q_idx, const void* k_idx,
-                   const uint16_t* Q, const uint16_t* K, const uint16_t* V,
-                   int q_begin, int q_end, int32_t* idx, float* O, float* lse) {
+static int forward_rows(int B, int n_q, int n_k, int q_pos0, const int32_t* seq_pos, int d,
+                        int dtype, int k, int H, int D, const void* q_idx, const void* k_idx,
+                        const uint16_t* Q, const uint16_t* K, const uint16_t* V,
+                        int q_begin, int q_end, int32_t* idx, float* O, float* lse) {
     if (B < 0 || n_q < 0 || n_k < 0 || d <= 0 || k < 1 || H < 1 || D < 1 ||
         q_begin < 0 || q_end > n_q || q_begin > q_end ||
         (dtype != ORACLE_FP8_E4M3FN && dtype != ORACLE_BF16))
@@ -263,7 +263,7 @@ int oracle_forward(int B, int n_q, int n_k, int q_pos0, int d, int dtype, int k,
         for (long t = 0; t < total; ++t) {
             if (!ok) continue;
             int b = (int)(t / rows), i = q_begin + (int)(t % rows);
-            long pos = (long)q_pos0 + i;
+            long pos = (long)(seq_pos ? seq_pos[b] : q_pos0) + i;
             size_t qoff = ((size_t)b * n_q + i) * d;
             for (int j = 0; j < n_k; ++j)
                 srow[j] = j > pos ? -INFINITY
@@ -278,6 +278,27 @@ int oracle_forward(int B, int n_q, int n_k, int q_pos0, int d, int dtype, int k,
         free(srow); free(buf); free(sel); free(z); free(acc);
     }
     return fail ? -2 : 0;
+}
+
+int oracle_forward(int B, int n_q, int n_k, int q_pos0, int d, int dtype, int k,
+                   int H, int D, const void* q_idx, const void* k_idx,
+                   const uint16_t* Q, const uint16_t* K, const uint16_t* V,
+                   int q_begin, int q_end, int32_t* idx, float* O, float* lse) {
+    return forward_rows(B, n_q, n_k, q_pos0, NULL, d, dtype, k, H, D, q_idx, k_idx, Q, K, V,
+                        q_begin, q_end, idx, O, lse);
+}
+
+/* oracle_forward for a batch whose sequences sit at different positions:
+ * query i of sequence b is at seq_pos[b] + i (sequences of different lengths
+ * in one padded [B][n_k] layout; keys past a query's position are not
+ * candidates). */
+int oracle_forward_seqpos(int B, int n_q, int n_k, const int32_t* seq_pos, int d, int dtype,
+                          int k, int H, int D, const void* q_idx, const void* k_idx,
+                          const uint16_t* Q, const uint16_t* K, const uint16_t* V,
+                          int q_begin, int q_end, int32_t* idx, float* O, float* lse) {
+    if (!seq_pos) return -1;
+    return forward_rows(B, n_q, n_k, 0, seq_pos, d, dtype, k, H, D, q_idx, k_idx, Q, K, V,
+                        q_begin, q_end, idx, O, lse);
 }
 
 /* Threads an OpenMP parallel region of this library runs with. */

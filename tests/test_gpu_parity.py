@@ -391,6 +391,30 @@ def test_full_decode_128k_clustered(gpu_lib):
     run_full(w, [(0, 1)])
 
 
+def test_full_decode_128k_ragged(gpu_lib):
+    # The benchmark's ragged batch: every fourth sequence against the oracle
+    # at its own position (one decode query each), properties on all.
+    w = synth.WORKLOADS["decode_128k_ragged"]
+    pos = w.positions(0)
+    say("full-size %s: generating inputs" % w.name)
+    x = synth.make_inputs(w, seed=0)
+    d = to_dev(x)
+    sp = torch.tensor(pos, dtype=torch.int32, device="cuda")
+    say("full-size %s: GPU forward" % w.name)
+    idx, O, lse = dsa.forward(d["q_idx"], d["k_idx"], d["Q"], d["K"], d["V"], 0, w.top_k,
+                              seq_pos=sp)
+    torch.cuda.synchronize()
+    for b in range(w.batch):
+        check_selection_properties(idx[b:b + 1], pos[b], w.top_k)
+    for b in range(0, w.batch, 4):
+        say("full-size %s: oracle sequence %d (position %d)" % (w.name, b, pos[b]))
+        sl = {k: v[b:b + 1] for k, v in x.items()}
+        i_ref, O_ref, l_ref = oracle.forward(sl["q_idx"], sl["k_idx"], sl["Q"], sl["K"],
+                                             sl["V"], pos[b], w.top_k)
+        assert np.array_equal(idx[b:b + 1].cpu().numpy(), i_ref), (b, pos[b])
+        assert_attn_close(O[b:b + 1], O_ref, lse[b:b + 1], l_ref, "ragged seq %d" % b)
+
+
 def prefill_samples(L, k):
     g = np.random.default_rng(L)
     rows = [(0, 3), (k - 3, k + 3), (2 * k - 1, 2 * k + 1), (L - 4, L)]

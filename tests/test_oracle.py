@@ -306,6 +306,32 @@ def test_forward_is_the_three_stages(name):
     check_topk_invariants(s, idx, w.q_pos0 + qb, w.top_k)
 
 
+def test_forward_seq_positions_are_per_sequence_calls():
+    # A batch whose sequences sit at different positions equals one call per
+    # sequence at its own q_pos0 (index scores, selection and attention all
+    # see only the keys up to that sequence's position).
+    w = synth.WORKLOADS["decode_32k"].replace(batch=4, n_k=600, q_pos0=0, top_k=40, n_heads=2)
+    x = synth.make_inputs(w, seed=3)
+    pos = [599, 10, 39, 300]
+    idx, O, lse = oracle.forward(x["q_idx"], x["k_idx"], x["Q"], x["K"], x["V"], 0, w.top_k,
+                                 seq_pos=pos)
+    for b, p in enumerate(pos):
+        sl = {k: v[b:b + 1] for k, v in x.items()}
+        i1, O1, l1 = oracle.forward(sl["q_idx"], sl["k_idx"], sl["Q"], sl["K"], sl["V"], p,
+                                    w.top_k)
+        assert np.array_equal(idx[b:b + 1], i1)
+        assert np.array_equal(O[b:b + 1], O1) and np.array_equal(lse[b:b + 1], l1)
+        m = min(w.top_k, p + 1)
+        assert np.all((idx[b, 0, :m] >= 0) & (idx[b, 0, :m] <= p)) and np.all(idx[b, 0, m:] == -1)
+    # the ragged workload's positions: seeded, inside [n_k / 8, n_k - 1]
+    r = synth.WORKLOADS["decode_128k_ragged"]
+    p0 = r.positions(0)
+    assert p0 == r.positions(0) and len(p0) == r.batch
+    assert min(p0) >= r.n_k // 8 and max(p0) <= r.n_k - 1
+    assert r.n_causal_pairs() == sum(p + 1 for p in p0)
+    assert r.n_selected() == sum(min(r.top_k, p + 1) for p in p0)
+
+
 def test_clustered_generator_range_and_ties():
     w = synth.WORKLOADS["decode_128k_clustered"].replace(batch=2, n_k=4096)
     x = synth.make_inputs(w, parts=("q_idx", "k_idx"))
