@@ -29,14 +29,21 @@ OP_TOPK, OP_ATTN, OP_FORWARD = 1, 2, 3
 HEAD_DIM = 128
 
 EXPORTS = ("dsa_workspace_size", "dsa_index_scores", "dsa_topk", "dsa_sparse_attn",
-           "dsa_forward", "dsa_forward_ragged", "dsa_forward_timed",
-           "dsa_forward_ragged_timed", "dsa_status_str", "dsa_last_error")
+           "dsa_forward", "dsa_forward_ragged", "dsa_forward_paged", "dsa_forward_timed",
+           "dsa_forward_ragged_timed", "dsa_forward_paged_timed", "dsa_status_str",
+           "dsa_last_error")
 
 
 class Problem(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("batch", "n_q", "n_k", "q_pos0", "d_idx", "idx_dtype", "top_k",
                  "n_heads", "head_dim")]
+
+
+class Pages(ctypes.Structure):
+    """dsa_pages: a paged key layout (block table on the device)."""
+    _fields_ = [("block_table", ctypes.c_void_p), ("page_size", ctypes.c_int32),
+                ("pages_per_seq", ctypes.c_int32), ("n_pages", ctypes.c_int32)]
 
 
 class DSAError(RuntimeError):
@@ -70,9 +77,14 @@ def load():
             lib.dsa_forward_timed.argtypes = [PP, P, P, P, P, P, P, P, P, P, S, P, P, P]
             lib.dsa_forward_ragged_timed.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, S, P, P,
                                                      P]
+            PG = ctypes.POINTER(Pages)
+            lib.dsa_forward_paged.argtypes = [PP, P, PG, P, P, P, P, P, P, P, P, P, S, P]
+            lib.dsa_forward_paged_timed.argtypes = [PP, P, PG, P, P, P, P, P, P, P, P, P, S, P,
+                                                    P, P]
             for f in (lib.dsa_workspace_size, lib.dsa_index_scores, lib.dsa_topk,
                       lib.dsa_sparse_attn, lib.dsa_forward, lib.dsa_forward_ragged,
-                      lib.dsa_forward_timed, lib.dsa_forward_ragged_timed):
+                      lib.dsa_forward_paged, lib.dsa_forward_timed,
+                      lib.dsa_forward_ragged_timed, lib.dsa_forward_paged_timed):
                 f.restype = I
             lib.dsa_status_str.argtypes = [I]
             lib.dsa_status_str.restype = ctypes.c_char_p
@@ -185,9 +197,18 @@ class Forward:
         self.device = torch.device(device)
         self.ws, self.ws_bytes = _workspace(problem, OP_FORWARD, self.device)
 
-    def __call__(self, q_idx, k_idx, Q, K, V, O, idx_out=None, lse=None, seq_pos=None):
+    def __call__(self, q_idx, k_idx, Q, K, V, O, idx_out=None, lse=None, seq_pos=None,
+                 pages=None):
         """seq_pos (int32 [B] on the device): a ragged decode batch through
-        dsa_forward_ragged (the problem has n_q = 1 and q_pos0 = 0)."""
+        dsa_forward_ragged (the problem has n_q = 1 and q_pos0 = 0); with
+        pages (a Pages), k_idx, K and V are the page pools
+        (dsa_forward_paged)."""
+        if pages is not None:
+            _check(load().dsa_forward_paged(
+                ctypes.byref(self.p), _ptr(seq_pos), ctypes.byref(pages), _ptr(q_idx),
+                _ptr(k_idx), _ptr(Q), _ptr(K), _ptr(V), _ptr(idx_out), _ptr(O), _ptr(lse),
+                _ptr(self.ws), self.ws_bytes, _stream(self.device)))
+            return
         if seq_pos is not None:
             _check(load().dsa_forward_ragged(
                 ctypes.byref(self.p), _ptr(seq_pos), _ptr(q_idx), _ptr(k_idx), _ptr(Q), _ptr(K),
@@ -198,12 +219,20 @@ class Forward:
                                   _ptr(K), _ptr(V), _ptr(idx_out), _ptr(O), _ptr(lse),
                                   _ptr(self.ws), self.ws_bytes, _stream(self.device)))
 
-    def timed(self, q_idx, k_idx, Q, K, V, O, idx_out=None, lse=None, seq_pos=None):
+    def timed(self, q_idx, k_idx, Q, K, V, O, idx_out=None, lse=None, seq_pos=None,
+              pages=None):
         """Run once through dsa_forward_timed (dsa_forward_ragged_timed with
-        seq_pos); returns ([indexer, top-k, attention] milliseconds, number of
-        row slabs). Blocks until done."""
+        seq_pos, dsa_forward_paged_timed with pages); returns ([indexer,
+        top-k, attention] milliseconds, number of row slabs). Blocks until
+        done."""
         ms = (ctypes.c_float * 3)()
         slabs = ctypes.c_int32(0)
+        if pages is not None:
+            _check(load().dsa_forward_paged_timed(
+                ctypes.byref(self.p), _ptr(seq_pos), ctypes.byref(pages), _ptr(q_idx),
+                _ptr(k_idx), _ptr(Q), _ptr(K), _ptr(V), _ptr(idx_out), _ptr(O), _ptr(lse),
+                _ptr(self.ws), self.ws_bytes, _stream(self.device), ms, ctypes.byref(slabs)))
+            return list(ms), slabs.value
         if seq_pos is not None:
             _check(load().dsa_forward_ragged_timed(
                 ctypes.byref(self.p), _ptr(seq_pos), _ptr(q_idx), _ptr(k_idx), _ptr(Q), _ptr(K),
@@ -240,4 +269,39 @@ def forward(q_idx, k_idx, Q, K, V, q_pos0, top_k, want_idx=True, want_lse=True, 
         if seq_pos.shape[0] != B:
             raise ValueError("seq_pos must have one entry per sequence")
     Forward(p, dev)(q_idx, k_idx, Q, K, V, O, idx, lse, seq_pos=seq_pos)
+    return idx, O, lse
+
+
+def make_pages(block_table, page_size, n_pages) -> Pages:
+    """dsa_pages for a block table (int32 [B, pages_per_seq] on the device)."""
+    _dev_tensor(block_table, "block_table", (torch.int32,), 2)
+    return Pages(block_table.data_ptr(), page_size, block_table.shape[1], n_pages)
+
+
+def forward_paged(q_idx, k_pool, Q, K_pool, V_pool, block_table, page_size, seq_pos, top_k,
+                  want_idx=True, want_lse=True):
+    """The fused chain over a paged layout (dsa_forward_paged): one query per
+    sequence at position seq_pos[b]; k_pool [n_pages, page_size, d_idx], K_pool
+    and V_pool [n_pages, page_size, 128]; block_table int32 [B, pages_per_seq].
+    Returns (idx with logical key indices, O, lse) as forward()."""
+    _dev_tensor(q_idx, "q_idx", _IDX_DTYPES, 3)
+    _dev_tensor(k_pool, "k_pool", (q_idx.dtype,), 3)
+    _dev_tensor(Q, "Q", (torch.bfloat16,), 4)
+    _dev_tensor(K_pool, "K_pool", (torch.bfloat16,), 3)
+    _dev_tensor(V_pool, "V_pool", (torch.bfloat16,), 3)
+    _dev_tensor(seq_pos, "seq_pos", (torch.int32,), 1)
+    B, n_q, d = q_idx.shape
+    n_pages = k_pool.shape[0]
+    if k_pool.shape[1] != page_size or K_pool.shape[:2] != (n_pages, page_size) or \
+            V_pool.shape != K_pool.shape:
+        raise ValueError("pools must be [n_pages, page_size, ...] alike")
+    pages = make_pages(block_table, page_size, n_pages)
+    n_k = block_table.shape[1] * page_size
+    H = Q.shape[2]
+    p = make_problem(B, n_q, n_k, 0, d, q_idx.dtype, top_k, H, Q.shape[3])
+    dev = Q.device
+    idx = torch.empty((B, n_q, top_k), dtype=torch.int32, device=dev) if want_idx else None
+    O = torch.empty_like(Q)
+    lse = torch.empty((B, n_q, H), dtype=torch.float32, device=dev) if want_lse else None
+    Forward(p, dev)(q_idx, k_pool, Q, K_pool, V_pool, O, idx, lse, seq_pos=seq_pos, pages=pages)
     return idx, O, lse

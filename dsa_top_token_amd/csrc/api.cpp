@@ -130,7 +130,7 @@ int prefill_slab_rows(const dsa_problem* p) {
 }
 
 struct ForwardLayout {
-    size_t scores, idx, topk, part, total;
+    size_t scores, idx, topk, part, prow, total;
 };
 
 ForwardLayout forward_layout(const dsa_problem* p) {
@@ -167,7 +167,9 @@ ForwardLayout forward_layout(const dsa_problem* p) {
         tb = db > tb ? db : tb;
     }
     L.part = L.topk + tb;
-    L.total = L.part + attn_ws_bytes(p);
+    // pool rows of the selection, for a paged layout's attention
+    L.prow = L.part + align_up(attn_ws_bytes(p));
+    L.total = L.prow + ib;
     return L;
 }
 
@@ -178,6 +180,8 @@ dsa_status hip_fail(hipError_t e, const char* what) {
 dsa::AttnArgs attn_args(const dsa_problem* p, const void* Q, const void* K, const void* V,
                         const int32_t* idx, void* O, float* lse, void* part) {
     dsa::AttnArgs a{};
+    a.kv_bstride = p->n_k;
+    a.kv_rows = p->n_k;
     a.Q = static_cast<const uint16_t*>(Q);
     a.K = static_cast<const uint16_t*>(K);
     a.V = static_cast<const uint16_t*>(V);
@@ -223,7 +227,8 @@ struct StageTimer {
 dsa_status forward_impl(const dsa_problem* p, const void* q_idx, const void* k_idx,
                         const void* Q, const void* K, const void* V, int32_t* idx_out, void* O,
                         float* lse, void* ws, size_t ws_bytes, void* stream, StageTimer* tm,
-                        int32_t* n_slabs, const int32_t* seq_pos = nullptr) {
+                        int32_t* n_slabs, const int32_t* seq_pos = nullptr,
+                        const dsa::KeyPages* pages = nullptr) {
     dsa_status s = check_problem(p);
     if (s != DSA_OK) return s;
     if ((s = check_ptrs({q_idx, k_idx, Q, K, V, O}, "q_idx, k_idx, Q, K, V, O")) != DSA_OK)
@@ -254,6 +259,7 @@ dsa_status forward_impl(const dsa_problem* p, const void* q_idx, const void* k_i
     ia.scale = index_scale(p->d_idx);
     ia.write_masked = 0;  // the selection never reads past a query's position
     ia.seq_pos = seq_pos;
+    if (pages) ia.pages = *pages;
     dsa::TopkArgs ta{};
     ta.scores = scores;
     ta.idx = idx;
@@ -321,6 +327,7 @@ dsa_status forward_impl(const dsa_problem* p, const void* q_idx, const void* k_i
             da.scale = index_scale(p->d_idx);
             da.fallback = scores;
             da.seq_pos = seq_pos;
+            if (pages) da.pages = *pages;
             hipError_t e = hipSuccess;
             if (tm) tm->mark(1);
             if ((e = dsa::launch_decode_select(da, ta.ws, 0, st)) != hipSuccess)
@@ -351,6 +358,16 @@ dsa_status forward_impl(const dsa_problem* p, const void* q_idx, const void* k_i
     }
     if (tm) tm->mark(2);
     dsa::AttnArgs aa = attn_args(p, Q, K, V, idx, O, lse, w + L.part);
+    if (pages) {
+        // the attention reads pool rows: translate the selection
+        int32_t* prow = reinterpret_cast<int32_t*>(w + L.prow);
+        hipError_t e = dsa::launch_page_rows(idx, prow, p->batch, p->n_q * p->top_k, p->n_k,
+                                             *pages, st);
+        if (e != hipSuccess) return hip_fail(e, "page rows launch");
+        aa.idx = prow;
+        aa.kv_bstride = 0;
+        aa.kv_rows = pages->n_pages * pages->page;
+    }
     if (p->n_q > 1 && dsa::attn_ranged_applies(p->batch, p->n_q, p->n_k))
         dsa::attn_set_ranged(aa, p->q_pos0, w + L.part);  // idx rows are sorted and causal
     hipError_t e = dsa::launch_sparse_attn(aa, st);
@@ -373,6 +390,31 @@ dsa_status check_ragged(const dsa_problem* p, const int32_t* seq_pos) {
     if (p->n_q != 1)
         return fail(DSA_E_UNSUPPORTED, "ragged batches take one query per sequence (n_q = %d)",
                     p->n_q);
+    return DSA_OK;
+}
+
+// A paged layout's description, checked and copied into kp.
+dsa_status check_paged(const dsa_problem* p, const int32_t* seq_pos, const dsa_pages* pg,
+                       dsa::KeyPages* kp) {
+    dsa_status s = check_ragged(p, seq_pos);
+    if (s != DSA_OK) return s;
+    if (!pg || !pg->block_table) return fail(DSA_E_NULL, "pages or pages->block_table is NULL");
+    if (misaligned(pg->block_table))
+        return fail(DSA_E_ALIGN, "pages->block_table is not 16-byte aligned");
+    if (pg->page_size < 256 || pg->page_size % 256 != 0)
+        return fail(DSA_E_SHAPE, "page_size = %d is not a positive multiple of 256",
+                    pg->page_size);
+    if (pg->pages_per_seq < 1 || (long long)pg->pages_per_seq * pg->page_size != p->n_k)
+        return fail(DSA_E_SHAPE, "pages_per_seq * page_size must equal n_k (%d * %d != %d)",
+                    pg->pages_per_seq, pg->page_size, p->n_k);
+    // attention rows are addressed with 32-bit byte offsets into the K/V pools
+    if (pg->n_pages < 1 || (long long)pg->n_pages * pg->page_size * 256 > 0xffffffffLL)
+        return fail(DSA_E_SHAPE, "n_pages = %d: the K/V pools must hold 1 page and < 4 GiB",
+                    pg->n_pages);
+    kp->table = pg->block_table;
+    kp->page = pg->page_size;
+    kp->per_seq = pg->pages_per_seq;
+    kp->n_pages = pg->n_pages;
     return DSA_OK;
 }
 
@@ -500,6 +542,39 @@ dsa_status dsa_forward_ragged_timed(const dsa_problem* p, const int32_t* seq_pos
     for (int i = 0; i < 3; ++i) stage_ms[i] = 0.f;
     s = forward_impl(p, q_idx, k_idx, Q, K, V, idx_out, O, lse, ws, ws_bytes, stream, &tm,
                      n_slabs, seq_pos);
+    hipError_t e = tm.finish(stage_ms);
+    if (s != DSA_OK) return s;
+    if (e != hipSuccess) return hip_fail(e, "stage timing events");
+    return ok();
+}
+
+dsa_status dsa_forward_paged(const dsa_problem* p, const int32_t* seq_pos, const dsa_pages* pg,
+                             const void* q_idx, const void* k_pool, const void* Q,
+                             const void* K_pool, const void* V_pool, int32_t* idx_out, void* O,
+                             float* lse, void* ws, size_t ws_bytes, void* stream) {
+    dsa::KeyPages kp{};
+    dsa_status s = check_paged(p, seq_pos, pg, &kp);
+    if (s != DSA_OK) return s;
+    s = forward_impl(p, q_idx, k_pool, Q, K_pool, V_pool, idx_out, O, lse, ws, ws_bytes, stream,
+                     nullptr, nullptr, seq_pos, &kp);
+    return s == DSA_OK ? ok() : s;
+}
+
+dsa_status dsa_forward_paged_timed(const dsa_problem* p, const int32_t* seq_pos,
+                                   const dsa_pages* pg, const void* q_idx, const void* k_pool,
+                                   const void* Q, const void* K_pool, const void* V_pool,
+                                   int32_t* idx_out, void* O, float* lse, void* ws,
+                                   size_t ws_bytes, void* stream, float* stage_ms,
+                                   int32_t* n_slabs) {
+    if (!stage_ms) return fail(DSA_E_NULL, "stage_ms is NULL");
+    dsa::KeyPages kp{};
+    dsa_status s = check_paged(p, seq_pos, pg, &kp);
+    if (s != DSA_OK) return s;
+    StageTimer tm;
+    tm.st = static_cast<hipStream_t>(stream);
+    for (int i = 0; i < 3; ++i) stage_ms[i] = 0.f;
+    s = forward_impl(p, q_idx, k_pool, Q, K_pool, V_pool, idx_out, O, lse, ws, ws_bytes, stream,
+                     &tm, n_slabs, seq_pos, &kp);
     hipError_t e = tm.finish(stage_ms);
     if (s != DSA_OK) return s;
     if (e != hipSuccess) return hip_fail(e, "stage timing events");

@@ -230,11 +230,12 @@ __device__ __forceinline__ void wave_attend(const AttnArgs& a, long long qrow, i
     const int m = lane & 15, g = lane >> 4;
     const int b = (int)(qrow / a.n_q);
     const int32_t* sel = a.idx + qrow * (long long)a.k;
-    const int n_k = a.n_k;
+    const int n_k = a.kv_rows;
+    const int nrec = (int)((uint32_t)n_k * (uint32_t)ROWB);  // < 2^32 bytes (checked by the host)
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(a.K + (size_t)b * n_k * HD), (short)0, n_k * ROWB, kBufWord3);
+        (void*)(a.K + (size_t)b * a.kv_bstride * HD), (short)0, nrec, kBufWord3);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(a.V + (size_t)b * n_k * HD), (short)0, n_k * ROWB, kBufWord3);
+        (void*)(a.V + (size_t)b * a.kv_bstride * HD), (short)0, nrec, kBufWord3);
 #pragma unroll
     for (int d = 0; d < 8; ++d) ws.o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
     ws.mrun = -__builtin_inff();
@@ -665,6 +666,28 @@ void attn_set_ranged(AttnArgs& a, int q_pos0, void* ws) {
     const size_t parts = (size_t)a.B * (size_t)a.parts_per_seq;
     a.part_lse = static_cast<float*>(ws);
     a.part_o = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + al(parts * 16 * 2 * sizeof(float)));
+}
+
+// Pool rows of the selected keys of a paged layout: prow[t] = key_row of
+// entry t of sequence t / per_seq for entries inside [0, n_k), -1 otherwise.
+__global__ __launch_bounds__(256) void page_rows_kernel(const int32_t* idx, int32_t* prow,
+                                                        long long total, int per_seq, int n_k,
+                                                        KeyPages pg) {
+    const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (t >= total) return;
+    const int j = idx[t];
+    prow[t] = (j >= 0 && j < n_k) ? (int32_t)key_row(pg, (int)(t / per_seq), n_k, j) : -1;
+}
+
+hipError_t launch_page_rows(const int32_t* idx, int32_t* prow, int B, int per_seq, int n_k,
+                            const KeyPages& pg, hipStream_t s) {
+    const long long total = (long long)B * per_seq;
+    if (total <= 0) return hipSuccess;
+    const long long nb = (total + 255) / 256;
+    if (nb > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(page_rows_kernel, dim3((unsigned)nb), dim3(256), 0, s, idx, prow, total,
+                       per_seq, n_k, pg);
+    return hipGetLastError();
 }
 
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t s) {

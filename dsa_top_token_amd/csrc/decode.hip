@@ -60,11 +60,11 @@ __device__ __forceinline__ Plan plan_row(const DecodeArgs& a, int b) {
 // Scores of keys t0 + 16*0.., as order keys, for the 16 keys of one tile whose
 // row index is key(i) for tile row i; lanes with column 0 hold rows 4g..4g+3.
 template <int DT, int D>
-__device__ __forceinline__ f32x4 key_tile(const uint8_t* kbase, int key_row, const Frag<DT, D>& fq,
+__device__ __forceinline__ f32x4 key_tile(const uint8_t* kpool, long long row, const Frag<DT, D>& fq,
                                           int g) {
     constexpr int RB = D * (DT == 0 ? 1 : 2);
     Frag<DT, D> fk;
-    fk.load(kbase + (size_t)key_row * RB, g);
+    fk.load(kpool + (size_t)row * RB, g);
     return tile_dot_k32<D>(fk, fq);
 }
 
@@ -116,14 +116,15 @@ __global__ __launch_bounds__(TH_NT) void decode_threshold_kernel(DecodeArgs a) {
     const int n = lane & 15, g = lane >> 4;
     Frag<DT, D> fq;
     fq.load(static_cast<const uint8_t*>(a.q) + ((size_t)b * a.n_q + a.q_row) * RB, g);
-    const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + (size_t)b * a.n_k * RB;
+    const uint8_t* kpool = static_cast<const uint8_t*>(a.k);
     // Waves take TH_TILES tiles of 16 samples at a time, all loads first.
     uint32_t lo = 0xffffffffu, hi = 0u;
     for (int t0 = wave * 16 * TH_TILES; t0 < p.ns; t0 += (TH_NT / 64) * 16 * TH_TILES) {
         Frag<DT, D> fk[TH_TILES];
 #pragma unroll
         for (int t = 0; t < TH_TILES; ++t)
-            fk[t].load(kbase + (size_t)(min(t0 + 16 * t + n, p.ns - 1) * p.S) * RB, g);
+            fk[t].load(kpool + (size_t)key_row(a.pages, b, a.n_k,
+                                               min(t0 + 16 * t + n, p.ns - 1) * p.S) * RB, g);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int t = 0; t < TH_TILES; ++t) {
@@ -227,8 +228,10 @@ __global__ __launch_bounds__(256) void decode_filter_kernel(DecodeArgs a) {
 
     Frag<DT, D> fq;
     fq.load(static_cast<const uint8_t*>(a.q) + ((size_t)b * a.n_q + a.q_row) * RB, g);
+    // the wave's 256 keys (one page of a paged layout holds them all)
+    const int kw0 = min(kb * KB + wave * KW, a.n_k - 1);
     const uint8_t* __restrict__ kbase =
-        static_cast<const uint8_t*>(a.k) + (size_t)b * a.n_k * RB;
+        static_cast<const uint8_t*>(a.k) + (size_t)key_row(a.pages, b, a.n_k, kw0) * RB;
     const int sel = n & (TILES - 1);
     const bool writer = n < TILES;
     uint32_t sk[STEPS][4];
@@ -245,7 +248,7 @@ __global__ __launch_bounds__(256) void decode_filter_kernel(DecodeArgs a) {
         Frag<DT, D> fk[TILES];
 #pragma unroll
         for (int t = 0; t < TILES; ++t)
-            fk[t].template load<true>(kbase + (size_t)min(k0 + 16 * t + n, a.n_k - 1) * RB, g);
+            fk[t].template load<true>(kbase + (size_t)(min(k0 + 16 * t + n, a.n_k - 1) - kw0) * RB, g);
         __builtin_amdgcn_sched_barrier(0);
         f32x4 acc[TILES];
 #pragma unroll
@@ -355,12 +358,14 @@ __global__ __launch_bounds__(256) void decode_filter_lds_kernel(DecodeArgs a) {
         return;
     }
     const uint32_t tau = a.tau[b];
-    const uint8_t* __restrict__ kbase = static_cast<const uint8_t*>(a.k) + (size_t)b * a.n_k * RB;
+    // the wave's 256 keys (one page of a paged layout holds them all)
+    const uint8_t* __restrict__ kbase =
+        static_cast<const uint8_t*>(a.k) + (size_t)key_row(a.pages, b, a.n_k, kw0) * RB;
     // 128-byte rows: copy lane l of instruction i moves granule
     // ((l % 8) ^ f(r)) of row r = 8 i + l / 8 into slot 64 i + l. Other
     // widths: copy i moves bytes [1024 i, 1024 i + 1024) of the step (rows
     // past the sequence read its last 16 bytes; they are masked later).
-    const size_t seq_bytes = (size_t)a.n_k * RB;
+    const size_t seq_bytes = (size_t)(a.n_k - kw0) * RB;  // from the wave's first key
     auto issue = [&](int st) {
         const int k0 = kw0 + st * 16 * TILES;
         uint8_t* dst = ring[wave][st & 1];
@@ -370,9 +375,9 @@ __global__ __launch_bounds__(256) void decode_filter_lds_kernel(DecodeArgs a) {
             if constexpr (SW) {
                 const int r = 8 * i + (lane >> 3);
                 const int j = (lane & 7) ^ ((r & 7) ^ ((r >> 3) & 1));
-                src = kbase + (size_t)min(k0 + r, a.n_k - 1) * RB + 16 * j;
+                src = kbase + (size_t)(min(k0 + r, a.n_k - 1) - kw0) * RB + 16 * j;
             } else {
-                src = kbase + min((size_t)k0 * RB + 1024 * i + 16 * lane, seq_bytes - 16);
+                src = kbase + min((size_t)(k0 - kw0) * RB + 1024 * i + 16 * lane, seq_bytes - 16);
             }
             __builtin_amdgcn_global_load_lds(src, dst + 1024 * i, 16, 0, kNontemporal);
         }
@@ -455,9 +460,10 @@ __device__ void row_scores(const DecodeArgs& a, int b, int nkeys, float* row) {
     const int n = lane & 15, g = lane >> 4;
     Frag<DT, D> fq;
     fq.load(static_cast<const uint8_t*>(a.q) + ((size_t)b * a.n_q + a.q_row) * RB, g);
-    const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + (size_t)b * a.n_k * RB;
+    const uint8_t* kpool = static_cast<const uint8_t*>(a.k);
     for (int t0 = wave * 16; t0 < nkeys; t0 += (SEL_NT / 64) * 16) {
-        const f32x4 acc = key_tile<DT, D>(kbase, min(t0 + n, nkeys - 1), fq, g);
+        const f32x4 acc =
+            key_tile<DT, D>(kpool, key_row(a.pages, b, a.n_k, min(t0 + n, nkeys - 1)), fq, g);
         if (n == 0) {
 #pragma unroll
             for (int r = 0; r < 4; ++r)

@@ -6,6 +6,24 @@
 
 namespace dsa {
 
+// Key rows of a sequence either follow one another ([B][n_k] rows) or sit in
+// pages of a shared pool: logical key j of sequence b is then row
+// table[b][j / page] * page + j % page of the pool. page is a multiple of 256,
+// so every 256-key run that starts at a multiple of 256 lies in one page.
+struct KeyPages {
+    const int32_t* table;   // [B][per_seq] physical page ids; null: [B][n_k] rows
+    int page, per_seq, n_pages;
+};
+
+// Row holding key j (0 <= j < n_k) of sequence b; page ids are clamped into
+// the pool.
+__device__ __forceinline__ long long key_row(const KeyPages& pg, int b, int n_k, int j) {
+    if (!pg.table) return (long long)b * n_k + j;
+    const int lp = j / pg.page;
+    const int pp = min(max(pg.table[(size_t)b * pg.per_seq + lp], 0), pg.n_pages - 1);
+    return (long long)pp * pg.page + (j - lp * pg.page);
+}
+
 // Indexer scores for query rows [q_begin, q_end) of every sequence.
 struct IndexArgs {
     const void* q;          // [B][n_q][d] fp8 e4m3fn or bf16
@@ -17,6 +35,7 @@ struct IndexArgs {
     int write_masked;       // 1: write -inf past each query's position
     const int32_t* seq_pos; // optional [B] (one query row per sequence only): each
                             // sequence's positions are offset by seq_pos[b]
+    KeyPages pages;         // k rows (one query row per sequence only)
     uint32_t* hist;         // optional (one query row per sequence only):
                             // per-row digit-1 histograms of the top-k schedule
 };
@@ -46,6 +65,11 @@ struct AttnArgs {
     float* lse;             // [B][n_q][H] or nullptr
     float* part;            // [B*n_q][n_split][16][128 + 4] fp32 partials
     int B, n_q, n_k, H, k;
+    // K/V rows of sequence b start at row b * kv_bstride; idx entries index
+    // rows [0, kv_rows) from there (n_k and n_k, or 0 and the pool's rows
+    // when idx holds pool rows of a paged layout).
+    long long kv_bstride;
+    int kv_rows;
     int n_split, split_len; // entries of idx handled per split (multiple of 128)
     // Key-range schedule (idx rows sorted ascending, causal, -1 padded at the
     // end): set by attn_set_ranged.
@@ -68,6 +92,7 @@ struct DecodeArgs {
     float* fallback;        // [B][n_k] score rows for rows the threshold misses
     const int32_t* seq_pos; // optional [B]: the query of sequence b sits at
                             // q_pos0 + seq_pos[b] + q_row
+    KeyPages pages;         // k rows
     uint32_t* tau;          // set by launch_decode_select from its workspace
     uint32_t* cnt;
     uint2* cand;
@@ -84,6 +109,9 @@ size_t topk_ws_bytes(int B, int rows, int n_k);
 uint32_t* topk_hist_ptr(void* ws);
 hipError_t launch_topk_prepare(const TopkArgs& a, void* ws, hipStream_t s);
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t s);
+// prow[b][s] = pool row of idx[b][s] (or -1) for per_seq entries per sequence.
+hipError_t launch_page_rows(const int32_t* idx, int32_t* prow, int B, int per_seq, int n_k,
+                            const KeyPages& pg, hipStream_t s);
 
 // Many query rows per sequence: sampled threshold, indexer sweep that keeps
 // only candidates, one-wave-per-row exact select, fallback for missed rows.

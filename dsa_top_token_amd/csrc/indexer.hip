@@ -160,8 +160,10 @@ __global__ __launch_bounds__(256) void index_decode_kernel(IndexArgs a) {
 
     Frag<DT, D> fq;
     fq.load(static_cast<const uint8_t*>(a.q) + ((size_t)b * a.n_q + a.q_begin) * RB, g);
+    // the wave's KW keys (one page of a paged layout holds them all)
+    const int kw0 = min(kb * KB + wave * KW, a.n_k - 1);
     const uint8_t* __restrict__ kbase =
-        static_cast<const uint8_t*>(a.k) + (size_t)b * a.n_k * RB;
+        static_cast<const uint8_t*>(a.k) + (size_t)key_row(a.pages, b, a.n_k, kw0) * RB;
     const int sel = n & (TILES - 1);
     const bool writer = n < TILES;
 
@@ -183,7 +185,7 @@ __global__ __launch_bounds__(256) void index_decode_kernel(IndexArgs a) {
         Frag<DT, D> fk[TILES];
 #pragma unroll
         for (int t = 0; t < TILES; ++t)
-            fk[t].template load<true>(kbase + (size_t)min(k0 + 16 * t + n, a.n_k - 1) * RB, g);
+            fk[t].template load<true>(kbase + (size_t)(min(k0 + 16 * t + n, a.n_k - 1) - kw0) * RB, g);
         // Keep every load of the step ahead of the first MFMA (the scheduler
         // would otherwise recycle two fragments and expose the latency).
         __builtin_amdgcn_sched_barrier(0);
@@ -231,7 +233,7 @@ __global__ __launch_bounds__(256) void index_decode_kernel(IndexArgs a) {
 template <int DT, int D>
 hipError_t launch_dt_d(const IndexArgs& a, hipStream_t s) {
     const int rows = a.q_end - a.q_begin;
-    if ((a.hist || a.seq_pos) && rows != 1) return hipErrorInvalidValue;
+    if ((a.hist || a.seq_pos || a.pages.table) && rows != 1) return hipErrorInvalidValue;
     if (rows == 1) {
         constexpr int TILES = 8, STEPS = 2, KB = 4 * 16 * TILES * STEPS;
         const long long nb = (long long)a.B * ((a.n_k + KB - 1) / KB);

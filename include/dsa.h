@@ -153,6 +153,42 @@ dsa_status dsa_forward_ragged_timed(const dsa_problem* p, const int32_t* seq_pos
                                     void* ws, size_t ws_bytes, void* stream,
                                     float* stage_ms, int32_t* n_slabs);
 
+/* A paged key layout: the keys of every sequence live in pages of page_size
+ * rows inside shared pools, logical key j of sequence b in row
+ * block_table[b][j / page_size] * page_size + j % page_size of a pool.
+ *   block_table  int32 [batch][pages_per_seq], device memory, 16-byte aligned
+ *                (ids outside [0, n_pages) are clamped into it)
+ *   page_size    keys per page, a multiple of 256
+ *   pages_per_seq  logical pages per sequence; n_k = pages_per_seq * page_size
+ *   n_pages      pages in each pool (n_pages * page_size * 256 < 4 GiB) */
+typedef struct {
+    const int32_t* block_table;
+    int32_t page_size, pages_per_seq, n_pages;
+} dsa_pages;
+
+/* dsa_forward_ragged over a paged layout (same definitions): k_pool
+ * [n_pages][page_size][d_idx] in idx_dtype, K_pool and V_pool
+ * [n_pages][page_size][128] bfloat16 replace k_idx, K and V; idx_out holds
+ * logical key indices as for dsa_forward. Same workspace as dsa_forward.
+ * Errors: those of dsa_forward_ragged; DSA_E_NULL (pages or its table
+ * NULL); DSA_E_SHAPE (page sizes as above). */
+dsa_status dsa_forward_paged(const dsa_problem* p, const int32_t* seq_pos,
+                             const dsa_pages* pages, const void* q_idx,
+                             const void* k_pool, const void* Q,
+                             const void* K_pool, const void* V_pool,
+                             int32_t* idx_out, void* O, float* lse, void* ws,
+                             size_t ws_bytes, void* stream);
+
+/* dsa_forward_paged for profiling, as dsa_forward_timed (blocks until the
+ * stream has finished; stage_ms must not be NULL). */
+dsa_status dsa_forward_paged_timed(const dsa_problem* p, const int32_t* seq_pos,
+                                   const dsa_pages* pages, const void* q_idx,
+                                   const void* k_pool, const void* Q,
+                                   const void* K_pool, const void* V_pool,
+                                   int32_t* idx_out, void* O, float* lse,
+                                   void* ws, size_t ws_bytes, void* stream,
+                                   float* stage_ms, int32_t* n_slabs);
+
 /* dsa_forward for profiling: the same work and results, plus the device time
  * of each stage. HIP events are recorded on `stream` around the indexer
  * kernel, the top-k kernels and the attention kernels of every row slab; the

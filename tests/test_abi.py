@@ -106,6 +106,31 @@ def test_ragged_forward_arguments():
                                   FAKE, None, FAKE, need - 1, None) == -5
 
 
+def test_paged_forward_arguments():
+    lib = dsa.load()
+    dec = prob(n_q=1, n_k=512, q_pos0=0)
+    need = dsa.workspace_size(dec, dsa.OP_FORWARD)
+    tail = (FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, need, None)
+
+    def call(pg, sp=FAKE, p=dec):
+        return lib.dsa_forward_paged(ctypes.byref(p), sp, pg, *tail)
+
+    ok = dict(block_table=0x100000, page_size=256, pages_per_seq=2, n_pages=8)
+    pg = lambda **kw: ctypes.byref(dsa.Pages(**{**ok, **kw}))
+    assert call(None) == -1
+    assert call(pg(block_table=None)) == -1
+    assert call(pg(block_table=0x100008)) == -4
+    assert call(pg(page_size=100)) == -2
+    assert call(pg(page_size=512)) == -2      # 2 x 512 != n_k
+    assert call(pg(n_pages=0)) == -2
+    assert call(pg(n_pages=1 << 16)) == -2    # K/V pools of 4 GiB
+    assert call(pg(), sp=None) == -1
+    assert call(pg(), p=prob(n_q=2, n_k=512)) == -3
+    # valid arguments get as far as the workspace check
+    assert lib.dsa_forward_paged(ctypes.byref(dec), FAKE, pg(), FAKE, FAKE, FAKE, FAKE, FAKE,
+                                 None, FAKE, None, FAKE, need - 1, None) == -5
+
+
 def test_attention_workspace_only_when_split():
     # decode-sized batches split each query's keys; prefill does not
     dec = synth.WORKLOADS["decode_128k_clustered"]
