@@ -171,12 +171,26 @@ def main():
     # a ragged batch: each sequence's query position (device int32 [B])
     sp = (torch.tensor(w.positions(args.seed), dtype=torch.int32, device=dev)
           if w.ragged else None)
+    pages = None
+    if w.page_size:
+        # k_idx, K and V moved into shuffled page pools (on the device)
+        table, n_pages = w.page_pool(args.seed)
+        per = w.n_k // w.page_size
+        perm = table.reshape(-1).to(dev).long()
+        for name in ("k_idx", "K", "V"):
+            t = d[name]
+            pool = torch.zeros((n_pages, w.page_size) + tuple(t.shape[2:]), dtype=t.dtype,
+                               device=dev)
+            pool[perm] = t.reshape((w.batch * per, w.page_size) + tuple(t.shape[2:]))
+            d[name] = pool
+        d["table"] = table.to(dev)
+        pages = dsa.make_pages(d["table"], w.page_size, n_pages)
     O = torch.empty_like(d["Q"])
     idx = torch.empty((w.batch, w.n_q, w.top_k), dtype=torch.int32, device=dev)
     lse = torch.empty((w.batch, w.n_q, w.n_heads), dtype=torch.float32, device=dev)
 
     def step():
-        fwd(d["q_idx"], d["k_idx"], d["Q"], d["K"], d["V"], O, idx, lse, seq_pos=sp)
+        fwd(d["q_idx"], d["k_idx"], d["Q"], d["K"], d["V"], O, idx, lse, seq_pos=sp, pages=pages)
 
     for _ in range(args.warmup):
         step()
@@ -201,7 +215,7 @@ def main():
         slabs = 1
         for _ in range(n_rep):
             ms3, slabs = fwd.timed(d["q_idx"], d["k_idx"], d["Q"], d["K"], d["V"], O, idx, lse,
-                                   seq_pos=sp)
+                                   seq_pos=sp, pages=pages)
             tot = [a + b for a, b in zip(tot, ms3)]
         stages = {n: t / n_rep for n, t in zip(names, tot)}
         dom = max(stages, key=stages.get)
@@ -245,6 +259,8 @@ def main():
         pos = w.positions(args.seed)
         out["config"]["ragged"] = {"positions": "seeded, uniform in [n_k/8, n_k-1]",
                                    "mean_len": round(sum(p + 1 for p in pos) / len(pos), 1)}
+    if w.page_size:
+        out["config"]["paged"] = {"page_size": w.page_size, "pool": "shuffled, 16 spare pages"}
     print(json.dumps(out))
 
 

@@ -18,7 +18,9 @@ Recipe (every tensor has its own CPU generator seeded with seed*1000 + tid):
   * Q [B, n_q, H, 128], K and V [B, n_k, 128]: N(0, 1) drawn in float32 and
     rounded to bfloat16;
   * ragged decode batches: each sequence's query position uniform in
-    [n_k / 8, n_k - 1] (rows share the padded [B, n_k] layout).
+    [n_k / 8, n_k - 1] (rows share the padded [B, n_k] layout);
+  * paged layouts: the B * n_k / P pages of P keys placed at a seeded random
+    permutation of a pool with 16 spare pages (page_pool()).
 """
 from __future__ import annotations
 
@@ -28,7 +30,7 @@ from typing import Dict, Optional
 import torch
 
 TID = {"q_idx": 1, "k_idx": 2, "Q": 3, "K": 4, "V": 5,
-       "centroids": 6, "assign": 7, "noise": 8, "positions": 9}
+       "centroids": 6, "assign": 7, "noise": 8, "positions": 9, "pages": 10}
 
 HEAD_DIM = 128
 N_CENTROIDS = 64
@@ -48,6 +50,7 @@ class Workload:
     n_heads: int
     clustered: bool = False
     ragged: bool = False  # decode only: per-sequence query positions (positions())
+    page_size: int = 0    # > 0: k_idx, K, V stored in shuffled pages of this many keys
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -63,6 +66,15 @@ class Workload:
             return [self.q_pos0] * self.batch
         g = _gen(seed, "positions", "cpu")
         return torch.randint(self.n_k // 8, self.n_k, (self.batch,), generator=g).tolist()
+
+    def page_pool(self, seed: int = 0):
+        """Physical page of every logical page, [B, n_k / P] (a seeded
+        permutation of a pool of B * n_k / P + 16 pages), and the pool size."""
+        per = self.n_k // self.page_size
+        n_pages = self.batch * per + 16
+        g = _gen(seed, "pages", "cpu")
+        perm = torch.randperm(n_pages, generator=g)[: self.batch * per]
+        return perm.reshape(self.batch, per).to(torch.int32), n_pages
 
     def n_selected(self, seed: int = 0) -> int:
         """Sum over queries of min(top_k, pos + 1): rows attended in total."""
@@ -98,9 +110,12 @@ WORKLOADS: Dict[str, Workload] = {
                 clustered=True),
     ]
 }
-# A ragged 128K decode batch (sequence lengths spread over the context).
+# A ragged 128K decode batch (sequence lengths spread over the context), and
+# the same batch over a paged layout (256-key pages in a shuffled pool).
 WORKLOADS["decode_128k_ragged"] = Workload("decode_128k_ragged", "decode", 64, 1, 131072, 0,
                                            128, "fp8", 2048, 16, ragged=True)
+WORKLOADS["decode_128k_paged"] = WORKLOADS["decode_128k_ragged"].replace(
+    name="decode_128k_paged", page_size=256)
 
 
 def _gen(seed: int, tid: str, device) -> torch.Generator:
