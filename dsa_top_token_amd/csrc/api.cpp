@@ -401,9 +401,7 @@ dsa_status check_paged(const dsa_problem* p, const int32_t* seq_pos, const dsa_p
     if (!pg || !pg->block_table) return fail(DSA_E_NULL, "pages or pages->block_table is NULL");
     if (misaligned(pg->block_table))
         return fail(DSA_E_ALIGN, "pages->block_table is not 16-byte aligned");
-    if (pg->page_size < 256 || pg->page_size % 256 != 0)
-        return fail(DSA_E_SHAPE, "page_size = %d is not a positive multiple of 256",
-                    pg->page_size);
+    if (pg->page_size < 1) return fail(DSA_E_SHAPE, "page_size = %d", pg->page_size);
     if (pg->pages_per_seq < 1 || (long long)pg->pages_per_seq * pg->page_size != p->n_k)
         return fail(DSA_E_SHAPE, "pages_per_seq * page_size must equal n_k (%d * %d != %d)",
                     pg->pages_per_seq, pg->page_size, p->n_k);

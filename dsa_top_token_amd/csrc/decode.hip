@@ -228,10 +228,11 @@ __global__ __launch_bounds__(256) void decode_filter_kernel(DecodeArgs a) {
 
     Frag<DT, D> fq;
     fq.load(static_cast<const uint8_t*>(a.q) + ((size_t)b * a.n_q + a.q_row) * RB, g);
-    // the wave's 256 keys (one page of a paged layout holds them all)
+    // the wave's 256 keys (contiguous unless pages are smaller)
     const int kw0 = min(kb * KB + wave * KW, a.n_k - 1);
-    const uint8_t* __restrict__ kbase =
-        static_cast<const uint8_t*>(a.k) + (size_t)key_row(a.pages, b, a.n_k, kw0) * RB;
+    const uint8_t* kpool = static_cast<const uint8_t*>(a.k);
+    const bool contig = run_contiguous(a.pages);
+    const uint8_t* __restrict__ kbase = kpool + (size_t)key_row(a.pages, b, a.n_k, kw0) * RB;
     const int sel = n & (TILES - 1);
     const bool writer = n < TILES;
     uint32_t sk[STEPS][4];
@@ -248,7 +249,8 @@ __global__ __launch_bounds__(256) void decode_filter_kernel(DecodeArgs a) {
         Frag<DT, D> fk[TILES];
 #pragma unroll
         for (int t = 0; t < TILES; ++t)
-            fk[t].template load<true>(kbase + (size_t)(min(k0 + 16 * t + n, a.n_k - 1) - kw0) * RB, g);
+            fk[t].template load<true>(key_ptr(a.pages, contig, kpool, kbase, kw0, b, a.n_k,
+                                              min(k0 + 16 * t + n, a.n_k - 1), RB), g);
         __builtin_amdgcn_sched_barrier(0);
         f32x4 acc[TILES];
 #pragma unroll
@@ -358,9 +360,10 @@ __global__ __launch_bounds__(256) void decode_filter_lds_kernel(DecodeArgs a) {
         return;
     }
     const uint32_t tau = a.tau[b];
-    // the wave's 256 keys (one page of a paged layout holds them all)
-    const uint8_t* __restrict__ kbase =
-        static_cast<const uint8_t*>(a.k) + (size_t)key_row(a.pages, b, a.n_k, kw0) * RB;
+    // the wave's 256 keys (contiguous unless pages are smaller)
+    const uint8_t* kpool = static_cast<const uint8_t*>(a.k);
+    const bool contig = run_contiguous(a.pages);
+    const uint8_t* __restrict__ kbase = kpool + (size_t)key_row(a.pages, b, a.n_k, kw0) * RB;
     // 128-byte rows: copy lane l of instruction i moves granule
     // ((l % 8) ^ f(r)) of row r = 8 i + l / 8 into slot 64 i + l. Other
     // widths: copy i moves bytes [1024 i, 1024 i + 1024) of the step (rows
@@ -375,9 +378,15 @@ __global__ __launch_bounds__(256) void decode_filter_lds_kernel(DecodeArgs a) {
             if constexpr (SW) {
                 const int r = 8 * i + (lane >> 3);
                 const int j = (lane & 7) ^ ((r & 7) ^ ((r >> 3) & 1));
-                src = kbase + (size_t)(min(k0 + r, a.n_k - 1) - kw0) * RB + 16 * j;
-            } else {
+                src = key_ptr(a.pages, contig, kpool, kbase, kw0, b, a.n_k, min(k0 + r, a.n_k - 1),
+                              RB) + 16 * j;
+            } else if (contig) {
                 src = kbase + min((size_t)(k0 - kw0) * RB + 1024 * i + 16 * lane, seq_bytes - 16);
+            } else {
+                // byte o of the step: column o % RB of chunk key o / RB
+                const int o = 1024 * i + 16 * lane, r = o / RB;
+                src = kpool + (size_t)key_row(a.pages, b, a.n_k, min(k0 + r, a.n_k - 1)) * RB +
+                      (o - r * RB);
             }
             __builtin_amdgcn_global_load_lds(src, dst + 1024 * i, 16, 0, kNontemporal);
         }

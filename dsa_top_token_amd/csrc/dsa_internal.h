@@ -8,8 +8,9 @@ namespace dsa {
 
 // Key rows of a sequence either follow one another ([B][n_k] rows) or sit in
 // pages of a shared pool: logical key j of sequence b is then row
-// table[b][j / page] * page + j % page of the pool. page is a multiple of 256,
-// so every 256-key run that starts at a multiple of 256 lies in one page.
+// table[b][j / page] * page + j % page of the pool. With page a multiple of
+// 256 every 256-key run that starts at a multiple of 256 lies in one page
+// (run_contiguous); other page sizes translate row by row.
 struct KeyPages {
     const int32_t* table;   // [B][per_seq] physical page ids; null: [B][n_k] rows
     int page, per_seq, n_pages;
@@ -22,6 +23,18 @@ __device__ __forceinline__ long long key_row(const KeyPages& pg, int b, int n_k,
     const int lp = j / pg.page;
     const int pp = min(max(pg.table[(size_t)b * pg.per_seq + lp], 0), pg.n_pages - 1);
     return (long long)pp * pg.page + (j - lp * pg.page);
+}
+
+__host__ __device__ __forceinline__ bool run_contiguous(const KeyPages& pg) {
+    return !pg.table || pg.page % 256 == 0;
+}
+
+// Address of key j's row: from the run's base row kw0 when 256-key runs are
+// contiguous, else through the page table.
+__device__ __forceinline__ const uint8_t* key_ptr(const KeyPages& pg, bool contig,
+                                                  const uint8_t* pool, const uint8_t* run,
+                                                  int kw0, int b, int n_k, int j, int rb) {
+    return contig ? run + (size_t)(j - kw0) * rb : pool + (size_t)key_row(pg, b, n_k, j) * rb;
 }
 
 // Indexer scores for query rows [q_begin, q_end) of every sequence.

@@ -160,10 +160,11 @@ __global__ __launch_bounds__(256) void index_decode_kernel(IndexArgs a) {
 
     Frag<DT, D> fq;
     fq.load(static_cast<const uint8_t*>(a.q) + ((size_t)b * a.n_q + a.q_begin) * RB, g);
-    // the wave's KW keys (one page of a paged layout holds them all)
+    // the wave's KW keys (contiguous unless pages are smaller)
     const int kw0 = min(kb * KB + wave * KW, a.n_k - 1);
-    const uint8_t* __restrict__ kbase =
-        static_cast<const uint8_t*>(a.k) + (size_t)key_row(a.pages, b, a.n_k, kw0) * RB;
+    const uint8_t* kpool = static_cast<const uint8_t*>(a.k);
+    const bool contig = run_contiguous(a.pages);
+    const uint8_t* __restrict__ kbase = kpool + (size_t)key_row(a.pages, b, a.n_k, kw0) * RB;
     const int sel = n & (TILES - 1);
     const bool writer = n < TILES;
 
@@ -185,7 +186,8 @@ __global__ __launch_bounds__(256) void index_decode_kernel(IndexArgs a) {
         Frag<DT, D> fk[TILES];
 #pragma unroll
         for (int t = 0; t < TILES; ++t)
-            fk[t].template load<true>(kbase + (size_t)(min(k0 + 16 * t + n, a.n_k - 1) - kw0) * RB, g);
+            fk[t].template load<true>(key_ptr(a.pages, contig, kpool, kbase, kw0, b, a.n_k,
+                                              min(k0 + 16 * t + n, a.n_k - 1), RB), g);
         // Keep every load of the step ahead of the first MFMA (the scheduler
         // would otherwise recycle two fragments and expose the latency).
         __builtin_amdgcn_sched_barrier(0);

@@ -111,11 +111,13 @@ WORKLOADS: Dict[str, Workload] = {
     ]
 }
 # A ragged 128K decode batch (sequence lengths spread over the context), and
-# the same batch over a paged layout (256-key pages in a shuffled pool).
+# the same batch over paged layouts (256- and 16-key pages in shuffled pools).
 WORKLOADS["decode_128k_ragged"] = Workload("decode_128k_ragged", "decode", 64, 1, 131072, 0,
                                            128, "fp8", 2048, 16, ragged=True)
 WORKLOADS["decode_128k_paged"] = WORKLOADS["decode_128k_ragged"].replace(
     name="decode_128k_paged", page_size=256)
+WORKLOADS["decode_128k_paged16"] = WORKLOADS["decode_128k_ragged"].replace(
+    name="decode_128k_paged16", page_size=16)
 
 
 def _gen(seed: int, tid: str, device) -> torch.Generator:

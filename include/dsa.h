@@ -158,7 +158,8 @@ dsa_status dsa_forward_ragged_timed(const dsa_problem* p, const int32_t* seq_pos
  * block_table[b][j / page_size] * page_size + j % page_size of a pool.
  *   block_table  int32 [batch][pages_per_seq], device memory, 16-byte aligned
  *                (ids outside [0, n_pages) are clamped into it)
- *   page_size    keys per page, a multiple of 256
+ *   page_size    keys per page (>= 1; multiples of 256 let the indexer stream
+ *                whole pages, other sizes translate key by key)
  *   pages_per_seq  logical pages per sequence; n_k = pages_per_seq * page_size
  *   n_pages      pages in each pool (n_pages * page_size * 256 < 4 GiB) */
 typedef struct {

@@ -120,8 +120,9 @@ def test_paged_forward_arguments():
     assert call(None) == -1
     assert call(pg(block_table=None)) == -1
     assert call(pg(block_table=0x100008)) == -4
-    assert call(pg(page_size=100)) == -2
+    assert call(pg(page_size=0)) == -2
     assert call(pg(page_size=512)) == -2      # 2 x 512 != n_k
+    assert call(pg(page_size=100)) == -2      # 2 x 100 != n_k
     assert call(pg(n_pages=0)) == -2
     assert call(pg(n_pages=1 << 16)) == -2    # K/V pools of 4 GiB
     assert call(pg(), sp=None) == -1

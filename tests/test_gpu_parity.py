@@ -329,6 +329,13 @@ PAGED = [
     (Workload("paged_topk", "decode", 3, 1, 2048, 0, 96, "fp8", 300, 8), 512, [2047, 40, 1500]),
     # wide bf16 rows, pages of 1024
     (Workload("paged_bf16", "decode", 2, 1, 9216, 0, 160, "bf16", 1000, 4), 1024, [9215, 5000]),
+    # pages smaller than a wave's 256-key run: translated key by key
+    (Workload("paged16_select", "decode", 3, 1, 16384, 0, 128, "fp8", 700, 4), 16,
+     [16383, 3000, 9999]),
+    (Workload("paged64_select_d96", "decode", 2, 1, 8192, 0, 96, "fp8", 400, 2), 64,
+     [8191, 5000]),
+    (Workload("paged32_topk", "decode", 2, 1, 2048, 0, 64, "fp8", 200, 2), 32, [2047, 600]),
+    (Workload("paged48_bf16", "decode", 2, 1, 9216, 0, 160, "bf16", 500, 2), 48, [9215, 4000]),
 ]
 
 
