@@ -209,7 +209,9 @@ __device__ __forceinline__ void find_bin12(const uint32_t* hist, uint32_t rem, u
 
 // The streaming indexer of one query row per sequence (see index_decode_kernel
 // in indexer.hip for the tile layout), keeping only keys at or above tau.
-template <int DT, int D>
+// CONTIG: 256-key runs are contiguous (whole-run address arithmetic); else
+// per-key pool rows.
+template <int DT, int D, bool CONTIG>
 __global__ __launch_bounds__(256) void decode_filter_kernel(DecodeArgs a) {
     constexpr int TILES = 8, STEPS = 2;
     constexpr int RB = D * (DT == 0 ? 1 : 2);
@@ -231,8 +233,10 @@ __global__ __launch_bounds__(256) void decode_filter_kernel(DecodeArgs a) {
     // the wave's 256 keys (contiguous unless pages are smaller)
     const int kw0 = min(kb * KB + wave * KW, a.n_k - 1);
     const uint8_t* kpool = static_cast<const uint8_t*>(a.k);
-    const bool contig = run_contiguous(a.pages);
+    constexpr bool contig = CONTIG;
     const uint8_t* __restrict__ kbase = kpool + (size_t)key_row(a.pages, b, a.n_k, kw0) * RB;
+    RunRows rr;
+    if constexpr (!contig) rr.load(a.pages, b, a.n_k, kw0);
     const int sel = n & (TILES - 1);
     const bool writer = n < TILES;
     uint32_t sk[STEPS][4];
@@ -249,8 +253,9 @@ __global__ __launch_bounds__(256) void decode_filter_kernel(DecodeArgs a) {
         Frag<DT, D> fk[TILES];
 #pragma unroll
         for (int t = 0; t < TILES; ++t)
-            fk[t].template load<true>(key_ptr(a.pages, contig, kpool, kbase, kw0, b, a.n_k,
-                                              min(k0 + 16 * t + n, a.n_k - 1), RB), g);
+            fk[t].template load<true>(run_key(contig, kpool, kbase, rr, kw0,
+                                              min(k0 + 16 * t + n, a.n_k - 1), 2 * st + t / 4,
+                                              16 * (t % 4) + n, RB), g);
         __builtin_amdgcn_sched_barrier(0);
         f32x4 acc[TILES];
 #pragma unroll
@@ -335,7 +340,7 @@ constexpr int LDS_RB_MAX = 160;
 // 1 KB copies (128-byte rows: swizzled per row as sw_slot gives; other
 // widths: the step's bytes in order), the same scores and candidate lists as
 // decode_filter_kernel.
-template <int DT, int D>
+template <int DT, int D, bool CONTIG>
 __global__ __launch_bounds__(256) void decode_filter_lds_kernel(DecodeArgs a) {
     constexpr int TILES = 4, STEPS = 4;
     constexpr int RB = D * (DT == 0 ? 1 : 2);
@@ -362,8 +367,10 @@ __global__ __launch_bounds__(256) void decode_filter_lds_kernel(DecodeArgs a) {
     const uint32_t tau = a.tau[b];
     // the wave's 256 keys (contiguous unless pages are smaller)
     const uint8_t* kpool = static_cast<const uint8_t*>(a.k);
-    const bool contig = run_contiguous(a.pages);
+    constexpr bool contig = CONTIG;
     const uint8_t* __restrict__ kbase = kpool + (size_t)key_row(a.pages, b, a.n_k, kw0) * RB;
+    RunRows rr;
+    if constexpr (!contig) rr.load(a.pages, b, a.n_k, kw0);
     // 128-byte rows: copy lane l of instruction i moves granule
     // ((l % 8) ^ f(r)) of row r = 8 i + l / 8 into slot 64 i + l. Other
     // widths: copy i moves bytes [1024 i, 1024 i + 1024) of the step (rows
@@ -378,15 +385,14 @@ __global__ __launch_bounds__(256) void decode_filter_lds_kernel(DecodeArgs a) {
             if constexpr (SW) {
                 const int r = 8 * i + (lane >> 3);
                 const int j = (lane & 7) ^ ((r & 7) ^ ((r >> 3) & 1));
-                src = key_ptr(a.pages, contig, kpool, kbase, kw0, b, a.n_k, min(k0 + r, a.n_k - 1),
-                              RB) + 16 * j;
-            } else if (contig) {
+                src = run_key(contig, kpool, kbase, rr, kw0, min(k0 + r, a.n_k - 1), st, r, RB) +
+                      16 * j;
+            } else if constexpr (contig) {
                 src = kbase + min((size_t)(k0 - kw0) * RB + 1024 * i + 16 * lane, seq_bytes - 16);
             } else {
                 // byte o of the step: column o % RB of chunk key o / RB
                 const int o = 1024 * i + 16 * lane, r = o / RB;
-                src = kpool + (size_t)key_row(a.pages, b, a.n_k, min(k0 + r, a.n_k - 1)) * RB +
-                      (o - r * RB);
+                src = kpool + (size_t)rr.row(st, r) * RB + (o - r * RB);
             }
             __builtin_amdgcn_global_load_lds(src, dst + 1024 * i, 16, 0, kNontemporal);
         }
@@ -638,10 +644,22 @@ hipError_t launch_d(const DecodeArgs& a, int part, hipStream_t s) {
         const int KB = 4 * SLOT;
         const long long nb = (long long)a.B * ((a.n_k + KB - 1) / KB);
         if (nb > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-        if constexpr (D * (DT == 0 ? 1 : 2) <= LDS_RB_MAX)
-            hipLaunchKernelGGL((decode_filter_lds_kernel<DT, D>), dim3((unsigned)nb), dim3(256), 0, s, a);
-        else
-            hipLaunchKernelGGL((decode_filter_kernel<DT, D>), dim3((unsigned)nb), dim3(256), 0, s, a);
+        const bool contig = run_contiguous(a.pages);
+        if constexpr (D * (DT == 0 ? 1 : 2) <= LDS_RB_MAX) {
+            if (contig)
+                hipLaunchKernelGGL((decode_filter_lds_kernel<DT, D, true>), dim3((unsigned)nb),
+                                   dim3(256), 0, s, a);
+            else
+                hipLaunchKernelGGL((decode_filter_lds_kernel<DT, D, false>), dim3((unsigned)nb),
+                                   dim3(256), 0, s, a);
+        } else {
+            if (contig)
+                hipLaunchKernelGGL((decode_filter_kernel<DT, D, true>), dim3((unsigned)nb),
+                                   dim3(256), 0, s, a);
+            else
+                hipLaunchKernelGGL((decode_filter_kernel<DT, D, false>), dim3((unsigned)nb),
+                                   dim3(256), 0, s, a);
+        }
     } else {
         hipLaunchKernelGGL((decode_select_kernel<DT, D>), dim3(a.B), dim3(SEL_NT), 0, s, a);
     }

@@ -10,7 +10,7 @@ namespace dsa {
 // pages of a shared pool: logical key j of sequence b is then row
 // table[b][j / page] * page + j % page of the pool. With page a multiple of
 // 256 every 256-key run that starts at a multiple of 256 lies in one page
-// (run_contiguous); other page sizes translate row by row.
+// (run_contiguous); other page sizes translate key by key (RunRows).
 struct KeyPages {
     const int32_t* table;   // [B][per_seq] physical page ids; null: [B][n_k] rows
     int page, per_seq, n_pages;
@@ -29,12 +29,32 @@ __host__ __device__ __forceinline__ bool run_contiguous(const KeyPages& pg) {
     return !pg.table || pg.page % 256 == 0;
 }
 
-// Address of key j's row: from the run's base row kw0 when 256-key runs are
-// contiguous, else through the page table.
-__device__ __forceinline__ const uint8_t* key_ptr(const KeyPages& pg, bool contig,
-                                                  const uint8_t* pool, const uint8_t* run,
-                                                  int kw0, int b, int n_k, int j, int rb) {
-    return contig ? run + (size_t)(j - kw0) * rb : pool + (size_t)key_row(pg, b, n_k, j) * rb;
+// Pool rows of the 256-key run that starts at key kw0 (a multiple of 256),
+// for layouts whose runs are not contiguous: lane l holds the rows of keys
+// kw0 + 64 q + l (q = 0..3, clamped to the last key), so the streaming loops
+// read a row with one lane shuffle instead of waiting on the page table.
+// Pool rows fit 32 bits (pools hold under 4 GiB).
+struct RunRows {
+    uint32_t r[4] = {0u, 0u, 0u, 0u};
+    __device__ __forceinline__ void load(const KeyPages& pg, int b, int n_k, int kw0) {
+        const int lane = threadIdx.x & 63;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            r[q] = (uint32_t)key_row(pg, b, n_k, min(kw0 + 64 * q + lane, n_k - 1));
+    }
+    // Row of key kw0 + 64 q + l (q a compile-time constant after unrolling;
+    // every lane of the wave must call it).
+    __device__ __forceinline__ uint32_t row(int q, int l) const {
+        return (uint32_t)__shfl((int)r[q], l);
+    }
+};
+
+// Address of key j = min(kw0 + 64 q + l, n_k - 1) of a wave's run: from the
+// run's first row when runs are contiguous, else from the run's pool rows.
+__device__ __forceinline__ const uint8_t* run_key(bool contig, const uint8_t* pool,
+                                                  const uint8_t* run, const RunRows& rr, int kw0,
+                                                  int j, int q, int l, int rb) {
+    return contig ? run + (size_t)(j - kw0) * rb : pool + (size_t)rr.row(q, l) * rb;
 }
 
 // Indexer scores for query rows [q_begin, q_end) of every sequence.

@@ -136,7 +136,9 @@ __global__ __launch_bounds__(256) void index_scores_kernel(IndexArgs a) {
 // leave as one contiguous store. With HIST the same lanes add the scores'
 // digit-1 radix to an LDS histogram that is flushed into the sequence's row
 // histogram at the end.
-template <int DT, int D, int TILES, int STEPS, bool HIST>
+// CONTIG: 256-key runs are contiguous (whole-run address arithmetic); else
+// per-key pool rows.
+template <int DT, int D, int TILES, int STEPS, bool HIST, bool CONTIG>
 __global__ __launch_bounds__(256) void index_decode_kernel(IndexArgs a) {
     static_assert(TILES == 8, "the tile pick below assumes 8 tiles per step");
     __shared__ uint32_t lhist[HIST ? topk::BINS : 1];
@@ -163,8 +165,11 @@ __global__ __launch_bounds__(256) void index_decode_kernel(IndexArgs a) {
     // the wave's KW keys (contiguous unless pages are smaller)
     const int kw0 = min(kb * KB + wave * KW, a.n_k - 1);
     const uint8_t* kpool = static_cast<const uint8_t*>(a.k);
-    const bool contig = run_contiguous(a.pages);
+    constexpr bool contig = CONTIG;
     const uint8_t* __restrict__ kbase = kpool + (size_t)key_row(a.pages, b, a.n_k, kw0) * RB;
+    static_assert(KW == 256, "one 256-key run per wave");
+    RunRows rr;
+    if constexpr (!contig) rr.load(a.pages, b, a.n_k, kw0);
     const int sel = n & (TILES - 1);
     const bool writer = n < TILES;
 
@@ -186,8 +191,9 @@ __global__ __launch_bounds__(256) void index_decode_kernel(IndexArgs a) {
         Frag<DT, D> fk[TILES];
 #pragma unroll
         for (int t = 0; t < TILES; ++t)
-            fk[t].template load<true>(key_ptr(a.pages, contig, kpool, kbase, kw0, b, a.n_k,
-                                              min(k0 + 16 * t + n, a.n_k - 1), RB), g);
+            fk[t].template load<true>(run_key(contig, kpool, kbase, rr, kw0,
+                                              min(k0 + 16 * t + n, a.n_k - 1), 2 * st + t / 4,
+                                              16 * (t % 4) + n, RB), g);
         // Keep every load of the step ahead of the first MFMA (the scheduler
         // would otherwise recycle two fragments and expose the latency).
         __builtin_amdgcn_sched_barrier(0);
@@ -240,11 +246,18 @@ hipError_t launch_dt_d(const IndexArgs& a, hipStream_t s) {
         constexpr int TILES = 8, STEPS = 2, KB = 4 * 16 * TILES * STEPS;
         const long long nb = (long long)a.B * ((a.n_k + KB - 1) / KB);
         if (nb > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-        if (a.hist)
-            hipLaunchKernelGGL((index_decode_kernel<DT, D, TILES, STEPS, true>),
+        const bool contig = run_contiguous(a.pages);
+        if (a.hist && contig)
+            hipLaunchKernelGGL((index_decode_kernel<DT, D, TILES, STEPS, true, true>),
+                               dim3((unsigned)nb), dim3(256), 0, s, a);
+        else if (a.hist)
+            hipLaunchKernelGGL((index_decode_kernel<DT, D, TILES, STEPS, true, false>),
+                               dim3((unsigned)nb), dim3(256), 0, s, a);
+        else if (contig)
+            hipLaunchKernelGGL((index_decode_kernel<DT, D, TILES, STEPS, false, true>),
                                dim3((unsigned)nb), dim3(256), 0, s, a);
         else
-            hipLaunchKernelGGL((index_decode_kernel<DT, D, TILES, STEPS, false>),
+            hipLaunchKernelGGL((index_decode_kernel<DT, D, TILES, STEPS, false, false>),
                                dim3((unsigned)nb), dim3(256), 0, s, a);
     } else if (rows <= 16) {
         // Few queries per sequence (decode): the 4 waves split the keys.

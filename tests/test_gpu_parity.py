@@ -502,23 +502,27 @@ def test_full_decode_128k_ragged(gpu_lib):
                                              sl["V"], pos[b], w.top_k)
         assert np.array_equal(idx[b:b + 1].cpu().numpy(), i_ref), (b, pos[b])
         assert_attn_close(O[b:b + 1], O_ref, lse[b:b + 1], l_ref, "ragged seq %d" % b)
-    # the same batch over the benchmark's paged layout: identical results
-    wp = synth.WORKLOADS["decode_128k_paged"]
-    table, n_pages = wp.page_pool(0)
-    P = wp.page_size
-    per = w.n_k // P
-    perm = table.reshape(-1).cuda().long()
-    pools = {}
-    for name in ("k_idx", "K", "V"):
-        t = d[name]
-        pool = torch.zeros((n_pages, P) + tuple(t.shape[2:]), dtype=t.dtype, device="cuda")
-        pool[perm] = t.reshape((w.batch * per, P) + tuple(t.shape[2:]))
-        pools[name] = pool
-    say("full-size %s: paged forward" % wp.name)
-    idx_p, O_p, lse_p = dsa.forward_paged(d["q_idx"], pools["k_idx"], d["Q"], pools["K"],
-                                          pools["V"], table.cuda(), P, sp, w.top_k)
-    assert torch.equal(idx_p, idx)
-    assert torch.equal(O_p.view(torch.int16), O.view(torch.int16)) and torch.equal(lse_p, lse)
+    # the same batch over the benchmark's paged layouts (256- and 16-key
+    # pages): identical results
+    for wname in ("decode_128k_paged", "decode_128k_paged16"):
+        wp = synth.WORKLOADS[wname]
+        table, n_pages = wp.page_pool(0)
+        P = wp.page_size
+        per = w.n_k // P
+        perm = table.reshape(-1).cuda().long()
+        pools = {}
+        for name in ("k_idx", "K", "V"):
+            t = d[name]
+            pool = torch.zeros((n_pages, P) + tuple(t.shape[2:]), dtype=t.dtype, device="cuda")
+            pool[perm] = t.reshape((w.batch * per, P) + tuple(t.shape[2:]))
+            pools[name] = pool
+        say("full-size %s: paged forward" % wp.name)
+        idx_p, O_p, lse_p = dsa.forward_paged(d["q_idx"], pools["k_idx"], d["Q"], pools["K"],
+                                              pools["V"], table.cuda(), P, sp, w.top_k)
+        assert torch.equal(idx_p, idx), wname
+        assert torch.equal(O_p.view(torch.int16), O.view(torch.int16)), wname
+        assert torch.equal(lse_p, lse), wname
+        del pools, idx_p, O_p, lse_p
 
 
 def prefill_samples(L, k):
