@@ -52,10 +52,15 @@ def _load():
             lib.oracle_forward.argtypes = [I] * 9 + [P] * 5 + [I, I, P, P, P]
             lib.oracle_forward_seqpos.argtypes = [I, I, I, P] + [I] * 5 + [P] * 5 + [I, I, P,
                                                                                   P, P]
+            F = ctypes.c_float
+            lib.oracle_select_threshold.argtypes = [I, I, I, I, I, F, P, P]
+            lib.oracle_forward_threshold.argtypes = ([I] * 7 + [F, I, I] + [P] * 5 +
+                                                     [I, I, P, P, P])
             lib.oracle_num_threads.argtypes = []
             for f in (lib.oracle_index_scores, lib.oracle_topk,
                       lib.oracle_sparse_attn, lib.oracle_forward,
-                      lib.oracle_forward_seqpos, lib.oracle_num_threads):
+                      lib.oracle_forward_seqpos, lib.oracle_select_threshold,
+                      lib.oracle_forward_threshold, lib.oracle_num_threads):
                 f.restype = I
             _lib = lib
     return _lib
@@ -122,6 +127,19 @@ def topk(scores: np.ndarray, pos_begin: int, k: int) -> np.ndarray:
     return out
 
 
+def select_threshold(scores: np.ndarray, pos_begin: int, k: int, tau: float) -> np.ndarray:
+    """Threshold-mode selection: per row the keys j <= pos scoring above tau
+    (fp32 compare), at most k of them (the highest, ties to the lower index);
+    [B, rows, k] int32, ascending, -1 padded."""
+    s = np.ascontiguousarray(scores, dtype=np.float32)
+    B, rows, n_k = s.shape
+    out = np.empty((B, rows, k), np.int32)
+    rc = _load().oracle_select_threshold(B, rows, n_k, pos_begin, k, float(np.float32(tau)),
+                                         _ptr(s), _ptr(out))
+    assert rc == 0, rc
+    return out
+
+
 def sparse_attn(Q, K, V, idx, want_lse: bool = True):
     """O [B, n_q, H, D] float32 and lse [B, n_q, H] float32 (or None)."""
     q, kk, vv = _raw(Q), _raw(K), _raw(V)
@@ -141,10 +159,11 @@ def sparse_attn(Q, K, V, idx, want_lse: bool = True):
 
 
 def forward(q_idx, k_idx, Q, K, V, q_pos0: int, k: int, q_begin: int = 0,
-            q_end=None, dtype=None, seq_pos=None):
+            q_end=None, dtype=None, seq_pos=None, tau=None):
     """All three stages for query rows [q_begin, q_end) of every sequence.
     With seq_pos (one int per sequence) query i of sequence b sits at
-    seq_pos[b] + i instead of q_pos0 + i.
+    seq_pos[b] + i instead of q_pos0 + i. With tau the selection runs in
+    threshold mode (select_threshold) instead of top-k.
 
     Returns (idx [B, rows, k] int32, O [B, rows, H, D] float32,
     lse [B, rows, H] float32)."""
@@ -158,6 +177,14 @@ def forward(q_idx, k_idx, Q, K, V, q_pos0: int, k: int, q_begin: int = 0,
     idx = np.empty((B, rows, k), np.int32)
     O = np.empty((B, rows, H, D), np.float32)
     lse = np.empty((B, rows, H), np.float32)
+    if tau is not None:
+        assert seq_pos is None, "threshold mode takes one q_pos0"
+        rc = _load().oracle_forward_threshold(B, n_q, n_k, q_pos0, d, _dtype_code(q_idx, dtype),
+                                              k, float(np.float32(tau)), H, D, _ptr(qi),
+                                              _ptr(ki), _ptr(q), _ptr(kk), _ptr(vv), q_begin,
+                                              q_end, _ptr(idx), _ptr(O), _ptr(lse))
+        assert rc == 0, rc
+        return idx, O, lse
     if seq_pos is not None:
         sp = np.ascontiguousarray(np.asarray(seq_pos, np.int32).reshape(B))
         rc = _load().oracle_forward_seqpos(B, n_q, n_k, _ptr(sp), d,

@@ -10,6 +10,9 @@
  *                runs over those keys only
  *   section 4.1  FP8 index stage, comparison-based selection, BF16 attention
  *   section 4.2  all query heads share one K/V set (MQA)
+ * Threshold-mode selection follows the sparse-attention explainer page
+ * (yunthe.com/news/469461.html), section 2.2: keys whose similarity exceeds
+ * a threshold are kept.
  * Readings where the page is silent (causal inclusion j <= pos, ties to the
  * lower key index, ascending output order with -1 padding, fp32 rounding of
  * the scale) are listed with the design notes of this repository.
@@ -130,6 +133,25 @@ static void topk_row(const float* row, int n_k, long pos, int k, cand_t* buf,
     for (int t = m; t < k; ++t) out[t] = -1;
 }
 
+/* Threshold-mode selection of one row. The sparse-attention explainer page
+ * (yunthe.com/news/469461.html, section 2.2) keeps, for each query, the keys
+ * whose similarity exceeds a threshold; here the similarity is the indexer
+ * score and the kept set is bounded by the k output slots: the candidates
+ * j <= pos with score > tau, and when more than k of them pass, the first k
+ * under the total order above. Written in ascending j, the rest -1. */
+static void thresh_row(const float* row, int n_k, long pos, int k, float tau, cand_t* buf,
+                       int32_t* out) {
+    int n = (int)(pos + 1 < n_k ? pos + 1 : n_k);
+    int c = 0;
+    for (int j = 0; j < n; ++j)
+        if (row[j] > tau) { buf[c].s = row[j]; buf[c].j = j; ++c; }
+    qsort(buf, (size_t)c, sizeof(cand_t), cmp_rank);
+    int m = c < k ? c : k;
+    for (int t = 0; t < m; ++t) out[t] = buf[t].j;
+    qsort(out, (size_t)m, sizeof(int32_t), cmp_int);
+    for (int t = m; t < k; ++t) out[t] = -1;
+}
+
 /* idx[b][r][0..k) for score rows scores[b][r][0..n_k) whose query sits at
  * position pos_begin + r. Returns 0, -1 on bad sizes, -2 on no memory. */
 int oracle_topk(int B, int rows, int n_k, int pos_begin, int k,
@@ -150,6 +172,32 @@ int oracle_topk(int B, int rows, int n_k, int pos_begin, int k,
             int r = (int)(t % rows);
             topk_row(scores + (size_t)t * n_k, n_k, (long)pos_begin + r, k, buf,
                      idx + (size_t)t * k);
+        }
+        free(buf);
+    }
+    return fail ? -2 : 0;
+}
+
+/* oracle_topk in threshold mode (thresh_row): the keys scoring above tau, at
+ * most k per row. */
+int oracle_select_threshold(int B, int rows, int n_k, int pos_begin, int k, float tau,
+                            const float* scores, int32_t* idx) {
+    if (B < 0 || rows < 0 || n_k < 0 || k < 1 || pos_begin < 0) return -1;
+    const long total = (long)B * rows;
+    int fail = 0;
+#pragma omp parallel
+    {
+        cand_t* buf = (cand_t*)malloc(sizeof(cand_t) * (size_t)(n_k > 0 ? n_k : 1));
+        if (!buf) {
+#pragma omp atomic write
+            fail = 1;
+        }
+#pragma omp for schedule(dynamic, 4)
+        for (long t = 0; t < total; ++t) {
+            if (!buf) continue;
+            int r = (int)(t % rows);
+            thresh_row(scores + (size_t)t * n_k, n_k, (long)pos_begin + r, k, tau, buf,
+                       idx + (size_t)t * k);
         }
         free(buf);
     }
@@ -234,9 +282,10 @@ int oracle_sparse_attn(int B, int n_q, int n_k, int H, int D, int k,
  * the DSA page, section 4.3: index, select, attend), without materialising
  * the full score matrix. Only query rows [q_begin, q_end) of each sequence are
  * computed; idx/O/lse are laid out [B][q_end-q_begin][...]. idx and lse may be
- * NULL. */
+ * NULL. A non-NULL tau selects in threshold mode (thresh_row). */
 static int forward_rows(int B, int n_q, int n_k, int q_pos0, const int32_t* seq_pos, int d,
-                        int dtype, int k, int H, int D, const void* q_idx, const void* k_idx,
+                        int dtype, int k, const float* tau, int H, int D, const void* q_idx,
+                        const void* k_idx,
                         const uint16_t* Q, const uint16_t* K, const uint16_t* V,
                         int q_begin, int q_end, int32_t* idx, float* O, float* lse) {
     if (B < 0 || n_q < 0 || n_k < 0 || d <= 0 || k < 1 || H < 1 || D < 1 ||
@@ -269,7 +318,8 @@ static int forward_rows(int B, int n_q, int n_k, int q_pos0, const int32_t* seq_
                 srow[j] = j > pos ? -INFINITY
                                   : index_score(q_idx, k_idx, dtype, qoff,
                                                 ((size_t)b * n_k + j) * d, d, scale);
-            topk_row(srow, n_k, pos, k, buf, sel);
+            if (tau) thresh_row(srow, n_k, pos, k, *tau, buf, sel);
+            else topk_row(srow, n_k, pos, k, buf, sel);
             if (idx) memcpy(idx + (size_t)t * k, sel, sizeof(int32_t) * (size_t)k);
             attn_row(H, D, n_k, k, Q + (((size_t)b * n_q + i) * H) * D,
                      K + (size_t)b * n_k * D, V + (size_t)b * n_k * D, sel, z, acc,
@@ -284,8 +334,18 @@ int oracle_forward(int B, int n_q, int n_k, int q_pos0, int d, int dtype, int k,
                    int H, int D, const void* q_idx, const void* k_idx,
                    const uint16_t* Q, const uint16_t* K, const uint16_t* V,
                    int q_begin, int q_end, int32_t* idx, float* O, float* lse) {
-    return forward_rows(B, n_q, n_k, q_pos0, NULL, d, dtype, k, H, D, q_idx, k_idx, Q, K, V,
-                        q_begin, q_end, idx, O, lse);
+    return forward_rows(B, n_q, n_k, q_pos0, NULL, d, dtype, k, NULL, H, D, q_idx, k_idx, Q,
+                        K, V, q_begin, q_end, idx, O, lse);
+}
+
+/* oracle_forward with threshold-mode selection: each query attends to the
+ * keys whose indexer score exceeds tau, at most k of them (thresh_row). */
+int oracle_forward_threshold(int B, int n_q, int n_k, int q_pos0, int d, int dtype, int k,
+                             float tau, int H, int D, const void* q_idx, const void* k_idx,
+                             const uint16_t* Q, const uint16_t* K, const uint16_t* V,
+                             int q_begin, int q_end, int32_t* idx, float* O, float* lse) {
+    return forward_rows(B, n_q, n_k, q_pos0, NULL, d, dtype, k, &tau, H, D, q_idx, k_idx, Q,
+                        K, V, q_begin, q_end, idx, O, lse);
 }
 
 /* oracle_forward for a batch whose sequences sit at different positions:
@@ -297,8 +357,8 @@ int oracle_forward_seqpos(int B, int n_q, int n_k, const int32_t* seq_pos, int d
                           const uint16_t* Q, const uint16_t* K, const uint16_t* V,
                           int q_begin, int q_end, int32_t* idx, float* O, float* lse) {
     if (!seq_pos) return -1;
-    return forward_rows(B, n_q, n_k, 0, seq_pos, d, dtype, k, H, D, q_idx, k_idx, Q, K, V,
-                        q_begin, q_end, idx, O, lse);
+    return forward_rows(B, n_q, n_k, 0, seq_pos, d, dtype, k, NULL, H, D, q_idx, k_idx, Q, K,
+                        V, q_begin, q_end, idx, O, lse);
 }
 
 /* Threads an OpenMP parallel region of this library runs with. */

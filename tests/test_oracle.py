@@ -228,6 +228,96 @@ def test_worked_example():
     assert np.allclose(lse[0, :, 0], lse_exp, atol=1e-7)
 
 
+def brute_threshold(scores, pos_begin, k, tau):
+    # Python list work only: the keys j <= pos scoring above tau, the highest
+    # k of them (ties to the lower index), ascending, -1 padded.
+    B, rows, n_k = scores.shape
+    out = np.full((B, rows, k), -1, np.int32)
+    t = float(np.float32(tau))
+    for b in range(B):
+        for r in range(rows):
+            n = min(pos_begin + r + 1, n_k)
+            row = [float(v) for v in scores[b, r, :n]]
+            cand = [j for j in range(n) if row[j] > t]
+            keep = sorted(sorted(cand, key=lambda j: (-row[j], j))[:k])
+            out[b, r, :len(keep)] = keep
+    return out
+
+
+@pytest.mark.parametrize("k", [1, 3, 40, 64])
+@pytest.mark.parametrize("tau", [-1.0, 0.0, 0.25, 0.5, 1.0, 10.0])
+def test_threshold_vs_brute(k, tau):
+    g = np.random.default_rng(k * 7 + int(tau * 4) + 100)
+    B, rows, n_k, pos_begin = 2, 23, 64, 41
+    s = (g.integers(0, 6, (B, rows, n_k)) * 0.25).astype(np.float32)  # ties at every level
+    for r in range(rows):
+        s[:, r, pos_begin + r + 1:] = -np.inf
+    got = oracle.select_threshold(s, pos_begin, k, tau)
+    assert np.array_equal(got, brute_threshold(s, pos_begin, k, tau))
+
+
+def test_threshold_special_cases():
+    w = synth.WORKLOADS["prefill_1k"].replace(n_q=200, n_k=200, top_k=32)
+    x = synth.make_inputs(w, parts=("q_idx", "k_idx"))
+    s = oracle.index_scores(x["q_idx"], x["k_idx"], 0)
+    # scores are >= 0 after the ReLU: a negative tau passes every key and the
+    # selection is the (separately pinned) top-k
+    assert np.array_equal(oracle.select_threshold(s, 0, 32, -0.5), oracle.topk(s, 0, 32))
+    assert np.array_equal(oracle.select_threshold(s, 0, 32, -0.5), brute_topk(s, 0, 32))
+    # a tau at or above the largest score keeps nothing
+    top = float(s[np.isfinite(s)].max())
+    assert np.all(oracle.select_threshold(s, 0, 32, top) == -1)
+    # with as many slots as keys, the selection is exactly {j <= pos : S_j > tau}
+    tau = float(np.quantile(s[np.isfinite(s)], 0.9))
+    got = oracle.select_threshold(s, 0, 200, tau)
+    for r in range(200):
+        exp = np.nonzero(s[0, r, :r + 1] > np.float32(tau))[0]
+        assert np.array_equal(got[0, r, :len(exp)], exp) and np.all(got[0, r, len(exp):] == -1)
+    # fewer slots: the kept keys are the highest-scoring of those sets
+    got8 = oracle.select_threshold(s, 0, 8, tau)
+    for r in range(200):
+        full = got[0, r][got[0, r] >= 0]
+        part = got8[0, r][got8[0, r] >= 0]
+        assert set(part) <= set(full) and len(part) == min(8, len(full))
+        if len(part) < len(full):
+            rest = sorted(set(full) - set(part))
+            assert s[0, r, part].min() >= s[0, r, rest].max()
+
+
+def test_threshold_worked_example():
+    ex = json.load(open(os.path.join(GOLDEN, "worked_example_d4.json")))
+    q = torch.tensor([ex["q_idx"]], dtype=torch.float32).to(torch.float8_e4m3fn)
+    k = torch.tensor([ex["k_idx"]], dtype=torch.float32).to(torch.float8_e4m3fn)
+    s = oracle.index_scores(q, k, ex["q_pos0"])
+    th = ex["threshold"]
+    for case in th["cases"]:
+        got = oracle.select_threshold(s, 0, case["top_k"], float(case["tau"]))[0]
+        assert got.tolist() == case["idx"], case["why"]
+    att = th["attention"]
+    V = torch.tensor([ex["attention"]["V"]], dtype=torch.bfloat16)
+    Q = torch.zeros((1, 4, att["Q_zero_heads"], 2), dtype=torch.bfloat16)
+    idx, O, lse = oracle.forward(q, k, Q, V, V, 0, att["top_k"], tau=float(att["tau"]))
+    assert np.array_equal(O[0, :, 0], np.array(att["O"], np.float32))
+    lse_exp = [{"-inf": -math.inf, "0": 0.0, "ln2": math.log(2)}[v] for v in att["lse"]]
+    assert np.allclose(lse[0, :, 0], lse_exp, atol=1e-7)
+
+
+def test_forward_threshold_is_the_stages():
+    w = synth.WORKLOADS["prefill_1k"].replace(n_q=200, n_k=200, top_k=32, n_heads=2)
+    x = synth.make_inputs(w)
+    s = oracle.index_scores(x["q_idx"], x["k_idx"], 0)
+    tau = float(np.quantile(s[np.isfinite(s)], 0.8))
+    idx, O, lse = oracle.forward(x["q_idx"], x["k_idx"], x["Q"], x["K"], x["V"], 0, 32, tau=tau)
+    idx2 = oracle.select_threshold(s, 0, 32, tau)
+    O2, lse2 = oracle.sparse_attn(x["Q"], x["K"], x["V"], idx2)
+    assert np.array_equal(idx, idx2)
+    assert np.array_equal(O, O2) and np.array_equal(lse, lse2)
+    # a negative tau gives the top-k forward
+    i3, O3, l3 = oracle.forward(x["q_idx"], x["k_idx"], x["Q"], x["K"], x["V"], 0, 32, tau=-1.0)
+    i4, O4, l4 = oracle.forward(x["q_idx"], x["k_idx"], x["Q"], x["K"], x["V"], 0, 32)
+    assert np.array_equal(i3, i4) and np.array_equal(O3, O4) and np.array_equal(l3, l4)
+
+
 def dense_attn_torch(Q, K, V, q_pos0):
     """Dense MQA attention with the causal mask, through torch's
     scaled_dot_product_attention in float64 (K/V expanded to every head)."""
