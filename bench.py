@@ -90,7 +90,7 @@ def cpu_baseline(w, x, target_s=12.0, seed=0):
             if not w.ragged:
                 xs = {k: v[:nseq] for k, v in x.items()}
                 oracle.forward(xs["q_idx"], xs["k_idx"], xs["Q"], xs["K"], xs["V"], w.q_pos0,
-                               w.top_k)
+                               w.top_k, tau=w.tau)
                 return nseq
             xs = {k: v[:nseq] for k, v in x.items()}  # each sequence at its own position
             oracle.forward(xs["q_idx"], xs["k_idx"], xs["Q"], xs["K"], xs["V"], 0, w.top_k,
@@ -120,7 +120,7 @@ def cpu_baseline(w, x, target_s=12.0, seed=0):
         q = 0
         for r in rows:
             oracle.forward(x["q_idx"], x["k_idx"], x["Q"], x["K"], x["V"], w.q_pos0, w.top_k,
-                           r, min(r + nthreads, w.n_q))
+                           r, min(r + nthreads, w.n_q), tau=w.tau)
             q += min(r + nthreads, w.n_q) - r
             if time.perf_counter() - t0 > target_s:
                 break
@@ -138,6 +138,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_128k_clustered")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--tau", type=float, default=None,
+                    help="threshold-mode selection at this tau (default: the workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stages", action="store_true",
                     help="skip the per-stage timing loops")
@@ -161,6 +163,8 @@ def main():
     from dsa_top_token_amd import synth
 
     w = synth.WORKLOADS[args.workload]
+    if args.tau is not None:
+        w = w.replace(tau=args.tau)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     x = synth.make_inputs(w, seed=args.seed)  # canonical CPU draw
@@ -190,7 +194,8 @@ def main():
     lse = torch.empty((w.batch, w.n_q, w.n_heads), dtype=torch.float32, device=dev)
 
     def step():
-        fwd(d["q_idx"], d["k_idx"], d["Q"], d["K"], d["V"], O, idx, lse, seq_pos=sp, pages=pages)
+        fwd(d["q_idx"], d["k_idx"], d["Q"], d["K"], d["V"], O, idx, lse, seq_pos=sp, pages=pages,
+            tau=w.tau)
 
     for _ in range(args.warmup):
         step()
@@ -215,7 +220,7 @@ def main():
         slabs = 1
         for _ in range(n_rep):
             ms3, slabs = fwd.timed(d["q_idx"], d["k_idx"], d["Q"], d["K"], d["V"], O, idx, lse,
-                                   seq_pos=sp, pages=pages)
+                                   seq_pos=sp, pages=pages, tau=w.tau)
             tot = [a + b for a, b in zip(tot, ms3)]
         stages = {n: t / n_rep for n, t in zip(names, tot)}
         dom = max(stages, key=stages.get)
@@ -259,6 +264,10 @@ def main():
         pos = w.positions(args.seed)
         out["config"]["ragged"] = {"positions": "seeded, uniform in [n_k/8, n_k-1]",
                                    "mean_len": round(sum(p + 1 for p in pos) / len(pos), 1)}
+    if w.tau is not None:
+        kept = (idx >= 0).sum(-1).float()
+        out["config"]["threshold"] = {"tau": w.tau, "kept_mean": round(float(kept.mean()), 1),
+                                      "kept_min": int(kept.min()), "kept_max": int(kept.max())}
     if w.page_size:
         out["config"]["paged"] = {"page_size": w.page_size, "pool": "shuffled, 16 spare pages"}
     print(json.dumps(out))

@@ -30,8 +30,8 @@ HEAD_DIM = 128
 
 EXPORTS = ("dsa_workspace_size", "dsa_index_scores", "dsa_topk", "dsa_sparse_attn",
            "dsa_forward", "dsa_forward_ragged", "dsa_forward_paged", "dsa_forward_timed",
-           "dsa_forward_ragged_timed", "dsa_forward_paged_timed", "dsa_status_str",
-           "dsa_last_error")
+           "dsa_forward_ragged_timed", "dsa_forward_paged_timed", "dsa_forward_threshold",
+           "dsa_forward_threshold_timed", "dsa_status_str", "dsa_last_error")
 
 
 class Problem(ctypes.Structure):
@@ -81,10 +81,15 @@ def load():
             lib.dsa_forward_paged.argtypes = [PP, P, PG, P, P, P, P, P, P, P, P, P, S, P]
             lib.dsa_forward_paged_timed.argtypes = [PP, P, PG, P, P, P, P, P, P, P, P, P, S, P,
                                                     P, P]
+            F = ctypes.c_float
+            lib.dsa_forward_threshold.argtypes = [PP, F, P, P, P, P, P, P, P, P, P, S, P]
+            lib.dsa_forward_threshold_timed.argtypes = [PP, F, P, P, P, P, P, P, P, P, P, S, P,
+                                                        P, P]
             for f in (lib.dsa_workspace_size, lib.dsa_index_scores, lib.dsa_topk,
                       lib.dsa_sparse_attn, lib.dsa_forward, lib.dsa_forward_ragged,
                       lib.dsa_forward_paged, lib.dsa_forward_timed,
-                      lib.dsa_forward_ragged_timed, lib.dsa_forward_paged_timed):
+                      lib.dsa_forward_ragged_timed, lib.dsa_forward_paged_timed,
+                      lib.dsa_forward_threshold, lib.dsa_forward_threshold_timed):
                 f.restype = I
             lib.dsa_status_str.argtypes = [I]
             lib.dsa_status_str.restype = ctypes.c_char_p
@@ -198,11 +203,20 @@ class Forward:
         self.ws, self.ws_bytes = _workspace(problem, OP_FORWARD, self.device)
 
     def __call__(self, q_idx, k_idx, Q, K, V, O, idx_out=None, lse=None, seq_pos=None,
-                 pages=None):
+                 pages=None, tau=None):
         """seq_pos (int32 [B] on the device): a ragged decode batch through
         dsa_forward_ragged (the problem has n_q = 1 and q_pos0 = 0); with
         pages (a Pages), k_idx, K and V are the page pools
-        (dsa_forward_paged)."""
+        (dsa_forward_paged); with tau (a float), threshold-mode selection
+        (dsa_forward_threshold)."""
+        if tau is not None:
+            if seq_pos is not None or pages is not None:
+                raise ValueError("threshold mode takes the contiguous dsa_forward layout")
+            _check(load().dsa_forward_threshold(
+                ctypes.byref(self.p), float(tau), _ptr(q_idx), _ptr(k_idx), _ptr(Q), _ptr(K),
+                _ptr(V), _ptr(idx_out), _ptr(O), _ptr(lse), _ptr(self.ws), self.ws_bytes,
+                _stream(self.device)))
+            return
         if pages is not None:
             _check(load().dsa_forward_paged(
                 ctypes.byref(self.p), _ptr(seq_pos), ctypes.byref(pages), _ptr(q_idx),
@@ -220,13 +234,21 @@ class Forward:
                                   _ptr(self.ws), self.ws_bytes, _stream(self.device)))
 
     def timed(self, q_idx, k_idx, Q, K, V, O, idx_out=None, lse=None, seq_pos=None,
-              pages=None):
+              pages=None, tau=None):
         """Run once through dsa_forward_timed (dsa_forward_ragged_timed with
-        seq_pos, dsa_forward_paged_timed with pages); returns ([indexer,
-        top-k, attention] milliseconds, number of row slabs). Blocks until
-        done."""
+        seq_pos, dsa_forward_paged_timed with pages,
+        dsa_forward_threshold_timed with tau); returns ([indexer, top-k,
+        attention] milliseconds, number of row slabs). Blocks until done."""
         ms = (ctypes.c_float * 3)()
         slabs = ctypes.c_int32(0)
+        if tau is not None:
+            if seq_pos is not None or pages is not None:
+                raise ValueError("threshold mode takes the contiguous dsa_forward layout")
+            _check(load().dsa_forward_threshold_timed(
+                ctypes.byref(self.p), float(tau), _ptr(q_idx), _ptr(k_idx), _ptr(Q), _ptr(K),
+                _ptr(V), _ptr(idx_out), _ptr(O), _ptr(lse), _ptr(self.ws), self.ws_bytes,
+                _stream(self.device), ms, ctypes.byref(slabs)))
+            return list(ms), slabs.value
         if pages is not None:
             _check(load().dsa_forward_paged_timed(
                 ctypes.byref(self.p), _ptr(seq_pos), ctypes.byref(pages), _ptr(q_idx),
@@ -246,11 +268,13 @@ class Forward:
         return list(ms), slabs.value
 
 
-def forward(q_idx, k_idx, Q, K, V, q_pos0, top_k, want_idx=True, want_lse=True, seq_pos=None):
+def forward(q_idx, k_idx, Q, K, V, q_pos0, top_k, want_idx=True, want_lse=True, seq_pos=None,
+            tau=None):
     """The fused chain. Returns (idx [B,n_q,top_k] int32 or None,
     O [B,n_q,H,128] bf16, lse [B,n_q,H] float32 or None). With seq_pos (int32
     [B] on the device; n_q = 1, q_pos0 = 0) the batch is ragged: the query of
-    sequence b sits at position seq_pos[b]."""
+    sequence b sits at position seq_pos[b]. With tau the selection runs in
+    threshold mode: the keys scoring above tau, at most top_k of them."""
     _dev_tensor(q_idx, "q_idx", _IDX_DTYPES, 3)
     _dev_tensor(k_idx, "k_idx", (q_idx.dtype,), 3)
     _dev_tensor(Q, "Q", (torch.bfloat16,), 4)
@@ -268,7 +292,7 @@ def forward(q_idx, k_idx, Q, K, V, q_pos0, top_k, want_idx=True, want_lse=True, 
         _dev_tensor(seq_pos, "seq_pos", (torch.int32,), 1)
         if seq_pos.shape[0] != B:
             raise ValueError("seq_pos must have one entry per sequence")
-    Forward(p, dev)(q_idx, k_idx, Q, K, V, O, idx, lse, seq_pos=seq_pos)
+    Forward(p, dev)(q_idx, k_idx, Q, K, V, O, idx, lse, seq_pos=seq_pos, tau=tau)
     return idx, O, lse
 
 

@@ -10,7 +10,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libdsa.so")
-SOURCES = ["indexer.hip", "topk.hip", "decode.hip", "prefill.hip", "attn.hip", "api.cpp"]
+SOURCES = ["indexer.hip", "topk.hip", "decode.hip", "prefill.hip", "attn.hip", "threshold.hip",
+           "api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 CFLAGS = [

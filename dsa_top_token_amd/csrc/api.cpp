@@ -228,7 +228,7 @@ dsa_status forward_impl(const dsa_problem* p, const void* q_idx, const void* k_i
                         const void* Q, const void* K, const void* V, int32_t* idx_out, void* O,
                         float* lse, void* ws, size_t ws_bytes, void* stream, StageTimer* tm,
                         int32_t* n_slabs, const int32_t* seq_pos = nullptr,
-                        const dsa::KeyPages* pages = nullptr) {
+                        const dsa::KeyPages* pages = nullptr, const float* tau = nullptr) {
     dsa_status s = check_problem(p);
     if (s != DSA_OK) return s;
     if ((s = check_ptrs({q_idx, k_idx, Q, K, V, O}, "q_idx, k_idx, Q, K, V, O")) != DSA_OK)
@@ -355,6 +355,24 @@ dsa_status forward_impl(const dsa_problem* p, const void* q_idx, const void* k_i
         if (tm) tm->mark(1);
         e = dsa::launch_topk(ta, st);
         if (e != hipSuccess) return hip_fail(e, "topk launch");
+    }
+    if (tau) {
+        // threshold mode: drop the selected keys scoring at or below tau
+        dsa::FloorArgs fa{};
+        fa.q = q_idx;
+        fa.k = k_idx;
+        fa.idx = idx;
+        fa.B = p->batch;
+        fa.n_q = p->n_q;
+        fa.n_k = p->n_k;
+        fa.d = p->d_idx;
+        fa.dtype = p->idx_dtype;
+        fa.top_k = p->top_k;
+        fa.scale = index_scale(p->d_idx);
+        fa.tau = *tau;
+        if (tm) tm->mark(1);
+        hipError_t e = dsa::launch_threshold_floor(fa, st);
+        if (e != hipSuccess) return hip_fail(e, "threshold launch");
     }
     if (tm) tm->mark(2);
     dsa::AttnArgs aa = attn_args(p, Q, K, V, idx, O, lse, w + L.part);
@@ -573,6 +591,32 @@ dsa_status dsa_forward_paged_timed(const dsa_problem* p, const int32_t* seq_pos,
     for (int i = 0; i < 3; ++i) stage_ms[i] = 0.f;
     s = forward_impl(p, q_idx, k_pool, Q, K_pool, V_pool, idx_out, O, lse, ws, ws_bytes, stream,
                      &tm, n_slabs, seq_pos, &kp);
+    hipError_t e = tm.finish(stage_ms);
+    if (s != DSA_OK) return s;
+    if (e != hipSuccess) return hip_fail(e, "stage timing events");
+    return ok();
+}
+
+dsa_status dsa_forward_threshold(const dsa_problem* p, float tau, const void* q_idx,
+                                 const void* k_idx, const void* Q, const void* K, const void* V,
+                                 int32_t* idx_out, void* O, float* lse, void* ws,
+                                 size_t ws_bytes, void* stream) {
+    dsa_status s = forward_impl(p, q_idx, k_idx, Q, K, V, idx_out, O, lse, ws, ws_bytes, stream,
+                                nullptr, nullptr, nullptr, nullptr, &tau);
+    return s == DSA_OK ? ok() : s;
+}
+
+dsa_status dsa_forward_threshold_timed(const dsa_problem* p, float tau, const void* q_idx,
+                                       const void* k_idx, const void* Q, const void* K,
+                                       const void* V, int32_t* idx_out, void* O, float* lse,
+                                       void* ws, size_t ws_bytes, void* stream, float* stage_ms,
+                                       int32_t* n_slabs) {
+    if (!stage_ms) return fail(DSA_E_NULL, "stage_ms is NULL");
+    StageTimer tm;
+    tm.st = static_cast<hipStream_t>(stream);
+    for (int i = 0; i < 3; ++i) stage_ms[i] = 0.f;
+    dsa_status s = forward_impl(p, q_idx, k_idx, Q, K, V, idx_out, O, lse, ws, ws_bytes, stream,
+                                &tm, n_slabs, nullptr, nullptr, &tau);
     hipError_t e = tm.finish(stage_ms);
     if (s != DSA_OK) return s;
     if (e != hipSuccess) return hip_fail(e, "stage timing events");

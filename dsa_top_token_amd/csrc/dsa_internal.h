@@ -175,6 +175,20 @@ size_t decode_select_ws_bytes(int B, int n_k);
 // part 0: sampled threshold, 1: indexer + filter, 2: exact select.
 hipError_t launch_decode_select(DecodeArgs a, void* ws, int part, hipStream_t s);
 
+// Threshold mode: removes from finished top-k lists [B][n_q][top_k] (one row
+// per query, ascending, -1 padded) every key whose indexer score is not above
+// tau, keeping the survivors in order and padding with -1.
+constexpr int kFloorMaxK = 4096;
+struct FloorArgs {
+    const void* q;      // [B][n_q][d] fp8 e4m3fn or bf16
+    const void* k;      // [B][n_k][d]
+    int32_t* idx;       // [B][n_q][top_k], rewritten in place
+    int B, n_q, n_k, d, dtype, top_k;
+    float scale;        // fl32(d^-0.5)
+    float tau;
+};
+hipError_t launch_threshold_floor(const FloorArgs& a, hipStream_t s);
+
 // Split plan of the attention: splits per query and entries per split.
 void attn_split_plan(int B, int n_q, int k, int* n_split, int* split_len);
 

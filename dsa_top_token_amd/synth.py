@@ -51,6 +51,7 @@ class Workload:
     clustered: bool = False
     ragged: bool = False  # decode only: per-sequence query positions (positions())
     page_size: int = 0    # > 0: k_idx, K, V stored in shuffled pages of this many keys
+    tau: Optional[float] = None  # threshold-mode selection: keys scoring above tau, <= top_k
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -118,6 +119,11 @@ WORKLOADS["decode_128k_paged"] = WORKLOADS["decode_128k_ragged"].replace(
     name="decode_128k_paged", page_size=256)
 WORKLOADS["decode_128k_paged16"] = WORKLOADS["decode_128k_ragged"].replace(
     name="decode_128k_paged16", page_size=16)
+# The clustered 128K decode batch in threshold mode: tau = 14 keeps from about
+# 200 to several thousand keys per query on these inputs, so some rows keep
+# all their passing keys and others are cut to the top_k highest.
+WORKLOADS["decode_128k_threshold"] = WORKLOADS["decode_128k_clustered"].replace(
+    name="decode_128k_threshold", tau=14.0)
 
 
 def _gen(seed: int, tid: str, device) -> torch.Generator:

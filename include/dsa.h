@@ -26,7 +26,7 @@
  *     with a sentence in dsa_last_error(). A failed HIP launch returns
  *     DSA_E_HIP. Device faults surface at the caller's synchronisation.
  *   - No call blocks the host or synchronises the stream, except the
- *     profiling variant dsa_forward_timed.
+ *     profiling variants (dsa_forward_timed and the other *_timed calls).
  */
 #ifndef DSA_H
 #define DSA_H
@@ -189,6 +189,34 @@ dsa_status dsa_forward_paged_timed(const dsa_problem* p, const int32_t* seq_pos,
                                    int32_t* idx_out, void* O, float* lse,
                                    void* ws, size_t ws_bytes, void* stream,
                                    float* stage_ms, int32_t* n_slabs);
+
+/* dsa_forward with threshold-mode selection. The sparse-attention explainer
+ * page (yunthe.com/news/469461.html), section 2.2, keeps for each query the
+ * keys whose similarity exceeds a threshold; here the similarity is the
+ * indexer score S (DSA page, section 3.2) and top_k bounds the kept set:
+ * query i keeps {j <= pos(i) : S_j > tau} (a float32 comparison, strict), and
+ * when more than top_k keys pass, the top_k highest of them (ties to the lower
+ * key index), which is the top-k selection of dsa_forward with the entries
+ * scoring <= tau removed. idx_out rows list the kept keys in ascending order,
+ * -1 padded (a query may keep none: O = 0, lse = -inf). Since S >= 0, a
+ * negative tau gives dsa_forward's results; a NaN tau keeps nothing. Same
+ * layouts, workspace and errors as dsa_forward. */
+dsa_status dsa_forward_threshold(const dsa_problem* p, float tau,
+                                 const void* q_idx, const void* k_idx,
+                                 const void* Q, const void* K, const void* V,
+                                 int32_t* idx_out, void* O, float* lse,
+                                 void* ws, size_t ws_bytes, void* stream);
+
+/* dsa_forward_threshold for profiling, as dsa_forward_timed (the threshold
+ * pass counts as top-k time; blocks until the stream has finished; stage_ms
+ * must not be NULL). */
+dsa_status dsa_forward_threshold_timed(const dsa_problem* p, float tau,
+                                       const void* q_idx, const void* k_idx,
+                                       const void* Q, const void* K,
+                                       const void* V, int32_t* idx_out, void* O,
+                                       float* lse, void* ws, size_t ws_bytes,
+                                       void* stream, float* stage_ms,
+                                       int32_t* n_slabs);
 
 /* dsa_forward for profiling: the same work and results, plus the device time
  * of each stage. HIP events are recorded on `stream` around the indexer

@@ -106,6 +106,22 @@ def test_ragged_forward_arguments():
                                   FAKE, None, FAKE, need - 1, None) == -5
 
 
+def test_threshold_forward_arguments():
+    lib = dsa.load()
+    dec = prob(n_q=1, n_k=64, q_pos0=63)
+    need = dsa.workspace_size(dec, dsa.OP_FORWARD)
+    args = lambda ws=FAKE, n=need: (FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, ws, n, None)
+    assert lib.dsa_forward_threshold(None, 0.5, *args()) == -1
+    assert lib.dsa_forward_threshold(ctypes.byref(dec), 0.5, None, *args()[1:]) == -1
+    assert lib.dsa_forward_threshold(ctypes.byref(prob(top_k=5000)), 0.5, *args()) == -3
+    assert lib.dsa_forward_threshold(ctypes.byref(dec), 0.5, *args(n=need - 1)) == -5
+    assert lib.dsa_forward_threshold(ctypes.byref(dec), 0.5, *args(ws=ODD)) == -4
+    ms = (ctypes.c_float * 3)()
+    assert lib.dsa_forward_threshold_timed(ctypes.byref(dec), 0.5, *args(), None, None) == -1
+    assert lib.dsa_forward_threshold_timed(ctypes.byref(dec), 0.5, *args(n=need - 1), ms,
+                                           None) == -5
+
+
 def test_paged_forward_arguments():
     lib = dsa.load()
     dec = prob(n_q=1, n_k=512, q_pos0=0)

@@ -396,6 +396,61 @@ def test_paged_threshold_miss_falls_back(gpu_lib):
         assert_attn_close(O[b:b + 1], O_ref, lse[b:b + 1], l_ref, "paged miss seq %d" % b)
 
 
+# Threshold mode: each workload at several tau, chosen from the oracle's
+# scores so that rows keep fewer keys than top_k, more (cut to top_k), none,
+# or all of them; a tau equal to a score checks the strict comparison.
+THRESH_W = [
+    synth.WORKLOADS["prefill_1k"],
+    Workload("thr_prefill_bf16_d160", "prefill", 1, 777, 777, 0, 160, "bf16", 100, 16),
+    Workload("thr_chunked_prefill", "prefill", 2, 50, 300, 250, 64, "fp8", 37, 3),
+    Workload("thr_decode_fp8_d96", "decode", 5, 1, 3001, 3000, 96, "fp8", 1024, 16),
+    Workload("thr_decode_20k", "decode", 3, 1, 20000, 19999, 128, "fp8", 2048, 16),
+    Workload("thr_decode_clustered", "decode", 2, 1, 40000, 39999, 128, "fp8", 1500, 16,
+             clustered=True),
+    Workload("thr_k4096_bf16_d256", "prefill", 2, 70, 70, 0, 256, "bf16", 4096, 4),
+]
+THRESH_MODES = ["q50", "q97", "at_kth", "zero", "negative", "above_max", "nan"]
+
+
+def pick_tau(s, mode, w):
+    fin = np.sort(s[np.isfinite(s)])
+    if mode == "q50":
+        return float(fin[len(fin) // 2])
+    if mode == "q97":
+        return float(fin[int(0.97 * (len(fin) - 1))])
+    if mode == "at_kth":
+        # the k-th highest score of the last row: equal scores must not pass
+        r = s[-1, -1][np.isfinite(s[-1, -1])]
+        return float(np.sort(r)[::-1][min(w.top_k, len(r)) - 1])
+    return {"zero": 0.0, "negative": -1.0, "above_max": float(fin[-1]),
+            "nan": float("nan")}[mode]
+
+
+@pytest.mark.parametrize("mode", THRESH_MODES)
+@pytest.mark.parametrize("w", THRESH_W, ids=lambda w: w.name)
+def test_forward_threshold_vs_oracle(gpu_lib, w, mode):
+    say("threshold %s %s" % (w.name, mode))
+    x = synth.make_inputs(w, seed=11)
+    s = oracle.index_scores(x["q_idx"], x["k_idx"], w.q_pos0)
+    tau = pick_tau(s, mode, w)
+    idx_ref, O_ref, lse_ref = oracle.forward(x["q_idx"], x["k_idx"], x["Q"], x["K"], x["V"],
+                                             w.q_pos0, w.top_k, tau=tau)
+    d = to_dev(x)
+    idx, O, lse = dsa.forward(d["q_idx"], d["k_idx"], d["Q"], d["K"], d["V"], w.q_pos0,
+                              w.top_k, tau=tau)
+    assert np.array_equal(idx.cpu().numpy(), idx_ref), (w.name, mode, tau)
+    assert_attn_close(O, O_ref, lse, lse_ref, "%s %s" % (w.name, mode))
+    if mode == "negative":
+        # every score is >= 0 > tau: the top-k forward, bit for bit
+        i2, O2, l2 = dsa.forward(d["q_idx"], d["k_idx"], d["Q"], d["K"], d["V"], w.q_pos0,
+                                 w.top_k)
+        assert torch.equal(idx, i2) and torch.equal(O.view(torch.int16), O2.view(torch.int16))
+        assert torch.equal(lse, l2)
+    if mode in ("above_max", "nan"):
+        assert torch.all(idx == -1) and torch.all(O.float() == 0)
+        assert torch.all(torch.isneginf(lse))
+
+
 def test_all_zero_query_selects_first_keys(gpu_lib):
     w = Workload("zeros", "prefill", 1, 600, 600, 0, 128, "fp8", 64, 2)
     x = synth.make_inputs(w, seed=6)
@@ -523,6 +578,29 @@ def test_full_decode_128k_ragged(gpu_lib):
         assert torch.equal(O_p.view(torch.int16), O.view(torch.int16)), wname
         assert torch.equal(lse_p, lse), wname
         del pools, idx_p, O_p, lse_p
+
+
+def test_full_decode_128k_threshold(gpu_lib):
+    # The benchmark's threshold-mode batch, every sequence against the oracle.
+    w = synth.WORKLOADS["decode_128k_threshold"]
+    say("full-size %s: generating inputs" % w.name)
+    x = synth.make_inputs(w, seed=0)
+    d = to_dev(x)
+    say("full-size %s: GPU forward" % w.name)
+    idx, O, lse = dsa.forward(d["q_idx"], d["k_idx"], d["Q"], d["K"], d["V"], w.q_pos0,
+                              w.top_k, tau=w.tau)
+    torch.cuda.synchronize()
+    kept = (idx >= 0).sum(-1).flatten().cpu().numpy()
+    say("full-size %s: kept keys per query min %d mean %.0f max %d" %
+        (w.name, kept.min(), kept.mean(), kept.max()))
+    assert kept.min() < w.top_k and kept.max() == w.top_k  # both regimes occur
+    for b0 in range(0, w.batch, 16):
+        say("full-size %s: oracle sequences %d-%d" % (w.name, b0, b0 + 16))
+        sl = {k: v[b0:b0 + 16] for k, v in x.items()}
+        idx_ref, O_ref, lse_ref = oracle.forward(sl["q_idx"], sl["k_idx"], sl["Q"], sl["K"],
+                                                 sl["V"], w.q_pos0, w.top_k, tau=w.tau)
+        assert np.array_equal(idx[b0:b0 + 16].cpu().numpy(), idx_ref), b0
+        assert_attn_close(O[b0:b0 + 16], O_ref, lse[b0:b0 + 16], lse_ref, "sequences %d+" % b0)
 
 
 def prefill_samples(L, k):
