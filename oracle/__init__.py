@@ -56,8 +56,11 @@ def _load():
             lib.oracle_select_threshold.argtypes = [I, I, I, I, I, F, P, P]
             lib.oracle_forward_threshold.argtypes = ([I] * 7 + [F, I, I] + [P] * 5 +
                                                      [I, I, P, P, P])
+            lib.oracle_index_project.argtypes = [I, I, I, I, P, P, P, I, P]
+            lib.oracle_encode.argtypes = [I, I, P, P]
             lib.oracle_num_threads.argtypes = []
-            for f in (lib.oracle_index_scores, lib.oracle_topk,
+            for f in (lib.oracle_index_project, lib.oracle_encode,
+                      lib.oracle_index_scores, lib.oracle_topk,
                       lib.oracle_sparse_attn, lib.oracle_forward,
                       lib.oracle_forward_seqpos, lib.oracle_select_threshold,
                       lib.oracle_forward_threshold, lib.oracle_num_threads):
@@ -99,6 +102,39 @@ def num_threads() -> int:
 
 def index_scale(d: int) -> float:
     return float(np.float32(_load().oracle_index_scale(d)))
+
+
+def encode(values, out_dtype: str) -> np.ndarray:
+    """float32 values -> e4m3fn codes (uint8, round to nearest even, saturating
+    at +-448) or bfloat16 codes (uint16, round to nearest even)."""
+    v = np.ascontiguousarray(np.asarray(values, np.float32).reshape(-1))
+    out = np.empty(v.shape, np.uint8 if out_dtype == "fp8" else np.uint16)
+    rc = _load().oracle_encode(v.size, 0 if out_dtype == "fp8" else 1, _ptr(v), _ptr(out))
+    assert rc == 0, rc
+    return out
+
+
+def index_project(X, W, out_dtype: str, out=None, out_rows=None) -> np.ndarray:
+    """Indexer projection rows: encode(fl32(X[r] . W[o])) for X [rows, d_model]
+    and W [d_idx, d_model] (bfloat16), written to row out_rows[r] (or r) of
+    out [n_out, d_idx] (raw uint8 / uint16 codes; a fresh zeroed array of
+    `rows` rows when out is None). Returns out."""
+    x, wt = _raw(X), _raw(W)
+    rows, d_model = x.shape
+    d_idx = wt.shape[0]
+    assert wt.shape == (d_idx, d_model)
+    code = np.uint8 if out_dtype == "fp8" else np.uint16
+    if out is None:
+        out = np.zeros((rows, d_idx), code)
+    assert out.dtype == code and out.shape[1] == d_idx and out.flags.c_contiguous
+    dst = None
+    if out_rows is not None:
+        dst = np.ascontiguousarray(np.asarray(out_rows, np.int32).reshape(rows))
+    rc = _load().oracle_index_project(rows, d_model, d_idx, 0 if out_dtype == "fp8" else 1,
+                                      _ptr(x), _ptr(wt), _ptr(dst) if dst is not None else None,
+                                      out.shape[0], _ptr(out))
+    assert rc == 0, rc
+    return out
 
 
 def index_scores(q_idx, k_idx, q_pos0: int, q_begin: int = 0, q_end=None,

@@ -57,6 +57,41 @@ static double dec_idx(const void* base, int dtype, size_t i) {
     return dec_bf16(((const uint16_t*)base)[i]);
 }
 
+/* Encoding a float32 value as e4m3fn: the nearest representable value, ties
+ * to the code with an even mantissa (its low bit 0), magnitudes beyond the
+ * largest finite value 448 saturating to +-448, NaN to the NaN code; the sign
+ * (also of a zero) is kept. The nearest code is found by bisection over the
+ * non-negative finite codes 0x00..0x7e, whose values increase with the code. */
+static uint8_t enc_e4m3fn_sat(float v) {
+    if (v != v) return 0x7f;
+    uint8_t s = signbit(v) ? 0x80 : 0x00;
+    double a = fabs((double)v);
+    if (a >= 448.0) return s | 0x7e;
+    int lo = 0, hi = 0x7e;               /* dec(lo) <= a < dec(hi) */
+    while (hi - lo > 1) {
+        int mid = (lo + hi) / 2;
+        if (dec_e4m3fn((uint8_t)mid) <= a) lo = mid;
+        else hi = mid;
+    }
+    double dl = a - dec_e4m3fn((uint8_t)lo), dh = dec_e4m3fn((uint8_t)hi) - a;
+    int c = dl < dh ? lo : dh < dl ? hi : ((lo & 1) ? hi : lo);
+    return s | (uint8_t)c;
+}
+
+/* Encoding a float32 value as bfloat16: of the two bfloat16 values around it
+ * (the upper half of its bits, and the next value away from zero) the nearer,
+ * ties to the even one; NaN to the quiet NaN 0x7fc0. */
+static uint16_t enc_bf16(float v) {
+    if (v != v) return 0x7fc0;
+    uint32_t u;
+    memcpy(&u, &v, 4);
+    uint16_t t = (uint16_t)(u >> 16);
+    if ((u & 0xffffu) == 0) return t;
+    double a = fabs((double)v);
+    double dl = a - fabs(dec_bf16(t)), dh = fabs(dec_bf16((uint16_t)(t + 1))) - a;
+    return dl < dh ? t : dh < dl ? (uint16_t)(t + 1) : ((t & 1) ? (uint16_t)(t + 1) : t);
+}
+
 /* The indexer's scale, dim^-0.5, evaluated in double as the page's Python
  * expression does and then rounded once to float32, the type the scores are
  * multiplied in. */
@@ -176,6 +211,52 @@ int oracle_topk(int B, int rows, int n_k, int pos_begin, int k,
         free(buf);
     }
     return fail ? -2 : 0;
+}
+
+/* The indexer projections (DSA page section 3.2: query_proj and key_proj are
+ * bias-free linear maps from the model width to the indexer width; section
+ * 4.1 runs the index stage in FP8): for each input row r,
+ *   y[o] = sum_c X[r][c] * W[o][c]      (W in nn.Linear's [d_idx][d_model] layout)
+ * accumulated in double, rounded to float32, then encoded as e4m3fn
+ * (enc_e4m3fn_sat) or bfloat16 (enc_bf16) into out row out_rows[r] (row r
+ * when out_rows is NULL) of out [n_out][d_idx]; other rows of out are left
+ * as they are (a decode step appends its new key rows to the cache this way).
+ * X [rows][d_model] and W are bfloat16 bit patterns. Returns 0, -1 on bad
+ * sizes or a destination row outside [0, n_out). */
+int oracle_index_project(int rows, int d_model, int d_idx, int out_dtype, const uint16_t* X,
+                         const uint16_t* W, const int32_t* out_rows, int n_out, void* out) {
+    if (rows < 0 || d_model < 1 || d_idx < 1 || n_out < 0 ||
+        (out_dtype != ORACLE_FP8_E4M3FN && out_dtype != ORACLE_BF16))
+        return -1;
+    for (int r = 0; r < rows; ++r) {
+        int dst = out_rows ? out_rows[r] : r;
+        if (dst < 0 || dst >= n_out) return -1;
+    }
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int r = 0; r < rows; ++r) {
+        int dst = out_rows ? out_rows[r] : r;
+        for (int o = 0; o < d_idx; ++o) {
+            double acc = 0.0;
+            for (int c = 0; c < d_model; ++c)
+                acc += dec_bf16(X[(size_t)r * d_model + c]) * dec_bf16(W[(size_t)o * d_model + c]);
+            float y = (float)acc;
+            if (out_dtype == ORACLE_FP8_E4M3FN)
+                ((uint8_t*)out)[(size_t)dst * d_idx + o] = enc_e4m3fn_sat(y);
+            else
+                ((uint16_t*)out)[(size_t)dst * d_idx + o] = enc_bf16(y);
+        }
+    }
+    return 0;
+}
+
+/* Encodings alone (for pinning them): n float32 values to e4m3fn or bf16. */
+int oracle_encode(int n, int out_dtype, const float* v, void* out) {
+    if (n < 0 || (out_dtype != ORACLE_FP8_E4M3FN && out_dtype != ORACLE_BF16)) return -1;
+    for (int i = 0; i < n; ++i) {
+        if (out_dtype == ORACLE_FP8_E4M3FN) ((uint8_t*)out)[i] = enc_e4m3fn_sat(v[i]);
+        else ((uint16_t*)out)[i] = enc_bf16(v[i]);
+    }
+    return 0;
 }
 
 /* oracle_topk in threshold mode (thresh_row): the keys scoring above tau, at

@@ -318,6 +318,79 @@ def test_forward_threshold_is_the_stages():
     assert np.array_equal(i3, i4) and np.array_equal(O3, O4) and np.array_equal(l3, l4)
 
 
+def test_encode_fp8_matches_torch_in_range():
+    # every finite e4m3fn value, every midpoint between neighbours (ties go
+    # to the even code), and random values inside the finite range
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn)
+    vals = codes.float().numpy()
+    fin = np.sort(np.unique(np.abs(vals[np.isfinite(vals)])))
+    mids = (fin[:-1] + fin[1:]) / 2
+    g = np.random.default_rng(5)
+    v = np.concatenate([fin, -fin, mids, -mids, g.uniform(-464, 464, 20000),
+                        g.standard_normal(20000) * 0.01, [0.0, -0.0, 460.0, -463.9]])
+    v = v.astype(np.float32)
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(oracle.encode(v, "fp8"), ref)
+
+
+def test_encode_fp8_saturates():
+    # beyond the rounding range of 448 the encoding saturates (torch's cast
+    # gives NaN there instead)
+    v = np.array([464.0, 464.01, 480.0, 1000.0, 3e38, np.inf, -470.0, -np.inf], np.float32)
+    assert oracle.encode(v, "fp8").tolist() == [0x7e] * 6 + [0xfe] * 2
+    assert oracle.encode(np.array([np.nan], np.float32), "fp8").tolist() == [0x7f]
+
+
+def test_encode_bf16_matches_torch():
+    g = np.random.default_rng(6)
+    u = g.integers(0, 2 ** 32, 50000, dtype=np.uint64).astype(np.uint32)
+    u[:1000] = (u[:1000] & 0xffff0000) | 0x8000  # exact ties, both parities
+    v = u.view(np.float32)
+    v = v[np.isfinite(v) & (np.abs(v) < 3e38)]
+    ref = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oracle.encode(v, "bf16"), ref)
+
+
+@pytest.mark.parametrize("out_dtype", ["fp8", "bf16"])
+def test_index_project_vs_integer_matmul(out_dtype):
+    g = np.random.default_rng(7)
+    rows, d_model, d_idx = 37, 256, 64
+    X = g.integers(-3, 4, (rows, d_model))
+    W = g.integers(-1, 2, (d_idx, d_model)) * (g.random((d_idx, d_model)) < 0.25)
+    Xt = torch.tensor(X, dtype=torch.bfloat16)
+    Wt = torch.tensor(W, dtype=torch.bfloat16)
+    got = oracle.index_project(Xt, Wt, out_dtype)
+    y = torch.from_numpy((X @ W.T).astype(np.float32))  # exact: small integers
+    cast = torch.float8_e4m3fn if out_dtype == "fp8" else torch.bfloat16
+    raw = y.to(cast)
+    ref = raw.view(torch.uint8) if out_dtype == "fp8" else raw.view(torch.int16)
+    assert np.abs(y.numpy()).max() < 448  # inside the range where torch's cast is defined
+    assert np.array_equal(got.view(np.int16) if out_dtype == "bf16" else got, ref.numpy())
+
+
+def test_index_project_rows_land_where_asked():
+    # a decode step appends one new key row per sequence into the k_idx cache
+    g = np.random.default_rng(8)
+    B, n_k, d_model, d_idx = 3, 10, 64, 32
+    X = torch.tensor(g.integers(-2, 3, (B, d_model)), dtype=torch.bfloat16)
+    W = torch.tensor(g.integers(-1, 2, (d_idx, d_model)), dtype=torch.bfloat16)
+    cache = g.integers(0, 256, (B * n_k, d_idx)).astype(np.uint8)
+    before = cache.copy()
+    pos = [4, 9, 0]
+    dst = [b * n_k + p for b, p in enumerate(pos)]
+    oracle.index_project(X, W, "fp8", out=cache, out_rows=dst)
+    alone = oracle.index_project(X, W, "fp8")
+    for b in range(B):
+        assert np.array_equal(cache[dst[b]], alone[b])
+    keep = np.ones(B * n_k, bool)
+    keep[dst] = False
+    assert np.array_equal(cache[keep], before[keep])
+    # a large row saturates
+    big = torch.full((1, d_model), 8.0, dtype=torch.bfloat16)
+    ones = torch.ones((d_idx, d_model), dtype=torch.bfloat16)
+    assert np.all(oracle.index_project(big, ones, "fp8") == 0x7e)  # 512 -> 448
+
+
 def dense_attn_torch(Q, K, V, q_pos0):
     """Dense MQA attention with the causal mask, through torch's
     scaled_dot_product_attention in float64 (K/V expanded to every head)."""
