@@ -20,6 +20,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -34,6 +36,8 @@ KERNEL_SOURCES = {
     ("decode", "indexer"): ["decode.hip", "frag.h"],
     ("decode", "topk"): ["decode.hip", "topk_common.h"],
     ("decode", "attn"): ["attn.hip"],
+    ("prefill", "project"): ["project.hip"],
+    ("decode", "project"): ["project.hip"],
 }
 
 
@@ -49,6 +53,12 @@ def stage_work(w, stage, seed=0):
     """Algorithmic work of one launch of `stage` on workload w:
     (bound, amount, unit, peak)."""
     es = 1 if w.idx_dtype == "fp8" else 2
+    if stage == "project":
+        # read the hidden rows once per projection and both weights, write the
+        # q rows and the new k rows
+        rows = w.batch * w.n_q
+        b = 2 * rows * w.d_model * 2 + 2 * w.d_idx * w.d_model * 2 + 2 * rows * w.d_idx * es
+        return "hbm", b / 1e9, "GB/s", PEAK["hbm"]
     pairs = w.n_causal_pairs(seed)
     if stage == "indexer":
         if w.mode == "decode":
@@ -78,6 +88,16 @@ def calib_copy(nbytes=1 << 30, reps=5):
     print(json.dumps({"calib_copy_bytes": nbytes, "reps": reps}))
 
 
+def project_oracle(oracle, x, wname, r0, r1, w):
+    """The oracle's indexer projection of hidden rows [r0, r1) with weight
+    x[wname], as a torch fp8 / bf16 tensor [r1 - r0, d_idx]."""
+    import torch
+    dt = "fp8" if w.idx_dtype == "fp8" else "bf16"
+    raw = oracle.index_project(x["X"][r0:r1], x[wname], dt)
+    tdt = torch.float8_e4m3fn if dt == "fp8" else torch.bfloat16
+    return torch.from_numpy(raw.view(np.uint8 if dt == "fp8" else np.int16)).view(tdt)
+
+
 def cpu_baseline(w, x, target_s=12.0, seed=0):
     """Time the oracle on a bounded sample of the workload's queries."""
     import oracle
@@ -89,8 +109,14 @@ def cpu_baseline(w, x, target_s=12.0, seed=0):
         def run(nseq):
             if not w.ragged:
                 xs = {k: v[:nseq] for k, v in x.items()}
-                oracle.forward(xs["q_idx"], xs["k_idx"], xs["Q"], xs["K"], xs["V"], w.q_pos0,
-                               w.top_k, tau=w.tau)
+                q_idx, k_idx = xs["q_idx"], xs["k_idx"]
+                if w.d_model:
+                    # the front-end: each sequence's query and its new key row
+                    q_idx = project_oracle(oracle, x, "W_q", 0, nseq, w).reshape(nseq, 1, -1)
+                    k_idx = k_idx.clone()
+                    k_idx[:, w.q_pos0] = project_oracle(oracle, x, "W_k", 0, nseq, w)
+                oracle.forward(q_idx, k_idx, xs["Q"], xs["K"], xs["V"], w.q_pos0, w.top_k,
+                               tau=w.tau)
                 return nseq
             xs = {k: v[:nseq] for k, v in x.items()}  # each sequence at its own position
             oracle.forward(xs["q_idx"], xs["k_idx"], xs["Q"], xs["K"], xs["V"], 0, w.top_k,
@@ -119,9 +145,14 @@ def cpu_baseline(w, x, target_s=12.0, seed=0):
         t0 = time.perf_counter()
         q = 0
         for r in rows:
+            r1 = min(r + nthreads, w.n_q)
+            if w.d_model:
+                # the front-end's work per query: its own q and k rows
+                project_oracle(oracle, x, "W_q", r, r1, w)
+                project_oracle(oracle, x, "W_k", r, r1, w)
             oracle.forward(x["q_idx"], x["k_idx"], x["Q"], x["K"], x["V"], w.q_pos0, w.top_k,
-                           r, min(r + nthreads, w.n_q), tau=w.tau)
-            q += min(r + nthreads, w.n_q) - r
+                           r, r1, tau=w.tau)
+            q += r1 - r
             if time.perf_counter() - t0 > target_s:
                 break
         dt = time.perf_counter() - t0
@@ -193,7 +224,29 @@ def main():
     idx = torch.empty((w.batch, w.n_q, w.top_k), dtype=torch.int32, device=dev)
     lse = torch.empty((w.batch, w.n_q, w.n_heads), dtype=torch.float32, device=dev)
 
+    project = None
+    if w.d_model:
+        if w.ragged or w.page_size:
+            raise SystemExit("the projection front-end runs on the contiguous layout")
+        # the indexer projection front-end: q_idx from every query row's hidden
+        # state; k_idx rows for the same tokens (decode: appended at each
+        # sequence's position; prefill: every key row)
+        rows = w.batch * w.n_q
+        proj = dsa.Projection(rows, w.d_model, w.d_idx, dev)
+        q_flat = d["q_idx"].view(rows, w.d_idx)
+        k_flat = d["k_idx"].view(w.batch * w.n_k, w.d_idx)
+        krows = None
+        if w.mode == "decode":
+            krows = torch.tensor([b * w.n_k + p for b, p in enumerate(w.positions(args.seed))],
+                                 dtype=torch.int32, device=dev)
+
+        def project():
+            proj(d["X"], d["W_q"], q_flat)
+            proj(d["X"], d["W_k"], k_flat, krows)
+
     def step():
+        if project:
+            project()
         fwd(d["q_idx"], d["k_idx"], d["Q"], d["K"], d["V"], O, idx, lse, seq_pos=sp, pages=pages,
             tau=w.tau)
 
@@ -223,6 +276,15 @@ def main():
                                    seq_pos=sp, pages=pages, tau=w.tau)
             tot = [a + b for a, b in zip(tot, ms3)]
         stages = {n: t / n_rep for n, t in zip(names, tot)}
+        if project:
+            # the projections run on torch's current stream: time them with its events
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(n_rep):
+                project()
+            e1.record()
+            e1.synchronize()
+            stages["project"] = e0.elapsed_time(e1) / n_rep
         dom = max(stages, key=stages.get)
         bound, amount, unit, peak = stage_work(w, dom, args.seed)
         achieved = amount / (stages[dom] / 1e3)
@@ -264,6 +326,10 @@ def main():
         pos = w.positions(args.seed)
         out["config"]["ragged"] = {"positions": "seeded, uniform in [n_k/8, n_k-1]",
                                    "mean_len": round(sum(p + 1 for p in pos) / len(pos), 1)}
+    if w.d_model:
+        out["config"]["projection"] = {"d_model": w.d_model, "front_end": "q_idx and new k_idx "
+                                       "rows projected from bf16 hidden states each step"}
+        out["data"] += "; integer hidden states and sparse {-1,0,1} projection weights"
     if w.tau is not None:
         kept = (idx >= 0).sum(-1).float()
         out["config"]["threshold"] = {"tau": w.tau, "kept_mean": round(float(kept.mean()), 1),

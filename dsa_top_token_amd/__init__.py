@@ -31,7 +31,8 @@ HEAD_DIM = 128
 EXPORTS = ("dsa_workspace_size", "dsa_index_scores", "dsa_topk", "dsa_sparse_attn",
            "dsa_forward", "dsa_forward_ragged", "dsa_forward_paged", "dsa_forward_timed",
            "dsa_forward_ragged_timed", "dsa_forward_paged_timed", "dsa_forward_threshold",
-           "dsa_forward_threshold_timed", "dsa_status_str", "dsa_last_error")
+           "dsa_forward_threshold_timed", "dsa_index_project", "dsa_status_str",
+           "dsa_last_error")
 
 
 class Problem(ctypes.Structure):
@@ -85,7 +86,9 @@ def load():
             lib.dsa_forward_threshold.argtypes = [PP, F, P, P, P, P, P, P, P, P, P, S, P]
             lib.dsa_forward_threshold_timed.argtypes = [PP, F, P, P, P, P, P, P, P, P, P, S, P,
                                                         P, P]
-            for f in (lib.dsa_workspace_size, lib.dsa_index_scores, lib.dsa_topk,
+            lib.dsa_index_project.argtypes = [I, I, I, I, P, P, P, P, I, P]
+            for f in (lib.dsa_index_project,
+                      lib.dsa_workspace_size, lib.dsa_index_scores, lib.dsa_topk,
                       lib.dsa_sparse_attn, lib.dsa_forward, lib.dsa_forward_ragged,
                       lib.dsa_forward_paged, lib.dsa_forward_timed,
                       lib.dsa_forward_ragged_timed, lib.dsa_forward_paged_timed,
@@ -294,6 +297,45 @@ def forward(q_idx, k_idx, Q, K, V, q_pos0, top_k, want_idx=True, want_lse=True, 
             raise ValueError("seq_pos must have one entry per sequence")
     Forward(p, dev)(q_idx, k_idx, Q, K, V, O, idx, lse, seq_pos=seq_pos, tau=tau)
     return idx, O, lse
+
+
+class Projection:
+    """dsa_index_project for fixed sizes (the call needs no workspace)."""
+
+    def __init__(self, rows, d_model, d_idx, device):
+        self.rows, self.d_model, self.d_idx = rows, d_model, d_idx
+        self.device = torch.device(device)
+
+    def __call__(self, X, W, out, out_rows=None):
+        """Encode X . W^T into out ([n_out, d_idx] float8_e4m3fn or bfloat16),
+        row out_rows[r] (int32 on the device) or r."""
+        dt = {torch.float8_e4m3fn: IDX_FP8, torch.bfloat16: IDX_BF16}[out.dtype]
+        _check(load().dsa_index_project(
+            self.rows, self.d_model, self.d_idx, dt, _ptr(X), _ptr(W), _ptr(out), _ptr(out_rows),
+            out.shape[0], _stream(self.device)))
+
+
+def index_project(X, W, out_dtype=torch.float8_e4m3fn, out=None, out_rows=None):
+    """The indexer projection: encode(fl32(X . W^T)) for X [rows, d_model]
+    and W [d_idx, d_model] (bfloat16, on the device), into a new
+    [rows, d_idx] tensor or into rows out_rows of `out`. Returns the output."""
+    _dev_tensor(X, "X", (torch.bfloat16,), 2)
+    _dev_tensor(W, "W", (torch.bfloat16,), 2)
+    rows, d_model = X.shape
+    d_idx = W.shape[0]
+    if W.shape[1] != d_model:
+        raise ValueError("W must be [d_idx, d_model]")
+    if out is None:
+        out = torch.empty((rows, d_idx), dtype=out_dtype, device=X.device)
+    _dev_tensor(out, "out", (torch.float8_e4m3fn, torch.bfloat16), 2)
+    if out.shape[1] != d_idx:
+        raise ValueError("out must have d_idx columns")
+    if out_rows is not None:
+        _dev_tensor(out_rows, "out_rows", (torch.int32,), 1)
+        if out_rows.shape[0] != rows:
+            raise ValueError("out_rows needs one entry per input row")
+    Projection(rows, d_model, d_idx, X.device)(X, W, out, out_rows)
+    return out
 
 
 def make_pages(block_table, page_size, n_pages) -> Pages:

@@ -11,7 +11,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libdsa.so")
 SOURCES = ["indexer.hip", "topk.hip", "decode.hip", "prefill.hip", "attn.hip", "threshold.hip",
-           "api.cpp"]
+           "project.hip", "api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 CFLAGS = [

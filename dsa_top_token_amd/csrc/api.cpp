@@ -33,6 +33,7 @@ dsa_status ok() {
 constexpr long long kMaxKeys = 4194304;
 constexpr int kMaxTopK = 4096;
 constexpr int kMaxHeads = 16;
+constexpr int kMaxModelWidth = 65536;
 constexpr int kHeadDim = 128;
 constexpr size_t kAlign = 256;
 constexpr size_t kScoreSlabBytes = size_t(2) << 30;  // score rows staged per forward pass
@@ -395,6 +396,19 @@ dsa_status forward_impl(const dsa_problem* p, const void* q_idx, const void* k_i
     return DSA_OK;
 }
 
+dsa_status check_project_sizes(int32_t rows, int32_t d_model, int32_t d_idx) {
+    if (rows < 1) return fail(DSA_E_SHAPE, "rows=%d must be >= 1", rows);
+    if (d_model < 32 || d_model % 32 != 0 || d_model > kMaxModelWidth)
+        return fail(DSA_E_UNSUPPORTED, "d_model=%d must be a multiple of 32 in [32, %d]", d_model,
+                    kMaxModelWidth);
+    if (d_idx < 32 || d_idx % 32 != 0 || d_idx > 256)
+        return fail(DSA_E_UNSUPPORTED, "d_idx=%d must be a multiple of 32 in [32, 256]", d_idx);
+    if ((long long)rows * d_model > (1LL << 40))
+        return fail(DSA_E_SHAPE, "rows * d_model = %lld is too large",
+                    (long long)rows * d_model);
+    return DSA_OK;
+}
+
 // Arguments a ragged batch adds to those of dsa_forward.
 dsa_status check_ragged(const dsa_problem* p, const int32_t* seq_pos) {
     dsa_status s = check_problem(p);
@@ -636,6 +650,36 @@ dsa_status dsa_forward_timed(const dsa_problem* p, const void* q_idx, const void
     hipError_t e = tm.finish(stage_ms);
     if (s != DSA_OK) return s;
     if (e != hipSuccess) return hip_fail(e, "stage timing events");
+    return ok();
+}
+
+dsa_status dsa_index_project(int32_t rows, int32_t d_model, int32_t d_idx, int32_t out_dtype,
+                             const void* X, const void* W, void* out, const int32_t* out_rows,
+                             int32_t n_out, void* stream) {
+    dsa_status s = check_project_sizes(rows, d_model, d_idx);
+    if (s != DSA_OK) return s;
+    if (out_dtype != DSA_IDX_FP8_E4M3FN && out_dtype != DSA_IDX_BF16)
+        return fail(DSA_E_UNSUPPORTED, "out_dtype=%d is neither fp8 e4m3fn (0) nor bf16 (1)",
+                    out_dtype);
+    if ((s = check_ptrs({X, W, out}, "X, W, out")) != DSA_OK) return s;
+    if (out_rows && misaligned(out_rows))
+        return fail(DSA_E_ALIGN, "out_rows is not 16-byte aligned");
+    if (n_out < 1) return fail(DSA_E_SHAPE, "n_out=%d must be >= 1", n_out);
+    if (!out_rows && n_out < rows)
+        return fail(DSA_E_SHAPE, "without out_rows the output needs rows=%d rows (n_out=%d)",
+                    rows, n_out);
+    dsa::ProjectArgs a{};
+    a.X = static_cast<const uint16_t*>(X);
+    a.W = static_cast<const uint16_t*>(W);
+    a.out = out;
+    a.out_rows = out_rows;
+    a.rows = rows;
+    a.d_model = d_model;
+    a.d_idx = d_idx;
+    a.out_dtype = out_dtype;
+    a.n_out = n_out;
+    hipError_t e = dsa::launch_project(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "projection launch");
     return ok();
 }
 

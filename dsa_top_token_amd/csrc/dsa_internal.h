@@ -189,6 +189,18 @@ struct FloorArgs {
 };
 hipError_t launch_threshold_floor(const FloorArgs& a, hipStream_t s);
 
+// Indexer projection: out row out_rows[r] (r when null) of [n_out][d_idx] =
+// encode(fl32(X[r] . W[o])) for X [rows][d_model], W [d_idx][d_model] bf16;
+// e4m3fn (out_dtype 0, nearest even, saturating) or bf16 (1).
+struct ProjectArgs {
+    const uint16_t* X;
+    const uint16_t* W;
+    void* out;
+    const int32_t* out_rows;  // optional [rows]; destinations outside [0, n_out) are skipped
+    int rows, d_model, d_idx, out_dtype, n_out;
+};
+hipError_t launch_project(const ProjectArgs& a, hipStream_t s);
+
 // Split plan of the attention: splits per query and entries per split.
 void attn_split_plan(int B, int n_q, int k, int* n_split, int* split_len);
 

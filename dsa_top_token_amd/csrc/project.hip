@@ -1,0 +1,235 @@
+// Indexer projection front-end on gfx950: q_idx = X W_q^T and k_idx = X W_k^T
+// in the indexer's input format, written to chosen rows of the output.
+//
+// DeepSeek-V3.2 DSA page (kwkr.cn/news/60693), section 3.2: the lightning
+// indexer maps the model width down to the indexer width with two bias-free
+// linear layers (query_proj, key_proj); section 4.1 runs the index stage in
+// FP8. For each input row r and output feature o,
+//   y = fl32(sum_c X[r][c] W[o][c])     (bf16 inputs, fp32 MFMA accumulation)
+// is encoded as e4m3fn (round to nearest even, saturating at +-448) or bf16
+// (round to nearest even) into row out_rows[r] of the output; a decode step
+// appends each sequence's new key row to the k_idx cache this way.
+//
+// Layout of the product (many rows): a wave owns RT tiles of 16 input rows
+// and all DI / 16 tiles of 16 output features. Per 32-wide step of the model
+// width it loads RT X fragments (streamed from HBM once) and DI / 16 W
+// fragments (W is in nn.Linear's [d_idx][d_model] layout, so a lane's B
+// operand, 8 consecutive elements of one W row, is one 16-byte load; W is
+// read from L2, so more row tiles per wave mean less W traffic per row), then
+// issues RT * DI / 16 bf16 MFMAs. Few rows (a decode batch) cannot fill the
+// chip that way: a 16-wave workgroup then owns 16 rows x 16 features, its
+// waves split the model width, and the partial tiles are added through LDS
+// in wave order (one launch, deterministic).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dsa_internal.h"
+
+namespace dsa {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int PJ_NT = 256;          // 4 waves
+// Many rows: row tiles per wave and steps of fragments in flight, sized so
+// the accumulators and fragments stay in registers.
+template <int DI> constexpr int pj_rt() { return DI <= 128 ? 4 : 2; }
+template <int DI> constexpr int pj_pf() { return DI <= 128 ? 2 : 1; }
+constexpr int PS_PF = 6;            // split-width kernel: steps in flight per wave
+constexpr int PJ_MIN_WGS = 192;     // fewer row workgroups: the split-width kernel
+constexpr int PS_NT = 1024;         // split-width kernel: 16 waves
+constexpr int PS_W = PS_NT / 64;
+
+// e4m3fn code of v: nearest value, ties to an even mantissa; |v| >= 448
+// saturates (the values in [448, 464] round there anyway); NaN -> 0x7f.
+__device__ __forceinline__ uint32_t to_e4m3fn_sat(float v) {
+    const uint32_t s = (__float_as_uint(v) >> 24) & 0x80u;
+    const float a = fabsf(v);
+    if (!(a == a)) return 0x7fu;
+    if (a >= 448.0f) return s | 0x7eu;
+    uint32_t c;
+    if (a < 0.015625f) {
+        // below 2^-6: codes m * 2^-9 (the scaling is exact, rintf rounds
+        // half to even; m = 8 is the smallest normal code)
+        c = (uint32_t)rintf(a * 512.0f);
+    } else {
+        // keep 3 mantissa bits, rounding half to even (a carry moves into the
+        // exponent); rebias the exponent from 127 to 7
+        uint32_t w = __float_as_uint(a);
+        w += 0x7ffffu + ((w >> 20) & 1u);
+        c = (((w >> 23) - 120u) << 3) | ((w >> 20) & 7u);
+        c = min(c, 0x7eu);
+    }
+    return s | c;
+}
+
+// bf16 code of v: round half to even; NaN -> 0x7fc0.
+__device__ __forceinline__ uint32_t to_bf16(float v) {
+    if (!(v == v)) return 0x7fc0u;
+    uint32_t u = __float_as_uint(v);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ void store_code(const ProjectArgs& a, int r, int col, float y) {
+    const int dst = a.out_rows ? a.out_rows[r] : r;
+    if (dst < 0 || dst >= a.n_out) return;  // destinations outside the output are skipped
+    const size_t o = (size_t)dst * a.d_idx + col;
+    if (a.out_dtype == 0) static_cast<uint8_t*>(a.out)[o] = (uint8_t)to_e4m3fn_sat(y);
+    else static_cast<uint16_t*>(a.out)[o] = (uint16_t)to_bf16(y);
+}
+
+__device__ __forceinline__ bf16x8 ld8(const uint16_t* p) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const i32x4*>(p));
+}
+
+template <int DI, int RT, int PF>
+__global__ __launch_bounds__(PJ_NT) void project_kernel(ProjectArgs a) {
+    constexpr int CT = DI / 16;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n = lane & 15, g = lane >> 4;
+    const int r0 = __builtin_amdgcn_readfirstlane((blockIdx.x * (PJ_NT / 64) + wave) * 16 * RT);
+    if (r0 >= a.rows) return;  // wave-uniform
+    const int kb = 0, ke = a.d_model;
+    // A operand: lane (n, g) holds elements [k + 8 g, +8) of row r0 + 16 t + n;
+    // B operand: the same elements of W row 16 c + n.
+    const uint16_t* xr[RT];
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+        xr[t] = a.X + (size_t)min(r0 + 16 * t + n, a.rows - 1) * a.d_model + 8 * g;
+    const uint16_t* wr = a.W + (size_t)n * a.d_model + 8 * g;
+    const size_t wstep = (size_t)16 * a.d_model;  // next column tile
+    f32x4 acc[RT][CT];
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+        for (int c = 0; c < CT; ++c) acc[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // A ring of PF steps of fragments in registers: step k + 32 p sits in
+    // slot p; the loop runs PF steps per pass so every slot index is static.
+    bf16x8 xf[PF][RT], wf[PF][CT];
+    auto load = [&](int p, int k) {
+#pragma unroll
+        for (int t = 0; t < RT; ++t) xf[p][t] = ld8(xr[t] + k);
+#pragma unroll
+        for (int c = 0; c < CT; ++c) wf[p][c] = ld8(wr + c * wstep + k);
+    };
+#pragma unroll
+    for (int p = 0; p < PF; ++p)
+        if (kb + 32 * p < ke) load(p, kb + 32 * p);
+    for (int k = kb; k < ke; k += 32 * PF) {
+#pragma unroll
+        for (int p = 0; p < PF; ++p) {
+            const int kp = k + 32 * p;
+            if (kp >= ke) break;  // uniform
+            bf16x8 xc[RT], wc[CT];
+#pragma unroll
+            for (int t = 0; t < RT; ++t) xc[t] = xf[p][t];
+#pragma unroll
+            for (int c = 0; c < CT; ++c) wc[c] = wf[p][c];
+            // refill the slot with the step PF ahead; it flies under the MFMAs
+            if (kp + 32 * PF < ke) load(p, kp + 32 * PF);
+#pragma unroll
+            for (int t = 0; t < RT; ++t)
+#pragma unroll
+                for (int c = 0; c < CT; ++c)
+                    acc[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xc[t], wc[c], acc[t][c],
+                                                                       0, 0, 0);
+        }
+    }
+    // lane (n, g), register i of tile (t, c): input row r0 + 16 t + 4 g + i,
+    // output feature 16 c + n
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = r0 + 16 * t + 4 * g + i;
+            if (r >= a.rows) continue;
+#pragma unroll
+            for (int c = 0; c < CT; ++c) store_code(a, r, 16 * c + n, acc[t][c][i]);
+        }
+}
+
+// Few rows: workgroup (bx, by) owns rows 16 bx .. +16 and features
+// 16 by .. +16 (small tiles spread the rows' loads over many CUs); wave w
+// takes the w-th of PS_W equal parts of the model width (a multiple of 32
+// each), then the PS_W partial tiles are added in wave order through LDS.
+template <int PF>
+__global__ __launch_bounds__(PS_NT) void project_small_kernel(ProjectArgs a) {
+    __shared__ f32x4 red[PS_W][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n = lane & 15, g = lane >> 4;
+    const int r0 = blockIdx.x * 16, c0 = blockIdx.y * 16;
+    const int part = (a.d_model / 32 + PS_W - 1) / PS_W * 32;
+    // scalar bounds: the step loop stays a uniform branch (no reconvergence waits)
+    const int kb = __builtin_amdgcn_readfirstlane(min(a.d_model, wave * part));
+    const int ke = __builtin_amdgcn_readfirstlane(min(a.d_model, kb + part));
+    const uint16_t* xr = a.X + (size_t)min(r0 + n, a.rows - 1) * a.d_model + 8 * g;
+    const uint16_t* wr = a.W + (size_t)(c0 + n) * a.d_model + 8 * g;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    bf16x8 xf[PF], wf[PF];
+#pragma unroll
+    for (int p = 0; p < PF; ++p)
+        if (kb + 32 * p < ke) {
+            xf[p] = ld8(xr + kb + 32 * p);
+            wf[p] = ld8(wr + kb + 32 * p);
+        }
+    for (int k = kb; k < ke; k += 32 * PF) {
+#pragma unroll
+        for (int p = 0; p < PF; ++p) {
+            const int kp = k + 32 * p;
+            if (kp >= ke) break;  // uniform
+            const bf16x8 x = xf[p], w = wf[p];
+            if (kp + 32 * PF < ke) {
+                xf[p] = ld8(xr + kp + 32 * PF);
+                wf[p] = ld8(wr + kp + 32 * PF);
+            }
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, w, acc, 0, 0, 0);
+        }
+    }
+    red[wave][lane] = acc;
+    __syncthreads();
+    // thread (lane l, register i) adds the waves' values in order
+    if (threadIdx.x < 64 * 4) {
+        const int l = threadIdx.x >> 2, i = threadIdx.x & 3;
+        float y = 0.f;
+#pragma unroll
+        for (int w = 0; w < PS_W; ++w) y += red[w][l][i];
+        const int r = r0 + 4 * (l >> 4) + i;
+        if (r < a.rows) store_code(a, r, c0 + (l & 15), y);
+    }
+}
+
+template <int DI>
+hipError_t launch_di(const ProjectArgs& a, hipStream_t s) {
+    constexpr long long rows_per_wg = (PJ_NT / 64) * 16 * pj_rt<DI>();
+    const long long nb = (a.rows + rows_per_wg - 1) / rows_per_wg;
+    if (nb < PJ_MIN_WGS) {
+        hipLaunchKernelGGL((project_small_kernel<PS_PF>),
+                           dim3((unsigned)((a.rows + 15) / 16), DI / 16), dim3(PS_NT), 0, s, a);
+        return hipGetLastError();
+    }
+    if (nb > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((project_kernel<DI, pj_rt<DI>(), pj_pf<DI>()>), dim3((unsigned)nb),
+                       dim3(PJ_NT), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_project(const ProjectArgs& a, hipStream_t s) {
+    switch (a.d_idx) {
+        case 32: return launch_di<32>(a, s);
+        case 64: return launch_di<64>(a, s);
+        case 96: return launch_di<96>(a, s);
+        case 128: return launch_di<128>(a, s);
+        case 160: return launch_di<160>(a, s);
+        case 192: return launch_di<192>(a, s);
+        case 224: return launch_di<224>(a, s);
+        case 256: return launch_di<256>(a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace dsa

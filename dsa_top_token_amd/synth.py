@@ -30,7 +30,8 @@ from typing import Dict, Optional
 import torch
 
 TID = {"q_idx": 1, "k_idx": 2, "Q": 3, "K": 4, "V": 5,
-       "centroids": 6, "assign": 7, "noise": 8, "positions": 9, "pages": 10}
+       "centroids": 6, "assign": 7, "noise": 8, "positions": 9, "pages": 10,
+       "X": 11, "W_q": 12, "W_k": 13, "W_q_mask": 14, "W_k_mask": 15}
 
 HEAD_DIM = 128
 N_CENTROIDS = 64
@@ -52,6 +53,8 @@ class Workload:
     ragged: bool = False  # decode only: per-sequence query positions (positions())
     page_size: int = 0    # > 0: k_idx, K, V stored in shuffled pages of this many keys
     tau: Optional[float] = None  # threshold-mode selection: keys scoring above tau, <= top_k
+    d_model: int = 0      # > 0: each step projects q_idx and the new k_idx rows from hidden
+                          # states X [rows, d_model] (make_inputs parts "X", "W_q", "W_k")
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -119,6 +122,15 @@ WORKLOADS["decode_128k_paged"] = WORKLOADS["decode_128k_ragged"].replace(
     name="decode_128k_paged", page_size=256)
 WORKLOADS["decode_128k_paged16"] = WORKLOADS["decode_128k_ragged"].replace(
     name="decode_128k_paged16", page_size=16)
+# The clustered 128K decode batch and the 64K prefill with the indexer
+# projection front-end (model width 4096, as the DSA page's "usual 4096
+# dimensions"): a decode step projects each sequence's query and appends its
+# new key row at the sequence's position; a prefill projects every token's
+# query and key.
+WORKLOADS["decode_128k_projected"] = WORKLOADS["decode_128k_clustered"].replace(
+    name="decode_128k_projected", d_model=4096)
+WORKLOADS["prefill_64k_projected"] = WORKLOADS["prefill_64k"].replace(
+    name="prefill_64k_projected", d_model=4096)
 # The clustered 128K decode batch in threshold mode: tau = 14 keeps from about
 # 200 to several thousand keys per query on these inputs, so some rows keep
 # all their passing keys and others are cut to the top_k highest.
@@ -184,4 +196,13 @@ def make_inputs(w: Workload, seed: int = 0, device: str = "cpu",
         out["K"] = _normal_bf16((B, nk, HEAD_DIM), seed, "K", device)
     if "V" in want:
         out["V"] = _normal_bf16((B, nk, HEAD_DIM), seed, "V", device)
+    if w.d_model and (parts is None or "X" in want):
+        # hidden states: integers in [-3, 3]; weights: {-1, 0, 1}, nonzero with
+        # probability 1/16 (projected values stay exact and well inside fp8)
+        rows = B * nq
+        out["X"] = _ints((rows, w.d_model), -3, 3, seed, "X", device).to(torch.bfloat16)
+        for name in ("W_q", "W_k"):
+            wv = _ints((d, w.d_model), -1, 1, seed, name, device)
+            keep = _ints((d, w.d_model), 0, 15, seed, name + "_mask", device) == 0
+            out[name] = (wv * keep).to(torch.bfloat16)
     return out

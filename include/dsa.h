@@ -232,6 +232,33 @@ dsa_status dsa_forward_timed(const dsa_problem* p, const void* q_idx,
                              float* lse, void* ws, size_t ws_bytes,
                              void* stream, float* stage_ms, int32_t* n_slabs);
 
+/* The indexer projections (DSA page, section 3.2: query_proj and key_proj
+ * are bias-free linear maps from the model width d_model to the indexer
+ * width d_idx; section 4.1: the index stage runs in FP8). For each input row
+ * r of X and output feature o,
+ *   y = fl32(sum_c X[r][c] * W[o][c])   (fp32 accumulation)
+ * is encoded in out_dtype into row out_rows[r] of out (row r when out_rows is
+ * NULL):
+ *   DSA_IDX_FP8_E4M3FN  round to nearest, ties to even; |y| >= 448 gives
+ *                       +-448 (saturating), NaN the NaN code
+ *   DSA_IDX_BF16        round to nearest, ties to even
+ * X bfloat16 [rows][d_model]; W bfloat16 [d_idx][d_model] (nn.Linear's weight
+ * layout); out [n_out][d_idx] in out_dtype; other rows of out are not
+ * touched, so out_rows = b * n_k + pos appends a decode step's new keys to a
+ * k_idx cache [B][n_k][d_idx]. out_rows: optional int32 [rows], device
+ * memory, 16-byte aligned; entries outside [0, n_out) are skipped; two input
+ * rows sent to one output row leave either. d_model: a multiple of 32 in
+ * [32, 65536]; d_idx: a multiple of 32 in [32, 256]. Sums over d_model are
+ * exact (order-independent) when the products and partial sums are
+ * integers below 2^24; otherwise the fp32 summation order is fixed, so
+ * results repeat bit for bit. No workspace. Errors: DSA_E_NULL,
+ * DSA_E_ALIGN (pointers), DSA_E_SHAPE (rows < 1, n_out < 1, or n_out < rows
+ * without out_rows), DSA_E_UNSUPPORTED (widths, dtype). */
+dsa_status dsa_index_project(int32_t rows, int32_t d_model, int32_t d_idx,
+                             int32_t out_dtype, const void* X, const void* W,
+                             void* out, const int32_t* out_rows, int32_t n_out,
+                             void* stream);
+
 /* Static name of a status code. */
 const char* dsa_status_str(int32_t status);
 

@@ -122,6 +122,20 @@ def test_threshold_forward_arguments():
                                            None) == -5
 
 
+def test_index_project_arguments():
+    lib = dsa.load()
+    call = lambda rows=64, dm=4096, di=128, dt=0, X=FAKE, W=FAKE, out=FAKE, orow=None, \
+        n_out=64: lib.dsa_index_project(rows, dm, di, dt, X, W, out, orow, n_out, None)
+    assert call(rows=0) == -2
+    assert call(dm=100) == -3 and call(dm=0) == -3 and call(dm=1 << 20) == -3
+    assert call(di=48) == -3 and call(di=512) == -3
+    assert call(dt=2) == -3
+    assert call(X=None) == -1 and call(W=None) == -1 and call(out=None) == -1
+    assert call(X=ODD) == -4 and call(orow=ODD) == -4
+    assert call(n_out=0) == -2
+    assert call(n_out=10) == -2               # fewer output rows than inputs, no out_rows
+
+
 def test_paged_forward_arguments():
     lib = dsa.load()
     dec = prob(n_q=1, n_k=512, q_pos0=0)

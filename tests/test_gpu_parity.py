@@ -451,6 +451,114 @@ def test_forward_threshold_vs_oracle(gpu_lib, w, mode):
         assert torch.all(torch.isneginf(lse))
 
 
+# Indexer projection: (rows, d_model, d_idx, out dtype, input range). "small"
+# inputs keep |y| well inside the fp8 range; "wide" ones saturate often and
+# land on rounding ties. Integer inputs keep every sum exact.
+PROJ = [
+    (1, 32, 32, "fp8", "small"),
+    (17, 96, 128, "fp8", "small"),
+    (64, 4096, 128, "fp8", "small"),      # a decode batch: the model width is split
+    (64, 4096, 128, "bf16", "small"),
+    (64, 4096, 128, "fp8", "wide"),
+    (1000, 512, 160, "fp8", "wide"),
+    (9000, 256, 256, "bf16", "wide"),     # two row tiles per wave
+    (20000, 1024, 96, "fp8", "small"),
+    (70001, 128, 64, "fp8", "wide"),
+]
+
+
+def proj_inputs(rows, d_model, d_idx, kind, seed):
+    g = np.random.default_rng(seed)
+    if kind == "small":
+        X = g.integers(-3, 4, (rows, d_model))
+        W = g.integers(-1, 2, (d_idx, d_model)) * (g.random((d_idx, d_model)) < 1 / 16)
+    else:
+        X = g.integers(-8, 9, (rows, d_model))
+        W = g.integers(-2, 3, (d_idx, d_model)) * (g.random((d_idx, d_model)) < 1 / 4)
+    return (torch.tensor(X, dtype=torch.bfloat16), torch.tensor(W, dtype=torch.bfloat16))
+
+
+def raw_bytes(t):
+    return t.view(torch.uint8).cpu().numpy() if t.element_size() == 1 else \
+        t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("rows,d_model,d_idx,dt,kind", PROJ)
+def test_index_project_bit_exact(gpu_lib, rows, d_model, d_idx, dt, kind):
+    say("index_project rows=%d d_model=%d d_idx=%d %s %s" % (rows, d_model, d_idx, dt, kind))
+    X, W = proj_inputs(rows, d_model, d_idx, kind, rows + d_model)
+    ref = oracle.index_project(X, W, dt)
+    cast = torch.float8_e4m3fn if dt == "fp8" else torch.bfloat16
+    got = dsa.index_project(X.cuda(), W.cuda(), cast)
+    assert np.array_equal(raw_bytes(got), ref)
+    if kind == "wide" and dt == "fp8" and d_model >= 2048:
+        assert (ref == 0x7e).any() and (ref == 0xfe).any()  # saturation was exercised
+
+
+def test_index_project_appends_to_cache(gpu_lib):
+    # one new key row per sequence into the k_idx cache at its position; a
+    # destination outside the cache is skipped
+    B, n_k, d_model, d_idx = 6, 1000, 2048, 128
+    X, W = proj_inputs(B, d_model, d_idx, "small", 3)
+    g = np.random.default_rng(4)
+    cache0 = g.integers(0, 0x7e, (B * n_k, d_idx)).astype(np.uint8)
+    pos = [0, 999, 500, 17, 3, 998]
+    dst = [b * n_k + p for b, p in enumerate(pos)]
+    dst_gpu = list(dst)
+    dst_gpu[4] = B * n_k + 5  # outside the cache
+    ref = oracle.index_project(X[[0, 1, 2, 3, 5]], W, "fp8", out=cache0.copy(),
+                               out_rows=[dst[i] for i in (0, 1, 2, 3, 5)])
+    cache = torch.from_numpy(cache0.copy()).cuda().view(torch.float8_e4m3fn)
+    rows = torch.tensor(dst_gpu, dtype=torch.int32, device="cuda")
+    dsa.index_project(X.cuda(), W.cuda(), out=cache, out_rows=rows)
+    assert np.array_equal(raw_bytes(cache), ref)
+
+
+@pytest.mark.parametrize("rows,d_model", [(64, 4096), (3000, 1024)])
+def test_index_project_real_valued_within_one_step(gpu_lib, rows, d_model):
+    # N(0, 1) inputs and N(0, 1/d_model) weights: sums are no longer exact, so
+    # the fp32 accumulation order may move a value across a rounding
+    # boundary; each code must be the oracle's or a neighbour
+    g = torch.Generator().manual_seed(9)
+    X = torch.randn((rows, d_model), generator=g).to(torch.bfloat16)
+    W = (torch.randn((128, d_model), generator=g) / d_model ** 0.5).to(torch.bfloat16)
+    ref = oracle.index_project(X, W, "fp8")
+    got = raw_bytes(dsa.index_project(X.cuda(), W.cuda()))
+    vr = torch.from_numpy(ref).view(torch.float8_e4m3fn).float().numpy()
+    vg = torch.from_numpy(got).view(torch.float8_e4m3fn).float().numpy()
+    step = np.maximum(np.abs(vr), np.abs(vg)) / 8 + 2.0 ** -9
+    assert np.all(np.abs(vr - vg) <= step)
+    assert np.mean(got == ref) > 0.99
+
+
+def test_projected_decode_step(gpu_lib):
+    # a decode step from hidden states: project the queries, append the new
+    # keys to the k_idx cache at each sequence's last position, then the
+    # forward; against the oracle's projection and forward
+    w = Workload("proj_decode", "decode", 4, 1, 3000, 2999, 128, "fp8", 256, 16)
+    x = synth.make_inputs(w, seed=13)
+    d_model = 1024
+    Xh, Wq = proj_inputs(w.batch, d_model, w.d_idx, "small", 21)
+    _, Wk = proj_inputs(w.batch, d_model, w.d_idx, "small", 22)
+    dst = [b * w.n_k + w.q_pos0 for b in range(w.batch)]
+    q_ref = oracle.index_project(Xh, Wq, "fp8")
+    k_ref = oracle.index_project(Xh, Wk, "fp8", out=raw_bytes(x["k_idx"]).reshape(-1, w.d_idx).copy(),
+                                 out_rows=dst)
+    q_ref_t = torch.from_numpy(q_ref).view(torch.float8_e4m3fn).reshape(w.batch, 1, w.d_idx)
+    k_ref_t = torch.from_numpy(k_ref).view(torch.float8_e4m3fn).reshape(w.batch, w.n_k, w.d_idx)
+    idx_ref, O_ref, lse_ref = oracle.forward(q_ref_t, k_ref_t, x["Q"], x["K"], x["V"], w.q_pos0,
+                                             w.top_k)
+    d = to_dev(x)
+    q = dsa.index_project(Xh.cuda(), Wq.cuda()).reshape(w.batch, 1, w.d_idx)
+    kc = d["k_idx"].reshape(-1, w.d_idx)
+    dsa.index_project(Xh.cuda(), Wk.cuda(), out=kc,
+                      out_rows=torch.tensor(dst, dtype=torch.int32, device="cuda"))
+    idx, O, lse = dsa.forward(q, d["k_idx"], d["Q"], d["K"], d["V"], w.q_pos0, w.top_k)
+    assert np.array_equal(raw_bytes(d["k_idx"]).reshape(-1, w.d_idx), k_ref)
+    assert np.array_equal(idx.cpu().numpy(), idx_ref)
+    assert_attn_close(O, O_ref, lse, lse_ref, "projected decode")
+
+
 def test_all_zero_query_selects_first_keys(gpu_lib):
     w = Workload("zeros", "prefill", 1, 600, 600, 0, 128, "fp8", 64, 2)
     x = synth.make_inputs(w, seed=6)
