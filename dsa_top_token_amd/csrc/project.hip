@@ -35,8 +35,10 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 constexpr int PJ_NT = 256;          // 4 waves
 // Many rows: row tiles per wave and steps of fragments in flight, sized so
 // the accumulators and fragments stay in registers.
+constexpr int PJ_PX = 2;            // many rows: steps of X in flight per wave
 template <int DI> constexpr int pj_rt() { return DI <= 128 ? 4 : 2; }
-template <int DI> constexpr int pj_pf() { return DI <= 128 ? 2 : 1; }
+template <int DI> constexpr int pj_px() { return PJ_PX; }
+template <int DI> constexpr int pj_pw() { return DI <= 128 ? 2 : 1; }
 constexpr int PS_PF = 6;            // split-width kernel: steps in flight per wave
 constexpr int PJ_MIN_WGS = 192;     // fewer row workgroups: the split-width kernel
 constexpr int PS_NT = 1024;         // split-width kernel: 16 waves
@@ -85,14 +87,15 @@ __device__ __forceinline__ bf16x8 ld8(const uint16_t* p) {
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const i32x4*>(p));
 }
 
-template <int DI, int RT, int PF>
+template <int DI, int RT, int PX, int PW>
 __global__ __launch_bounds__(PJ_NT) void project_kernel(ProjectArgs a) {
+    static_assert(PX % PW == 0, "static ring slots");
     constexpr int CT = DI / 16;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n = lane & 15, g = lane >> 4;
     const int r0 = __builtin_amdgcn_readfirstlane((blockIdx.x * (PJ_NT / 64) + wave) * 16 * RT);
     if (r0 >= a.rows) return;  // wave-uniform
-    const int kb = 0, ke = a.d_model;
+    const int ke = a.d_model;
     // A operand: lane (n, g) holds elements [k + 8 g, +8) of row r0 + 16 t + n;
     // B operand: the same elements of W row 16 c + n.
     const uint16_t* xr[RT];
@@ -106,30 +109,38 @@ __global__ __launch_bounds__(PJ_NT) void project_kernel(ProjectArgs a) {
     for (int t = 0; t < RT; ++t)
 #pragma unroll
         for (int c = 0; c < CT; ++c) acc[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // A ring of PF steps of fragments in registers: step k + 32 p sits in
-    // slot p; the loop runs PF steps per pass so every slot index is static.
-    bf16x8 xf[PF][RT], wf[PF][CT];
-    auto load = [&](int p, int k) {
+    // Register rings: X fragments (streamed from HBM) PX steps ahead, W
+    // fragments (L2 hits) PW steps ahead; step k + 32 p uses X slot p and
+    // W slot p % PW, and the loop runs PX steps per pass so every slot index
+    // is static.
+    bf16x8 xf[PX][RT], wf[PW][CT];
+    auto load_x = [&](int p, int k) {
 #pragma unroll
         for (int t = 0; t < RT; ++t) xf[p][t] = ld8(xr[t] + k);
+    };
+    auto load_w = [&](int p, int k) {
 #pragma unroll
         for (int c = 0; c < CT; ++c) wf[p][c] = ld8(wr + c * wstep + k);
     };
 #pragma unroll
-    for (int p = 0; p < PF; ++p)
-        if (kb + 32 * p < ke) load(p, kb + 32 * p);
-    for (int k = kb; k < ke; k += 32 * PF) {
+    for (int p = 0; p < PX; ++p)
+        if (32 * p < ke) load_x(p, 32 * p);
 #pragma unroll
-        for (int p = 0; p < PF; ++p) {
+    for (int p = 0; p < PW; ++p)
+        if (32 * p < ke) load_w(p, 32 * p);
+    for (int k = 0; k < ke; k += 32 * PX) {
+#pragma unroll
+        for (int p = 0; p < PX; ++p) {
             const int kp = k + 32 * p;
             if (kp >= ke) break;  // uniform
             bf16x8 xc[RT], wc[CT];
 #pragma unroll
             for (int t = 0; t < RT; ++t) xc[t] = xf[p][t];
 #pragma unroll
-            for (int c = 0; c < CT; ++c) wc[c] = wf[p][c];
-            // refill the slot with the step PF ahead; it flies under the MFMAs
-            if (kp + 32 * PF < ke) load(p, kp + 32 * PF);
+            for (int c = 0; c < CT; ++c) wc[c] = wf[p % PW][c];
+            // refill both slots; the loads fly under these MFMAs
+            if (kp + 32 * PX < ke) load_x(p, kp + 32 * PX);
+            if (kp + 32 * PW < ke) load_w(p % PW, kp + 32 * PW);
 #pragma unroll
             for (int t = 0; t < RT; ++t)
 #pragma unroll
@@ -211,8 +222,8 @@ hipError_t launch_di(const ProjectArgs& a, hipStream_t s) {
         return hipGetLastError();
     }
     if (nb > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((project_kernel<DI, pj_rt<DI>(), pj_pf<DI>()>), dim3((unsigned)nb),
-                       dim3(PJ_NT), 0, s, a);
+    hipLaunchKernelGGL((project_kernel<DI, pj_rt<DI>(), pj_px<DI>(), pj_pw<DI>()>),
+                       dim3((unsigned)nb), dim3(PJ_NT), 0, s, a);
     return hipGetLastError();
 }
 
