@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstring>
 #include <string>
 #include <utility>
 #include <vector>
@@ -131,10 +132,18 @@ int prefill_slab_rows(const dsa_problem* p) {
 }
 
 struct ForwardLayout {
-    size_t scores, idx, topk, part, prow, total;
+    size_t scores, idx, topk, part, prow, done, total;
 };
 
-ForwardLayout forward_layout(const dsa_problem* p) {
+// Threshold mode's per-row flags (rows a select kernel finished) sit after
+// everything else.
+ForwardLayout with_done(ForwardLayout L, const dsa_problem* p) {
+    L.done = L.total;
+    L.total += align_up((size_t)p->batch * p->n_q * sizeof(uint32_t));
+    return L;
+}
+
+ForwardLayout forward_layout_core(const dsa_problem* p) {
     ForwardLayout L;
     L.scores = 0;
     if (p->n_q > 1) {
@@ -172,6 +181,17 @@ ForwardLayout forward_layout(const dsa_problem* p) {
     L.prow = L.part + align_up(attn_ws_bytes(p));
     L.total = L.prow + ib;
     return L;
+}
+
+ForwardLayout forward_layout(const dsa_problem* p) { return with_done(forward_layout_core(p), p); }
+
+// Order key of a float (float order as unsigned order, -0.0 with +0.0), as
+// the select kernels rank scores.
+uint32_t order_key(float f) {
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
 dsa_status hip_fail(hipError_t e, const char* what) {
@@ -246,6 +266,17 @@ dsa_status forward_impl(const dsa_problem* p, const void* q_idx, const void* k_i
     float* scores = reinterpret_cast<float*>(w + L.scores);
     int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(w + L.idx);
     const int R = slab_rows(p);
+    // Threshold mode: a negative tau keeps every key (the top-k result); else
+    // the select kernels and the rescoring pass drop scores not above tau.
+    dsa::ScoreFloor floor{};
+    const bool floor_on = tau && !(*tau < 0.0f);
+    if (floor_on) {
+        floor.on = 1;
+        floor.key = *tau != *tau ? 0xffffffffu : order_key(*tau);
+        floor.done = reinterpret_cast<uint32_t*>(w + L.done);
+        hipError_t e = dsa::launch_floor_reset(floor.done, (long long)p->batch * p->n_q, st);
+        if (e != hipSuccess) return hip_fail(e, "threshold reset launch");
+    }
 
     dsa::IndexArgs ia{};
     ia.q = q_idx;
@@ -291,6 +322,7 @@ dsa_status forward_impl(const dsa_problem* p, const void* q_idx, const void* k_i
             pa.rstride = NS;
             pa.rows = (p->n_q - s0 + NS - 1) / NS;
             pa.scale = index_scale(p->d_idx);
+            pa.floor = floor;
             static const char* what[4] = {"prefill threshold launch", "prefill indexer launch",
                                           "prefill select launch", "prefill fallback launch"};
             static const int stage[4] = {1, 0, 1, 1};
@@ -329,6 +361,7 @@ dsa_status forward_impl(const dsa_problem* p, const void* q_idx, const void* k_i
             da.fallback = scores;
             da.seq_pos = seq_pos;
             if (pages) da.pages = *pages;
+            da.floor = floor;
             hipError_t e = hipSuccess;
             if (tm) tm->mark(1);
             if ((e = dsa::launch_decode_select(da, ta.ws, 0, st)) != hipSuccess)
@@ -357,8 +390,9 @@ dsa_status forward_impl(const dsa_problem* p, const void* q_idx, const void* k_i
         e = dsa::launch_topk(ta, st);
         if (e != hipSuccess) return hip_fail(e, "topk launch");
     }
-    if (tau) {
-        // threshold mode: drop the selected keys scoring at or below tau
+    if (floor_on) {
+        // threshold mode: drop the selected keys scoring at or below tau in
+        // the rows no select kernel has finished
         dsa::FloorArgs fa{};
         fa.q = q_idx;
         fa.k = k_idx;
@@ -371,6 +405,7 @@ dsa_status forward_impl(const dsa_problem* p, const void* q_idx, const void* k_i
         fa.top_k = p->top_k;
         fa.scale = index_scale(p->d_idx);
         fa.tau = *tau;
+        fa.done = floor.done;
         if (tm) tm->mark(1);
         hipError_t e = dsa::launch_threshold_floor(fa, st);
         if (e != hipSuccess) return hip_fail(e, "threshold launch");

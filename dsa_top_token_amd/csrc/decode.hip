@@ -612,7 +612,15 @@ __global__ __launch_bounds__(SEL_NT) void decode_select_kernel(DecodeArgs a) {
         rem -= res[1];
         __syncthreads();
     }
-    const uint32_t T = kmin + prefix;  // keep every key above T and the first rem keys equal to T
+    uint32_t T = kmin + prefix;  // keep every key above T and the first rem keys equal to T
+    // Threshold mode: when the k-th key is not above the floor, the kept set
+    // is every key above the floor (all candidates, since they outrank the
+    // k-th key); otherwise the top-k set is already above it.
+    const bool floored = a.floor.on && T <= a.floor.key;
+    if (floored) {
+        T = a.floor.key;
+        rem = 0;
+    }
     // Ordered compaction (the list is sorted by index): thread t takes a
     // contiguous block; the T-ties are cut in list order.
     const int E = (cnt + SEL_NT - 1) / SEL_NT;
@@ -634,6 +642,10 @@ __global__ __launch_bounds__(SEL_NT) void decode_select_kernel(DecodeArgs a) {
             ++eb;
         }
     }
+    if (floored)
+        for (int j = (int)(tot >> 16) + tid; j < k; j += SEL_NT) out[j] = -1;
+    if (a.floor.on && tid == 0)
+        a.floor.done[(size_t)b * a.n_q + a.q_row] = 1u;
 }
 
 template <int DT, int D>

@@ -114,6 +114,16 @@ struct AttnArgs {
 
 // One query row per sequence, selection without a materialised score row
 // (sampled threshold, filtered candidates, exact select).
+// Threshold mode inside a select kernel: keep only keys whose order key is
+// above `key` (the order key of tau; 0xffffffff keeps nothing). A select
+// kernel that finishes a row this way (its exact path) sets done[row]
+// (row = b * n_q + query row), so the rescoring pass skips that row.
+struct ScoreFloor {
+    int on;
+    uint32_t key;
+    uint32_t* done;  // [B][n_q]
+};
+
 struct DecodeArgs {
     const void* q;          // [B][n_q][d]
     const void* k;          // [B][n_k][d]
@@ -129,6 +139,7 @@ struct DecodeArgs {
     uint32_t* tau;          // set by launch_decode_select from its workspace
     uint32_t* cnt;
     uint2* cand;
+    ScoreFloor floor;       // threshold mode (optional)
 };
 
 hipError_t launch_index_scores(const IndexArgs& a, hipStream_t s);
@@ -163,6 +174,7 @@ struct PrefillArgs {
     uint32_t* fb_list;
     uint32_t* fb_count;
     float* fb_scores;
+    ScoreFloor floor;       // threshold mode (optional)
 };
 
 int prefill_cap(int top_k);
@@ -186,8 +198,11 @@ struct FloorArgs {
     int B, n_q, n_k, d, dtype, top_k;
     float scale;        // fl32(d^-0.5)
     float tau;
+    const uint32_t* done;  // optional [B][n_q]: rows a select kernel already finished
 };
 hipError_t launch_threshold_floor(const FloorArgs& a, hipStream_t s);
+// Clears the done flags of rows [0, rows) before the selection.
+hipError_t launch_floor_reset(uint32_t* done, long long rows, hipStream_t s);
 
 // Indexer projection: out row out_rows[r] (r when null) of [n_out][d_idx] =
 // encode(fl32(X[r] . W[o])) for X [rows][d_model], W [d_idx][d_model] bf16;

@@ -804,7 +804,15 @@ __device__ __forceinline__ void select_row(const PrefillArgs& a, long long task,
         prefix = res[5];
         rem = res[6];
     }
-    const uint32_t T = kmin + prefix;  // keep every key above T and the first rem keys equal to T
+    uint32_t T = kmin + prefix;  // keep every key above T and the first rem keys equal to T
+    // Threshold mode: when the k-th key is not above the floor, the kept set
+    // is every key above the floor (all on the list, since they outrank the
+    // k-th key); otherwise the top-k set is already above it.
+    const bool floored = a.floor.on && T <= a.floor.key;
+    if (floored) {
+        T = a.floor.key;
+        rem = 0;
+    }
     // Ordered compaction: every key above T, and the T-ties in list order.
     bool gt[PER], eq[PER];
 #pragma unroll
@@ -820,6 +828,9 @@ __device__ __forceinline__ void select_row(const PrefillArgs& a, long long task,
         if (gt[e]) out[gb + min(eb, rem)] = (int32_t)ix[e];
         else if (eq[e] && eb < rem) out[gb + eb] = (int32_t)ix[e];
     }
+    if (floored)
+        for (int j = (int)(tot >> 16) + tid; j < k; j += SL_NT) out[j] = -1;
+    if (a.floor.on && tid == 0) a.floor.done[(size_t)b * a.n_q + qrow(a, i)] = 1u;
 }
 template <int PER>
 __global__ __launch_bounds__(SL_NT) void prefill_select_kernel(PrefillArgs a) {

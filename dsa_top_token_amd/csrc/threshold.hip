@@ -22,18 +22,15 @@ using namespace frag;
 
 constexpr int TF_NT = 1024;  // threads per row
 constexpr int TF_W = TF_NT / 64;
+constexpr long long TF_GRID = 1024;  // workgroups of the row loop (four per CU)
 
-template <int DT, int D>
-__global__ __launch_bounds__(TF_NT) void threshold_floor_kernel(FloorArgs a) {
+// One row: rescore its listed keys, keep those above tau, compact in list
+// order, pad with -1. Every thread of the workgroup calls it.
+template <int DT, int D, int U>
+__device__ __forceinline__ void floor_row(const FloorArgs& a, long long row, int32_t* kept,
+                                          uint32_t* wsum, int wave, int n, int g, int K) {
     constexpr int RB = D * (DT == 0 ? 1 : 2);
-    constexpr int U = RB <= 192 ? 4 : 2;  // tiles a wave loads before its first MFMA
-    __shared__ int32_t kept[kFloorMaxK];  // entry e: its key if kept, else -1
-    __shared__ uint32_t wsum[TF_W];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int n = lane & 15, g = lane >> 4;
-    const long long row = blockIdx.x;  // b * n_q + i
     const int b = (int)(row / a.n_q);
-    const int K = a.top_k;
     int32_t* list = a.idx + row * K;
     Frag<DT, D> fq;  // the query, in every column of the tile
     fq.load(static_cast<const uint8_t*>(a.q) + (size_t)row * RB, g);
@@ -92,11 +89,46 @@ __global__ __launch_bounds__(TF_NT) void threshold_floor_kernel(FloorArgs a) {
 }
 
 template <int DT, int D>
+__global__ __launch_bounds__(TF_NT) void threshold_floor_kernel(FloorArgs a) {
+    constexpr int RB = D * (DT == 0 ? 1 : 2);
+    constexpr int U = RB <= 192 ? 4 : 2;  // tiles a wave loads before its first MFMA
+    __shared__ int32_t kept[kFloorMaxK];  // entry e: its key if kept, else -1
+    __shared__ uint32_t wsum[TF_W];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n = lane & 15, g = lane >> 4;
+    __shared__ uint32_t todo[TF_NT];
+    const int K = a.top_k;
+    // Workgroup w takes rows w, w + G, w + 2G, ... (G workgroups; the rows
+    // left to finish, such as the short first rows of a prefill, spread over
+    // all of them). Most rows are usually done: each pass reads TF_NT flags
+    // at once and compacts the rest into an LDS list, then finishes those
+    // rows one by one.
+    const long long rows = (long long)a.B * a.n_q;
+    const long long G = gridDim.x;
+    for (long long c0 = blockIdx.x; c0 < rows; c0 += G * TF_NT) {
+        const long long r = c0 + G * threadIdx.x;
+        const bool need = r < rows && !(a.done && a.done[r]);  // done: a select kernel applied tau
+        uint32_t total;
+        const uint32_t pos = topk::block_excl_scan<TF_NT>(need ? 1u : 0u, wsum, &total);
+        if (need) todo[pos] = (uint32_t)threadIdx.x;
+        __syncthreads();
+        for (uint32_t q = 0; q < total; ++q) {
+            floor_row<DT, D, U>(a, c0 + G * todo[q], kept, wsum, wave, n, g, K);
+            __syncthreads();  // kept[] and wsum are reused by the next row
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void floor_reset_kernel(uint32_t* done, long long rows) {
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (i < rows) done[i] = 0u;
+}
+
+template <int DT, int D>
 hipError_t launch_d(const FloorArgs& a, hipStream_t s) {
     const long long rows = (long long)a.B * a.n_q;
-    if (rows > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((threshold_floor_kernel<DT, D>), dim3((unsigned)rows), dim3(TF_NT), 0, s,
-                       a);
+    const unsigned grid = (unsigned)(rows < TF_GRID ? rows : TF_GRID);
+    hipLaunchKernelGGL((threshold_floor_kernel<DT, D>), dim3(grid), dim3(TF_NT), 0, s, a);
     return hipGetLastError();
 }
 
@@ -116,6 +148,13 @@ hipError_t launch_dt(const FloorArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+hipError_t launch_floor_reset(uint32_t* done, long long rows, hipStream_t s) {
+    if (rows < 1 || (rows + 255) / 256 > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(floor_reset_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s,
+                       done, rows);
+    return hipGetLastError();
+}
 
 hipError_t launch_threshold_floor(const FloorArgs& a, hipStream_t s) {
     if (a.top_k < 1 || a.top_k > kFloorMaxK || a.B < 1 || a.n_q < 1) return hipErrorInvalidValue;
