@@ -729,6 +729,83 @@ def test_full_prefill_64k(gpu_lib):
         assert np.array_equal(bits(got), bits(ref)), (a, b)
 
 
+def test_full_prefill_64k_threshold(gpu_lib):
+    # The 64K prefill in threshold mode (tau 14) at full size: sampled rows
+    # against the oracle, properties on every row.
+    w = synth.WORKLOADS["prefill_64k"]
+    tau = 14.0
+    say("full-size %s threshold: generating inputs" % w.name)
+    x = synth.make_inputs(w, seed=0)
+    d = to_dev(x)
+    say("full-size %s threshold: GPU forward" % w.name)
+    idx, O, lse = dsa.forward(d["q_idx"], d["k_idx"], d["Q"], d["K"], d["V"], 0, w.top_k,
+                              tau=tau)
+    torch.cuda.synchronize()
+    kept = (idx >= 0).sum(-1)
+    pos = torch.arange(w.n_q, device=idx.device)[None, :, None]
+    slot = torch.arange(w.top_k, device=idx.device)[None, None, :]
+    valid = slot < kept[..., None]
+    assert torch.all(torch.where(valid, (idx >= 0) & (idx <= pos), idx == -1))
+    inc = idx[:, :, 1:] > idx[:, :, :-1]
+    assert torch.all(torch.where(valid[:, :, 1:], inc, True))
+    assert int(kept.min()) == 0 and int(kept.max()) == w.top_k  # both regimes occur
+    for (a, b) in prefill_samples(w.n_q, w.top_k):
+        say("full-size %s threshold: oracle rows [%d, %d)" % (w.name, a, b))
+        idx_ref, O_ref, lse_ref = oracle.forward(x["q_idx"], x["k_idx"], x["Q"], x["K"], x["V"],
+                                                 0, w.top_k, a, b, tau=tau)
+        assert np.array_equal(idx[:, a:b].cpu().numpy(), idx_ref), (a, b)
+        assert_attn_close(O[:, a:b], O_ref, lse[:, a:b], lse_ref, "rows %d-%d" % (a, b))
+
+
+def test_full_decode_128k_projected(gpu_lib):
+    # The projected 128K decode step at full size: q rows and the appended
+    # key rows byte for byte, then every sequence's forward against the
+    # oracle's chain.
+    w = synth.WORKLOADS["decode_128k_projected"]
+    say("full-size %s: generating inputs" % w.name)
+    x = synth.make_inputs(w, seed=0)
+    d = to_dev(x)
+    B, di = w.batch, w.d_idx
+    dst = [b * w.n_k + w.q_pos0 for b in range(B)]
+    say("full-size %s: GPU projections and forward" % w.name)
+    q = dsa.index_project(d["X"], d["W_q"]).reshape(B, 1, di)
+    dsa.index_project(d["X"], d["W_k"], out=d["k_idx"].view(-1, di),
+                      out_rows=torch.tensor(dst, dtype=torch.int32, device="cuda"))
+    idx, O, lse = dsa.forward(q, d["k_idx"], d["Q"], d["K"], d["V"], w.q_pos0, w.top_k)
+    torch.cuda.synchronize()
+    say("full-size %s: oracle projections" % w.name)
+    q_ref = oracle.index_project(x["X"], x["W_q"], "fp8")
+    k_new = oracle.index_project(x["X"], x["W_k"], "fp8")
+    assert np.array_equal(raw_bytes(q).reshape(B, di), q_ref)
+    kc = raw_bytes(d["k_idx"]).reshape(-1, di)
+    assert np.array_equal(kc[dst], k_new)
+    k_ref = raw_bytes(x["k_idx"]).reshape(-1, di).copy()
+    k_ref[dst] = k_new
+    assert np.array_equal(kc, k_ref)  # no other cache row changed
+    q_t = torch.from_numpy(q_ref).view(torch.float8_e4m3fn).reshape(B, 1, di)
+    k_t = torch.from_numpy(k_ref).view(torch.float8_e4m3fn).reshape(B, w.n_k, di)
+    say("full-size %s: oracle forward" % w.name)
+    idx_ref, O_ref, lse_ref = oracle.forward(q_t, k_t, x["Q"], x["K"], x["V"], w.q_pos0, w.top_k)
+    assert np.array_equal(idx.cpu().numpy(), idx_ref)
+    assert_attn_close(O, O_ref, lse, lse_ref, w.name)
+
+
+def test_full_prefill_64k_projection_rows(gpu_lib):
+    # The 64K prefill's projections at full size (one launch over all 65536
+    # hidden rows), sampled rows against the oracle byte for byte.
+    w = synth.WORKLOADS["prefill_64k_projected"]
+    say("full-size %s: generating hidden states" % w.name)
+    x = synth.make_inputs(w, seed=0, parts=("X",))
+    X = x["X"].cuda()
+    for wname in ("W_q", "W_k"):
+        say("full-size %s: projection %s" % (w.name, wname))
+        out = dsa.index_project(X, x[wname].cuda())
+        torch.cuda.synchronize()
+        for (a, b) in [(0, 16), (31999, 32040), (w.n_q - 9, w.n_q)]:
+            ref = oracle.index_project(x["X"][a:b], x[wname], "fp8")
+            assert np.array_equal(raw_bytes(out[a:b]), ref), (wname, a, b)
+
+
 def test_full_prefill_128k_bf16(gpu_lib):
     w = synth.WORKLOADS["prefill_128k"]
     x, d = run_full(w, prefill_samples(w.n_q, w.top_k))
