@@ -32,17 +32,17 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int PJ_NT = 256;          // 4 waves
-// Many rows: row tiles per wave and steps of fragments in flight, sized so
-// the accumulators and fragments stay in registers.
-constexpr int PJ_PX = 2;            // many rows: steps of X in flight per wave
+// Many-rows kernel: 4 waves; row tiles per wave and steps of X and W
+// fragments in flight, sized so accumulators and fragments stay in registers.
+constexpr int PJ_NT = 256;
 template <int DI> constexpr int pj_rt() { return DI <= 128 ? 4 : 2; }
-template <int DI> constexpr int pj_px() { return PJ_PX; }
+constexpr int PJ_PX = 2;
 template <int DI> constexpr int pj_pw() { return DI <= 128 ? 2 : 1; }
-constexpr int PS_PF = 6;            // split-width kernel: steps in flight per wave
-constexpr int PJ_MIN_WGS = 192;     // fewer row workgroups: the split-width kernel
-constexpr int PS_NT = 1024;         // split-width kernel: 16 waves
+constexpr int PJ_MIN_WGS = 192;     // fewer row workgroups than this: the split-width kernel
+// Split-width kernel: 16 waves, steps of fragments in flight per wave.
+constexpr int PS_NT = 1024;
 constexpr int PS_W = PS_NT / 64;
+constexpr int PS_PF = 6;
 
 // e4m3fn code of v: nearest value, ties to an even mantissa; |v| >= 448
 // saturates (the values in [448, 464] round there anyway); NaN -> 0x7f.
@@ -222,7 +222,7 @@ hipError_t launch_di(const ProjectArgs& a, hipStream_t s) {
         return hipGetLastError();
     }
     if (nb > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((project_kernel<DI, pj_rt<DI>(), pj_px<DI>(), pj_pw<DI>()>),
+    hipLaunchKernelGGL((project_kernel<DI, pj_rt<DI>(), PJ_PX, pj_pw<DI>()>),
                        dim3((unsigned)nb), dim3(PJ_NT), 0, s, a);
     return hipGetLastError();
 }
