@@ -39,6 +39,15 @@ template <int DI> constexpr int pj_rt() { return DI <= 128 ? 4 : 2; }
 constexpr int PJ_PX = 2;
 template <int DI> constexpr int pj_pw() { return DI <= 128 ? 2 : 1; }
 constexpr int PJ_MIN_WGS = 192;     // fewer row workgroups than this: the split-width kernel
+// LDS-staged many-rows kernel (d_idx <= 128, model width a multiple of 64):
+// chunks of 64 model-width columns (128 bytes of every X and W row) in a ring
+// of pl_nbuf buffers, pl_nbuf - 1 chunks in flight. Measured at 65536 x 4096:
+// two workgroups per CU beat a deeper ring (d_idx 128: 2 row tiles per wave,
+// 2 buffers, 64 KB; d_idx <= 64: 1 row tile, 3 buffers).
+template <int DI> constexpr int pl_rt() { return DI <= 64 ? 1 : 2; }
+template <int DI> constexpr int pl_nbuf() { return DI <= 64 ? 3 : 2; }
+template <int DI> constexpr int pl_rows() { return 4 * 16 * pl_rt<DI>(); }  // per workgroup
+constexpr int kNontemporal = 2;           // cache policy of the X copies (read once)
 // Split-width kernel: 16 waves, steps of fragments in flight per wave.
 constexpr int PS_NT = 1024;
 constexpr int PS_W = PS_NT / 64;
@@ -85,6 +94,135 @@ __device__ __forceinline__ void store_code(const ProjectArgs& a, int r, int col,
 
 __device__ __forceinline__ bf16x8 ld8(const uint16_t* p) {
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const i32x4*>(p));
+}
+
+// s_waitcnt with vmcnt = N (expcnt and lgkmcnt left open).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
+}
+
+// Waits until at most `ahead` chunks of OPS copies each are in flight
+// (0 <= ahead <= A).
+template <int A, int OPS>
+__device__ __forceinline__ void wait_chunks(int ahead) {
+    if constexpr (A > 0) {
+        if (ahead >= A) {
+            wait_vmcnt<A * OPS>();
+            return;
+        }
+        wait_chunks<A - 1, OPS>(ahead);
+    } else {
+        wait_vmcnt<0>();
+    }
+}
+
+// Slot of granule j (16 bytes) of row r in a chunk of 128-byte rows: each
+// copy instruction still moves 8 whole rows (1 KB) of global memory, and the
+// 16 rows a fragment read touches (fixed j) land in 16 distinct bank groups.
+__device__ __forceinline__ int pl_slot(int r, int j) {
+    return 8 * r + (j ^ ((r & 7) ^ ((r >> 3) & 1)));
+}
+
+// Many rows through LDS: wave w of the workgroup owns PL_RT tiles of 16 rows
+// and every feature. Per 64-column chunk the wave copies its X rows with
+// global->LDS copies of 1 KB (8 whole 128-byte lines each) and a
+// quarter of the chunk's W rows (shared by the workgroup), waits for its own
+// copies, meets the other waves at a barrier, then reads fragments from LDS
+// for two 32-wide MFMA steps.
+template <int DI>
+__global__ __launch_bounds__(PJ_NT) void project_lds_kernel(ProjectArgs a) {
+    constexpr int PL_RT = pl_rt<DI>(), PL_NBUF = pl_nbuf<DI>(), PL_ROWS = pl_rows<DI>();
+    constexpr int CT = DI / 16;
+    constexpr int WR = 16 * PL_RT;    // rows per wave
+    constexpr int XB = 4 * WR * 128;  // X bytes of a chunk (4 waves)
+    constexpr int WB = DI * 128;      // W bytes of a chunk
+    constexpr int X_OPS = WR / 8;     // X copies per wave per chunk
+    constexpr int W_OPS = DI / 32;    // W copies per wave per chunk (DI / 8 over 4 waves)
+    constexpr int OPS = X_OPS + W_OPS;
+    static_assert(DI % 32 == 0 && DI <= 128 && PL_NBUF * (XB + WB) <= 160 * 1024, "LDS ring");
+    static_assert(PL_NBUF >= 2 && (PL_NBUF - 2) * OPS < 64, "copies in flight");
+    __shared__ __attribute__((aligned(16))) uint8_t ring[PL_NBUF][XB + WB];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n = lane & 15, g = lane >> 4;
+    const int r0 = (int)blockIdx.x * PL_ROWS + WR * wave;  // may pass the last row: clamped
+    const int nch = a.d_model / 64;
+    const size_t rowb = (size_t)a.d_model * 2;
+    const uint8_t* Xb = reinterpret_cast<const uint8_t*>(a.X);
+    const uint8_t* Wb = reinterpret_cast<const uint8_t*>(a.W);
+    // copy lane l moves granule (l % 8) ^ f(r) of row r = 8 i + l / 8 into slot 64 i + l
+    const int cr = lane >> 3, cp = lane & 7;
+    auto issue = [&](int c) {
+        uint8_t* buf = ring[c % PL_NBUF];
+        const size_t kb = (size_t)c * 128;
+#pragma unroll
+        for (int i = 0; i < X_OPS; ++i) {
+            const int r = 8 * i + cr;
+            const int j = cp ^ ((r & 7) ^ ((r >> 3) & 1));
+            const size_t grow = (size_t)min(r0 + r, a.rows - 1);
+            __builtin_amdgcn_global_load_lds(Xb + grow * rowb + kb + 16 * j,
+                                             buf + WR * 128 * wave + 1024 * i, 16, 0, kNontemporal);
+        }
+#pragma unroll
+        for (int u = 0; u < W_OPS; ++u) {
+            const int i = wave + 4 * u;
+            const int r = 8 * i + cr;
+            const int j = cp ^ ((r & 7) ^ ((r >> 3) & 1));
+            __builtin_amdgcn_global_load_lds(Wb + (size_t)r * rowb + kb + 16 * j,
+                                             buf + XB + 1024 * i, 16, 0, 0);
+        }
+    };
+    f32x4 acc[PL_RT][CT];
+#pragma unroll
+    for (int t = 0; t < PL_RT; ++t)
+#pragma unroll
+        for (int c = 0; c < CT; ++c) acc[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // PL_NBUF - 1 chunks ahead of the one being read
+#pragma unroll
+    for (int c = 0; c < PL_NBUF - 1; ++c)
+        if (c < nch) issue(c);
+    for (int c = 0; c < nch; ++c) {
+        // chunk c has landed once only the later chunks' copies remain; the
+        // barrier (no release fence, which would wait for every copy in
+        // flight) also means every wave is done reading chunk c - 1
+        __builtin_amdgcn_sched_barrier(0);
+        wait_chunks<PL_NBUF - 2, OPS>(min(PL_NBUF - 2, nch - 1 - c));
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        if (c + PL_NBUF - 1 < nch) issue(c + PL_NBUF - 1);  // into chunk c - 1's buffer
+        const uint8_t* xs = ring[c % PL_NBUF] + WR * 128 * wave;
+        const uint8_t* ws = ring[c % PL_NBUF] + XB;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            bf16x8 af[PL_RT], bf[CT];
+#pragma unroll
+            for (int t = 0; t < PL_RT; ++t)
+                af[t] = __builtin_bit_cast(
+                    bf16x8, *reinterpret_cast<const i32x4*>(xs + 16 * pl_slot(16 * t + n, 4 * s + g)));
+#pragma unroll
+            for (int f = 0; f < CT; ++f)
+                bf[f] = __builtin_bit_cast(
+                    bf16x8, *reinterpret_cast<const i32x4*>(ws + 16 * pl_slot(16 * f + n, 4 * s + g)));
+#pragma unroll
+            for (int t = 0; t < PL_RT; ++t)
+#pragma unroll
+                for (int f = 0; f < CT; ++f)
+                    acc[t][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[t], bf[f], acc[t][f], 0,
+                                                                       0, 0);
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < PL_RT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = r0 + 16 * t + 4 * g + i;
+            if (r >= a.rows) continue;
+#pragma unroll
+            for (int f = 0; f < CT; ++f) store_code(a, r, 16 * f + n, acc[t][f][i]);
+        }
 }
 
 template <int DI, int RT, int PX, int PW>
@@ -222,6 +360,13 @@ hipError_t launch_di(const ProjectArgs& a, hipStream_t s) {
         return hipGetLastError();
     }
     if (nb > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    if constexpr (DI <= 128) {
+        if (a.d_model % 64 == 0) {
+            const long long nl = (a.rows + pl_rows<DI>() - 1) / pl_rows<DI>();
+            hipLaunchKernelGGL((project_lds_kernel<DI>), dim3((unsigned)nl), dim3(PJ_NT), 0, s, a);
+            return hipGetLastError();
+        }
+    }
     hipLaunchKernelGGL((project_kernel<DI, pj_rt<DI>(), PJ_PX, pj_pw<DI>()>),
                        dim3((unsigned)nb), dim3(PJ_NT), 0, s, a);
     return hipGetLastError();

@@ -464,6 +464,12 @@ PROJ = [
     (9000, 256, 256, "bf16", "wide"),     # two row tiles per wave
     (20000, 1024, 96, "fp8", "small"),
     (70001, 128, 64, "fp8", "wide"),
+    # the LDS-staged many-rows kernel at each of its ring shapes, odd chunk
+    # counts, and the register kernel for a model width not a multiple of 64
+    (50000, 192, 128, "fp8", "wide"),
+    (60001, 320, 96, "bf16", "small"),
+    (52000, 64, 32, "fp8", "wide"),
+    (50001, 160, 128, "fp8", "small"),
 ]
 
 
