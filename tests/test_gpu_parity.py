@@ -639,6 +639,24 @@ def run_full(w, sample_rows, gen_device="cpu"):
     return x, d
 
 
+def test_max_size_decode(gpu_lib):
+    # The largest problem the library accepts in one dimension: a decode row
+    # of 4194304 keys (past the sampled-threshold select's 1M keys, so the
+    # chunked top-k path over written score rows) with the largest top_k.
+    w = Workload("max_keys_decode", "decode", 1, 1, 4194304, 4194303, 128, "fp8", 4096, 16)
+    say("max-size decode: generating inputs")
+    x = synth.make_inputs(w, seed=2)
+    d = to_dev(x)
+    say("max-size decode: GPU forward")
+    idx, O, lse = dsa.forward(d["q_idx"], d["k_idx"], d["Q"], d["K"], d["V"], w.q_pos0, w.top_k)
+    torch.cuda.synchronize()
+    say("max-size decode: oracle")
+    idx_ref, O_ref, lse_ref = oracle.forward(x["q_idx"], x["k_idx"], x["Q"], x["K"], x["V"],
+                                             w.q_pos0, w.top_k)
+    assert np.array_equal(idx.cpu().numpy(), idx_ref)
+    assert_attn_close(O, O_ref, lse, lse_ref, "max-size decode")
+
+
 def test_full_decode_32k(gpu_lib):
     w = synth.WORKLOADS["decode_32k"]
     run_full(w, [(0, 1)])
