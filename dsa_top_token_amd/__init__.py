@@ -31,8 +31,8 @@ HEAD_DIM = 128
 EXPORTS = ("dsa_workspace_size", "dsa_index_scores", "dsa_topk", "dsa_sparse_attn",
            "dsa_forward", "dsa_forward_ragged", "dsa_forward_paged", "dsa_forward_timed",
            "dsa_forward_ragged_timed", "dsa_forward_paged_timed", "dsa_forward_threshold",
-           "dsa_forward_threshold_timed", "dsa_index_project", "dsa_status_str",
-           "dsa_last_error")
+           "dsa_forward_threshold_timed", "dsa_forward_ext", "dsa_forward_ext_timed",
+           "dsa_index_project", "dsa_status_str", "dsa_last_error")
 
 
 class Problem(ctypes.Structure):
@@ -45,6 +45,12 @@ class Pages(ctypes.Structure):
     """dsa_pages: a paged key layout (block table on the device)."""
     _fields_ = [("block_table", ctypes.c_void_p), ("page_size", ctypes.c_int32),
                 ("pages_per_seq", ctypes.c_int32), ("n_pages", ctypes.c_int32)]
+
+
+class Options(ctypes.Structure):
+    """dsa_forward_options: layout and mode of dsa_forward_ext."""
+    _fields_ = [("seq_pos", ctypes.c_void_p), ("pages", ctypes.POINTER(Pages)),
+                ("threshold_mode", ctypes.c_int32), ("tau", ctypes.c_float)]
 
 
 class DSAError(RuntimeError):
@@ -86,8 +92,11 @@ def load():
             lib.dsa_forward_threshold.argtypes = [PP, F, P, P, P, P, P, P, P, P, P, S, P]
             lib.dsa_forward_threshold_timed.argtypes = [PP, F, P, P, P, P, P, P, P, P, P, S, P,
                                                         P, P]
+            PO = ctypes.POINTER(Options)
+            lib.dsa_forward_ext.argtypes = [PP, PO, P, P, P, P, P, P, P, P, P, S, P]
+            lib.dsa_forward_ext_timed.argtypes = [PP, PO, P, P, P, P, P, P, P, P, P, S, P, P, P]
             lib.dsa_index_project.argtypes = [I, I, I, I, P, P, P, P, I, P]
-            for f in (lib.dsa_index_project,
+            for f in (lib.dsa_index_project, lib.dsa_forward_ext, lib.dsa_forward_ext_timed,
                       lib.dsa_workspace_size, lib.dsa_index_scores, lib.dsa_topk,
                       lib.dsa_sparse_attn, lib.dsa_forward, lib.dsa_forward_ragged,
                       lib.dsa_forward_paged, lib.dsa_forward_timed,
@@ -197,6 +206,12 @@ def sparse_attn(Q, K, V, idx, want_lse=True, q_pos0=None):
     return O, lse
 
 
+def _options(seq_pos, pages, tau):
+    """dsa_forward_options for a ragged and/or paged batch in threshold mode."""
+    return Options(None if seq_pos is None else seq_pos.data_ptr(),
+                   None if pages is None else ctypes.pointer(pages), 1, float(tau))
+
+
 class Forward:
     """dsa_forward with its workspace allocated once for a fixed problem."""
 
@@ -212,9 +227,14 @@ class Forward:
         pages (a Pages), k_idx, K and V are the page pools
         (dsa_forward_paged); with tau (a float), threshold-mode selection
         (dsa_forward_threshold)."""
+        if tau is not None and (seq_pos is not None or pages is not None):
+            opt = _options(seq_pos, pages, tau)
+            _check(load().dsa_forward_ext(
+                ctypes.byref(self.p), ctypes.byref(opt), _ptr(q_idx), _ptr(k_idx), _ptr(Q),
+                _ptr(K), _ptr(V), _ptr(idx_out), _ptr(O), _ptr(lse), _ptr(self.ws), self.ws_bytes,
+                _stream(self.device)))
+            return
         if tau is not None:
-            if seq_pos is not None or pages is not None:
-                raise ValueError("threshold mode takes the contiguous dsa_forward layout")
             _check(load().dsa_forward_threshold(
                 ctypes.byref(self.p), float(tau), _ptr(q_idx), _ptr(k_idx), _ptr(Q), _ptr(K),
                 _ptr(V), _ptr(idx_out), _ptr(O), _ptr(lse), _ptr(self.ws), self.ws_bytes,
@@ -244,9 +264,14 @@ class Forward:
         attention] milliseconds, number of row slabs). Blocks until done."""
         ms = (ctypes.c_float * 3)()
         slabs = ctypes.c_int32(0)
+        if tau is not None and (seq_pos is not None or pages is not None):
+            opt = _options(seq_pos, pages, tau)
+            _check(load().dsa_forward_ext_timed(
+                ctypes.byref(self.p), ctypes.byref(opt), _ptr(q_idx), _ptr(k_idx), _ptr(Q),
+                _ptr(K), _ptr(V), _ptr(idx_out), _ptr(O), _ptr(lse), _ptr(self.ws), self.ws_bytes,
+                _stream(self.device), ms, ctypes.byref(slabs)))
+            return list(ms), slabs.value
         if tau is not None:
-            if seq_pos is not None or pages is not None:
-                raise ValueError("threshold mode takes the contiguous dsa_forward layout")
             _check(load().dsa_forward_threshold_timed(
                 ctypes.byref(self.p), float(tau), _ptr(q_idx), _ptr(k_idx), _ptr(Q), _ptr(K),
                 _ptr(V), _ptr(idx_out), _ptr(O), _ptr(lse), _ptr(self.ws), self.ws_bytes,
@@ -345,11 +370,12 @@ def make_pages(block_table, page_size, n_pages) -> Pages:
 
 
 def forward_paged(q_idx, k_pool, Q, K_pool, V_pool, block_table, page_size, seq_pos, top_k,
-                  want_idx=True, want_lse=True):
+                  want_idx=True, want_lse=True, tau=None):
     """The fused chain over a paged layout (dsa_forward_paged): one query per
     sequence at position seq_pos[b]; k_pool [n_pages, page_size, d_idx], K_pool
     and V_pool [n_pages, page_size, 128]; block_table int32 [B, pages_per_seq].
-    Returns (idx with logical key indices, O, lse) as forward()."""
+    With tau, threshold-mode selection (dsa_forward_ext). Returns (idx with
+    logical key indices, O, lse) as forward()."""
     _dev_tensor(q_idx, "q_idx", _IDX_DTYPES, 3)
     _dev_tensor(k_pool, "k_pool", (q_idx.dtype,), 3)
     _dev_tensor(Q, "Q", (torch.bfloat16,), 4)
@@ -369,5 +395,6 @@ def forward_paged(q_idx, k_pool, Q, K_pool, V_pool, block_table, page_size, seq_
     idx = torch.empty((B, n_q, top_k), dtype=torch.int32, device=dev) if want_idx else None
     O = torch.empty_like(Q)
     lse = torch.empty((B, n_q, H), dtype=torch.float32, device=dev) if want_lse else None
-    Forward(p, dev)(q_idx, k_pool, Q, K_pool, V_pool, O, idx, lse, seq_pos=seq_pos, pages=pages)
+    Forward(p, dev)(q_idx, k_pool, Q, K_pool, V_pool, O, idx, lse, seq_pos=seq_pos, pages=pages,
+                    tau=tau)
     return idx, O, lse

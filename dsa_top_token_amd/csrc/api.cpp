@@ -406,6 +406,7 @@ dsa_status forward_impl(const dsa_problem* p, const void* q_idx, const void* k_i
         fa.scale = index_scale(p->d_idx);
         fa.tau = *tau;
         fa.done = floor.done;
+        if (pages) fa.pages = *pages;
         if (tm) tm->mark(1);
         hipError_t e = dsa::launch_threshold_floor(fa, st);
         if (e != hipSuccess) return hip_fail(e, "threshold launch");
@@ -666,6 +667,52 @@ dsa_status dsa_forward_threshold_timed(const dsa_problem* p, float tau, const vo
     for (int i = 0; i < 3; ++i) stage_ms[i] = 0.f;
     dsa_status s = forward_impl(p, q_idx, k_idx, Q, K, V, idx_out, O, lse, ws, ws_bytes, stream,
                                 &tm, n_slabs, nullptr, nullptr, &tau);
+    hipError_t e = tm.finish(stage_ms);
+    if (s != DSA_OK) return s;
+    if (e != hipSuccess) return hip_fail(e, "stage timing events");
+    return ok();
+}
+
+// Arguments of dsa_forward_ext: the layout (ragged, paged) and the mode.
+dsa_status check_options(const dsa_problem* p, const dsa_forward_options* o, dsa::KeyPages* kp) {
+    if (!o) return check_problem(p);
+    if (o->pages) return check_paged(p, o->seq_pos, o->pages, kp);
+    if (o->seq_pos) return check_ragged(p, o->seq_pos);
+    return check_problem(p);
+}
+
+dsa_status forward_ext(const dsa_problem* p, const dsa_forward_options* o, const void* q_idx,
+                       const void* k_idx, const void* Q, const void* K, const void* V,
+                       int32_t* idx_out, void* O, float* lse, void* ws, size_t ws_bytes,
+                       void* stream, StageTimer* tm, int32_t* n_slabs) {
+    dsa::KeyPages kp{};
+    dsa_status s = check_options(p, o, &kp);
+    if (s != DSA_OK) return s;
+    const float* tau = o && o->threshold_mode ? &o->tau : nullptr;
+    return forward_impl(p, q_idx, k_idx, Q, K, V, idx_out, O, lse, ws, ws_bytes, stream, tm,
+                        n_slabs, o ? o->seq_pos : nullptr, o && o->pages ? &kp : nullptr, tau);
+}
+
+dsa_status dsa_forward_ext(const dsa_problem* p, const dsa_forward_options* options,
+                           const void* q_idx, const void* k_idx, const void* Q, const void* K,
+                           const void* V, int32_t* idx_out, void* O, float* lse, void* ws,
+                           size_t ws_bytes, void* stream) {
+    dsa_status s = forward_ext(p, options, q_idx, k_idx, Q, K, V, idx_out, O, lse, ws, ws_bytes,
+                               stream, nullptr, nullptr);
+    return s == DSA_OK ? ok() : s;
+}
+
+dsa_status dsa_forward_ext_timed(const dsa_problem* p, const dsa_forward_options* options,
+                                 const void* q_idx, const void* k_idx, const void* Q,
+                                 const void* K, const void* V, int32_t* idx_out, void* O,
+                                 float* lse, void* ws, size_t ws_bytes, void* stream,
+                                 float* stage_ms, int32_t* n_slabs) {
+    if (!stage_ms) return fail(DSA_E_NULL, "stage_ms is NULL");
+    StageTimer tm;
+    tm.st = static_cast<hipStream_t>(stream);
+    for (int i = 0; i < 3; ++i) stage_ms[i] = 0.f;
+    dsa_status s = forward_ext(p, options, q_idx, k_idx, Q, K, V, idx_out, O, lse, ws, ws_bytes,
+                               stream, &tm, n_slabs);
     hipError_t e = tm.finish(stage_ms);
     if (s != DSA_OK) return s;
     if (e != hipSuccess) return hip_fail(e, "stage timing events");

@@ -199,6 +199,7 @@ struct FloorArgs {
     float scale;        // fl32(d^-0.5)
     float tau;
     const uint32_t* done;  // optional [B][n_q]: rows a select kernel already finished
+    KeyPages pages;        // k rows (a paged layout's pool when pages.table is set)
 };
 hipError_t launch_threshold_floor(const FloorArgs& a, hipStream_t s);
 // Clears the done flags of rows [0, rows) before the selection.

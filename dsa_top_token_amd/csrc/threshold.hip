@@ -34,7 +34,7 @@ __device__ __forceinline__ void floor_row(const FloorArgs& a, long long row, int
     int32_t* list = a.idx + row * K;
     Frag<DT, D> fq;  // the query, in every column of the tile
     fq.load(static_cast<const uint8_t*>(a.q) + (size_t)row * RB, g);
-    const uint8_t* kb = static_cast<const uint8_t*>(a.k) + (size_t)b * a.n_k * RB;
+    const uint8_t* kpool = static_cast<const uint8_t*>(a.k);
     // Tile t holds entries 16 t .. 16 t + 15 as the MFMA's key rows: lane
     // (n, g) loads entry 16 t + n and gets the scores of entries
     // 16 t + 4 g + r (r = 0..3). A wave takes tiles t0 + TF_W u, u < U, at a
@@ -52,7 +52,8 @@ __device__ __forceinline__ void floor_row(const FloorArgs& a, long long row, int
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             any[u] = __ballot(j[u] >= 0) != 0ull;  // lists are -1 padded at the end
-            if (any[u]) fk[u].load(kb + (size_t)(j[u] >= 0 ? j[u] : 0) * RB, g);
+            if (any[u])
+                fk[u].load(kpool + (size_t)key_row(a.pages, b, a.n_k, j[u] >= 0 ? j[u] : 0) * RB, g);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {

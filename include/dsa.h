@@ -232,6 +232,37 @@ dsa_status dsa_forward_timed(const dsa_problem* p, const void* q_idx,
                              float* lse, void* ws, size_t ws_bytes,
                              void* stream, float* stage_ms, int32_t* n_slabs);
 
+/* Layout and mode of dsa_forward_ext (any combination):
+ *   seq_pos         optional: a ragged decode batch, as dsa_forward_ragged
+ *   pages           optional: a paged key layout, as dsa_forward_paged (needs
+ *                   seq_pos; k_idx, K and V are then the pools)
+ *   threshold_mode  nonzero: threshold-mode selection at tau, as
+ *                   dsa_forward_threshold */
+typedef struct {
+    const int32_t* seq_pos;
+    const dsa_pages* pages;
+    int32_t threshold_mode;
+    float tau;
+} dsa_forward_options;
+
+/* dsa_forward with the options above (NULL options: dsa_forward itself). The
+ * definitions, layouts, workspace and errors are those of the entry points
+ * each option stands for; results equal theirs bit for bit. */
+dsa_status dsa_forward_ext(const dsa_problem* p, const dsa_forward_options* options,
+                           const void* q_idx, const void* k_idx, const void* Q,
+                           const void* K, const void* V, int32_t* idx_out, void* O,
+                           float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* dsa_forward_ext for profiling, as dsa_forward_timed (blocks until the
+ * stream has finished; stage_ms must not be NULL). */
+dsa_status dsa_forward_ext_timed(const dsa_problem* p,
+                                 const dsa_forward_options* options,
+                                 const void* q_idx, const void* k_idx,
+                                 const void* Q, const void* K, const void* V,
+                                 int32_t* idx_out, void* O, float* lse,
+                                 void* ws, size_t ws_bytes, void* stream,
+                                 float* stage_ms, int32_t* n_slabs);
+
 /* The indexer projections (DSA page, section 3.2: query_proj and key_proj
  * are bias-free linear maps from the model width d_model to the indexer
  * width d_idx; section 4.1: the index stage runs in FP8). For each input row

@@ -56,10 +56,13 @@ def _load():
             lib.oracle_select_threshold.argtypes = [I, I, I, I, I, F, P, P]
             lib.oracle_forward_threshold.argtypes = ([I] * 7 + [F, I, I] + [P] * 5 +
                                                      [I, I, P, P, P])
+            lib.oracle_forward_seqpos_threshold.argtypes = ([I, I, I, P] + [I] * 3 + [F, I, I] +
+                                                            [P] * 5 + [I, I, P, P, P])
             lib.oracle_index_project.argtypes = [I, I, I, I, P, P, P, I, P]
             lib.oracle_encode.argtypes = [I, I, P, P]
             lib.oracle_num_threads.argtypes = []
             for f in (lib.oracle_index_project, lib.oracle_encode,
+                      lib.oracle_forward_seqpos_threshold,
                       lib.oracle_index_scores, lib.oracle_topk,
                       lib.oracle_sparse_attn, lib.oracle_forward,
                       lib.oracle_forward_seqpos, lib.oracle_select_threshold,
@@ -213,8 +216,15 @@ def forward(q_idx, k_idx, Q, K, V, q_pos0: int, k: int, q_begin: int = 0,
     idx = np.empty((B, rows, k), np.int32)
     O = np.empty((B, rows, H, D), np.float32)
     lse = np.empty((B, rows, H), np.float32)
+    if tau is not None and seq_pos is not None:
+        sp = np.ascontiguousarray(np.asarray(seq_pos, np.int32).reshape(B))
+        rc = _load().oracle_forward_seqpos_threshold(
+            B, n_q, n_k, _ptr(sp), d, _dtype_code(q_idx, dtype), k, float(np.float32(tau)), H, D,
+            _ptr(qi), _ptr(ki), _ptr(q), _ptr(kk), _ptr(vv), q_begin, q_end, _ptr(idx), _ptr(O),
+            _ptr(lse))
+        assert rc == 0, rc
+        return idx, O, lse
     if tau is not None:
-        assert seq_pos is None, "threshold mode takes one q_pos0"
         rc = _load().oracle_forward_threshold(B, n_q, n_k, q_pos0, d, _dtype_code(q_idx, dtype),
                                               k, float(np.float32(tau)), H, D, _ptr(qi),
                                               _ptr(ki), _ptr(q), _ptr(kk), _ptr(vv), q_begin,

@@ -442,6 +442,17 @@ int oracle_forward_seqpos(int B, int n_q, int n_k, const int32_t* seq_pos, int d
                         V, q_begin, q_end, idx, O, lse);
 }
 
+/* oracle_forward_seqpos with threshold-mode selection (thresh_row). */
+int oracle_forward_seqpos_threshold(int B, int n_q, int n_k, const int32_t* seq_pos, int d,
+                                    int dtype, int k, float tau, int H, int D, const void* q_idx,
+                                    const void* k_idx, const uint16_t* Q, const uint16_t* K,
+                                    const uint16_t* V, int q_begin, int q_end, int32_t* idx,
+                                    float* O, float* lse) {
+    if (!seq_pos) return -1;
+    return forward_rows(B, n_q, n_k, 0, seq_pos, d, dtype, k, &tau, H, D, q_idx, k_idx, Q, K, V,
+                        q_begin, q_end, idx, O, lse);
+}
+
 /* Threads an OpenMP parallel region of this library runs with. */
 int oracle_num_threads(void) {
 #ifdef _OPENMP

@@ -122,6 +122,32 @@ def test_threshold_forward_arguments():
                                            None) == -5
 
 
+def test_forward_ext_arguments():
+    lib = dsa.load()
+    dec = prob(n_q=1, n_k=512, q_pos0=0)
+    need = dsa.workspace_size(dec, dsa.OP_FORWARD)
+    tail = lambda n=need: (FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, n, None)
+    pg = dsa.Pages(block_table=0x100000, page_size=256, pages_per_seq=2, n_pages=8)
+    opt = lambda **kw: ctypes.byref(dsa.Options(**kw))
+    # no options: the checks of dsa_forward
+    assert lib.dsa_forward_ext(ctypes.byref(dec), None, *tail(need - 1)) == -5
+    # pages need seq_pos; ragged and paged need one query per sequence at q_pos0 = 0
+    assert lib.dsa_forward_ext(ctypes.byref(dec), opt(pages=ctypes.pointer(pg)), *tail()) == -1
+    assert lib.dsa_forward_ext(ctypes.byref(prob(n_q=2, n_k=512)),
+                               opt(seq_pos=0x100000, threshold_mode=1, tau=1.0), *tail()) == -3
+    assert lib.dsa_forward_ext(ctypes.byref(dec), opt(seq_pos=0x100008), *tail()) == -4
+    bad = dsa.Pages(block_table=0x100000, page_size=100, pages_per_seq=2, n_pages=8)
+    assert lib.dsa_forward_ext(ctypes.byref(dec), opt(seq_pos=0x100000, pages=ctypes.pointer(bad)),
+                               *tail()) == -2
+    # valid layouts and modes get as far as the workspace check
+    for o in (opt(threshold_mode=1, tau=0.5), opt(seq_pos=0x100000, threshold_mode=1, tau=0.5),
+              opt(seq_pos=0x100000, pages=ctypes.pointer(pg), threshold_mode=1, tau=0.5)):
+        assert lib.dsa_forward_ext(ctypes.byref(dec), o, *tail(need - 1)) == -5
+    ms = (ctypes.c_float * 3)()
+    assert lib.dsa_forward_ext_timed(ctypes.byref(dec), None, *tail(), None, None) == -1
+    assert lib.dsa_forward_ext_timed(ctypes.byref(dec), None, *tail(need - 1), ms, None) == -5
+
+
 def test_index_project_arguments():
     lib = dsa.load()
     call = lambda rows=64, dm=4096, di=128, dt=0, X=FAKE, W=FAKE, out=FAKE, orow=None, \

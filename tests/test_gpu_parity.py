@@ -565,6 +565,35 @@ def test_projected_decode_step(gpu_lib):
     assert_attn_close(O, O_ref, lse, lse_ref, "projected decode")
 
 
+@pytest.mark.parametrize("w,pos", RAGGED[:3], ids=lambda v: v.name if hasattr(v, "name") else "")
+def test_forward_ragged_paged_threshold(gpu_lib, w, pos):
+    # threshold mode in a ragged batch (dsa_forward_ext) against the oracle
+    # at each sequence's position, then the same batch in 16- and 256-key
+    # pages: identical results
+    x = synth.make_inputs(w, seed=17)
+    s = oracle.index_scores(x["q_idx"], x["k_idx"], 0)
+    tau = float(np.quantile(s[np.isfinite(s)], 0.98))
+    say("ragged threshold %s tau=%.3f" % (w.name, tau))
+    idx_ref, O_ref, lse_ref = oracle.forward(x["q_idx"], x["k_idx"], x["Q"], x["K"], x["V"], 0,
+                                             w.top_k, seq_pos=pos, tau=tau)
+    d = to_dev(x)
+    sp = torch.tensor(pos, dtype=torch.int32, device="cuda")
+    idx, O, lse = dsa.forward(d["q_idx"], d["k_idx"], d["Q"], d["K"], d["V"], 0, w.top_k,
+                              seq_pos=sp, tau=tau)
+    assert np.array_equal(idx.cpu().numpy(), idx_ref)
+    assert_attn_close(O, O_ref, lse, lse_ref, "ragged threshold")
+    for P in (16, 256):
+        if w.n_k % P:
+            continue
+        kp, table = to_pages(x["k_idx"], P, 3, P)
+        Kp, _ = to_pages(x["K"], P, 3, P)
+        Vp, _ = to_pages(x["V"], P, 3, P)
+        i2, O2, l2 = dsa.forward_paged(d["q_idx"], kp.cuda(), d["Q"], Kp.cuda(), Vp.cuda(),
+                                       table.cuda(), P, sp, w.top_k, tau=tau)
+        assert torch.equal(i2, idx), P
+        assert torch.equal(O2.view(torch.int16), O.view(torch.int16)) and torch.equal(l2, lse), P
+
+
 def test_all_zero_query_selects_first_keys(gpu_lib):
     w = Workload("zeros", "prefill", 1, 600, 600, 0, 128, "fp8", 64, 2)
     x = synth.make_inputs(w, seed=6)

@@ -391,6 +391,23 @@ def test_index_project_rows_land_where_asked():
     assert np.all(oracle.index_project(big, ones, "fp8") == 0x7e)  # 512 -> 448
 
 
+def test_forward_threshold_seq_positions_are_per_sequence_calls():
+    # threshold mode in a ragged batch equals one threshold-mode call per
+    # sequence at its own position
+    w = synth.WORKLOADS["decode_32k"].replace(batch=3, n_k=700, q_pos0=0, top_k=50, n_heads=2)
+    x = synth.make_inputs(w, seed=4)
+    pos = [699, 30, 333]
+    tau = 9.0
+    idx, O, lse = oracle.forward(x["q_idx"], x["k_idx"], x["Q"], x["K"], x["V"], 0, w.top_k,
+                                 seq_pos=pos, tau=tau)
+    for b, p in enumerate(pos):
+        sl = {k: v[b:b + 1] for k, v in x.items()}
+        i1, O1, l1 = oracle.forward(sl["q_idx"], sl["k_idx"], sl["Q"], sl["K"], sl["V"], p,
+                                    w.top_k, tau=tau)
+        assert np.array_equal(idx[b:b + 1], i1)
+        assert np.array_equal(O[b:b + 1], O1) and np.array_equal(lse[b:b + 1], l1)
+
+
 def dense_attn_torch(Q, K, V, q_pos0):
     """Dense MQA attention with the causal mask, through torch's
     scaled_dot_product_attention in float64 (K/V expanded to every head)."""
