@@ -27,6 +27,27 @@ def test_header_declares_the_boundary():
         assert n in names
 
 
+def test_header_compiles_as_c_and_matches_the_binding(tmp_path):
+    # the boundary is plain C: the header compiles with a C99 compiler, and
+    # the option structs have the sizes the ctypes binding assumes
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "t.c"
+    src.write_text('#include "dsa.h"\n#include <stdio.h>\nint main(void) {\n'
+                   '  printf("%d %d %d\\n", (int)sizeof(dsa_problem), (int)sizeof(dsa_pages),\n'
+                   '         (int)sizeof(dsa_forward_options));\n  return 0;\n}\n')
+    exe = tmp_path / "t"
+    subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic",
+                    "-I" + os.path.dirname(HEADER), str(src), "-o", str(exe)], check=True)
+    sizes = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True,
+                                            check=True).stdout.split()]
+    assert sizes == [ctypes.sizeof(dsa.Problem), ctypes.sizeof(dsa.Pages),
+                     ctypes.sizeof(dsa.Options)]
+
+
 def test_library_exports_every_declared_symbol():
     lib = dsa.load()
     for name in declared_functions():
