@@ -101,7 +101,6 @@ def project_oracle(oracle, x, wname, r0, r1, w):
 def cpu_baseline(w, x, target_s=12.0, seed=0):
     """Time the oracle on a bounded sample of the workload's queries."""
     import oracle
-    t_probe0 = time.perf_counter()
     if w.mode == "decode":
         # one decode row per sequence: sample sequences
         pos = w.positions(seed)
@@ -131,10 +130,18 @@ def cpu_baseline(w, x, target_s=12.0, seed=0):
         if tp < target_s:
             n = int(min(w.batch, max(probe, probe * target_s / max(tp, 1e-3))))
             n = max(probe, n // probe * probe)
+        # a whole batch that runs faster than the target is run again (at
+        # most 64 passes) so that the rate rests on seconds of CPU work
         t0 = time.perf_counter()
-        q = run(n)
-        dt = time.perf_counter() - t0
-        sample = "%d of %d sequences (one decode query each), all stages" % (n, w.batch)
+        q, reps = 0, 0
+        while True:
+            q += run(n)
+            reps += 1
+            dt = time.perf_counter() - t0
+            if dt >= target_s or reps >= 64:
+                break
+        sample = "%d of %d sequences (one decode query each), all stages, %d pass%s" % (
+            n, w.batch, reps, "" if reps == 1 else "es")
     else:
         # prefill: a stratified set of query rows
         nthreads = oracle.num_threads()
@@ -157,7 +164,6 @@ def cpu_baseline(w, x, target_s=12.0, seed=0):
                 break
         dt = time.perf_counter() - t0
         sample = "%d query rows of %d, strided through the prefill, all stages" % (q, w.n_q)
-    del t_probe0
     return {"value": q / dt, "unit": "queries/s", "cores": oracle.num_threads(),
             "kind": "oracle", "sample": sample, "seconds": round(dt, 3)}
 
