@@ -78,4 +78,4 @@ def test_cpu_baseline_leg(mode):
     if mode == "decode":
         assert r["sample"].startswith("4 of 4 sequences")
     else:
-        assert "query rows of 256" in r["sample"]
+        assert "of the prefill's 256" in r["sample"] and "strided sweep" in r["sample"]
