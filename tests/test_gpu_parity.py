@@ -137,6 +137,8 @@ def random_selection(g, B, n_q, n_k, k, q_pos0, holes=True):
     (3, 1, 6000, 16, 2048, 5999),  # decode-like
     (1, 17, 17, 1, 4096, 0),       # k far above the row length
     (2, 5, 900, 13, 96, 895),
+    (4, 50, 3000, 16, 1000, 2950),  # two splits of 512 slots, the second ragged
+    (1, 2047, 2100, 4, 64, 53),     # the most rows that still take the split path
 ])
 def test_sparse_attn_vs_oracle(gpu_lib, B, n_q, n_k, H, k, q_pos0):
     say("sparse_attn B=%d n_q=%d n_k=%d H=%d k=%d" % (B, n_q, n_k, H, k))
