@@ -1,6 +1,7 @@
 // C ABI of the DSA library: argument validation, workspace layout and the
 // launch sequence of each call. Every check runs on the host before anything
 // is enqueued; the library allocates no device memory.
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -120,9 +121,14 @@ size_t topk_ws_bytes_max(const dsa_problem* p) {
 // Slabs of the many-row path: slab s holds query rows s, s + n, s + 2n, ...
 // (n slabs), so every slab mixes short and long rows; the candidate lists of
 // one slab stay within kPrefillSlabBytes.
+// The budget itself can be lowered for tests (dsa_internal_set_prefill_slab_bytes),
+// so that small problems run as several slabs.
+std::atomic<size_t> g_prefill_slab_bytes{kPrefillSlabBytes};
+
 int prefill_slabs(const dsa_problem* p) {
     const size_t row_bytes = (size_t)p->batch * dsa::prefill_cap(p->top_k) * 8;
-    const size_t per = kPrefillSlabBytes / row_bytes > 0 ? kPrefillSlabBytes / row_bytes : 1;
+    const size_t budget = g_prefill_slab_bytes.load();
+    const size_t per = budget / row_bytes > 0 ? budget / row_bytes : 1;
     return (int)(((size_t)p->n_q + per - 1) / per);
 }
 
@@ -487,6 +493,15 @@ dsa_status check_paged(const dsa_problem* p, const int32_t* seq_pos, const dsa_p
 }  // namespace
 
 extern "C" {
+
+// Not part of the public interface: lowers the candidate-list budget of one
+// many-row slab (0 restores the default of 4 GiB) and returns the previous
+// budget. Tests use it to run small prefill problems as several slabs; the
+// workspace size of a forward call follows the budget in force when it is
+// asked for, so a caller must not change it between sizing and calling.
+size_t dsa_internal_set_prefill_slab_bytes(size_t bytes) {
+    return g_prefill_slab_bytes.exchange(bytes ? bytes : kPrefillSlabBytes);
+}
 
 dsa_status dsa_workspace_size(const dsa_problem* p, int32_t op, size_t* bytes) {
     if (!bytes) return fail(DSA_E_NULL, "bytes is NULL");

@@ -52,6 +52,7 @@ def _load():
             lib.oracle_forward.argtypes = [I] * 9 + [P] * 5 + [I, I, P, P, P]
             lib.oracle_forward_seqpos.argtypes = [I, I, I, P] + [I] * 5 + [P] * 5 + [I, I, P,
                                                                                   P, P]
+            lib.oracle_forward_rowlist.argtypes = [I] * 9 + [P] * 5 + [P, I, P, P, P]
             F = ctypes.c_float
             lib.oracle_select_threshold.argtypes = [I, I, I, I, I, F, P, P]
             lib.oracle_forward_threshold.argtypes = ([I] * 7 + [F, I, I] + [P] * 5 +
@@ -66,6 +67,7 @@ def _load():
                       lib.oracle_index_scores, lib.oracle_topk,
                       lib.oracle_sparse_attn, lib.oracle_forward,
                       lib.oracle_forward_seqpos, lib.oracle_select_threshold,
+                      lib.oracle_forward_rowlist,
                       lib.oracle_forward_threshold, lib.oracle_num_threads):
                 f.restype = I
             _lib = lib
@@ -243,5 +245,29 @@ def forward(q_idx, k_idx, Q, K, V, q_pos0: int, k: int, q_begin: int = 0,
                                 k, H, D, _ptr(qi), _ptr(ki), _ptr(q), _ptr(kk),
                                 _ptr(vv), q_begin, q_end, _ptr(idx), _ptr(O),
                                 _ptr(lse))
+    assert rc == 0, rc
+    return idx, O, lse
+
+
+def forward_rows(q_idx, k_idx, Q, K, V, q_pos0: int, k: int, rows, dtype=None):
+    """forward() for a list of query rows (any order, repeats allowed) of
+    every sequence: output entry t is query row rows[t]. One parallel call, so
+    strided samples of a long prefill cost no more than a contiguous block.
+
+    Returns (idx [B, len(rows), k] int32, O [B, len(rows), H, D] float32,
+    lse [B, len(rows), H] float32)."""
+    qi, ki = _raw(q_idx), _raw(k_idx)
+    q, kk, vv = _raw(Q), _raw(K), _raw(V)
+    B, n_q, d = qi.shape
+    n_k = ki.shape[1]
+    H, D = q.shape[2], q.shape[3]
+    rl = np.ascontiguousarray(np.asarray(rows, np.int32).reshape(-1))
+    n = rl.shape[0]
+    idx = np.empty((B, n, k), np.int32)
+    O = np.empty((B, n, H, D), np.float32)
+    lse = np.empty((B, n, H), np.float32)
+    rc = _load().oracle_forward_rowlist(B, n_q, n_k, q_pos0, d, _dtype_code(q_idx, dtype), k, H,
+                                        D, _ptr(qi), _ptr(ki), _ptr(q), _ptr(kk), _ptr(vv),
+                                        _ptr(rl), n, _ptr(idx), _ptr(O), _ptr(lse))
     assert rc == 0, rc
     return idx, O, lse

@@ -368,11 +368,15 @@ static int forward_rows(int B, int n_q, int n_k, int q_pos0, const int32_t* seq_
                         int dtype, int k, const float* tau, int H, int D, const void* q_idx,
                         const void* k_idx,
                         const uint16_t* Q, const uint16_t* K, const uint16_t* V,
-                        int q_begin, int q_end, int32_t* idx, float* O, float* lse) {
+                        int q_begin, int q_end, const int32_t* row_list, int32_t* idx, float* O,
+                        float* lse) {
     if (B < 0 || n_q < 0 || n_k < 0 || d <= 0 || k < 1 || H < 1 || D < 1 ||
-        q_begin < 0 || q_end > n_q || q_begin > q_end ||
+        q_begin < 0 || q_begin > q_end || (!row_list && q_end > n_q) ||
         (dtype != ORACLE_FP8_E4M3FN && dtype != ORACLE_BF16))
         return -1;
+    if (row_list)
+        for (int r = q_begin; r < q_end; ++r)
+            if (row_list[r] < 0 || row_list[r] >= n_q) return -1;
     const float scale = oracle_index_scale(d);
     const int rows = q_end - q_begin;
     const long total = (long)B * rows;
@@ -392,7 +396,8 @@ static int forward_rows(int B, int n_q, int n_k, int q_pos0, const int32_t* seq_
 #pragma omp for schedule(dynamic, 1)
         for (long t = 0; t < total; ++t) {
             if (!ok) continue;
-            int b = (int)(t / rows), i = q_begin + (int)(t % rows);
+            int b = (int)(t / rows), i = row_list ? row_list[q_begin + (int)(t % rows)]
+                                                  : q_begin + (int)(t % rows);
             long pos = (long)(seq_pos ? seq_pos[b] : q_pos0) + i;
             size_t qoff = ((size_t)b * n_q + i) * d;
             for (int j = 0; j < n_k; ++j)
@@ -416,7 +421,19 @@ int oracle_forward(int B, int n_q, int n_k, int q_pos0, int d, int dtype, int k,
                    const uint16_t* Q, const uint16_t* K, const uint16_t* V,
                    int q_begin, int q_end, int32_t* idx, float* O, float* lse) {
     return forward_rows(B, n_q, n_k, q_pos0, NULL, d, dtype, k, NULL, H, D, q_idx, k_idx, Q,
-                        K, V, q_begin, q_end, idx, O, lse);
+                        K, V, q_begin, q_end, NULL, idx, O, lse);
+}
+
+/* oracle_forward over a list of query rows: entry t of the outputs is query
+ * row rows[t] of its sequence (the same per-row chain; rows may repeat or come
+ * in any order), so sampled rows of a long prefill run as one parallel call. */
+int oracle_forward_rowlist(int B, int n_q, int n_k, int q_pos0, int d, int dtype, int k,
+                           int H, int D, const void* q_idx, const void* k_idx,
+                           const uint16_t* Q, const uint16_t* K, const uint16_t* V,
+                           const int32_t* rows, int n_rows, int32_t* idx, float* O, float* lse) {
+    if (!rows || n_rows < 0) return -1;
+    return forward_rows(B, n_q, n_k, q_pos0, NULL, d, dtype, k, NULL, H, D, q_idx, k_idx, Q,
+                        K, V, 0, n_rows, rows, idx, O, lse);
 }
 
 /* oracle_forward with threshold-mode selection: each query attends to the
@@ -426,7 +443,7 @@ int oracle_forward_threshold(int B, int n_q, int n_k, int q_pos0, int d, int dty
                              const uint16_t* Q, const uint16_t* K, const uint16_t* V,
                              int q_begin, int q_end, int32_t* idx, float* O, float* lse) {
     return forward_rows(B, n_q, n_k, q_pos0, NULL, d, dtype, k, &tau, H, D, q_idx, k_idx, Q,
-                        K, V, q_begin, q_end, idx, O, lse);
+                        K, V, q_begin, q_end, NULL, idx, O, lse);
 }
 
 /* oracle_forward for a batch whose sequences sit at different positions:
@@ -439,7 +456,7 @@ int oracle_forward_seqpos(int B, int n_q, int n_k, const int32_t* seq_pos, int d
                           int q_begin, int q_end, int32_t* idx, float* O, float* lse) {
     if (!seq_pos) return -1;
     return forward_rows(B, n_q, n_k, 0, seq_pos, d, dtype, k, NULL, H, D, q_idx, k_idx, Q, K,
-                        V, q_begin, q_end, idx, O, lse);
+                        V, q_begin, q_end, NULL, idx, O, lse);
 }
 
 /* oracle_forward_seqpos with threshold-mode selection (thresh_row). */
@@ -450,7 +467,7 @@ int oracle_forward_seqpos_threshold(int B, int n_q, int n_k, const int32_t* seq_
                                     float* O, float* lse) {
     if (!seq_pos) return -1;
     return forward_rows(B, n_q, n_k, 0, seq_pos, d, dtype, k, &tau, H, D, q_idx, k_idx, Q, K, V,
-                        q_begin, q_end, idx, O, lse);
+                        q_begin, q_end, NULL, idx, O, lse);
 }
 
 /* Threads an OpenMP parallel region of this library runs with. */

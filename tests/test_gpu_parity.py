@@ -608,6 +608,83 @@ def test_all_zero_query_selects_first_keys(gpu_lib):
         assert list(idx[i, :m]) == list(range(m)) and np.all(idx[i, m:] == -1)
 
 
+def test_prefill_1k_seed0_every_row(gpu_lib):
+    # The 1K prefill exactly as the benchmark draws it (seed 0): scores of
+    # every row bit for bit, every index list bit for bit, attention within
+    # tolerance, all 1024 rows.
+    w = synth.WORKLOADS["prefill_1k"]
+    say("prefill_1k seed 0: every row")
+    x = synth.make_inputs(w, seed=0)
+    d = to_dev(x)
+    idx, O, lse = dsa.forward(d["q_idx"], d["k_idx"], d["Q"], d["K"], d["V"], 0, w.top_k)
+    idx_ref, O_ref, lse_ref = oracle.forward(x["q_idx"], x["k_idx"], x["Q"], x["K"], x["V"], 0,
+                                             w.top_k)
+    assert np.array_equal(idx.cpu().numpy(), idx_ref)
+    assert_attn_close(O, O_ref, lse, lse_ref, "prefill_1k seed 0")
+    s = dsa.index_scores(d["q_idx"], d["k_idx"], 0).cpu().numpy()
+    assert np.array_equal(bits(s), bits(oracle.index_scores(x["q_idx"], x["k_idx"], 0)))
+    check_topk_every_row(d, w, idx)
+
+
+# Many-row prefills whose top_k takes the larger select instantiations (list
+# entries per thread: 14 for top_k 2048, 18 for 2800, 26 for 4096), on rows
+# longer than top_k, every row against the oracle.
+BIG_K = [
+    Workload("prefill_bf16_d160_k2048", "prefill", 1, 12000, 12000, 0, 160, "bf16", 2048, 2),
+    Workload("prefill_fp8_d128_k2800", "prefill", 1, 10000, 10000, 0, 128, "fp8", 2800, 2),
+    Workload("prefill_fp8_d128_k4096", "prefill", 1, 10000, 10000, 0, 128, "fp8", 4096, 2),
+]
+
+
+@pytest.mark.parametrize("w", BIG_K, ids=lambda w: w.name)
+def test_prefill_large_topk_every_row(gpu_lib, w):
+    say("large top_k prefill %s" % w.name)
+    x = synth.make_inputs(w, seed=21)
+    d = to_dev(x)
+    idx, O, lse = dsa.forward(d["q_idx"], d["k_idx"], d["Q"], d["K"], d["V"], 0, w.top_k)
+    torch.cuda.synchronize()
+    check_topk_every_row(d, w, idx)
+    say("large top_k prefill %s: oracle" % w.name)
+    idx_ref, O_ref, lse_ref = oracle.forward(x["q_idx"], x["k_idx"], x["Q"], x["K"], x["V"], 0,
+                                             w.top_k)
+    assert np.array_equal(idx.cpu().numpy(), idx_ref)
+    assert_attn_close(O, O_ref, lse, lse_ref, w.name)
+
+
+@pytest.mark.parametrize("w,n_slabs", [
+    (Workload("prefill_b2_slabs4", "prefill", 2, 6000, 6000, 0, 128, "fp8", 300, 2), 4),
+    (Workload("prefill_bf16_slabs3_chunked", "prefill", 1, 3001, 5000, 1999, 96, "bf16", 500, 3),
+     3),
+], ids=lambda v: v.name if isinstance(v, Workload) else str(v))
+def test_prefill_forced_slabs_every_row(gpu_lib, w, n_slabs):
+    # A lowered slab budget splits the many-row path into strided slabs (rows
+    # s, s + n, s + 2n, ... for slab s), each with its own threshold, filter,
+    # select and fallback launches over the same workspace: every row against
+    # the oracle, and identical to the one-slab result.
+    x = synth.make_inputs(w, seed=23)
+    d = to_dev(x)
+    idx1, O1, lse1 = dsa.forward(d["q_idx"], d["k_idx"], d["Q"], d["K"], d["V"], w.q_pos0,
+                                 w.top_k)
+    cap = (3 * w.top_k + 768 + 63) // 64 * 64
+    row_bytes = w.batch * cap * 8
+    per = (w.n_q + n_slabs - 1) // n_slabs
+    old = set_prefill_slab_bytes(per * row_bytes)
+    try:
+        assert prefill_slab_count(d, w) == n_slabs
+        say("forced slabs %s: %d slabs" % (w.name, n_slabs))
+        idx, O, lse = dsa.forward(d["q_idx"], d["k_idx"], d["Q"], d["K"], d["V"], w.q_pos0,
+                                  w.top_k)
+        torch.cuda.synchronize()
+    finally:
+        set_prefill_slab_bytes(old)
+    idx_ref, O_ref, lse_ref = oracle.forward(x["q_idx"], x["k_idx"], x["Q"], x["K"], x["V"],
+                                             w.q_pos0, w.top_k)
+    assert np.array_equal(idx.cpu().numpy(), idx_ref)
+    assert_attn_close(O, O_ref, lse, lse_ref, w.name)
+    assert torch.equal(idx, idx1)
+    assert torch.equal(O.view(torch.int16), O1.view(torch.int16)) and torch.equal(lse, lse1)
+
+
 @pytest.mark.parametrize("w,rows", [
     # every row reaches both 12288-key ranges; two sequences
     (Workload("ranged_chunked", "prefill", 2, 1100, 20000, 18900, 64, "fp8", 300, 16),
@@ -649,6 +726,97 @@ def check_selection_properties(idx, q_pos0, k):
     assert torch.all(torch.where(valid, idx <= pos, True))
     inc = idx[:, :, 1:] > idx[:, :, :-1]
     assert torch.all(torch.where(valid[:, :, 1:], inc, True))
+
+
+def check_topk_every_row(d, w, idx, rows_per_slab=None):
+    """Every row's index list against an independent top-k computed on the GPU
+    with torch (neither the HIP path nor the oracle): the integer indexer
+    inputs make the dot an exact integer |n| <= 2560, so an fp32 matmul gives
+    it exactly; one fp32 multiply by fl32(d^-0.5) and ReLU give the score
+    (the DSA page, section 3.2). The kept set is then the first min(k, pos+1)
+    causal keys under (score desc, index asc) (section 3.3), found with a
+    torch top-k over int64 keys (score bits << 32 | ~index) and listed in
+    ascending index order, -1 padded."""
+    torch.backends.cuda.matmul.allow_tf32 = False
+    B, n_q, dq = d["q_idx"].shape
+    n_k = d["k_idx"].shape[1]
+    k = w.top_k
+    scale = torch.tensor(np.float32(oracle.index_scale(dq)), device="cuda")
+    if rows_per_slab is None:
+        rows_per_slab = max(1, min(n_q, (1 << 26) // n_k))
+    j = torch.arange(n_k, device="cuda", dtype=torch.int64)
+    low = (0xFFFFFFFF - j)[None, :]
+    for b in range(B):
+        kf = d["k_idx"][b].float()
+        kt = kf.t().contiguous()
+        for r0 in range(0, n_q, rows_per_slab):
+            r1 = min(n_q, r0 + rows_per_slab)
+            qf = d["q_idx"][b, r0:r1].float()
+            dots = torch.mm(qf, kt)
+            # the dot must be an exact integer for this check to be the score
+            assert torch.equal(dots, dots.round()) and float(dots.abs().max()) <= 2560.0
+            sc = torch.relu(dots * scale)
+            key = (sc.view(torch.int32).to(torch.int64) << 32) | low
+            pos = w.q_pos0 + torch.arange(r0, r1, device="cuda", dtype=torch.int64)[:, None]
+            key = torch.where(j[None, :] <= pos, key, torch.full_like(key, -1))
+            kk = min(k, n_k)
+            top = torch.topk(key, kk, dim=1, sorted=False).values
+            sel = torch.where(top >= 0, 0xFFFFFFFF - (top & 0xFFFFFFFF), torch.full_like(top, n_k))
+            sel = torch.sort(sel, dim=1).values
+            sel = torch.where(sel < n_k, sel, torch.full_like(sel, -1)).to(torch.int32)
+            if kk < k:
+                sel = torch.cat([sel, torch.full((r1 - r0, k - kk), -1, dtype=torch.int32,
+                                                 device="cuda")], 1)
+            got = idx[b, r0:r1]
+            if not torch.equal(got, sel):
+                bad = (got != sel).any(1).nonzero()[:, 0]
+                raise AssertionError("%s: %d rows of sequence %d differ from the torch top-k, "
+                                     "first row %d" % (w.name, bad.numel(), b, r0 + int(bad[0])))
+        del kf, kt
+
+
+def strided_rows(n_q, k, n=1024, seed=0):
+    """About n query rows spread over the prefill (a seeded offset, then a
+    fixed stride) plus the rows around top_k and the last row."""
+    step = max(1, n_q // n)
+    off = int(np.random.default_rng(seed + n_q).integers(0, step))
+    rows = set(range(off, n_q, step))
+    rows.update(r for r in (0, 1, k - 2, k - 1, k, k + 1, 2 * k, n_q - 2, n_q - 1) if 0 <= r < n_q)
+    return sorted(rows)
+
+
+def oracle_rows_check(x, idx, O, lse, w, rows):
+    """Oracle comparison of the listed query rows (one parallel oracle call)."""
+    say("%s: oracle on %d rows" % (w.name, len(rows)))
+    idx_ref, O_ref, lse_ref = oracle.forward_rows(x["q_idx"], x["k_idx"], x["Q"], x["K"],
+                                                  x["V"], w.q_pos0, w.top_k, rows)
+    rt = torch.tensor(rows, device=idx.device, dtype=torch.long)
+    got = idx.index_select(1, rt).cpu().numpy()
+    if not np.array_equal(got, idx_ref):
+        bad = np.nonzero((got != idx_ref).any(-1))
+        raise AssertionError("%s: rows %s differ from the oracle" %
+                             (w.name, sorted(set(rows[i] for i in bad[1]))[:10]))
+    assert_attn_close(O.index_select(1, rt), O_ref, lse.index_select(1, rt), lse_ref,
+                      "%s %d rows" % (w.name, len(rows)))
+
+
+def set_prefill_slab_bytes(nbytes):
+    """The library's many-row slab budget (an internal, non-ABI knob; 0
+    restores the default). Returns the previous budget."""
+    import ctypes
+    f = dsa.load().dsa_internal_set_prefill_slab_bytes
+    f.argtypes = [ctypes.c_size_t]
+    f.restype = ctypes.c_size_t
+    return f(nbytes)
+
+
+def prefill_slab_count(d, w):
+    p = dsa.make_problem(w.batch, w.n_q, w.n_k, w.q_pos0, w.d_idx, w.idx_dtype, w.top_k,
+                         w.n_heads)
+    fwd = dsa.Forward(p, "cuda")
+    O = torch.empty_like(d["Q"])
+    _, slabs = fwd.timed(d["q_idx"], d["k_idx"], d["Q"], d["K"], d["V"], O)
+    return slabs
 
 
 def run_full(w, sample_rows, gen_device="cpu"):
@@ -774,9 +942,27 @@ def prefill_samples(L, k):
     return rows
 
 
+def run_full_prefill(w):
+    """The full-size prefill in the benchmark's launch configuration: every
+    row's index list against the torch top-k, about 1024 strided rows (and
+    the rows around top_k) against the oracle, properties on every row."""
+    say("full-size %s: generating inputs" % w.name)
+    x = synth.make_inputs(w, seed=0)
+    d = to_dev(x)
+    say("full-size %s: GPU forward" % w.name)
+    idx, O, lse = dsa.forward(d["q_idx"], d["k_idx"], d["Q"], d["K"], d["V"], w.q_pos0,
+                              w.top_k)
+    torch.cuda.synchronize()
+    check_selection_properties(idx, w.q_pos0, w.top_k)
+    say("full-size %s: torch top-k of every row" % w.name)
+    check_topk_every_row(d, w, idx)
+    oracle_rows_check(x, idx, O, lse, w, strided_rows(w.n_q, w.top_k))
+    return x, d
+
+
 def test_full_prefill_64k(gpu_lib):
     w = synth.WORKLOADS["prefill_64k"]
-    x, d = run_full(w, prefill_samples(w.n_q, w.top_k))
+    x, d = run_full_prefill(w)
     # indexer scores of sampled row slabs at full width, bit for bit
     for (a, b) in [(5, 9), (40000, 40006), (w.n_q - 3, w.n_q)]:
         got = dsa.index_scores(d["q_idx"], d["k_idx"], 0, a, b).cpu().numpy()
@@ -862,18 +1048,34 @@ def test_full_prefill_64k_projection_rows(gpu_lib):
 
 
 def test_full_prefill_128k_bf16(gpu_lib):
+    # two strided slabs of 65536 rows in the benchmark's configuration
     w = synth.WORKLOADS["prefill_128k"]
-    x, d = run_full(w, prefill_samples(w.n_q, w.top_k))
+    x, d = run_full_prefill(w)
     for (a, b) in [(0, 4), (99999, 100003), (w.n_q - 2, w.n_q)]:
         got = dsa.index_scores(d["q_idx"], d["k_idx"], 0, a, b).cpu().numpy()
         ref = oracle.index_scores(x["q_idx"], x["k_idx"], 0, a, b)
         assert np.array_equal(bits(got), bits(ref)), (a, b)
 
 
-def test_full_prefill_batch2_many_slabs(gpu_lib):
-    # two sequences, several score slabs per forward call
+def test_full_prefill_batch2_three_slabs(gpu_lib):
+    # two sequences of 40000 rows as three strided slabs (a lowered slab
+    # budget): every row against the torch top-k, sampled rows against the
+    # oracle
     w = Workload("prefill_b2_40k", "prefill", 2, 40000, 40000, 0, 128, "fp8", 1024, 16)
-    run_full(w, [(0, 2), (1022, 1026), (6550, 6560), (13107, 13110), (39998, 40000)])
+    cap = (3 * w.top_k + 768 + 63) // 64 * 64
+    old = set_prefill_slab_bytes(13334 * w.batch * cap * 8)
+    try:
+        say("full-size %s: generating inputs" % w.name)
+        x = synth.make_inputs(w, seed=0)
+        d = to_dev(x)
+        assert prefill_slab_count(d, w) == 3
+        idx, O, lse = dsa.forward(d["q_idx"], d["k_idx"], d["Q"], d["K"], d["V"], 0, w.top_k)
+        torch.cuda.synchronize()
+    finally:
+        set_prefill_slab_bytes(old)
+    check_selection_properties(idx, 0, w.top_k)
+    check_topk_every_row(d, w, idx)
+    oracle_rows_check(x, idx, O, lse, w, strided_rows(w.n_q, w.top_k, n=256))
 
 
 @pytest.mark.parametrize("name", ["decode_chunked_20k", "prefill_1k"])

@@ -521,3 +521,18 @@ def test_clustered_generator_range_and_ties():
     s = oracle.index_scores(x["q_idx"], x["k_idx"], w.q_pos0)
     # heavy ties: far fewer distinct scores than keys
     assert len(np.unique(s[0, 0])) < 400
+
+
+def test_forward_row_list_is_the_contiguous_forward():
+    # forward_rows over any list of rows (strided, reversed, repeated) gives
+    # row for row what the contiguous call gives: the same per-row chain
+    w = synth.WORKLOADS["prefill_1k"].replace(batch=2, n_q=300, n_k=300, top_k=24, n_heads=2)
+    x = synth.make_inputs(w, seed=4)
+    idx, O, lse = oracle.forward(x["q_idx"], x["k_idx"], x["Q"], x["K"], x["V"], 0, w.top_k)
+    rows = [299, 0, 7, 7, 150] + list(range(3, 300, 37))
+    i2, O2, l2 = oracle.forward_rows(x["q_idx"], x["k_idx"], x["Q"], x["K"], x["V"], 0,
+                                     w.top_k, rows)
+    assert np.array_equal(i2, idx[:, rows])
+    assert np.array_equal(O2, O[:, rows]) and np.array_equal(l2, lse[:, rows])
+    with pytest.raises(AssertionError):
+        oracle.forward_rows(x["q_idx"], x["k_idx"], x["Q"], x["K"], x["V"], 0, w.top_k, [300])
