@@ -32,7 +32,7 @@ EXPORTS = ("dsa_workspace_size", "dsa_index_scores", "dsa_topk", "dsa_sparse_att
            "dsa_forward", "dsa_forward_ragged", "dsa_forward_paged", "dsa_forward_timed",
            "dsa_forward_ragged_timed", "dsa_forward_paged_timed", "dsa_forward_threshold",
            "dsa_forward_threshold_timed", "dsa_forward_ext", "dsa_forward_ext_timed",
-           "dsa_index_project", "dsa_status_str", "dsa_last_error")
+           "dsa_index_project", "dsa_forward_noalloc", "dsa_status_str", "dsa_last_error")
 
 
 class Problem(ctypes.Structure):
@@ -80,6 +80,7 @@ def load():
             lib.dsa_topk.argtypes = [PP, P, I, I, P, P, S, P]
             lib.dsa_sparse_attn.argtypes = [PP, P, P, P, P, P, P, P, S, P]
             lib.dsa_forward.argtypes = [PP, P, P, P, P, P, P, P, P, P, S, P]
+            lib.dsa_forward_noalloc.argtypes = [PP, P, P, P, P, P, P, P, P, P]
             lib.dsa_forward_ragged.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, S, P]
             lib.dsa_forward_timed.argtypes = [PP, P, P, P, P, P, P, P, P, P, S, P, P, P]
             lib.dsa_forward_ragged_timed.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, S, P, P,
@@ -99,6 +100,7 @@ def load():
             for f in (lib.dsa_index_project, lib.dsa_forward_ext, lib.dsa_forward_ext_timed,
                       lib.dsa_workspace_size, lib.dsa_index_scores, lib.dsa_topk,
                       lib.dsa_sparse_attn, lib.dsa_forward, lib.dsa_forward_ragged,
+                      lib.dsa_forward_noalloc,
                       lib.dsa_forward_paged, lib.dsa_forward_timed,
                       lib.dsa_forward_ragged_timed, lib.dsa_forward_paged_timed,
                       lib.dsa_forward_threshold, lib.dsa_forward_threshold_timed):
@@ -321,6 +323,36 @@ def forward(q_idx, k_idx, Q, K, V, q_pos0, top_k, want_idx=True, want_lse=True, 
         if seq_pos.shape[0] != B:
             raise ValueError("seq_pos must have one entry per sequence")
     Forward(p, dev)(q_idx, k_idx, Q, K, V, O, idx, lse, seq_pos=seq_pos, tau=tau)
+    return idx, O, lse
+
+
+def forward_noalloc(q_idx, k_idx, Q, K, V, q_pos0, top_k, O, idx=None, lse=None):
+    """The fused chain through dsa_forward_noalloc: no workspace, the library's
+    static device scratch instead. The caller passes the outputs (O
+    [B,n_q,H,128] bf16; idx [B,n_q,top_k] int32 and lse [B,n_q,H] float32 may
+    be None), so the call allocates nothing. Calls that overlap on one GPU
+    share that scratch and must not run concurrently."""
+    _dev_tensor(q_idx, "q_idx", _IDX_DTYPES, 3)
+    _dev_tensor(k_idx, "k_idx", (q_idx.dtype,), 3)
+    _dev_tensor(Q, "Q", (torch.bfloat16,), 4)
+    _dev_tensor(K, "K", (torch.bfloat16,), 3)
+    _dev_tensor(V, "V", (torch.bfloat16,), 3)
+    _dev_tensor(O, "O", (torch.bfloat16,), 4)
+    B, n_q, d = q_idx.shape
+    p = make_problem(B, n_q, k_idx.shape[1], q_pos0, d, q_idx.dtype, top_k, Q.shape[2],
+                     Q.shape[3])
+    if O.shape != Q.shape:
+        raise ValueError("O must have Q's shape")
+    if idx is not None:
+        _dev_tensor(idx, "idx", (torch.int32,), 3)
+        if tuple(idx.shape) != (B, n_q, top_k):
+            raise ValueError("idx must be [B, n_q, top_k]")
+    if lse is not None:
+        _dev_tensor(lse, "lse", (torch.float32,), 3)
+        if tuple(lse.shape) != (B, n_q, Q.shape[2]):
+            raise ValueError("lse must be [B, n_q, H]")
+    _check(load().dsa_forward_noalloc(ctypes.byref(p), _ptr(q_idx), _ptr(k_idx), _ptr(Q), _ptr(K),
+                                      _ptr(V), _ptr(idx), _ptr(O), _ptr(lse), _stream(Q.device)))
     return idx, O, lse
 
 

@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <utility>
 #include <vector>
@@ -490,6 +491,50 @@ dsa_status check_paged(const dsa_problem* p, const int32_t* seq_pos, const dsa_p
     return DSA_OK;
 }
 
+// Scratch of dsa_forward_noalloc: a file-scope device array, so that the
+// call needs neither an allocation nor a caller workspace. Every GPU the
+// library runs on holds its own copy (at its own address) until the process
+// ends; each call on a GPU overwrites that GPU's copy, so calls that overlap
+// on one GPU race. In host code `scratch` names a host-side stand-in, never
+// the device memory: kernels get the address hipGetSymbolAddress returns.
+constexpr size_t kScratchBytes = DSA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// Device address of the current GPU's scratch array, looked up once per
+// device (with that device current) and kept. The stream must belong to the
+// current device.
+dsa_status scratch_address(hipStream_t st, void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(DSA_E_UNSUPPORTED, "device %d is outside the %d devices this call tracks",
+                    dev, kMaxDevices);
+    if (st) {
+        hipDevice_t sd = -1;
+        e = hipStreamGetDevice(st, &sd);
+        if (e != hipSuccess) return hip_fail(e, "hipStreamGetDevice");
+        if ((int)sd != dev)
+            return fail(DSA_E_UNSUPPORTED,
+                        "the stream belongs to device %d while device %d is current; make the "
+                        "stream's device current", (int)sd, dev);
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!ptr) return fail(DSA_E_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+        g_scratch_dev[dev] = ptr;
+    }
+    *out = g_scratch_dev[dev];
+    return DSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -596,6 +641,24 @@ dsa_status dsa_forward(const dsa_problem* p, const void* q_idx, const void* k_id
                        void* ws, size_t ws_bytes, void* stream) {
     dsa_status s = forward_impl(p, q_idx, k_idx, Q, K, V, idx_out, O, lse, ws, ws_bytes, stream,
                                 nullptr, nullptr);
+    return s == DSA_OK ? ok() : s;
+}
+
+dsa_status dsa_forward_noalloc(const dsa_problem* p, const void* q_idx, const void* k_idx,
+                               const void* Q, const void* K, const void* V, int32_t* idx_out,
+                               void* O, float* lse, void* stream) {
+    dsa_status s = check_problem(p);
+    if (s != DSA_OK) return s;
+    const size_t need = forward_layout(p).total;
+    if (need > kScratchBytes)
+        return fail(DSA_E_WORKSPACE,
+                    "dsa_forward_noalloc takes problems whose forward workspace fits its "
+                    "%zu-byte static scratch; this one needs %zu bytes (call dsa_forward with a "
+                    "workspace)", kScratchBytes, need);
+    void* ws = nullptr;
+    if ((s = scratch_address(static_cast<hipStream_t>(stream), &ws)) != DSA_OK) return s;
+    s = forward_impl(p, q_idx, k_idx, Q, K, V, idx_out, O, lse, ws, kScratchBytes, stream,
+                     nullptr, nullptr);
     return s == DSA_OK ? ok() : s;
 }
 

@@ -125,6 +125,25 @@ dsa_status dsa_forward(const dsa_problem* p, const void* q_idx,
                        const void* V, int32_t* idx_out, void* O, float* lse,
                        void* ws, size_t ws_bytes, void* stream);
 
+/* dsa_forward without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation). The same work and results as dsa_forward, with the
+ * workspace in a static device array of DSA_NOALLOC_SCRATCH_BYTES (128 MiB)
+ * that the library holds on every GPU it runs on until the process ends; the
+ * call itself allocates nothing. Problems whose forward workspace
+ * (dsa_workspace_size with DSA_OP_FORWARD) exceeds that size are refused with
+ * DSA_E_WORKSPACE before anything is enqueued: every decode batch up to
+ * 64 x 128K keys with top_k 2048 fits, long prefills do not. Every call on
+ * a GPU shares that GPU's array: calls that overlap in time on one GPU (on
+ * different streams, or from different threads) race and must be ordered by
+ * the caller. The stream must belong to the current device (else
+ * DSA_E_UNSUPPORTED). Other errors: those of dsa_forward. */
+#define DSA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+dsa_status dsa_forward_noalloc(const dsa_problem* p, const void* q_idx,
+                               const void* k_idx, const void* Q, const void* K,
+                               const void* V, int32_t* idx_out, void* O,
+                               float* lse, void* stream);
+
 /* dsa_forward for a ragged decode batch (DSA page, sections 3.3 and 4.3, per
  * sequence): one query per sequence (n_q = 1, and q_pos0 = 0 in *p), the
  * query of sequence b at position seq_pos[b], seeing keys 0..seq_pos[b] of its
