@@ -154,6 +154,21 @@ def _dev_tensor(t, name, dtypes, ndim):
 _IDX_DTYPES = (torch.float8_e4m3fn, torch.bfloat16)
 
 
+def selection_stats(p: Problem, ws, ws_bytes, seq_pos=None):
+    """Diagnostics of the last forward call on this problem and workspace
+    (dsa_internal_selection_stats, not part of the public interface; it
+    synchronises the device): (rows longer than top_k, candidates kept for
+    them, rows recomputed by a fallback, rows whose lists overflowed)."""
+    lib = load()
+    f = lib.dsa_internal_selection_stats
+    f.argtypes = [ctypes.POINTER(Problem), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                  ctypes.c_void_p]
+    f.restype = ctypes.c_int32
+    out = (ctypes.c_int64 * 4)()
+    _check(f(ctypes.byref(p), _ptr(ws), ws_bytes, _ptr(seq_pos), out))
+    return tuple(int(v) for v in out)
+
+
 def _workspace(p, op, dev):
     n = workspace_size(p, op)
     return torch.empty(max(n, 1), dtype=torch.uint8, device=dev), n

@@ -40,7 +40,7 @@ constexpr int kMaxModelWidth = 65536;
 constexpr int kHeadDim = 128;
 constexpr size_t kAlign = 256;
 constexpr size_t kScoreSlabBytes = size_t(2) << 30;  // score rows staged per forward pass
-constexpr size_t kPrefillSlabBytes = size_t(4) << 30;  // candidate lists per forward pass
+constexpr size_t kPrefillSlabBytes = size_t(12) << 30;  // candidate lists per forward pass
 constexpr size_t kPartFloats = 16 * (kHeadDim + 4);   // attention partial per (task)
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -122,14 +122,26 @@ size_t topk_ws_bytes_max(const dsa_problem* p) {
 // Slabs of the many-row path: slab s holds query rows s, s + n, s + 2n, ...
 // (n slabs), so every slab mixes short and long rows; the candidate lists of
 // one slab stay within kPrefillSlabBytes.
-// The budget itself can be lowered for tests (dsa_internal_set_prefill_slab_bytes),
+// Tests can cap the rows of a slab instead (dsa_internal_set_prefill_slab_rows),
 // so that small problems run as several slabs.
-std::atomic<size_t> g_prefill_slab_bytes{kPrefillSlabBytes};
+std::atomic<int> g_prefill_slab_rows{0};
+
+int prefill_maxlen(const dsa_problem* p) {
+    const long long m = (long long)p->q_pos0 + p->n_q;
+    return (int)(m < p->n_k ? m : p->n_k);
+}
+
+// Key ranges per row of the many-row path, decided once for the problem.
+int prefill_nr(const dsa_problem* p) {
+    return dsa::prefill_nranges(prefill_maxlen(p), (long long)p->batch * p->n_q);
+}
 
 int prefill_slabs(const dsa_problem* p) {
-    const size_t row_bytes = (size_t)p->batch * dsa::prefill_cap(p->top_k) * 8;
-    const size_t budget = g_prefill_slab_bytes.load();
-    const size_t per = budget / row_bytes > 0 ? budget / row_bytes : 1;
+    const size_t row_bytes =
+        (size_t)p->batch * prefill_nr(p) * dsa::prefill_cap(p->top_k) * 8;
+    size_t per = kPrefillSlabBytes / row_bytes > 0 ? kPrefillSlabBytes / row_bytes : 1;
+    const int cap_rows = g_prefill_slab_rows.load();
+    if (cap_rows > 0 && per > (size_t)cap_rows) per = (size_t)cap_rows;
     return (int)(((size_t)p->n_q + per - 1) / per);
 }
 
@@ -159,7 +171,7 @@ ForwardLayout forward_layout_core(const dsa_problem* p) {
         L.idx = 0;
         L.topk = ib;
         const size_t pw = align_up(dsa::prefill_ws_bytes(p->batch, prefill_slab_rows(p), p->n_k,
-                                                         p->top_k));
+                                                         p->top_k, prefill_nr(p)));
         if (dsa::attn_ranged_applies(p->batch, p->n_q, p->n_k)) {
             // the key-range attention's partials reuse the select's buffers,
             // which are dead once the last slab's select has run
@@ -329,6 +341,7 @@ dsa_status forward_impl(const dsa_problem* p, const void* q_idx, const void* k_i
             pa.rstride = NS;
             pa.rows = (p->n_q - s0 + NS - 1) / NS;
             pa.scale = index_scale(p->d_idx);
+            pa.nr = prefill_nr(p);
             pa.floor = floor;
             static const char* what[4] = {"prefill threshold launch", "prefill indexer launch",
                                           "prefill select launch", "prefill fallback launch"};
@@ -539,13 +552,79 @@ dsa_status scratch_address(hipStream_t st, void** out) {
 
 extern "C" {
 
-// Not part of the public interface: lowers the candidate-list budget of one
-// many-row slab (0 restores the default of 4 GiB) and returns the previous
-// budget. Tests use it to run small prefill problems as several slabs; the
-// workspace size of a forward call follows the budget in force when it is
-// asked for, so a caller must not change it between sizing and calling.
-size_t dsa_internal_set_prefill_slab_bytes(size_t bytes) {
-    return g_prefill_slab_bytes.exchange(bytes ? bytes : kPrefillSlabBytes);
+// Not part of the public interface: caps the query rows of one many-row slab
+// (0 restores the default, set by a 12 GiB budget for the candidate lists)
+// and returns the previous cap. Tests use it to run small prefill problems as
+// several slabs; the workspace size of a forward call follows the cap in
+// force when it is asked for, so a caller must not change it between sizing
+// and calling.
+int32_t dsa_internal_set_prefill_slab_rows(int32_t rows) {
+    return g_prefill_slab_rows.exchange(rows > 0 ? rows : 0);
+}
+
+// Not part of the public interface: selection statistics of the last
+// forward call on this problem and workspace (blocking: synchronises the
+// device, then copies counters back). out[0] rows longer than top_k (the
+// last slab's rows for a many-row problem), out[1] candidates the indexer
+// kept for them, out[2] rows recomputed by a fallback, out[3] rows whose
+// candidate lists overflowed. Problems on the score-row schedule report
+// out[1..3] = -1. seq_pos: the ragged batch's device positions, or NULL.
+dsa_status dsa_internal_selection_stats(const dsa_problem* p, const void* ws, size_t ws_bytes,
+                                        const int32_t* seq_pos, int64_t* out) {
+    dsa_status s = check_problem(p);
+    if (s != DSA_OK) return s;
+    if (!ws || !out) return fail(DSA_E_NULL, "ws and out must not be NULL");
+    const ForwardLayout L = forward_layout(p);
+    if (ws_bytes < L.total) return fail(DSA_E_WORKSPACE, "workspace smaller than the forward's");
+    hipError_t e = hipDeviceSynchronize();
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+    const char* w = static_cast<const char*>(ws);
+    long long o[4] = {0, -1, -1, -1};
+    if (p->n_q > 1) {
+        const int NS = prefill_slabs(p);
+        dsa::PrefillArgs pa{};
+        pa.B = p->batch;
+        pa.n_q = p->n_q;
+        pa.n_k = p->n_k;
+        pa.q_pos0 = p->q_pos0;
+        pa.top_k = p->top_k;
+        pa.row0 = NS - 1;
+        pa.rstride = NS;
+        pa.rows = (p->n_q - (NS - 1) + NS - 1) / NS;
+        pa.nr = prefill_nr(p);
+        e = dsa::prefill_stats(pa, w + L.topk, o);
+    } else if (dsa::decode_select_applies(slab_rows(p), p->n_k, p->top_k)) {
+        std::vector<int32_t> sp;
+        if (seq_pos) {
+            sp.resize(p->batch);
+            e = hipMemcpy(sp.data(), seq_pos, sp.size() * 4, hipMemcpyDeviceToHost);
+        }
+        if (e == hipSuccess)
+            e = dsa::decode_stats(p->batch, p->n_k, p->q_pos0, seq_pos ? sp.data() : nullptr,
+                                  p->top_k, w + L.topk, o);
+    } else {
+        o[0] = p->batch;
+    }
+    if (e != hipSuccess) return hip_fail(e, "selection statistics");
+    for (int i = 0; i < 4; ++i) out[i] = o[i];
+    return ok();
+}
+
+// Not part of the public interface: the many-row plan of a problem,
+// out = {slabs, rows per slab, key ranges per row, keys per range,
+// candidate-list capacity per (row, range), prefill workspace bytes}.
+dsa_status dsa_internal_prefill_plan(const dsa_problem* p, int64_t* out) {
+    dsa_status s = check_problem(p);
+    if (s != DSA_OK) return s;
+    if (!out) return fail(DSA_E_NULL, "out is NULL");
+    const int nr = prefill_nr(p);
+    out[0] = prefill_slabs(p);
+    out[1] = prefill_slab_rows(p);
+    out[2] = nr;
+    out[3] = dsa::prefill_range_len(prefill_maxlen(p), nr);
+    out[4] = dsa::prefill_cap(p->top_k);
+    out[5] = (int64_t)dsa::prefill_ws_bytes(p->batch, prefill_slab_rows(p), p->n_k, p->top_k, nr);
+    return ok();
 }
 
 dsa_status dsa_workspace_size(const dsa_problem* p, int32_t op, size_t* bytes) {

@@ -26,6 +26,8 @@
 // recomputes the row's scores into the workspace and runs the per-row radix
 // selection on them.
 #include "frag.h"
+
+#include <vector>
 #include "topk_common.h"
 
 namespace dsa {
@@ -704,6 +706,34 @@ size_t decode_select_ws_bytes(int B, int n_k) {
     const size_t n_slots = (n_k + SLOT - 1) / SLOT;
     auto al = [](size_t x) { return (x + 255) / 256 * 256; };
     return al((size_t)B * 4) + al((size_t)B * n_slots * 4) + al((size_t)B * n_slots * SLOT * 8);
+}
+
+hipError_t decode_stats(int B, int n_k, long long q_pos, const int32_t* seq_pos_host, int top_k,
+                        const void* ws, long long out[4]) {
+    const size_t n_slots = (n_k + SLOT - 1) / SLOT;
+    auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+    std::vector<uint32_t> cnt((size_t)B * n_slots);
+    hipError_t e = hipMemcpy(cnt.data(), static_cast<const char*>(ws) + al((size_t)B * 4),
+                             cnt.size() * 4, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return e;
+    long long rows = 0, cand = 0, fb = 0, over = 0;
+    for (int b = 0; b < B; ++b) {
+        const long long pos = seq_pos_host ? (long long)seq_pos_host[b] + q_pos : q_pos;
+        const long long n = pos + 1 < n_k ? pos + 1 : n_k;
+        if (n <= top_k) continue;
+        const size_t used = (size_t)((n + SLOT - 1) / SLOT);
+        long long tot = 0;
+        for (size_t x = 0; x < used; ++x) tot += cnt[(size_t)b * n_slots + x];
+        ++rows;
+        cand += tot;
+        fb += tot < top_k || tot > SEL_CAP;
+        over += tot > SEL_CAP;
+    }
+    out[0] = rows;
+    out[1] = cand;
+    out[2] = fb;
+    out[3] = over;
+    return hipSuccess;
 }
 
 hipError_t launch_decode_select(DecodeArgs a, void* ws, int part, hipStream_t s) {

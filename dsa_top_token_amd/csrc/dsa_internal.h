@@ -167,10 +167,11 @@ struct PrefillArgs {
     int B, n_q, n_k, q_pos0, d, dtype, top_k;
     int row0, rstride, rows;
     float scale;
-    int cap;                // candidates kept per row (set by launch_prefill_select)
+    int cap;                // candidates kept per (row, key range) (set by launch_prefill_select)
+    int rk, nr;             // keys per range (set by launch_prefill_select), ranges per row (caller)
     float* tau_acc;         // workspace pointers (set by launch_prefill_select)
-    uint32_t* cnt;
-    uint2* cand;
+    uint32_t* cnt;          // [rows][nr] sub-list lengths
+    uint2* cand;            // [nr][rows][cap] sub-lists (accumulator - threshold, key index)
     uint32_t* fb_list;
     uint32_t* fb_count;
     float* fb_scores;
@@ -178,14 +179,30 @@ struct PrefillArgs {
 };
 
 int prefill_cap(int top_k);
-size_t prefill_ws_bytes(int B, int rows, int n_k, int top_k);
+// Key ranges per row of the many-row filter for a problem of `rows` query
+// rows (all sequences) of at most maxlen keys; every slab of the problem
+// uses this count (PrefillArgs::nr, prefill_ws_bytes).
+int prefill_nranges(int maxlen, long long rows);
+size_t prefill_ws_bytes(int B, int rows, int n_k, int top_k, int nr);
+// Keys per range for rows of up to maxlen keys in nr ranges (a multiple of
+// 128; nr ranges cover maxlen keys).
+int prefill_range_len(int maxlen, int nr);
 // part 0: threshold, 1: indexer sweep, 2: select, 3: fallback.
 hipError_t launch_prefill_select(PrefillArgs a, void* ws, int part, hipStream_t s);
+// Selection statistics read back from a many-row slab's workspace after its
+// select ran (blocking copies): out = {rows longer than top_k, candidates on
+// their lists, rows recomputed by the fallback, rows whose lists overflowed}.
+hipError_t prefill_stats(const PrefillArgs& a, const void* ws, long long out[4]);
 
 bool decode_select_applies(int rows, int n_k, int top_k);
 size_t decode_select_ws_bytes(int B, int n_k);
 // part 0: sampled threshold, 1: indexer + filter, 2: exact select.
 hipError_t launch_decode_select(DecodeArgs a, void* ws, int part, hipStream_t s);
+// The same for the decode select (seq_pos_host: per-sequence positions or
+// NULL, added to q_pos); fallback rows are those with fewer than top_k
+// candidates or more than the select holds.
+hipError_t decode_stats(int B, int n_k, long long q_pos, const int32_t* seq_pos_host, int top_k,
+                        const void* ws, long long out[4]);
 
 // Threshold mode: removes from finished top-k lists [B][n_q][top_k] (one row
 // per query, ascending, -1 padded) every key whose indexer score is not above

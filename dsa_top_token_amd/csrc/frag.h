@@ -81,6 +81,27 @@ __device__ __forceinline__ f32x4 tile_dot(const Frag<0, D>& a, const Frag<0, D>&
     return acc;
 }
 
+// tile_dot accumulated onto c0 instead of zero: acc = c0 + a . b.
+template <int D>
+__device__ __forceinline__ f32x4 tile_dot_c(const Frag<0, D>& a, const Frag<0, D>& b, f32x4 acc) {
+#pragma unroll
+    for (int c = 0; c < Frag<0, D>::NB; ++c)
+        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            a.big[c], b.big[c], acc, 0, 0, 0, kE8M0One, 0, kE8M0One);
+#pragma unroll
+    for (int c = 0; c < Frag<0, D>::NS; ++c)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a.small[c], b.small[c], acc, 0, 0, 0);
+    return acc;
+}
+
+template <int D>
+__device__ __forceinline__ f32x4 tile_dot_c(const Frag<1, D>& a, const Frag<1, D>& b, f32x4 acc) {
+#pragma unroll
+    for (int c = 0; c < Frag<1, D>::NC; ++c)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v[c], b.v[c], acc, 0, 0, 0);
+    return acc;
+}
+
 // The same fp8 product through v_mfma_f32_16x16x32_fp8_fp8 only (the 32-byte
 // chunks split into four 8-byte steps, the pairing of bytes unchanged).
 template <int D>
@@ -107,16 +128,6 @@ __device__ __forceinline__ f32x4 tile_dot_k32(const Frag<1, D>& a, const Frag<1,
     for (int c = 0; c < Frag<1, D>::NC; ++c)
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v[c], b.v[c], acc, 0, 0, 0);
     return acc;
-}
-
-// Wait states before reading the accumulators of the scaled 16x16x128 fp8
-// MFMA: reads the scheduler places a few cycles after the instruction have
-// returned incomplete rows 8..15, so the results are read only after this
-// padding, with no instruction allowed to move across it.
-__device__ __forceinline__ void mfma_drain() {
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
 }
 
 template <int D>

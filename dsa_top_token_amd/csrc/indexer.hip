@@ -79,17 +79,25 @@ __global__ __launch_bounds__(256) void index_scores_kernel(IndexArgs a) {
             }
             continue;
         }
-        f32x4 acc[4];
+        // All four key fragments are in registers before the first MFMA: a
+        // load issued between the MFMAs could return into an A or B operand
+        // register of an MFMA still queued behind a dependent accumulate
+        // (the operands are read when it starts, not when it issues), and
+        // neither the hardware nor the compiler orders that write after the
+        // read. The epilogue consumes every accumulator before the next
+        // iteration's loads are issued.
+        Frag<DT, D> fb[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const int kr = min(k0 + 16 * t + m, a.n_k - 1);
-            Frag<DT, D> fb;
-            fb.load(kbase + (size_t)kr * RB, g);
-            acc[t] = tile_dot<D>(fa, fb);
+            fb[t].load(kbase + (size_t)kr * RB, g);
         }
-        if constexpr (DT == 0) {
-            if constexpr (Frag<0, D>::NB > 0) mfma_drain();
-        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        __builtin_amdgcn_sched_barrier(0);
+        f32x4 acc[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[t] = tile_dot<D>(fa, fb[t]);
+        __builtin_amdgcn_sched_barrier(0);
         // Output tile layout: lane holds rows 4g + r, key column m.
 #pragma unroll
         for (int r = 0; r < 4; ++r) {

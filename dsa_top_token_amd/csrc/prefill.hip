@@ -37,6 +37,7 @@
 #include "lanes.h"
 
 #include <type_traits>
+#include <vector>
 
 namespace dsa {
 namespace {
@@ -53,6 +54,14 @@ constexpr int TH_TARGET = 64;     // samples expected above tau
 constexpr int TH_UN = 4;          // sampled-key tiles loaded together per pass
 constexpr int FL_CHUNK = 64;      // keys per staged chunk of the filter
 constexpr int FB_WGS = 256;       // fallback workgroups
+// Key ranges of the many-row filter: a row longer than kRangeMin keys is cut
+// into at most kRangesMax ranges of rk keys (a multiple of every slot width),
+// each scored by workgroups of its own into a sub-list of its own, so that no
+// workgroup streams more than rk keys and the longest rows no longer set the
+// kernel time by themselves.
+constexpr int kRangeMin = 16384;
+constexpr int kRangesMax = 4;
+constexpr long long kRangeRowsMin = 16384;  // B x rows from which rows are not split
 constexpr int kBufWord3 = 0x00020000;  // buffer descriptor word 3: 32-bit data format
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
@@ -72,6 +81,14 @@ __device__ float raw_threshold(float tau, float scale) {
     for (int it = 0; it < 64 && x * scale < tau; ++it)
         x = __uint_as_float(__float_as_uint(x) + 1u);
     return x;
+}
+
+// The filter's accumulator threshold tau': t rounded toward zero to 8
+// significant bits when t >= 1/16 (then acc - tau' is exact for integer
+// indexer inputs: see the filter), smaller thresholds unchanged. Keys with
+// acc >= t all have acc >= tau', so the lists keep at least those keys.
+__device__ __forceinline__ float snap_tau(float t) {
+    return t >= 0.0625f ? __uint_as_float(__float_as_uint(t) & 0xFFFF0000u) : t;
 }
 
 // The bin of a wave-private histogram (nbins, bins owned top-down by lanes)
@@ -131,38 +148,41 @@ __device__ __forceinline__ void load_cm(Frag<1, D>& f, const uint8_t* tile, int 
         f.v[c] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const i32x4*>(t + (4 * c + g) * COLB));
 }
 
-// Row-major key chunks in LDS: chunk key r occupies RB contiguous bytes at
-// tile + r RB, its 16-byte granule q at granule slot q ^ sw(r). The chunk is
+// Row-major key slots in LDS: slot key r occupies RB contiguous bytes at
+// tile + r RB, its 16-byte granule q at granule slot q ^ sw(r). The slot is
 // contiguous in global memory too, so each 1 KB global->LDS copy reads 1 KB
 // of consecutive bytes (every 4 lanes one 64-byte segment: XOR keeps aligned
-// groups of four granules together). A fragment read touches chunk keys
-// r = 16 a + 4 u + b (a, b = 0..3) for one tile u; the row pitch already
-// separates some values of b in the LDS banks, so sw takes a and the bits of
-// b that the pitch leaves together, as far as q ^ sw stays below GPR.
+// groups of four granules together). A fragment read touches slot keys
+// r = 16 G a + 4 u + b (a, b = 0..3) for one tile u of a 64 G-key slot; the
+// row pitch already separates some values of b in the LDS banks, so sw takes
+// a and the bits of b that the pitch leaves together, as far as q ^ sw stays
+// below GPR.
 constexpr int gcd_c(int x, int y) { return y == 0 ? x : gcd_c(y, x % y); }
+constexpr int log2_c(int x) { return x <= 1 ? 0 : 1 + log2_c(x / 2); }
 
-template <int RB>
+template <int RB, int G>
 struct RingSw {
     static constexpr int GPR = RB / 16;             // granules per key row
     static constexpr int P2 = GPR & -GPR;           // largest power of two dividing GPR
     static constexpr int SWM = (P2 < 16 ? P2 : 16) - 1;
     static constexpr int SB = (RB / 4) % 64 == 32 ? 1 : 0;  // pitch separates b & 1 only
+    static constexpr int AS = 4 + log2_c(G);        // r >> AS = a
     __device__ static __forceinline__ int sw(int r) {
-        return (((r >> 4) & 3) | (((r & 3) >> SB) << 2)) & SWM;
+        return (((r >> AS) & 3) | (((r & 3) >> SB) << 2)) & SWM;
     }
-    // byte b of chunk key r
+    // byte b of slot key r
     __device__ static __forceinline__ const uint8_t* at(const uint8_t* tile, int r, int b) {
         return tile + r * RB + 16 * ((b >> 4) ^ sw(r)) + (b & 15);
     }
 };
 
-// Fragment of chunk key r from a row-major ring slot (the same bytes, in the
+// Fragment of slot key r from a row-major ring slot (the same bytes, in the
 // same register slots, as Frag::load takes from a contiguous row). The XOR
 // only touches the low bits of the granule index, so each read is a
 // per-lane base plus a constant offset.
-template <int RB, int D>
+template <int RB, int G, int D>
 __device__ __forceinline__ void load_rm(Frag<0, D>& f, const uint8_t* tile, int r, int g) {
-    using W = RingSw<RB>;
+    using W = RingSw<RB, G>;
     const int sw = W::sw(r);
     const uint8_t* row = tile + r * RB;
     // granule 8c + h ^ sw = 8 (c ^ (sw >> 3)) + (h ^ (sw & 7))
@@ -182,9 +202,9 @@ __device__ __forceinline__ void load_rm(Frag<0, D>& f, const uint8_t* tile, int 
             W::at(tile, r, 128 * Frag<0, D>::NB + 32 * c + 8 * g));
 }
 
-template <int RB, int D>
+template <int RB, int G, int D>
 __device__ __forceinline__ void load_rm(Frag<1, D>& f, const uint8_t* tile, int r, int g) {
-    using W = RingSw<RB>;
+    using W = RingSw<RB, G>;
     const int sw = W::sw(r);
     // granule 4c + g ^ sw = 4 (c ^ (sw >> 2)) + (g ^ (sw & 3))
     const uint8_t* base = tile + r * RB + 16 * (g ^ (sw & 3));
@@ -289,7 +309,7 @@ __global__ __launch_bounds__(256) void prefill_threshold_kernel(PrefillArgs a) {
                                 tacc = 0.0f;  // zero mode
                             } else {
                                 const float tau = __uint_as_float(tkey & 0x7fffffffu);
-                                tacc = raw_threshold(tau, a.scale);
+                                tacc = snap_tau(raw_threshold(tau, a.scale));
                             }
                         }
                         a.tau_acc[(size_t)b * a.rows + grow] = tacc;
@@ -303,122 +323,169 @@ __global__ __launch_bounds__(256) void prefill_threshold_kernel(PrefillArgs a) {
 
 // ------------------------------------------------------------------- filter
 
-// Ring depth of the key-chunk pipeline (chunks in flight ahead of the one
-// being consumed is FL_NBUF - 1).
-template <int RB>
-constexpr int fl_nbuf() { return FL_CHUNK * RB <= 8192 || RB <= 320 ? 3 : 2; }
+// Slot width of the filter's key ring, in 64-key units: lane (n, g) of a
+// consumer wave scores keys [16 G g, 16 G g + 16 G) of a 64 G-key slot for
+// its query n, so one accept mask covers 16 G consecutive keys of one row and
+// a row's four lanes hold the slot in index order. Two units halve the
+// per-row prefix and emission passes per score; wide rows keep one (the
+// fragments of all 4 G key tiles of a slot sit in registers at once).
+template <int DT, int D>
+constexpr int filter_g() { return DT == 0 && D <= 128 ? 2 : 1; }
 
 // Query tiles per consumer wave of the filter. Two tiles halve the ring
-// traffic and fragment reads per row (bf16 128K: 7.7 -> 6.4 ms); fp8 keys
-// are cheap to stream and there one tile keeps the longest workgroup's
-// chunk chain (which sets the kernel time at 64K) short.
+// traffic and fragment reads per row (bf16 128K: 7.7 -> 6.4 ms).
 template <int DT, int D>
 constexpr int filter_qt() { return DT == 1 ? 2 : 1; }
 
-// Waits until at most `ahead` chunks of GPR copies each are in flight
+// Consumer waves per filter workgroup. Eight waves (two per SIMD) share
+// each key slot of the narrow fp8 rows, so two workgroups per CU keep four
+// consumer waves on every SIMD to hide one another's LDS and MFMA latency;
+// wider rows keep four.
+template <int DT, int D>
+constexpr int filter_nw() { return filter_g<DT, D>() == 2 ? 8 : 4; }
+
+// Ring depth of the key-slot pipeline (slots in flight ahead of the one
+// being consumed is NBUF - 1).
+template <int RB, int G>
+constexpr int fl_nbuf() { return FL_CHUNK * G * RB <= 20480 ? 3 : 2; }
+
+// Waits until at most `ahead` slots of CPS copies each are in flight
 // (0 <= ahead <= A).
-template <int A, int GPR>
+template <int A, int CPS>
 __device__ __forceinline__ void wait_chunks(int ahead) {
     if constexpr (A > 0) {
         if (ahead >= A) {
-            wait_vmcnt<A * GPR>();
+            wait_vmcnt<A * CPS>();
             return;
         }
-        wait_chunks<A - 1, GPR>(ahead);
+        wait_chunks<A - 1, CPS>(ahead);
     } else {
         wait_vmcnt<0>();
     }
 }
-static_assert(FL_CHUNK == 64, "the producer's lane -> key map covers 64 keys");
+static_assert(FL_CHUNK == 64, "the producer's lane -> key map covers 64-key units");
 
+// The threshold enters the MFMA as its initial accumulator: the product of a
+// key tile with a query tile starting from -tau' leaves acc - tau' for every
+// pair, so the accept bit of a key is the sign bit of its accumulator
+// (+0.0 when acc == tau' is accepted). tau' is the row's accumulator
+// threshold rounded toward zero to 8 significant bits, so with integer
+// indexer inputs (exact products and sums, |acc| < 2^13) every partial sum is
+// a multiple of ulp(tau') >= 2^-11 below 2^13 and acc - tau' is exact. The
+// lists hold acc - tau'; the select adds tau' back (exact for the same
+// reason).
+//
 // QT query tiles of 16 rows per consumer wave share every key fragment read
 // from the ring (the workgroup covers 64 QT rows).
-template <int DT, int D, int QT>
-__global__ __launch_bounds__(320) void prefill_filter_kernel(PrefillArgs a) {
+template <int DT, int D, int QT, int G, int NW>
+__global__ __launch_bounds__(64 * (NW + 1)) void prefill_filter_kernel(PrefillArgs a) {
     constexpr int RB = D * (DT == 0 ? 1 : 2);
     // Ring layout: row-major for fp8 keys (timed 1.31 -> 1.20 ms at 64K),
     // granule-major for bf16 (row-major timed 6.4 -> 6.9 ms at 128K).
     constexpr bool RM = DT == 0;
-    constexpr int WROWS = 16 * QT;   // rows per consumer wave
-    constexpr int ROWS = 4 * WROWS;  // rows per workgroup
-    constexpr int GPR = RB / 16;            // 16-byte granules per key row
-    constexpr int NBUF = fl_nbuf<RB>();
-    static_assert(RB % 16 == 0 && (NBUF - 1) * GPR < 64, "chunk pipeline");
-    // Key chunks: row-major with swizzled granules (RingSw), or granule-major
+    static_assert(RM || G == 1, "granule-major slots hold 64 keys");
+    constexpr int SK = FL_CHUNK * G;       // keys per slot
+    constexpr int LK = 16 * G;             // keys per lane per slot
+    constexpr int NU = 4 * G;              // 16-key tiles per slot
+    constexpr int WROWS = 16 * QT;         // rows per consumer wave
+    constexpr int ROWS = NW * WROWS;       // rows per workgroup (NW consumer waves)
+    constexpr int LKH = LK < 16 ? LK : 16; // accumulators staged per lane at a time
+    constexpr int GPR = RB / 16;           // 16-byte granules per key row
+    constexpr int CPS = G * GPR;           // 1 KB copies per slot
+    constexpr int NBUF = fl_nbuf<RB, G>();
+    static_assert(RB % 16 == 0 && (NBUF - 1) * CPS < 64, "slot pipeline");
+    // Key slots: row-major with swizzled granules (RingSw), or granule-major
     // (granule j of the key at row position rp at slot + j * 1024 + 16 rp).
-    __shared__ __attribute__((aligned(16))) uint8_t ring[NBUF][FL_CHUNK * RB];
-    // per-wave copy of each lane's 16 accumulators: [wave][u][lane] x 4
-    __shared__ f32x4 stage[4][4][64];
+    __shared__ __attribute__((aligned(16))) uint8_t ring[NBUF][SK * RB];
+    // per-wave stage of 16 of a lane's accumulators at a time: value i of
+    // lane l at [i][l] (a lane's reads of different i hit different banks)
+    __shared__ float stage[NW][LKH * 64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n = lane & 15, g = lane >> 4;
     const int n_blk = (a.rows + ROWS - 1) / ROWS;
-    // largest blocks (latest rows) first
-    const int blk = n_blk - 1 - (int)(blockIdx.x / (unsigned)a.B);
+    // Work item (sequence b, row block blk, key range rg): the block's rows
+    // against keys [rg rk, (rg + 1) rk), into sub-list rg of each row. Largest
+    // blocks (latest rows) first; ranges past the block's last key are empty.
+    // Consecutive workgroups are dealt in turn to the 8 XCDs and, within an
+    // XCD, to its 4 shader engines, so each run of 32 consecutive workgroups
+    // takes one range of 32 blocks: every shader engine gets every range
+    // (later ranges are shorter or empty).
     const int b = blockIdx.x % a.B;
+    const int j = (int)(blockIdx.x / (unsigned)a.B);
+    const int rg = (j >> 5) % a.nr;
+    const int bj = (j >> 5) / a.nr * 32 + (j & 31);
+    if (bj >= n_blk) return;  // the grid covers whole runs of 32
+    const int blk = n_blk - 1 - bj;
     const int i0 = blk * ROWS;
     const int kend = row_len(a, min(i0 + ROWS, a.rows) - 1);
-    const int n_chunks = (kend + FL_CHUNK - 1) / FL_CHUNK;
+    const int kr0 = rg * a.rk;
+    if (kr0 >= kend) return;  // the whole workgroup
+    const int kr1 = min(kr0 + a.rk, kend);
+    const int c0 = kr0 / SK;              // rk is a multiple of SK
+    const int c1 = (kr1 + SK - 1) / SK;
     const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + (size_t)b * a.n_k * RB;
 
-    if (wave == 4) {
-        // Producer: global -> LDS copies, NBUF - 1 chunks ahead.
+    if (wave == NW) {
+        // Producer: global -> LDS copies, NBUF - 1 slots ahead.
         //   row-major (RM): copy i moves granules 64 i .. 64 i + 63 of the
-        //     chunk: lane l fills granule slot s = P % GPR of chunk key
+        //     slot: lane l fills granule slot s = P % GPR of slot key
         //     r = P / GPR (P = 64 i + l) with the key's granule s ^ sw(r);
         //   granule-major: copy j moves granule j of every key, lane l taking
-        //     the key at row position l (chunk key 16 ((l / 4) % 4) + 4 (l / 16)
+        //     the key at row position l (slot key 16 ((l / 4) % 4) + 4 (l / 16)
         //     + l % 4).
         const int kr = 16 * ((lane >> 2) & 3) + 4 * (lane >> 4) + (lane & 3);
         auto issue = [&](int c) {
             uint8_t* dst = ring[c % NBUF];
 #pragma unroll
-            for (int i = 0; i < GPR; ++i) {
+            for (int i = 0; i < CPS; ++i) {
                 if constexpr (RM) {
-                    const int P = 64 * i + lane, r = P / GPR, q = (P % GPR) ^ RingSw<RB>::sw(r);
-                    const int key = min(c * FL_CHUNK + r, a.n_k - 1);
+                    const int P = 64 * i + lane, r = P / GPR,
+                              q = (P % GPR) ^ RingSw<RB, G>::sw(r);
+                    const int key = min(c * SK + r, a.n_k - 1);
                     __builtin_amdgcn_global_load_lds(kbase + (size_t)key * RB + 16 * q,
                                                      dst + 1024 * i, 16, 0, 0);
                 } else {
-                    const int key = min(c * FL_CHUNK + kr, a.n_k - 1);
+                    const int key = min(c * SK + kr, a.n_k - 1);
                     __builtin_amdgcn_global_load_lds(kbase + (size_t)key * RB + 16 * i,
                                                      dst + i * (FL_CHUNK * 16), 16, 0, 0);
                 }
             }
         };
-        const int pre = min(NBUF - 1, n_chunks);
-        for (int c = 0; c < pre; ++c) issue(c);
-        for (int c = 0; c < n_chunks; ++c) {
-            // chunk c has landed once at most `ahead` later chunks are in flight
-            const int ahead = min(c + NBUF - 1, n_chunks) - c - 1;
-            wait_chunks<NBUF - 2, GPR>(ahead);
+        const int pre = min(c0 + NBUF - 1, c1);
+        for (int c = c0; c < pre; ++c) issue(c);
+        for (int c = c0; c < c1; ++c) {
+            // slot c has landed once at most `ahead` later slots are in flight
+            const int ahead = min(c + NBUF - 1, c1) - c - 1;
+            wait_chunks<NBUF - 2, CPS>(ahead);
             // A workgroup barrier without the release fence of __syncthreads
             // (that fence would wait for every copy in flight); the wait
-            // above has already made chunk c visible in LDS.
+            // above has already made slot c visible in LDS.
             asm volatile("" ::: "memory");
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
-            if (c + NBUF - 1 < n_chunks) issue(c + NBUF - 1);
+            if (c + NBUF - 1 < c1) issue(c + NBUF - 1);
         }
         wait_vmcnt<0>();
         return;
     }
 
-    // Consumers: wave w scores rows [i0 + WROWS w, +WROWS) against each chunk,
+    // Consumers: wave w scores rows [i0 + WROWS w, +WROWS) against each slot,
     // query tile t holding rows i0 + WROWS w + 16 t + n.
     const int wi0 = i0 + wave * WROWS;
     int my_i[QT], my_len[QT];
     bool live[QT];
-    float tau[QT];
+    f32x4 cinit[QT];   // -tau' of the lane's query, the MFMAs' initial accumulator
     Frag<DT, D> fq[QT];
-    int row_vo[QT];    // byte offset of the row's list in the wave's list block
-    uint32_t cnt[QT];  // each row's list length (same in the row's 4 lanes)
+    int row_vo[QT];    // byte offset of the row's sub-list rg in the wave's list block
+    uint32_t cnt[QT];  // each row's sub-list length (same in the row's 4 lanes)
 #pragma unroll
     for (int t = 0; t < QT; ++t) {
         const int r = wi0 + 16 * t + n;
         live[t] = r < a.rows;
         my_i[t] = min(r, a.rows - 1);
         my_len[t] = live[t] ? row_len(a, my_i[t]) : 0;
-        tau[t] = live[t] ? a.tau_acc[(size_t)b * a.rows + my_i[t]] : __builtin_inff();
+        const float tau = live[t] ? a.tau_acc[(size_t)b * a.rows + my_i[t]] : __builtin_inff();
+        cinit[t] = f32x4{-tau, -tau, -tau, -tau};
         fq[t].load(static_cast<const uint8_t*>(a.q) + ((size_t)b * a.n_q + qrow(a, my_i[t])) * RB, g);
         row_vo[t] = (16 * t + n) * a.cap * 8;
         cnt[t] = 0;
@@ -428,56 +495,60 @@ __global__ __launch_bounds__(320) void prefill_filter_kernel(PrefillArgs a) {
     const bool wave_live = wi0s < a.rows;
     const int w_kend = wave_live ? row_len(a, min(wi0s + WROWS - 1, a.rows - 1)) : 0;
     const int w_kmin = wave_live ? row_len(a, wi0s) : 0;
-    // The wave's WROWS lists are consecutive: one buffer descriptor covers
-    // them, and a store takes a 32-bit byte offset.
+    // Sub-lists are stored range-major ([range][row][cap]), so the wave's
+    // WROWS sub-lists of range rg are consecutive: one buffer descriptor
+    // covers them, and a store takes a 32-bit byte offset.
     const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(a.cand + ((size_t)b * a.rows + (wave_live ? wi0s : 0)) * a.cap), (short)0,
-        WROWS * a.cap * 8, kBufWord3);
-    wait_vmcnt<0>();  // the query fragments are in registers before the chunk loop
+        (void*)(a.cand + ((size_t)rg * a.B * a.rows + (size_t)b * a.rows + (wave_live ? wi0s : 0)) *
+                             a.cap),
+        (short)0, WROWS * a.cap * 8, kBufWord3);
+    wait_vmcnt<0>();  // the query fragments are in registers before the slot loop
     const uint32_t cap = (uint32_t)a.cap;
+    float* stg = &stage[wave][0];
+    // value i of this lane in the stage: byte 256 i + 4 lane
+    const uint8_t* sb = reinterpret_cast<const uint8_t*>(stg + lane);
+    constexpr uint32_t LMASK = LK == 32 ? 0xffffffffu : (1u << LK) - 1u;
 
-    // A operand row n of key tile u is chunk key 16 (n / 4) + 4 u + n % 4
-    // (row position 16 u + n), so output row 4 g + r of tile u is key
-    // 16 g + 4 u + r: lane (n, g) holds keys [16 g, 16 g + 16) of the chunk.
-    // Chunks below w_kmin lie inside every row's causal range; only the
+    // A operand row n of key tile u is slot key 16 G (n / 4) + 4 u + n % 4
+    // (row position 16 u + n in the granule-major layout), so output row
+    // 4 g + r of tile u is key 16 G g + 4 u + r: lane (n, g) holds keys
+    // [16 G g, 16 G g + 16 G) of the slot, value i = 4 u + r.
+    // Slots below w_kmin lie inside every row's causal range; only the
     // later ones (TAIL) mask keys past a row's end.
-    auto chunk = [&](const int c, auto tail_tag) {
+    auto slot = [&](const int c, auto tail_tag) {
         constexpr bool TAIL = decltype(tail_tag)::value;
         __syncthreads();
-        const int k0 = c * FL_CHUNK;
+        const int k0 = c * SK;
         if (k0 < w_kend) {
             const uint8_t* tile = ring[c % NBUF];
-            // Every fragment load of the chunk completes before the first
+            // Every fragment load of the slot completes before the first
             // MFMA, so no load can overwrite an operand register of an MFMA
             // still queued behind a dependent accumulate chain.
-            // A operand row n of key tile u: chunk key 16 (n / 4) + 4 u + n % 4
-            // (row position 16 u + n in the granule-major layout)
-            Frag<DT, D> fk[4];
+            Frag<DT, D> fk[NU];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                if constexpr (RM) load_rm<RB>(fk[u], tile, 16 * (n >> 2) + 4 * u + (n & 3), g);
+            for (int u = 0; u < NU; ++u) {
+                if constexpr (RM) load_rm<RB, G>(fk[u], tile, LK * (n >> 2) + 4 * u + (n & 3), g);
                 else load_cm<FL_CHUNK * 16>(fk[u], tile, 16 * u + n, g);
             }
             __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
             __builtin_amdgcn_sched_barrier(0);
-            f32x4 acc[QT][4];
+            f32x4 acc[QT][NU];
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
+            for (int u = 0; u < NU; ++u)
 #pragma unroll
-                for (int t = 0; t < QT; ++t) acc[t][u] = tile_dot<D>(fk[u], fq[t]);
+                for (int t = 0; t < QT; ++t) acc[t][u] = tile_dot_c<D>(fk[u], fq[t], cinit[t]);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int t = 0; t < QT; ++t) {
-                // bit i of rej: sign of (accumulator of key 16 g + i) - tau
+                // bit i of rej: sign of acc - tau' for key 16 G g + i
                 uint32_t rej = 0;
 #pragma unroll
-                for (int i = 15; i >= 0; --i)
-                    rej = __builtin_amdgcn_alignbit(
-                        rej, __float_as_uint(acc[t][i >> 2][i & 3] - tau[t]), 31);
-                uint32_t bits = ~rej & 0xffffu;
+                for (int i = LK - 1; i >= 0; --i)
+                    rej = __builtin_amdgcn_alignbit(rej, __float_as_uint(acc[t][i >> 2][i & 3]), 31);
+                uint32_t bits = ~rej & LMASK;
                 if constexpr (TAIL) {
-                    const int v = my_len[t] - (k0 + 16 * g);
-                    bits &= v >= 16 ? 0xffffu : (v <= 0 ? 0u : (1u << v) - 1u);
+                    const int v = my_len[t] - (k0 + LK * g);
+                    bits &= v >= LK ? LMASK : (v <= 0 ? 0u : (1u << v) - 1u);
                 }
                 // The row's lanes g = 0..3 hold consecutive key ranges:
                 // exclusive prefix of their counts.
@@ -489,42 +560,76 @@ __global__ __launch_bounds__(320) void prefill_filter_kernel(PrefillArgs a) {
                 const uint32_t o = cnt[t] + ((g & 1) ? x1 : 0u) + ((g & 2) ? x2 : 0u);
                 // An overflowing row's list is abandoned (the row is
                 // recomputed by the fallback); nothing is stored at or past cap.
-                const uint32_t ne = cnt[t] + tot > cap ? 0u : lc;
-                if (ne == 0u) bits = 0u;
+                if (cnt[t] + tot > cap) bits = 0u;
                 cnt[t] += tot;
-                if (__ballot(bits != 0u) != 0ull) {
+                const int vo0 = row_vo[t] + (int)o * 8;
+                // 16 accumulators at a time go through the stage; a lane's
+                // lower 16 keys precede its upper 16, so order is kept.
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) stage[wave][u][lane] = acc[t][u];
-                    // accumulator i of this lane: byte (i / 4) * 1024 + (i % 4) * 4
-                    // of its stage column, = (260 i) & 0xC0C
-                    const uint8_t* sb = reinterpret_cast<const uint8_t*>(&stage[wave][0][lane]);
-                    const uint32_t kb = (uint32_t)(k0 + 16 * g);
-                    int vo = row_vo[t] + (int)o * 8;
-                    while (bits != 0u) {
-                        const int i = __builtin_ctz(bits);
-                        bits &= bits - 1u;
-                        const uint32_t v = *reinterpret_cast<const uint32_t*>(sb + ((i * 260) & 0xC0C));
-                        const u32x2 e = {v, kb + (uint32_t)i};
-                        __builtin_amdgcn_raw_buffer_store_b64(e, lrs, vo, 0, 0);
-                        vo += 8;
+                for (int h = 0; h < LK / LKH; ++h) {
+                    uint32_t hb = LK == LKH ? bits : ((bits >> (LKH * h)) & 0xffffu);
+                    if (__ballot(hb != 0u) == 0ull) continue;
+                    int vo = h == 0 ? vo0 : vo0 + 8 * __popc(bits & 0xffffu);
+#pragma unroll
+                    for (int i = 0; i < LKH; ++i) {
+                        const int v = LKH * h + i;
+                        stg[64 * i + lane] = acc[t][v >> 2][v & 3];
+                    }
+                    const uint32_t kb = (uint32_t)(k0 + LK * g + LKH * h);
+                    // Four entries per round: their stage reads are issued
+                    // together, so a round waits for one LDS latency. Past a
+                    // lane's last entry, ctz(hb | 2^31) keeps the read inside
+                    // the stage (bit 31 only exists when LKH is 32) and the
+                    // store is skipped.
+                    while (hb != 0u) {
+                        uint32_t ix[4];
+                        bool has[4];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            has[j] = hb != 0u;
+                            ix[j] = (uint32_t)__builtin_ctz(hb | (1u << (LKH - 1)));
+                            hb &= hb - 1u;
+                        }
+                        uint32_t v[4];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            v[j] = *reinterpret_cast<const uint32_t*>(sb + 256 * ix[j]);
+                        // all four reads complete here (one wait), none sunk
+                        // into its conditional store
+                        asm volatile("" ::"v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]));
+                        // consecutive entries of the lane leave in pairs (16-byte stores)
+#pragma unroll
+                        for (int j = 0; j < 4; j += 2) {
+                            if (has[j + 1])
+                                __builtin_amdgcn_raw_buffer_store_b128(
+                                    i32x4{(int)v[j], (int)(kb + ix[j]), (int)v[j + 1],
+                                          (int)(kb + ix[j + 1])},
+                                    lrs, vo + 8 * j, 0, 0);
+                            else if (j == 0 || has[j])
+                                __builtin_amdgcn_raw_buffer_store_b64(u32x2{v[j], kb + ix[j]}, lrs,
+                                                                      vo + 8 * j, 0, 0);
+                        }
+                        vo += 32;
                     }
                 }
             }
         }
     };
-    const int c_full = min(n_chunks, w_kmin / FL_CHUNK);
-    int c = 0;
-    for (; c < c_full; ++c) chunk(c, std::false_type{});
-    for (; c < n_chunks; ++c) chunk(c, std::true_type{});
+    const int c_full = max(c0, min(c1, w_kmin / SK));
+    int c = c0;
+    for (; c < c_full; ++c) slot(c, std::false_type{});
+    for (; c < c1; ++c) slot(c, std::true_type{});
 #pragma unroll
     for (int t = 0; t < QT; ++t)
-        if (g == 0 && live[t]) a.cnt[(size_t)b * a.rows + my_i[t]] = cnt[t];
+        if (g == 0 && live[t]) a.cnt[((size_t)b * a.rows + my_i[t]) * a.nr + rg] = cnt[t];
 }
 
 // ------------------------------------------------------------------- select
 
-__device__ __forceinline__ uint32_t cand_key(uint32_t acc_bits, float scale) {
-    return rank_key(relu_scaled(__uint_as_float(acc_bits), scale));
+// Order key of a list entry: the filter stores acc - tau' (tau' the row's
+// threshold, exact for integer indexer inputs), so acc = entry + tau'.
+__device__ __forceinline__ uint32_t cand_key(uint32_t d_bits, float tau, float scale) {
+    return rank_key(relu_scaled(__uint_as_float(d_bits) + tau, scale));
 }
 
 constexpr int SL_NT = 512;      // threads per select workgroup (one row each)
@@ -576,35 +681,49 @@ struct SelRow {
     uint2 raw[PER];
 };
 
-// Entries below this bound are fetched before the count is known; a row's
-// list almost always holds about 2 top_k entries or more.
-__device__ __forceinline__ int sel_spec(const PrefillArgs& a) { return min(a.cap, 2 * a.top_k); }
-
+// The row's list: its sub-lists (one per key range) concatenated in range
+// order, which is index order, so entry j of the list is entry j - pre[q] of
+// sub-list q (pre: the exclusive prefix of the sub-list lengths). cnt > cap
+// marks a row whose sub-lists overflowed or together exceed cap. Trivial rows
+// (at most top_k keys) read nothing.
 template <int PER>
 __device__ __forceinline__ void sel_fetch(const PrefillArgs& a, long long task, SelRow<PER>& r) {
     if (task >= (long long)a.B * a.rows) return;
-    r.cnt = a.cnt[task];
+    r.cnt = 0;
     r.tau = a.tau_acc[task];
-    const uint2* cl = a.cand + (size_t)task * a.cap;
-    const int spec = sel_spec(a);
+    const int n = row_len(a, (int)(task % a.rows));
+    if (n <= a.top_k) return;
+    const int nr = min((n + a.rk - 1) / a.rk, a.nr);  // ranges holding the row's keys
+    const uint32_t cap = (uint32_t)a.cap;
+    const uint32_t* cp = a.cnt + task * a.nr;
+    uint32_t pre[kRangesMax + 1];
+    pre[0] = 0;
+    bool over = false;
 #pragma unroll
-    for (int e = 0; e < PER; ++e) {
-        const int j = e * SL_NT + (int)threadIdx.x;
-        r.raw[e] = j < spec ? cl[j] : make_uint2(0u, 0u);
+    for (int q = 0; q < kRangesMax; ++q) {
+        const uint32_t c = q < nr ? cp[q] : 0u;
+        over |= c > cap;
+        pre[q + 1] = pre[q] + min(c, cap + 1u);
     }
-}
-
-// The rest of the thread's entries, once the count is known (entries past
-// the count are not read).
-template <int PER>
-__device__ __forceinline__ void sel_fetch_rest(const PrefillArgs& a, long long task, int cn,
-                                               SelRow<PER>& r) {
+    r.cnt = over || pre[kRangesMax] > cap ? cap + 1u : pre[kRangesMax];
+    if (r.cnt > cap) return;
     const uint2* cl = a.cand + (size_t)task * a.cap;
-    const int spec = sel_spec(a);
+    const size_t rstep = (size_t)a.B * a.rows * a.cap;  // sub-list q at cl + q rstep
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
-        const int j = e * SL_NT + (int)threadIdx.x;
-        if (j >= spec && j < cn) r.raw[e] = cl[j];
+        const uint32_t j = (uint32_t)(e * SL_NT) + threadIdx.x;
+        uint2 v = make_uint2(0u, 0u);
+        if (j < r.cnt) {
+            uint32_t q = 0, o = j;
+#pragma unroll
+            for (int x = 1; x < kRangesMax; ++x)
+                if (j >= pre[x]) {
+                    q = (uint32_t)x;
+                    o = j - pre[x];
+                }
+            v = cl[q * rstep + o];
+        }
+        r.raw[e] = v;
     }
 }
 
@@ -663,7 +782,6 @@ __device__ __forceinline__ void select_row(const PrefillArgs& a, long long task,
         return;
     }
     const int cn = (int)cnt;
-    sel_fetch_rest<PER>(a, task, cn, rw);
     const float scale = a.scale;
     constexpr uint32_t ZERO_KEY = 0x80000000u;  // order key of a zero score
     // An entry past the count holds key 0, below every candidate's order key
@@ -673,7 +791,7 @@ __device__ __forceinline__ void select_row(const PrefillArgs& a, long long task,
     uint32_t key[PER], ix[PER];
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
-        key[e] = e * SL_NT + tid < cn ? cand_key(rw.raw[e].x, scale) : 0u;
+        key[e] = e * SL_NT + tid < cn ? cand_key(rw.raw[e].x, rw.tau, scale) : 0u;
         ix[e] = rw.raw[e].y;
     }
 
@@ -891,10 +1009,14 @@ hipError_t launch_d(const PrefillArgs& a, int part, hipStream_t s) {
                            a);
     } else if (part == 1) {
         constexpr int QT = filter_qt<DT, D>();
-        const long long nb = (long long)a.B * ((a.rows + 64 * QT - 1) / (64 * QT));
+        constexpr int G = filter_g<DT, D>();
+        constexpr int NW = filter_nw<DT, D>();
+        constexpr int ROWS = 16 * QT * NW;
+        const long long nb =
+            (long long)a.B * a.nr * (((a.rows + ROWS - 1) / ROWS + 31) / 32 * 32);
         if (nb > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL((prefill_filter_kernel<DT, D, QT>), dim3((unsigned)nb), dim3(320), 0, s,
-                           a);
+        hipLaunchKernelGGL((prefill_filter_kernel<DT, D, QT, G, NW>), dim3((unsigned)nb),
+                           dim3(64 * (NW + 1)), 0, s, a);
     } else if (part == 2) {
         if (rows > 0x7fffffffLL) return hipErrorInvalidConfiguration;
         const dim3 grid((unsigned)rows), blk(SL_NT);
@@ -936,24 +1058,90 @@ int prefill_cap(int top_k) {
     return (3 * top_k + 768 + 63) / 64 * 64;
 }
 
-size_t prefill_ws_bytes(int B, int rows, int n_k, int top_k) {
+namespace {
+int range_keys(int maxlen) {
+    int rk = (maxlen + kRangesMax - 1) / kRangesMax;
+    rk = (rk + 127) / 128 * 128;
+    return rk < kRangeMin ? kRangeMin : rk;
+}
+}  // namespace
+
+// Keys per range when a row of up to maxlen keys is cut into nr ranges: a
+// multiple of every slot width (128 keys), nr ranges covering maxlen keys.
+int prefill_range_len(int maxlen, int nr) {
+    const long long rk = ((long long)maxlen + nr - 1) / nr;
+    return (int)((rk + 127) / 128 * 128);
+}
+
+int prefill_nranges(int maxlen, long long rows) {
+    // Ranges pay off when few row blocks would otherwise leave CUs idle
+    // (few long rows, e.g. a chunk of queries at the end of a long context).
+    // With many rows every CU already holds whole blocks, and the extra
+    // sub-lists would only cost memory (more slabs).
+    if (rows >= kRangeRowsMin) return 1;
+    const int rk = range_keys(maxlen);
+    const int nr = (maxlen + rk - 1) / rk;
+    return nr < 1 ? 1 : nr;
+}
+
+size_t prefill_ws_bytes(int B, int rows, int n_k, int top_k, int nr_) {
     auto al = [](size_t x) { return (x + 255) / 256 * 256; };
-    const size_t r = (size_t)B * rows;
-    return al(r * 4) + al(r * 4) + al(r * (size_t)prefill_cap(top_k) * 8) + al(r * 4) + al(4) +
-           al((size_t)FB_WGS * n_k * 4);
+    const size_t r = (size_t)B * rows, nr = (size_t)nr_;
+    return al(r * 4) + al(r * nr * 4) + al(r * nr * (size_t)prefill_cap(top_k) * 8) + al(r * 4) +
+           al(4) + al((size_t)FB_WGS * n_k * 4);
+}
+
+hipError_t prefill_stats(const PrefillArgs& a0, const void* ws, long long out[4]) {
+    auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+    const size_t r = (size_t)a0.B * a0.rows;
+    const int cap = prefill_cap(a0.top_k);
+    const long long ml = (long long)a0.q_pos0 + a0.n_q;
+    const int maxlen = (int)(ml < a0.n_k ? ml : a0.n_k);
+    const int nr = a0.nr, rk = prefill_range_len(maxlen, nr);
+    const char* p = static_cast<const char*>(ws) + al(r * 4);
+    std::vector<uint32_t> cnt(r * nr);
+    hipError_t e = hipMemcpy(cnt.data(), p, cnt.size() * 4, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return e;
+    p += al(r * nr * 4) + al(r * nr * (size_t)cap * 8) + al(r * 4);
+    uint32_t fb = 0;
+    if ((e = hipMemcpy(&fb, p, 4, hipMemcpyDeviceToHost)) != hipSuccess) return e;
+    long long rows = 0, cand = 0, over = 0;
+    for (size_t t = 0; t < r; ++t) {
+        const long long pos = (long long)a0.q_pos0 + a0.row0 + (long long)(t % a0.rows) * a0.rstride;
+        const long long n = pos + 1 < a0.n_k ? pos + 1 : a0.n_k;
+        if (n <= a0.top_k) continue;
+        const int q = (int)std::min<long long>((n + rk - 1) / rk, nr);
+        long long tot = 0;
+        bool ov = false;
+        for (int x = 0; x < q; ++x) {
+            tot += cnt[t * nr + x];
+            ov |= cnt[t * nr + x] > (uint32_t)cap;
+        }
+        ++rows;
+        cand += tot;
+        over += ov || tot > cap;
+    }
+    out[0] = rows;
+    out[1] = cand;
+    out[2] = fb;
+    out[3] = over;
+    return hipSuccess;
 }
 
 hipError_t launch_prefill_select(PrefillArgs a, void* ws, int part, hipStream_t s) {
     auto al = [](size_t x) { return (x + 255) / 256 * 256; };
     const size_t r = (size_t)a.B * a.rows;
     a.cap = prefill_cap(a.top_k);
+    const long long ml = (long long)a.q_pos0 + a.n_q;
+    const int maxlen = (int)(ml < a.n_k ? ml : a.n_k);
+    a.rk = prefill_range_len(maxlen, a.nr);  // a.nr: set by the caller (prefill_nranges)
     char* p = static_cast<char*>(ws);
     a.tau_acc = reinterpret_cast<float*>(p);
     p += al(r * 4);
     a.cnt = reinterpret_cast<uint32_t*>(p);
-    p += al(r * 4);
+    p += al(r * a.nr * 4);
     a.cand = reinterpret_cast<uint2*>(p);
-    p += al(r * (size_t)a.cap * 8);
+    p += al(r * a.nr * (size_t)a.cap * 8);
     a.fb_list = reinterpret_cast<uint32_t*>(p);
     p += al(r * 4);
     a.fb_count = reinterpret_cast<uint32_t*>(p);

@@ -237,13 +237,13 @@ def test_forward_workspace_fits(name):
     p = dsa.make_problem(w.batch, w.n_q, w.n_k, w.q_pos0, w.d_idx, w.idx_dtype, w.top_k,
                          w.n_heads)
     n = dsa.workspace_size(p, dsa.OP_FORWARD)
-    # score slab (<= 2 GiB) or candidate lists (<= 4 GiB), or the key-range
+    # score slab (<= 2 GiB) or candidate lists (<= 12 GiB), or the key-range
     # attention partials that reuse them (one 16-head fp16 row + 16 (lse,
     # scale) pairs per (row, 12288-key range) pair), + index lists + fallback
     # score rows (256 rows of n_k) + thresholds, counts and attention partials
     idx_bytes = w.batch * w.n_q * w.top_k * 4
     ranges = -(-w.n_k // 12288)
-    big = max(4 << 30, w.batch * w.n_q * ranges * (16 * 128 * 2 + 16 * 8))
+    big = max(12 << 30, w.batch * w.n_q * ranges * (16 * 128 * 2 + 16 * 8))
     assert idx_bytes <= n <= big + idx_bytes + 256 * w.n_k * 4 + (64 << 20)
 
 

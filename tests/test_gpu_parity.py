@@ -651,6 +651,26 @@ def test_prefill_large_topk_every_row(gpu_lib, w):
     assert_attn_close(O, O_ref, lse, lse_ref, w.name)
 
 
+@pytest.mark.parametrize("w", [
+    # few query rows at the end of a long context: each row's keys are
+    # scored in up to four key ranges by separate workgroups, into separate
+    # sub-lists the select concatenates in order
+    Workload("chunk_50k_fp8_ranges", "prefill", 2, 700, 50000, 49300, 128, "fp8", 512, 2),
+    Workload("chunk_70k_bf16_ranges", "prefill", 1, 500, 70000, 69500, 160, "bf16", 2048, 2),
+], ids=lambda w: w.name)
+def test_prefill_key_ranges_every_row(gpu_lib, w):
+    say("key-range prefill %s" % w.name)
+    x = synth.make_inputs(w, seed=29)
+    d = to_dev(x)
+    idx, O, lse = dsa.forward(d["q_idx"], d["k_idx"], d["Q"], d["K"], d["V"], w.q_pos0, w.top_k)
+    torch.cuda.synchronize()
+    check_topk_every_row(d, w, idx)
+    idx_ref, O_ref, lse_ref = oracle.forward(x["q_idx"], x["k_idx"], x["Q"], x["K"], x["V"],
+                                             w.q_pos0, w.top_k)
+    assert np.array_equal(idx.cpu().numpy(), idx_ref)
+    assert_attn_close(O, O_ref, lse, lse_ref, w.name)
+
+
 @pytest.mark.parametrize("w,n_slabs", [
     (Workload("prefill_b2_slabs4", "prefill", 2, 6000, 6000, 0, 128, "fp8", 300, 2), 4),
     (Workload("prefill_bf16_slabs3_chunked", "prefill", 1, 3001, 5000, 1999, 96, "bf16", 500, 3),
@@ -665,10 +685,8 @@ def test_prefill_forced_slabs_every_row(gpu_lib, w, n_slabs):
     d = to_dev(x)
     idx1, O1, lse1 = dsa.forward(d["q_idx"], d["k_idx"], d["Q"], d["K"], d["V"], w.q_pos0,
                                  w.top_k)
-    cap = (3 * w.top_k + 768 + 63) // 64 * 64
-    row_bytes = w.batch * cap * 8
     per = (w.n_q + n_slabs - 1) // n_slabs
-    old = set_prefill_slab_bytes(per * row_bytes)
+    old = set_prefill_slab_rows(per)
     try:
         assert prefill_slab_count(d, w) == n_slabs
         say("forced slabs %s: %d slabs" % (w.name, n_slabs))
@@ -676,7 +694,7 @@ def test_prefill_forced_slabs_every_row(gpu_lib, w, n_slabs):
                                   w.top_k)
         torch.cuda.synchronize()
     finally:
-        set_prefill_slab_bytes(old)
+        set_prefill_slab_rows(old)
     idx_ref, O_ref, lse_ref = oracle.forward(x["q_idx"], x["k_idx"], x["Q"], x["K"], x["V"],
                                              w.q_pos0, w.top_k)
     assert np.array_equal(idx.cpu().numpy(), idx_ref)
@@ -800,14 +818,14 @@ def oracle_rows_check(x, idx, O, lse, w, rows):
                       "%s %d rows" % (w.name, len(rows)))
 
 
-def set_prefill_slab_bytes(nbytes):
-    """The library's many-row slab budget (an internal, non-ABI knob; 0
-    restores the default). Returns the previous budget."""
+def set_prefill_slab_rows(rows):
+    """Caps the query rows of one many-row slab (an internal, non-ABI knob of
+    the library; 0 restores the default). Returns the previous cap."""
     import ctypes
-    f = dsa.load().dsa_internal_set_prefill_slab_bytes
-    f.argtypes = [ctypes.c_size_t]
-    f.restype = ctypes.c_size_t
-    return f(nbytes)
+    f = dsa.load().dsa_internal_set_prefill_slab_rows
+    f.argtypes = [ctypes.c_int32]
+    f.restype = ctypes.c_int32
+    return f(rows)
 
 
 def prefill_slab_count(d, w):
@@ -1062,8 +1080,7 @@ def test_full_prefill_batch2_three_slabs(gpu_lib):
     # budget): every row against the torch top-k, sampled rows against the
     # oracle
     w = Workload("prefill_b2_40k", "prefill", 2, 40000, 40000, 0, 128, "fp8", 1024, 16)
-    cap = (3 * w.top_k + 768 + 63) // 64 * 64
-    old = set_prefill_slab_bytes(13334 * w.batch * cap * 8)
+    old = set_prefill_slab_rows(13334)
     try:
         say("full-size %s: generating inputs" % w.name)
         x = synth.make_inputs(w, seed=0)
@@ -1072,7 +1089,7 @@ def test_full_prefill_batch2_three_slabs(gpu_lib):
         idx, O, lse = dsa.forward(d["q_idx"], d["k_idx"], d["Q"], d["K"], d["V"], 0, w.top_k)
         torch.cuda.synchronize()
     finally:
-        set_prefill_slab_bytes(old)
+        set_prefill_slab_rows(old)
     check_selection_properties(idx, 0, w.top_k)
     check_topk_every_row(d, w, idx)
     oracle_rows_check(x, idx, O, lse, w, strided_rows(w.n_q, w.top_k, n=256))
