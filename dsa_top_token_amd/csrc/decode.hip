@@ -36,7 +36,6 @@ namespace {
 using namespace frag;
 using namespace topk;
 
-constexpr int TH_TILES = 8;       // sample tiles a threshold wave loads at once
 constexpr int TH_MAX_SAMPLES = 8192;
 constexpr int SLOT = 256;          // keys per filter wave = one candidate list
 constexpr int SEL_NT = 1024;         // select threads per row (1024 timed 12.8 us against 16.6 with 512)
@@ -74,10 +73,10 @@ constexpr int TH_NT = 1024;   // threads of the threshold workgroup (one per row
 constexpr int RB12 = 4096;    // 12-bit digits of the select rounds
 
 // Bin of a 256-bin histogram holding the rem-th largest counted key, found
-// by wave 0 alone: res[0] = bin, res[1] = keys in higher bins.
-__device__ __forceinline__ void find_bin8(const uint32_t* hist, uint32_t rem, uint32_t* res) {
-    if (threadIdx.x >= 64) return;
-    const int lane = threadIdx.x;
+// by one whole wave: bin and the number of keys in higher bins, in every lane.
+__device__ __forceinline__ void find_bin8_wave(const uint32_t* hist, uint32_t rem, uint32_t& bin,
+                                               uint32_t& above_bin) {
+    const int lane = threadIdx.x & 63;
     const int hi = 255 - 4 * lane;
     uint32_t c[4], loc = 0;
 #pragma unroll
@@ -86,13 +85,50 @@ __device__ __forceinline__ void find_bin8(const uint32_t* hist, uint32_t rem, ui
         loc += c[q];
     }
     uint32_t above = wave_incl_scan(loc) - loc;
+    int fb = -1;
+    uint32_t fa = 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         if (above < rem && above + c[q] >= rem) {
-            res[0] = (uint32_t)(hi - q);
-            res[1] = above;
+            fb = hi - q;
+            fa = above;
         }
         above += c[q];
+    }
+    const unsigned long long mk = __ballot(fb >= 0);
+    const int src = mk ? __ffsll((long long)mk) - 1 : 0;
+    bin = mk ? (uint32_t)__builtin_amdgcn_readlane(fb, src) : 0u;
+    above_bin = mk ? (uint32_t)__builtin_amdgcn_readlane((int)fa, src) : 0u;
+}
+
+// Sample rows are read with LPR consecutive lanes per row (GPL 16-byte
+// granules per lane), so each load instruction covers whole contiguous rows:
+// reads in the MFMA fragment layout, where consecutive lanes fall in
+// different rows, cost the address unit about one cycle per lane.
+template <int RB> struct SampleShape {
+    static constexpr int NG = RB / 16;  // granules per row
+    static constexpr int LPR = NG <= 2 ? 2 : NG <= 4 ? 4 : NG <= 8 ? 8 : 16;
+    static constexpr int GPL = (NG + LPR - 1) / LPR;
+    static constexpr int RPI = 64 / LPR;        // rows per load instruction
+    static constexpr int NB = GPL == 1 ? 16 : 8;  // load instructions in flight
+};
+
+// The 16 fp8 e4m3fn (DT 0) or 8 bf16 (DT 1) values of a granule as float.
+template <int DT>
+__device__ __forceinline__ void granule_values(i32x4 w, float* v) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        if constexpr (DT == 0) {
+            const auto lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[c], 1.0f, false);
+            const auto hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[c], 1.0f, true);
+            v[4 * c] = lo[0];
+            v[4 * c + 1] = lo[1];
+            v[4 * c + 2] = hi[0];
+            v[4 * c + 3] = hi[1];
+        } else {
+            v[2 * c] = __uint_as_float((uint32_t)w[c] << 16);
+            v[2 * c + 1] = __uint_as_float((uint32_t)w[c] & 0xffff0000u);
+        }
     }
 }
 
@@ -100,87 +136,128 @@ __device__ __forceinline__ void find_bin8(const uint32_t* hist, uint32_t rem, ui
 // two 8-bit radix rounds over the keys relative to the smallest sample give
 // the lower edge of the bin holding the m-th largest sample (at least m
 // samples reach it). tau only steers how many candidates the filter keeps;
-// the selection is exact for any tau.
+// the selection is exact for any tau, so the sample scores are fp32 VALU dot
+// products (summation order of their own) rather than the filter's MFMAs.
 template <int DT, int D>
 __global__ __launch_bounds__(TH_NT) void decode_threshold_kernel(DecodeArgs a) {
-    __shared__ uint32_t samp[TH_MAX_SAMPLES];
-    __shared__ uint32_t hist[256];
-    __shared__ uint32_t res[4];
     constexpr int RB = D * (DT == 0 ? 1 : 2);
+    constexpr int WAVES = TH_NT / 64;
+    constexpr int EPG = DT == 0 ? 16 : 8;  // values per granule
+    using SS = SampleShape<RB>;
+    __shared__ uint32_t samp[TH_MAX_SAMPLES];
+    __shared__ uint32_t hist[2][256];
+    __shared__ uint32_t wlo[WAVES], whi[WAVES];
+    __shared__ uint32_t res[2];
     const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
     const int b = blockIdx.x;
     const Plan p = plan_row(a, b);
     if (p.n <= a.top_k || p.ns <= p.m) {
         if (tid == 0) a.tau[b] = 0u;  // every key is a candidate
         return;
     }
-    const int lane = tid & 63, wave = tid >> 6;
-    const int n = lane & 15, g = lane >> 4;
-    Frag<DT, D> fq;
-    fq.load(static_cast<const uint8_t*>(a.q) + ((size_t)b * a.n_q + a.q_row) * RB, g);
+    const int pl = lane % SS::LPR, rl = lane / SS::LPR;
+    const uint8_t* qrow = static_cast<const uint8_t*>(a.q) + ((size_t)b * a.n_q + a.q_row) * RB;
+    float qv[SS::GPL][EPG];
+#pragma unroll
+    for (int g = 0; g < SS::GPL; ++g) {
+        const int gi = pl + SS::LPR * g;
+        const i32x4 w = gi < SS::NG ? *reinterpret_cast<const i32x4*>(qrow + 16 * gi)
+                                    : i32x4{0, 0, 0, 0};
+        granule_values<DT>(w, qv[g]);
+    }
     const uint8_t* kpool = static_cast<const uint8_t*>(a.k);
-    // Waves take TH_TILES tiles of 16 samples at a time, all loads first.
     uint32_t lo = 0xffffffffu, hi = 0u;
-    for (int t0 = wave * 16 * TH_TILES; t0 < p.ns; t0 += (TH_NT / 64) * 16 * TH_TILES) {
-        Frag<DT, D> fk[TH_TILES];
+    // Row r = wave * RPI + rl + (u + NB * t) * WAVES * RPI: NB instructions
+    // per lane in flight, then their dot products.
+    for (int i0 = wave * SS::RPI; i0 < p.ns; i0 += WAVES * SS::RPI * SS::NB) {
+        i32x4 w[SS::NB][SS::GPL];
 #pragma unroll
-        for (int t = 0; t < TH_TILES; ++t)
-            fk[t].load(kpool + (size_t)key_row(a.pages, b, a.n_k,
-                                               min(t0 + 16 * t + n, p.ns - 1) * p.S) * RB, g);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int u = 0; u < SS::NB; ++u) {
+            const int i = min(i0 + u * WAVES * SS::RPI + rl, p.ns - 1);
+            const uint8_t* row = kpool + (size_t)key_row(a.pages, b, a.n_k, i * p.S) * RB;
 #pragma unroll
-        for (int t = 0; t < TH_TILES; ++t) {
-            const f32x4 acc = tile_dot_k32<D>(fk[t], fq);
-            if (n == 0) {
+            for (int g = 0; g < SS::GPL; ++g) {
+                const int gi = pl + SS::LPR * g;
+                w[u][g] = gi < SS::NG ? *reinterpret_cast<const i32x4*>(row + 16 * gi)
+                                      : i32x4{0, 0, 0, 0};
+            }
+        }
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int i = t0 + 16 * t + 4 * g + r;
-                    if (i < p.ns) {
-                        const uint32_t key = rank_key(relu_scaled(acc[r], a.scale));
-                        samp[i] = key;
-                        lo = min(lo, key);
-                        hi = max(hi, key);
-                    }
-                }
+        for (int u = 0; u < SS::NB; ++u) {
+            float s = 0.f;
+#pragma unroll
+            for (int g = 0; g < SS::GPL; ++g) {
+                float kv[EPG];
+                granule_values<DT>(w[u][g], kv);
+#pragma unroll
+                for (int e = 0; e < EPG; ++e) s = fmaf(kv[e], qv[g][e], s);
+            }
+#pragma unroll
+            for (int off = SS::LPR / 2; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+            const int i = i0 + u * WAVES * SS::RPI + rl;
+            if (pl == 0 && i < p.ns) {
+                const uint32_t key = rank_key(relu_scaled(s, a.scale));
+                samp[i] = key;
+                lo = min(lo, key);
+                hi = max(hi, key);
             }
         }
     }
-    if (tid == 0) {
-        res[2] = 0xffffffffu;
-        res[3] = 0u;
-    }
-    __syncthreads();
     lo = wave_min(lo);
     hi = wave_max(hi);
     if (lane == 0) {
-        atomicMin(&res[2], lo);
-        atomicMax(&res[3], hi);
+        wlo[wave] = lo;
+        whi[wave] = hi;
+    }
+    if (tid < 512) (&hist[0][0])[tid] = 0u;
+    __syncthreads();
+    uint32_t kmin = 0xffffffffu, kmax = 0u;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) {
+        kmin = min(kmin, wlo[w]);
+        kmax = max(kmax, whi[w]);
+    }
+    // order keys of non-negative scores: the range is below 2^31
+    const int bits = 32 - __clz((int)(kmax - kmin));
+    if (bits == 0) {  // every sample has the same key
+        if (tid == 0) a.tau[b] = kmin;
+        return;
+    }
+    const int sh0 = bits > 8 ? bits - 8 : 0;
+    for (int i0 = 0; i0 < p.ns; i0 += TH_NT) {
+        const int i = i0 + tid;
+        hist_add(hist[0], i < p.ns ? (samp[i] - kmin) >> sh0 : 0u, i < p.ns);
     }
     __syncthreads();
-    const uint32_t kmin = res[2];
-    const uint32_t range = res[3] - kmin;
-    const int bits = 32 - __clz((int)range);
-    uint32_t rem = (uint32_t)p.m, prefix = 0;
-    int sh = bits;
-    for (int r = 0; r < 2 && sh > 0; ++r) {
-        const int hsh = sh;
-        sh = sh > 8 ? sh - 8 : 0;
-        if (tid < 256) hist[tid] = 0u;
-        __syncthreads();
-        for (int i0 = 0; i0 < p.ns; i0 += TH_NT) {
-            const int i = i0 + tid;
-            const uint32_t d = i < p.ns ? samp[i] - kmin : 0u;
-            const uint32_t dmask = (1u << (hsh - sh)) - 1u;  // this round's bits [sh, hsh)
-            hist_add(hist, (d >> sh) & dmask, i < p.ns && (r == 0 || (d >> hsh) == prefix));
+    if (wave == 0) {
+        uint32_t bin, above;
+        find_bin8_wave(hist[0], (uint32_t)p.m, bin, above);
+        if (lane == 0) {
+            res[0] = bin;
+            res[1] = above;
         }
-        __syncthreads();
-        find_bin8(hist, rem, res);
-        __syncthreads();
-        prefix = (prefix << (hsh - sh)) | res[0];
-        rem -= res[1];
-        __syncthreads();
     }
-    if (tid == 0) a.tau[b] = kmin + (prefix << sh);
+    __syncthreads();
+    const uint32_t b0 = res[0];
+    const uint32_t rem = (uint32_t)p.m - res[1];
+    if (sh0 == 0) {
+        if (tid == 0) a.tau[b] = kmin + b0;
+        return;
+    }
+    const int sh1 = sh0 > 8 ? sh0 - 8 : 0;
+    const uint32_t dmask = (1u << (sh0 - sh1)) - 1u;
+    for (int i0 = 0; i0 < p.ns; i0 += TH_NT) {
+        const int i = i0 + tid;
+        const uint32_t d = i < p.ns ? samp[i] - kmin : 0u;
+        hist_add(hist[1], (d >> sh1) & dmask, i < p.ns && (d >> sh0) == b0);
+    }
+    __syncthreads();
+    if (wave == 0) {
+        uint32_t bin, above;
+        find_bin8_wave(hist[1], rem, bin, above);
+        if (lane == 0) a.tau[b] = kmin + ((((b0 << (sh0 - sh1)) | bin)) << sh1);
+    }
 }
 
 // Bin of an RB12-bin histogram holding the rem-th largest counted key over
