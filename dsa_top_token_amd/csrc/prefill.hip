@@ -632,9 +632,7 @@ __device__ __forceinline__ uint32_t cand_key(uint32_t d_bits, float tau, float s
     return rank_key(relu_scaled(__uint_as_float(d_bits) + tau, scale));
 }
 
-constexpr int SL_NT = 512;      // threads per select workgroup (one row each)
 constexpr int SL_GMAX = 1024;   // keys of a radix bin gathered for the refinement rounds
-
 
 // Bin of a 256-bin histogram holding the rem-th largest counted key, found
 // by wave 0: res[0] = bin, res[1] = keys in higher bins. Called by wave 0.
@@ -666,14 +664,19 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// One SL_NT-thread workgroup per row. Thread t holds list entries
-// t, t + SL_NT, t + 2 SL_NT, ... in registers, so every load instruction of a
-// wave reads 64 consecutive entries (a lane-per-slice layout made the address
-// unit the bottleneck). The k-th key T is found by 8-bit radix rounds over
-// the keys relative to the row's smallest: block-wide while the current bin
-// holds many keys, then by wave 0 alone over the keys of that bin gathered
-// into LDS. Positions in list (= index) order come from ballots within a
-// wave and one table of per-(slot, wave) counts scanned by wave 0.
+// One NT-thread workgroup per row. Thread t holds list entries t, t + NT,
+// t + 2 NT, ... in registers, so every load instruction of a wave reads 64
+// consecutive entries (a lane-per-slice layout made the address unit the
+// bottleneck). Each row is a chain of dependent steps, so the kernel is
+// bound by how many rows a CU holds at once: two registers per entry (the
+// key relative to a lower bound, and the index), ballots taken again after
+// a scan rather than kept per entry, and eight waves per SIMD where that fits
+// without spilling (128 threads per row with four times the entries per
+// thread held more rows but ran each 2.6 times longer). The k-th key T is
+// found by 8-bit radix rounds: workgroup-wide while the current bin holds
+// many keys, then by wave 0 alone over the keys of that bin gathered into
+// LDS. Positions in list (= index) order come from ballots within a wave and
+// one table of per-(slot, wave) counts scanned by wave 0.
 template <int PER>
 struct SelRow {
     uint32_t cnt;
@@ -686,7 +689,7 @@ struct SelRow {
 // sub-list q (pre: the exclusive prefix of the sub-list lengths). cnt > cap
 // marks a row whose sub-lists overflowed or together exceed cap. Trivial rows
 // (at most top_k keys) read nothing.
-template <int PER>
+template <int NT, int PER>
 __device__ __forceinline__ void sel_fetch(const PrefillArgs& a, long long task, SelRow<PER>& r) {
     if (task >= (long long)a.B * a.rows) return;
     r.cnt = 0;
@@ -708,10 +711,18 @@ __device__ __forceinline__ void sel_fetch(const PrefillArgs& a, long long task, 
     r.cnt = over || pre[kRangesMax] > cap ? cap + 1u : pre[kRangesMax];
     if (r.cnt > cap) return;
     const uint2* cl = a.cand + (size_t)task * a.cap;
+    if (nr == 1) {  // one sub-list (workgroup-uniform)
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            const uint32_t j = (uint32_t)(e * NT) + threadIdx.x;
+            r.raw[e] = j < r.cnt ? cl[j] : make_uint2(0u, 0u);
+        }
+        return;
+    }
     const size_t rstep = (size_t)a.B * a.rows * a.cap;  // sub-list q at cl + q rstep
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
-        const uint32_t j = (uint32_t)(e * SL_NT) + threadIdx.x;
+        const uint32_t j = (uint32_t)(e * NT) + threadIdx.x;
         uint2 v = make_uint2(0u, 0u);
         if (j < r.cnt) {
             uint32_t q = 0, o = j;
@@ -727,25 +738,25 @@ __device__ __forceinline__ void sel_fetch(const PrefillArgs& a, long long task, 
     }
 }
 
-// Exclusive prefix, in list order, of two flags per entry packed as
-// (count of fa) << 16 | (count of fb): pre[e] for this thread's entry e
-// (list index e SL_NT + tid), *total for the row. tbl needs
-// PER * SL_NT / 64 + 1 words. Two workgroup barriers; call from every thread.
-template <int PER>
-__device__ __forceinline__ void list_prefix2(const bool fa[PER], const bool fb[PER], uint32_t* tbl,
-                                             uint32_t pre[PER], uint32_t* total) {
-    constexpr int NW = SL_NT / 64, NE = PER * NW;
+// Counts of two flags per (entry slot e, wave), packed (count of fa) << 16 |
+// (count of fb), into tbl, then their exclusive scan in list order by wave 0
+// ((slot, wave) order is list order: slot e's NT entries precede slot
+// e + 1's). Returns the row totals, packed the same way. tbl needs
+// PER * NT / 64 + 1 words. Two workgroup barriers; call from every thread.
+template <int NT, int PER, typename Flags>
+__device__ __forceinline__ uint32_t list_scan2(Flags flags, uint32_t* tbl) {
+    constexpr int NW = NT / 64, NE = PER * NW;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
-        const unsigned long long ma = __ballot(fa[e]), mb = __ballot(fb[e]);
-        pre[e] = (__builtin_amdgcn_mbcnt_hi((uint32_t)(ma >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)ma, 0u)) << 16) |
-                 __builtin_amdgcn_mbcnt_hi((uint32_t)(mb >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mb, 0u));
+        bool fa, fb;
+        flags(e, fa, fb);
+        const unsigned long long ma = __ballot(fa), mb = __ballot(fb);
         if (lane == 0) tbl[e * NW + w] = ((uint32_t)__popcll(ma) << 16) | (uint32_t)__popcll(mb);
+        __builtin_amdgcn_sched_barrier(0);  // one entry at a time: short live ranges
     }
     __syncthreads();
     if (w == 0) {
-        // (slot, wave) order is list order: slot e's 512 entries precede slot e + 1's
         uint32_t carry = 0;
 #pragma unroll
         for (int b0 = 0; b0 < NE; b0 += 64) {
@@ -757,22 +768,30 @@ __device__ __forceinline__ void list_prefix2(const bool fa[PER], const bool fb[P
         if (lane == 0) tbl[NE] = carry;
     }
     __syncthreads();
-#pragma unroll
-    for (int e = 0; e < PER; ++e) pre[e] += tbl[e * NW + w];
-    *total = tbl[NE];
+    return tbl[NE];
 }
 
-template <int PER>
-__device__ __forceinline__ void select_row(const PrefillArgs& a, long long task, SelRow<PER> rw,
+// Packed position of this thread's entry among the flagged entries before it
+// in list order, from the scanned table entry of its (slot, wave).
+__device__ __forceinline__ uint32_t list_pos2(bool fa, bool fb, uint32_t base) {
+    const unsigned long long ma = __ballot(fa), mb = __ballot(fb);
+    return base +
+           ((__builtin_amdgcn_mbcnt_hi((uint32_t)(ma >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)ma, 0u)) << 16) |
+            __builtin_amdgcn_mbcnt_hi((uint32_t)(mb >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mb, 0u)));
+}
+
+template <int NT, int PER>
+__device__ __forceinline__ void select_row(const PrefillArgs& a, long long task, const SelRow<PER>& rw,
                                            uint32_t* hist, uint32_t* gk, uint32_t* tbl,
-                                           uint32_t* res) {
-    const int tid = threadIdx.x;
+                                           uint32_t* wmax, uint32_t* res) {
+    constexpr int NW = NT / 64;
+    const int tid = threadIdx.x, w = tid >> 6;
     const int b = (int)(task / a.rows), i = (int)(task % a.rows);
     const int n = row_len(a, i);
     const int k = a.top_k;
     int32_t* out = a.idx + ((size_t)b * a.n_q + qrow(a, i)) * k;
     if (n <= k) {
-        fill_prefix(out, n, k, tid, SL_NT);
+        fill_prefix(out, n, k, tid, NT);
         return;
     }
     const uint32_t cnt = rw.cnt;
@@ -783,91 +802,85 @@ __device__ __forceinline__ void select_row(const PrefillArgs& a, long long task,
     }
     const int cn = (int)cnt;
     const float scale = a.scale;
-    constexpr uint32_t ZERO_KEY = 0x80000000u;  // order key of a zero score
-    // An entry past the count holds key 0, below every candidate's order key
-    // (scores are >= +0.0, so keys are >= ZERO_KEY): such entries never pass a
-    // comparison against ZERO_KEY or T, and the radix rounds place them in
-    // digit 0 (d = max(key, kmin) - kmin = 0), below the k-th key.
-    uint32_t key[PER], ix[PER];
+    // Keys are held as dk = key - kmin + 1, kmin being the order key of a
+    // score of exactly tau' (every entry holds acc - tau' >= +0.0, so every
+    // listed key is at least kmin and its dk at least 1). An entry past the
+    // count holds dk = 0: below every listed key, so it never reaches the k-th
+    // key, and never equal to it.
+    const uint32_t kmin = cand_key(0u, rw.tau, scale);
+    uint32_t dk[PER], ix[PER];
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
-        key[e] = e * SL_NT + tid < cn ? cand_key(rw.raw[e].x, rw.tau, scale) : 0u;
+        dk[e] = e * NT + tid < cn ? cand_key(rw.raw[e].x, rw.tau, scale) - kmin + 1u : 0u;
         ix[e] = rw.raw[e].y;
     }
+    if (tid == 0) res[4] = 0u;
 
     if (zero_mode) {
         // The list holds every key with a positive score (plus some zeros);
-        // every key off the list scores zero.
-        bool pos[PER], none[PER];
-#pragma unroll
-        for (int e = 0; e < PER; ++e) {
-            pos[e] = key[e] > ZERO_KEY;
-            none[e] = false;
-        }
-        uint32_t rk[PER], np;
-        list_prefix2<PER>(pos, none, tbl, rk, &np);
-        np >>= 16;
+        // every key off the list scores zero. With tau' = 0, kmin is the key
+        // of a zero score, so an entry is positive when its dk exceeds 1.
+        const uint32_t np = list_scan2<NT, PER>(
+            [&](int e, bool& fa, bool& fb) {
+                fa = dk[e] > 1u;
+                fb = false;
+            },
+            tbl) >> 16;
         if (np < (uint32_t)k) {
             // Positives plus the lowest-index zeros. With P the positives in
-            // index order, P[r] - r zeros precede P[r]; the first cs
-            // positives (P[r] - r < Z) come before the Z-th zero.
+            // index order, P[r] - r zeros precede P[r]; P[r] - r does not
+            // decrease with r, so the positives with P[r] - r < Z (those
+            // before the Z-th zero) are the first cs of them.
             const uint32_t Z = (uint32_t)k - np;
-            bool early[PER];
-#pragma unroll
-            for (int e = 0; e < PER; ++e) early[e] = pos[e] && ix[e] - (rk[e] >> 16) < Z;
-            uint32_t dummy[PER], cs;
-            list_prefix2<PER>(early, none, tbl, dummy, &cs);
-            cs >>= 16;
-            const uint32_t head = Z + cs;  // out[0, head) = 0 .. head - 1
-            for (uint32_t o = tid; o < head; o += SL_NT) out[o] = (int32_t)o;
+            uint32_t early = 0;
 #pragma unroll
             for (int e = 0; e < PER; ++e) {
-                const uint32_t r = rk[e] >> 16;
-                if (pos[e] && r >= cs) out[Z + r] = (int32_t)ix[e];
+                const bool pos = dk[e] > 1u;
+                const uint32_t r = list_pos2(pos, false, tbl[e * NW + w]) >> 16;
+                early += pos && ix[e] - r < Z ? 1u : 0u;
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            early = wave_incl_scan(early);
+            if ((tid & 63) == 63) atomicAdd(&res[4], early);
+            __syncthreads();
+            const uint32_t cs = res[4];
+            const uint32_t head = Z + cs;  // out[0, head) = 0 .. head - 1
+            for (uint32_t o = tid; o < head; o += NT) out[o] = (int32_t)o;
+#pragma unroll
+            for (int e = 0; e < PER; ++e) {
+                const bool pos = dk[e] > 1u;
+                const uint32_t r = list_pos2(pos, false, tbl[e * NW + w]) >> 16;
+                if (pos && r >= cs) out[Z + r] = (int32_t)ix[e];
+                __builtin_amdgcn_sched_barrier(0);
             }
             return;
         }
     }
 
-    // Range of the row's order keys; digits are taken relative to the smallest.
-    uint32_t lo = 0xffffffffu, hi = 0u;
+    // Radix digits of dk, from the top bit of the row's largest dk.
+    uint32_t hi = 0u;
 #pragma unroll
-    for (int e = 0; e < PER; ++e) {
-        lo = min(lo, key[e] - 1u);  // an entry past the count wraps to the top
-        hi = max(hi, key[e]);
-    }
-    lo += 1u;
-    if (tid == 0) {
-        res[2] = 0xffffffffu;
-        res[3] = 0u;
-        res[4] = 0u;
-    }
-    __syncthreads();
-    lo = wave_min(lo);
+    for (int e = 0; e < PER; ++e) hi = max(hi, dk[e]);
     hi = wave_max(hi);
-    if ((tid & 63) == 0 && lo <= hi) {
-        atomicMin(&res[2], lo);
-        atomicMax(&res[3], hi);
-    }
+    if ((tid & 63) == 0) wmax[w] = hi;
     __syncthreads();
-    const uint32_t kmin = res[2];
-    const uint32_t range = res[3] - kmin;
-    // Radix rounds over bits [sh, hsh) of d = key - kmin, from the top.
+    uint32_t range = 0u;
+#pragma unroll
+    for (int x = 0; x < NW; ++x) range = max(range, wmax[x]);
+    // Radix rounds over bits [sh, hsh) of dk, from the top.
     uint32_t rem = (uint32_t)k, prefix = 0;
     int sh = 32 - __clz((int)range);
     bool first = true, gathered = false;
-    uint32_t G = 0;
     while (sh > 0 && !gathered) {
         const int hsh = sh;
         sh = sh > 8 ? sh - 8 : 0;
         const uint32_t mask = (1u << (hsh - sh)) - 1u;
-        if (tid < 256) hist[tid] = 0u;
+        for (int x = tid; x < 256; x += NT) hist[x] = 0u;
         __syncthreads();
 #pragma unroll
         for (int e = 0; e < PER; ++e) {
-            if (e * SL_NT >= cn) continue;  // workgroup-uniform
-            const uint32_t d = max(key[e], kmin) - kmin;
-            hist_add(hist, (d >> sh) & mask, first || (d >> hsh) == prefix);
+            if (e * NT >= cn) continue;  // workgroup-uniform
+            hist_add(hist, (dk[e] >> sh) & mask, first || (dk[e] >> hsh) == prefix);
         }
         __syncthreads();
         if (tid < 64) wave_find_bin8(hist, rem, res);
@@ -880,16 +893,15 @@ __device__ __forceinline__ void select_row(const PrefillArgs& a, long long task,
         if (sh > 0 && hist[bin] <= (uint32_t)SL_GMAX) {
 #pragma unroll
             for (int e = 0; e < PER; ++e) {
-                if (e * SL_NT >= cn) continue;
-                const uint32_t d = max(key[e], kmin) - kmin;
-                if ((d >> sh) == prefix) gk[atomicAdd(&res[4], 1u)] = d;
+                if (e * NT >= cn) continue;
+                if ((dk[e] >> sh) == prefix) gk[atomicAdd(&res[4], 1u)] = dk[e];
             }
             gathered = true;
         }
         __syncthreads();
     }
     if (gathered) {
-        G = res[4];
+        const uint32_t G = res[4];
         if (tid < 64) {
             // wave 0 alone: the remaining rounds over the gathered keys
             while (sh > 0) {
@@ -922,43 +934,49 @@ __device__ __forceinline__ void select_row(const PrefillArgs& a, long long task,
         prefix = res[5];
         rem = res[6];
     }
-    uint32_t T = kmin + prefix;  // keep every key above T and the first rem keys equal to T
+    // The k-th key T = kmin + prefix - 1: keep every key above T and the
+    // first rem keys equal to it (in dk terms: above, or equal to, prefix).
+    uint32_t Td = prefix;
     // Threshold mode: when the k-th key is not above the floor, the kept set
     // is every key above the floor (all on the list, since they outrank the
-    // k-th key); otherwise the top-k set is already above it.
-    const bool floored = a.floor.on && T <= a.floor.key;
+    // k-th key); otherwise the top-k set is already above it. A floor below
+    // kmin keeps every listed key (dk above 0).
+    const bool floored = a.floor.on && kmin + prefix - 1u <= a.floor.key;
     if (floored) {
-        T = a.floor.key;
+        Td = a.floor.key >= kmin ? a.floor.key - kmin + 1u : 0u;
         rem = 0;
     }
     // Ordered compaction: every key above T, and the T-ties in list order.
-    bool gt[PER], eq[PER];
+    const uint32_t tot = list_scan2<NT, PER>(
+        [&](int e, bool& fa, bool& fb) {
+            fa = dk[e] > Td;
+            fb = dk[e] == Td;
+        },
+        tbl);
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
-        gt[e] = key[e] > T;
-        eq[e] = key[e] == T;
-    }
-    uint32_t pk[PER], tot;
-    list_prefix2<PER>(gt, eq, tbl, pk, &tot);
-#pragma unroll
-    for (int e = 0; e < PER; ++e) {
-        const uint32_t gb = pk[e] >> 16, eb = pk[e] & 0xffffu;
-        if (gt[e]) out[gb + min(eb, rem)] = (int32_t)ix[e];
-        else if (eq[e] && eb < rem) out[gb + eb] = (int32_t)ix[e];
+        const bool gt = dk[e] > Td, eq = dk[e] == Td;
+        const uint32_t pk = list_pos2(gt, eq, tbl[e * NW + w]);
+        const uint32_t gb = pk >> 16, eb = pk & 0xffffu;
+        if (gt) out[gb + min(eb, rem)] = (int32_t)ix[e];
+        else if (eq && eb < rem) out[gb + eb] = (int32_t)ix[e];
+        __builtin_amdgcn_sched_barrier(0);
     }
     if (floored)
-        for (int j = (int)(tot >> 16) + tid; j < k; j += SL_NT) out[j] = -1;
+        for (int j = (int)(tot >> 16) + tid; j < k; j += NT) out[j] = -1;
     if (a.floor.on && tid == 0) a.floor.done[(size_t)b * a.n_q + qrow(a, i)] = 1u;
 }
-template <int PER>
-__global__ __launch_bounds__(SL_NT) void prefill_select_kernel(PrefillArgs a) {
+
+template <int NT, int PER>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(PER <= 14 ? 8 : 1))) void prefill_select_kernel(PrefillArgs a) {
     __shared__ uint32_t hist[256];
     __shared__ uint32_t gk[SL_GMAX];
-    __shared__ uint32_t tbl[PER * SL_NT / 64 + 1];
+    __shared__ uint32_t tbl[PER * NT / 64 + 1];
+    __shared__ uint32_t wmax[NT / 64];
     __shared__ uint32_t res[8];
     SelRow<PER> rw;
-    sel_fetch<PER>(a, blockIdx.x, rw);
-    select_row<PER>(a, blockIdx.x, rw, hist, gk, tbl, res);
+    sel_fetch<NT, PER>(a, blockIdx.x, rw);
+    select_row<NT, PER>(a, blockIdx.x, rw, hist, gk, tbl, wmax, res);
 }
 
 // ----------------------------------------------------------------- fallback
@@ -1019,16 +1037,16 @@ hipError_t launch_d(const PrefillArgs& a, int part, hipStream_t s) {
                            dim3(64 * (NW + 1)), 0, s, a);
     } else if (part == 2) {
         if (rows > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-        const dim3 grid((unsigned)rows), blk(SL_NT);
-        // PER = ceil(cap / SL_NT) entries per thread at most
-        const int per = (a.cap + SL_NT - 1) / SL_NT;
-        if (per <= 2) hipLaunchKernelGGL(prefill_select_kernel<2>, grid, blk, 0, s, a);
-        else if (per <= 4) hipLaunchKernelGGL(prefill_select_kernel<4>, grid, blk, 0, s, a);
-        else if (per <= 8) hipLaunchKernelGGL(prefill_select_kernel<8>, grid, blk, 0, s, a);
-        else if (per <= 11) hipLaunchKernelGGL(prefill_select_kernel<11>, grid, blk, 0, s, a);
-        else if (per <= 14) hipLaunchKernelGGL(prefill_select_kernel<14>, grid, blk, 0, s, a);
-        else if (per <= 18) hipLaunchKernelGGL(prefill_select_kernel<18>, grid, blk, 0, s, a);
-        else if (per <= 26) hipLaunchKernelGGL(prefill_select_kernel<26>, grid, blk, 0, s, a);
+        const dim3 grid((unsigned)rows), blk(512);
+        // PER = ceil(cap / 512) entries per thread at most
+        const int per = (a.cap + 511) / 512;
+        if (per <= 2) hipLaunchKernelGGL((prefill_select_kernel<512, 2>), grid, blk, 0, s, a);
+        else if (per <= 4) hipLaunchKernelGGL((prefill_select_kernel<512, 4>), grid, blk, 0, s, a);
+        else if (per <= 8) hipLaunchKernelGGL((prefill_select_kernel<512, 8>), grid, blk, 0, s, a);
+        else if (per <= 11) hipLaunchKernelGGL((prefill_select_kernel<512, 11>), grid, blk, 0, s, a);
+        else if (per <= 14) hipLaunchKernelGGL((prefill_select_kernel<512, 14>), grid, blk, 0, s, a);
+        else if (per <= 18) hipLaunchKernelGGL((prefill_select_kernel<512, 18>), grid, blk, 0, s, a);
+        else if (per <= 26) hipLaunchKernelGGL((prefill_select_kernel<512, 26>), grid, blk, 0, s, a);
         else return hipErrorInvalidValue;
     } else {
         hipLaunchKernelGGL((prefill_fallback_kernel<DT, D>), dim3(FB_WGS), dim3(512), 0, s, a);
