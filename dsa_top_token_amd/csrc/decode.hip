@@ -5,22 +5,25 @@
 // scores every key of the query's prefix and the query keeps its top_k keys.
 // Here the full score row never reaches memory:
 //   threshold  one workgroup per sequence scores every S-th key
-//              (S = max(top_k / 32, ceil(n/8192))) and takes as tau the lower edge
-//              of the bin (two 8-bit radix rounds over the sample keys
+//              (S = max(top_k / 32, ceil(n/8192))) with fp32 VALU dot
+//              products over coalesced row loads, and takes as tau the lower
+//              edge of the bin (two 8-bit radix rounds over the sample keys
 //              relative to the smallest) holding the m-th largest sample,
 //              m = ceil(2 * top_k / S). About 2 * top_k keys of the row are
 //              expected to reach tau.
 //   filter     the streaming indexer kernel scores every key and keeps only
 //              those whose order key is >= tau, each wave writing its own
 //              (order key, index) list for its 256 keys in ascending index
-//              order (no device atomics). 128-byte key rows are streamed by
-//              contiguous nontemporal global->LDS copies into a two-buffer
-//              ring per wave; other widths load MFMA fragments directly.
-//   select     one workgroup per sequence loads the candidates into LDS,
-//              finds the exact k-th key T by 12-bit radix rounds over the
-//              keys relative to the smallest candidate, and writes the
-//              selection in ascending index order, cutting the T-ties in
-//              list (= index) order.
+//              order (no device atomics). Key rows of up to 160 bytes are
+//              streamed by contiguous nontemporal global->LDS copies into a
+//              two-buffer ring per wave; wider rows load MFMA fragments
+//              directly.
+//   select     one workgroup per sequence loads the candidates into LDS and
+//              finds the exact k-th key T from the keys relative to tau: a
+//              12-bit radix round over the workgroup, then wave 0 alone over
+//              the keys of T's bin once it is small (further workgroup rounds
+//              otherwise); it writes the selection in ascending index order,
+//              cutting the T-ties in list (= index) order.
 // The result is exact whenever at least top_k keys reach tau, which select
 // checks; otherwise (or when the candidates exceed its LDS list) select
 // recomputes the row's scores into the workspace and runs the per-row radix
@@ -41,7 +44,7 @@ constexpr int SLOT = 256;          // keys per filter wave = one candidate list
 constexpr int SEL_NT = 1024;         // select threads per row (1024 timed 12.8 us against 16.6 with 512)
 constexpr int SEL_CAP = 12288;     // candidates select can hold in LDS
 constexpr int SEL_MAX_SLOTS = 4096;
-
+constexpr int SEL_GMAX = 1024;     // keys of a radix bin gathered for wave 0
 struct Plan {
     int n, S, ns, m;
 };
@@ -71,6 +74,13 @@ __device__ __forceinline__ f32x4 key_tile(const uint8_t* kpool, long long row, c
 
 constexpr int TH_NT = 1024;   // threads of the threshold workgroup (one per row)
 constexpr int RB12 = 4096;    // 12-bit digits of the select rounds
+
+// Orders one wave's LDS accesses across its lanes.
+__device__ __forceinline__ void wave_lds_fence() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
 // Bin of a 256-bin histogram holding the rem-th largest counted key, found
 // by one whole wave: bin and the number of keys in higher bins, in every lane.
@@ -651,33 +661,32 @@ __global__ __launch_bounds__(SEL_NT) void decode_select_kernel(DecodeArgs a) {
     }
     __syncthreads();
     const int cnt = (int)total;
-    // Exact k-th key T: 12-bit radix rounds over the order keys relative to
-    // the smallest candidate, as many as the key range needs.
-    uint32_t lo = 0xffffffffu, hi = 0u;
-    for (int i = tid; i < cnt; i += SEL_NT) {
-        lo = min(lo, keys[i]);
-        hi = max(hi, keys[i]);
-    }
-    if (tid == 0) {
-        res[2] = 0xffffffffu;
-        res[3] = 0u;
-    }
-    __syncthreads();
-    lo = wave_min(lo);
+    // Exact k-th key T from the order keys relative to tau (every listed key
+    // reached it): 12-bit radix rounds over the workgroup from the top bit of
+    // the largest, until the bin holding the k-th key is small enough to be
+    // gathered into LDS (soff is free by now); wave 0 alone then takes 8-bit
+    // rounds over the gathered keys' remaining bits.
+    const uint32_t kmin = a.tau[b];
+    uint32_t hi = 0u;
+    for (int i = tid; i < cnt; i += SEL_NT) hi = max(hi, keys[i]);
     hi = wave_max(hi);
-    if ((tid & 63) == 0) {
-        atomicMin(&res[2], lo);
-        atomicMax(&res[3], hi);
-    }
+    if ((tid & 63) == 0) wsum[tid >> 6] = hi;
+    if (tid == 0) res[2] = 0u;
     __syncthreads();
-    const uint32_t kmin = res[2];
-    const uint32_t range = res[3] - kmin;
-    __syncthreads();
+    uint32_t kmax = 0u;
+#pragma unroll
+    for (int x = 0; x < SEL_NT / 64; ++x) kmax = max(kmax, wsum[x]);
+    __syncthreads();  // wsum is rewritten by the scans below
+    const uint32_t range = kmax - kmin;
     const int R = (32 - __clz((int)range) + 11) / 12;
     uint32_t rem = (uint32_t)k, prefix = 0;
-    for (int r = 0; r < R; ++r) {
+    uint32_t* gk = soff;
+    int cur_sh = 0;
+    bool gathered = false;
+    for (int r = 0; r < R && !gathered; ++r) {
         const int sh = 12 * (R - 1 - r);
-        const int hsh = r == 0 ? 0 : sh + 12;
+        const int hsh = sh + 12;
+        cur_sh = sh;
         for (int q = tid; q < RB12; q += SEL_NT) hist[q] = 0u;
         __syncthreads();
         for (int i0 = 0; i0 < cnt; i0 += SEL_NT) {
@@ -689,7 +698,51 @@ __global__ __launch_bounds__(SEL_NT) void decode_select_kernel(DecodeArgs a) {
         find_bin12<SEL_NT>(hist, rem, wsum, res);
         prefix = (prefix << 12) | res[0];
         rem -= res[1];
+        if (sh > 0 && hist[res[0]] <= (uint32_t)SEL_GMAX) {
+            const uint32_t low = (1u << sh) - 1u;
+            for (int i0 = 0; i0 < cnt; i0 += SEL_NT) {
+                const int i = i0 + tid;
+                const uint32_t d = i < cnt ? keys[i] - kmin : 0u;
+                const bool take = i < cnt && (d >> sh) == prefix;
+                const uint32_t slot = wave_append(take, &res[2]);
+                if (take) gk[slot] = d & low;
+            }
+            gathered = true;
+        }
         __syncthreads();
+    }
+    if (gathered) {
+        if (tid < 64) {
+            const uint32_t G = res[2];
+            uint32_t sp = 0, rm = rem;  // bits [s2, cur_sh) found so far
+            int s2 = cur_sh;
+            while (s2 > 0) {
+                const int h2 = s2;
+                s2 = s2 > 8 ? s2 - 8 : 0;
+                const uint32_t mask = (1u << (h2 - s2)) - 1u;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) hist[tid + 64 * q] = 0u;
+                wave_lds_fence();
+                for (uint32_t g0 = 0; g0 < G; g0 += 64) {
+                    const uint32_t gi = g0 + tid;
+                    const uint32_t v = gi < G ? gk[gi] : 0u;
+                    hist_add(hist, (v >> s2) & mask, gi < G && (v >> h2) == sp);
+                }
+                wave_lds_fence();
+                uint32_t bin, above;
+                find_bin8_wave(hist, rm, bin, above);
+                sp = (sp << (h2 - s2)) | bin;
+                rm -= above;
+                wave_lds_fence();  // hist is cleared again by the next round
+            }
+            if (tid == 0) {
+                res[0] = (prefix << cur_sh) | sp;
+                res[1] = rm;
+            }
+        }
+        __syncthreads();
+        prefix = res[0];
+        rem = res[1];
     }
     uint32_t T = kmin + prefix;  // keep every key above T and the first rem keys equal to T
     // Threshold mode: when the k-th key is not above the floor, the kept set

@@ -8,27 +8,30 @@
 //   threshold  per 16-row block: scores every S-th key of each row's prefix
 //              (MFMA), two 9-bit radix rounds over those samples give tau,
 //              the lower edge of the 18-bit bin holding the m-th largest
-//              sample (m S ~ 2 top_k); tau becomes the smallest fp32
-//              accumulator whose scaled score reaches it. A row whose sample
-//              threshold is not positive keeps every non-negative
-//              accumulator instead ("zero mode").
-//   filter     per 64- or 128-row block: a producer wave streams the block's causal
-//              keys into an LDS ring of 64-key chunks with global->LDS copies
-//              (several chunks in flight); four
-//              consumer waves of 16 or 32 rows each score every chunk on MFMA.
-//              Keys are the MFMA row operand, so each lane holds 16
-//              consecutive keys of one query; a subtract and a funnel shift
-//              per score build the lane's accept mask, and the accepted
-//              (accumulator, index) pairs go to the row's list in ascending
-//              index order.
-//   select     one 256-thread workgroup per row with its list in registers:
-//              radix rounds of 12-bit digits over the order keys relative to
-//              the row's smallest (as many rounds as the key range needs)
-//              give the exact k-th key T; the T-ties are cut in list (=
-//              index) order. A zero-mode row with fewer than top_k positive
-//              scores takes its positives plus the lowest-index zero scores.
-//              A row whose threshold kept fewer than top_k keys, or more than
-//              its list holds, is queued.
+//              sample (m S ~ 2 top_k); tau becomes tau', the smallest fp32
+//              accumulator whose scaled score reaches it, rounded toward zero
+//              to 8 significant bits. A row whose sample threshold is not
+//              positive keeps every non-negative accumulator instead ("zero
+//              mode").
+//   filter     per 128-row block: a producer wave streams the block's causal
+//              keys into an LDS ring of key slots (128 keys for narrow fp8
+//              rows, else 64) with global->LDS copies, several slots in
+//              flight; consumer waves (eight of 16 rows, or four of 32) score
+//              every slot on MFMA, starting each accumulator at -tau', so a
+//              score's accept bit is its sign bit. Keys are the MFMA row
+//              operand, so each lane holds consecutive keys of one query and
+//              one funnel shift per score builds the lane's accept mask; the
+//              accepted (acc - tau', index) pairs go to the row's list in
+//              ascending index order. Problems with few rows cut the keys
+//              into up to four ranges, each with its own sub-list per row.
+//   select     one 512-thread workgroup per row with its list in registers:
+//              8-bit radix rounds over the order keys relative to the key of
+//              tau' give the exact k-th key T (wave 0 finishes once T's bin
+//              is small); the T-ties are cut in list (= index) order. A
+//              zero-mode row with fewer than top_k positive scores takes its
+//              positives plus the lowest-index zero scores. A row whose
+//              threshold kept fewer than top_k keys, or more than its list
+//              holds, is queued.
 //   fallback   a persistent kernel recomputes each queued row's scores into
 //              the workspace and selects on them with the per-row radix
 //              schedule.
@@ -893,8 +896,10 @@ __device__ __forceinline__ void select_row(const PrefillArgs& a, long long task,
         if (sh > 0 && hist[bin] <= (uint32_t)SL_GMAX) {
 #pragma unroll
             for (int e = 0; e < PER; ++e) {
-                if (e * NT >= cn) continue;
-                if ((dk[e] >> sh) == prefix) gk[atomicAdd(&res[4], 1u)] = dk[e];
+                if (e * NT >= cn) continue;  // workgroup-uniform
+                const bool take = (dk[e] >> sh) == prefix;
+                const uint32_t slot = wave_append(take, &res[4]);
+                if (take) gk[slot] = dk[e];
             }
             gathered = true;
         }

@@ -33,6 +33,20 @@ __device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t bin, bool acti
     if (active && !same) atomicAdd(&hist[bin], 1u);
 }
 
+// Slot of this lane's item in an LDS list whose length is *count, for the
+// lanes that pass `take`: one atomic per wave (lanes of a wave take
+// consecutive slots), so a long list does not serialise on the counter.
+// Called by every lane of the wave; the result is meaningful where take holds.
+__device__ __forceinline__ uint32_t wave_append(bool take, uint32_t* count) {
+    const unsigned long long m = __ballot(take);
+    if (m == 0ull) return 0u;
+    const int leader = __ffsll((long long)m) - 1;
+    uint32_t base = 0u;
+    if ((int)__lane_id() == leader) base = atomicAdd(count, (uint32_t)__popcll(m));
+    base = (uint32_t)__builtin_amdgcn_readlane((int)base, leader);
+    return base + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
 // Inclusive prefix sum across the 64 lanes of a wave: DPP row shifts within
 // each 16-lane row, then the row totals (read from lanes 15, 31, 47).
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
