@@ -131,6 +131,23 @@ int prefill_maxlen(const dsa_problem* p) {
     return (int)(m < p->n_k ? m : p->n_k);
 }
 
+// Many query rows per sequence over short key rows take the score-row path
+// (scores of every causal pair into the workspace, exact per-row radix
+// selection on them) when the whole score matrix fits one slab: with short
+// rows the sampled threshold, candidate filter and select cost more launches
+// and passes than writing and reading the scores. Tests move the limit
+// (dsa_internal_set_prefill_direct) to run either path at small sizes.
+constexpr int kPrefillDirectMaxKeys = 4096;  // faster at every size measured up to 4096 keys
+std::atomic<int> g_prefill_direct_max{kPrefillDirectMaxKeys};
+
+bool prefill_direct(const dsa_problem* p) {
+    return p->n_q > 1 && p->n_k <= g_prefill_direct_max.load() &&
+           (size_t)p->batch * p->n_q * p->n_k * sizeof(float) <= kScoreSlabBytes;
+}
+
+// The many-row path (sampled threshold, candidate filter, select).
+bool prefill_many_row(const dsa_problem* p) { return p->n_q > 1 && !prefill_direct(p); }
+
 // Key ranges per row of the many-row path, decided once for the problem.
 int prefill_nr(const dsa_problem* p) {
     return dsa::prefill_nranges(prefill_maxlen(p), (long long)p->batch * p->n_q);
@@ -165,7 +182,7 @@ ForwardLayout with_done(ForwardLayout L, const dsa_problem* p) {
 ForwardLayout forward_layout_core(const dsa_problem* p) {
     ForwardLayout L;
     L.scores = 0;
-    if (p->n_q > 1) {
+    if (prefill_many_row(p)) {
         // many rows: candidate lists and thresholds, no score rows
         const size_t ib = align_up((size_t)p->batch * p->n_q * p->top_k * sizeof(int32_t));
         L.idx = 0;
@@ -321,7 +338,8 @@ dsa_status forward_impl(const dsa_problem* p, const void* q_idx, const void* k_i
     ta.seq_pos = seq_pos;
     ta.ws = w + L.topk;
     int slabs = 0;
-    if (p->n_q > 1) {
+    const bool many_row = prefill_many_row(p);
+    if (many_row) {
         // Many query rows: threshold, indexer sweep keeping candidates,
         // per-row select and fallback, slab by slab.
         const int NS = prefill_slabs(p);
@@ -353,7 +371,7 @@ dsa_status forward_impl(const dsa_problem* p, const void* q_idx, const void* k_i
             }
         }
     }
-    for (int r0 = 0; p->n_q == 1 && r0 < p->n_q; r0 += R, ++slabs) {
+    for (int r0 = 0; !many_row && r0 < p->n_q; r0 += R, ++slabs) {
         const int r1 = r0 + R < p->n_q ? r0 + R : p->n_q;
         ia.q_begin = r0;
         ia.q_end = r1;
@@ -562,6 +580,15 @@ int32_t dsa_internal_set_prefill_slab_rows(int32_t rows) {
     return g_prefill_slab_rows.exchange(rows > 0 ? rows : 0);
 }
 
+// Not part of the public interface: the longest key rows (n_k) with which a
+// many-row problem takes the score-row path instead of the many-row path
+// (0 never; a negative value restores the default). Returns the previous
+// limit. The workspace size follows the limit in force when it is asked
+// for, so a caller must not change it between sizing and calling.
+int32_t dsa_internal_set_prefill_direct(int32_t max_keys) {
+    return g_prefill_direct_max.exchange(max_keys < 0 ? kPrefillDirectMaxKeys : max_keys);
+}
+
 // Not part of the public interface: selection statistics of the last
 // forward call on this problem and workspace (blocking: synchronises the
 // device, then copies counters back). out[0] rows longer than top_k (the
@@ -580,7 +607,7 @@ dsa_status dsa_internal_selection_stats(const dsa_problem* p, const void* ws, si
     if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
     const char* w = static_cast<const char*>(ws);
     long long o[4] = {0, -1, -1, -1};
-    if (p->n_q > 1) {
+    if (prefill_many_row(p)) {
         const int NS = prefill_slabs(p);
         dsa::PrefillArgs pa{};
         pa.B = p->batch;
@@ -603,7 +630,7 @@ dsa_status dsa_internal_selection_stats(const dsa_problem* p, const void* ws, si
             e = dsa::decode_stats(p->batch, p->n_k, p->q_pos0, seq_pos ? sp.data() : nullptr,
                                   p->top_k, w + L.topk, o);
     } else {
-        o[0] = p->batch;
+        o[0] = (long long)p->batch * p->n_q;
     }
     if (e != hipSuccess) return hip_fail(e, "selection statistics");
     for (int i = 0; i < 4; ++i) out[i] = o[i];

@@ -705,7 +705,9 @@ hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t s) {
         hipLaunchKernelGGL(attn_range_merge_kernel, dim3((unsigned)rows), dim3(256), 0, s, a);
         return hipGetLastError();
     }
-    if (rows >= 2048) {
+    if (rows >= 2048 || a.n_split == 1) {
+        // one wave per row; also for few rows of one split each, where a
+        // combine pass would only copy the split's partial
         if (rows > 0x7fffffffLL) return hipErrorInvalidConfiguration;
         hipLaunchKernelGGL(sparse_attn_kernel, dim3((unsigned)rows), dim3(64), 0, s, a);
         return hipGetLastError();

@@ -48,6 +48,27 @@ def to_dev(x):
     return {k: v.to("cuda") for k, v in x.items()}
 
 
+def set_prefill_direct(max_keys):
+    """Sets the longest key rows with which a many-row problem takes the
+    score-row path (an internal, non-ABI knob of the library; 0 never, a
+    negative value the default). Returns the previous limit."""
+    import ctypes
+    f = dsa.load().dsa_internal_set_prefill_direct
+    f.argtypes = [ctypes.c_int32]
+    f.restype = ctypes.c_int32
+    return f(max_keys)
+
+
+@pytest.fixture(autouse=True)
+def many_row_path():
+    """Every test here runs small prefill problems through the many-row path
+    (sampled threshold, candidate filter, select), which long contexts take;
+    test_prefill_score_row_path covers the path short ones take by default."""
+    prev = set_prefill_direct(0)
+    yield
+    set_prefill_direct(prev)
+
+
 SMALL = [
     synth.WORKLOADS["prefill_1k"],
     Workload("prefill_bf16_d160_ragged", "prefill", 1, 777, 777, 0, 160, "bf16", 100, 16),
@@ -451,6 +472,43 @@ def test_forward_threshold_vs_oracle(gpu_lib, w, mode):
     if mode in ("above_max", "nan"):
         assert torch.all(idx == -1) and torch.all(O.float() == 0)
         assert torch.all(torch.isneginf(lse))
+
+
+# Many query rows over short key rows: the score-row path (every causal
+# score into the workspace, exact per-row selection), the default up to 4096
+# keys.
+DIRECT = [
+    synth.WORKLOADS["prefill_1k"],
+    Workload("direct_bf16_d160", "prefill", 1, 777, 777, 0, 160, "bf16", 100, 16),
+    Workload("direct_chunked", "prefill", 2, 50, 300, 250, 64, "fp8", 37, 3),
+    Workload("direct_k4096_bf16_d256", "prefill", 2, 70, 70, 0, 256, "bf16", 4096, 4),
+    Workload("direct_d192_k1", "prefill", 1, 130, 130, 0, 192, "fp8", 1, 5),
+    Workload("direct_4k_fp8", "prefill", 1, 4096, 4096, 0, 128, "fp8", 1024, 16),
+    Workload("direct_b3_2k_fp8_d96", "prefill", 3, 2000, 2048, 48, 96, "fp8", 300, 4),
+]
+
+
+@pytest.mark.parametrize("tau_mode", [None, "q97", "at_kth"])
+@pytest.mark.parametrize("w", DIRECT, ids=lambda w: w.name)
+def test_prefill_score_row_path(gpu_lib, w, tau_mode):
+    say("score-row path %s %s" % (w.name, tau_mode))
+    set_prefill_direct(-1)
+    p = dsa.make_problem(w.batch, w.n_q, w.n_k, w.q_pos0, w.d_idx, w.idx_dtype, w.top_k,
+                         w.n_heads)
+    st = dsa.selection_stats(p, *(lambda f: (f.ws, f.ws_bytes))(dsa.Forward(p, "cuda")))
+    assert st[1] == -1, "problem does not take the score-row path: %s" % (st,)
+    seed = 0 if w.name == "prefill_1k" else 17
+    x = synth.make_inputs(w, seed=seed)
+    tau = None
+    if tau_mode is not None:
+        tau = pick_tau(oracle.index_scores(x["q_idx"], x["k_idx"], w.q_pos0), tau_mode, w)
+    idx_ref, O_ref, lse_ref = oracle.forward(x["q_idx"], x["k_idx"], x["Q"], x["K"], x["V"],
+                                             w.q_pos0, w.top_k, tau=tau)
+    d = to_dev(x)
+    idx, O, lse = dsa.forward(d["q_idx"], d["k_idx"], d["Q"], d["K"], d["V"], w.q_pos0,
+                              w.top_k, tau=tau)
+    assert np.array_equal(idx.cpu().numpy(), idx_ref), (w.name, tau_mode)
+    assert_attn_close(O, O_ref, lse, lse_ref, "%s %s" % (w.name, tau_mode))
 
 
 # Indexer projection: (rows, d_model, d_idx, out dtype, input range). "small"
