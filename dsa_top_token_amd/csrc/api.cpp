@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -281,6 +282,24 @@ struct StageTimer {
     }
 };
 
+// Host-side launch log: with DSA_LOG set to a non-empty value other than
+// "0", every forward call prints one line to stderr naming the problem, the
+// selection path it takes and the workspace it uses.
+bool log_on() {
+    const char* v = std::getenv("DSA_LOG");
+    return v && v[0] && !(v[0] == '0' && v[1] == 0);
+}
+
+void log_forward(const dsa_problem* p, const char* path, int slabs, size_t ws_bytes,
+                 const int32_t* seq_pos, const dsa::KeyPages* pages, const float* tau) {
+    std::fprintf(stderr,
+                 "dsa: forward B=%d n_q=%d n_k=%d q_pos0=%d d_idx=%d %s top_k=%d H=%d%s%s%s: %s, "
+                 "%d slab(s), workspace %zu bytes\n",
+                 p->batch, p->n_q, p->n_k, p->q_pos0, p->d_idx, p->idx_dtype ? "bf16" : "fp8",
+                 p->top_k, p->n_heads, seq_pos ? ", ragged" : "", pages ? ", paged" : "",
+                 tau ? ", threshold mode" : "", path, slabs, ws_bytes);
+}
+
 dsa_status forward_impl(const dsa_problem* p, const void* q_idx, const void* k_idx,
                         const void* Q, const void* K, const void* V, int32_t* idx_out, void* O,
                         float* lse, void* ws, size_t ws_bytes, void* stream, StageTimer* tm,
@@ -467,6 +486,20 @@ dsa_status forward_impl(const dsa_problem* p, const void* q_idx, const void* k_i
     if (e != hipSuccess) return hip_fail(e, "sparse_attn launch");
     if (tm) tm->mark(-1);
     if (n_slabs) *n_slabs = slabs;
+    if (log_on()) {
+        const char* path;
+        char buf[96];
+        if (many_row) {
+            std::snprintf(buf, sizeof buf, "many-row selection (%d key range(s), list cap %d)",
+                          prefill_nr(p), dsa::prefill_cap(p->top_k));
+            path = buf;
+        } else if (p->n_q == 1 && dsa::decode_select_applies(R, p->n_k, p->top_k)) {
+            path = "decode selection (sampled threshold, candidate filter, select)";
+        } else {
+            path = "score rows and per-row selection";
+        }
+        log_forward(p, path, slabs, L.total, seq_pos, pages, tau);
+    }
     return DSA_OK;
 }
 

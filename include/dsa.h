@@ -27,6 +27,10 @@
  *     DSA_E_HIP. Device faults surface at the caller's synchronisation.
  *   - No call blocks the host or synchronises the stream, except the
  *     profiling variants (dsa_forward_timed and the other *_timed calls).
+ *   - With the environment variable DSA_LOG set (to anything but "" or "0"),
+ *     every forward call prints one line to stderr: the problem, the
+ *     selection path it takes (many-row selection, score rows, or the decode
+ *     selection) and the workspace bytes it uses.
  */
 #ifndef DSA_H
 #define DSA_H

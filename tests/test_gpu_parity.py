@@ -242,6 +242,27 @@ def test_decode_threshold_misses_falls_back(gpu_lib):
     assert_attn_close(O, O_ref, lse, lse_ref, "sampled only")
 
 
+def test_forward_launch_log(gpu_lib, capfd, monkeypatch):
+    # DSA_LOG=1: every forward call names its problem, selection path and
+    # workspace on stderr; unset or "0" keeps the library silent.
+    runs = [(Workload("log_decode", "decode", 2, 1, 9000, 8999, 128, "fp8", 300, 4),
+             "decode selection"),
+            (Workload("log_prefill", "prefill", 1, 600, 600, 0, 64, "fp8", 50, 2),
+             "many-row selection")]
+    for w, path in runs:
+        d = to_dev(synth.make_inputs(w, seed=3))
+        for on in ("1", "0"):
+            monkeypatch.setenv("DSA_LOG", on)
+            dsa.forward(d["q_idx"], d["k_idx"], d["Q"], d["K"], d["V"], w.q_pos0, w.top_k)
+            torch.cuda.synchronize()
+            err = capfd.readouterr().err
+            if on == "1":
+                assert "dsa: forward B=%d n_q=%d n_k=%d" % (w.batch, w.n_q, w.n_k) in err, err
+                assert path in err, err
+            else:
+                assert "dsa: forward" not in err, err
+
+
 def test_prefill_threshold_misses_fall_back(gpu_lib):
     # Only the keys the prefill threshold pass samples (every S-th key,
     # S = 2 top_k / 64 = 20) score above zero. Rows longer than 1280 keys have
