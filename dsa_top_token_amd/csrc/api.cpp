@@ -622,6 +622,12 @@ int32_t dsa_internal_set_prefill_direct(int32_t max_keys) {
     return g_prefill_direct_max.exchange(max_keys < 0 ? kPrefillDirectMaxKeys : max_keys);
 }
 
+// Not part of the public interface: the shortest key rows (n_k) with which a
+// one-query-per-sequence problem takes the sampled-threshold decode
+// selection instead of score rows (0 restores the default). Returns the
+// previous value; workspace sizes follow the value in force when asked for.
+int32_t dsa_internal_set_decode_select_min(int32_t n_k) { return dsa::set_decode_select_min(n_k); }
+
 // Not part of the public interface: selection statistics of the last
 // forward call on this problem and workspace (blocking: synchronises the
 // device, then copies counters back). out[0] rows longer than top_k (the

@@ -242,6 +242,48 @@ def test_decode_threshold_misses_falls_back(gpu_lib):
     assert_attn_close(O, O_ref, lse, lse_ref, "sampled only")
 
 
+def set_decode_select_min(n_k):
+    """Sets the shortest key rows that take the sampled-threshold decode
+    selection (an internal, non-ABI knob of the library; 0 restores the
+    default). Returns the previous value."""
+    import ctypes
+    f = dsa.load().dsa_internal_set_decode_select_min
+    f.argtypes = [ctypes.c_int32]
+    f.restype = ctypes.c_int32
+    return f(n_k)
+
+
+# Decode batches long enough for the sampled-threshold selection, run through
+# the score-row path instead (scores, then the chunked top-k schedule whose
+# first histogram the indexer kernel builds), which shorter rows and top_k
+# beyond the select's list take.
+DECODE_SCORE_ROWS = [w for w in SMALL if w.mode == "decode" and w.n_k >= 8192]
+
+
+@pytest.mark.parametrize("w", DECODE_SCORE_ROWS, ids=lambda w: w.name)
+def test_forward_decode_score_rows(gpu_lib, w):
+    say("decode score rows %s" % w.name)
+    x = synth.make_inputs(w, seed=5)
+    idx_ref, O_ref, lse_ref = oracle.forward(x["q_idx"], x["k_idx"], x["Q"], x["K"], x["V"],
+                                             w.q_pos0, w.top_k)
+    d = to_dev(x)
+    prev = set_decode_select_min(1 << 30)
+    try:
+        p = dsa.make_problem(w.batch, w.n_q, w.n_k, w.q_pos0, w.d_idx, w.idx_dtype, w.top_k,
+                             w.n_heads)
+        fwd = dsa.Forward(p, "cuda")
+        idx = torch.empty(w.batch, 1, w.top_k, dtype=torch.int32, device="cuda")
+        O = torch.empty_like(d["Q"])
+        lse = torch.empty(w.batch, 1, w.n_heads, dtype=torch.float32, device="cuda")
+        fwd(d["q_idx"], d["k_idx"], d["Q"], d["K"], d["V"], O, idx, lse)
+        torch.cuda.synchronize()
+        assert dsa.selection_stats(p, fwd.ws, fwd.ws_bytes)[1] == -1  # not the select path
+    finally:
+        set_decode_select_min(prev)
+    assert np.array_equal(idx.cpu().numpy(), idx_ref)
+    assert_attn_close(O, O_ref, lse, lse_ref, "%s score rows" % w.name)
+
+
 def test_forward_launch_log(gpu_lib, capfd, monkeypatch):
     # DSA_LOG=1: every forward call names its problem, selection path and
     # workspace on stderr; unset or "0" keeps the library silent.
