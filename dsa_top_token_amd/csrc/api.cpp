@@ -132,6 +132,14 @@ int prefill_maxlen(const dsa_problem* p) {
     return (int)(m < p->n_k ? m : p->n_k);
 }
 
+// Shortest key rows that take the sampled-threshold decode selection beyond
+// the kernels' own limit (tests raise it to run long rows on score rows).
+std::atomic<int> g_select_min_keys{0};
+
+bool decode_select_on(int rows, int n_k, int top_k) {
+    return n_k >= g_select_min_keys.load() && dsa::decode_select_applies(rows, n_k, top_k);
+}
+
 // Many query rows per sequence over short key rows take the score-row path
 // (scores of every causal pair into the workspace, exact per-row radix
 // selection on them) when the whole score matrix fits one slab: with short
@@ -209,7 +217,7 @@ ForwardLayout forward_layout_core(const dsa_problem* p) {
     const size_t ib = align_up((size_t)p->batch * p->n_q * p->top_k * sizeof(int32_t));
     L.topk = L.idx + ib;
     size_t tb = align_up(dsa::topk_ws_bytes(p->batch, R, p->n_k));
-    if (dsa::decode_select_applies(R, p->n_k, p->top_k)) {
+    if (decode_select_on(R, p->n_k, p->top_k)) {
         const size_t db = align_up(dsa::decode_select_ws_bytes(p->batch, p->n_k));
         tb = db > tb ? db : tb;
     }
@@ -397,7 +405,7 @@ dsa_status forward_impl(const dsa_problem* p, const void* q_idx, const void* k_i
         ta.rows = r1 - r0;
         ta.pos_begin = (long long)p->q_pos0 + r0;
         ta.idx_row0 = r0;
-        if (dsa::decode_select_applies(ta.rows, p->n_k, p->top_k)) {
+        if (decode_select_on(ta.rows, p->n_k, p->top_k)) {
             // One query row per sequence: sampled threshold, indexer that
             // keeps only candidates, exact select; no score row is written.
             dsa::DecodeArgs da{};
@@ -493,7 +501,7 @@ dsa_status forward_impl(const dsa_problem* p, const void* q_idx, const void* k_i
             std::snprintf(buf, sizeof buf, "many-row selection (%d key range(s), list cap %d)",
                           prefill_nr(p), dsa::prefill_cap(p->top_k));
             path = buf;
-        } else if (p->n_q == 1 && dsa::decode_select_applies(R, p->n_k, p->top_k)) {
+        } else if (p->n_q == 1 && decode_select_on(R, p->n_k, p->top_k)) {
             path = "decode selection (sampled threshold, candidate filter, select)";
         } else {
             path = "score rows and per-row selection";
@@ -626,7 +634,9 @@ int32_t dsa_internal_set_prefill_direct(int32_t max_keys) {
 // one-query-per-sequence problem takes the sampled-threshold decode
 // selection instead of score rows (0 restores the default). Returns the
 // previous value; workspace sizes follow the value in force when asked for.
-int32_t dsa_internal_set_decode_select_min(int32_t n_k) { return dsa::set_decode_select_min(n_k); }
+int32_t dsa_internal_set_decode_select_min(int32_t n_k) {
+    return g_select_min_keys.exchange(n_k > 0 ? n_k : 0);
+}
 
 // Not part of the public interface: selection statistics of the last
 // forward call on this problem and workspace (blocking: synchronises the
@@ -659,7 +669,7 @@ dsa_status dsa_internal_selection_stats(const dsa_problem* p, const void* ws, si
         pa.rows = (p->n_q - (NS - 1) + NS - 1) / NS;
         pa.nr = prefill_nr(p);
         e = dsa::prefill_stats(pa, w + L.topk, o);
-    } else if (dsa::decode_select_applies(slab_rows(p), p->n_k, p->top_k)) {
+    } else if (decode_select_on(slab_rows(p), p->n_k, p->top_k)) {
         std::vector<int32_t> sp;
         if (seq_pos) {
             sp.resize(p->batch);

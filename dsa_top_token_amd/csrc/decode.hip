@@ -30,7 +30,6 @@
 // selection on them.
 #include "frag.h"
 
-#include <atomic>
 #include <vector>
 #include "topk_common.h"
 
@@ -828,14 +827,9 @@ hipError_t launch_dt(const DecodeArgs& a, int part, hipStream_t s) {
 
 }  // namespace
 
-// Shortest key rows that take the sampled-threshold selection (tests move it).
-static std::atomic<int> g_select_min_keys{8192};
-
-int set_decode_select_min(int n_k) { return g_select_min_keys.exchange(n_k > 0 ? n_k : 8192); }
-
 bool decode_select_applies(int rows, int n_k, int top_k) {
-    return rows == 1 && n_k >= g_select_min_keys.load() &&
-           (long long)n_k <= (long long)SEL_MAX_SLOTS * SLOT && top_k <= SEL_CAP;
+    return rows == 1 && n_k >= 8192 && (long long)n_k <= (long long)SEL_MAX_SLOTS * SLOT &&
+           top_k <= SEL_CAP;
 }
 
 size_t decode_select_ws_bytes(int B, int n_k) {

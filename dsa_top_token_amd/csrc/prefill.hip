@@ -13,10 +13,11 @@
 //              to 8 significant bits. A row whose sample threshold is not
 //              positive keeps every non-negative accumulator instead ("zero
 //              mode").
-//   filter     per 128-row block: a producer wave streams the block's causal
-//              keys into an LDS ring of key slots (128 keys for narrow fp8
-//              rows, else 64) with global->LDS copies, several slots in
-//              flight; consumer waves (eight of 16 rows, or four of 32) score
+//   filter     per 96- or 128-row block: a producer wave streams the
+//              block's causal keys into an LDS ring of key slots (128 keys
+//              for narrow fp8 rows, else 64) with global->LDS copies, several
+//              slots in flight; consumer waves (eight of 16 rows, or three or
+//              four of 32) score
 //              every slot on MFMA, starting each accumulator at -tau', so a
 //              score's accept bit is its sign bit. Keys are the MFMA row
 //              operand, so each lane holds consecutive keys of one query and
@@ -341,11 +342,16 @@ template <int DT, int D>
 constexpr int filter_qt() { return DT == 1 ? 2 : 1; }
 
 // Consumer waves per filter workgroup. Eight waves (two per SIMD) share
-// each key slot of the narrow fp8 rows, so two workgroups per CU keep four
-// consumer waves on every SIMD to hide one another's LDS and MFMA latency;
-// wider rows keep four.
+// each key slot of the narrow fp8 rows; wider rows keep four, and bf16 rows
+// wider than 128 values three: their waves need more than 128 VGPRs (three
+// waves per SIMD), and a workgroup of four waves (three consumers and the
+// producer, one per SIMD) lets two workgroups share a CU where five waves
+// (two on one SIMD) left room for one. bf16 d = 160 at 131072 rows: 5.0 ms
+// against 6.1 with four consumers.
 template <int DT, int D>
-constexpr int filter_nw() { return filter_g<DT, D>() == 2 ? 8 : 4; }
+constexpr int filter_nw() {
+    return filter_g<DT, D>() == 2 ? 8 : (DT == 1 && D > 128 ? 3 : 4);
+}
 
 // Ring depth of the key-slot pipeline (slots in flight ahead of the one
 // being consumed is NBUF - 1).
@@ -894,12 +900,15 @@ __device__ __forceinline__ void select_row(const PrefillArgs& a, long long task,
         first = false;
         // Few keys left in the bin: gather them for wave 0.
         if (sh > 0 && hist[bin] <= (uint32_t)SL_GMAX) {
+            // Independent per-key atomics: the entries' appends overlap in
+            // the LDS pipeline. Appends chained through one wave-wide
+            // reservation per entry (ballot, atomic, broadcast) timed 2.28
+            // against 1.63 ms at 131072 rows, and one reservation for all of
+            // a wave's entries 1.95.
 #pragma unroll
             for (int e = 0; e < PER; ++e) {
                 if (e * NT >= cn) continue;  // workgroup-uniform
-                const bool take = (dk[e] >> sh) == prefix;
-                const uint32_t slot = wave_append(take, &res[4]);
-                if (take) gk[slot] = dk[e];
+                if ((dk[e] >> sh) == prefix) gk[atomicAdd(&res[4], 1u)] = dk[e];
             }
             gathered = true;
         }
