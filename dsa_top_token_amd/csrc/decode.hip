@@ -4,13 +4,15 @@
 // DeepSeek-V3.2 DSA page (kwkr.cn/news/60693), sections 3.2-3.3: the indexer
 // scores every key of the query's prefix and the query keeps its top_k keys.
 // Here the full score row never reaches memory:
-//   threshold  one workgroup per sequence scores every S-th key
-//              (S = max(top_k / 32, ceil(n/8192))) with fp32 VALU dot
-//              products over coalesced row loads, and takes as tau the lower
-//              edge of the bin (two 8-bit radix rounds over the sample keys
-//              relative to the smallest) holding the m-th largest sample,
-//              m = ceil(2 * top_k / S). About 2 * top_k keys of the row are
-//              expected to reach tau.
+//   threshold  every S-th key of the row (S = max(top_k / 32, ceil(n/8192)))
+//              is scored with fp32 VALU dot products over coalesced row loads
+//              by several small workgroups per sequence (a sampled row is a
+//              scattered read, and one CU alone pulls them at a fraction of
+//              the chip's rate); then one workgroup per sequence takes as tau
+//              the lower edge of the bin (two 8-bit radix rounds over the
+//              sample keys relative to the smallest) holding the m-th largest
+//              sample, m = ceil(2 * top_k / S). About 2 * top_k keys of the
+//              row are expected to reach tau.
 //   filter     the streaming indexer kernel scores every key and keeps only
 //              those whose order key is >= tau, each wave writing its own
 //              (order key, index) list for its 256 keys in ascending index
@@ -30,6 +32,7 @@
 // selection on them.
 #include "frag.h"
 
+#include <algorithm>
 #include <vector>
 #include "topk_common.h"
 
@@ -142,18 +145,79 @@ __device__ __forceinline__ void granule_values(i32x4 w, float* v) {
     }
 }
 
-// Sampled threshold of each row: every S-th key's order key into LDS, then
-// two 8-bit radix rounds over the keys relative to the smallest sample give
-// the lower edge of the bin holding the m-th largest sample (at least m
-// samples reach it). tau only steers how many candidates the filter keeps;
+constexpr int SP_NT = 256;  // threads of a sampling workgroup
+constexpr int SP_NB = 8;    // sample load instructions in flight per lane
+
+// Samples scored by one sampling workgroup.
+template <int RB>
+constexpr int sample_chunk() { return (SP_NT / 64) * SP_NB * SampleShape<RB>::RPI; }
+
+// Sample scores of each row: sampling workgroup (b, part) scores samples
+// [part C, part C + C) of row b (C = sample_chunk) and writes their order
+// keys to a.samp[b][i]. tau only steers how many candidates the filter keeps;
 // the selection is exact for any tau, so the sample scores are fp32 VALU dot
 // products (summation order of their own) rather than the filter's MFMAs.
 template <int DT, int D>
-__global__ __launch_bounds__(TH_NT) void decode_threshold_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(SP_NT) void decode_sample_kernel(DecodeArgs a, int per_row) {
     constexpr int RB = D * (DT == 0 ? 1 : 2);
-    constexpr int WAVES = TH_NT / 64;
+    constexpr int WAVES = SP_NT / 64;
     constexpr int EPG = DT == 0 ? 16 : 8;  // values per granule
     using SS = SampleShape<RB>;
+    const int b = (int)(blockIdx.x / (unsigned)per_row);
+    const int i_lo = (int)(blockIdx.x % (unsigned)per_row) * sample_chunk<RB>();
+    const Plan p = plan_row(a, b);
+    if (p.n <= a.top_k || p.ns <= p.m || i_lo >= p.ns) return;  // (the threshold kernel's cases)
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int pl = lane % SS::LPR, rl = lane / SS::LPR;
+    const uint8_t* qrow = static_cast<const uint8_t*>(a.q) + ((size_t)b * a.n_q + a.q_row) * RB;
+    float qv[SS::GPL][EPG];
+#pragma unroll
+    for (int g = 0; g < SS::GPL; ++g) {
+        const int gi = pl + SS::LPR * g;
+        const i32x4 w = gi < SS::NG ? *reinterpret_cast<const i32x4*>(qrow + 16 * gi)
+                                    : i32x4{0, 0, 0, 0};
+        granule_values<DT>(w, qv[g]);
+    }
+    const uint8_t* kpool = static_cast<const uint8_t*>(a.k);
+    uint32_t* out = a.samp + (size_t)b * TH_MAX_SAMPLES;
+    // Sample i_lo + (u WAVES + wave) RPI + rl: SP_NB instructions per lane in
+    // flight, then their dot products.
+    i32x4 w[SP_NB][SS::GPL];
+#pragma unroll
+    for (int u = 0; u < SP_NB; ++u) {
+        const int i = min(i_lo + (u * WAVES + wave) * SS::RPI + rl, p.ns - 1);
+        const uint8_t* row = kpool + (size_t)key_row(a.pages, b, a.n_k, i * p.S) * RB;
+#pragma unroll
+        for (int g = 0; g < SS::GPL; ++g) {
+            const int gi = pl + SS::LPR * g;
+            w[u][g] = gi < SS::NG ? *reinterpret_cast<const i32x4*>(row + 16 * gi)
+                                  : i32x4{0, 0, 0, 0};
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < SP_NB; ++u) {
+        float s = 0.f;
+#pragma unroll
+        for (int g = 0; g < SS::GPL; ++g) {
+            float kv[EPG];
+            granule_values<DT>(w[u][g], kv);
+#pragma unroll
+            for (int e = 0; e < EPG; ++e) s = fmaf(kv[e], qv[g][e], s);
+        }
+#pragma unroll
+        for (int off = SS::LPR / 2; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+        const int i = i_lo + (u * WAVES + wave) * SS::RPI + rl;
+        if (pl == 0 && i < p.ns) out[i] = rank_key(relu_scaled(s, a.scale));
+    }
+}
+
+// Sampled threshold of each row (one workgroup per sequence): the row's
+// sample keys into LDS, then two 8-bit radix rounds over the keys relative to
+// the smallest sample give the lower edge of the bin holding the m-th largest
+// sample (at least m samples reach it).
+template <int DT, int D>
+__global__ __launch_bounds__(TH_NT) void decode_threshold_kernel(DecodeArgs a) {
+    constexpr int WAVES = TH_NT / 64;
     __shared__ uint32_t samp[TH_MAX_SAMPLES];
     __shared__ uint32_t hist[2][256];
     __shared__ uint32_t wlo[WAVES], whi[WAVES];
@@ -166,53 +230,13 @@ __global__ __launch_bounds__(TH_NT) void decode_threshold_kernel(DecodeArgs a) {
         if (tid == 0) a.tau[b] = 0u;  // every key is a candidate
         return;
     }
-    const int pl = lane % SS::LPR, rl = lane / SS::LPR;
-    const uint8_t* qrow = static_cast<const uint8_t*>(a.q) + ((size_t)b * a.n_q + a.q_row) * RB;
-    float qv[SS::GPL][EPG];
-#pragma unroll
-    for (int g = 0; g < SS::GPL; ++g) {
-        const int gi = pl + SS::LPR * g;
-        const i32x4 w = gi < SS::NG ? *reinterpret_cast<const i32x4*>(qrow + 16 * gi)
-                                    : i32x4{0, 0, 0, 0};
-        granule_values<DT>(w, qv[g]);
-    }
-    const uint8_t* kpool = static_cast<const uint8_t*>(a.k);
+    const uint32_t* in = a.samp + (size_t)b * TH_MAX_SAMPLES;
     uint32_t lo = 0xffffffffu, hi = 0u;
-    // Row r = wave * RPI + rl + (u + NB * t) * WAVES * RPI: NB instructions
-    // per lane in flight, then their dot products.
-    for (int i0 = wave * SS::RPI; i0 < p.ns; i0 += WAVES * SS::RPI * SS::NB) {
-        i32x4 w[SS::NB][SS::GPL];
-#pragma unroll
-        for (int u = 0; u < SS::NB; ++u) {
-            const int i = min(i0 + u * WAVES * SS::RPI + rl, p.ns - 1);
-            const uint8_t* row = kpool + (size_t)key_row(a.pages, b, a.n_k, i * p.S) * RB;
-#pragma unroll
-            for (int g = 0; g < SS::GPL; ++g) {
-                const int gi = pl + SS::LPR * g;
-                w[u][g] = gi < SS::NG ? *reinterpret_cast<const i32x4*>(row + 16 * gi)
-                                      : i32x4{0, 0, 0, 0};
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < SS::NB; ++u) {
-            float s = 0.f;
-#pragma unroll
-            for (int g = 0; g < SS::GPL; ++g) {
-                float kv[EPG];
-                granule_values<DT>(w[u][g], kv);
-#pragma unroll
-                for (int e = 0; e < EPG; ++e) s = fmaf(kv[e], qv[g][e], s);
-            }
-#pragma unroll
-            for (int off = SS::LPR / 2; off >= 1; off >>= 1) s += __shfl_xor(s, off);
-            const int i = i0 + u * WAVES * SS::RPI + rl;
-            if (pl == 0 && i < p.ns) {
-                const uint32_t key = rank_key(relu_scaled(s, a.scale));
-                samp[i] = key;
-                lo = min(lo, key);
-                hi = max(hi, key);
-            }
-        }
+    for (int i = tid; i < p.ns; i += TH_NT) {
+        const uint32_t key = in[i];
+        samp[i] = key;
+        lo = min(lo, key);
+        hi = max(hi, key);
     }
     lo = wave_min(lo);
     hi = wave_max(hi);
@@ -783,6 +807,18 @@ __global__ __launch_bounds__(SEL_NT) void decode_select_kernel(DecodeArgs a) {
 template <int DT, int D>
 hipError_t launch_d(const DecodeArgs& a, int part, hipStream_t s) {
     if (part == 0) {
+        // sampling workgroups per row: enough for the most samples any row
+        // of the problem can take (at most 8192, and at most ceil(n_k / S)
+        // with S >= max(1, top_k / 32))
+        const long long smin = a.top_k / 32 > 1 ? a.top_k / 32 : 1;
+        const long long ns_max = std::min<long long>(TH_MAX_SAMPLES, (a.n_k + smin - 1) / smin);
+        constexpr int CH = sample_chunk<D * (DT == 0 ? 1 : 2)>();
+        const int per_row = (int)((ns_max + CH - 1) / CH);
+        const long long nb = (long long)a.B * per_row;
+        if (nb > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+        if (nb > 0)
+            hipLaunchKernelGGL((decode_sample_kernel<DT, D>), dim3((unsigned)nb), dim3(SP_NT), 0, s,
+                               a, per_row);
         hipLaunchKernelGGL((decode_threshold_kernel<DT, D>), dim3(a.B), dim3(TH_NT), 0, s, a);
     } else if (part == 1) {
         const int KB = 4 * SLOT;
@@ -835,7 +871,8 @@ bool decode_select_applies(int rows, int n_k, int top_k) {
 size_t decode_select_ws_bytes(int B, int n_k) {
     const size_t n_slots = (n_k + SLOT - 1) / SLOT;
     auto al = [](size_t x) { return (x + 255) / 256 * 256; };
-    return al((size_t)B * 4) + al((size_t)B * n_slots * 4) + al((size_t)B * n_slots * SLOT * 8);
+    return al((size_t)B * 4) + al((size_t)B * n_slots * 4) + al((size_t)B * n_slots * SLOT * 8) +
+           al((size_t)B * TH_MAX_SAMPLES * 4);
 }
 
 hipError_t decode_stats(int B, int n_k, long long q_pos, const int32_t* seq_pos_host, int top_k,
@@ -875,6 +912,8 @@ hipError_t launch_decode_select(DecodeArgs a, void* ws, int part, hipStream_t s)
     a.cnt = reinterpret_cast<uint32_t*>(p);
     p += al((size_t)a.B * n_slots * 4);
     a.cand = reinterpret_cast<uint2*>(p);
+    p += al((size_t)a.B * n_slots * SLOT * 8);
+    a.samp = reinterpret_cast<uint32_t*>(p);
     return a.dtype == 0 ? launch_dt<0>(a, part, s) : launch_dt<1>(a, part, s);
 }
 

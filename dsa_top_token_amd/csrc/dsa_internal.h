@@ -139,6 +139,7 @@ struct DecodeArgs {
     uint32_t* tau;          // set by launch_decode_select from its workspace
     uint32_t* cnt;
     uint2* cand;
+    uint32_t* samp;         // [B][8192] sample order keys (set by launch_decode_select)
     ScoreFloor floor;       // threshold mode (optional)
 };
 
