@@ -5,7 +5,7 @@
 // indexer scores each query's causal prefix and the query keeps its top_k
 // keys; the page fuses indexing, selection and masking to avoid writing the
 // intermediates. Kernels, per slab of query rows:
-//   threshold  per 16-row block: scores every S-th key of each row's prefix
+//   threshold  per 16- or 32-row block: scores every S-th key of each row's prefix
 //              (MFMA), two 9-bit radix rounds over those samples give tau,
 //              the lower edge of the 18-bit bin holding the m-th largest
 //              sample (m S ~ 2 top_k); tau becomes tau', the smallest fp32
@@ -13,11 +13,11 @@
 //              to 8 significant bits. A row whose sample threshold is not
 //              positive keeps every non-negative accumulator instead ("zero
 //              mode").
-//   filter     per 96- or 128-row block: a producer wave streams the
+//   filter     per block of 64 to 352 rows: a producer wave streams the
 //              block's causal keys into an LDS ring of key slots (128 keys
 //              for narrow fp8 rows, else 64) with global->LDS copies, several
-//              slots in flight; consumer waves (eight of 16 rows, or three or
-//              four of 32) score
+//              slots in flight; consumer waves (eight of 16 rows for narrow
+//              fp8 rows, else four, eleven or three of 16 or 32) score
 //              every slot on MFMA, starting each accumulator at -tau', so a
 //              score's accept bit is its sign bit. Keys are the MFMA row
 //              operand, so each lane holds consecutive keys of one query and
@@ -49,13 +49,12 @@ namespace {
 using namespace frag;
 using namespace topk;
 
-constexpr int TH_ROWS = 16;       // rows per threshold workgroup
+constexpr int TH_ROWS_MAX = 32;   // rows per threshold workgroup (at most)
 constexpr int TH_DIG = 9;         // bits per digit of the two threshold rounds (the
-                                  // 16 x 512-bin histogram fits four workgroups per CU)
+                                  // 16 x 512-word histogram fits four workgroups per CU)
 constexpr int TH_BINS = 1 << TH_DIG;
 constexpr int TH_MAX_SAMPLES = 4096;
 constexpr int TH_TARGET = 64;     // samples expected above tau
-constexpr int TH_UN = 4;          // sampled-key tiles loaded together per pass
 constexpr int FL_CHUNK = 64;      // keys per staged chunk of the filter
 constexpr int FB_WGS = 256;       // fallback workgroups
 // Key ranges of the many-row filter: a row longer than kRangeMin keys is cut
@@ -98,21 +97,22 @@ __device__ __forceinline__ float snap_tau(float t) {
 // The bin of a wave-private histogram (nbins, bins owned top-down by lanes)
 // holding the rem-th largest counted key: returns bin, *above = count of
 // keys in higher bins. Every lane of the wave calls it.
+// The counts are the 16-bit fields at bit sh of the histogram words.
 template <int NBINS>
-__device__ __forceinline__ uint32_t wave_find_bin(const uint32_t* hist, uint32_t rem,
+__device__ __forceinline__ uint32_t wave_find_bin(const uint32_t* hist, int sh, uint32_t rem,
                                                   uint32_t* above_out) {
     constexpr int PER = NBINS / 64;
     const int lane = threadIdx.x & 63;
     const int hi = NBINS - 1 - lane * PER;
     uint32_t loc = 0;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) loc += hist[hi - i];
+    for (int i = 0; i < PER; ++i) loc += (hist[hi - i] >> sh) & 0xffffu;
     uint32_t above = wave_incl_scan(loc) - loc;
     uint32_t bin = 0, ab = 0;
     bool found = false;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-        const uint32_t c = hist[hi - i];
+        const uint32_t c = (hist[hi - i] >> sh) & 0xffffu;
         if (!found && above < rem && above + c >= rem) {
             found = true;
             bin = (uint32_t)(hi - i);
@@ -229,11 +229,44 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // ---------------------------------------------------------------- threshold
 
+// Histogram update of packed 16-bit counts: lanes adding to the same word
+// as the wave's first active lane add through it (inc is 1 << 0 or 1 << 16).
+__device__ __forceinline__ void hist_add16(uint32_t* hist, uint32_t word, uint32_t inc,
+                                           bool active) {
+    const unsigned long long act = __ballot(active);
+    if (act == 0ull) return;
+    const int leader = __ffsll((long long)act) - 1;
+    const uint32_t lw = __builtin_amdgcn_readlane(word, leader);
+    const uint32_t li = __builtin_amdgcn_readlane(inc, leader);
+    const bool same = active && word == lw && inc == li;
+    const unsigned long long same_mask = __ballot(same);
+    if ((int)__lane_id() == leader) atomicAdd(&hist[lw], li * (uint32_t)__popcll(same_mask));
+    if (active && !same) atomicAdd(&hist[word], inc);
+}
+
+// Query tiles of 16 rows per threshold workgroup, and sampled-key tiles
+// loaded together per pass. Every sampled key row is loaded once per
+// workgroup and scored against all its query tiles; the sampled rows are the
+// same for every workgroup of a slab, so these loads are L2 reads whose volume
+// the rows per workgroup set. bf16 d = 160 at 131072 rows: two tiles of
+// 16 rows with two key tiles per pass took the threshold and select from
+// 2.36 to 2.18 ms (one tile with four key tiles: 2.36; two with four, more
+// registers: 2.42); fp8 d = 128 at 65536 rows gained nothing from two tiles.
+template <int DT>
+constexpr int th_qt() { return DT == 1 ? 2 : 1; }
+template <int DT>
+constexpr int th_un() { return DT == 1 ? 2 : 4; }
+
+// Each workgroup covers 16 th_qt rows with one sample stride S. Row 16 t + j
+// counts in the 16-bit field 16 t of word [j][bin] (at most 4096 samples per
+// row).
 template <int DT, int D>
 __global__ __launch_bounds__(256) void prefill_threshold_kernel(PrefillArgs a) {
-    __shared__ uint32_t hist[TH_ROWS][TH_BINS];
+    constexpr int TH_QT = th_qt<DT>(), TH_UN = th_un<DT>(), TH_ROWS = 16 * TH_QT;
+    __shared__ uint32_t hist[16][TH_BINS];
     __shared__ uint32_t digit1[TH_ROWS];
     __shared__ uint32_t rem1[TH_ROWS];
+    static_assert(TH_ROWS <= TH_ROWS_MAX && TH_MAX_SAMPLES < 65536, "at most two 16-bit counts per word");
     constexpr int RB = D * (DT == 0 ? 1 : 2);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n = lane & 15, g = lane >> 4;
@@ -247,21 +280,25 @@ __global__ __launch_bounds__(256) void prefill_threshold_kernel(PrefillArgs a) {
     const uint32_t m = (uint32_t)((2 * a.top_k + S - 1) / S);
     const int ns_max = (nmax + S - 1) / S;
 
-    Frag<DT, D> fq;  // A operand: the block's 16 query rows
-    fq.load(static_cast<const uint8_t*>(a.q) +
-                ((size_t)b * a.n_q + qrow(a, min(r0 + n, a.rows - 1))) * RB, g);
-    const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + (size_t)b * a.n_k * RB;
-    // Sample count of the rows this lane's scores belong to (rows 4g + r).
-    int ns_r[4];
+    Frag<DT, D> fq[TH_QT];  // A operands: query tile t holds rows r0 + 16 t + n
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int row = r0 + 4 * g + r;
-        ns_r[r] = row < a.rows ? (row_len(a, row) + S - 1) / S : 0;
-    }
+    for (int t = 0; t < TH_QT; ++t)
+        fq[t].load(static_cast<const uint8_t*>(a.q) +
+                       ((size_t)b * a.n_q + qrow(a, min(r0 + 16 * t + n, a.rows - 1))) * RB, g);
+    const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + (size_t)b * a.n_k * RB;
+    // Sample count of the rows this lane's scores belong to (rows 16 t + 4g + r).
+    int ns_r[TH_QT][4];
+#pragma unroll
+    for (int t = 0; t < TH_QT; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = r0 + 16 * t + 4 * g + r;
+            ns_r[t][r] = row < a.rows ? (row_len(a, row) + S - 1) / S : 0;
+        }
 
 #pragma unroll 1
     for (int round = 0; round < 2; ++round) {
-        for (int i = threadIdx.x; i < TH_ROWS * TH_BINS; i += 256) (&hist[0][0])[i] = 0u;
+        for (int i = threadIdx.x; i < 16 * TH_BINS; i += 256) (&hist[0][0])[i] = 0u;
         __syncthreads();
         // TH_UN tiles per pass: their sampled key rows are loaded together
         // (one memory latency per pass, not per tile).
@@ -273,26 +310,29 @@ __global__ __launch_bounds__(256) void prefill_threshold_kernel(PrefillArgs a) {
 #pragma unroll
             for (int u = 0; u < TH_UN; ++u) {
                 const int t0 = t00 + 64 * u;
-                const f32x4 acc = tile_dot_k32<D>(fq, fk[u]);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = 4 * g + r;
-                    const uint32_t key = rank_key(relu_scaled(acc[r], a.scale));
-                    const bool ok = t0 + n < ns_r[r];
-                    const bool in = round == 0 ? ok : ok && (key >> (32 - TH_DIG)) == digit1[row];
-                    const uint32_t bin = round == 0 ? (key >> (32 - TH_DIG))
-                                                    : ((key >> (32 - 2 * TH_DIG)) & (TH_BINS - 1u));
-                    hist_add(&hist[0][0], (uint32_t)row * TH_BINS + bin, in);
+                for (int t = 0; t < TH_QT; ++t) {
+                    const f32x4 acc = tile_dot_k32<D>(fq[t], fk[u]);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int j = 4 * g + r, row = 16 * t + j;
+                        const uint32_t key = rank_key(relu_scaled(acc[r], a.scale));
+                        const bool ok = t0 + n < ns_r[t][r];
+                        const bool in = round == 0 ? ok : ok && (key >> (32 - TH_DIG)) == digit1[row];
+                        const uint32_t bin = round == 0 ? (key >> (32 - TH_DIG))
+                                                        : ((key >> (32 - 2 * TH_DIG)) & (TH_BINS - 1u));
+                        hist_add16(&hist[0][0], (uint32_t)j * TH_BINS + bin, 1u << (16 * t), in);
+                    }
                 }
             }
         }
         __syncthreads();
-        // Each wave resolves 4 rows.
-        for (int rr = 0; rr < 4; ++rr) {
-            const int row = wave * 4 + rr;
+        // Each wave resolves TH_ROWS / 4 rows.
+        for (int rr = 0; rr < TH_ROWS / 4; ++rr) {
+            const int row = wave * (TH_ROWS / 4) + rr;
             uint32_t above;
             const uint32_t want = round == 0 ? m : rem1[row];
-            const uint32_t bin = wave_find_bin<TH_BINS>(hist[row], want, &above);
+            const uint32_t bin = wave_find_bin<TH_BINS>(hist[row & 15], 16 * (row >> 4), want, &above);
             if (lane == 0) {
                 if (round == 0) {
                     digit1[row] = bin;
@@ -341,16 +381,19 @@ constexpr int filter_g() { return DT == 0 && D <= 128 ? 2 : 1; }
 template <int DT, int D>
 constexpr int filter_qt() { return DT == 1 ? 2 : 1; }
 
-// Consumer waves per filter workgroup. Eight waves (two per SIMD) share
-// each key slot of the narrow fp8 rows; wider rows keep four, and bf16 rows
-// wider than 128 values three: their waves need more than 128 VGPRs (three
-// waves per SIMD), and a workgroup of four waves (three consumers and the
-// producer, one per SIMD) lets two workgroups share a CU where five waves
-// (two on one SIMD) left room for one. bf16 d = 160 at 131072 rows: 5.0 ms
-// against 6.1 with four consumers.
+// Consumer waves per filter workgroup. Every workgroup streams its rows'
+// causal keys through the ring once, so the rows per workgroup set how often
+// each key row is read: 96-row workgroups re-read the 320-byte keys of a
+// 131072-row bf16 d = 160 prefill 28.6 GB worth, and the address and data
+// units were the filter's busiest. Eleven consumer waves and the producer
+// (three waves per SIMD, their registers fit in 170) cover 352 rows, one
+// workgroup per CU: 5.0 -> 4.2 ms. Eight waves (two per SIMD) share each key
+// slot of the narrow fp8 rows (eleven: 0.99 against 1.02 ms at 65536 rows,
+// fifteen 1.22); other fp8 widths keep four, and wider bf16 rows three
+// (their waves need more than 170 registers).
 template <int DT, int D>
 constexpr int filter_nw() {
-    return filter_g<DT, D>() == 2 ? 8 : (DT == 1 && D > 128 ? 3 : 4);
+    return filter_g<DT, D>() == 2 ? 8 : (DT == 1 && D > 128 ? (D <= 160 ? 11 : 3) : 4);
 }
 
 // Ring depth of the key-slot pipeline (slots in flight ahead of the one
@@ -1035,6 +1078,7 @@ template <int DT, int D>
 hipError_t launch_d(const PrefillArgs& a, int part, hipStream_t s) {
     const long long rows = (long long)a.B * a.rows;
     if (part == 0) {
+        constexpr int TH_ROWS = 16 * th_qt<DT>();
         const long long nb = (long long)a.B * ((a.rows + TH_ROWS - 1) / TH_ROWS);
         if (nb > 0x7fffffffLL) return hipErrorInvalidConfiguration;
         hipLaunchKernelGGL((prefill_threshold_kernel<DT, D>), dim3((unsigned)nb), dim3(256), 0, s,
