@@ -218,7 +218,7 @@ ForwardLayout forward_layout_core(const dsa_problem* p) {
     L.topk = L.idx + ib;
     size_t tb = align_up(dsa::topk_ws_bytes(p->batch, R, p->n_k));
     if (decode_select_on(R, p->n_k, p->top_k)) {
-        const size_t db = align_up(dsa::decode_select_ws_bytes(p->batch, p->n_k));
+        const size_t db = align_up(dsa::decode_select_ws_bytes(p->batch, p->n_k, p->top_k));
         tb = db > tb ? db : tb;
     }
     L.part = L.topk + tb;

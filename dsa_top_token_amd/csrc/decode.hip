@@ -52,6 +52,15 @@ struct Plan {
     int n, S, ns, m;
 };
 
+// Most samples any row of a problem with n_k keys can take: ns = ceil(n / S)
+// with S >= max(1, top_k / 32) and S >= ceil(n / TH_MAX_SAMPLES). The sample
+// keys of sequence b sit at a.samp[b * sample_cap(n_k, top_k) + i].
+__host__ __device__ inline int sample_cap(int n_k, int top_k) {
+    const long long smin = top_k / 32 > 1 ? top_k / 32 : 1;
+    const long long c = ((long long)n_k + smin - 1) / smin;
+    return (int)(c < TH_MAX_SAMPLES ? c : TH_MAX_SAMPLES);
+}
+
 __device__ __forceinline__ Plan plan_row(const DecodeArgs& a, int b) {
     Plan p;
     const long long pos = (long long)a.q_pos0 + a.q_row + (a.seq_pos ? a.seq_pos[b] : 0);
@@ -179,7 +188,7 @@ __global__ __launch_bounds__(SP_NT) void decode_sample_kernel(DecodeArgs a, int 
         granule_values<DT>(w, qv[g]);
     }
     const uint8_t* kpool = static_cast<const uint8_t*>(a.k);
-    uint32_t* out = a.samp + (size_t)b * TH_MAX_SAMPLES;
+    uint32_t* out = a.samp + (size_t)b * sample_cap(a.n_k, a.top_k);
     // Sample i_lo + (u WAVES + wave) RPI + rl: SP_NB instructions per lane in
     // flight, then their dot products.
     i32x4 w[SP_NB][SS::GPL];
@@ -230,7 +239,7 @@ __global__ __launch_bounds__(TH_NT) void decode_threshold_kernel(DecodeArgs a) {
         if (tid == 0) a.tau[b] = 0u;  // every key is a candidate
         return;
     }
-    const uint32_t* in = a.samp + (size_t)b * TH_MAX_SAMPLES;
+    const uint32_t* in = a.samp + (size_t)b * sample_cap(a.n_k, a.top_k);
     uint32_t lo = 0xffffffffu, hi = 0u;
     for (int i = tid; i < p.ns; i += TH_NT) {
         const uint32_t key = in[i];
@@ -808,10 +817,8 @@ template <int DT, int D>
 hipError_t launch_d(const DecodeArgs& a, int part, hipStream_t s) {
     if (part == 0) {
         // sampling workgroups per row: enough for the most samples any row
-        // of the problem can take (at most 8192, and at most ceil(n_k / S)
-        // with S >= max(1, top_k / 32))
-        const long long smin = a.top_k / 32 > 1 ? a.top_k / 32 : 1;
-        const long long ns_max = std::min<long long>(TH_MAX_SAMPLES, (a.n_k + smin - 1) / smin);
+        // of the problem can take
+        const long long ns_max = sample_cap(a.n_k, a.top_k);
         constexpr int CH = sample_chunk<D * (DT == 0 ? 1 : 2)>();
         const int per_row = (int)((ns_max + CH - 1) / CH);
         const long long nb = (long long)a.B * per_row;
@@ -868,11 +875,11 @@ bool decode_select_applies(int rows, int n_k, int top_k) {
            top_k <= SEL_CAP;
 }
 
-size_t decode_select_ws_bytes(int B, int n_k) {
+size_t decode_select_ws_bytes(int B, int n_k, int top_k) {
     const size_t n_slots = (n_k + SLOT - 1) / SLOT;
     auto al = [](size_t x) { return (x + 255) / 256 * 256; };
     return al((size_t)B * 4) + al((size_t)B * n_slots * 4) + al((size_t)B * n_slots * SLOT * 8) +
-           al((size_t)B * TH_MAX_SAMPLES * 4);
+           al((size_t)B * sample_cap(n_k, top_k) * 4);
 }
 
 hipError_t decode_stats(int B, int n_k, long long q_pos, const int32_t* seq_pos_host, int top_k,

@@ -196,7 +196,7 @@ hipError_t launch_prefill_select(PrefillArgs a, void* ws, int part, hipStream_t 
 hipError_t prefill_stats(const PrefillArgs& a, const void* ws, long long out[4]);
 
 bool decode_select_applies(int rows, int n_k, int top_k);
-size_t decode_select_ws_bytes(int B, int n_k);
+size_t decode_select_ws_bytes(int B, int n_k, int top_k);
 // part 0: sampled threshold, 1: indexer + filter, 2: exact select.
 hipError_t launch_decode_select(DecodeArgs a, void* ws, int part, hipStream_t s);
 // The same for the decode select (seq_pos_host: per-sequence positions or
