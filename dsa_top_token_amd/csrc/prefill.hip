@@ -16,7 +16,7 @@
 //   filter     per block of 64 to 352 rows: a producer wave streams the
 //              block's causal keys into an LDS ring of key slots (128 keys
 //              for narrow fp8 rows, else 64) with global->LDS copies, several
-//              slots in flight; consumer waves (eight of 16 rows for narrow
+//              slots in flight; consumer waves (eleven of 16 rows for narrow
 //              fp8 rows, else four, eleven or three of 16 or 32) score
 //              every slot on MFMA, starting each accumulator at -tau', so a
 //              score's accept bit is its sign bit. Keys are the MFMA row
@@ -387,13 +387,13 @@ constexpr int filter_qt() { return DT == 1 ? 2 : 1; }
 // 131072-row bf16 d = 160 prefill 28.6 GB worth, and the address and data
 // units were the filter's busiest. Eleven consumer waves and the producer
 // (three waves per SIMD, their registers fit in 170) cover 352 rows, one
-// workgroup per CU: 5.0 -> 4.2 ms. Eight waves (two per SIMD) share each key
-// slot of the narrow fp8 rows (eleven: 0.99 against 1.02 ms at 65536 rows,
-// fifteen 1.22); other fp8 widths keep four, and wider bf16 rows three
-// (their waves need more than 170 registers).
+// workgroup per CU: 5.0 -> 4.2 ms. The narrow fp8 rows (128-key slots) also
+// take eleven consumer waves of 16 rows: 0.99 against 1.02 ms with eight at
+// 65536 rows (fifteen, four per SIMD: 1.22). Other fp8 widths keep four, and
+// wider bf16 rows three (their waves need more than 170 registers).
 template <int DT, int D>
 constexpr int filter_nw() {
-    return filter_g<DT, D>() == 2 ? 8 : (DT == 1 && D > 128 ? (D <= 160 ? 11 : 3) : 4);
+    return filter_g<DT, D>() == 2 ? 11 : (DT == 1 && D > 128 ? (D <= 160 ? 11 : 3) : 4);
 }
 
 // Ring depth of the key-slot pipeline (slots in flight ahead of the one
