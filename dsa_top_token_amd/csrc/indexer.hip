@@ -283,8 +283,23 @@ hipError_t launch_dt_d(const IndexArgs& a, hipStream_t s) {
         constexpr int QB = 64, KB = 256;
         const long long nb = (long long)a.B * ((rows + QB - 1) / QB) * ((a.n_k + KB - 1) / KB);
         if (nb > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL((index_scores_kernel<DT, D, 4, 1, 4, false>), dim3((unsigned)nb),
-                           dim3(256), 0, s, a);
+        // Few blocks (1024 x 1024 scores: 64 of 256 CUs): one 64-key step per
+        // wave, four times the workgroups. Not for fp8 rows wider than 128
+        // values: their tiles chain a scaled 16x16x128 MFMA with further
+        // MFMAs, and without the loop the register holding the scale
+        // exponent is free after the last tile, so it was reused for an
+        // accumulator read while the last scaled MFMA still sat behind the
+        // previous tile's chain (d = 192 returned wrong scores). In the loop
+        // the scale register stays live across iterations.
+        constexpr bool one_step_ok = DT == 1 || D <= 128;
+        if (one_step_ok && nb < 1024) {
+            const long long nb1 = (long long)a.B * ((rows + QB - 1) / QB) * ((a.n_k + 63) / 64);
+            hipLaunchKernelGGL((index_scores_kernel<DT, D, 4, 1, (one_step_ok ? 1 : 4), false>),
+                               dim3((unsigned)nb1), dim3(256), 0, s, a);
+        } else {
+            hipLaunchKernelGGL((index_scores_kernel<DT, D, 4, 1, 4, false>), dim3((unsigned)nb),
+                               dim3(256), 0, s, a);
+        }
     }
     return hipGetLastError();
 }

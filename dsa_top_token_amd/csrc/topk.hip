@@ -63,6 +63,120 @@ __global__ __launch_bounds__(ROW_NT) void topk_row_kernel(TopkArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Short rows (at most WV_MAXN keys): one wave per row with the row's order
+// keys in registers, lane l holding keys [WV_E l, WV_E l + WV_E). Up to four
+// 8-bit radix rounds over a wave-private 256-bin LDS histogram find the k-th
+// key; a round whose chosen bin is taken whole ends the search early (every
+// key of that bin is then kept). One wave scan of the per-lane counts gives
+// each kept key its place in ascending index order.
+constexpr int WV_E = 16;               // keys per lane
+constexpr int WV_MAXN = 64 * WV_E;     // keys per row at most
+constexpr int WV_ROWS = 4;             // rows (waves) per workgroup
+
+// Orders one wave's LDS accesses across its lanes.
+__device__ __forceinline__ void wave_sync_lds() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(64 * WV_ROWS) void topk_wave_kernel(TopkArgs a) {
+    __shared__ uint32_t hist_all[WV_ROWS][256];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const long long rid = (long long)blockIdx.x * WV_ROWS + w;
+    if (rid >= (long long)a.B * a.rows) return;  // whole wave; no workgroup barrier follows
+    const int b = (int)(rid / a.rows), r = (int)(rid % a.rows);
+    const long long pos = a.pos_begin + r + (a.seq_pos ? a.seq_pos[b] : 0);
+    const int n = (int)max(0LL, min((long long)a.n_k, pos + 1));
+    const float* row = a.scores + (size_t)rid * a.n_k;
+    int32_t* out = a.idx + ((size_t)b * a.idx_rows + a.idx_row0 + r) * a.k;
+    if (n <= a.k) {
+        fill_prefix(out, n, a.k, lane, 64);
+        return;
+    }
+    uint32_t* hist = hist_all[w];
+    const int j0 = WV_E * lane;
+    uint32_t key[WV_E];
+    bool ok[WV_E];
+#pragma unroll
+    for (int q = 0; q < WV_E; q += 4) load4<VEC>(row, j0 + q, n, key + q, ok + q);
+    // pre: the k-th key's bits found so far; rem: its rank among the keys
+    // sharing them; sh: the lowest bit position those bits reach (24, 16, 8
+    // or 0 once the first round is done).
+    uint32_t pre = 0u, rem = (uint32_t)a.k;
+    int sh = 24;
+#pragma unroll 1
+    for (int d = 3; d >= 0; --d) {
+        const int s8 = 8 * d;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) hist[4 * lane + q] = 0u;
+        wave_sync_lds();
+#pragma unroll
+        for (int i = 0; i < WV_E; ++i) {
+            const bool in = ok[i] && (d == 3 || (key[i] >> (s8 + 8)) == (pre >> (s8 + 8)));
+            hist_add(hist, (key[i] >> s8) & 255u, in);
+        }
+        wave_sync_lds();
+        // bin holding the rem-th largest counted key (lanes own bins top-down)
+        const int hi = 255 - 4 * lane;
+        uint32_t c[4], loc = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            c[q] = hist[hi - q];
+            loc += c[q];
+        }
+        uint32_t above = wave_incl_scan(loc) - loc;
+        int fb = -1;
+        uint32_t fa = 0, fc = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (above < rem && above + c[q] >= rem) {
+                fb = hi - q;
+                fa = above;
+                fc = c[q];
+            }
+            above += c[q];
+        }
+        const unsigned long long mk = __ballot(fb >= 0);
+        const int src = __ffsll((long long)mk) - 1;  // exactly one lane holds the bin
+        const uint32_t bin = (uint32_t)__builtin_amdgcn_readlane(fb, src);
+        const uint32_t ab = (uint32_t)__builtin_amdgcn_readlane((int)fa, src);
+        const uint32_t cb = (uint32_t)__builtin_amdgcn_readlane((int)fc, src);
+        pre |= bin << s8;
+        rem -= ab;
+        sh = s8;
+        if (rem == cb) break;  // the whole bin is kept
+        wave_sync_lds();       // the next round clears the histogram
+    }
+    // Kept: keys whose bits from sh up exceed pre's, and the first rem keys
+    // (in index order) equal to them there.
+    const uint32_t th = pre >> sh;
+    uint32_t gt = 0, eq = 0;
+#pragma unroll
+    for (int i = 0; i < WV_E; ++i) {
+        const uint32_t kh = key[i] >> sh;
+        gt += ok[i] && kh > th ? 1u : 0u;
+        eq += ok[i] && kh == th ? 1u : 0u;
+    }
+    const uint32_t pk = (gt << 16) | eq;
+    const uint32_t ex = wave_incl_scan(pk) - pk;
+    uint32_t gb = ex >> 16, eb = ex & 0xffffu;
+#pragma unroll
+    for (int i = 0; i < WV_E; ++i) {
+        if (!ok[i]) continue;
+        const uint32_t kh = key[i] >> sh;
+        if (kh > th) {
+            out[gb + min(eb, rem)] = j0 + i;
+            ++gb;
+        } else if (kh == th) {
+            if (eb < rem) out[gb + eb] = j0 + i;
+            ++eb;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Chunked schedule.
 
 struct MultiWs {
@@ -436,6 +550,16 @@ hipError_t launch_topk(const TopkArgs& t, hipStream_t s) {
     if (rows > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     const bool vec = (t.n_k % 4 == 0) && ((reinterpret_cast<uintptr_t>(t.scores) & 15) == 0);
     if (!topk_use_chunked(t.B, t.rows, t.n_k)) {
+        if (t.n_k <= WV_MAXN) {
+            const long long nb = (rows + WV_ROWS - 1) / WV_ROWS;
+            if (vec)
+                hipLaunchKernelGGL(topk_wave_kernel<true>, dim3((unsigned)nb), dim3(64 * WV_ROWS), 0,
+                                   s, t);
+            else
+                hipLaunchKernelGGL(topk_wave_kernel<false>, dim3((unsigned)nb), dim3(64 * WV_ROWS), 0,
+                                   s, t);
+            return hipGetLastError();
+        }
         if (vec)
             hipLaunchKernelGGL(topk_row_kernel<true>, dim3((unsigned)rows), dim3(ROW_NT), 0, s, t);
         else

@@ -119,7 +119,7 @@ def test_topk_bit_exact_on_oracle_scores(gpu_lib, w):
     assert np.array_equal(got, ref)
 
 
-@pytest.mark.parametrize("n_k", [1000, 4097, 9999, 20000])
+@pytest.mark.parametrize("n_k", [1000, 1024, 1025, 4097, 9999, 20000])
 @pytest.mark.parametrize("levels", [1, 3, 40, 0])
 @pytest.mark.parametrize("k", [1, 7, 600])
 def test_topk_ties_and_ragged_rows(gpu_lib, n_k, levels, k):
