@@ -67,7 +67,9 @@ __global__ __launch_bounds__(ROW_NT) void topk_row_kernel(TopkArgs a) {
 // keys in registers, lane l holding keys [WV_E l, WV_E l + WV_E). Up to four
 // 8-bit radix rounds over a wave-private 256-bin LDS histogram find the k-th
 // key; a round whose chosen bin is taken whole ends the search early (every
-// key of that bin is then kept). One wave scan of the per-lane counts gives
+// key of that bin is then kept), and once the chosen bin holds at most 64
+// keys they are gathered, one per lane, and the k-th key is found among
+// them by comparing every pair. One wave scan of the per-lane counts gives
 // each kept key its place in ascending index order.
 constexpr int WV_E = 16;               // keys per lane
 constexpr int WV_MAXN = 64 * WV_E;     // keys per row at most
@@ -83,6 +85,8 @@ __device__ __forceinline__ void wave_sync_lds() {
 template <bool VEC>
 __global__ __launch_bounds__(64 * WV_ROWS) void topk_wave_kernel(TopkArgs a) {
     __shared__ uint32_t hist_all[WV_ROWS][256];
+    __shared__ uint32_t gath_all[WV_ROWS][64];
+    __shared__ uint32_t gcnt_all[WV_ROWS];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const long long rid = (long long)blockIdx.x * WV_ROWS + w;
     if (rid >= (long long)a.B * a.rows) return;  // whole wave; no workgroup barrier follows
@@ -147,6 +151,34 @@ __global__ __launch_bounds__(64 * WV_ROWS) void topk_wave_kernel(TopkArgs a) {
         rem -= ab;
         sh = s8;
         if (rem == cb) break;  // the whole bin is kept
+        if (cb <= 64u && s8 > 0) {
+            // Gather the bin's keys (any order), one per lane, then the
+            // rem-th largest of them: the key with fewer than rem keys above
+            // it and at least rem at or above it.
+            uint32_t* gath = gath_all[w];
+            if (lane == 0) gcnt_all[w] = 0u;
+            wave_sync_lds();
+#pragma unroll
+            for (int i = 0; i < WV_E; ++i) {
+                const bool in = ok[i] && (key[i] >> s8) == (pre >> s8);
+                const uint32_t slot = wave_append(in, &gcnt_all[w]);
+                if (in) gath[slot] = key[i];
+            }
+            wave_sync_lds();
+            const uint32_t mine = lane < (int)cb ? gath[lane] : 0u;
+            uint32_t ngt = 0, nge = 0;
+            for (uint32_t x = 0; x < cb; ++x) {
+                const uint32_t o = gath[x];
+                ngt += o > mine ? 1u : 0u;
+                nge += o >= mine ? 1u : 0u;
+            }
+            const unsigned long long hit = __ballot(lane < (int)cb && ngt < rem && rem <= nge);
+            const int hl = __ffsll((long long)hit) - 1;  // lanes holding the k-th key agree
+            pre = (uint32_t)__builtin_amdgcn_readlane((int)mine, hl);
+            rem -= (uint32_t)__builtin_amdgcn_readlane((int)ngt, hl);
+            sh = 0;
+            break;
+        }
         wave_sync_lds();       // the next round clears the histogram
     }
     // Kept: keys whose bits from sh up exceed pre's, and the first rem keys
