@@ -155,7 +155,7 @@ __device__ __forceinline__ void load4(const float* row, int j, int n, uint32_t k
 // LDS: hist[BINS], cand[CAP] (keys of the digit-1 threshold bin, when they
 // fit), wsum[NT/64], res[4].
 template <int NT, int CAP, bool VEC>
-__device__ void row_topk(const float* row, int n, int k, int32_t* out, uint32_t* hist,
+__device__ __forceinline__ void row_topk(const float* row, int n, int k, int32_t* out, uint32_t* hist,
                          uint32_t* cand, uint32_t* wsum, uint32_t* res) {
     const int tid = threadIdx.x;
     // Digit 1.
