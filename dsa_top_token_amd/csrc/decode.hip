@@ -155,25 +155,30 @@ __device__ __forceinline__ void granule_values(i32x4 w, float* v) {
 }
 
 constexpr int SP_NT = 256;  // threads of a sampling workgroup
-constexpr int SP_NB = 8;    // sample load instructions in flight per lane
+// Sample load instructions in flight per lane: 8, or 4 (twice the sampling
+// workgroups) when 8 would leave fewer than 512 of them: 32 rows of 32K keys
+// 24.8 -> 23.9 us for the threshold and select; 64 rows of 128K keys keep 8
+// (512 workgroups), where 4 made the sampling kernel 0.4 us slower.
+constexpr int SP_NB_MAX = 8;
+constexpr int SP_MIN_WGS = 512;
 
 // Samples scored by one sampling workgroup.
-template <int RB>
-constexpr int sample_chunk() { return (SP_NT / 64) * SP_NB * SampleShape<RB>::RPI; }
+template <int RB, int NB>
+constexpr int sample_chunk() { return (SP_NT / 64) * NB * SampleShape<RB>::RPI; }
 
 // Sample scores of each row: sampling workgroup (b, part) scores samples
-// [part C, part C + C) of row b (C = sample_chunk) and writes their order
+// [part C, part C + C) of row b (C = sample_chunk<RB, SP_NB>) and writes their order
 // keys to a.samp[b][i]. tau only steers how many candidates the filter keeps;
 // the selection is exact for any tau, so the sample scores are fp32 VALU dot
 // products (summation order of their own) rather than the filter's MFMAs.
-template <int DT, int D>
+template <int DT, int D, int SP_NB>
 __global__ __launch_bounds__(SP_NT) void decode_sample_kernel(DecodeArgs a, int per_row) {
     constexpr int RB = D * (DT == 0 ? 1 : 2);
     constexpr int WAVES = SP_NT / 64;
     constexpr int EPG = DT == 0 ? 16 : 8;  // values per granule
     using SS = SampleShape<RB>;
     const int b = (int)(blockIdx.x / (unsigned)per_row);
-    const int i_lo = (int)(blockIdx.x % (unsigned)per_row) * sample_chunk<RB>();
+    const int i_lo = (int)(blockIdx.x % (unsigned)per_row) * sample_chunk<RB, SP_NB>();
     const Plan p = plan_row(a, b);
     if (p.n <= a.top_k || p.ns <= p.m || i_lo >= p.ns) return;  // (the threshold kernel's cases)
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -818,14 +823,21 @@ hipError_t launch_d(const DecodeArgs& a, int part, hipStream_t s) {
     if (part == 0) {
         // sampling workgroups per row: enough for the most samples any row
         // of the problem can take
+        constexpr int RB = D * (DT == 0 ? 1 : 2);
         const long long ns_max = sample_cap(a.n_k, a.top_k);
-        constexpr int CH = sample_chunk<D * (DT == 0 ? 1 : 2)>();
+        constexpr int CH8 = sample_chunk<RB, SP_NB_MAX>(), CH4 = sample_chunk<RB, SP_NB_MAX / 2>();
+        const long long nb8 = (long long)a.B * ((ns_max + CH8 - 1) / CH8);
+        const bool half = nb8 < SP_MIN_WGS;
+        const int CH = half ? CH4 : CH8;
         const int per_row = (int)((ns_max + CH - 1) / CH);
         const long long nb = (long long)a.B * per_row;
         if (nb > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-        if (nb > 0)
-            hipLaunchKernelGGL((decode_sample_kernel<DT, D>), dim3((unsigned)nb), dim3(SP_NT), 0, s,
-                               a, per_row);
+        if (nb > 0 && half)
+            hipLaunchKernelGGL((decode_sample_kernel<DT, D, SP_NB_MAX / 2>), dim3((unsigned)nb),
+                               dim3(SP_NT), 0, s, a, per_row);
+        else if (nb > 0)
+            hipLaunchKernelGGL((decode_sample_kernel<DT, D, SP_NB_MAX>), dim3((unsigned)nb),
+                               dim3(SP_NT), 0, s, a, per_row);
         hipLaunchKernelGGL((decode_threshold_kernel<DT, D>), dim3(a.B), dim3(TH_NT), 0, s, a);
     } else if (part == 1) {
         const int KB = 4 * SLOT;
