@@ -64,13 +64,15 @@ __global__ __launch_bounds__(ROW_NT) void topk_row_kernel(TopkArgs a) {
 
 // ---------------------------------------------------------------------------
 // Short rows (at most WV_MAXN keys): one wave per row with the row's order
-// keys in registers, lane l holding keys [WV_E l, WV_E l + WV_E). Up to four
-// 8-bit radix rounds over a wave-private 256-bin LDS histogram find the k-th
-// key; a round whose chosen bin is taken whole ends the search early (every
-// key of that bin is then kept), and once the chosen bin holds at most 64
-// keys they are gathered, one per lane, and the k-th key is found among
-// them by comparing every pair. One wave scan of the per-lane counts gives
-// each kept key its place in ascending index order.
+// keys in registers, lane l holding keys [WV_E l, WV_E l + WV_E). The bits
+// above the highest one where the row's smallest and largest keys differ are
+// common to every key, so the search starts there; 8-bit radix rounds over a
+// wave-private 256-bin LDS histogram then find the k-th key. A round whose
+// chosen bin is taken whole ends the search early (every key of that bin is
+// then kept), and once the chosen bin holds at most 64 keys they are
+// gathered, one per lane, and the k-th key is found among them by comparing
+// every pair. One wave scan of the per-lane counts gives each kept key its
+// place in ascending index order.
 constexpr int WV_E = 16;               // keys per lane
 constexpr int WV_MAXN = 64 * WV_E;     // keys per row at most
 constexpr int WV_ROWS = 4;             // rows (waves) per workgroup
@@ -86,7 +88,6 @@ template <bool VEC>
 __global__ __launch_bounds__(64 * WV_ROWS) void topk_wave_kernel(TopkArgs a) {
     __shared__ uint32_t hist_all[WV_ROWS][256];
     __shared__ uint32_t gath_all[WV_ROWS][64];
-    __shared__ uint32_t gcnt_all[WV_ROWS];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const long long rid = (long long)blockIdx.x * WV_ROWS + w;
     if (rid >= (long long)a.B * a.rows) return;  // whole wave; no workgroup barrier follows
@@ -105,21 +106,36 @@ __global__ __launch_bounds__(64 * WV_ROWS) void topk_wave_kernel(TopkArgs a) {
     bool ok[WV_E];
 #pragma unroll
     for (int q = 0; q < WV_E; q += 4) load4<VEC>(row, j0 + q, n, key + q, ok + q);
-    // pre: the k-th key's bits found so far; rem: its rank among the keys
-    // sharing them; sh: the lowest bit position those bits reach (24, 16, 8
-    // or 0 once the first round is done).
-    uint32_t pre = 0u, rem = (uint32_t)a.k;
-    int sh = 24;
+    uint32_t kmin = ~0u, kmax = 0u;
+#pragma unroll
+    for (int i = 0; i < WV_E; ++i) {
+        kmin = ok[i] ? min(kmin, key[i]) : kmin;
+        kmax = ok[i] ? max(kmax, key[i]) : kmax;
+    }
+    kmin = (uint32_t)__builtin_amdgcn_readfirstlane((int)wave_min(kmin));
+    kmax = (uint32_t)__builtin_amdgcn_readfirstlane((int)wave_max(kmax));
+    // pre: the k-th key's bits found so far, bits sh..31 (the row's common
+    // bits to start with); rem: its rank among the keys sharing them.
+    const uint32_t dif = kmin ^ kmax;
+    int sh = dif == 0u ? 0 : 32 - __builtin_clz(dif);
+    uint32_t pre = sh >= 32 ? 0u : (kmin >> sh) << sh;
+    uint32_t rem = (uint32_t)a.k;
 #pragma unroll 1
-    for (int d = 3; d >= 0; --d) {
-        const int s8 = 8 * d;
+    while (sh > 0) {
+        // digit: bits s..s+7; those at or above sh are already fixed and
+        // equal in every counted key, so they only narrow the bins in use
+        const int s = max(sh - 8, 0);
+        const uint32_t ph = sh >= 32 ? 0u : pre >> sh;
 #pragma unroll
         for (int q = 0; q < 4; ++q) hist[4 * lane + q] = 0u;
         wave_sync_lds();
+        // Plain LDS atomics: from the first differing bit on, keys spread
+        // over many bins, and an aggregating add would put a serial chain
+        // of lane votes on the path of every key.
 #pragma unroll
         for (int i = 0; i < WV_E; ++i) {
-            const bool in = ok[i] && (d == 3 || (key[i] >> (s8 + 8)) == (pre >> (s8 + 8)));
-            hist_add(hist, (key[i] >> s8) & 255u, in);
+            const bool in = ok[i] && (sh >= 32 || (key[i] >> sh) == ph);
+            if (in) atomicAdd(&hist[(key[i] >> s) & 255u], 1u);
         }
         wave_sync_lds();
         // bin holding the rem-th largest counted key (lanes own bins top-down)
@@ -147,22 +163,24 @@ __global__ __launch_bounds__(64 * WV_ROWS) void topk_wave_kernel(TopkArgs a) {
         const uint32_t bin = (uint32_t)__builtin_amdgcn_readlane(fb, src);
         const uint32_t ab = (uint32_t)__builtin_amdgcn_readlane((int)fa, src);
         const uint32_t cb = (uint32_t)__builtin_amdgcn_readlane((int)fc, src);
-        pre |= bin << s8;
+        pre |= bin << s;
         rem -= ab;
-        sh = s8;
+        sh = s;
         if (rem == cb) break;  // the whole bin is kept
-        if (cb <= 64u && s8 > 0) {
-            // Gather the bin's keys (any order), one per lane, then the
-            // rem-th largest of them: the key with fewer than rem keys above
-            // it and at least rem at or above it.
+        if (cb <= 64u && s > 0) {
+            // Gather the bin's keys (any order), one per lane, each lane's
+            // slots given by a wave scan of its counts; then the rem-th
+            // largest of them: the key with fewer than rem keys above it and
+            // at least rem at or above it.
             uint32_t* gath = gath_all[w];
-            if (lane == 0) gcnt_all[w] = 0u;
-            wave_sync_lds();
+            const uint32_t ps = pre >> s;
+            uint32_t cnt = 0;
+#pragma unroll
+            for (int i = 0; i < WV_E; ++i) cnt += ok[i] && (key[i] >> s) == ps ? 1u : 0u;
+            uint32_t slot = wave_incl_scan(cnt) - cnt;
 #pragma unroll
             for (int i = 0; i < WV_E; ++i) {
-                const bool in = ok[i] && (key[i] >> s8) == (pre >> s8);
-                const uint32_t slot = wave_append(in, &gcnt_all[w]);
-                if (in) gath[slot] = key[i];
+                if (ok[i] && (key[i] >> s) == ps) gath[slot++] = key[i];
             }
             wave_sync_lds();
             const uint32_t mine = lane < (int)cb ? gath[lane] : 0u;
