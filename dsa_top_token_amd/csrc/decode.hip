@@ -228,7 +228,13 @@ __global__ __launch_bounds__(SP_NT) void decode_sample_kernel(DecodeArgs a, int 
 // Sampled threshold of each row (one workgroup per sequence): the row's
 // sample keys into LDS, then two 8-bit radix rounds over the keys relative to
 // the smallest sample give the lower edge of the bin holding the m-th largest
-// sample (at least m samples reach it).
+// sample (at least m samples reach it). The histograms here, and those of
+// the select kernel's one-wave rounds, take plain LDS atomics: aggregating
+// the lanes of a wave that share a bin first (a vote, a first-lane pick and a
+// read-lane per key) timed slower on these short latency-bound rounds. The
+// select kernel's workgroup-wide 12-bit rounds keep the aggregated add: on
+// ragged batches many candidates share a bin there, and plain atomics on them
+// timed slower.
 template <int DT, int D>
 __global__ __launch_bounds__(TH_NT) void decode_threshold_kernel(DecodeArgs a) {
     constexpr int WAVES = TH_NT / 64;
@@ -275,7 +281,7 @@ __global__ __launch_bounds__(TH_NT) void decode_threshold_kernel(DecodeArgs a) {
     const int sh0 = bits > 8 ? bits - 8 : 0;
     for (int i0 = 0; i0 < p.ns; i0 += TH_NT) {
         const int i = i0 + tid;
-        hist_add(hist[0], i < p.ns ? (samp[i] - kmin) >> sh0 : 0u, i < p.ns);
+        if (i < p.ns) atomicAdd(&hist[0][(samp[i] - kmin) >> sh0], 1u);
     }
     __syncthreads();
     if (wave == 0) {
@@ -298,7 +304,7 @@ __global__ __launch_bounds__(TH_NT) void decode_threshold_kernel(DecodeArgs a) {
     for (int i0 = 0; i0 < p.ns; i0 += TH_NT) {
         const int i = i0 + tid;
         const uint32_t d = i < p.ns ? samp[i] - kmin : 0u;
-        hist_add(hist[1], (d >> sh1) & dmask, i < p.ns && (d >> sh0) == b0);
+        if (i < p.ns && (d >> sh0) == b0) atomicAdd(&hist[1][(d >> sh1) & dmask], 1u);
     }
     __syncthreads();
     if (wave == 0) {
@@ -764,7 +770,7 @@ __global__ __launch_bounds__(SEL_NT) void decode_select_kernel(DecodeArgs a) {
                 for (uint32_t g0 = 0; g0 < G; g0 += 64) {
                     const uint32_t gi = g0 + tid;
                     const uint32_t v = gi < G ? gk[gi] : 0u;
-                    hist_add(hist, (v >> s2) & mask, gi < G && (v >> h2) == sp);
+                    if (gi < G && (v >> h2) == sp) atomicAdd(&hist[(v >> s2) & mask], 1u);
                 }
                 wave_lds_fence();
                 uint32_t bin, above;
