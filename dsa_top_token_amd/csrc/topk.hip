@@ -63,82 +63,88 @@ __global__ __launch_bounds__(ROW_NT) void topk_row_kernel(TopkArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Short rows (at most WV_MAXN keys): one wave per row with the row's order
-// keys in registers, lane l holding keys [WV_E l, WV_E l + WV_E). The bits
-// above the highest one where the row's smallest and largest keys differ are
-// common to every key, so the search starts there; 8-bit radix rounds over a
-// wave-private 256-bin LDS histogram then find the k-th key. A round whose
-// chosen bin is taken whole ends the search early (every key of that bin is
-// then kept), and once the chosen bin holds at most 64 keys they are
-// gathered, one per lane, and the k-th key is found among them by comparing
-// every pair. One wave scan of the per-lane counts gives each kept key its
-// place in ascending index order.
-constexpr int WV_E = 16;               // keys per lane
-constexpr int WV_MAXN = 64 * WV_E;     // keys per row at most
-constexpr int WV_ROWS = 4;             // rows (waves) per workgroup
+// Short rows (at most WV_MAXN keys): each row split over NWV waves of one
+// workgroup, lane l of wave h holding keys 64 E h + E l + i, i < E (E =
+// WV_MAXN / (64 NWV) keys per lane), so waves of several rows share a SIMD
+// and hide each other's latency. The bits above the highest one where
+// the row's smallest and largest keys differ are common to every key, so the
+// search starts there; 8-bit radix rounds over a shared 256-bin LDS histogram
+// filled by plain LDS atomics then find the k-th key. A round whose chosen
+// bin is taken whole ends the search early (every key of that bin is then
+// kept), and once the chosen bin holds at most 64 keys they are gathered, one
+// per lane, and the k-th key is found among them by comparing every pair.
+// Wave scans of the per-lane counts, offset by the earlier waves' totals,
+// give each kept key its place in ascending index order. Every decision
+// comes from shared values, so all waves take the same path through the
+// barriers.
+constexpr int WV_MAXN = 1024;          // keys per row at most
+constexpr int WV_NWV = 2;              // waves per row
 
-// Orders one wave's LDS accesses across its lanes.
-__device__ __forceinline__ void wave_sync_lds() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-template <bool VEC>
-__global__ __launch_bounds__(64 * WV_ROWS) void topk_wave_kernel(TopkArgs a) {
-    __shared__ uint32_t hist_all[WV_ROWS][256];
-    __shared__ uint32_t gath_all[WV_ROWS][64];
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const long long rid = (long long)blockIdx.x * WV_ROWS + w;
-    if (rid >= (long long)a.B * a.rows) return;  // whole wave; no workgroup barrier follows
+template <bool VEC, int NWV>
+__global__ __launch_bounds__(64 * NWV) void topk_wave_kernel(TopkArgs a) {
+    constexpr int NT = 64 * NWV;
+    constexpr int KPL = WV_MAXN / NT;  // keys per lane
+    static_assert(KPL % 4 == 0 && KPL * NT == WV_MAXN, "lane layout");
+    __shared__ uint32_t hist[256];
+    __shared__ uint32_t gath[64];
+    __shared__ uint32_t xmm[2 * NWV];  // per-wave key minimum and maximum
+    __shared__ uint32_t xg[NWV];       // per-wave counts of gathered keys
+    __shared__ uint32_t xc[NWV];       // per-wave packed kept counts
+    const int tid = threadIdx.x, lane = tid & 63, h = tid >> 6;
+    const long long rid = blockIdx.x;
     const int b = (int)(rid / a.rows), r = (int)(rid % a.rows);
     const long long pos = a.pos_begin + r + (a.seq_pos ? a.seq_pos[b] : 0);
     const int n = (int)max(0LL, min((long long)a.n_k, pos + 1));
     const float* row = a.scores + (size_t)rid * a.n_k;
     int32_t* out = a.idx + ((size_t)b * a.idx_rows + a.idx_row0 + r) * a.k;
-    if (n <= a.k) {
-        fill_prefix(out, n, a.k, lane, 64);
+    if (n <= a.k) {  // the whole workgroup
+        fill_prefix(out, n, a.k, tid, NT);
         return;
     }
-    uint32_t* hist = hist_all[w];
-    const int j0 = WV_E * lane;
-    uint32_t key[WV_E];
-    bool ok[WV_E];
+    const int j0 = 64 * KPL * h + KPL * lane;
+    uint32_t key[KPL];
+    bool ok[KPL];
 #pragma unroll
-    for (int q = 0; q < WV_E; q += 4) load4<VEC>(row, j0 + q, n, key + q, ok + q);
+    for (int q = 0; q < KPL; q += 4) load4<VEC>(row, j0 + q, n, key + q, ok + q);
     uint32_t kmin = ~0u, kmax = 0u;
 #pragma unroll
-    for (int i = 0; i < WV_E; ++i) {
+    for (int i = 0; i < KPL; ++i) {
         kmin = ok[i] ? min(kmin, key[i]) : kmin;
         kmax = ok[i] ? max(kmax, key[i]) : kmax;
     }
-    kmin = (uint32_t)__builtin_amdgcn_readfirstlane((int)wave_min(kmin));
-    kmax = (uint32_t)__builtin_amdgcn_readfirstlane((int)wave_max(kmax));
-    // pre: the k-th key's bits found so far, bits sh..31 (the row's common
-    // bits to start with); rem: its rank among the keys sharing them.
+    kmin = wave_min(kmin);
+    kmax = wave_max(kmax);
+    if (lane == 0) {
+        xmm[2 * h] = kmin;
+        xmm[2 * h + 1] = kmax;
+    }
+    __syncthreads();
+    kmin = ~0u;
+    kmax = 0u;
+#pragma unroll
+    for (int x = 0; x < NWV; ++x) {
+        kmin = min(kmin, xmm[2 * x]);
+        kmax = max(kmax, xmm[2 * x + 1]);
+    }
+    kmin = (uint32_t)__builtin_amdgcn_readfirstlane((int)kmin);
+    kmax = (uint32_t)__builtin_amdgcn_readfirstlane((int)kmax);
     const uint32_t dif = kmin ^ kmax;
     int sh = dif == 0u ? 0 : 32 - __builtin_clz(dif);
     uint32_t pre = sh >= 32 ? 0u : (kmin >> sh) << sh;
     uint32_t rem = (uint32_t)a.k;
 #pragma unroll 1
     while (sh > 0) {
-        // digit: bits s..s+7; those at or above sh are already fixed and
-        // equal in every counted key, so they only narrow the bins in use
         const int s = max(sh - 8, 0);
         const uint32_t ph = sh >= 32 ? 0u : pre >> sh;
+        for (int x = tid; x < 256; x += NT) hist[x] = 0u;
+        __syncthreads();
 #pragma unroll
-        for (int q = 0; q < 4; ++q) hist[4 * lane + q] = 0u;
-        wave_sync_lds();
-        // Plain LDS atomics: from the first differing bit on, keys spread
-        // over many bins, and an aggregating add would put a serial chain
-        // of lane votes on the path of every key.
-#pragma unroll
-        for (int i = 0; i < WV_E; ++i) {
+        for (int i = 0; i < KPL; ++i) {
             const bool in = ok[i] && (sh >= 32 || (key[i] >> sh) == ph);
             if (in) atomicAdd(&hist[(key[i] >> s) & 255u], 1u);
         }
-        wave_sync_lds();
-        // bin holding the rem-th largest counted key (lanes own bins top-down)
+        __syncthreads();
+        // both waves find the same bin (lanes own bins top-down)
         const int hi = 255 - 4 * lane;
         uint32_t c[4], loc = 0;
 #pragma unroll
@@ -159,30 +165,30 @@ __global__ __launch_bounds__(64 * WV_ROWS) void topk_wave_kernel(TopkArgs a) {
             above += c[q];
         }
         const unsigned long long mk = __ballot(fb >= 0);
-        const int src = __ffsll((long long)mk) - 1;  // exactly one lane holds the bin
+        const int src = __ffsll((long long)mk) - 1;
         const uint32_t bin = (uint32_t)__builtin_amdgcn_readlane(fb, src);
         const uint32_t ab = (uint32_t)__builtin_amdgcn_readlane((int)fa, src);
         const uint32_t cb = (uint32_t)__builtin_amdgcn_readlane((int)fc, src);
         pre |= bin << s;
         rem -= ab;
         sh = s;
-        if (rem == cb) break;  // the whole bin is kept
+        if (rem == cb) break;
         if (cb <= 64u && s > 0) {
-            // Gather the bin's keys (any order), one per lane, each lane's
-            // slots given by a wave scan of its counts; then the rem-th
-            // largest of them: the key with fewer than rem keys above it and
-            // at least rem at or above it.
-            uint32_t* gath = gath_all[w];
             const uint32_t ps = pre >> s;
             uint32_t cnt = 0;
 #pragma unroll
-            for (int i = 0; i < WV_E; ++i) cnt += ok[i] && (key[i] >> s) == ps ? 1u : 0u;
-            uint32_t slot = wave_incl_scan(cnt) - cnt;
+            for (int i = 0; i < KPL; ++i) cnt += ok[i] && (key[i] >> s) == ps ? 1u : 0u;
+            const uint32_t inc = wave_incl_scan(cnt);
+            if (lane == 63) xg[h] = inc;
+            __syncthreads();
+            uint32_t slot = inc - cnt;
 #pragma unroll
-            for (int i = 0; i < WV_E; ++i) {
+            for (int x = 0; x < NWV - 1; ++x) slot += x < h ? xg[x] : 0u;
+#pragma unroll
+            for (int i = 0; i < KPL; ++i) {
                 if (ok[i] && (key[i] >> s) == ps) gath[slot++] = key[i];
             }
-            wave_sync_lds();
+            __syncthreads();
             const uint32_t mine = lane < (int)cb ? gath[lane] : 0u;
             uint32_t ngt = 0, nge = 0;
             for (uint32_t x = 0; x < cb; ++x) {
@@ -191,29 +197,32 @@ __global__ __launch_bounds__(64 * WV_ROWS) void topk_wave_kernel(TopkArgs a) {
                 nge += o >= mine ? 1u : 0u;
             }
             const unsigned long long hit = __ballot(lane < (int)cb && ngt < rem && rem <= nge);
-            const int hl = __ffsll((long long)hit) - 1;  // lanes holding the k-th key agree
+            const int hl = __ffsll((long long)hit) - 1;
             pre = (uint32_t)__builtin_amdgcn_readlane((int)mine, hl);
             rem -= (uint32_t)__builtin_amdgcn_readlane((int)ngt, hl);
             sh = 0;
             break;
         }
-        wave_sync_lds();       // the next round clears the histogram
+        __syncthreads();  // the next round clears the histogram
     }
-    // Kept: keys whose bits from sh up exceed pre's, and the first rem keys
-    // (in index order) equal to them there.
     const uint32_t th = pre >> sh;
     uint32_t gt = 0, eq = 0;
 #pragma unroll
-    for (int i = 0; i < WV_E; ++i) {
+    for (int i = 0; i < KPL; ++i) {
         const uint32_t kh = key[i] >> sh;
         gt += ok[i] && kh > th ? 1u : 0u;
         eq += ok[i] && kh == th ? 1u : 0u;
     }
     const uint32_t pk = (gt << 16) | eq;
-    const uint32_t ex = wave_incl_scan(pk) - pk;
+    const uint32_t inc = wave_incl_scan(pk);
+    if (lane == 63) xc[h] = inc;
+    __syncthreads();
+    uint32_t ex = inc - pk;
+#pragma unroll
+    for (int x = 0; x < NWV - 1; ++x) ex += x < h ? xc[x] : 0u;
     uint32_t gb = ex >> 16, eb = ex & 0xffffu;
 #pragma unroll
-    for (int i = 0; i < WV_E; ++i) {
+    for (int i = 0; i < KPL; ++i) {
         if (!ok[i]) continue;
         const uint32_t kh = key[i] >> sh;
         if (kh > th) {
@@ -601,13 +610,12 @@ hipError_t launch_topk(const TopkArgs& t, hipStream_t s) {
     const bool vec = (t.n_k % 4 == 0) && ((reinterpret_cast<uintptr_t>(t.scores) & 15) == 0);
     if (!topk_use_chunked(t.B, t.rows, t.n_k)) {
         if (t.n_k <= WV_MAXN) {
-            const long long nb = (rows + WV_ROWS - 1) / WV_ROWS;
             if (vec)
-                hipLaunchKernelGGL(topk_wave_kernel<true>, dim3((unsigned)nb), dim3(64 * WV_ROWS), 0,
-                                   s, t);
+                hipLaunchKernelGGL((topk_wave_kernel<true, WV_NWV>), dim3((unsigned)rows),
+                                   dim3(64 * WV_NWV), 0, s, t);
             else
-                hipLaunchKernelGGL(topk_wave_kernel<false>, dim3((unsigned)nb), dim3(64 * WV_ROWS), 0,
-                                   s, t);
+                hipLaunchKernelGGL((topk_wave_kernel<false, WV_NWV>), dim3((unsigned)rows),
+                                   dim3(64 * WV_NWV), 0, s, t);
             return hipGetLastError();
         }
         if (vec)
