@@ -309,7 +309,7 @@ __global__ __launch_bounds__(CH_NT) void topk_hist_kernel(MultiArgs a) {
         bool ok[4];
         load4<VEC>(row, base + 4 * threadIdx.x, j1, key, ok);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) hist_add(hist, key[e] >> SHIFT1, ok[e]);
+        for (int e = 0; e < 4; ++e) hist_inc(hist, key[e] >> SHIFT1, ok[e]);
     }
     __syncthreads();
     uint32_t* g = a.w.hist + (size_t)slot * BINS;
@@ -461,7 +461,7 @@ __global__ __launch_bounds__(SB_NT) void topk_select_b_kernel(MultiArgs a) {
     for (int base = 0; base < (int)cnt; base += SB_NT) {
         const int i = base + tid;
         const bool ok = i < (int)cnt;
-        hist_add(hist, ok ? (keys[i] >> SHIFT2) & (BINS - 1) : 0u, ok);
+        hist_inc(hist, ok ? (keys[i] >> SHIFT2) & (BINS - 1) : 0u, ok);
     }
     __syncthreads();
     find_bin<SB_NT>(hist, rem, wsum, res);
@@ -474,7 +474,7 @@ __global__ __launch_bounds__(SB_NT) void topk_select_b_kernel(MultiArgs a) {
     for (int base = 0; base < (int)cnt; base += SB_NT) {
         const int i = base + tid;
         const bool ok = i < (int)cnt && (keys[i] >> SHIFT2) == pre22;
-        hist_add(hist, ok ? keys[i] & 1023u : 0u, ok);
+        hist_inc(hist, ok ? keys[i] & 1023u : 0u, ok);
     }
     __syncthreads();
     find_bin<SB_NT>(hist, rem, wsum, res);
@@ -489,7 +489,7 @@ __global__ __launch_bounds__(SB_NT) void topk_select_b_kernel(MultiArgs a) {
     for (int base = 0; base < (int)cnt; base += SB_NT) {
         const int i = base + tid;
         const bool ok = i < (int)cnt && keys[i] == T;
-        hist_add(hist, ok ? (JMAX - jj[i]) >> 11 : 0u, ok);
+        hist_inc(hist, ok ? (JMAX - jj[i]) >> 11 : 0u, ok);
     }
     __syncthreads();
     find_bin<SB_NT>(hist, rem, wsum, res);
@@ -501,7 +501,7 @@ __global__ __launch_bounds__(SB_NT) void topk_select_b_kernel(MultiArgs a) {
     for (int base = 0; base < (int)cnt; base += SB_NT) {
         const int i = base + tid;
         const bool ok = i < (int)cnt && keys[i] == T && ((JMAX - jj[i]) >> 11) == a1;
-        hist_add(hist, ok ? (JMAX - jj[i]) & 2047u : 0u, ok);
+        hist_inc(hist, ok ? (JMAX - jj[i]) & 2047u : 0u, ok);
     }
     __syncthreads();
     find_bin<SB_NT>(hist, remj, wsum, res);
